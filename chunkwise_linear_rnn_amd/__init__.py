@@ -1,0 +1,26 @@
+"""MI355X (gfx950) chunkwise gated linear attention: Python binding of libgla_mi355x.so.
+
+The binding only marshals arguments: it checks tensor shapes/dtypes/devices, allocates
+outputs and the workspace with torch, and passes raw device pointers plus the current
+HIP stream to the C ABI declared in include/gla.h.  Every step of the computation runs
+in the library's HIP kernels; there is no CPU or PyTorch fallback.  If the library is
+not built, every call raises.
+
+Entry points mirror the C ABI:
+    fwd(q, k, v, log_alpha, S0=None, ...)              -> (o, S_T)
+    bwd(q, k, v, log_alpha, dO, S0=None, dS_T=None)     -> (dq, dk, dv, dlog_alpha, dS0)
+    gate_cumsum(log_alpha, chunk)                       -> (g, gamma)
+    chunk_states(k, v, log_alpha, S0=None)              -> (states, S_T)
+    workspace_bytes(desc, pass_), validate(desc, pass_), status_string(code)
+and GLAFunction, a torch.autograd.Function over fwd/bwd.
+"""
+from __future__ import annotations
+
+from ._native import (GlaDesc, GlaError, F32, BF16, MATERIALIZED, RECOMPUTE, PASS_FWD,  # noqa: F401
+                      PASS_BWD, PASS_STATES, lib, lib_path, make_desc, status_string, validate,
+                      version, workspace_bytes)
+from .ops import fwd, bwd, gate_cumsum, chunk_states, GLAFunction, gla  # noqa: F401
+
+__all__ = ["fwd", "bwd", "gate_cumsum", "chunk_states", "GLAFunction", "gla", "GlaDesc",
+           "GlaError", "make_desc", "workspace_bytes", "validate", "status_string", "version",
+           "lib", "lib_path"]

@@ -1,0 +1,95 @@
+"""ctypes view of the C ABI in include/gla.h (libgla_mi355x.so, built in-tree).
+
+Nothing here touches a GPU: loading the library and the host-only entry points
+(gla_validate, gla_workspace_bytes, gla_status_string, gla_version) work on a machine
+without one.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libgla_mi355x.so"
+
+F32, BF16 = 0, 1
+MATERIALIZED, RECOMPUTE = 0, 1
+PASS_FWD, PASS_BWD, PASS_STATES = 0, 1, 2
+
+# Every function include/gla.h declares, with its ctypes signature.
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+
+
+class GlaDesc(ctypes.Structure):
+    _fields_ = [("B", _i32), ("H", _i32), ("T", _i32), ("dk", _i32), ("dv", _i32),
+                ("chunk", _i32), ("subchunk", _i32), ("dtype", _i32), ("state_mode", _i32)]
+
+    def __repr__(self):
+        return "GlaDesc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+_PDESC = ctypes.POINTER(GlaDesc)
+SIGNATURES = {
+    "gla_status_string": (ctypes.c_char_p, [_i32]),
+    "gla_version": (_i32, []),
+    "gla_validate": (_i32, [_PDESC, _i32]),
+    "gla_workspace_bytes": (_i32, [_PDESC, _i32, ctypes.POINTER(_sz)]),
+    "gla_gate_cumsum": (_i32, [_PDESC, _vp, _vp, _vp, _vp]),
+    "gla_chunk_states": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "gla_chunk_fwd": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "gla_chunk_bwd": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it first "
+                               "(python -m chunkwise_linear_rnn_amd.build)")
+        h = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+class GlaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)}")
+
+
+def status_string(code: int) -> str:
+    return lib().gla_status_string(int(code)).decode()
+
+
+def version() -> int:
+    return int(lib().gla_version())
+
+
+def make_desc(B, H, T, dk, dv, chunk=64, subchunk=16, dtype=BF16, state_mode=RECOMPUTE) -> GlaDesc:
+    return GlaDesc(B, H, T, dk, dv, chunk, subchunk, dtype, state_mode)
+
+
+def validate(desc: GlaDesc, pass_: int = PASS_FWD) -> int:
+    return int(lib().gla_validate(ctypes.byref(desc), int(pass_)))
+
+
+def workspace_bytes(desc: GlaDesc, pass_: int = PASS_FWD) -> int:
+    out = _sz(0)
+    st = lib().gla_workspace_bytes(ctypes.byref(desc), int(pass_), ctypes.byref(out))
+    if st != 0:
+        raise GlaError(st, "gla_workspace_bytes")
+    return int(out.value)

@@ -1,0 +1,315 @@
+// C ABI of libgla_mi355x.so: argument validation, workspace planning and launch
+// sequencing on the caller's stream.  See include/gla.h for the contract.
+//
+// Pipelines (page "Gated Linear Attention Transformers with Hardware-Efficient
+// Training", atlas.scime.ai summary, section Approach):
+//   forward, materialized states:  gate cumsum -> intra-chunk (A, Qh, Kh^T, e^gamma)
+//                                  -> state scan (writes every S_[i]) -> output
+//   forward, recomputed states:    intra-chunk (cumsum fused) -> fused state+output
+//   backward:                      gate cumsum -> intra-chunk -> state scan (S_[i]) ->
+//                                  reverse state scan (dS_[i+1], dS0); both scans also
+//                                  form the chunk totals of q*dq - k*dk from their fp32
+//                                  states -> chunk backward (dq, dk, dv, chunk-local D
+//                                  suffix sums) -> closed-form gate gradient scan
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <initializer_list>
+
+#include "gla.h"
+#include "gla_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Dims {
+  long B, H, T, dk, dv, C, N, BH;
+  int dtype;
+  size_t esz;   // bytes per element of the [B,H,T,*] tensors and of MFMA operands
+};
+
+Dims dims_of(const gla_desc_t* d) {
+  Dims x;
+  x.B = d->B; x.H = d->H; x.T = d->T; x.dk = d->dk; x.dv = d->dv; x.C = d->chunk;
+  x.N = x.T > 0 ? (x.T + x.C - 1) / x.C : 0;
+  x.BH = x.B * x.H;
+  x.dtype = d->dtype;
+  x.esz = d->dtype == GLA_F32 ? 4 : 2;
+  return x;
+}
+
+// Workspace carving.  Every region is 256-byte aligned.
+struct Plan {
+  size_t g = 0, A = 0, Qh = 0, QhT = 0, Kh = 0, KhT = 0, eg = 0, st = 0, dst = 0, ST = 0,
+         cT = 0, Dloc = 0, crossF = 0, crossR = 0, carry = 0, total = 0;
+};
+
+Plan plan_of(const gla_desc_t* d, int pass) {
+  const Dims x = dims_of(d);
+  Plan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  const size_t rowsP = (size_t)x.BH * x.N * x.C;          // padded token rows
+  const size_t gB = (size_t)x.BH * x.T * x.dk * 4;
+  const size_t AB = (size_t)x.BH * x.N * x.C * x.C * x.esz;
+  const size_t opB = rowsP * x.dk * x.esz;
+  const size_t egB = (size_t)x.BH * x.N * x.dk * 4;
+  const size_t stB = (size_t)x.BH * x.N * x.dk * x.dv * x.esz;
+  const bool mat = d->state_mode == GLA_STATES_MATERIALIZED;
+  if (pass == GLA_PASS_FWD) {
+    if (mat) p.g = take(gB);
+    p.A = take(AB);
+    p.Qh = take(opB);
+    p.KhT = take(opB);
+    p.eg = take(egB);
+    if (mat) p.st = take(stB);
+  } else if (pass == GLA_PASS_BWD) {
+    // the scans' transposed operands are kept in fp32 (split into two bf16 halves)
+    const size_t op32 = rowsP * x.dk * 4;
+    const size_t crossB = (size_t)x.BH * x.N * (x.dv / 64) * x.dk * 4;
+    p.g = take(gB);
+    p.A = take(AB);
+    p.QhT = take(op32);
+    p.Kh = take(opB);
+    p.KhT = take(op32);
+    p.eg = take(egB);
+    p.st = take(stB);
+    p.dst = take(stB);
+    p.ST = take((size_t)x.BH * x.dk * x.dv * 4);
+    p.cT = take((size_t)x.BH * x.dk * 4);
+    p.Dloc = take(gB);
+    p.crossF = take(crossB);
+    p.crossR = take(crossB);
+    p.carry = take(egB);
+  } else {
+    p.KhT = take(opB);
+    p.eg = take(egB);
+  }
+  p.total = off;
+  return p;
+}
+
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+gla_status_t dev(hipError_t e) { return e == hipSuccess ? GLA_OK : GLA_ERR_DEVICE; }
+
+// Zero or copy a [BH,dk,dv] fp32 state with a kernel (safe under stream capture).
+__global__ void k_state_copy(const float* __restrict__ src, float* __restrict__ dst, long n) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    dst[i] = src ? src[i] : 0.f;
+}
+gla_status_t state_copy(const float* src, float* dst, long n, hipStream_t s) {
+  if (!dst || n == 0) return GLA_OK;
+  const long blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  hipLaunchKernelGGL(k_state_copy, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
+  return dev(hipGetLastError());
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gla_status_string(gla_status_t s) {
+  switch (s) {
+    case GLA_OK: return "GLA_OK";
+    case GLA_ERR_INVALID_ARG: return "GLA_ERR_INVALID_ARG";
+    case GLA_ERR_UNSUPPORTED: return "GLA_ERR_UNSUPPORTED";
+    case GLA_ERR_WORKSPACE: return "GLA_ERR_WORKSPACE";
+    case GLA_ERR_DEVICE: return "GLA_ERR_DEVICE";
+  }
+  return "GLA_ERR_UNKNOWN";
+}
+
+int32_t gla_version(void) { return 10000 * 0 + 100 * 1 + 0; }
+
+gla_status_t gla_validate(const gla_desc_t* d, int32_t pass) {
+  if (!d) return GLA_ERR_INVALID_ARG;
+  if (pass < 0 || pass > 2) return GLA_ERR_INVALID_ARG;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->dk < 0 || d->dv < 0) return GLA_ERR_INVALID_ARG;
+  if (d->chunk < 1 || d->subchunk < 1 || d->chunk % d->subchunk != 0) return GLA_ERR_INVALID_ARG;
+  if (d->dtype != GLA_F32 && d->dtype != GLA_BF16) return GLA_ERR_INVALID_ARG;
+  if (d->state_mode != GLA_STATES_MATERIALIZED && d->state_mode != GLA_STATES_RECOMPUTE)
+    return GLA_ERR_INVALID_ARG;
+  if (d->chunk != 64 && d->chunk != 128) return GLA_ERR_UNSUPPORTED;
+  if (d->subchunk != 16) return GLA_ERR_UNSUPPORTED;
+  if (d->dtype == GLA_F32 && d->chunk != 64) return GLA_ERR_UNSUPPORTED;
+  if (d->dk < 64 || d->dk > 256 || d->dk % 64 != 0) return GLA_ERR_UNSUPPORTED;
+  if (d->dv < 64 || d->dv > 1024 || d->dv % 64 != 0) return GLA_ERR_UNSUPPORTED;
+  const long long bh = (long long)d->B * d->H;
+  if (bh > 65535) return GLA_ERR_UNSUPPORTED;
+  if (bh * (long long)d->T > (1LL << 31) - 1) return GLA_ERR_UNSUPPORTED;
+  if (((long long)d->T + d->chunk - 1) / d->chunk > 65535) return GLA_ERR_UNSUPPORTED;
+  return GLA_OK;
+}
+
+gla_status_t gla_workspace_bytes(const gla_desc_t* d, int32_t pass, size_t* bytes) {
+  if (!bytes) return GLA_ERR_INVALID_ARG;
+  const gla_status_t st = gla_validate(d, pass);
+  if (st != GLA_OK) return st;
+  *bytes = plan_of(d, pass).total;
+  return GLA_OK;
+}
+
+gla_status_t gla_gate_cumsum(const gla_desc_t* d, const void* log_alpha, float* g, float* gamma,
+                             void* stream) {
+  const gla_status_t st = gla_validate(d, GLA_PASS_FWD);
+  if (st != GLA_OK) return st;
+  const Dims x = dims_of(d);
+  if (x.BH * x.T == 0) return GLA_OK;
+  if (!log_alpha || (!g && !gamma)) return GLA_ERR_INVALID_ARG;
+  if (!aligned16(log_alpha) || !aligned16(g) || !aligned16(gamma)) return GLA_ERR_INVALID_ARG;
+  return dev(gla::launch_gate_cumsum(x.dtype, log_alpha, g, gamma, (int)x.BH, (int)x.T,
+                                     (int)x.dk, (int)x.C, (hipStream_t)stream));
+}
+
+gla_status_t gla_chunk_states(const gla_desc_t* d, const void* k, const void* v,
+                              const void* log_alpha, const float* S0, float* states, float* S_T,
+                              void* ws, size_t ws_bytes, void* stream) {
+  const gla_status_t st = gla_validate(d, 2);
+  if (st != GLA_OK) return st;
+  const Dims x = dims_of(d);
+  hipStream_t s = (hipStream_t)stream;
+  if (x.BH == 0) return GLA_OK;
+  if (x.T == 0) return state_copy(S0, S_T, x.BH * x.dk * x.dv, s);
+  if (!k || !v || !log_alpha || !states) return GLA_ERR_INVALID_ARG;
+  for (const void* p : std::initializer_list<const void*>{k, v, log_alpha, S0, states, S_T, ws})
+    if (!aligned16(p)) return GLA_ERR_INVALID_ARG;
+  const Plan p = plan_of(d, 2);
+  if (!ws || ws_bytes < p.total) return GLA_ERR_WORKSPACE;
+  char* w = (char*)ws;
+  gla::IntraArgs ia{};
+  ia.dtype = x.dtype; ia.C = (int)x.C; ia.BH = (int)x.BH; ia.T = (int)x.T; ia.dk = (int)x.dk;
+  ia.N = (int)x.N; ia.want_A = false; ia.q = k; ia.k = k; ia.la = log_alpha; ia.g = nullptr;
+  ia.KhT = w + p.KhT; ia.eg = (float*)(w + p.eg);
+  gla_status_t rs = dev(gla::launch_intra(ia, s));
+  if (rs != GLA_OK) return rs;
+  gla::ScanArgs sa{};
+  sa.dtype = x.dtype; sa.C = (int)x.C; sa.BH = (int)x.BH; sa.T = (int)x.T; sa.dk = (int)x.dk;
+  sa.dv = (int)x.dv; sa.N = (int)x.N; sa.reverse = false; sa.store = 3;
+  sa.XT = w + p.KhT; sa.Y = v; sa.eg = (const float*)(w + p.eg); sa.S_in = S0;
+  sa.states = states; sa.S_out = S_T;
+  return dev(gla::launch_state_scan(sa, s));
+}
+
+gla_status_t gla_chunk_fwd(const gla_desc_t* d, const void* q, const void* k, const void* v,
+                           const void* log_alpha, const float* S0, void* o, float* S_T, void* ws,
+                           size_t ws_bytes, void* stream) {
+  const gla_status_t st = gla_validate(d, GLA_PASS_FWD);
+  if (st != GLA_OK) return st;
+  const Dims x = dims_of(d);
+  hipStream_t s = (hipStream_t)stream;
+  if (x.BH == 0) return GLA_OK;
+  if (x.T == 0) return state_copy(S0, S_T, x.BH * x.dk * x.dv, s);
+  if (!q || !k || !v || !log_alpha || !o) return GLA_ERR_INVALID_ARG;
+  for (const void* p : std::initializer_list<const void*>{q, k, v, log_alpha, S0, o, S_T, ws})
+    if (!aligned16(p)) return GLA_ERR_INVALID_ARG;
+  const Plan p = plan_of(d, GLA_PASS_FWD);
+  if (!ws || ws_bytes < p.total) return GLA_ERR_WORKSPACE;
+  char* w = (char*)ws;
+  const bool mat = d->state_mode == GLA_STATES_MATERIALIZED;
+  gla_status_t rs = GLA_OK;
+  if (mat) {
+    rs = dev(gla::launch_gate_cumsum(x.dtype, log_alpha, (float*)(w + p.g), nullptr, (int)x.BH,
+                                     (int)x.T, (int)x.dk, (int)x.C, s));
+    if (rs != GLA_OK) return rs;
+  }
+  gla::IntraArgs ia{};
+  ia.dtype = x.dtype; ia.C = (int)x.C; ia.BH = (int)x.BH; ia.T = (int)x.T; ia.dk = (int)x.dk;
+  ia.N = (int)x.N; ia.want_A = true; ia.q = q; ia.k = k; ia.la = log_alpha;
+  ia.g = mat ? (const float*)(w + p.g) : nullptr;
+  ia.A = w + p.A; ia.Qh = w + p.Qh; ia.KhT = w + p.KhT; ia.eg = (float*)(w + p.eg);
+  rs = dev(gla::launch_intra(ia, s));
+  if (rs != GLA_OK) return rs;
+  if (mat) {
+    gla::ScanArgs sa{};
+    sa.dtype = x.dtype; sa.C = (int)x.C; sa.BH = (int)x.BH; sa.T = (int)x.T; sa.dk = (int)x.dk;
+    sa.dv = (int)x.dv; sa.N = (int)x.N; sa.reverse = false; sa.store = 2;
+    sa.XT = w + p.KhT; sa.Y = v; sa.eg = (const float*)(w + p.eg); sa.S_in = S0;
+    sa.states = w + p.st; sa.S_out = S_T;
+    rs = dev(gla::launch_state_scan(sa, s));
+    if (rs != GLA_OK) return rs;
+    gla::OutArgs oa{};
+    oa.dtype = x.dtype; oa.C = (int)x.C; oa.BH = (int)x.BH; oa.T = (int)x.T; oa.dk = (int)x.dk;
+    oa.dv = (int)x.dv; oa.N = (int)x.N; oa.Qh = w + p.Qh; oa.A = w + p.A; oa.STt = w + p.st;
+    oa.v = v; oa.o = o;
+    return dev(gla::launch_output(oa, s));
+  }
+  gla::FusedArgs fa{};
+  fa.dtype = x.dtype; fa.C = (int)x.C; fa.BH = (int)x.BH; fa.T = (int)x.T; fa.dk = (int)x.dk;
+  fa.dv = (int)x.dv; fa.N = (int)x.N; fa.Qh = w + p.Qh; fa.KhT = w + p.KhT; fa.A = w + p.A;
+  fa.v = v; fa.eg = (const float*)(w + p.eg); fa.S0 = S0; fa.o = o; fa.S_T = S_T;
+  return dev(gla::launch_fwd_fused(fa, s));
+}
+
+gla_status_t gla_chunk_bwd(const gla_desc_t* d, const void* q, const void* k, const void* v,
+                           const void* log_alpha, const float* S0, const void* dO,
+                           const float* dS_T, void* dq, void* dk, void* dv, void* dlog_alpha,
+                           float* dS0, void* ws, size_t ws_bytes, void* stream) {
+  const gla_status_t st = gla_validate(d, GLA_PASS_BWD);
+  if (st != GLA_OK) return st;
+  const Dims x = dims_of(d);
+  hipStream_t s = (hipStream_t)stream;
+  if (x.BH == 0) return GLA_OK;
+  if (x.T == 0) return state_copy(dS_T, dS0, x.BH * x.dk * x.dv, s);
+  if (!q || !k || !v || !log_alpha || !dO || !dq || !dk || !dv || !dlog_alpha)
+    return GLA_ERR_INVALID_ARG;
+  for (const void* p : std::initializer_list<const void*>{q, k, v, log_alpha, S0, dO, dS_T, dq,
+                                                          dk, dv, dlog_alpha, dS0, ws})
+    if (!aligned16(p)) return GLA_ERR_INVALID_ARG;
+  const Plan p = plan_of(d, GLA_PASS_BWD);
+  if (!ws || ws_bytes < p.total) return GLA_ERR_WORKSPACE;
+  char* w = (char*)ws;
+  const int C = (int)x.C, BH = (int)x.BH, T = (int)x.T, DK = (int)x.dk, DV = (int)x.dv,
+            N = (int)x.N;
+  gla_status_t rs = dev(gla::launch_gate_cumsum(x.dtype, log_alpha, (float*)(w + p.g), nullptr,
+                                                BH, T, DK, C, s));
+  if (rs != GLA_OK) return rs;
+  gla::IntraArgs ia{};
+  ia.dtype = x.dtype; ia.C = C; ia.BH = BH; ia.T = T; ia.dk = DK; ia.N = N; ia.want_A = true;
+  ia.xt_f32 = x.dtype == GLA_BF16;
+  ia.q = q; ia.k = k; ia.la = log_alpha; ia.g = (const float*)(w + p.g);
+  ia.A = w + p.A; ia.QhT = w + p.QhT; ia.Kh = w + p.Kh; ia.KhT = w + p.KhT;
+  ia.eg = (float*)(w + p.eg);
+  rs = dev(gla::launch_intra(ia, s));
+  if (rs != GLA_OK) return rs;
+  // forward scan: chunk-start states S_[i]; cross term rowsum(S_[i] * Qh_i^T dO_i)
+  gla::ScanArgs sa{};
+  sa.dtype = x.dtype; sa.C = C; sa.BH = BH; sa.T = T; sa.dk = DK; sa.dv = DV; sa.N = N;
+  sa.reverse = false; sa.xt_f32 = ia.xt_f32; sa.store = 1;
+  sa.XT = w + p.KhT; sa.Y = v; sa.X2T = w + p.QhT; sa.Y2 = dO; sa.cross = (float*)(w + p.crossF);
+  sa.eg = (const float*)(w + p.eg); sa.S_in = S0; sa.states = w + p.st;
+  sa.S_out = dS_T ? (float*)(w + p.ST) : nullptr;
+  rs = dev(gla::launch_state_scan(sa, s));
+  if (rs != GLA_OK) return rs;
+  // reverse scan: dS_[i+1]; cross term rowsum(dS_[i+1] * Kh_i^T V_i)
+  gla::ScanArgs ra = sa;
+  ra.reverse = true; ra.XT = w + p.QhT; ra.Y = dO; ra.X2T = w + p.KhT; ra.Y2 = v;
+  ra.cross = (float*)(w + p.crossR); ra.S_in = dS_T; ra.states = w + p.dst; ra.S_out = dS0;
+  rs = dev(gla::launch_state_scan(ra, s));
+  if (rs != GLA_OK) return rs;
+  if (dS_T) {
+    rs = dev(gla::launch_state_dot(dS_T, (const float*)(w + p.ST), (float*)(w + p.cT), BH, DK,
+                                   DV, s));
+    if (rs != GLA_OK) return rs;
+  }
+  gla::BwdArgs ba{};
+  ba.dtype = x.dtype; ba.C = C; ba.BH = BH; ba.T = T; ba.dk = DK; ba.dv = DV; ba.N = N;
+  ba.q = q; ba.k = k; ba.v = v; ba.dO = dO; ba.g = (const float*)(w + p.g); ba.gamma = nullptr;
+  ba.A = w + p.A; ba.Kh = w + p.Kh; ba.S = w + p.st; ba.dS = w + p.dst;
+  ba.dq = dq; ba.dk_out = dk; ba.dv_out = dv; ba.Dloc = (float*)(w + p.Dloc);
+  rs = dev(gla::launch_bwd_chunk(ba, s));
+  if (rs != GLA_OK) return rs;
+  return dev(gla::launch_gate_grad(x.dtype, (const float*)(w + p.Dloc),
+                                   (const float*)(w + p.crossF), (const float*)(w + p.crossR),
+                                   dS_T ? (const float*)(w + p.cT) : nullptr,
+                                   (float*)(w + p.carry), dlog_alpha, BH, T, DK, DV, C, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+// Device-side building blocks shared by the gfx950 GLA kernels: element types, the
+// MFMA 16x16 tile step, operand-fragment loads, and global<->LDS tile staging.
+//
+// MFMA conventions (CDNA4 v_mfma_f32_16x16x32_bf16 and v_mfma_f32_16x16x4_f32, checked
+// on the device): in a wave of 64 lanes, lane l has r = l % 16 and q = l / 16.
+//   accumulator (16x16 fp32 tile D):  lane holds D[4q + i][r], i = 0..3   (f32x4)
+//   one "k32 step" D += A(16x32) * B(32x16): lane supplies 8 values of row r of A and
+//   the same 8 k-indices of column r of B.  Which 8 of the 32 k-indices lane group q
+//   carries is a free choice as long as A and B agree; two choices are used:
+//     contiguous   k = 8q + e                       (one 16-byte bf16 load)
+//     acc-order    k = 4q + e (e<4), 16 + 4q + e-4   (matches two stacked accumulator
+//                  tiles, so an fp32 accumulator can feed the next product as B)
+// For fp32 operands the k32 step is 8 v_mfma_f32_16x16x4_f32, the e-th taking element
+// e from every lane group.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gla {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;   // 4 waves per workgroup everywhere
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// e^x with the hardware base-2 exponential.  Arguments here are differences of
+// cumulative log-gates (<= 0 in every use), so no overflow handling is needed.
+__device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// ---------------------------------------------------------------------------------
+// Operand fragments and the k32 MFMA step
+// ---------------------------------------------------------------------------------
+template <typename OpT> struct Frag;
+template <> struct Frag<bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void set(int e, float x) { v[e] = (bf16)x; }
+  __device__ __forceinline__ float get(int e) const { return (float)v[e]; }
+};
+template <> struct Frag<float> {
+  float v[8];
+  __device__ __forceinline__ void set(int e, float x) { v[e] = x; }
+  __device__ __forceinline__ float get(int e) const { return v[e]; }
+};
+
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+// Contiguous-order fragment: p points at (row, k0) of a k-contiguous tile; reads
+// p[8q .. 8q+7].  p + 8q must be 16-byte aligned.
+__device__ __forceinline__ void load_frag_c(Frag<bf16>& f, const bf16* p) {
+  f.v = *reinterpret_cast<const bf16x8*>(p + 8 * (lane_id() >> 4));
+}
+__device__ __forceinline__ void load_frag_c(Frag<float>& f, const float* p) {
+  const f32x4* s = reinterpret_cast<const f32x4*>(p + 8 * (lane_id() >> 4));
+  f32x4 a = s[0], b = s[1];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = b[e]; }
+}
+// Acc-order fragment: reads p[4q .. 4q+3] and p[16+4q .. 16+4q+3].
+__device__ __forceinline__ void load_frag_a(Frag<bf16>& f, const bf16* p) {
+  const int q = lane_id() >> 4;
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(p + 4 * q);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 16 + 4 * q);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = b[e]; }
+}
+__device__ __forceinline__ void load_frag_a(Frag<float>& f, const float* p) {
+  const int q = lane_id() >> 4;
+  f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * q);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 16 + 4 * q);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = b[e]; }
+}
+// B fragment (acc order) from two stacked fp32 accumulator tiles (rows 0-15, 16-31).
+template <typename OpT>
+__device__ __forceinline__ void frag_from_acc(Frag<OpT>& f, const f32x4& lo, const f32x4& hi) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f.set(e, lo[e]); f.set(4 + e, hi[e]); }
+}
+
+// ---------------------------------------------------------------------------------
+// Vector loads of 8 consecutive input elements, widened to fp32
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ void load8(float (&x)[8], const bf16* p) {
+  bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+}
+__device__ __forceinline__ void load8(float (&x)[8], const float* p) {
+  f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+}
+__device__ __forceinline__ void store8(bf16* p, const float (&x)[8]) {
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (bf16)x[e];
+  *reinterpret_cast<bf16x8*>(p) = v;
+}
+__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { a[e] = x[e]; b[e] = x[4 + e]; }
+  reinterpret_cast<f32x4*>(p)[0] = a;
+  reinterpret_cast<f32x4*>(p)[1] = b;
+}
+__device__ __forceinline__ void zero8(float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = 0.f;
+}
+
+// ---------------------------------------------------------------------------------
+// Tile staging, global (row-major, `rows` valid rows, zero beyond) -> LDS.
+// All threads of the workgroup take part; the caller places the barriers.
+// ---------------------------------------------------------------------------------
+// Same orientation: lds[r * lld + c] = src[r * gld + c], c in [0, COLS).
+template <typename OpT, typename Tin, int ROWS, int COLS>
+__device__ __forceinline__ void stage_rows(OpT* lds, int lld, const Tin* src, long gld, int rows) {
+  constexpr int kVec = COLS / 8;
+  for (int idx = threadIdx.x; idx < ROWS * kVec; idx += kThreads) {
+    const int r = idx / kVec, c = (idx % kVec) * 8;
+    float x[8];
+    if (r < rows) load8(x, src + r * gld + c); else zero8(x);
+    store8(lds + r * lld + c, x);
+  }
+}
+// Transposed: lds[c * lld + r] = src[r * gld + c] for r in [0, ROWS), c in [0, COLS).
+// Each thread moves a 2-row x 8-column block so that bf16 pairs go out as 32-bit words.
+template <typename OpT, typename Tin, int ROWS, int COLS>
+__device__ __forceinline__ void stage_cols(OpT* lds, int lld, const Tin* src, long gld, int rows) {
+  constexpr int kVec = COLS / 8;
+  for (int idx = threadIdx.x; idx < (ROWS / 2) * kVec; idx += kThreads) {
+    const int r = (idx / kVec) * 2, c = (idx % kVec) * 8;
+    float x0[8], x1[8];
+    if (r < rows) load8(x0, src + r * gld + c); else zero8(x0);
+    if (r + 1 < rows) load8(x1, src + (r + 1) * gld + c); else zero8(x1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (sizeof(OpT) == 2) {
+        bf16x2 w;
+        w[0] = (bf16)x0[e];
+        w[1] = (bf16)x1[e];
+        *reinterpret_cast<bf16x2*>(lds + (c + e) * lld + r) = w;
+      } else {
+        f32x2 w;
+        w[0] = x0[e];
+        w[1] = x1[e];
+        *reinterpret_cast<f32x2*>(lds + (c + e) * lld + r) = w;
+      }
+    }
+  }
+}
+
+}  // namespace gla

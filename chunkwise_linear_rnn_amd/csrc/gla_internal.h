@@ -1,0 +1,76 @@
+// Host-side launchers of the gfx950 GLA kernels (internal to libgla_mi355x.so).
+// dtype: 0 = fp32 inputs / fp32 operands, 1 = bf16 inputs / bf16 MFMA operands.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace gla {
+
+struct IntraArgs {
+  int dtype, C, BH, T, dk, N;
+  bool want_A;
+  bool xt_f32;           // write QhT / KhT in fp32 (bf16 inputs only)
+  const void *q, *k, *la;
+  const float* g;        // chunk-local cumsum from the gate kernel, or NULL (computed)
+  void* A;               // [BH][N][C][C]       operand type
+  void *Qh, *QhT, *Kh, *KhT;
+  float* eg;             // [BH][N][dk]
+};
+hipError_t launch_intra(const IntraArgs& a, hipStream_t s);
+
+hipError_t launch_gate_cumsum(int dtype, const void* la, float* g, float* gamma, int BH, int T,
+                              int dk, int C, hipStream_t s);
+hipError_t launch_state_dot(const float* dST, const float* ST, float* cT, int BH, int dk, int dv,
+                            hipStream_t s);
+hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* crossF,
+                            const float* crossR, const float* cT, float* carry, void* dla,
+                            int BH, int T, int dk, int dv, int C, hipStream_t s);
+
+// Inter-chunk state scan.  store: 0 = none, 1 = operand type [dk][dv], 2 = operand type
+// [dv][dk], 3 = fp32 [dk][dv].  With X2T/Y2/cross set, every step also forms the
+// product P_i = X2_i^T Y2_i for the tile and writes the row sums of (held state * P_i)
+// to cross [BH][N][dv/64][dk] (fp32).
+struct ScanArgs {
+  int dtype, C, BH, T, dk, dv, N;
+  bool reverse;
+  bool xt_f32;           // XT / X2T are fp32 (split into two bf16 halves for the MFMA)
+  int store;
+  const void* XT;        // [BH][N][dk][C] (Kh^T forward, Qh^T reverse)
+  const void* Y;         // [BH][T][dv]    input type (v forward, dO reverse)
+  const void* X2T;       // optional second pair for the chunk-total cross term
+  const void* Y2;
+  float* cross;
+  const float* eg;       // [BH][N][dk]
+  const float* S_in;     // [BH][dk][dv] or NULL
+  void* states;          // see store
+  float* S_out;          // [BH][dk][dv] or NULL
+};
+hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s);
+
+struct OutArgs {
+  int dtype, C, BH, T, dk, dv, N;
+  const void *Qh, *A, *STt, *v;
+  void* o;
+};
+hipError_t launch_output(const OutArgs& a, hipStream_t s);
+
+struct FusedArgs {
+  int dtype, C, BH, T, dk, dv, N;
+  const void *Qh, *KhT, *A, *v;
+  const float* eg;
+  const float* S0;
+  void* o;
+  float* S_T;
+};
+hipError_t launch_fwd_fused(const FusedArgs& a, hipStream_t s);
+
+struct BwdArgs {
+  int dtype, C, BH, T, dk, dv, N;
+  const void *q, *k, *v, *dO;
+  const float *g, *gamma;
+  const void *A, *Kh, *S, *dS;
+  void *dq, *dk_out, *dv_out;
+  float* Dloc;
+};
+hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s);
+
+}  // namespace gla

@@ -1,0 +1,212 @@
+// Output kernels of the chunkwise GLA forward (page "Gated Linear Attention Transformers
+// with Hardware-Efficient Training", atlas.scime.ai summary, section Approach).
+//
+//   k_output     materialized states: one workgroup per (batch*head, chunk, 64 values)
+//                computes O_i = Qh_i S_[i] + A_i V_i from the chunk-start state written by
+//                the state scan ([dv][dk] layout, so both MFMA operands are
+//                dk-contiguous) and the intra-chunk matrix A.
+//   k_fwd_fused  non-materialized states: one workgroup per (batch*head, 64 values) keeps
+//                its dk x 64 slice of the state in fp32 accumulators and walks the chunks:
+//                O_i = Qh_i S + A_i V_i, then S <- diag(exp(gamma_i)) S + Kh_i^T V_i.  No
+//                per-chunk state ever reaches memory.  The state accumulators feed the
+//                Qh S product directly as the MFMA B operand (acc-order fragments).
+#include "gla_common.cuh"
+#include "gla_internal.h"
+
+namespace gla {
+
+template <typename Tin, typename OpT, int C>
+__global__ __launch_bounds__(kThreads) void k_output(const OpT* __restrict__ Qh,
+                                                     const OpT* __restrict__ A,
+                                                     const OpT* __restrict__ STt,
+                                                     const Tin* __restrict__ V,
+                                                     Tin* __restrict__ O, int T, int dk, int dv,
+                                                     int N) {
+  constexpr int TV = 64, VLD = C + 8, NM = C / 16;
+  __shared__ __attribute__((aligned(16))) OpT vs[TV * VLD];
+  const int v0 = blockIdx.x * TV, i = blockIdx.y, bh = blockIdx.z;
+  const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
+  const int t0 = i * C, rows = min(C, T - t0);
+
+  stage_cols<OpT, Tin, C, TV>(vs, VLD, V + ((long)bh * T + t0) * dv + v0, dv, rows);
+
+  f32x4 acc[NM];   // acc[m][e] = O[16m + 4qd + e][v0 + 16w + r]
+#pragma unroll
+  for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const OpT* sp = STt + (((long)bh * N + i) * dv + v0 + 16 * w + r) * dk;
+  const OpT* qp = Qh + ((long)bh * N * C + t0) * dk;
+  for (int kb = 0; kb < dk / 32; ++kb) {
+    Frag<OpT> fb;
+    load_frag_c(fb, sp + kb * 32);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      Frag<OpT> fa;
+      load_frag_c(fa, qp + (long)(16 * m + r) * dk + kb * 32);
+      mma(acc[m], fa, fb);
+    }
+  }
+  __syncthreads();
+  const OpT* ap = A + ((long)bh * N + i) * C * C;
+#pragma unroll
+  for (int kb = 0; kb < C / 32; ++kb) {
+    Frag<OpT> fb;
+    load_frag_c(fb, vs + (16 * w + r) * VLD + kb * 32);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if (32 * kb <= 16 * m + 15) {
+        Frag<OpT> fa;
+        load_frag_c(fa, ap + (16 * m + r) * C + kb * 32);
+        mma(acc[m], fa, fb);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * m + 4 * qd + e;
+      if (t < rows) O[((long)bh * T + t0 + t) * dv + v0 + 16 * w + r] = from_f32<Tin>(acc[m][e]);
+    }
+}
+
+template <typename Tin, typename OpT, int C, int DK>
+__global__ __launch_bounds__(kThreads) void k_fwd_fused(
+    const OpT* __restrict__ Qh, const OpT* __restrict__ KhT, const OpT* __restrict__ A,
+    const float* __restrict__ eg, const Tin* __restrict__ V, const float* __restrict__ S0,
+    Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N) {
+  constexpr int TV = 64, VLD = C + 8, NM = C / 16, NP = DK / 16;
+  __shared__ __attribute__((aligned(16))) OpT vs[TV * VLD];
+  const int v0 = blockIdx.x * TV, bh = blockIdx.y;
+  const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
+  const int col = v0 + 16 * w + r;
+
+  f32x4 S[NP];   // S[p][e] = state[16p + 4qd + e][col]
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      S[p][e] = S0 ? S0[((long)bh * DK + 16 * p + 4 * qd + e) * dv + col] : 0.f;
+
+  for (int i = 0; i < N; ++i) {
+    const int t0 = i * C, rows = min(C, T - t0);
+    stage_cols<OpT, Tin, C, TV>(vs, VLD, V + ((long)bh * T + t0) * dv + v0, dv, rows);
+    __syncthreads();
+
+    // O_i = Qh_i S + A_i V_i
+    f32x4 acc[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const OpT* qp = Qh + ((long)bh * N * C + t0) * DK;
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      Frag<OpT> fb;
+      frag_from_acc(fb, S[2 * kb], S[2 * kb + 1]);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        Frag<OpT> fa;
+        load_frag_a(fa, qp + (16 * m + r) * DK + kb * 32);
+        mma(acc[m], fa, fb);
+      }
+    }
+    const OpT* ap = A + ((long)bh * N + i) * C * C;
+#pragma unroll
+    for (int kb = 0; kb < C / 32; ++kb) {
+      Frag<OpT> fb;
+      load_frag_c(fb, vs + (16 * w + r) * VLD + kb * 32);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        if (32 * kb <= 16 * m + 15) {
+          Frag<OpT> fa;
+          load_frag_c(fa, ap + (16 * m + r) * C + kb * 32);
+          mma(acc[m], fa, fb);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * m + 4 * qd + e;
+        if (t < rows) O[((long)bh * T + t0 + t) * dv + col] = from_f32<Tin>(acc[m][e]);
+      }
+
+    // S <- diag(exp(gamma_i)) S + Kh_i^T V_i
+    const float* egp = eg + ((long)bh * N + i) * DK + 4 * qd;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const f32x4 dec = *reinterpret_cast<const f32x4*>(egp + 16 * p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[p][e] *= dec[e];
+    }
+    const OpT* kp = KhT + ((long)bh * N + i) * DK * C;
+#pragma unroll
+    for (int kb = 0; kb < C / 32; ++kb) {
+      Frag<OpT> fb;
+      load_frag_c(fb, vs + (16 * w + r) * VLD + kb * 32);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        Frag<OpT> fa;
+        load_frag_c(fa, kp + (16 * p + r) * C + kb * 32);
+        mma(S[p], fa, fb);
+      }
+    }
+    __syncthreads();
+  }
+  if (S_T) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S_T[((long)bh * DK + 16 * p + 4 * qd + e) * dv + col] = S[p][e];
+  }
+}
+
+// ---------------------------------------------------------------------------------
+template <typename Tin, typename OpT, int C>
+static hipError_t launch_output_t(const OutArgs& a, hipStream_t s) {
+  dim3 grid(a.dv / 64, a.N, a.BH);
+  hipLaunchKernelGGL((k_output<Tin, OpT, C>), grid, dim3(kThreads), 0, s, (const OpT*)a.Qh,
+                     (const OpT*)a.A, (const OpT*)a.STt, (const Tin*)a.v, (Tin*)a.o, a.T, a.dk,
+                     a.dv, a.N);
+  return hipGetLastError();
+}
+
+hipError_t launch_output(const OutArgs& a, hipStream_t s) {
+  if (a.BH == 0 || a.N == 0) return hipSuccess;
+  if (a.dtype == 0) {
+    if (a.C == 64) return launch_output_t<float, float, 64>(a, s);
+    return launch_output_t<float, float, 128>(a, s);
+  }
+  if (a.C == 64) return launch_output_t<bf16, bf16, 64>(a, s);
+  return launch_output_t<bf16, bf16, 128>(a, s);
+}
+
+template <typename Tin, typename OpT, int C, int DK>
+static hipError_t launch_fused_t2(const FusedArgs& a, hipStream_t s) {
+  dim3 grid(a.dv / 64, a.BH);
+  hipLaunchKernelGGL((k_fwd_fused<Tin, OpT, C, DK>), grid, dim3(kThreads), 0, s,
+                     (const OpT*)a.Qh, (const OpT*)a.KhT, (const OpT*)a.A, a.eg,
+                     (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N);
+  return hipGetLastError();
+}
+template <typename Tin, typename OpT, int C>
+static hipError_t launch_fused_t(const FusedArgs& a, hipStream_t s) {
+  switch (a.dk) {
+    case 64: return launch_fused_t2<Tin, OpT, C, 64>(a, s);
+    case 128: return launch_fused_t2<Tin, OpT, C, 128>(a, s);
+    case 192: return launch_fused_t2<Tin, OpT, C, 192>(a, s);
+    default: return launch_fused_t2<Tin, OpT, C, 256>(a, s);
+  }
+}
+
+hipError_t launch_fwd_fused(const FusedArgs& a, hipStream_t s) {
+  if (a.BH == 0 || a.N == 0) return hipSuccess;
+  if (a.dtype == 0) {
+    if (a.C == 64) return launch_fused_t<float, float, 64>(a, s);
+    return launch_fused_t<float, float, 128>(a, s);
+  }
+  if (a.C == 64) return launch_fused_t<bf16, bf16, 64>(a, s);
+  return launch_fused_t<bf16, bf16, 128>(a, s);
+}
+
+}  // namespace gla

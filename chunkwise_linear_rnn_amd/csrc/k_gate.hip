@@ -1,0 +1,127 @@
+// Gate kernels of the chunkwise GLA path (page "Gated Linear Attention Transformers with
+// Hardware-Efficient Training", atlas.scime.ai summary, section Approach):
+//   k_gate_cumsum     chunk-local inclusive cumsum of log_alpha (the first step of the
+//                     chunkwise form) and the chunk totals gamma.
+//   k_state_dot       c_T[d] = sum_v dS_T[d,v] * S_T[d,v], the final-state term of the
+//                     closed-form gate gradient.
+//   k_gate_carry,     the closed-form gate gradient: a reverse cumulative sum over the
+//   k_gate_grad       whole sequence of D = q*dq - k*dk plus c_T, taken in two levels:
+//                     chunk-local suffix sums come from the backward chunk kernel, the
+//                     suffix over later chunks from the chunk totals the state scans form.
+// All three are HBM-bound: coalesced along the contiguous d dimension, no MFMA.
+#include "gla_common.cuh"
+#include "gla_internal.h"
+
+namespace gla {
+
+template <typename Tin>
+__global__ __launch_bounds__(kThreads) void k_gate_cumsum(const Tin* __restrict__ la,
+                                                          float* __restrict__ g,
+                                                          float* __restrict__ gamma, int T,
+                                                          int dk, int C, int N) {
+  const int i = blockIdx.x, bh = blockIdx.y;
+  const int t0 = i * C, t1 = min(T, t0 + C);
+  const long base = (long)bh * T * dk;
+  for (int d = threadIdx.x; d < dk; d += kThreads) {
+    float acc = 0.f;
+    for (int t = t0; t < t1; ++t) {
+      acc += to_f32(la[base + (long)t * dk + d]);
+      if (g) g[base + (long)t * dk + d] = acc;
+    }
+    if (gamma) gamma[((long)bh * N + i) * dk + d] = acc;
+  }
+}
+
+// One wave per state row d; lanes stride over v.
+__global__ __launch_bounds__(kThreads) void k_state_dot(const float* __restrict__ dST,
+                                                        const float* __restrict__ ST,
+                                                        float* __restrict__ cT, int dk,
+                                                        int dv) {
+  const int bh = blockIdx.x, w = wave_id(), l = lane_id();
+  for (int d = w; d < dk; d += kThreads / kWave) {
+    const long row = ((long)bh * dk + d) * dv;
+    float s = 0.f;
+    for (int v = l; v < dv; v += kWave) s += dST[row + v] * ST[row + v];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if (l == 0) cT[(long)bh * dk + d] = s;
+  }
+}
+
+// carry[i][d] = c_T[d] + sum over chunks j > i of the chunk total of D, each chunk total
+// being the sum over the 64-column tiles of (forward cross term - reverse cross term).
+__global__ __launch_bounds__(kThreads) void k_gate_carry(const float* __restrict__ crossF,
+                                                         const float* __restrict__ crossR,
+                                                         const float* __restrict__ cT,
+                                                         float* __restrict__ carry, int dk,
+                                                         int ntile, int N) {
+  const int bh = blockIdx.y;
+  const int d = blockIdx.x * kThreads + threadIdx.x;
+  if (d >= dk) return;
+  float run = cT ? cT[(long)bh * dk + d] : 0.f;
+  for (int j = N - 1; j >= 0; --j) {
+    carry[((long)bh * N + j) * dk + d] = run;
+    const long base = ((long)bh * N + j) * ntile * dk + d;
+    float tot = 0.f;
+    for (int u = 0; u < ntile; ++u) tot += crossF[base + (long)u * dk] - crossR[base + (long)u * dk];
+    run += tot;
+  }
+}
+
+template <typename Tin>
+__global__ __launch_bounds__(kThreads) void k_gate_grad(const float* __restrict__ Dloc,
+                                                        const float* __restrict__ carry,
+                                                        Tin* __restrict__ dla, int T, int dk,
+                                                        int C, int N) {
+  const int i = blockIdx.x, bh = blockIdx.y;
+  const int t0 = i * C, t1 = min(T, t0 + C);
+  const long base = (long)bh * T * dk;
+  for (int d = threadIdx.x; d < dk; d += kThreads) {
+    const float cr = carry[((long)bh * N + i) * dk + d];
+    for (int t = t0; t < t1; ++t)
+      dla[base + (long)t * dk + d] = from_f32<Tin>(Dloc[base + (long)t * dk + d] + cr);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------
+hipError_t launch_gate_cumsum(int dtype, const void* la, float* g, float* gamma, int BH, int T,
+                              int dk, int C, hipStream_t s) {
+  const int N = (T + C - 1) / C;
+  if (BH == 0 || N == 0) return hipSuccess;
+  dim3 grid(N, BH);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_gate_cumsum<float>, grid, dim3(kThreads), 0, s, (const float*)la, g,
+                       gamma, T, dk, C, N);
+  else
+    hipLaunchKernelGGL(k_gate_cumsum<bf16>, grid, dim3(kThreads), 0, s, (const bf16*)la, g,
+                       gamma, T, dk, C, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_dot(const float* dST, const float* ST, float* cT, int BH, int dk, int dv,
+                            hipStream_t s) {
+  if (BH == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_state_dot, dim3(BH), dim3(kThreads), 0, s, dST, ST, cT, dk, dv);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* crossF,
+                            const float* crossR, const float* cT, float* carry, void* dla,
+                            int BH, int T, int dk, int dv, int C, hipStream_t s) {
+  const int N = (T + C - 1) / C;
+  if (BH == 0 || N == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gate_carry, dim3((dk + kThreads - 1) / kThreads, BH), dim3(kThreads), 0, s,
+                     crossF, crossR, cT, carry, dk, dv / 64, N);
+  dim3 grid(N, BH);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_gate_grad<float>, grid, dim3(kThreads), 0, s, Dloc, carry, (float*)dla,
+                       T, dk, C, N);
+  else
+    hipLaunchKernelGGL(k_gate_grad<bf16>, grid, dim3(kThreads), 0, s, Dloc, carry, (bf16*)dla,
+                       T, dk, C, N);
+  return hipGetLastError();
+}
+
+}  // namespace gla

@@ -1,0 +1,278 @@
+// Intra-chunk kernel of the chunkwise GLA path (page "Gated Linear Attention Transformers
+// with Hardware-Efficient Training", atlas.scime.ai summary, section Approach: two-level
+// (secondary) chunking so that most intra-chunk products run on half-precision matrix
+// units).  One workgroup per (batch*head, chunk).
+//
+// It forms the chunk's decayed causal attention matrix
+//     A[t][s] = sum_d q_td k_sd exp(g_td - g_sd),  s <= t  (zero above the diagonal)
+// with g the chunk-local cumsum of log_alpha, split into 16-row sub-chunks:
+//   - a sub-block with t in sub-chunk I and s in an earlier sub-chunk J is the MFMA
+//     product (Q_I * exp(g_I - g_rho)) (K_J * exp(g_rho - g_J))^T, rho = first row of I;
+//     both exponents are <= 0, so the rounded (bf16) operands stay in [0, |x|];
+//   - a diagonal sub-block is summed element by element in fp32 from log-space
+//     differences exp(g_t - g_s), which is in [0,1] for any finite gates.
+// Alongside it emits, for the chunk, the decayed operands the inter-chunk kernels
+// consume (each nullable): Qh = q*exp(g) token-major, its transpose QhT, Kh =
+// k*exp(gamma - g) token-major, its transpose KhT, and exp(gamma).  The transposed
+// operands feed the state scans; they are written either in the MFMA operand type or in
+// fp32 (XT = float), which the backward's scans split into two bf16 halves.
+//
+// g either comes from the gate-cumsum kernel (G_WS) or is computed here from log_alpha
+// by a segmented column scan.  Internally g is held multiplied by log2(e) so every decay
+// is one v_exp_f32.
+#include "gla_common.cuh"
+#include "gla_internal.h"
+
+namespace gla {
+
+// (t, s) of the p-th entry, row-major, of a 16x16 lower triangle with its diagonal.
+__device__ __forceinline__ void tri_decode(int p, int& t, int& s) {
+  int tt = (int)((sqrtf(8.f * (float)p + 1.f) - 1.f) * 0.5f);
+  if ((tt + 1) * (tt + 2) / 2 <= p) ++tt;
+  if (tt * (tt + 1) / 2 > p) --tt;
+  t = tt;
+  s = p - tt * (tt + 1) / 2;
+}
+// (I, J), J < I, of the p-th strictly-lower sub-chunk pair, ordered by I then J.
+__device__ __forceinline__ void pair_decode(int p, int& I, int& J) {
+  int ii = (int)((sqrtf(8.f * (float)p + 1.f) + 1.f) * 0.5f);
+  if (ii * (ii - 1) / 2 > p) --ii;
+  if ((ii + 1) * ii / 2 <= p) ++ii;
+  I = ii;
+  J = p - ii * (ii - 1) / 2;
+}
+
+template <typename Tin, typename OpT, typename XT, int C, bool G_WS, bool WANT_A>
+__global__ __launch_bounds__(kThreads) void k_intra(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ la,
+    const float* __restrict__ gws, OpT* __restrict__ A_out, OpT* __restrict__ Qh_out,
+    XT* __restrict__ QhT_out, OpT* __restrict__ Kh_out, XT* __restrict__ KhT_out,
+    float* __restrict__ eg_out, int T, int dk, int N) {
+  constexpr int DB = 64;                    // dk columns per pass
+  constexpr int NS = C / 16;                // sub-chunks
+  constexpr int NPAIR = NS * (NS - 1) / 2;  // off-diagonal sub-block pairs
+  constexpr int PPW = (NPAIR + 3) / 4;      // pairs per wave
+  constexpr int NITEM = NS * 136 * 4;       // diagonal (pair, 16-column quarter) items
+  constexpr int IPT = (NITEM + kThreads - 1) / kThreads;
+  constexpr int GLD = DB + 4;
+  constexpr int XLD = DB + 8;
+
+  __shared__ float gs[C * GLD];
+  __shared__ __attribute__((aligned(16))) Tin qs[C * XLD];
+  __shared__ __attribute__((aligned(16))) Tin ks[C * XLD];
+  __shared__ float segtot[4 * DB];
+
+  const int i = blockIdx.x, bh = blockIdx.y;
+  const int t0 = i * C, rows = min(C, T - t0);
+  const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
+  const long in_base = ((long)bh * T + t0) * dk;
+
+  f32x4 accp[PPW > 0 ? PPW : 1];
+  float accd[IPT];
+#pragma unroll
+  for (int p = 0; p < (PPW > 0 ? PPW : 1); ++p) accp[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) accd[j] = 0.f;
+
+  for (int d0 = 0; d0 < dk; d0 += DB) {
+    // ---- g block (times log2 e); rows past T continue the last valid row -------------
+    if constexpr (G_WS) {
+      for (int idx = threadIdx.x; idx < C * (DB / 8); idx += kThreads) {
+        const int rr = idx / (DB / 8), c = (idx % (DB / 8)) * 8;
+        float x[8];
+        load8(x, gws + in_base + (long)min(rr, rows - 1) * dk + d0 + c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gs[rr * GLD + c + e] = x[e] * kLog2e;
+      }
+    } else {
+      for (int idx = threadIdx.x; idx < C * (DB / 8); idx += kThreads) {
+        const int rr = idx / (DB / 8), c = (idx % (DB / 8)) * 8;
+        float x[8];
+        if (rr < rows) load8(x, la + in_base + (long)rr * dk + d0 + c); else zero8(x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gs[rr * GLD + c + e] = x[e] * kLog2e;
+      }
+      __syncthreads();
+      {
+        constexpr int L = C / 4;
+        const int col = threadIdx.x % DB, seg = threadIdx.x / DB;
+        float run = 0.f;
+        for (int rr = seg * L; rr < seg * L + L; ++rr) {
+          run += gs[rr * GLD + col];
+          gs[rr * GLD + col] = run;
+        }
+        segtot[seg * DB + col] = run;
+        __syncthreads();
+        float off = 0.f;
+        for (int s2 = 0; s2 < seg; ++s2) off += segtot[s2 * DB + col];
+        if (seg > 0)
+          for (int rr = seg * L; rr < seg * L + L; ++rr) gs[rr * GLD + col] += off;
+      }
+    }
+    stage_rows<Tin, Tin, C, DB>(qs, XLD, q + in_base + d0, dk, rows);
+    stage_rows<Tin, Tin, C, DB>(ks, XLD, k + in_base + d0, dk, rows);
+    __syncthreads();
+
+    // ---- decayed operands for the inter-chunk kernels ---------------------------------
+    const float* glast = gs + (C - 1) * GLD;   // gamma * log2 e
+    if (eg_out && threadIdx.x < DB)
+      eg_out[((long)bh * N + i) * dk + d0 + threadIdx.x] = __builtin_amdgcn_exp2f(glast[threadIdx.x]);
+    if (Qh_out || Kh_out) {
+      for (int idx = threadIdx.x; idx < C * (DB / 8); idx += kThreads) {
+        const int rr = idx / (DB / 8), c = (idx % (DB / 8)) * 8;
+        const long o = ((long)bh * N * C + t0 + rr) * dk + d0 + c;
+        float x[8];
+        if (Qh_out) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            x[e] = to_f32(qs[rr * XLD + c + e]) * __builtin_amdgcn_exp2f(gs[rr * GLD + c + e]);
+          store8(Qh_out + o, x);
+        }
+        if (Kh_out) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            x[e] = to_f32(ks[rr * XLD + c + e]) *
+                   __builtin_amdgcn_exp2f(glast[c + e] - gs[rr * GLD + c + e]);
+          store8(Kh_out + o, x);
+        }
+      }
+    }
+    if (QhT_out || KhT_out) {
+      for (int idx = threadIdx.x; idx < DB * (C / 8); idx += kThreads) {
+        const int c = idx / (C / 8), r8 = (idx % (C / 8)) * 8;
+        const long o = (((long)bh * N + i) * dk + d0 + c) * C + r8;
+        float x[8];
+        if (QhT_out) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            x[e] = to_f32(qs[(r8 + e) * XLD + c]) * __builtin_amdgcn_exp2f(gs[(r8 + e) * GLD + c]);
+          store8(QhT_out + o, x);
+        }
+        if (KhT_out) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            x[e] = to_f32(ks[(r8 + e) * XLD + c]) *
+                   __builtin_amdgcn_exp2f(glast[c] - gs[(r8 + e) * GLD + c]);
+          store8(KhT_out + o, x);
+        }
+      }
+    }
+
+    if constexpr (WANT_A) {
+      // ---- off-diagonal sub-blocks: MFMA on rebased operands ----------------------------
+#pragma unroll
+      for (int pi = 0; pi < PPW; ++pi) {
+        const int p = w + 4 * pi;
+        if (p < NPAIR) {
+          int I, J;
+          pair_decode(p, I, J);
+          const int rho = 16 * I, tq = 16 * I + r, sk = 16 * J + r;
+#pragma unroll
+          for (int kb = 0; kb < DB / 32; ++kb) {
+            const int c0 = kb * 32 + 8 * qd;
+            Frag<OpT> fa, fb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float gr = gs[rho * GLD + c0 + e];
+              fa.set(e, to_f32(qs[tq * XLD + c0 + e]) *
+                            __builtin_amdgcn_exp2f(gs[tq * GLD + c0 + e] - gr));
+              fb.set(e, to_f32(ks[sk * XLD + c0 + e]) *
+                            __builtin_amdgcn_exp2f(gr - gs[sk * GLD + c0 + e]));
+            }
+            mma(accp[pi], fa, fb);
+          }
+        }
+      }
+      // ---- diagonal sub-blocks: fp32, log-space ---------------------------------------
+#pragma unroll
+      for (int j = 0; j < IPT; ++j) {
+        const int item = threadIdx.x + kThreads * j;
+        if (item < NITEM) {
+          const int quarter = item & 3, pr = item >> 2;
+          const int I = pr / 136;
+          int tt, ss;
+          tri_decode(pr % 136, tt, ss);
+          const int t = 16 * I + tt, s = 16 * I + ss, cb = quarter * 16;
+          float acc = 0.f;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float xq[8], xk[8];
+            load8(xq, qs + t * XLD + cb + 8 * h);
+            load8(xk, ks + s * XLD + cb + 8 * h);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int c = cb + 8 * h + e;
+              acc += xq[e] * xk[e] * __builtin_amdgcn_exp2f(gs[t * GLD + c] - gs[s * GLD + c]);
+            }
+          }
+          accd[j] += acc;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if constexpr (WANT_A) {
+    OpT* Ab = A_out + ((long)bh * N + i) * C * C;
+#pragma unroll
+    for (int pi = 0; pi < PPW; ++pi) {
+      const int p = w + 4 * pi;
+      if (p < NPAIR) {
+        int I, J;
+        pair_decode(p, I, J);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          Ab[(16 * I + 4 * qd + e) * C + 16 * J + r] = from_f32<OpT>(accp[pi][e]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      float v = accd[j];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      const int item = threadIdx.x + kThreads * j;
+      if (item < NITEM && (item & 3) == 0) {
+        const int pr = item >> 2, I = pr / 136;
+        int tt, ss;
+        tri_decode(pr % 136, tt, ss);
+        Ab[(16 * I + tt) * C + 16 * I + ss] = from_f32<OpT>(v);
+      }
+    }
+    for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
+      const int t = idx / C, s = idx % C;
+      if (s > t) Ab[idx] = from_f32<OpT>(0.f);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+template <typename Tin, typename OpT, typename XT, int C, bool GW, bool WA>
+static void launch_intra_k(const IntraArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((k_intra<Tin, OpT, XT, C, GW, WA>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
+                     (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.la, a.g, (OpT*)a.A,
+                     (OpT*)a.Qh, (XT*)a.QhT, (OpT*)a.Kh, (XT*)a.KhT, a.eg, a.T, a.dk, a.N);
+}
+template <typename Tin, typename OpT, typename XT, int C>
+static hipError_t launch_intra_t(const IntraArgs& a, hipStream_t s) {
+  if (a.want_A) {
+    if (a.g) launch_intra_k<Tin, OpT, XT, C, true, true>(a, s);
+    else launch_intra_k<Tin, OpT, XT, C, false, true>(a, s);
+  } else {
+    if (a.g) launch_intra_k<Tin, OpT, XT, C, true, false>(a, s);
+    else launch_intra_k<Tin, OpT, XT, C, false, false>(a, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_intra(const IntraArgs& a, hipStream_t s) {
+  if (a.BH == 0 || a.N == 0) return hipSuccess;
+  if (a.dtype == 0) return launch_intra_t<float, float, float, 64>(a, s);
+  if (a.xt_f32) {
+    if (a.C == 64) return launch_intra_t<bf16, bf16, float, 64>(a, s);
+    return launch_intra_t<bf16, bf16, float, 128>(a, s);
+  }
+  if (a.C == 64) return launch_intra_t<bf16, bf16, bf16, 64>(a, s);
+  return launch_intra_t<bf16, bf16, bf16, 128>(a, s);
+}
+
+}  // namespace gla

@@ -1,0 +1,204 @@
+// Inter-chunk state scan of the chunkwise GLA path with materialized states (page "Gated
+// Linear Attention Transformers with Hardware-Efficient Training", atlas.scime.ai
+// summary, section Approach: materialized inter-chunk states).
+//
+// One workgroup owns a 64 x 64 fp32 tile (dk rows x dv columns) of one (batch, head)
+// state and walks the chunks in order (forward) or in reverse (the state gradient):
+//     forward:  S_[i+1]  = diag(exp(gamma_i)) S_[i]    + Kh_i^T V_i,   Kh = k*exp(gamma-g)
+//     reverse:  dS_[i]   = diag(exp(gamma_i)) dS_[i+1] + Qh_i^T dO_i,  Qh = q*exp(g)
+// Before each chunk the tile is written out (the chunk-start state S_[i], or dS_[i+1]).
+// The product is a k32 MFMA over the chunk's tokens: the transposed decayed operand
+// comes ready-made from the intra-chunk kernel, the value-side tile is staged into LDS
+// transposed so both operands are token-contiguous.  The tile stays in fp32 accumulators
+// across the whole sequence.  When the transposed operand arrives in fp32 and the MFMA
+// runs in bf16, it is split into a bf16 high part and a bf16 remainder (two MFMAs), so
+// the state carries no operand rounding; the kernel is bound by the state writes, not by
+// the matrix units.
+//
+// Chunk totals of the closed-form gate gradient (optional cross term): summed over one
+// chunk, the intra-chunk parts of q*dq - k*dk cancel pairwise, so the chunk total is
+//     sum_t (q*dq_inter - k*dk_inter) = rowsum(S_[i] * (Qh_i^T dO_i))
+//                                     - rowsum(dS_[i+1] * (Kh_i^T V_i)).
+// The forward scan forms the first term and the reverse scan the second, each from the
+// fp32 state it holds, for its 64 columns; the gate-gradient kernel adds the tiles.
+#include <type_traits>
+
+#include "gla_common.cuh"
+#include "gla_internal.h"
+
+namespace gla {
+
+// Operand fragment of the transposed decayed operand: one MFMA operand, or (fp32 source,
+// bf16 MFMA) a high part plus remainder.
+template <typename OpT, typename XTy>
+struct XFrag {
+  static constexpr bool kSplit = std::is_same<XTy, float>::value && std::is_same<OpT, bf16>::value;
+  Frag<OpT> hi, lo;
+  __device__ __forceinline__ void load(const XTy* p) {
+    if constexpr (kSplit) {
+      float x[8];
+      load8(x, p + 8 * (lane_id() >> 4));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hi.set(e, x[e]);
+        lo.set(e, x[e] - hi.get(e));
+      }
+    } else {
+      load_frag_c(hi, p);
+    }
+  }
+  __device__ __forceinline__ void apply(f32x4& acc, const Frag<OpT>& b) const {
+    mma(acc, hi, b);
+    if constexpr (kSplit) mma(acc, lo, b);
+  }
+};
+
+template <typename Tin, typename OpT, typename XTy, int C, int STORE, bool CROSS>
+__global__ __launch_bounds__(kThreads) void k_state_scan(
+    const XTy* __restrict__ XT, const Tin* __restrict__ Y, const XTy* __restrict__ X2T,
+    const Tin* __restrict__ Y2, float* __restrict__ cross, const float* __restrict__ eg,
+    const float* __restrict__ S_in, void* __restrict__ states, float* __restrict__ S_out,
+    int T, int dk, int dv, int N, int reverse) {
+  constexpr int TV = 64, YLD = C + 8;
+  __shared__ __attribute__((aligned(16))) OpT ys[TV * YLD];
+  __shared__ __attribute__((aligned(16))) OpT y2s[CROSS ? TV * YLD : 8];
+  const int v0 = blockIdx.x * TV, k0 = blockIdx.y * 64, bh = blockIdx.z;
+  const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
+  const int row0 = k0 + 16 * w + 4 * qd;   // accumulator rows row0 .. row0+3
+
+  f32x4 acc[4];   // acc[j][e] = S[row0 + e][v0 + 16 j + r]
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc[j][e] = S_in ? S_in[((long)bh * dk + row0 + e) * dv + v0 + 16 * j + r] : 0.f;
+
+  for (int step = 0; step < N; ++step) {
+    const int i = reverse ? N - 1 - step : step;
+    if constexpr (STORE != 0) {
+      const long sb = ((long)bh * N + i) * dk * dv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = v0 + 16 * j + r;
+        if constexpr (STORE == 1) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            ((OpT*)states)[sb + (long)(row0 + e) * dv + col] = from_f32<OpT>(acc[j][e]);
+        } else if constexpr (STORE == 3) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ((float*)states)[sb + (long)(row0 + e) * dv + col] = acc[j][e];
+        } else {
+          OpT* p = (OpT*)states + sb + (long)col * dk + row0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[e] = from_f32<OpT>(acc[j][e]);
+        }
+      }
+    }
+    const int t0 = i * C, rows = min(C, T - t0);
+    stage_cols<OpT, Tin, C, TV>(ys, YLD, Y + ((long)bh * T + t0) * dv + v0, dv, rows);
+    if constexpr (CROSS)
+      stage_cols<OpT, Tin, C, TV>(y2s, YLD, Y2 + ((long)bh * T + t0) * dv + v0, dv, rows);
+    __syncthreads();
+
+    if constexpr (CROSS) {
+      f32x4 P[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) P[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const XTy* x2p = X2T + (((long)bh * N + i) * dk + k0 + 16 * w + r) * C;
+#pragma unroll
+      for (int kb = 0; kb < C / 32; ++kb) {
+        XFrag<OpT, XTy> fa;
+        fa.load(x2p + kb * 32);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          Frag<OpT> fb;
+          load_frag_c(fb, y2s + (16 * j + r) * YLD + kb * 32);
+          fa.apply(P[j], fb);
+        }
+      }
+      float part[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s += acc[j][e] * P[j][e];
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 8);
+        part[e] = s;
+      }
+      if (r == 0) {
+        f32x4 o = {part[0], part[1], part[2], part[3]};
+        *reinterpret_cast<f32x4*>(cross + (((long)bh * N + i) * gridDim.x + blockIdx.x) * dk +
+                                  row0) = o;
+      }
+    }
+
+    const f32x4 dec = *reinterpret_cast<const f32x4*>(eg + ((long)bh * N + i) * dk + row0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[j][e] *= dec[e];
+
+    const XTy* xp = XT + (((long)bh * N + i) * dk + k0 + 16 * w + r) * C;
+#pragma unroll
+    for (int kb = 0; kb < C / 32; ++kb) {
+      XFrag<OpT, XTy> fa;
+      fa.load(xp + kb * 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        Frag<OpT> fb;
+        load_frag_c(fb, ys + (16 * j + r) * YLD + kb * 32);
+        fa.apply(acc[j], fb);
+      }
+    }
+    __syncthreads();
+  }
+  if (S_out) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        S_out[((long)bh * dk + row0 + e) * dv + v0 + 16 * j + r] = acc[j][e];
+  }
+}
+
+template <typename Tin, typename OpT, typename XTy, int C, int STORE, bool CROSS>
+static void launch_scan_k(const ScanArgs& a, hipStream_t s) {
+  dim3 grid(a.dv / 64, a.dk / 64, a.BH);
+  hipLaunchKernelGGL((k_state_scan<Tin, OpT, XTy, C, STORE, CROSS>), grid, dim3(kThreads), 0, s,
+                     (const XTy*)a.XT, (const Tin*)a.Y, (const XTy*)a.X2T, (const Tin*)a.Y2,
+                     a.cross, a.eg, a.S_in, a.states, a.S_out, a.T, a.dk, a.dv, a.N,
+                     a.reverse ? 1 : 0);
+}
+
+template <typename Tin, typename OpT, typename XTy, int C>
+static hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
+  if (a.cross) {
+    // the backward: operand-type states, [dk][dv]
+    launch_scan_k<Tin, OpT, XTy, C, 1, true>(a, s);
+  } else {
+    switch (a.store) {
+      case 0: launch_scan_k<Tin, OpT, XTy, C, 0, false>(a, s); break;
+      case 1: launch_scan_k<Tin, OpT, XTy, C, 1, false>(a, s); break;
+      case 2: launch_scan_k<Tin, OpT, XTy, C, 2, false>(a, s); break;
+      default: launch_scan_k<Tin, OpT, XTy, C, 3, false>(a, s); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s) {
+  if (a.BH == 0 || a.N == 0) return hipSuccess;
+  if (a.cross && a.store != 1) return hipErrorInvalidValue;
+  if (a.dtype == 0) return launch_scan_t<float, float, float, 64>(a, s);
+  if (a.xt_f32) {
+    if (a.C == 64) return launch_scan_t<bf16, bf16, float, 64>(a, s);
+    return launch_scan_t<bf16, bf16, float, 128>(a, s);
+  }
+  if (a.C == 64) return launch_scan_t<bf16, bf16, bf16, 64>(a, s);
+  return launch_scan_t<bf16, bf16, bf16, 128>(a, s);
+}
+
+}  // namespace gla

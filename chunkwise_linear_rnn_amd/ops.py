@@ -1,0 +1,170 @@
+"""Tensor-level wrappers over the C ABI.  Argument marshalling only: shapes and dtypes
+are checked, outputs and the workspace are allocated with torch on the inputs' device,
+and raw pointers plus torch's current HIP stream go to libgla_mi355x.so."""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._native import (BF16, F32, MATERIALIZED, RECOMPUTE, PASS_BWD, PASS_FWD, PASS_STATES,
+                      GlaError, lib, make_desc, workspace_bytes)
+
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+_MODES = {"materialized": MATERIALIZED, "recompute": RECOMPUTE}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor on {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _desc_from(q, v, chunk, subchunk, state_mode):
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be [B, H, T, d]")
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    mode = _MODES[state_mode] if isinstance(state_mode, str) else int(state_mode)
+    return make_desc(B, H, T, dk, dv, chunk, subchunk, _DT[q.dtype], mode)
+
+
+def _workspace(desc, pass_, device, workspace):
+    need = workspace_bytes(desc, pass_)
+    if workspace is not None:
+        if workspace.device != device or workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace must hold at least {need} bytes on {device}")
+        return workspace, need
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=device), need
+
+
+def _call(name, st):
+    if st != 0:
+        raise GlaError(st, name)
+
+
+def fwd(q, k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, state_mode="recompute",
+        final_state=True, workspace=None):
+    """o, S_T = the GLA layer forward (S_T is None when final_state is False)."""
+    desc = _desc_from(q, v, chunk, subchunk, state_mode)
+    dev, dt = q.device, q.dtype
+    B, H, T, dk, dv = desc.B, desc.H, desc.T, desc.dk, desc.dv
+    for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)),
+                      (v, "v", (B, H, T, dv)), (log_alpha, "log_alpha", (B, H, T, dk))):
+        _check(t, n, shp, dt, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if final_state else None
+    ws, need = _workspace(desc, PASS_FWD, dev, workspace)
+    _call("gla_chunk_fwd", lib().gla_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(log_alpha), _ptr(S0), _ptr(o), _ptr(S_T),
+                                               _ptr(ws), need, _stream(dev)))
+    return o, S_T
+
+
+def bwd(q, k, v, log_alpha, dO, S0=None, dS_T=None, *, chunk=64, subchunk=16,
+        want_dS0=True, workspace=None):
+    """dq, dk, dv, dlog_alpha, dS0 for the loss gradient (dO, dS_T)."""
+    desc = _desc_from(q, v, chunk, subchunk, RECOMPUTE)
+    dev, dt = q.device, q.dtype
+    B, H, T, dk, dv = desc.B, desc.H, desc.T, desc.dk, desc.dv
+    for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)),
+                      (v, "v", (B, H, T, dv)), (log_alpha, "log_alpha", (B, H, T, dk)),
+                      (dO, "dO", (B, H, T, dv))):
+        _check(t, n, shp, dt, dev)
+    for t, n in ((S0, "S0"), (dS_T, "dS_T")):
+        if t is not None:
+            _check(t, n, (B, H, dk, dv), torch.float32, dev)
+    dq = torch.empty_like(q)
+    dk_ = torch.empty_like(k)
+    dv_ = torch.empty_like(v)
+    dla = torch.empty_like(log_alpha)
+    dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None
+    ws, need = _workspace(desc, PASS_BWD, dev, workspace)
+    _call("gla_chunk_bwd", lib().gla_chunk_bwd(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(S0), _ptr(dO),
+        _ptr(dS_T), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(dS0), _ptr(ws), need,
+        _stream(dev)))
+    return dq, dk_, dv_, dla, dS0
+
+
+def gate_cumsum(log_alpha, chunk=64):
+    """g (chunk-local inclusive cumsum, fp32) and gamma (chunk totals, fp32)."""
+    if log_alpha.dim() != 4 or log_alpha.dtype not in _DT:
+        raise ValueError("log_alpha must be [B,H,T,dk] float32/bfloat16")
+    B, H, T, dk = log_alpha.shape
+    desc = make_desc(B, H, T, dk, 64, chunk, 16, _DT[log_alpha.dtype], RECOMPUTE)
+    _check(log_alpha, "log_alpha", (B, H, T, dk), log_alpha.dtype, log_alpha.device)
+    N = (T + chunk - 1) // chunk
+    g = torch.empty((B, H, T, dk), dtype=torch.float32, device=log_alpha.device)
+    gamma = torch.empty((B, H, N, dk), dtype=torch.float32, device=log_alpha.device)
+    _call("gla_gate_cumsum", lib().gla_gate_cumsum(ctypes.byref(desc), _ptr(log_alpha), _ptr(g),
+                                                   _ptr(gamma), _stream(log_alpha.device)))
+    return g, gamma
+
+
+def chunk_states(k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, workspace=None):
+    """states [B,H,N,dk,dv] (state before every chunk, fp32) and S_T."""
+    desc = _desc_from(k, v, chunk, subchunk, MATERIALIZED)
+    dev, dt = k.device, k.dtype
+    B, H, T, dk, dv = desc.B, desc.H, desc.T, desc.dk, desc.dv
+    for t, n, shp in ((k, "k", (B, H, T, dk)), (v, "v", (B, H, T, dv)),
+                      (log_alpha, "log_alpha", (B, H, T, dk))):
+        _check(t, n, shp, dt, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    N = (T + chunk - 1) // chunk
+    states = torch.empty((B, H, N, dk, dv), dtype=torch.float32, device=dev)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    ws, need = _workspace(desc, PASS_STATES, dev, workspace)
+    _call("gla_chunk_states", lib().gla_chunk_states(
+        ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(S0), _ptr(states), _ptr(S_T),
+        _ptr(ws), need, _stream(dev)))
+    return states, S_T
+
+
+class GLAFunction(torch.autograd.Function):
+    """Autograd wrapper: forward runs gla_chunk_fwd, backward gla_chunk_bwd (which
+    recomputes the chunk states from the saved inputs)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, log_alpha, S0, chunk, subchunk, state_mode):
+        o, S_T = fwd(q, k, v, log_alpha, S0, chunk=chunk, subchunk=subchunk,
+                     state_mode=state_mode)
+        ctx.save_for_backward(q, k, v, log_alpha, S0)
+        ctx.cfg = (chunk, subchunk)
+        return o, S_T
+
+    @staticmethod
+    def backward(ctx, dO, dS_T):
+        q, k, v, log_alpha, S0 = ctx.saved_tensors
+        chunk, subchunk = ctx.cfg
+        dO = dO.contiguous() if dO is not None else torch.zeros_like(
+            q.new_empty(q.shape[:-1] + (v.shape[-1],)))
+        dS_T = dS_T.contiguous() if dS_T is not None else None
+        dq, dk, dv, dla, dS0 = bwd(q, k, v, log_alpha, dO, S0, dS_T, chunk=chunk,
+                                   subchunk=subchunk, want_dS0=S0 is not None)
+        return dq, dk, dv, dla, dS0, None, None, None
+
+
+def gla(q, k, v, log_alpha, S0=None, chunk=64, subchunk=16, state_mode="recompute"):
+    """Differentiable GLA layer: returns (o, S_T)."""
+    return GLAFunction.apply(q, k, v, log_alpha, S0, chunk, subchunk, state_mode)

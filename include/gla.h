@@ -1,0 +1,136 @@
+/*
+ * gla.h -- C ABI of the MI355X (gfx950) chunkwise gated-linear-attention library
+ *          (libgla_mi355x.so).
+ *
+ * The operation (page "Gated Linear Attention Transformers with Hardware-Efficient
+ * Training", atlas.scime.ai summary, section Approach): a linear-attention recurrent
+ * state with the data-dependent low-rank gate G_t = alpha_t^T 1, evaluated with the
+ * pages' I/O-aware chunkwise algorithm.  Per batch b and head h:
+ *
+ *     S_t = diag(alpha_t) S_{t-1} + k_t^T v_t,     o_t = q_t S_t,     S_{-1} = S0,
+ *     alpha_t = exp(log_alpha_t)  (0 < alpha <= 1, i.e. log_alpha <= 0),
+ *
+ * with S a dk x dv matrix.  The backward returns the gradient of a loss L through its
+ * incoming gradients dO = dL/do and dS_T = dL/dS_T; the gate gradient uses the pages'
+ * closed form (Approach: no per-step states are needed), the reverse cumulative sum
+ * over time of q*dq - k*dk plus rowsum(dS_T * S_T).
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are dense, row-major, contiguous device buffers:
+ *      q, k, log_alpha, dq, dk, dlog_alpha  [B, H, T, dk]
+ *      v, o, dO, dv                          [B, H, T, dv]
+ *      S0, S_T, dS_T, dS0                    [B, H, dk, dv]   always float32
+ *    The element type of the [B,H,T,*] tensors is desc->dtype (GLA_F32 or GLA_BF16).
+ *    Base pointers must be 16-byte aligned.
+ *  - The caller owns every buffer.  The library never allocates device memory: scratch
+ *    space comes from the caller's workspace `ws` of at least gla_workspace_bytes()
+ *    bytes (16-byte aligned; its contents on entry do not matter).
+ *  - Outputs are overwritten, never accumulated, and must not alias any input.
+ *  - Calls enqueue kernels on `stream` (a hipStream_t; NULL is the default stream) and
+ *    return before they finish.  The library keeps no global mutable state, so calls
+ *    are reentrant; two calls that share a workspace must be ordered on one stream.
+ *  - Nullable pointers (marked) mean "zero" for inputs and "not wanted" for outputs.
+ *  - Errors are reported by status code; no C++ exception crosses this boundary.  All
+ *    argument checks run on the host before any launch, and on an error no output is
+ *    touched.  Kernel-launch failures surface as GLA_ERR_DEVICE.
+ *  - Preconditions that are not checked: log_alpha finite and <= 0 (a value > 0 or a
+ *    non-finite value gives unspecified output), inputs finite.
+ */
+#ifndef GLA_MI355X_H
+#define GLA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GLA_OK = 0,
+  GLA_ERR_INVALID_ARG = 1,   /* NULL required pointer, negative size, bad enum, ...   */
+  GLA_ERR_UNSUPPORTED = 2,   /* valid request outside what the kernels implement      */
+  GLA_ERR_WORKSPACE = 3,     /* workspace NULL or smaller than gla_workspace_bytes()  */
+  GLA_ERR_DEVICE = 4         /* a HIP call or kernel launch failed                    */
+} gla_status_t;
+
+typedef enum { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype_t;
+
+/* How inter-chunk states are handled in the forward (Approach section: materialized or
+ * non-materialized inter-chunk states).
+ *  GLA_STATES_MATERIALIZED: every chunk-start state S_[i] is written to the workspace
+ *    by the state-scan kernel, then a chunk-parallel kernel forms the outputs.
+ *  GLA_STATES_RECOMPUTE: the state stays on chip; one kernel walks the chunks of a
+ *    (batch, head, dv-slice) and emits the outputs directly (no per-chunk state tensor
+ *    in memory).
+ * The backward always recomputes the chunk-start states from the inputs (the API is
+ * stateless); the mode only changes the forward. */
+typedef enum { GLA_STATES_MATERIALIZED = 0, GLA_STATES_RECOMPUTE = 1 } gla_state_mode_t;
+
+typedef enum { GLA_PASS_FWD = 0, GLA_PASS_BWD = 1 } gla_pass_t;
+
+typedef struct {
+  int32_t B, H, T;     /* batch, heads, sequence length (any of them may be 0)          */
+  int32_t dk, dv;      /* key and value head dimensions                                  */
+  int32_t chunk;       /* chunk size C of the chunkwise form                             */
+  int32_t subchunk;    /* secondary (sub-)chunk size c of the intra-chunk part           */
+  int32_t dtype;       /* gla_dtype_t                                                    */
+  int32_t state_mode;  /* gla_state_mode_t                                               */
+} gla_desc_t;
+
+/* Supported by this build (else GLA_ERR_UNSUPPORTED):
+ *   chunk in {64, 128}; subchunk == 16; dk in {64, 128, 192, 256};
+ *   dv a multiple of 64 up to 1024; fp32 only with chunk 64; B*H <= 65535;
+ *   B*H*T < 2^31; ceil(T/chunk) <= 65535; any T >= 0 (a ragged last chunk is masked). */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* gla_status_string(gla_status_t status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int32_t gla_version(void);
+
+/* Host-only validation of a descriptor for a pass (no device call).  Returns GLA_OK,
+ * GLA_ERR_INVALID_ARG (desc NULL, a negative size, chunk or subchunk < 1,
+ * chunk % subchunk != 0, unknown dtype/mode/pass) or GLA_ERR_UNSUPPORTED. */
+gla_status_t gla_validate(const gla_desc_t* desc, int32_t pass);
+
+/* Workspace bytes needed by gla_chunk_fwd (pass = GLA_PASS_FWD), gla_chunk_bwd
+ * (GLA_PASS_BWD) or gla_chunk_states (pass = 2) for `desc`; writes them to *bytes.
+ * Host-only; same errors as gla_validate, plus GLA_ERR_INVALID_ARG for bytes == NULL. */
+gla_status_t gla_workspace_bytes(const gla_desc_t* desc, int32_t pass, size_t* bytes);
+
+/* Gate log-cumsum (the first step of the chunkwise form, Approach section):
+ *   g[b,h,t,:] = sum of log_alpha[b,h,u,:] over u from the start of t's chunk to t,
+ *   gamma[b,h,i,:] = g at the last row of chunk i (a ragged last chunk ends at T-1).
+ * g: float32 [B,H,T,dk]; gamma: float32 [B,H,ceil(T/chunk),dk]. */
+gla_status_t gla_gate_cumsum(const gla_desc_t* desc, const void* log_alpha,
+                             float* g, float* gamma, void* stream);
+
+/* Inter-chunk state recurrence with materialized states (Approach section):
+ *   S_[0] = S0,  S_[i+1] = diag(exp(gamma_i)) S_[i] + (K_i * exp(gamma_i - g_i))^T V_i,
+ * writes states[b,h,i,:,:] = S_[i] for i < N = ceil(T/chunk) (float32
+ * [B,H,N,dk,dv]) and S_T = S_[N] (nullable).  S0 nullable (zero). */
+gla_status_t gla_chunk_states(const gla_desc_t* desc, const void* k, const void* v,
+                              const void* log_alpha, const float* S0, float* states,
+                              float* S_T, void* ws, size_t ws_bytes, void* stream);
+
+/* Forward of the layer.  Inputs q, k, v, log_alpha, S0 (nullable: zero).
+ * Outputs o (required) and S_T (nullable). */
+gla_status_t gla_chunk_fwd(const gla_desc_t* desc, const void* q, const void* k,
+                           const void* v, const void* log_alpha, const float* S0,
+                           void* o, float* S_T, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the layer for the loss gradient (dO, dS_T).  Inputs q, k, v, log_alpha,
+ * S0 (nullable), dO (required), dS_T (nullable: zero).  Outputs dq, dk, dv,
+ * dlog_alpha (required) and dS0 (nullable). */
+gla_status_t gla_chunk_bwd(const gla_desc_t* desc, const void* q, const void* k,
+                           const void* v, const void* log_alpha, const float* S0,
+                           const void* dO, const float* dS_T, void* dq, void* dk,
+                           void* dv, void* dlog_alpha, float* dS0, void* ws,
+                           size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_MI355X_H */

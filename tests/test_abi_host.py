@@ -1,0 +1,104 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports every
+function include/gla.h declares, and its argument validation / workspace planning
+behave as documented."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def native():
+    import chunkwise_linear_rnn_amd._native as nat
+    if not os.path.exists(nat.lib_path()):
+        from chunkwise_linear_rnn_amd.build import build
+        build(verbose=False)
+    nat.lib()
+    return nat
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "gla.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gla_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(native):
+    names = _header_functions()
+    assert "gla_chunk_fwd" in names and "gla_chunk_bwd" in names
+    h = native.lib()
+    for n in names:
+        assert hasattr(h, n), n
+    assert set(names) == set(native.SIGNATURES)
+
+
+def test_status_strings_and_version(native):
+    assert native.status_string(0) == "GLA_OK"
+    assert native.status_string(3) == "GLA_ERR_WORKSPACE"
+    assert native.status_string(99) == "GLA_ERR_UNKNOWN"
+    assert native.version() >= 100
+
+
+def test_validation_codes(native):
+    D = native.make_desc
+    ok = D(2, 4, 2048, 256, 512, 64, 16, native.BF16, native.RECOMPUTE)
+    assert native.validate(ok, native.PASS_FWD) == 0
+    assert native.validate(ok, native.PASS_BWD) == 0
+    assert native.lib().gla_validate(None, 0) == 1
+    assert native.validate(ok, 7) == 1
+    cases_invalid = [D(-1, 1, 8, 64, 64), D(1, 1, 8, 64, 64, 0), D(1, 1, 8, 64, 64, 64, 0),
+                     D(1, 1, 8, 64, 64, 64, 24), D(1, 1, 8, 64, 64, 64, 16, 5),
+                     D(1, 1, 8, 64, 64, 64, 16, 1, 9)]
+    for d in cases_invalid:
+        assert native.validate(d) == 1, d
+    cases_unsup = [D(1, 1, 8, 64, 64, 32, 16), D(1, 1, 8, 64, 64, 64, 32), D(1, 1, 8, 96, 64),
+                   D(1, 1, 8, 320, 64), D(1, 1, 8, 64, 96), D(1, 1, 8, 64, 2048),
+                   D(1, 1, 8, 64, 64, 128, 16, native.F32), D(70000, 1, 8, 64, 64)]
+    for d in cases_unsup:
+        assert native.validate(d) == 2, d
+    # empty problems are valid
+    assert native.validate(D(0, 4, 100, 64, 64)) == 0
+    assert native.validate(D(1, 1, 0, 64, 64)) == 0
+
+
+def test_workspace_planning(native):
+    D = native.make_desc
+    d = D(4, 4, 2048, 256, 512, 64, 16, native.BF16, native.RECOMPUTE)
+    rec = native.workspace_bytes(d, native.PASS_FWD)
+    d.state_mode = native.MATERIALIZED
+    mat = native.workspace_bytes(d, native.PASS_FWD)
+    bwd = native.workspace_bytes(d, native.PASS_BWD)
+    # materialized keeps every chunk state: B*H*N*dk*dv bf16 = 128 MiB at this shape
+    assert mat - rec >= 4 * 4 * 32 * 256 * 512 * 2
+    assert bwd > mat
+    assert native.workspace_bytes(d, native.PASS_STATES) > 0
+    assert native.workspace_bytes(D(0, 4, 100, 64, 64), native.PASS_BWD) == 0
+    with pytest.raises(native.GlaError):
+        native.workspace_bytes(D(1, 1, 8, 64, 96), native.PASS_FWD)
+    out = ctypes.c_size_t(0)
+    assert native.lib().gla_workspace_bytes(ctypes.byref(d), 0, None) == 1
+    assert native.lib().gla_workspace_bytes(ctypes.byref(d), 0, ctypes.byref(out)) == 0
+
+
+def test_errors_before_any_launch(native):
+    """Invalid calls return their code on the host without touching a device."""
+    L = native.lib()
+    D = native.make_desc
+    bad = D(1, 1, 8, 64, 96)
+    p = ctypes.c_void_p(16)
+    assert L.gla_chunk_fwd(ctypes.byref(bad), p, p, p, p, None, p, None, p, 1 << 20, None) == 2
+    good = D(1, 1, 64, 64, 64)
+    # required pointer missing
+    assert L.gla_chunk_fwd(ctypes.byref(good), None, p, p, p, None, p, None, p, 1 << 20, None) == 1
+    # misaligned pointer
+    q = ctypes.c_void_p(18)
+    assert L.gla_chunk_fwd(ctypes.byref(good), q, p, p, p, None, p, None, p, 1 << 20, None) == 1
+    # workspace too small / missing
+    assert L.gla_chunk_fwd(ctypes.byref(good), p, p, p, p, None, p, None, p, 16, None) == 3
+    assert L.gla_chunk_fwd(ctypes.byref(good), p, p, p, p, None, p, None, None, 0, None) == 3
+    assert L.gla_chunk_bwd(ctypes.byref(good), p, p, p, p, None, None, None, p, p, p, p, None,
+                           p, 1 << 30, None) == 1
+    assert L.gla_gate_cumsum(ctypes.byref(good), None, p, p, None) == 1

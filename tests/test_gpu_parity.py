@@ -1,0 +1,270 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases (several chunks, ragged tails, initial and final state gradients) are
+compared element by element on every output.  The full-size workloads are compared on
+sampled (batch, head) pairs, for which the oracle runs the whole sequence."""
+import numpy as np
+import pytest
+
+from gla_inputs import CONFIGS, GlaConfig, generate
+from oracle import chunkwise
+from tests.gpu_util import TOL, check, dev_inputs, host, oracle_heads, pick, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def gla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import chunkwise_linear_rnn_amd as m
+    m.lib()
+    return m
+
+
+DEV = "cuda:0"
+
+
+def _states(cfg, rng_seed=7, scale=0.5):
+    rng = np.random.default_rng(rng_seed)
+    shp = (cfg.B, cfg.H, cfg.dk, cfg.dv)
+    S0 = (rng.standard_normal(shp) * scale).astype(np.float32)
+    dST = (rng.standard_normal(shp) * scale).astype(np.float32)
+    return S0, dST
+
+
+SMALL = [
+    # name, dtype, B, H, T, dk, dv, chunk, gate_mean
+    ("f32_ragged", "f32", 1, 2, 200, 64, 128, 64, 0.0),
+    ("f32_dk128", "f32", 2, 1, 130, 128, 64, 64, -3.0),
+    ("bf16_c64", "bf16", 2, 2, 300, 128, 64, 64, 0.0),
+    ("bf16_c128", "bf16", 1, 2, 333, 64, 128, 128, -3.0),
+    ("bf16_dk192_slow", "bf16", 1, 1, 257, 192, 192, 64, 2.0),
+    ("bf16_dk256", "bf16", 1, 1, 190, 256, 256, 128, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+@pytest.mark.parametrize("mode", ["recompute", "materialized"])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_small_cases(gla, case, mode, with_state):
+    name, dt, B, H, T, dk, dv, C, gm = case
+    say(f"[small] {name} mode={mode} state={with_state}")
+    cfg = GlaConfig(name, dt, B, H, T, dk, dv, C, gate_mean=gm, seed=3)
+    d = generate(cfg)
+    x = dev_inputs(d, dt, DEV)
+    S0n, dSTn = _states(cfg) if with_state else (None, None)
+    S0 = torch.from_numpy(S0n).to(DEV) if with_state else None
+    dST = torch.from_numpy(dSTn).to(DEV) if with_state else None
+    o, ST = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], S0, chunk=C, state_mode=mode)
+    dq, dk_, dv_, dla, dS0 = gla.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["dO"], S0, dST,
+                                      chunk=C)
+    torch.cuda.synchronize()
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    ref = oracle_heads(d, heads, None if S0n is None else S0n.astype(np.float64),
+                       None if dSTn is None else dSTn.astype(np.float64))
+    got = {"o": o, "S_T": ST, "dq": dq, "dk": dk_, "dv": dv_, "dla": dla, "dS0": dS0}
+    for k in ("o", "S_T", "dq", "dk", "dv", "dla", "dS0"):
+        check(k, pick(host(got[k]), heads), ref[k], dt)
+
+
+def test_tiny_f32_config(gla):
+    """The tiny fp32 workload, every output against the oracle."""
+    cfg = CONFIGS["tiny_f32"]
+    say(f"[config] {cfg}")
+    d = generate(cfg)
+    x = dev_inputs(d, cfg.dtype, DEV)
+    for mode in ("recompute", "materialized"):
+        o, ST = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], chunk=cfg.chunk, state_mode=mode)
+        g = gla.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["dO"], chunk=cfg.chunk)
+        torch.cuda.synchronize()
+        ref = oracle_heads(d, [(0, 0)])
+        check("o", host(o)[0:1, 0], ref["o"], "f32")
+        check("S_T", host(ST)[0:1, 0], ref["S_T"], "f32")
+        for k, t in zip(("dq", "dk", "dv", "dla", "dS0"), g):
+            check(k, host(t)[0:1, 0], ref[k], "f32")
+
+
+@pytest.mark.parametrize("cfg_name,heads", [
+    ("gla340m_t2k", [(0, 0), (7, 3)]),
+    ("gla1p3b_t2k", [(0, 1), (3, 3)]),
+])
+def test_full_size_configs_sampled_heads(gla, cfg_name, heads):
+    cfg = CONFIGS[cfg_name]
+    say(f"[config] {cfg} heads={heads}")
+    d = generate(cfg)
+    x = dev_inputs(d, cfg.dtype, DEV)
+    o, ST = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], chunk=cfg.chunk)
+    g = gla.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["dO"], chunk=cfg.chunk)
+    torch.cuda.synchronize()
+    ref = oracle_heads(d, heads)
+    check("o", pick(host(o), heads), ref["o"], cfg.dtype)
+    check("S_T", pick(host(ST), heads), ref["S_T"], cfg.dtype)
+    for k, t in zip(("dq", "dk", "dv", "dla", "dS0"), g):
+        check(k, pick(host(t), heads), ref[k], cfg.dtype)
+
+
+def test_long_sequence_chained(gla):
+    """T = 20480 as one call and as 10 chained 2048-token calls (S_T -> S0)."""
+    cfg = CONFIGS["long_t20k"]
+    say(f"[config] {cfg}")
+    d = generate(cfg, with_dO=False)
+    x = dev_inputs(d, cfg.dtype, DEV, names=("q", "k", "v", "log_alpha"))
+    o1, S1 = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], chunk=cfg.chunk)
+    seg = 2048
+    S = None
+    outs = []
+    for j in range(cfg.T // seg):
+        sl = slice(j * seg, (j + 1) * seg)
+        oj, S = gla.fwd(*(x[n][:, :, sl].contiguous() for n in ("q", "k", "v", "log_alpha")), S,
+                        chunk=cfg.chunk)
+        outs.append(oj)
+    o2 = torch.cat(outs, dim=2)
+    torch.cuda.synchronize()
+    from oracle.compare import normwise
+    a, b = host(o1), host(o2)
+    nw = normwise(b, a)
+    say(f"    chained vs single: normwise={nw:.3e} bitwise={np.array_equal(a, b)}")
+    assert nw <= 1e-6
+    assert normwise(host(S), host(S1)) <= 1e-6
+    heads = [(0, 2)]
+    ref = oracle_heads(d, heads, bwd=False)
+    check("o", pick(a, heads), ref["o"], cfg.dtype)
+    check("S_T", pick(host(S1), heads), ref["S_T"], cfg.dtype)
+
+
+@pytest.mark.parametrize("T,C", [(1024, 64), (1024, 128), (4096, 64), (4096, 128),
+                                 (8192, 64), (8192, 128)])
+def test_sweep_configs(gla, T, C):
+    cfg = CONFIGS[f"sweep_t{T}_c{C}"]
+    heads = [(cfg.B - 1, 1)]
+    say(f"[config] {cfg} heads={heads}")
+    d = generate(cfg)
+    x = dev_inputs(d, cfg.dtype, DEV)
+    o, ST = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], chunk=C)
+    g = gla.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["dO"], chunk=C)
+    torch.cuda.synchronize()
+    ref = oracle_heads(d, heads)
+    check("o", pick(host(o), heads), ref["o"], cfg.dtype)
+    check("S_T", pick(host(ST), heads), ref["S_T"], cfg.dtype)
+    for k, t in zip(("dq", "dk", "dv", "dla", "dS0"), g):
+        check(k, pick(host(t), heads), ref[k], cfg.dtype)
+
+
+def test_gate_cumsum_kernel(gla):
+    cfg = GlaConfig("gc", "bf16", 2, 3, 333, 128, 64, 64, seed=11)
+    say(f"[kernel] gate cumsum {cfg}")
+    d = generate(cfg, with_dO=False)
+    x = dev_inputs(d, "bf16", DEV, names=("log_alpha",))
+    g, gamma = gla.gate_cumsum(x["log_alpha"], 64)
+    torch.cuda.synchronize()
+    gr, gamr = chunkwise.gate_cumsum(d["log_alpha"], 64)
+    assert np.max(np.abs(host(g) - gr)) < 1e-5
+    assert np.max(np.abs(host(gamma) - gamr)) < 1e-5
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_chunk_states_kernel(gla, dt):
+    cfg = GlaConfig("cs", dt, 1, 2, 300, 128, 128, 64, seed=5)
+    say(f"[kernel] chunk states {cfg}")
+    d = generate(cfg, with_dO=False)
+    x = dev_inputs(d, dt, DEV, names=("k", "v", "log_alpha"))
+    S0n, _ = _states(cfg)
+    states, ST = gla.chunk_states(x["k"], x["v"], x["log_alpha"], torch.from_numpy(S0n).to(DEV))
+    torch.cuda.synchronize()
+    gr, gamr = chunkwise.gate_cumsum(d["log_alpha"], 64)
+    sr, STr = chunkwise.chunk_states(d["k"], d["v"], gr, gamr, 64, S0n.astype(np.float64))
+    check("states", host(states), sr, dt)
+    check("S_T", host(ST), STr, dt)
+
+
+def test_empty_and_degenerate(gla):
+    say("[edge] empty and degenerate sizes")
+    S0 = torch.randn(1, 2, 64, 64, device=DEV)
+    e = torch.empty(1, 2, 0, 64, device=DEV)
+    o, ST = gla.fwd(e, e, e, e, S0)
+    assert o.shape == (1, 2, 0, 64) and torch.equal(ST, S0)
+    o, ST = gla.fwd(e, e, e, e, None)
+    assert torch.count_nonzero(ST) == 0
+    dST = torch.randn(1, 2, 64, 64, device=DEV)
+    g = gla.bwd(e, e, e, e, e, S0, dST)
+    assert torch.equal(g[4], dST)
+    z = torch.empty(0, 2, 10, 64, device=DEV)
+    o, ST = gla.fwd(z, z, z, z)
+    assert o.numel() == 0
+    # T = 1 and T < chunk: one ragged chunk
+    for T in (1, 5, 63, 65):
+        cfg = GlaConfig("edge", "f32", 1, 1, T, 64, 64, 64, seed=T)
+        d = generate(cfg)
+        x = dev_inputs(d, "f32", DEV)
+        o, ST = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"])
+        g = gla.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["dO"])
+        torch.cuda.synchronize()
+        ref = oracle_heads(d, [(0, 0)])
+        check(f"o T={T}", host(o)[0], ref["o"], "f32")
+        for k, t in zip(("dq", "dk", "dv", "dla", "dS0"), g):
+            check(f"{k} T={T}", host(t)[0], ref[k], "f32")
+
+
+def test_vanishing_and_unit_gates(gla):
+    """alpha -> 0 leaves only the current token; alpha = 1 is causal linear attention.
+
+    For alpha -> 0 the true gate gradient is ~alpha (1e-35 here) while the closed form
+    sums O(1) terms q*dq and k*dk that cancel exactly; its error can only be bounded
+    relative to those terms, so dlog_alpha is checked against sum_t |q dq| + |k dk|."""
+    say("[edge] extreme gates")
+    cfg = GlaConfig("ext", "f32", 1, 2, 150, 64, 64, 64, seed=9)
+    d = generate(cfg)
+    for la_val in (-80.0, 0.0):
+        d2 = dict(d)
+        d2["log_alpha"] = np.full_like(d["log_alpha"], la_val)
+        d2["log_alpha_store"] = d2["log_alpha"].astype(np.float32)
+        x = dev_inputs(d2, "f32", DEV)
+        o, ST = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"])
+        g = gla.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["dO"])
+        torch.cuda.synchronize()
+        heads = [(0, 0), (0, 1)]
+        ref = oracle_heads(d2, heads)
+        check(f"o la={la_val}", pick(host(o), heads), ref["o"], "f32")
+        for k, t in zip(("dq", "dk", "dv", "dS0"), (g[0], g[1], g[2], g[4])):
+            check(f"{k} la={la_val}", pick(host(t), heads), ref[k], "f32")
+        qq, kk = pick(d2["q"], heads), pick(d2["k"], heads)
+        terms = np.sum(np.abs(qq * ref["dq"]) + np.abs(kk * ref["dk"]), axis=-2)   # [heads, dk]
+        err = np.abs(pick(host(g[3]), heads) - ref["dla"])
+        bound = 1e-4 * terms[:, None, :]
+        say(f"    dla la={la_val} max err/bound = {np.max(err / bound):.3e}")
+        assert np.all(err <= bound)
+        if la_val == 0.0:
+            check("dla la=0", pick(host(g[3]), heads), ref["dla"], "f32")
+
+
+def test_deterministic_and_modes_agree(gla):
+    cfg = GlaConfig("det", "bf16", 2, 2, 512, 128, 128, 64, seed=4)
+    say(f"[invariant] determinism {cfg}")
+    d = generate(cfg)
+    x = dev_inputs(d, "bf16", DEV)
+    a = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], state_mode="recompute")
+    b = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], state_mode="recompute")
+    c = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], state_mode="materialized")
+    g1 = gla.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["dO"])
+    g2 = gla.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["dO"])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    for u, w in zip(g1, g2):
+        assert torch.equal(u, w)
+    from oracle.compare import normwise
+    assert normwise(host(c[0]), host(a[0])) < 5e-3
+
+
+def test_invalid_arguments_raise(gla):
+    say("[edge] invalid arguments")
+    x = torch.zeros(1, 1, 64, 96, device=DEV)
+    with pytest.raises(gla.GlaError):
+        gla.fwd(x, x, x, x)
+    y = torch.zeros(1, 1, 64, 64, device=DEV)
+    with pytest.raises(gla.GlaError):
+        gla.fwd(y, y, y, y, chunk=32)
+    with pytest.raises(ValueError):
+        gla.fwd(y, y, y.double(), y)
