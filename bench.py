@@ -1,0 +1,354 @@
+#!/usr/bin/env python3
+"""Throughput of the chunkwise GLA layer, forward + backward, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gla1p3b_t2k]
+
+A step is one gla_chunk_fwd plus one gla_chunk_bwd over the whole batch of seeded
+synthetic inputs (already resident in device memory), with every output and workspace
+preallocated.  K steps are timed between two device synchronisations; every kernel
+launch is also bracketed by HIP events (the traced entry points of the C ABI, recorded
+on the stream the kernels run on) to get each stage's average duration.  One JSON line
+goes to stdout; a per-stage table goes to stderr.
+
+The roofline object describes the stage with the largest time per step, against the
+MI355X peak for its bound (HBM 8 TB/s, or dense bf16 MFMA 2.5 PFLOP/s); its `achieved`
+uses the algorithmic bytes or flops per launch listed in STAGE_WORK below.  `traffic`
+is the measured HBM bytes per launch of that stage from the committed rocprofv3 counter
+summary, or null when no summary matches the current kernel source.
+
+The CPU baseline times the fp64 oracle (step recurrence + direct backward) on a bounded
+sample of the same workload with a process pool on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12          # bytes/s
+PEAK_BF16 = 2.5e15         # dense bf16 MFMA flop/s
+PEAK_F32 = 157.3e12        # fp32 (MFMA / packed vector) flop/s
+METRIC = "GLA fwd+bwd tokens/s at 1.3B shape T=2K, 1 GPU; % of bf16 MFMA peak"
+
+# Kernel source of each stage (for matching committed counter summaries).
+STAGE_SOURCE = {
+    "gate_cumsum": "k_gate.hip", "gate_carry": "k_gate.hip", "gate_grad": "k_gate.hip",
+    "state_dot": "k_gate.hip", "intra": "k_intra.hip", "state_scan": "k_state.hip",
+    "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip", "output": "k_fwd.hip",
+    "fwd_fused": "k_fwd.hip", "bwd_chunk": "k_bwd.hip",
+}
+
+
+def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
+    """(algorithmic HBM bytes, algorithmic flops) of one launch of `stage`.
+
+    Per token and head: each tensor the stage must read or write once, in its storage
+    type; flops count a multiply-add as 2 and the causal intra-chunk products at half
+    the chunk (C/2 average partners)."""
+    BH, N = B * H, (T + C - 1) // C
+    tok = BH * T
+    tokp = BH * N * C                      # padded rows of per-chunk operands
+    st = BH * N * dk * dv * e              # one materialized state tensor
+    if stage == "gate_cumsum":
+        return tok * dk * (e + 4), tok * dk
+    if stage == "intra":
+        if pass_ == "fwd":
+            byt = 3 * tok * dk * e + 2 * tokp * dk * e + BH * N * C * C * e + BH * N * dk * 4
+            if mode == "materialized":
+                byt += tok * dk * (4 - e)  # reads fp32 g instead of log_alpha
+        else:
+            byt = (tok * dk * 4 + 2 * tok * dk * e + BH * N * C * C * e + 2 * tokp * dk * 4
+                   + tokp * dk * e + BH * N * dk * 4)
+        return byt, tok * C * dk
+    if stage in ("state_scan_fwd", "state_scan_rev"):
+        byt = 2 * tokp * dk * 4 + 2 * tok * dv * e + st + BH * N * (dv // 64) * dk * 4
+        return byt, tok * 4 * dk * dv
+    if stage == "state_scan":
+        return tokp * dk * e + tok * dv * e + st + BH * dk * dv * 4, tok * 2 * dk * dv
+    if stage == "output":
+        return tokp * dk * e + BH * N * C * C * e + st + 2 * tok * dv * e, tok * (2 * dk * dv + C * dv)
+    if stage == "fwd_fused":
+        byt = 2 * tokp * dk * e + BH * N * C * C * e + 2 * tok * dv * e + BH * dk * dv * 4
+        return byt, tok * (4 * dk * dv + C * dv)
+    if stage == "bwd_chunk":
+        byt = (tok * (2 * dk * e + 2 * dv * e + dk * 4) + BH * N * C * C * e + tokp * dk * e
+               + 2 * st + tok * (2 * dk * e + dv * e + dk * 4))
+        return byt, tok * (6 * dk * dv + C * (2 * dk + 2 * dv))
+    if stage == "gate_carry":
+        return 2 * BH * N * (dv // 64) * dk * 4 + BH * N * dk * 4, 0
+    if stage == "gate_grad":
+        return tok * dk * (4 + e), tok * dk
+    if stage == "state_dot":
+        return 2 * BH * dk * dv * 4, 2 * BH * dk * dv
+    return 0, 0
+
+
+def path_flops(B, H, T, dk, dv, C):
+    """Algorithmic flops of one forward + backward (causal intra counted at C/2)."""
+    tok = B * H * T
+    return tok * (4 * dk * dv + C * (dk + dv)) + tok * (8 * dk * dv + C * (3 * dk + 2 * dv))
+
+
+# ---------------------------------------------------------------------------------
+# HIP events through the runtime the library uses
+# ---------------------------------------------------------------------------------
+class HipEvents:
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.h.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = ev
+        return arr
+
+    def elapsed_ms(self, a, b):
+        out = ctypes.c_float()
+        err = self.h.hipEventElapsedTime(ctypes.byref(out), a, b)
+        if err != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({err})")
+        return float(out.value)
+
+    def destroy(self, arr):
+        for ev in arr:
+            self.h.hipEventDestroy(ev)
+
+
+# ---------------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample
+# ---------------------------------------------------------------------------------
+def _oracle_head(args):
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    q, k, v, la, dO = args
+    from oracle import recurrence_fwd, recurrence_bwd
+    t0 = time.perf_counter()
+    recurrence_fwd(q, k, v, la)
+    recurrence_bwd(q, k, v, la, dO)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(d, cfg, T_sample):
+    import multiprocessing as mp
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    workers = max(1, min(16, cores, cfg.B * cfg.H))
+    heads = [(i // cfg.H, i % cfg.H) for i in range(workers)]
+    jobs = [tuple(d[n][b, h, :T_sample].copy() for n in ("q", "k", "v", "log_alpha", "dO"))
+            for b, h in heads]
+    env_before = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                                 "MKL_NUM_THREADS")}
+    for k in env_before:
+        os.environ[k] = "1"
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_head, jobs)
+    wall = time.perf_counter() - t0
+    for k, val in env_before.items():
+        if val is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = val
+    tokens = workers * T_sample / cfg.H     # head-tokens -> tokens (each token has H heads)
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": (f"fp64 step recurrence + direct backward, {workers} (batch, head) pairs x "
+                       f"first {T_sample} tokens of {cfg.name}, one process per head, "
+                       f"{wall:.2f} s wall")}
+
+
+def counter_traffic(stage, workload):
+    """HBM bytes per launch from a committed counter summary that matches the current
+    kernel source, else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{stage}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    src = os.path.join(ROOT, "chunkwise_linear_rnn_amd", "csrc", STAGE_SOURCE[stage])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gla1p3b_t2k")
+    ap.add_argument("--state-mode", default="recompute", choices=["recompute", "materialized"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
+                    help="tokens per (batch, head) in the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration runs)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (sharding is a "
+              "design note only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import chunkwise_linear_rnn_amd as gla
+    from chunkwise_linear_rnn_amd import _native as nat
+    from gla_inputs import CONFIGS, generate
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {cfg}", file=sys.stderr, flush=True)
+    d = generate(cfg)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def up(name):
+        a = d[name + "_store"]
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v, la, dO = (up(n) for n in ("q", "k", "v", "log_alpha", "dO"))
+    B, H, T, dk, dv, C = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.chunk
+    mode = nat.RECOMPUTE if args.state_mode == "recompute" else nat.MATERIALIZED
+    desc = nat.make_desc(B, H, T, dk, dv, C, cfg.subchunk, nat.BF16 if cfg.dtype == "bf16" else nat.F32, mode)
+    o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    dq, dk_, dv_, dla = (torch.empty_like(x) for x in (q, k, v, la))
+    wsf_n = nat.workspace_bytes(desc, nat.PASS_FWD)
+    wsb_n = nat.workspace_bytes(desc, nat.PASS_BWD)
+    wsf = torch.empty(wsf_n, dtype=torch.uint8, device=dev)
+    wsb = torch.empty(wsb_n, dtype=torch.uint8, device=dev)
+    fwd_stages = nat.trace_stages(desc, nat.PASS_FWD)
+    bwd_stages = nat.trace_stages(desc, nat.PASS_BWD, False)
+    nf, nb = len(fwd_stages) + 1, len(bwd_stages) + 1
+    L = nat.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    hip = HipEvents()
+    total_steps = args.warmup + args.steps
+    evf = [hip.create(nf) for _ in range(total_steps)]
+    evb = [hip.create(nb) for _ in range(total_steps)]
+
+    def step(j):
+        st = L.gla_chunk_fwd_traced(ctypes.byref(desc), P(q), P(k), P(v), P(la), None, P(o), P(S_T),
+                                    P(wsf), wsf_n, sp, evf[j], nf)
+        if st:
+            raise nat.GlaError(st, "gla_chunk_fwd_traced")
+        st = L.gla_chunk_bwd_traced(ctypes.byref(desc), P(q), P(k), P(v), P(la), None, P(dO), None,
+                                    P(dq), P(dk_), P(dv_), P(dla), None, P(wsb), wsb_n, sp, evb[j], nb)
+        if st:
+            raise nat.GlaError(st, "gla_chunk_bwd_traced")
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for j in range(args.warmup):
+        step(j)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.warmup, total_steps):
+        step(j)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-stage means over the timed steps
+    stages = {}
+    for j in range(args.warmup, total_steps):
+        for names, evs, tag in ((fwd_stages, evf[j], "fwd"), (bwd_stages, evb[j], "bwd")):
+            for s_i, name in enumerate(names):
+                key = (tag, name)
+                stages.setdefault(key, 0.0)
+                stages[key] += hip.elapsed_ms(evs[s_i], evs[s_i + 1])
+    for key in stages:
+        stages[key] /= args.steps
+    gpu_ms_from_events = sum(stages.values())
+
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 3 x {nbytes} B copies", file=sys.stderr, flush=True)
+
+    e = 2 if cfg.dtype == "bf16" else 4
+    mode_s = args.state_mode
+    print(f"[bench] {cfg.name}: {ms_per_step:.4f} ms/step (wall), {gpu_ms_from_events:.4f} ms "
+          f"(sum of stage events)", file=sys.stderr)
+    print(f"{'pass':4s} {'stage':16s} {'us':>9s} {'GB/s':>8s} {'TFLOP/s':>8s}", file=sys.stderr)
+    dom_key, dom_ms = None, -1.0
+    for (tag, name), ms in stages.items():
+        byt, fl = stage_work(name, tag, mode_s, B, H, T, dk, dv, C, e)
+        print(f"{tag:4s} {name:16s} {ms * 1e3:9.2f} {byt / ms / 1e6:8.0f} {fl / ms / 1e9:8.1f}",
+              file=sys.stderr)
+        if ms > dom_ms:
+            dom_key, dom_ms = (tag, name), ms
+    byt, fl = stage_work(dom_key[1], dom_key[0], mode_s, B, H, T, dk, dv, C, e)
+    ai = fl / byt if byt else float("inf")
+    ridge = PEAK_BF16 / PEAK_HBM
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": byt / (dom_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": fl / (dom_ms * 1e-3) / 1e12, "peak": PEAK_BF16 / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = counter_traffic(dom_key[1], cfg.name)
+    roof["kernel"] = f"{dom_key[0]}:{dom_key[1]}"
+    roof["avg_launch_us"] = dom_ms * 1e3
+    roof["algorithmic_bytes_per_launch"] = byt
+    roof["algorithmic_flops_per_launch"] = fl
+
+    tokens = B * T
+    value = tokens / (ms_per_step * 1e-3)
+    flops = path_flops(B, H, T, dk, dv, C)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": C,
+                   "subchunk": cfg.subchunk, "state_mode": mode_s, "global_batch": B,
+                   "seq_len": T, "parallelism": "none (1 GPU)"},
+        "tflops": tflops, "mfma_peak_frac": flops / (ms_per_step * 1e-3) / PEAK_BF16,
+        "roofline": roof,
+    }
+    for arr in evf + evb:
+        hip.destroy(arr)
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(d, cfg, min(args.cpu_tokens, T))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

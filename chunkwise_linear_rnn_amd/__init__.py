@@ -17,8 +17,8 @@ and GLAFunction, a torch.autograd.Function over fwd/bwd.
 from __future__ import annotations
 
 from ._native import (GlaDesc, GlaError, F32, BF16, MATERIALIZED, RECOMPUTE, PASS_FWD,  # noqa: F401
-                      PASS_BWD, PASS_STATES, lib, lib_path, make_desc, status_string, validate,
-                      version, workspace_bytes)
+                      PASS_BWD, PASS_STATES, lib, lib_path, make_desc, status_string, trace_stages,
+                      validate, version, workspace_bytes)
 from .ops import fwd, bwd, gate_cumsum, chunk_states, GLAFunction, gla  # noqa: F401
 
 __all__ = ["fwd", "bwd", "gate_cumsum", "chunk_states", "GLAFunction", "gla", "GlaDesc",

@@ -39,6 +39,11 @@ SIGNATURES = {
     "gla_chunk_fwd": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "gla_chunk_bwd": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp, _sz, _vp]),
+    "gla_trace_stages": (_i32, [_PDESC, _i32, _i32, ctypes.POINTER(ctypes.c_char_p), _i32]),
+    "gla_chunk_fwd_traced": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
+                                    ctypes.POINTER(_vp), _i32]),
+    "gla_chunk_bwd_traced": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _vp, _sz, _vp, ctypes.POINTER(_vp), _i32]),
 }
 
 _lib = None
@@ -85,6 +90,15 @@ def make_desc(B, H, T, dk, dv, chunk=64, subchunk=16, dtype=BF16, state_mode=REC
 
 def validate(desc: GlaDesc, pass_: int = PASS_FWD) -> int:
     return int(lib().gla_validate(ctypes.byref(desc), int(pass_)))
+
+
+def trace_stages(desc: GlaDesc, pass_: int, with_dS_T: bool = False) -> list:
+    n = int(lib().gla_trace_stages(ctypes.byref(desc), int(pass_), int(bool(with_dS_T)), None, 0))
+    if n < 0:
+        raise ValueError("bad descriptor or pass")
+    names = (ctypes.c_char_p * n)()
+    lib().gla_trace_stages(ctypes.byref(desc), int(pass_), int(bool(with_dS_T)), names, n)
+    return [x.decode() for x in names]
 
 
 def workspace_bytes(desc: GlaDesc, pass_: int = PASS_FWD) -> int:

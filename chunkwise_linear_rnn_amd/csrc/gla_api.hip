@@ -112,9 +112,53 @@ gla_status_t state_copy(const float* src, float* dst, long n, hipStream_t s) {
   return dev(hipGetLastError());
 }
 
+// Records caller-provided events between kernel launches (profiling); inert when the
+// caller passes none.
+struct Tracer {
+  void** ev;
+  int n;
+  hipStream_t s;
+  int k = 0;
+  gla_status_t mark() {
+    if (!ev) return GLA_OK;
+    if (k >= n) return GLA_ERR_INVALID_ARG;
+    return dev(hipEventRecord((hipEvent_t)ev[k++], s));
+  }
+};
+
+// Stage names of each pipeline, in launch order.
+const char* const kFwdMat[] = {"gate_cumsum", "intra", "state_scan", "output"};
+const char* const kFwdRec[] = {"intra", "fwd_fused"};
+const char* const kBwd[] = {"gate_cumsum", "intra", "state_scan_fwd", "state_scan_rev",
+                            "state_dot", "bwd_chunk", "gate_carry", "gate_grad"};
+
+int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, int max) {
+  const char* const* src;
+  int n;
+  if (pass == GLA_PASS_FWD) {
+    if (d->state_mode == GLA_STATES_MATERIALIZED) { src = kFwdMat; n = 4; }
+    else { src = kFwdRec; n = 2; }
+  } else {
+    src = kBwd; n = 8;
+  }
+  int m = 0;
+  for (int j = 0; j < n; ++j) {
+    if (pass == GLA_PASS_BWD && j == 4 && !with_dST) continue;
+    if (out && m < max) out[m] = src[j];
+    ++m;
+  }
+  return m;
+}
+
 }  // namespace
 
 extern "C" {
+
+int32_t gla_trace_stages(const gla_desc_t* d, int32_t pass, int32_t with_dS_T, const char** names,
+                         int32_t max_names) {
+  if (!d || (pass != GLA_PASS_FWD && pass != GLA_PASS_BWD)) return -1;
+  return stage_list(d, pass, with_dS_T, names, max_names);
+}
 
 const char* gla_status_string(gla_status_t s) {
   switch (s) {
@@ -198,11 +242,15 @@ gla_status_t gla_chunk_states(const gla_desc_t* d, const void* k, const void* v,
   return dev(gla::launch_state_scan(sa, s));
 }
 
-gla_status_t gla_chunk_fwd(const gla_desc_t* d, const void* q, const void* k, const void* v,
-                           const void* log_alpha, const float* S0, void* o, float* S_T, void* ws,
-                           size_t ws_bytes, void* stream) {
+gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void* k,
+                                  const void* v, const void* log_alpha, const float* S0, void* o,
+                                  float* S_T, void* ws, size_t ws_bytes, void* stream,
+                                  void** events, int32_t n_events) {
   const gla_status_t st = gla_validate(d, GLA_PASS_FWD);
   if (st != GLA_OK) return st;
+  if (events && n_events < stage_list(d, GLA_PASS_FWD, 0, nullptr, 0) + 1)
+    return GLA_ERR_INVALID_ARG;
+  Tracer tr{events, n_events, (hipStream_t)stream};
   const Dims x = dims_of(d);
   hipStream_t s = (hipStream_t)stream;
   if (x.BH == 0) return GLA_OK;
@@ -216,6 +264,7 @@ gla_status_t gla_chunk_fwd(const gla_desc_t* d, const void* q, const void* k, co
   const bool mat = d->state_mode == GLA_STATES_MATERIALIZED;
   gla_status_t rs = GLA_OK;
   if (mat) {
+    if ((rs = tr.mark()) != GLA_OK) return rs;
     rs = dev(gla::launch_gate_cumsum(x.dtype, log_alpha, (float*)(w + p.g), nullptr, (int)x.BH,
                                      (int)x.T, (int)x.dk, (int)x.C, s));
     if (rs != GLA_OK) return rs;
@@ -225,6 +274,7 @@ gla_status_t gla_chunk_fwd(const gla_desc_t* d, const void* q, const void* k, co
   ia.N = (int)x.N; ia.want_A = true; ia.q = q; ia.k = k; ia.la = log_alpha;
   ia.g = mat ? (const float*)(w + p.g) : nullptr;
   ia.A = w + p.A; ia.Qh = w + p.Qh; ia.KhT = w + p.KhT; ia.eg = (float*)(w + p.eg);
+  if ((rs = tr.mark()) != GLA_OK) return rs;
   rs = dev(gla::launch_intra(ia, s));
   if (rs != GLA_OK) return rs;
   if (mat) {
@@ -233,27 +283,42 @@ gla_status_t gla_chunk_fwd(const gla_desc_t* d, const void* q, const void* k, co
     sa.dv = (int)x.dv; sa.N = (int)x.N; sa.reverse = false; sa.store = 2;
     sa.XT = w + p.KhT; sa.Y = v; sa.eg = (const float*)(w + p.eg); sa.S_in = S0;
     sa.states = w + p.st; sa.S_out = S_T;
+    if ((rs = tr.mark()) != GLA_OK) return rs;
     rs = dev(gla::launch_state_scan(sa, s));
     if (rs != GLA_OK) return rs;
     gla::OutArgs oa{};
     oa.dtype = x.dtype; oa.C = (int)x.C; oa.BH = (int)x.BH; oa.T = (int)x.T; oa.dk = (int)x.dk;
     oa.dv = (int)x.dv; oa.N = (int)x.N; oa.Qh = w + p.Qh; oa.A = w + p.A; oa.STt = w + p.st;
     oa.v = v; oa.o = o;
-    return dev(gla::launch_output(oa, s));
+    if ((rs = tr.mark()) != GLA_OK) return rs;
+    if ((rs = dev(gla::launch_output(oa, s))) != GLA_OK) return rs;
+    return tr.mark();
   }
   gla::FusedArgs fa{};
   fa.dtype = x.dtype; fa.C = (int)x.C; fa.BH = (int)x.BH; fa.T = (int)x.T; fa.dk = (int)x.dk;
   fa.dv = (int)x.dv; fa.N = (int)x.N; fa.Qh = w + p.Qh; fa.KhT = w + p.KhT; fa.A = w + p.A;
   fa.v = v; fa.eg = (const float*)(w + p.eg); fa.S0 = S0; fa.o = o; fa.S_T = S_T;
-  return dev(gla::launch_fwd_fused(fa, s));
+  if ((rs = tr.mark()) != GLA_OK) return rs;
+  if ((rs = dev(gla::launch_fwd_fused(fa, s))) != GLA_OK) return rs;
+  return tr.mark();
 }
 
-gla_status_t gla_chunk_bwd(const gla_desc_t* d, const void* q, const void* k, const void* v,
-                           const void* log_alpha, const float* S0, const void* dO,
-                           const float* dS_T, void* dq, void* dk, void* dv, void* dlog_alpha,
-                           float* dS0, void* ws, size_t ws_bytes, void* stream) {
+gla_status_t gla_chunk_fwd(const gla_desc_t* d, const void* q, const void* k, const void* v,
+                           const void* log_alpha, const float* S0, void* o, float* S_T, void* ws,
+                           size_t ws_bytes, void* stream) {
+  return gla_chunk_fwd_traced(d, q, k, v, log_alpha, S0, o, S_T, ws, ws_bytes, stream, nullptr, 0);
+}
+
+gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void* k,
+                                  const void* v, const void* log_alpha, const float* S0,
+                                  const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
+                                  void* dlog_alpha, float* dS0, void* ws, size_t ws_bytes,
+                                  void* stream, void** events, int32_t n_events) {
   const gla_status_t st = gla_validate(d, GLA_PASS_BWD);
   if (st != GLA_OK) return st;
+  if (events && n_events < stage_list(d, GLA_PASS_BWD, dS_T != nullptr, nullptr, 0) + 1)
+    return GLA_ERR_INVALID_ARG;
+  Tracer tr{events, n_events, (hipStream_t)stream};
   const Dims x = dims_of(d);
   hipStream_t s = (hipStream_t)stream;
   if (x.BH == 0) return GLA_OK;
@@ -268,8 +333,10 @@ gla_status_t gla_chunk_bwd(const gla_desc_t* d, const void* q, const void* k, co
   char* w = (char*)ws;
   const int C = (int)x.C, BH = (int)x.BH, T = (int)x.T, DK = (int)x.dk, DV = (int)x.dv,
             N = (int)x.N;
-  gla_status_t rs = dev(gla::launch_gate_cumsum(x.dtype, log_alpha, (float*)(w + p.g), nullptr,
-                                                BH, T, DK, C, s));
+  gla_status_t rs = tr.mark();
+  if (rs != GLA_OK) return rs;
+  rs = dev(gla::launch_gate_cumsum(x.dtype, log_alpha, (float*)(w + p.g), nullptr, BH, T, DK, C,
+                                   s));
   if (rs != GLA_OK) return rs;
   gla::IntraArgs ia{};
   ia.dtype = x.dtype; ia.C = C; ia.BH = BH; ia.T = T; ia.dk = DK; ia.N = N; ia.want_A = true;
@@ -277,6 +344,7 @@ gla_status_t gla_chunk_bwd(const gla_desc_t* d, const void* q, const void* k, co
   ia.q = q; ia.k = k; ia.la = log_alpha; ia.g = (const float*)(w + p.g);
   ia.A = w + p.A; ia.QhT = w + p.QhT; ia.Kh = w + p.Kh; ia.KhT = w + p.KhT;
   ia.eg = (float*)(w + p.eg);
+  if ((rs = tr.mark()) != GLA_OK) return rs;
   rs = dev(gla::launch_intra(ia, s));
   if (rs != GLA_OK) return rs;
   // forward scan: chunk-start states S_[i]; cross term rowsum(S_[i] * Qh_i^T dO_i)
@@ -286,15 +354,18 @@ gla_status_t gla_chunk_bwd(const gla_desc_t* d, const void* q, const void* k, co
   sa.XT = w + p.KhT; sa.Y = v; sa.X2T = w + p.QhT; sa.Y2 = dO; sa.cross = (float*)(w + p.crossF);
   sa.eg = (const float*)(w + p.eg); sa.S_in = S0; sa.states = w + p.st;
   sa.S_out = dS_T ? (float*)(w + p.ST) : nullptr;
+  if ((rs = tr.mark()) != GLA_OK) return rs;
   rs = dev(gla::launch_state_scan(sa, s));
   if (rs != GLA_OK) return rs;
   // reverse scan: dS_[i+1]; cross term rowsum(dS_[i+1] * Kh_i^T V_i)
   gla::ScanArgs ra = sa;
   ra.reverse = true; ra.XT = w + p.QhT; ra.Y = dO; ra.X2T = w + p.KhT; ra.Y2 = v;
   ra.cross = (float*)(w + p.crossR); ra.S_in = dS_T; ra.states = w + p.dst; ra.S_out = dS0;
+  if ((rs = tr.mark()) != GLA_OK) return rs;
   rs = dev(gla::launch_state_scan(ra, s));
   if (rs != GLA_OK) return rs;
   if (dS_T) {
+    if ((rs = tr.mark()) != GLA_OK) return rs;
     rs = dev(gla::launch_state_dot(dS_T, (const float*)(w + p.ST), (float*)(w + p.cT), BH, DK,
                                    DV, s));
     if (rs != GLA_OK) return rs;
@@ -304,12 +375,27 @@ gla_status_t gla_chunk_bwd(const gla_desc_t* d, const void* q, const void* k, co
   ba.q = q; ba.k = k; ba.v = v; ba.dO = dO; ba.g = (const float*)(w + p.g); ba.gamma = nullptr;
   ba.A = w + p.A; ba.Kh = w + p.Kh; ba.S = w + p.st; ba.dS = w + p.dst;
   ba.dq = dq; ba.dk_out = dk; ba.dv_out = dv; ba.Dloc = (float*)(w + p.Dloc);
+  if ((rs = tr.mark()) != GLA_OK) return rs;
   rs = dev(gla::launch_bwd_chunk(ba, s));
   if (rs != GLA_OK) return rs;
-  return dev(gla::launch_gate_grad(x.dtype, (const float*)(w + p.Dloc),
-                                   (const float*)(w + p.crossF), (const float*)(w + p.crossR),
-                                   dS_T ? (const float*)(w + p.cT) : nullptr,
-                                   (float*)(w + p.carry), dlog_alpha, BH, T, DK, DV, C, s));
+  if ((rs = tr.mark()) != GLA_OK) return rs;
+  rs = dev(gla::launch_gate_carry((const float*)(w + p.crossF), (const float*)(w + p.crossR),
+                                  dS_T ? (const float*)(w + p.cT) : nullptr, (float*)(w + p.carry),
+                                  BH, T, DK, DV, C, s));
+  if (rs != GLA_OK) return rs;
+  if ((rs = tr.mark()) != GLA_OK) return rs;
+  rs = dev(gla::launch_gate_grad(x.dtype, (const float*)(w + p.Dloc), (const float*)(w + p.carry),
+                                 dlog_alpha, BH, T, DK, C, s));
+  if (rs != GLA_OK) return rs;
+  return tr.mark();
+}
+
+gla_status_t gla_chunk_bwd(const gla_desc_t* d, const void* q, const void* k, const void* v,
+                           const void* log_alpha, const float* S0, const void* dO,
+                           const float* dS_T, void* dq, void* dk, void* dv, void* dlog_alpha,
+                           float* dS0, void* ws, size_t ws_bytes, void* stream) {
+  return gla_chunk_bwd_traced(d, q, k, v, log_alpha, S0, dO, dS_T, dq, dk, dv, dlog_alpha, dS0, ws,
+                              ws_bytes, stream, nullptr, 0);
 }
 
 }  // extern "C"

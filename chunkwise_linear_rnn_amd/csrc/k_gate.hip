@@ -107,13 +107,19 @@ hipError_t launch_state_dot(const float* dST, const float* ST, float* cT, int BH
   return hipGetLastError();
 }
 
-hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* crossF,
-                            const float* crossR, const float* cT, float* carry, void* dla,
-                            int BH, int T, int dk, int dv, int C, hipStream_t s) {
+hipError_t launch_gate_carry(const float* crossF, const float* crossR, const float* cT,
+                             float* carry, int BH, int T, int dk, int dv, int C, hipStream_t s) {
   const int N = (T + C - 1) / C;
   if (BH == 0 || N == 0) return hipSuccess;
   hipLaunchKernelGGL(k_gate_carry, dim3((dk + kThreads - 1) / kThreads, BH), dim3(kThreads), 0, s,
                      crossF, crossR, cT, carry, dk, dv / 64, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* carry, void* dla, int BH,
+                            int T, int dk, int C, hipStream_t s) {
+  const int N = (T + C - 1) / C;
+  if (BH == 0 || N == 0) return hipSuccess;
   dim3 grid(N, BH);
   if (dtype == 0)
     hipLaunchKernelGGL(k_gate_grad<float>, grid, dim3(kThreads), 0, s, Dloc, carry, (float*)dla,

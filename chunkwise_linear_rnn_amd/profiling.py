@@ -1,0 +1,86 @@
+"""Summaries of rocprofv3 output for this library's kernels (text, a few KB).
+
+    python -m chunkwise_linear_rnn_amd.profiling stats <run_kernel_stats.csv> "<command>"
+    python -m chunkwise_linear_rnn_amd.profiling counters <FETCH csv> <WRITE csv> <copy bytes> \
+        <stage> <workload> "<commands>"
+
+`stats` renders the per-kernel table of a `rocprofv3 --kernel-trace --stats` run.
+`counters` turns two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of
+`bench.py --copy-calibration` into HBM bytes per launch of one stage: the counters are
+scaled so that the plain 1 GiB device copy in the same run reads and writes exactly its
+size; the result is written as JSON (matched by bench.py against the kernel source hash).
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+STAGE_KERNEL = {"bwd_chunk": "k_bwd_chunk", "fwd_fused": "k_fwd_fused", "intra": "k_intra",
+                "state_scan_fwd": "k_state_scan", "state_scan_rev": "k_state_scan",
+                "output": "k_output", "gate_cumsum": "k_gate_cumsum", "gate_grad": "k_gate_grad",
+                "gate_carry": "k_gate_carry"}
+STAGE_SOURCE = {"bwd_chunk": "k_bwd.hip", "fwd_fused": "k_fwd.hip", "intra": "k_intra.hip",
+                "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip",
+                "output": "k_fwd.hip", "gate_cumsum": "k_gate.hip", "gate_grad": "k_gate.hip",
+                "gate_carry": "k_gate.hip"}
+
+
+def short(name: str) -> str:
+    m = re.search(r"(k_[a-z_]+)", name)
+    return m.group(1) if m else name[:40]
+
+
+def stats_table(path: str, command: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    out = [f"command: {command}", "",
+           f"{'kernel':18s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'share%':>7s}  symbol"]
+    for r in rows:
+        out.append(f"{short(r['Name']):18s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                   f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                   f"{float(r['Percentage']):7.2f}  {r['Name'][:90]}")
+    return "\n".join(out) + "\n"
+
+
+def _counter_rows(path, counter):
+    rows = list(csv.DictReader(open(path)))
+    key = next(k for k in rows[0] if k.lower() in ("counter_value", "value"))
+    name_key = next(k for k in rows[0] if k.lower() in ("kernel_name", "kernel-name", "name"))
+    cname = next(k for k in rows[0] if k.lower() in ("counter_name", "counter"))
+    return [(r[name_key], float(r[key])) for r in rows if r[cname] == counter]
+
+
+def counters(fetch_csv, write_csv, copy_bytes, stage, workload, command, root):
+    f = _counter_rows(fetch_csv, "FETCH_SIZE")
+    w = _counter_rows(write_csv, "WRITE_SIZE")
+    copy_f = [v for n, v in f if "copy" in n.lower() or "elementwise" in n.lower()]
+    copy_w = [v for n, v in w if "copy" in n.lower() or "elementwise" in n.lower()]
+    sel = STAGE_KERNEL[stage]
+    kf = [v for n, v in f if sel in n]
+    kw = [v for n, v in w if sel in n]
+    if stage.startswith("state_scan"):   # two scans per step, same kernel: keep one of each pair
+        kf, kw = kf[0::2] if stage.endswith("fwd") else kf[1::2], kw[0::2] if stage.endswith("fwd") else kw[1::2]
+    sf = copy_bytes / (1024.0 * (sum(copy_f) / len(copy_f)))
+    sw = copy_bytes / (1024.0 * (sum(copy_w) / len(copy_w)))
+    fetch = sum(kf) / len(kf) * 1024.0 * sf
+    write = sum(kw) / len(kw) * 1024.0 * sw
+    src = os.path.join(root, "chunkwise_linear_rnn_amd", "csrc", STAGE_SOURCE[stage])
+    return {"stage": stage, "workload": workload,
+            "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+            "fetch_kib_raw": sum(kf) / len(kf), "write_kib_raw": sum(kw) / len(kw),
+            "copy_scale_fetch": sf, "copy_scale_write": sw,
+            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+            "traffic_bytes_per_launch": fetch + write, "launches": len(kf), "command": command}
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        sys.stdout.write(stats_table(sys.argv[2], sys.argv[3]))
+    elif sys.argv[1] == "counters":
+        root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+        rec = counters(sys.argv[2], sys.argv[3], float(sys.argv[4]), sys.argv[5], sys.argv[6],
+                       sys.argv[7], root)
+        print(json.dumps(rec, indent=1))

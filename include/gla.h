@@ -129,6 +129,35 @@ gla_status_t gla_chunk_bwd(const gla_desc_t* desc, const void* q, const void* k,
                            void* dv, void* dlog_alpha, float* dS0, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* Stage tracing, for profiling.  The *_traced variants behave exactly like
+ * gla_chunk_fwd / gla_chunk_bwd and additionally record caller-created hipEvent_t
+ * handles on `stream`: events[j] right before the j-th kernel launch and events[n] after
+ * the last, where n is the stage count from gla_trace_stages (events == NULL records
+ * nothing).  The elapsed time between events[j] and events[j+1] is the duration of stage
+ * j.  n_events smaller than n + 1 is GLA_ERR_INVALID_ARG (checked before any launch).
+ *
+ * gla_trace_stages returns n for a pass (with_dS_T: whether the backward gets a dS_T) and
+ * writes up to max_names static stage names to `names` (nullable); -1 on a NULL desc or a
+ * bad pass.  The stages are
+ *   forward, materialized: gate_cumsum, intra, state_scan, output
+ *   forward, recompute:    intra, fwd_fused
+ *   backward:              gate_cumsum, intra, state_scan_fwd, state_scan_rev,
+ *                          [state_dot when dS_T is given], bwd_chunk, gate_carry, gate_grad */
+int32_t gla_trace_stages(const gla_desc_t* desc, int32_t pass, int32_t with_dS_T,
+                         const char** names, int32_t max_names);
+
+gla_status_t gla_chunk_fwd_traced(const gla_desc_t* desc, const void* q, const void* k,
+                                  const void* v, const void* log_alpha, const float* S0,
+                                  void* o, float* S_T, void* ws, size_t ws_bytes, void* stream,
+                                  void** events, int32_t n_events);
+
+gla_status_t gla_chunk_bwd_traced(const gla_desc_t* desc, const void* q, const void* k,
+                                  const void* v, const void* log_alpha, const float* S0,
+                                  const void* dO, const float* dS_T, void* dq, void* dk,
+                                  void* dv, void* dlog_alpha, float* dS0, void* ws,
+                                  size_t ws_bytes, void* stream, void** events,
+                                  int32_t n_events);
+
 #ifdef __cplusplus
 }
 #endif
