@@ -130,7 +130,7 @@ struct Tracer {
 const char* const kFwdMat[] = {"gate_cumsum", "intra", "state_scan", "output"};
 const char* const kFwdRec[] = {"intra", "fwd_fused"};
 const char* const kBwd[] = {"gate_cumsum", "intra", "state_scan_fwd", "state_scan_rev",
-                            "state_dot", "bwd_chunk", "gate_carry", "gate_grad"};
+                            "state_dot", "bwd_chunk", "gate_tot", "gate_grad"};
 
 int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, int max) {
   const char* const* src;
@@ -385,7 +385,8 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   if (rs != GLA_OK) return rs;
   if ((rs = tr.mark()) != GLA_OK) return rs;
   rs = dev(gla::launch_gate_grad(x.dtype, (const float*)(w + p.Dloc), (const float*)(w + p.carry),
-                                 dlog_alpha, BH, T, DK, C, s));
+                                 dS_T ? (const float*)(w + p.cT) : nullptr, dlog_alpha, BH, T, DK,
+                                 C, s));
   if (rs != GLA_OK) return rs;
   return tr.mark();
 }

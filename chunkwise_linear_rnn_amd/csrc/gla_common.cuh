@@ -30,6 +30,16 @@ constexpr int kThreads = 256;   // 4 waves per workgroup everywhere
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// MI355X places workgroup L of a launch (linear id) on XCD L % 8, and each XCD has its
+// own L2.  This maps the linear id to a logical tile id such that logical ids
+// [x*per + min(x, rem), ...) all run on XCD x: tiles that are consecutive in logical order
+// (and share operands) share one L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_logical(int L, int total) {
+  const int x = L % kXcds, slot = L / kXcds, per = total / kXcds, rem = total % kXcds;
+  return x * per + (x < rem ? x : rem) + slot;
+}
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // e^x with the hardware base-2 exponential.  Arguments here are differences of
@@ -170,5 +180,144 @@ __device__ __forceinline__ void stage_cols(OpT* lds, int lld, const Tin* src, lo
     }
   }
 }
+
+// Fragment of 8 consecutive input elements (widened, then rounded to the operand type);
+// zero when !valid.
+template <typename OpT, typename Tin>
+__device__ __forceinline__ void load_frag_gc(Frag<OpT>& f, const Tin* p, bool valid) {
+  float x[8];
+  if (valid) load8(x, p + 8 * (lane_id() >> 4)); else zero8(x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.set(e, x[e]);
+}
+
+// An operand as high part + remainder in the MFMA type (bf16), or as is (fp32).
+template <typename OpT>
+struct SFrag {
+  Frag<OpT> hi, lo;
+  __device__ __forceinline__ void set(int e, float x) {
+    hi.set(e, x);
+    if constexpr (sizeof(OpT) == 2) lo.set(e, x - hi.get(e));
+  }
+};
+template <typename OpT>
+__device__ __forceinline__ void mma_split(f32x4& acc, const SFrag<OpT>& a, const SFrag<OpT>& b) {
+  mma(acc, a.hi, b.hi);
+  if constexpr (sizeof(OpT) == 2) {
+    mma(acc, a.hi, b.lo);
+    mma(acc, a.lo, b.hi);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Register-staged tile copies (global -> registers now, registers -> LDS later), so
+// the next chunk's loads are in flight while the current chunk computes.
+// ---------------------------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// A contiguous global tile of ROWS x COLS elements (row-major, COLS contiguous) moved as
+// 16-byte units into an LDS tile with row stride LD (elements).
+template <typename T, int ROWS, int COLS, int LD>
+struct FlatTile {
+  static constexpr int kPer = 16 / (int)sizeof(T);            // elements per unit
+  static constexpr int kUnits = ROWS * COLS / kPer;
+  static constexpr int kPerThread = (kUnits + kThreads - 1) / kThreads;
+  u32x4 u[kPerThread];
+  __device__ __forceinline__ void load(const T* __restrict__ g) {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int idx = threadIdx.x + j * kThreads;
+      if (kUnits % kThreads == 0 || idx < kUnits)
+        u[j] = *reinterpret_cast<const u32x4*>(g + (long)idx * kPer);
+    }
+  }
+  __device__ __forceinline__ void store(T* lds) const {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int idx = threadIdx.x + j * kThreads;
+      if (kUnits % kThreads == 0 || idx < kUnits) {
+        const int e = idx * kPer, r = e / COLS, c = e % COLS;
+        *reinterpret_cast<u32x4*>(lds + r * LD + c) = u[j];
+      }
+    }
+  }
+};
+
+// ROWS x COLS tile of a row-major [*, gld] matrix (rows beyond `rows` zero) moved as
+// 16-byte units into an LDS tile with row stride LD, same orientation.
+template <typename T, int ROWS, int COLS, int LD>
+struct RowTile {
+  static constexpr int kPer = 16 / (int)sizeof(T);
+  static constexpr int kUnitsRow = COLS / kPer;
+  static constexpr int kUnits = ROWS * kUnitsRow;
+  static constexpr int kPerThread = (kUnits + kThreads - 1) / kThreads;
+  u32x4 u[kPerThread];
+  __device__ __forceinline__ void load(const T* __restrict__ g, long gld, int rows) {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int idx = threadIdx.x + j * kThreads;
+      const int r = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
+      if (kUnits % kThreads == 0 || idx < kUnits)
+        u[j] = r < rows ? *reinterpret_cast<const u32x4*>(g + r * gld + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(T* lds) const {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int idx = threadIdx.x + j * kThreads;
+      const int r = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
+      if (kUnits % kThreads == 0 || idx < kUnits)
+        *reinterpret_cast<u32x4*>(lds + r * LD + c) = u[j];
+    }
+  }
+};
+
+// Same as FlatTile, for a tile whose rows are contiguous in global memory and COLS
+// elements long (alias kept for readability at call sites).
+template <typename T, int ROWS, int COLS, int LD>
+using FlatTileRows = FlatTile<T, ROWS, COLS, LD>;
+
+// ROWS x 64 slice of a row-major [*, gld] input (Tin), rows beyond `rows` zero, staged
+// transposed (lds[c * LD + r], OpT) through 2-row x 8-column units.
+template <typename OpT, typename Tin, int ROWS, int LD>
+struct ColTile {
+  static constexpr int kUnits = (ROWS / 2) * 8;
+  static constexpr int kPerThread = (kUnits + kThreads - 1) / kThreads;
+  float x0[kPerThread][8], x1[kPerThread][8];
+  __device__ __forceinline__ void load(const Tin* __restrict__ g, long gld, int rows) {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int idx = threadIdx.x + j * kThreads;
+      const int r = (idx / 8) * 2, c = (idx % 8) * 8;
+      if (kUnits % kThreads == 0 || idx < kUnits) {
+        if (r < rows) load8(x0[j], g + r * gld + c); else zero8(x0[j]);
+        if (r + 1 < rows) load8(x1[j], g + (r + 1) * gld + c); else zero8(x1[j]);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(OpT* lds) const {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int idx = threadIdx.x + j * kThreads;
+      const int r = (idx / 8) * 2, c = (idx % 8) * 8;
+      if (kUnits % kThreads == 0 || idx < kUnits) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if constexpr (sizeof(OpT) == 2) {
+            bf16x2 w;
+            w[0] = (bf16)x0[j][e];
+            w[1] = (bf16)x1[j][e];
+            *reinterpret_cast<bf16x2*>(lds + (c + e) * LD + r) = w;
+          } else {
+            f32x2 w;
+            w[0] = x0[j][e];
+            w[1] = x1[j][e];
+            *reinterpret_cast<f32x2*>(lds + (c + e) * LD + r) = w;
+          }
+        }
+      }
+    }
+  }
+};
 
 }  // namespace gla

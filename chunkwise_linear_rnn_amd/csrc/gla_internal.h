@@ -21,10 +21,11 @@ hipError_t launch_gate_cumsum(int dtype, const void* la, float* g, float* gamma,
                               int dk, int C, hipStream_t s);
 hipError_t launch_state_dot(const float* dST, const float* ST, float* cT, int BH, int dk, int dv,
                             hipStream_t s);
+// chunk totals of D from the scans' cross terms -> tot [BH][N][dk]
 hipError_t launch_gate_carry(const float* crossF, const float* crossR, const float* cT,
-                             float* carry, int BH, int T, int dk, int dv, int C, hipStream_t s);
-hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* carry, void* dla, int BH,
-                            int T, int dk, int C, hipStream_t s);
+                             float* tot, int BH, int T, int dk, int dv, int C, hipStream_t s);
+hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* tot, const float* cT,
+                            void* dla, int BH, int T, int dk, int C, hipStream_t s);
 
 // Inter-chunk state scan.  store: 0 = none, 1 = operand type [dk][dv], 2 = operand type
 // [dv][dk], 3 = fp32 [dk][dv].  With X2T/Y2/cross set, every step also forms the

@@ -1,8 +1,8 @@
-// Backward chunk kernel of the chunkwise GLA path (page "Gated Linear Attention
+// Backward chunk kernels of the chunkwise GLA path (page "Gated Linear Attention
 // Transformers with Hardware-Efficient Training", atlas.scime.ai summary, section
-// Approach: two-level chunking and a closed-form gate gradient).  One workgroup per
-// (batch*head, chunk) computes, from the chunk-start state S_[i] and the state gradient
-// dS_[i+1] produced by the two state scans:
+// Approach: two-level chunking and a closed-form gate gradient).  Per (batch*head,
+// chunk), from the chunk-start state S_[i] and the state gradient dS_[i+1] written by the
+// two state scans:
 //
 //   dA = tril(dO V^T)
 //   dQ = (dO S_[i]^T) * exp(g)           + sum_{s<=t} dA_ts k_s * exp(g_t - g_s)
@@ -20,51 +20,407 @@
 // in fp32 from log-space differences, each exp(g_t - g_s) shared by its dQ and dK terms.
 // The chunk-local suffix sums of D are completed by the gate-gradient kernel with the
 // chunk totals that the two state scans form from their fp32 states.
+//
+// Kernels
+//   k_bwd_dqk  (chunk 64) dq, dk and D.  One pass over 64-wide dv blocks accumulates dA,
+//              dO S^T and V dS^T together: dO and V tiles go through LDS (shared by the 4
+//              waves), each wave's S / dS fragments are prefetched straight into registers
+//              (double-buffered); then the intra-chunk part runs per 64-wide dk block.
+//   k_bwd_dv   (chunk 64) dv = Kh dS + A^T dO per (chunk, 64 values), XCD-aware.
+//   k_bwd_chunk (chunk 128, and fp32 operands) all of the above in one workgroup per
+//              chunk, operands read straight from memory.
 #include "gla_common.cuh"
 #include "gla_internal.h"
 
 namespace gla {
 
-template <typename OpT, typename Tin>
-__device__ __forceinline__ void load_frag_gc(Frag<OpT>& f, const Tin* p, bool valid) {
-  float x[8];
-  if (valid) load8(x, p + 8 * (lane_id() >> 4)); else zero8(x);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f.set(e, x[e]);
-}
-
-// An operand as high part + remainder in the MFMA type (bf16), or as is (fp32).
-template <typename OpT>
-struct SFrag {
-  Frag<OpT> hi, lo;
-  __device__ __forceinline__ void set(int e, float x) {
-    hi.set(e, x);
-    if constexpr (sizeof(OpT) == 2) lo.set(e, x - hi.get(e));
-  }
+// LDS of the intra-chunk / D phase for one dk block of DB columns.
+template <int C, int DB, typename Tin>
+struct IntraLds {
+  static constexpr int FLD = C + 4, GLD = DB + 4, XLD = DB + 8;
+  float* dAs;   // [C][FLD] dA in fp32 (written before the first block)
+  float* gs;    // [C][GLD] g * log2 e
+  Tin* qs;      // [C][XLD]
+  Tin* ks;
+  float* dqd;   // [C][GLD]
+  float* dkd;
+  static constexpr int bytes_blk = C * GLD * 4 * 3 + C * XLD * (int)sizeof(Tin) * 2;
 };
-template <typename OpT>
-__device__ __forceinline__ void mma_split(f32x4& acc, const SFrag<OpT>& a, const SFrag<OpT>& b) {
-  mma(acc, a.hi, b.hi);
-  if constexpr (sizeof(OpT) == 2) {
-    mma(acc, a.hi, b.lo);
-    mma(acc, a.lo, b.hi);
+
+// Stage g (times log2 e; rows past T continue the last valid row), q, k for dk columns
+// [d0, d0 + DB) of the chunk.  Ends with a barrier.
+template <int C, int DB, int DK, typename Tin>
+__device__ __forceinline__ void bwd_stage_block(const IntraLds<C, DB, Tin>& L, const Tin* q,
+                                                const Tin* k, const float* g, long tok0,
+                                                int rows, int d0) {
+  constexpr int GLD = IntraLds<C, DB, Tin>::GLD, XLD = IntraLds<C, DB, Tin>::XLD;
+  for (int idx = threadIdx.x; idx < C * (DB / 8); idx += kThreads) {
+    const int rr = idx / (DB / 8), c = (idx % (DB / 8)) * 8;
+    float x[8];
+    load8(x, g + (tok0 + min(rr, rows - 1)) * DK + d0 + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) L.gs[rr * GLD + c + e] = x[e] * kLog2e;
+  }
+  stage_rows<Tin, Tin, C, DB>(L.qs, XLD, q + tok0 * DK + d0, DK, rows);
+  stage_rows<Tin, Tin, C, DB>(L.ks, XLD, k + tok0 * DK + d0, DK, rows);
+  __syncthreads();
+}
+
+// Given the inter-chunk products dO S^T (adq) and V dS^T (adk) of this block, unscaled,
+// in accumulator layout (wave column tile ct, M-tiles mg + MG*jj), finish dq, dk: decay
+// scaling, intra-chunk terms, output, D suffix sums.  Ends with a barrier.
+template <int C, int DB, int DK, int NMW, int MG, typename Tin, typename OpT>
+__device__ __forceinline__ void bwd_finish_block(const IntraLds<C, DB, Tin>& L,
+                                                 f32x4 (&adq)[NMW], f32x4 (&adk)[NMW],
+                                                 Tin* dq, Tin* dk_out, float* Dloc, long tok0,
+                                                 int rows, int d0, int ct, int mg) {
+  constexpr int NS = C / 16;
+  constexpr int FLD = IntraLds<C, DB, Tin>::FLD, GLD = IntraLds<C, DB, Tin>::GLD,
+                XLD = IntraLds<C, DB, Tin>::XLD;
+  const int l = lane_id(), r = l & 15, qd = l >> 4;
+  const int c = 16 * ct + r;   // column of this lane within the block
+  const float gl = L.gs[(C - 1) * GLD + c];   // gamma * log2 e
+#pragma unroll
+  for (int jj = 0; jj < NMW; ++jj) {
+    const int m = mg + MG * jj;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float gt = L.gs[(16 * m + 4 * qd + e) * GLD + c];
+      adq[jj][e] *= __builtin_amdgcn_exp2f(gt);
+      adk[jj][e] *= __builtin_amdgcn_exp2f(gl - gt);
+    }
+  }
+  // intra-chunk, off-diagonal sub-blocks
+#pragma unroll
+  for (int jj = 0; jj < NMW; ++jj) {
+    const int m = mg + MG * jj;
+    if (m > 0) {   // dq rows of sub-chunk I = m, sources J < I
+      const int rho = 16 * m;
+      const float gr = L.gs[rho * GLD + c];
+      f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < (16 * m + 31) / 32; ++kb) {
+        SFrag<OpT> fa, fb;
+        float xa[8];
+        load8(xa, L.dAs + (16 * m + r) * FLD + kb * 32 + 8 * qd);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int s = kb * 32 + 8 * qd + e;
+          fa.set(e, xa[e]);
+          fb.set(e, s < rho ? to_f32(L.ks[s * XLD + c]) *
+                                  __builtin_amdgcn_exp2f(gr - L.gs[s * GLD + c])
+                            : 0.f);
+        }
+        mma_split(tmp, fa, fb);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        adq[jj][e] += tmp[e] * __builtin_amdgcn_exp2f(L.gs[(rho + 4 * qd + e) * GLD + c] - gr);
+    }
+    if (m < NS - 1) {   // dk rows of sub-chunk J = m, sources I > J
+      const int rho = 16 * m + 15;
+      const float gr = L.gs[rho * GLD + c];
+      f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = (16 * m + 16) / 32; kb < C / 32; ++kb) {
+        SFrag<OpT> fa, fb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = kb * 32 + 8 * qd + e;
+          const bool on = t > rho;
+          fa.set(e, on ? L.dAs[t * FLD + 16 * m + r] : 0.f);
+          fb.set(e, on ? to_f32(L.qs[t * XLD + c]) * __builtin_amdgcn_exp2f(L.gs[t * GLD + c] - gr)
+                       : 0.f);
+        }
+        mma_split(tmp, fa, fb);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        adk[jj][e] += tmp[e] * __builtin_amdgcn_exp2f(gr - L.gs[(16 * m + 4 * qd + e) * GLD + c]);
+    }
+  }
+  // intra-chunk, diagonal sub-blocks: one thread per (sub-chunk, column)
+  {
+    const int m = threadIdx.x / DB, cc = threadIdx.x % DB, base = 16 * m;
+    float gt[16], qv[16], kv[16], aq[16], ak[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      gt[j] = L.gs[(base + j) * GLD + cc];
+      qv[j] = to_f32(L.qs[(base + j) * XLD + cc]);
+      kv[j] = to_f32(L.ks[(base + j) * XLD + cc]);
+      aq[j] = 0.f;
+      ak[j] = 0.f;
+    }
+    const float* dAm = L.dAs + base * FLD + base;
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+#pragma unroll
+      for (int s = 0; s <= t; ++s) {
+        const float ex = __builtin_amdgcn_exp2f(gt[t] - gt[s]) * dAm[t * FLD + s];
+        aq[t] += ex * kv[s];
+        ak[s] += ex * qv[t];
+      }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      L.dqd[(base + j) * GLD + cc] = aq[j];
+      L.dkd[(base + j) * GLD + cc] = ak[j];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int jj = 0; jj < NMW; ++jj) {
+    const int m = mg + MG * jj;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * m + 4 * qd + e;
+      adq[jj][e] += L.dqd[t * GLD + c];
+      adk[jj][e] += L.dkd[t * GLD + c];
+    }
+  }
+  __syncthreads();
+  // finish dq, dk; D = q*dq - k*dk into dqd
+#pragma unroll
+  for (int jj = 0; jj < NMW; ++jj) {
+    const int m = mg + MG * jj;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * m + 4 * qd + e;
+      if (t < rows) {
+        dq[(tok0 + t) * DK + d0 + c] = from_f32<Tin>(adq[jj][e]);
+        dk_out[(tok0 + t) * DK + d0 + c] = from_f32<Tin>(adk[jj][e]);
+      }
+      L.dqd[t * GLD + c] =
+          to_f32(L.qs[t * XLD + c]) * adq[jj][e] - to_f32(L.ks[t * XLD + c]) * adk[jj][e];
+    }
+  }
+  __syncthreads();
+  // chunk-local suffix sums of D, column by column (segmented)
+  {
+    constexpr int NSEG = kThreads / DB, SL = C / NSEG;
+    const int col = threadIdx.x % DB, seg = threadIdx.x / DB;
+    float run = 0.f;
+    for (int rr = seg * SL + SL - 1; rr >= seg * SL; --rr) {
+      run += L.dqd[rr * GLD + col];
+      L.dqd[rr * GLD + col] = run;
+    }
+    L.dkd[seg * DB + col] = run;
+    __syncthreads();
+    float off = 0.f;
+    for (int s2 = seg + 1; s2 < NSEG; ++s2) off += L.dkd[s2 * DB + col];
+    for (int rr = seg * SL; rr < seg * SL + SL; ++rr)
+      if (rr < rows) Dloc[(tok0 + rr) * DK + d0 + col] = L.dqd[rr * GLD + col] + off;
+  }
+  __syncthreads();
+}
+
+// =====================================================================================
+// chunk 64: k_bwd_dqk
+// =====================================================================================
+template <typename Tin, typename OpT, int DK>
+__global__ __launch_bounds__(kThreads) void k_bwd_dqk(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const Tin* __restrict__ dO, const float* __restrict__ g, const OpT* __restrict__ S,
+    const OpT* __restrict__ dS, Tin* __restrict__ dq, Tin* __restrict__ dk_out,
+    float* __restrict__ Dloc, int T, int dv, int N) {
+  static_assert(sizeof(Tin) == sizeof(OpT), "input and operand types match");
+  constexpr int C = 64, NM = 4, NJ = DK / 64, DB = 64, YLD = 64 + 8;
+  using IL = IntraLds<C, DB, Tin>;
+  constexpr int o_dA = 0;
+  constexpr int o_p = C * IL::FLD * 4;
+  constexpr int b1 = 2 * C * YLD * (int)sizeof(OpT);
+  constexpr int bytes = o_p + (b1 > IL::bytes_blk ? b1 : IL::bytes_blk);
+  __shared__ __attribute__((aligned(16))) char arena[bytes];
+  OpT* dOs = (OpT*)(arena + o_p);
+  OpT* Vs = dOs + C * YLD;
+  IL L;
+  L.dAs = (float*)(arena + o_dA);
+  L.gs = (float*)(arena + o_p);
+  L.qs = (Tin*)(arena + o_p + C * IL::GLD * 4);
+  L.ks = L.qs + C * IL::XLD;
+  L.dqd = (float*)(L.ks + C * IL::XLD);
+  L.dkd = L.dqd + C * IL::GLD;
+
+  const int i = blockIdx.x, bh = blockIdx.y;
+  const int t0 = i * C, rows = min(C, T - t0);
+  const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
+  const long tok0 = (long)bh * T + t0;
+  const OpT* Si = S + ((long)bh * N + i) * DK * dv;
+  const OpT* dSi = dS + ((long)bh * N + i) * DK * dv;
+  const int NV = dv / 64;
+
+  f32x4 adq[NJ][NM], adk[NJ][NM], adA[NM];   // adA[n] = dA tile (w, n), n <= w
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      adq[j][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      adk[j][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+  for (int n = 0; n < NM; ++n) adA[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  RowTile<OpT, C, 64, YLD> tdO, tV;
+  Frag<OpT> sA[NJ][2], dsA[NJ][2], sB[NJ][2], dsB[NJ][2];
+  auto fetch = [&](int vb, Frag<OpT> (&fs)[NJ][2], Frag<OpT> (&fds)[NJ][2]) {
+    tdO.load((const OpT*)dO + tok0 * dv + vb * 64, dv, rows);
+    tV.load((const OpT*)v + tok0 * dv + vb * 64, dv, rows);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const long off = (long)(64 * j + 16 * w + r) * dv + vb * 64 + kb * 32;
+        load_frag_c(fs[j][kb], Si + off);
+        load_frag_c(fds[j][kb], dSi + off);
+      }
+  };
+  auto body = [&](int vb, Frag<OpT> (&fs)[NJ][2], Frag<OpT> (&fds)[NJ][2],
+                  Frag<OpT> (&ns)[NJ][2], Frag<OpT> (&nds)[NJ][2]) {
+    tdO.store(dOs);
+    tV.store(Vs);
+    __syncthreads();
+    if (vb + 1 < NV) fetch(vb + 1, ns, nds);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      Frag<OpT> fO[NM], fV[NM], fOw;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        load_frag_c(fO[m], dOs + (16 * m + r) * YLD + kb * 32);
+        load_frag_c(fV[m], Vs + (16 * m + r) * YLD + kb * 32);
+      }
+      load_frag_c(fOw, dOs + (16 * w + r) * YLD + kb * 32);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          mma(adq[j][m], fO[m], fs[j][kb]);
+          mma(adk[j][m], fV[m], fds[j][kb]);
+        }
+#pragma unroll
+      for (int n = 0; n < NM; ++n)
+        if (n <= w) mma(adA[n], fOw, fV[n]);
+    }
+    __syncthreads();
+  };
+  fetch(0, sA, dsA);
+  int vb = 0;
+  for (; vb + 1 < NV; vb += 2) {
+    body(vb, sA, dsA, sB, dsB);
+    body(vb + 1, sB, dsB, sA, dsA);
+  }
+  if (vb < NV) body(vb, sA, dsA, sB, dsB);
+
+  // dA tiles (w, n <= w) to LDS, diagonal tile masked above the diagonal
+#pragma unroll
+  for (int n = 0; n < NM; ++n)
+    if (n <= w) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tl = 4 * qd + e;
+        L.dAs[(16 * w + tl) * IL::FLD + 16 * n + r] = (n == w && r > tl) ? 0.f : adA[n][e];
+      }
+    }
+
+  // intra-chunk part and D, per 64-wide dk block (wave w: columns 16w.. of each block)
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    bwd_stage_block<C, DB, DK, Tin>(L, q, k, g, tok0, rows, 64 * j);
+    bwd_finish_block<C, DB, DK, NM, 1, Tin, OpT>(L, adq[j], adk[j], dq, dk_out, Dloc, tok0, rows,
+                                                 64 * j, w, 0);
   }
 }
 
+// =====================================================================================
+// chunk 64: k_bwd_dv
+// =====================================================================================
+template <typename Tin, typename OpT, int DK>
+__global__ __launch_bounds__(kThreads) void k_bwd_dv(const OpT* __restrict__ Kh,
+                                                     const OpT* __restrict__ A,
+                                                     const OpT* __restrict__ dS,
+                                                     const Tin* __restrict__ dO,
+                                                     Tin* __restrict__ dv_out, int T, int dv,
+                                                     int N) {
+  constexpr int C = 64, NM = 4, KLD = DK + 8, ALD = C + 8, SLD = DK + 8, OLD = C + 8,
+                ULD = 64 + 8;
+  __shared__ __attribute__((aligned(16))) OpT ksh[C * KLD];
+  __shared__ __attribute__((aligned(16))) OpT aT[C * ALD];
+  __shared__ __attribute__((aligned(16))) OpT dsT[64 * SLD];
+  __shared__ __attribute__((aligned(16))) OpT doT[64 * OLD];
+  // XCD-aware: the dv tiles of one chunk share Kh and A
+  const int nvt = dv / 64;
+  const int lt = xcd_logical(blockIdx.x, gridDim.x);
+  const int vt = lt % nvt, i = (lt / nvt) % N, bh = lt / (nvt * N);
+  const int v0 = vt * 64, t0 = i * C, rows = min(C, T - t0);
+  const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
+  {
+    FlatTile<OpT, C, DK, KLD> tk;
+    tk.load(Kh + ((long)bh * N * C + t0) * DK);
+    ColTile<OpT, OpT, C, ALD> ta;
+    ta.load(A + ((long)bh * N + i) * C * C, C, C);
+    tk.store(ksh);
+    ta.store(aT);
+  }
+  {
+    ColTile<OpT, OpT, DK, SLD> ts;
+    ts.load(dS + ((long)bh * N + i) * DK * dv + v0, dv, DK);
+    ColTile<OpT, Tin, C, OLD> to;
+    to.load(dO + ((long)bh * T + t0) * dv + v0, dv, rows);
+    ts.store(dsT);
+    to.store(doT);
+  }
+  __syncthreads();
+  f32x4 acc[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < DK / 32; ++kb) {
+    Frag<OpT> fb;
+    load_frag_c(fb, dsT + (16 * w + r) * SLD + kb * 32);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      Frag<OpT> fa;
+      load_frag_c(fa, ksh + (16 * m + r) * KLD + kb * 32);
+      mma(acc[m], fa, fb);
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < C / 32; ++kb) {
+    Frag<OpT> fb;
+    load_frag_c(fb, doT + (16 * w + r) * OLD + kb * 32);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if (32 * kb + 31 >= 16 * m) {
+        Frag<OpT> fa;
+        load_frag_c(fa, aT + (16 * m + r) * ALD + kb * 32);
+        mma(acc[m], fa, fb);
+      }
+    }
+  }
+  __syncthreads();
+  Tin* outs = (Tin*)ksh;   // reuse as [C][ULD]
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      outs[(16 * m + 4 * qd + e) * ULD + 16 * w + r] = from_f32<Tin>(acc[m][e]);
+  __syncthreads();
+  constexpr int kPer = 16 / (int)sizeof(Tin), kUnits = C * 64 / kPer;
+  for (int idx = threadIdx.x; idx < kUnits; idx += kThreads) {
+    const int e0 = idx * kPer, rr = e0 / 64, cc = e0 % 64;
+    if (rr < rows)
+      *reinterpret_cast<u32x4*>(dv_out + ((long)bh * T + t0 + rr) * dv + v0 + cc) =
+          *reinterpret_cast<const u32x4*>(outs + rr * ULD + cc);
+  }
+}
+
+// =====================================================================================
+// chunk 128: k_bwd_chunk (everything in one workgroup per chunk)
+// =====================================================================================
 template <int C, int DK, typename Tin, typename OpT>
 struct BwdLds {
-  static constexpr int NS = C / 16;
   static constexpr int DB = (C == 64) ? 64 : 32;
-  static constexpr int ALD = C + 8, FLD = C + 4, GLD = DB + 4, XLD = DB + 8;
-  // phase 1-2 (dA in fp32)
+  using IL = IntraLds<C, DB, Tin>;
+  static constexpr int ALD = C + 8;
   static constexpr int o_dA = 0;
-  static constexpr int o_g = o_dA + C * FLD * 4;
-  static constexpr int o_q = o_g + C * GLD * 4;
-  static constexpr int o_k = o_q + C * XLD * (int)sizeof(Tin);
-  static constexpr int o_dqd = o_k + C * XLD * (int)sizeof(Tin);
-  static constexpr int o_dkd = o_dqd + C * GLD * 4;
-  static constexpr int end12 = o_dkd + C * GLD * 4;
-  // phase 3
+  static constexpr int o_blk = o_dA + C * IL::FLD * 4;
+  static constexpr int end12 = o_blk + IL::bytes_blk;
   static constexpr int o_AT = 0;
   static constexpr int o_dOT = o_AT + C * ALD * (int)sizeof(OpT);
   static constexpr int o_dST = o_dOT + 64 * ALD * (int)sizeof(OpT);
@@ -79,24 +435,25 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(
     const OpT* __restrict__ Kh, const OpT* __restrict__ S, const OpT* __restrict__ dS,
     Tin* __restrict__ dq, Tin* __restrict__ dk_out, Tin* __restrict__ dv_out,
     float* __restrict__ Dloc, int T, int dv, int N) {
-  using L = BwdLds<C, DK, Tin, OpT>;
-  constexpr int NS = L::NS, NM = C / 16, DB = L::DB, ALD = L::ALD, FLD = L::FLD, GLD = L::GLD,
-                XLD = L::XLD;
+  using BL = BwdLds<C, DK, Tin, OpT>;
+  using IL = typename BL::IL;
+  constexpr int NM = C / 16, DB = BL::DB, ALD = BL::ALD, FLD = IL::FLD;
   constexpr int CT = DB / 16, MG = 4 / CT, NMW = NM / MG;
-  __shared__ __attribute__((aligned(16))) char arena[L::bytes];
-  float* dAs = (float*)(arena + L::o_dA);
-  float* gs = (float*)(arena + L::o_g);
-  Tin* qs = (Tin*)(arena + L::o_q);
-  Tin* ks = (Tin*)(arena + L::o_k);
-  float* dqd = (float*)(arena + L::o_dqd);
-  float* dkd = (float*)(arena + L::o_dkd);
+  __shared__ __attribute__((aligned(16))) char arena[BL::bytes];
+  IL L;
+  L.dAs = (float*)(arena + BL::o_dA);
+  L.gs = (float*)(arena + BL::o_blk);
+  L.qs = (Tin*)(arena + BL::o_blk + C * IL::GLD * 4);
+  L.ks = L.qs + C * IL::XLD;
+  L.dqd = (float*)(L.ks + C * IL::XLD);
+  L.dkd = L.dqd + C * IL::GLD;
 
   const int i = blockIdx.x, bh = blockIdx.y;
   const int t0 = i * C, rows = min(C, T - t0);
   const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
-  const long tok0 = (long)bh * T + t0;   // row index of the chunk's first token
+  const long tok0 = (long)bh * T + t0;
 
-  // ---------------- phase 1: dA = tril(dO V^T) -------------------------------------
+  // phase 1: dA = tril(dO V^T)
   {
     constexpr int NT = NM * (NM + 1) / 2;
     for (int p = w; p < NT; p += 4) {
@@ -116,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tl = 4 * qd + e;
-        dAs[(16 * m + tl) * FLD + 16 * n + r] = (m == n && r > tl) ? 0.f : acc[e];
+        L.dAs[(16 * m + tl) * FLD + 16 * n + r] = (m == n && r > tl) ? 0.f : acc[e];
       }
     }
   }
@@ -125,182 +482,42 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(
   const OpT* Si = S + ((long)bh * N + i) * DK * dv;
   const OpT* dSi = dS + ((long)bh * N + i) * DK * dv;
 
-  // ---------------- phase 2: dq, dk, D per dk block --------------------------------
+  // phase 2: dq, dk, D per dk block
   for (int d0 = 0; d0 < DK; d0 += DB) {
-    for (int idx = threadIdx.x; idx < C * (DB / 8); idx += kThreads) {
-      const int rr = idx / (DB / 8), c = (idx % (DB / 8)) * 8;
-      float x[8];
-      load8(x, g + (tok0 + min(rr, rows - 1)) * DK + d0 + c);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gs[rr * GLD + c + e] = x[e] * kLog2e;
-    }
-    stage_rows<Tin, Tin, C, DB>(qs, XLD, q + tok0 * DK + d0, DK, rows);
-    stage_rows<Tin, Tin, C, DB>(ks, XLD, k + tok0 * DK + d0, DK, rows);
-    __syncthreads();
-
-    const int c = 16 * ct + r;   // column of this lane within the block
+    bwd_stage_block<C, DB, DK, Tin>(L, q, k, g, tok0, rows, d0);
+    const int c = 16 * ct + r;
     f32x4 adq[NMW], adk[NMW];
 #pragma unroll
     for (int jj = 0; jj < NMW; ++jj) {
       adq[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
       adk[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // inter-chunk parts: dO S^T and V dS^T (contract over dv)
-    {
-      const OpT* sp = Si + (long)(d0 + c) * dv;
-      const OpT* dsp = dSi + (long)(d0 + c) * dv;
-      for (int kb = 0; kb < dv / 32; ++kb) {
-        Frag<OpT> fS, fdS;
-        load_frag_c(fS, sp + kb * 32);
-        load_frag_c(fdS, dsp + kb * 32);
+    const OpT* sp = Si + (long)(d0 + c) * dv;
+    const OpT* dsp = dSi + (long)(d0 + c) * dv;
+    for (int kb = 0; kb < dv / 32; ++kb) {
+      Frag<OpT> fS, fdS;
+      load_frag_c(fS, sp + kb * 32);
+      load_frag_c(fdS, dsp + kb * 32);
 #pragma unroll
-        for (int jj = 0; jj < NMW; ++jj) {
-          const int m = mg + MG * jj;
-          const bool valid = 16 * m + r < rows;
-          Frag<OpT> fa;
-          load_frag_gc(fa, dO + (tok0 + 16 * m + r) * dv + kb * 32, valid);
-          mma(adq[jj], fa, fS);
-          load_frag_gc(fa, v + (tok0 + 16 * m + r) * dv + kb * 32, valid);
-          mma(adk[jj], fa, fdS);
-        }
+      for (int jj = 0; jj < NMW; ++jj) {
+        const int m = mg + MG * jj;
+        const bool valid = 16 * m + r < rows;
+        Frag<OpT> fa;
+        load_frag_gc(fa, dO + (tok0 + 16 * m + r) * dv + kb * 32, valid);
+        mma(adq[jj], fa, fS);
+        load_frag_gc(fa, v + (tok0 + 16 * m + r) * dv + kb * 32, valid);
+        mma(adk[jj], fa, fdS);
       }
     }
-    const float gl = gs[(C - 1) * GLD + c];   // gamma * log2 e
-#pragma unroll
-    for (int jj = 0; jj < NMW; ++jj) {
-      const int m = mg + MG * jj;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float gt = gs[(16 * m + 4 * qd + e) * GLD + c];
-        adq[jj][e] *= __builtin_amdgcn_exp2f(gt);
-        adk[jj][e] *= __builtin_amdgcn_exp2f(gl - gt);
-      }
-    }
-    // intra-chunk, off-diagonal sub-blocks
-#pragma unroll
-    for (int jj = 0; jj < NMW; ++jj) {
-      const int m = mg + MG * jj;
-      if (m > 0) {   // dq rows of sub-chunk I = m, sources J < I
-        const int rho = 16 * m;
-        const float gr = gs[rho * GLD + c];
-        f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = 0; kb < (16 * m + 31) / 32; ++kb) {
-          SFrag<OpT> fa, fb;
-          float xa[8];
-          load8(xa, dAs + (16 * m + r) * FLD + kb * 32 + 8 * qd);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int s = kb * 32 + 8 * qd + e;
-            fa.set(e, xa[e]);
-            fb.set(e, s < rho ? to_f32(ks[s * XLD + c]) *
-                                    __builtin_amdgcn_exp2f(gr - gs[s * GLD + c])
-                              : 0.f);
-          }
-          mma_split(tmp, fa, fb);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          adq[jj][e] += tmp[e] * __builtin_amdgcn_exp2f(gs[(rho + 4 * qd + e) * GLD + c] - gr);
-      }
-      if (m < NS - 1) {   // dk rows of sub-chunk J = m, sources I > J
-        const int rho = 16 * m + 15;
-        const float gr = gs[rho * GLD + c];
-        f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = (16 * m + 16) / 32; kb < C / 32; ++kb) {
-          SFrag<OpT> fa, fb;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int t = kb * 32 + 8 * qd + e;
-            const bool on = t > rho;
-            fa.set(e, on ? dAs[t * FLD + 16 * m + r] : 0.f);
-            fb.set(e, on ? to_f32(qs[t * XLD + c]) * __builtin_amdgcn_exp2f(gs[t * GLD + c] - gr)
-                         : 0.f);
-          }
-          mma_split(tmp, fa, fb);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          adk[jj][e] += tmp[e] * __builtin_amdgcn_exp2f(gr - gs[(16 * m + 4 * qd + e) * GLD + c]);
-      }
-    }
-    // intra-chunk, diagonal sub-blocks: one thread per (sub-chunk, column)
-    {
-      const int m = threadIdx.x / DB, cc = threadIdx.x % DB, base = 16 * m;
-      float gt[16], qv[16], kv[16], aq[16], ak[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        gt[j] = gs[(base + j) * GLD + cc];
-        qv[j] = to_f32(qs[(base + j) * XLD + cc]);
-        kv[j] = to_f32(ks[(base + j) * XLD + cc]);
-        aq[j] = 0.f;
-        ak[j] = 0.f;
-      }
-      const float* dAm = dAs + base * FLD + base;
-#pragma unroll
-      for (int t = 0; t < 16; ++t)
-#pragma unroll
-        for (int s = 0; s <= t; ++s) {
-          const float ex = __builtin_amdgcn_exp2f(gt[t] - gt[s]) * dAm[t * FLD + s];
-          aq[t] += ex * kv[s];
-          ak[s] += ex * qv[t];
-        }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        dqd[(base + j) * GLD + cc] = aq[j];
-        dkd[(base + j) * GLD + cc] = ak[j];
-      }
-    }
-    __syncthreads();
-    // finish dq, dk; D = q*dq - k*dk into dqd
-#pragma unroll
-    for (int jj = 0; jj < NMW; ++jj) {
-      const int m = mg + MG * jj;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * m + 4 * qd + e;
-        adq[jj][e] += dqd[t * GLD + c];
-        adk[jj][e] += dkd[t * GLD + c];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int jj = 0; jj < NMW; ++jj) {
-      const int m = mg + MG * jj;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * m + 4 * qd + e;
-        if (t < rows) {
-          dq[(tok0 + t) * DK + d0 + c] = from_f32<Tin>(adq[jj][e]);
-          dk_out[(tok0 + t) * DK + d0 + c] = from_f32<Tin>(adk[jj][e]);
-        }
-        dqd[t * GLD + c] = to_f32(qs[t * XLD + c]) * adq[jj][e] - to_f32(ks[t * XLD + c]) * adk[jj][e];
-      }
-    }
-    __syncthreads();
-    // chunk-local suffix sums of D, column by column (segmented)
-    {
-      constexpr int NSEG = kThreads / DB, SL = C / NSEG;
-      const int col = threadIdx.x % DB, seg = threadIdx.x / DB;
-      float run = 0.f;
-      for (int rr = seg * SL + SL - 1; rr >= seg * SL; --rr) {
-        run += dqd[rr * GLD + col];
-        dqd[rr * GLD + col] = run;
-      }
-      dkd[seg * DB + col] = run;
-      __syncthreads();
-      float off = 0.f;
-      for (int s2 = seg + 1; s2 < NSEG; ++s2) off += dkd[s2 * DB + col];
-      for (int rr = seg * SL; rr < seg * SL + SL; ++rr)
-        if (rr < rows) Dloc[(tok0 + rr) * DK + d0 + col] = dqd[rr * GLD + col] + off;
-    }
-    __syncthreads();
+    bwd_finish_block<C, DB, DK, NMW, MG, Tin, OpT>(L, adq, adk, dq, dk_out, Dloc, tok0, rows, d0,
+                                                   ct, mg);
   }
 
-  // ---------------- phase 3: dv = Kh dS_[i+1] + A^T dO ------------------------------
+  // phase 3: dv = Kh dS_[i+1] + A^T dO
   {
-    OpT* ATs = (OpT*)(arena + L::o_AT);
-    OpT* dOT = (OpT*)(arena + L::o_dOT);
-    OpT* dST = (OpT*)(arena + L::o_dST);
+    OpT* ATs = (OpT*)(arena + BL::o_AT);
+    OpT* dOT = (OpT*)(arena + BL::o_dOT);
+    OpT* dST = (OpT*)(arena + BL::o_dST);
     constexpr int SLD = DK + 8;
     stage_cols<OpT, OpT, C, C>(ATs, ALD, A + ((long)bh * N + i) * C * C, C, C);
     const OpT* khp = Kh + ((long)bh * N * C + t0) * DK;
@@ -350,12 +567,24 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(
 // ---------------------------------------------------------------------------------
 template <typename Tin, typename OpT, int C, int DK>
 static hipError_t launch_bwd_t2(const BwdArgs& a, hipStream_t s) {
-  dim3 grid(a.N, a.BH);
-  hipLaunchKernelGGL((k_bwd_chunk<Tin, OpT, C, DK>), grid, dim3(kThreads), 0, s,
-                     (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,
-                     (const OpT*)a.A, (const OpT*)a.Kh, (const OpT*)a.S, (const OpT*)a.dS,
-                     (Tin*)a.dq, (Tin*)a.dk_out, (Tin*)a.dv_out, a.Dloc, a.T, a.dv, a.N);
-  return hipGetLastError();
+  if constexpr (C == 64 && sizeof(OpT) == 2) {
+    hipLaunchKernelGGL((k_bwd_dqk<Tin, OpT, DK>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
+                       (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,
+                       (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq, (Tin*)a.dk_out, a.Dloc, a.T,
+                       a.dv, a.N);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_bwd_dv<Tin, OpT, DK>), dim3((a.dv / 64) * a.N * a.BH), dim3(kThreads), 0,
+                       s, (const OpT*)a.Kh, (const OpT*)a.A, (const OpT*)a.dS, (const Tin*)a.dO,
+                       (Tin*)a.dv_out, a.T, a.dv, a.N);
+    return hipGetLastError();
+  } else {
+    hipLaunchKernelGGL((k_bwd_chunk<Tin, OpT, C, DK>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
+                       (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,
+                       (const OpT*)a.A, (const OpT*)a.Kh, (const OpT*)a.S, (const OpT*)a.dS,
+                       (Tin*)a.dq, (Tin*)a.dk_out, (Tin*)a.dv_out, a.Dloc, a.T, a.dv, a.N);
+    return hipGetLastError();
+  }
 }
 template <typename Tin, typename OpT, int C>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {

@@ -10,6 +10,11 @@
 //                O_i = Qh_i S + A_i V_i, then S <- diag(exp(gamma_i)) S + Kh_i^T V_i.  No
 //                per-chunk state ever reaches memory.  The state accumulators feed the
 //                Qh S product directly as the MFMA B operand (acc-order fragments).
+//                Chunk 64: each chunk's Qh, Kh^T, A and V^T tiles are staged into LDS
+//                with cooperative 16-byte loads, the next chunk's tiles are loaded into
+//                registers while the current one computes, and O leaves through LDS as
+//                16-byte row stores.  Chunk 128 and fp32 operands (tiles too large for
+//                LDS) read the operand fragments straight from memory.
 #include "gla_common.cuh"
 #include "gla_internal.h"
 
@@ -24,7 +29,10 @@ __global__ __launch_bounds__(kThreads) void k_output(const OpT* __restrict__ Qh,
                                                      int N) {
   constexpr int TV = 64, VLD = C + 8, NM = C / 16;
   __shared__ __attribute__((aligned(16))) OpT vs[TV * VLD];
-  const int v0 = blockIdx.x * TV, i = blockIdx.y, bh = blockIdx.z;
+  // 1-D grid, XCD-aware: the dv tiles of one chunk share Qh and A
+  const int nvt = dv / TV;
+  const int lt = xcd_logical(blockIdx.x, gridDim.x);
+  const int v0 = (lt % nvt) * TV, i = (lt / nvt) % N, bh = lt / (nvt * N);
   const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
   const int t0 = i * C, rows = min(C, T - t0);
 
@@ -71,13 +79,136 @@ __global__ __launch_bounds__(kThreads) void k_output(const OpT* __restrict__ Qh,
 }
 
 template <typename Tin, typename OpT, int C, int DK>
+__global__ __launch_bounds__(kThreads) void k_fwd_fused_staged(
+    const OpT* __restrict__ Qh, const OpT* __restrict__ KhT, const OpT* __restrict__ A,
+    const float* __restrict__ eg, const Tin* __restrict__ V, const float* __restrict__ S0,
+    Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N) {
+  constexpr int TV = 64, NM = C / 16, NP = DK / 16;
+  constexpr int QLD = DK + 8, KLD = C + 8, ALD = C + 8, VLD = C + 8, OLD = TV + 8;
+  __shared__ __attribute__((aligned(16))) OpT qs[C * QLD];
+  __shared__ __attribute__((aligned(16))) OpT ks[DK * KLD];
+  __shared__ __attribute__((aligned(16))) OpT as_[C * ALD];
+  __shared__ __attribute__((aligned(16))) OpT vs[TV * VLD];
+  __shared__ __attribute__((aligned(16))) Tin os_[C * OLD];
+  __shared__ float egs[DK];
+  // 1-D grid, XCD-aware: the dv tiles of one bh share every Qh / Kh^T / A tile
+  const int nvt = dv / TV;
+  const int lt = xcd_logical(blockIdx.x, gridDim.x);
+  const int v0 = (lt % nvt) * TV, bh = lt / nvt;
+  const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
+  const int col = v0 + 16 * w + r;
+
+  f32x4 S[NP];   // S[p][e] = state[16p + 4qd + e][col]
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      S[p][e] = S0 ? S0[((long)bh * DK + 16 * p + 4 * qd + e) * dv + col] : 0.f;
+
+  FlatTile<OpT, C, DK, QLD> tq;
+  FlatTile<OpT, DK, C, KLD> tk;
+  FlatTile<OpT, C, C, ALD> ta;
+  ColTile<OpT, Tin, C, VLD> tv;
+  float egr = 0.f;
+  auto fetch = [&](int i) {
+    const int t0 = i * C;
+    tq.load(Qh + ((long)bh * N * C + t0) * DK);
+    tk.load(KhT + ((long)bh * N + i) * DK * C);
+    ta.load(A + ((long)bh * N + i) * C * C);
+    tv.load(V + ((long)bh * T + t0) * dv + v0, dv, min(C, T - t0));
+    if (threadIdx.x < DK) egr = eg[((long)bh * N + i) * DK + threadIdx.x];
+  };
+  if (N > 0) fetch(0);
+
+  for (int i = 0; i < N; ++i) {
+    const int t0 = i * C, rows = min(C, T - t0);
+    tq.store(qs);
+    tk.store(ks);
+    ta.store(as_);
+    tv.store(vs);
+    if (threadIdx.x < DK) egs[threadIdx.x] = egr;
+    __syncthreads();
+    if (i + 1 < N) fetch(i + 1);
+
+    // O_i = Qh_i S + A_i V_i
+    f32x4 acc[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      Frag<OpT> fb;
+      frag_from_acc(fb, S[2 * kb], S[2 * kb + 1]);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        Frag<OpT> fa;
+        load_frag_a(fa, qs + (16 * m + r) * QLD + kb * 32);
+        mma(acc[m], fa, fb);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < C / 32; ++kb) {
+      Frag<OpT> fb;
+      load_frag_c(fb, vs + (16 * w + r) * VLD + kb * 32);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        if (32 * kb <= 16 * m + 15) {
+          Frag<OpT> fa;
+          load_frag_c(fa, as_ + (16 * m + r) * ALD + kb * 32);
+          mma(acc[m], fa, fb);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) os_[(16 * m + 4 * qd + e) * OLD + 16 * w + r] = from_f32<Tin>(acc[m][e]);
+
+    // S <- diag(exp(gamma_i)) S + Kh_i^T V_i
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const f32x4 dec = *reinterpret_cast<const f32x4*>(egs + 16 * p + 4 * qd);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[p][e] *= dec[e];
+    }
+#pragma unroll
+    for (int kb = 0; kb < C / 32; ++kb) {
+      Frag<OpT> fb;
+      load_frag_c(fb, vs + (16 * w + r) * VLD + kb * 32);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        Frag<OpT> fa;
+        load_frag_c(fa, ks + (16 * p + r) * KLD + kb * 32);
+        mma(S[p], fa, fb);
+      }
+    }
+    __syncthreads();
+    // O tile out: C rows x 64 values, 16-byte row pieces
+    constexpr int kPer = 16 / (int)sizeof(Tin), kUnits = C * TV / kPer;
+    for (int idx = threadIdx.x; idx < kUnits; idx += kThreads) {
+      const int e0 = idx * kPer, rr = e0 / TV, cc = e0 % TV;
+      if (rr < rows)
+        *reinterpret_cast<u32x4*>(O + ((long)bh * T + t0 + rr) * dv + v0 + cc) =
+            *reinterpret_cast<const u32x4*>(os_ + rr * OLD + cc);
+    }
+  }
+  if (S_T) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S_T[((long)bh * DK + 16 * p + 4 * qd + e) * dv + col] = S[p][e];
+  }
+}
+
+template <typename Tin, typename OpT, int C, int DK>
 __global__ __launch_bounds__(kThreads) void k_fwd_fused(
     const OpT* __restrict__ Qh, const OpT* __restrict__ KhT, const OpT* __restrict__ A,
     const float* __restrict__ eg, const Tin* __restrict__ V, const float* __restrict__ S0,
     Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N) {
   constexpr int TV = 64, VLD = C + 8, NM = C / 16, NP = DK / 16;
   __shared__ __attribute__((aligned(16))) OpT vs[TV * VLD];
-  const int v0 = blockIdx.x * TV, bh = blockIdx.y;
+  const int nvt = dv / TV;
+  const int lt = xcd_logical(blockIdx.x, gridDim.x);
+  const int v0 = (lt % nvt) * TV, bh = lt / nvt;
   const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
   const int col = v0 + 16 * w + r;
 
@@ -164,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd_fused(
 // ---------------------------------------------------------------------------------
 template <typename Tin, typename OpT, int C>
 static hipError_t launch_output_t(const OutArgs& a, hipStream_t s) {
-  dim3 grid(a.dv / 64, a.N, a.BH);
+  dim3 grid((a.dv / 64) * a.N * a.BH);
   hipLaunchKernelGGL((k_output<Tin, OpT, C>), grid, dim3(kThreads), 0, s, (const OpT*)a.Qh,
                      (const OpT*)a.A, (const OpT*)a.STt, (const Tin*)a.v, (Tin*)a.o, a.T, a.dk,
                      a.dv, a.N);
@@ -183,7 +314,13 @@ hipError_t launch_output(const OutArgs& a, hipStream_t s) {
 
 template <typename Tin, typename OpT, int C, int DK>
 static hipError_t launch_fused_t2(const FusedArgs& a, hipStream_t s) {
-  dim3 grid(a.dv / 64, a.BH);
+  dim3 grid((a.dv / 64) * a.BH);
+  if constexpr (C == 64 && sizeof(OpT) == 2) {
+    hipLaunchKernelGGL((k_fwd_fused_staged<Tin, OpT, C, DK>), grid, dim3(kThreads), 0, s,
+                       (const OpT*)a.Qh, (const OpT*)a.KhT, (const OpT*)a.A, a.eg,
+                       (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((k_fwd_fused<Tin, OpT, C, DK>), grid, dim3(kThreads), 0, s,
                      (const OpT*)a.Qh, (const OpT*)a.KhT, (const OpT*)a.A, a.eg,
                      (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N);

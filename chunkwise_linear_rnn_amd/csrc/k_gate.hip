@@ -4,7 +4,7 @@
 //                     chunkwise form) and the chunk totals gamma.
 //   k_state_dot       c_T[d] = sum_v dS_T[d,v] * S_T[d,v], the final-state term of the
 //                     closed-form gate gradient.
-//   k_gate_carry,     the closed-form gate gradient: a reverse cumulative sum over the
+//   k_gate_tot,       the closed-form gate gradient: a reverse cumulative sum over the
 //   k_gate_grad       whole sequence of D = q*dq - k*dk plus c_T, taken in two levels:
 //                     chunk-local suffix sums come from the backward chunk kernel, the
 //                     suffix over later chunks from the chunk totals the state scans form.
@@ -19,14 +19,21 @@ __global__ __launch_bounds__(kThreads) void k_gate_cumsum(const Tin* __restrict_
                                                           float* __restrict__ g,
                                                           float* __restrict__ gamma, int T,
                                                           int dk, int C, int N) {
+  constexpr int U = 16;   // rows loaded per batch, so the loads are in flight together
   const int i = blockIdx.x, bh = blockIdx.y;
   const int t0 = i * C, t1 = min(T, t0 + C);
   const long base = (long)bh * T * dk;
   for (int d = threadIdx.x; d < dk; d += kThreads) {
     float acc = 0.f;
-    for (int t = t0; t < t1; ++t) {
-      acc += to_f32(la[base + (long)t * dk + d]);
-      if (g) g[base + (long)t * dk + d] = acc;
+    for (int tb = t0; tb < t1; tb += U) {
+      float x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = tb + u < t1 ? to_f32(la[base + (long)(tb + u) * dk + d]) : 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        acc += x[u];
+        if (g && tb + u < t1) g[base + (long)(tb + u) * dk + d] = acc;
+      }
     }
     if (gamma) gamma[((long)bh * N + i) * dk + d] = acc;
   }
@@ -48,38 +55,44 @@ __global__ __launch_bounds__(kThreads) void k_state_dot(const float* __restrict_
   }
 }
 
-// carry[i][d] = c_T[d] + sum over chunks j > i of the chunk total of D, each chunk total
-// being the sum over the 64-column tiles of (forward cross term - reverse cross term).
-__global__ __launch_bounds__(kThreads) void k_gate_carry(const float* __restrict__ crossF,
-                                                         const float* __restrict__ crossR,
-                                                         const float* __restrict__ cT,
-                                                         float* __restrict__ carry, int dk,
-                                                         int ntile, int N) {
-  const int bh = blockIdx.y;
-  const int d = blockIdx.x * kThreads + threadIdx.x;
-  if (d >= dk) return;
-  float run = cT ? cT[(long)bh * dk + d] : 0.f;
-  for (int j = N - 1; j >= 0; --j) {
-    carry[((long)bh * N + j) * dk + d] = run;
+// tot[j][d] = chunk total of D for chunk j: the sum over the 64-column tiles of
+// (forward cross term - reverse cross term).
+__global__ __launch_bounds__(kThreads) void k_gate_tot(const float* __restrict__ crossF,
+                                                       const float* __restrict__ crossR,
+                                                       float* __restrict__ tot, int dk,
+                                                       int ntile, int N) {
+  const int j = blockIdx.x, bh = blockIdx.y;
+  for (int d = threadIdx.x; d < dk; d += kThreads) {
     const long base = ((long)bh * N + j) * ntile * dk + d;
-    float tot = 0.f;
-    for (int u = 0; u < ntile; ++u) tot += crossF[base + (long)u * dk] - crossR[base + (long)u * dk];
-    run += tot;
+    float t = 0.f;
+    for (int u = 0; u < ntile; ++u) t += crossF[base + (long)u * dk] - crossR[base + (long)u * dk];
+    tot[((long)bh * N + j) * dk + d] = t;
   }
 }
 
+// dlog_alpha[t] = (chunk-local suffix sum of D at t) + c_T + sum of chunk totals of the
+// later chunks.
 template <typename Tin>
 __global__ __launch_bounds__(kThreads) void k_gate_grad(const float* __restrict__ Dloc,
-                                                        const float* __restrict__ carry,
+                                                        const float* __restrict__ tot,
+                                                        const float* __restrict__ cT,
                                                         Tin* __restrict__ dla, int T, int dk,
                                                         int C, int N) {
+  constexpr int U = 16;
   const int i = blockIdx.x, bh = blockIdx.y;
   const int t0 = i * C, t1 = min(T, t0 + C);
   const long base = (long)bh * T * dk;
   for (int d = threadIdx.x; d < dk; d += kThreads) {
-    const float cr = carry[((long)bh * N + i) * dk + d];
-    for (int t = t0; t < t1; ++t)
-      dla[base + (long)t * dk + d] = from_f32<Tin>(Dloc[base + (long)t * dk + d] + cr);
+    float cr = cT ? cT[(long)bh * dk + d] : 0.f;
+    for (int j = i + 1; j < N; ++j) cr += tot[((long)bh * N + j) * dk + d];
+    for (int tb = t0; tb < t1; tb += U) {
+      float x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = tb + u < t1 ? Dloc[base + (long)(tb + u) * dk + d] : 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (tb + u < t1) dla[base + (long)(tb + u) * dk + d] = from_f32<Tin>(x[u] + cr);
+    }
   }
 }
 
@@ -108,24 +121,25 @@ hipError_t launch_state_dot(const float* dST, const float* ST, float* cT, int BH
 }
 
 hipError_t launch_gate_carry(const float* crossF, const float* crossR, const float* cT,
-                             float* carry, int BH, int T, int dk, int dv, int C, hipStream_t s) {
+                             float* tot, int BH, int T, int dk, int dv, int C, hipStream_t s) {
+  (void)cT;
   const int N = (T + C - 1) / C;
   if (BH == 0 || N == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gate_carry, dim3((dk + kThreads - 1) / kThreads, BH), dim3(kThreads), 0, s,
-                     crossF, crossR, cT, carry, dk, dv / 64, N);
+  hipLaunchKernelGGL(k_gate_tot, dim3(N, BH), dim3(kThreads), 0, s, crossF, crossR, tot, dk,
+                     dv / 64, N);
   return hipGetLastError();
 }
 
-hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* carry, void* dla, int BH,
-                            int T, int dk, int C, hipStream_t s) {
+hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* tot, const float* cT,
+                            void* dla, int BH, int T, int dk, int C, hipStream_t s) {
   const int N = (T + C - 1) / C;
   if (BH == 0 || N == 0) return hipSuccess;
   dim3 grid(N, BH);
   if (dtype == 0)
-    hipLaunchKernelGGL(k_gate_grad<float>, grid, dim3(kThreads), 0, s, Dloc, carry, (float*)dla,
-                       T, dk, C, N);
+    hipLaunchKernelGGL(k_gate_grad<float>, grid, dim3(kThreads), 0, s, Dloc, tot, cT,
+                       (float*)dla, T, dk, C, N);
   else
-    hipLaunchKernelGGL(k_gate_grad<bf16>, grid, dim3(kThreads), 0, s, Dloc, carry, (bf16*)dla,
+    hipLaunchKernelGGL(k_gate_grad<bf16>, grid, dim3(kThreads), 0, s, Dloc, tot, cT, (bf16*)dla,
                        T, dk, C, N);
   return hipGetLastError();
 }

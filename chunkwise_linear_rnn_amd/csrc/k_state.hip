@@ -59,12 +59,24 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
     const Tin* __restrict__ Y2, float* __restrict__ cross, const float* __restrict__ eg,
     const float* __restrict__ S_in, void* __restrict__ states, float* __restrict__ S_out,
     int T, int dk, int dv, int N, int reverse) {
-  constexpr int TV = 64, YLD = C + 8;
+  constexpr int TV = 64, TK = 64, YLD = C + 8, XLD = C + (sizeof(XTy) == 4 ? 4 : 8);
+  constexpr int SLD = 64 + 8;   // state tile staging for 16-byte row stores
+  using StT = typename std::conditional<STORE == 3, float, OpT>::type;
   __shared__ __attribute__((aligned(16))) OpT ys[TV * YLD];
   __shared__ __attribute__((aligned(16))) OpT y2s[CROSS ? TV * YLD : 8];
-  const int v0 = blockIdx.x * TV, k0 = blockIdx.y * 64, bh = blockIdx.z;
+  __shared__ __attribute__((aligned(16))) XTy xs[TK * XLD];
+  __shared__ __attribute__((aligned(16))) XTy x2s[CROSS ? TK * XLD : 8];
+  __shared__ __attribute__((aligned(16))) StT ss[STORE != 0 ? 64 * SLD : 8];
+  __shared__ float egs[TK];
+  // 1-D grid, XCD-aware: the dv tiles of one (bh, dk tile) share the Kh^T / Qh^T tiles
+  // and the dk tiles of one bh share the value-side tiles, so they run on one XCD.
+  const int nvt = dv / TV, nkt = dk / TK;
+  const int lt = xcd_logical(blockIdx.x, gridDim.x);
+  const int vt = lt % nvt, kt = (lt / nvt) % nkt, bh = lt / (nvt * nkt);
+  const int v0 = vt * TV, k0 = kt * TK;
   const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
-  const int row0 = k0 + 16 * w + 4 * qd;   // accumulator rows row0 .. row0+3
+  const int rl = 16 * w + 4 * qd;          // tile-local accumulator rows rl .. rl+3
+  const int row0 = k0 + rl;
 
   f32x4 acc[4];   // acc[j][e] = S[row0 + e][v0 + 16 j + r]
 #pragma unroll
@@ -73,42 +85,67 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
     for (int e = 0; e < 4; ++e)
       acc[j][e] = S_in ? S_in[((long)bh * dk + row0 + e) * dv + v0 + 16 * j + r] : 0.f;
 
+  // next chunk's tiles, loaded into registers while the current chunk computes
+  FlatTileRows<XTy, TK, C, XLD> tx, tx2;
+  ColTile<OpT, Tin, C, YLD> ty, ty2;
+  float egr = 0.f;
+  auto fetch = [&](int i) {
+    const int t0 = i * C, rows = min(C, T - t0);
+    const long xo = (((long)bh * N + i) * dk + k0) * C;
+    tx.load(XT + xo);
+    ty.load(Y + ((long)bh * T + t0) * dv + v0, dv, rows);
+    if constexpr (CROSS) {
+      tx2.load(X2T + xo);
+      ty2.load(Y2 + ((long)bh * T + t0) * dv + v0, dv, rows);
+    }
+    if (threadIdx.x < TK) egr = eg[((long)bh * N + i) * dk + k0 + threadIdx.x];
+  };
+  if (N > 0) fetch(reverse ? N - 1 : 0);
+
   for (int step = 0; step < N; ++step) {
     const int i = reverse ? N - 1 - step : step;
+    tx.store(xs);
+    ty.store(ys);
+    if constexpr (CROSS) {
+      tx2.store(x2s);
+      ty2.store(y2s);
+    }
+    if (threadIdx.x < TK) egs[threadIdx.x] = egr;
     if constexpr (STORE != 0) {
-      const long sb = ((long)bh * N + i) * dk * dv;
+      // the state before this chunk, through LDS
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = v0 + 16 * j + r;
-        if constexpr (STORE == 1) {
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            ((OpT*)states)[sb + (long)(row0 + e) * dv + col] = from_f32<OpT>(acc[j][e]);
-        } else if constexpr (STORE == 3) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ((float*)states)[sb + (long)(row0 + e) * dv + col] = acc[j][e];
-        } else {
-          OpT* p = (OpT*)states + sb + (long)col * dk + row0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p[e] = from_f32<OpT>(acc[j][e]);
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (STORE == 2)
+            ss[(16 * j + r) * SLD + rl + e] = (StT)acc[j][e];    // [v][k]
+          else
+            ss[(rl + e) * SLD + 16 * j + r] = (StT)acc[j][e];    // [k][v]
         }
+    }
+    __syncthreads();
+    if (step + 1 < N) fetch(reverse ? i - 1 : i + 1);
+    if constexpr (STORE != 0) {
+      constexpr int kPer = 16 / (int)sizeof(StT), kUnits = 64 * 64 / kPer;
+      const long sb = ((long)bh * N + i) * dk * dv;
+      for (int idx = threadIdx.x; idx < kUnits; idx += kThreads) {
+        const int e0 = idx * kPer, a = e0 / 64, b = e0 % 64;
+        long off;
+        if constexpr (STORE == 2) off = sb + (long)(v0 + a) * dk + k0 + b;
+        else off = sb + (long)(k0 + a) * dv + v0 + b;
+        *reinterpret_cast<u32x4*>((StT*)states + off) =
+            *reinterpret_cast<const u32x4*>(ss + a * SLD + b);
       }
     }
-    const int t0 = i * C, rows = min(C, T - t0);
-    stage_cols<OpT, Tin, C, TV>(ys, YLD, Y + ((long)bh * T + t0) * dv + v0, dv, rows);
-    if constexpr (CROSS)
-      stage_cols<OpT, Tin, C, TV>(y2s, YLD, Y2 + ((long)bh * T + t0) * dv + v0, dv, rows);
-    __syncthreads();
 
     if constexpr (CROSS) {
       f32x4 P[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) P[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const XTy* x2p = X2T + (((long)bh * N + i) * dk + k0 + 16 * w + r) * C;
 #pragma unroll
       for (int kb = 0; kb < C / 32; ++kb) {
         XFrag<OpT, XTy> fa;
-        fa.load(x2p + kb * 32);
+        fa.load(x2s + (16 * w + r) * XLD + kb * 32);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           Frag<OpT> fb;
@@ -119,33 +156,31 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
       float part[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float s = 0.f;
+        float sum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s += acc[j][e] * P[j][e];
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 8);
-        part[e] = s;
+        for (int j = 0; j < 4; ++j) sum += acc[j][e] * P[j][e];
+        sum += __shfl_xor(sum, 1);
+        sum += __shfl_xor(sum, 2);
+        sum += __shfl_xor(sum, 4);
+        sum += __shfl_xor(sum, 8);
+        part[e] = sum;
       }
       if (r == 0) {
         f32x4 o = {part[0], part[1], part[2], part[3]};
-        *reinterpret_cast<f32x4*>(cross + (((long)bh * N + i) * gridDim.x + blockIdx.x) * dk +
-                                  row0) = o;
+        *reinterpret_cast<f32x4*>(cross + (((long)bh * N + i) * nvt + vt) * dk + row0) = o;
       }
     }
 
-    const f32x4 dec = *reinterpret_cast<const f32x4*>(eg + ((long)bh * N + i) * dk + row0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int e = 0; e < 4; ++e) {
+      const float dec = egs[rl + e];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[j][e] *= dec[e];
-
-    const XTy* xp = XT + (((long)bh * N + i) * dk + k0 + 16 * w + r) * C;
+      for (int j = 0; j < 4; ++j) acc[j][e] *= dec;
+    }
 #pragma unroll
     for (int kb = 0; kb < C / 32; ++kb) {
       XFrag<OpT, XTy> fa;
-      fa.load(xp + kb * 32);
+      fa.load(xs + (16 * w + r) * XLD + kb * 32);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         Frag<OpT> fb;
@@ -166,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
 
 template <typename Tin, typename OpT, typename XTy, int C, int STORE, bool CROSS>
 static void launch_scan_k(const ScanArgs& a, hipStream_t s) {
-  dim3 grid(a.dv / 64, a.dk / 64, a.BH);
+  dim3 grid((a.dv / 64) * (a.dk / 64) * a.BH);
   hipLaunchKernelGGL((k_state_scan<Tin, OpT, XTy, C, STORE, CROSS>), grid, dim3(kThreads), 0, s,
                      (const XTy*)a.XT, (const Tin*)a.Y, (const XTy*)a.X2T, (const Tin*)a.Y2,
                      a.cross, a.eg, a.S_in, a.states, a.S_out, a.T, a.dk, a.dv, a.N,

@@ -22,11 +22,11 @@ import sys
 STAGE_KERNEL = {"bwd_chunk": "k_bwd_chunk", "fwd_fused": "k_fwd_fused", "intra": "k_intra",
                 "state_scan_fwd": "k_state_scan", "state_scan_rev": "k_state_scan",
                 "output": "k_output", "gate_cumsum": "k_gate_cumsum", "gate_grad": "k_gate_grad",
-                "gate_carry": "k_gate_carry"}
+                "gate_tot": "k_gate_tot"}
 STAGE_SOURCE = {"bwd_chunk": "k_bwd.hip", "fwd_fused": "k_fwd.hip", "intra": "k_intra.hip",
                 "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip",
                 "output": "k_fwd.hip", "gate_cumsum": "k_gate.hip", "gate_grad": "k_gate.hip",
-                "gate_carry": "k_gate.hip"}
+                "gate_tot": "k_gate.hip"}
 
 
 def short(name: str) -> str:
