@@ -64,8 +64,8 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
             byt = 3 * tok * dk * e + 2 * tokp * dk * e + BH * N * C * C * e + BH * N * dk * 4
             if mode == "materialized":
                 byt += tok * dk * (4 - e)  # reads fp32 g instead of log_alpha
-        else:
-            byt = (tok * dk * 4 + 2 * tok * dk * e + BH * N * C * C * e + 2 * tokp * dk * 4
+        else:   # reads log_alpha, q, k; writes g (fp32), A, Qh^T, Kh^T (fp32), Kh, e^gamma
+            byt = (3 * tok * dk * e + tok * dk * 4 + BH * N * C * C * e + 2 * tokp * dk * 4
                    + tokp * dk * e + BH * N * dk * 4)
         return byt, tok * C * dk
     if stage in ("state_scan_fwd", "state_scan_rev"):

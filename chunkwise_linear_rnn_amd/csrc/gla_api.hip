@@ -6,7 +6,7 @@
 //   forward, materialized states:  gate cumsum -> intra-chunk (A, Qh, Kh^T, e^gamma)
 //                                  -> state scan (writes every S_[i]) -> output
 //   forward, recomputed states:    intra-chunk (cumsum fused) -> fused state+output
-//   backward:                      gate cumsum -> intra-chunk -> state scan (S_[i]) ->
+//   backward:                      intra-chunk (cumsum fused, writes g) -> state scan (S_[i]) ->
 //                                  reverse state scan (dS_[i+1], dS0); both scans also
 //                                  form the chunk totals of q*dq - k*dk from their fp32
 //                                  states -> chunk backward (dq, dk, dv, chunk-local D
@@ -129,8 +129,8 @@ struct Tracer {
 // Stage names of each pipeline, in launch order.
 const char* const kFwdMat[] = {"gate_cumsum", "intra", "state_scan", "output"};
 const char* const kFwdRec[] = {"intra", "fwd_fused"};
-const char* const kBwd[] = {"gate_cumsum", "intra", "state_scan_fwd", "state_scan_rev",
-                            "state_dot", "bwd_chunk", "gate_tot", "gate_grad"};
+const char* const kBwd[] = {"intra", "state_scan_fwd", "state_scan_rev", "state_dot",
+                            "bwd_chunk", "gate_tot", "gate_grad"};
 
 int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, int max) {
   const char* const* src;
@@ -139,11 +139,11 @@ int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, in
     if (d->state_mode == GLA_STATES_MATERIALIZED) { src = kFwdMat; n = 4; }
     else { src = kFwdRec; n = 2; }
   } else {
-    src = kBwd; n = 8;
+    src = kBwd; n = 7;
   }
   int m = 0;
   for (int j = 0; j < n; ++j) {
-    if (pass == GLA_PASS_BWD && j == 4 && !with_dST) continue;
+    if (pass == GLA_PASS_BWD && j == 3 && !with_dST) continue;
     if (out && m < max) out[m] = src[j];
     ++m;
   }
@@ -333,15 +333,11 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   char* w = (char*)ws;
   const int C = (int)x.C, BH = (int)x.BH, T = (int)x.T, DK = (int)x.dk, DV = (int)x.dv,
             N = (int)x.N;
-  gla_status_t rs = tr.mark();
-  if (rs != GLA_OK) return rs;
-  rs = dev(gla::launch_gate_cumsum(x.dtype, log_alpha, (float*)(w + p.g), nullptr, BH, T, DK, C,
-                                   s));
-  if (rs != GLA_OK) return rs;
+  gla_status_t rs = GLA_OK;
   gla::IntraArgs ia{};
   ia.dtype = x.dtype; ia.C = C; ia.BH = BH; ia.T = T; ia.dk = DK; ia.N = N; ia.want_A = true;
   ia.xt_f32 = x.dtype == GLA_BF16;
-  ia.q = q; ia.k = k; ia.la = log_alpha; ia.g = (const float*)(w + p.g);
+  ia.q = q; ia.k = k; ia.la = log_alpha; ia.g = nullptr; ia.g2_out = (float*)(w + p.g);
   ia.A = w + p.A; ia.QhT = w + p.QhT; ia.Kh = w + p.Kh; ia.KhT = w + p.KhT;
   ia.eg = (float*)(w + p.eg);
   if ((rs = tr.mark()) != GLA_OK) return rs;

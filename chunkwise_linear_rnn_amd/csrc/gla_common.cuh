@@ -277,21 +277,30 @@ struct RowTile {
 template <typename T, int ROWS, int COLS, int LD>
 using FlatTileRows = FlatTile<T, ROWS, COLS, LD>;
 
-// ROWS x 64 slice of a row-major [*, gld] input (Tin), rows beyond `rows` zero, staged
-// transposed (lds[c * LD + r], OpT) through 2-row x 8-column units.
+// ROWS x 64 slice of a row-major [*, gld] matrix, rows beyond `rows` zero, staged
+// transposed (lds[c * LD + r]) through 2-row x 8-column units.  The loads keep the raw
+// 16-byte words (no use of the data until store), so they stay in flight.  Input and
+// LDS element types are the same (bf16 or fp32).
 template <typename OpT, typename Tin, int ROWS, int LD>
 struct ColTile {
+  static_assert(sizeof(OpT) == sizeof(Tin), "same element type in and out");
+  static constexpr int kWords = sizeof(Tin) == 2 ? 1 : 2;   // 16-byte words per 8 elements
   static constexpr int kUnits = (ROWS / 2) * 8;
   static constexpr int kPerThread = (kUnits + kThreads - 1) / kThreads;
-  float x0[kPerThread][8], x1[kPerThread][8];
+  u32x4 x0[kPerThread][kWords], x1[kPerThread][kWords];
   __device__ __forceinline__ void load(const Tin* __restrict__ g, long gld, int rows) {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       const int idx = threadIdx.x + j * kThreads;
       const int r = (idx / 8) * 2, c = (idx % 8) * 8;
       if (kUnits % kThreads == 0 || idx < kUnits) {
-        if (r < rows) load8(x0[j], g + r * gld + c); else zero8(x0[j]);
-        if (r + 1 < rows) load8(x1[j], g + (r + 1) * gld + c); else zero8(x1[j]);
+#pragma unroll
+        for (int h = 0; h < kWords; ++h) {
+          const int ce = c + h * (8 / kWords);
+          x0[j][h] = r < rows ? *reinterpret_cast<const u32x4*>(g + r * gld + ce) : u32x4{0u, 0u, 0u, 0u};
+          x1[j][h] = r + 1 < rows ? *reinterpret_cast<const u32x4*>(g + (r + 1) * gld + ce)
+                                  : u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
   }
@@ -301,18 +310,21 @@ struct ColTile {
       const int idx = threadIdx.x + j * kThreads;
       const int r = (idx / 8) * 2, c = (idx % 8) * 8;
       if (kUnits % kThreads == 0 || idx < kUnits) {
+        if constexpr (sizeof(OpT) == 2) {
+          // word w of a row holds elements 2w (low half) and 2w+1 (high half)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if constexpr (sizeof(OpT) == 2) {
-            bf16x2 w;
-            w[0] = (bf16)x0[j][e];
-            w[1] = (bf16)x1[j][e];
-            *reinterpret_cast<bf16x2*>(lds + (c + e) * LD + r) = w;
-          } else {
-            f32x2 w;
-            w[0] = x0[j][e];
-            w[1] = x1[j][e];
-            *reinterpret_cast<f32x2*>(lds + (c + e) * LD + r) = w;
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t a = x0[j][0][w], b = x1[j][0][w];
+            *reinterpret_cast<uint32_t*>(lds + (c + 2 * w) * LD + r) = (a & 0xFFFFu) | (b << 16);
+            *reinterpret_cast<uint32_t*>(lds + (c + 2 * w + 1) * LD + r) = (a >> 16) | (b & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            u32x4 const& A = x0[j][e / 4];
+            u32x4 const& B = x1[j][e / 4];
+            uint32_t pr[2] = {A[e % 4], B[e % 4]};
+            *reinterpret_cast<uint2*>(lds + (c + e) * LD + r) = *reinterpret_cast<uint2*>(pr);
           }
         }
       }

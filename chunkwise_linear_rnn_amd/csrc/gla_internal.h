@@ -8,12 +8,13 @@ namespace gla {
 struct IntraArgs {
   int dtype, C, BH, T, dk, N;
   bool want_A;
-  bool xt_f32;           // write QhT / KhT in fp32 (bf16 inputs only)
+  bool xt_f32;           // write QhT / KhT as bf16 high part + remainder (bf16 inputs only)
   const void *q, *k, *la;
   const float* g;        // chunk-local cumsum from the gate kernel, or NULL (computed)
   void* A;               // [BH][N][C][C]       operand type
   void *Qh, *QhT, *Kh, *KhT;
   float* eg;             // [BH][N][dk]
+  float* g2_out;         // [BH][T][dk] g * log2(e), or NULL
 };
 hipError_t launch_intra(const IntraArgs& a, hipStream_t s);
 
@@ -34,7 +35,7 @@ hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* tot, cons
 struct ScanArgs {
   int dtype, C, BH, T, dk, dv, N;
   bool reverse;
-  bool xt_f32;           // XT / X2T are fp32 (split into two bf16 halves for the MFMA)
+  bool xt_f32;           // XT / X2T rows hold a bf16 high part then its remainder
   int store;
   const void* XT;        // [BH][N][dk][C] (Kh^T forward, Qh^T reverse)
   const void* Y;         // [BH][T][dv]    input type (v forward, dO reverse)
@@ -68,7 +69,7 @@ hipError_t launch_fwd_fused(const FusedArgs& a, hipStream_t s);
 struct BwdArgs {
   int dtype, C, BH, T, dk, dv, N;
   const void *q, *k, *v, *dO;
-  const float *g, *gamma;
+  const float *g, *gamma;   // g: g * log2(e) [BH][T][dk] (from the intra-chunk kernel)
   const void *A, *Kh, *S, *dS;
   void *dq, *dk_out, *dv_out;
   float* Dloc;

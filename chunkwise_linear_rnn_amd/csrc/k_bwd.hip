@@ -47,8 +47,8 @@ struct IntraLds {
   static constexpr int bytes_blk = C * GLD * 4 * 3 + C * XLD * (int)sizeof(Tin) * 2;
 };
 
-// Stage g (times log2 e; rows past T continue the last valid row), q, k for dk columns
-// [d0, d0 + DB) of the chunk.  Ends with a barrier.
+// Stage g (already times log2 e; rows past T continue the last valid row), q, k for dk
+// columns [d0, d0 + DB) of the chunk.  Ends with a barrier.
 template <int C, int DB, int DK, typename Tin>
 __device__ __forceinline__ void bwd_stage_block(const IntraLds<C, DB, Tin>& L, const Tin* q,
                                                 const Tin* k, const float* g, long tok0,
@@ -59,7 +59,7 @@ __device__ __forceinline__ void bwd_stage_block(const IntraLds<C, DB, Tin>& L, c
     float x[8];
     load8(x, g + (tok0 + min(rr, rows - 1)) * DK + d0 + c);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) L.gs[rr * GLD + c + e] = x[e] * kLog2e;
+    for (int e = 0; e < 8; ++e) L.gs[rr * GLD + c + e] = x[e];
   }
   stage_rows<Tin, Tin, C, DB>(L.qs, XLD, q + tok0 * DK + d0, DK, rows);
   stage_rows<Tin, Tin, C, DB>(L.ks, XLD, k + tok0 * DK + d0, DK, rows);

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd_fused_staged(
   __shared__ __attribute__((aligned(16))) OpT ks[DK * KLD];
   __shared__ __attribute__((aligned(16))) OpT as_[C * ALD];
   __shared__ __attribute__((aligned(16))) OpT vs[TV * VLD];
-  __shared__ __attribute__((aligned(16))) Tin os_[C * OLD];
+  __shared__ __attribute__((aligned(16))) Tin os_[2][C * OLD];   // O tile, double-buffered
   __shared__ float egs[DK];
   // 1-D grid, XCD-aware: the dv tiles of one bh share every Qh / Kh^T / A tile
   const int nvt = dv / TV;
@@ -120,14 +120,27 @@ __global__ __launch_bounds__(kThreads) void k_fwd_fused_staged(
   };
   if (N > 0) fetch(0);
 
+  // O tile of the previous chunk leaves right after the first barrier of the next chunk,
+  // before that chunk's prefetch (vector memory operations complete in order).
+  constexpr int kPer = 16 / (int)sizeof(Tin), kUnits = C * TV / kPer;
+  auto store_o = [&](int ip) {
+    const int tp = ip * C, rp = min(C, T - tp);
+    const Tin* ob = os_[ip & 1];
+    for (int idx = threadIdx.x; idx < kUnits; idx += kThreads) {
+      const int e0 = idx * kPer, rr = e0 / TV, cc = e0 % TV;
+      if (rr < rp)
+        *reinterpret_cast<u32x4*>(O + ((long)bh * T + tp + rr) * dv + v0 + cc) =
+            *reinterpret_cast<const u32x4*>(ob + rr * OLD + cc);
+    }
+  };
   for (int i = 0; i < N; ++i) {
-    const int t0 = i * C, rows = min(C, T - t0);
     tq.store(qs);
     tk.store(ks);
     ta.store(as_);
     tv.store(vs);
     if (threadIdx.x < DK) egs[threadIdx.x] = egr;
     __syncthreads();
+    if (i > 0) store_o(i - 1);
     if (i + 1 < N) fetch(i + 1);
 
     // O_i = Qh_i S + A_i V_i
@@ -158,10 +171,11 @@ __global__ __launch_bounds__(kThreads) void k_fwd_fused_staged(
         }
       }
     }
+    Tin* ob = os_[i & 1];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) os_[(16 * m + 4 * qd + e) * OLD + 16 * w + r] = from_f32<Tin>(acc[m][e]);
+      for (int e = 0; e < 4; ++e) ob[(16 * m + 4 * qd + e) * OLD + 16 * w + r] = from_f32<Tin>(acc[m][e]);
 
     // S <- diag(exp(gamma_i)) S + Kh_i^T V_i
 #pragma unroll
@@ -182,15 +196,8 @@ __global__ __launch_bounds__(kThreads) void k_fwd_fused_staged(
       }
     }
     __syncthreads();
-    // O tile out: C rows x 64 values, 16-byte row pieces
-    constexpr int kPer = 16 / (int)sizeof(Tin), kUnits = C * TV / kPer;
-    for (int idx = threadIdx.x; idx < kUnits; idx += kThreads) {
-      const int e0 = idx * kPer, rr = e0 / TV, cc = e0 % TV;
-      if (rr < rows)
-        *reinterpret_cast<u32x4*>(O + ((long)bh * T + t0 + rr) * dv + v0 + cc) =
-            *reinterpret_cast<const u32x4*>(os_ + rr * OLD + cc);
-    }
   }
+  if (N > 0) store_o(N - 1);
   if (S_T) {
 #pragma unroll
     for (int p = 0; p < NP; ++p)

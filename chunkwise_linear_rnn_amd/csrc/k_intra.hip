@@ -14,12 +14,13 @@
 // Alongside it emits, for the chunk, the decayed operands the inter-chunk kernels
 // consume (each nullable): Qh = q*exp(g) token-major, its transpose QhT, Kh =
 // k*exp(gamma - g) token-major, its transpose KhT, and exp(gamma).  The transposed
-// operands feed the state scans; they are written either in the MFMA operand type or in
-// fp32 (XT = float), which the backward's scans split into two bf16 halves.
+// operands feed the state scans; they are written either in the MFMA operand type or
+// (XT = float with bf16 operands) as a bf16 high part plus bf16 remainder per row, which
+// the backward's scans feed to two MFMAs so the states carry no operand rounding.
 //
 // g either comes from the gate-cumsum kernel (G_WS) or is computed here from log_alpha
 // by a segmented column scan.  Internally g is held multiplied by log2(e) so every decay
-// is one v_exp_f32.
+// is one v_exp_f32; g2_out (nullable) receives it for the backward chunk kernel.
 #include "gla_common.cuh"
 #include "gla_internal.h"
 
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ la,
     const float* __restrict__ gws, OpT* __restrict__ A_out, OpT* __restrict__ Qh_out,
     XT* __restrict__ QhT_out, OpT* __restrict__ Kh_out, XT* __restrict__ KhT_out,
-    float* __restrict__ eg_out, int T, int dk, int N) {
+    float* __restrict__ eg_out, float* __restrict__ g2_out, int T, int dk, int N) {
   constexpr int DB = 64;                    // dk columns per pass
   constexpr int NS = C / 16;                // sub-chunks
   constexpr int NPAIR = NS * (NS - 1) / 2;  // off-diagonal sub-block pairs
@@ -112,6 +113,17 @@ __global__ __launch_bounds__(kThreads) void k_intra(
     stage_rows<Tin, Tin, C, DB>(qs, XLD, q + in_base + d0, dk, rows);
     stage_rows<Tin, Tin, C, DB>(ks, XLD, k + in_base + d0, dk, rows);
     __syncthreads();
+    if (g2_out) {   // g * log2 e for the backward chunk kernel
+      for (int idx = threadIdx.x; idx < C * (DB / 8); idx += kThreads) {
+        const int rr = idx / (DB / 8), c = (idx % (DB / 8)) * 8;
+        if (rr < rows) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = gs[rr * GLD + c + e];
+          store8(g2_out + in_base + (long)rr * dk + d0 + c, x);
+        }
+      }
+    }
 
     // ---- decayed operands for the inter-chunk kernels ---------------------------------
     const float* glast = gs + (C - 1) * GLD;   // gamma * log2 e
@@ -138,22 +150,41 @@ __global__ __launch_bounds__(kThreads) void k_intra(
       }
     }
     if (QhT_out || KhT_out) {
+      // transposed per chunk: [dk][C] in the operand type, or (XT = float) as a bf16 high
+      // part [dk][0..C) followed by its bf16 remainder [dk][C..2C) in the same bytes
+      constexpr bool kSplit = sizeof(XT) == 4 && sizeof(OpT) == 2;
       for (int idx = threadIdx.x; idx < DB * (C / 8); idx += kThreads) {
         const int c = idx / (C / 8), r8 = (idx % (C / 8)) * 8;
-        const long o = (((long)bh * N + i) * dk + d0 + c) * C + r8;
+        const long rowi = ((long)bh * N + i) * dk + d0 + c;
         float x[8];
-        if (QhT_out) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            x[e] = to_f32(qs[(r8 + e) * XLD + c]) * __builtin_amdgcn_exp2f(gs[(r8 + e) * GLD + c]);
-          store8(QhT_out + o, x);
-        }
-        if (KhT_out) {
+        for (int pass = 0; pass < 2; ++pass) {
+          XT* dst = pass == 0 ? QhT_out : KhT_out;
+          if (!dst) continue;
+          if (pass == 0) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            x[e] = to_f32(ks[(r8 + e) * XLD + c]) *
-                   __builtin_amdgcn_exp2f(glast[c] - gs[(r8 + e) * GLD + c]);
-          store8(KhT_out + o, x);
+            for (int e = 0; e < 8; ++e)
+              x[e] = to_f32(qs[(r8 + e) * XLD + c]) * __builtin_amdgcn_exp2f(gs[(r8 + e) * GLD + c]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              x[e] = to_f32(ks[(r8 + e) * XLD + c]) *
+                     __builtin_amdgcn_exp2f(glast[c] - gs[(r8 + e) * GLD + c]);
+          }
+          if constexpr (kSplit) {
+            bf16* b = reinterpret_cast<bf16*>(dst) + rowi * 2 * C + r8;
+            float lo[8];
+            bf16x8 hv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              hv[e] = (bf16)x[e];
+              lo[e] = x[e] - (float)hv[e];
+            }
+            *reinterpret_cast<bf16x8*>(b) = hv;
+            store8(b + C, lo);
+          } else {
+            store8(dst + rowi * C + r8, x);
+          }
         }
       }
     }
@@ -250,7 +281,8 @@ template <typename Tin, typename OpT, typename XT, int C, bool GW, bool WA>
 static void launch_intra_k(const IntraArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_intra<Tin, OpT, XT, C, GW, WA>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
                      (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.la, a.g, (OpT*)a.A,
-                     (OpT*)a.Qh, (XT*)a.QhT, (OpT*)a.Kh, (XT*)a.KhT, a.eg, a.T, a.dk, a.N);
+                     (OpT*)a.Qh, (XT*)a.QhT, (OpT*)a.Kh, (XT*)a.KhT, a.eg, a.g2_out, a.T, a.dk,
+                     a.N);
 }
 template <typename Tin, typename OpT, typename XT, int C>
 static hipError_t launch_intra_t(const IntraArgs& a, hipStream_t s) {

@@ -10,10 +10,9 @@
 // The product is a k32 MFMA over the chunk's tokens: the transposed decayed operand
 // comes ready-made from the intra-chunk kernel, the value-side tile is staged into LDS
 // transposed so both operands are token-contiguous.  The tile stays in fp32 accumulators
-// across the whole sequence.  When the transposed operand arrives in fp32 and the MFMA
-// runs in bf16, it is split into a bf16 high part and a bf16 remainder (two MFMAs), so
-// the state carries no operand rounding; the kernel is bound by the state writes, not by
-// the matrix units.
+// across the whole sequence.  In the backward the transposed operand arrives as a bf16
+// high part plus bf16 remainder (two MFMAs), so the state carries no operand rounding;
+// the kernel is bound by the state writes, not by the matrix units.
 //
 // Chunk totals of the closed-form gate gradient (optional cross term): summed over one
 // chunk, the intra-chunk parts of q*dq - k*dk cancel pairwise, so the chunk total is
@@ -28,44 +27,34 @@
 
 namespace gla {
 
-// Operand fragment of the transposed decayed operand: one MFMA operand, or (fp32 source,
-// bf16 MFMA) a high part plus remainder.
-template <typename OpT, typename XTy>
+// Transposed decayed operand in LDS: rows of C tokens in the operand type, or (SPLIT) a
+// bf16 high part in [0, C) and its bf16 remainder in [C, 2C) of each row.
+template <typename OpT, bool SPLIT>
 struct XFrag {
-  static constexpr bool kSplit = std::is_same<XTy, float>::value && std::is_same<OpT, bf16>::value;
   Frag<OpT> hi, lo;
-  __device__ __forceinline__ void load(const XTy* p) {
-    if constexpr (kSplit) {
-      float x[8];
-      load8(x, p + 8 * (lane_id() >> 4));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        hi.set(e, x[e]);
-        lo.set(e, x[e] - hi.get(e));
-      }
-    } else {
-      load_frag_c(hi, p);
-    }
+  __device__ __forceinline__ void load(const OpT* row, int kb, int C) {
+    load_frag_c(hi, row + kb * 32);
+    if constexpr (SPLIT) load_frag_c(lo, row + C + kb * 32);
   }
   __device__ __forceinline__ void apply(f32x4& acc, const Frag<OpT>& b) const {
     mma(acc, hi, b);
-    if constexpr (kSplit) mma(acc, lo, b);
+    if constexpr (SPLIT) mma(acc, lo, b);
   }
 };
 
-template <typename Tin, typename OpT, typename XTy, int C, int STORE, bool CROSS>
+template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS>
 __global__ __launch_bounds__(kThreads) void k_state_scan(
-    const XTy* __restrict__ XT, const Tin* __restrict__ Y, const XTy* __restrict__ X2T,
+    const OpT* __restrict__ XT, const Tin* __restrict__ Y, const OpT* __restrict__ X2T,
     const Tin* __restrict__ Y2, float* __restrict__ cross, const float* __restrict__ eg,
     const float* __restrict__ S_in, void* __restrict__ states, float* __restrict__ S_out,
     int T, int dk, int dv, int N, int reverse) {
-  constexpr int TV = 64, TK = 64, YLD = C + 8, XLD = C + (sizeof(XTy) == 4 ? 4 : 8);
+  constexpr int TV = 64, TK = 64, YLD = C + 8, XW = SPLIT ? 2 * C : C, XLD = XW + 8;
   constexpr int SLD = 64 + 8;   // state tile staging for 16-byte row stores
   using StT = typename std::conditional<STORE == 3, float, OpT>::type;
   __shared__ __attribute__((aligned(16))) OpT ys[TV * YLD];
   __shared__ __attribute__((aligned(16))) OpT y2s[CROSS ? TV * YLD : 8];
-  __shared__ __attribute__((aligned(16))) XTy xs[TK * XLD];
-  __shared__ __attribute__((aligned(16))) XTy x2s[CROSS ? TK * XLD : 8];
+  __shared__ __attribute__((aligned(16))) OpT xs[TK * XLD];
+  __shared__ __attribute__((aligned(16))) OpT x2s[CROSS ? TK * XLD : 8];
   __shared__ __attribute__((aligned(16))) StT ss[STORE != 0 ? 64 * SLD : 8];
   __shared__ float egs[TK];
   // 1-D grid, XCD-aware: the dv tiles of one (bh, dk tile) share the Kh^T / Qh^T tiles
@@ -86,12 +75,12 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
       acc[j][e] = S_in ? S_in[((long)bh * dk + row0 + e) * dv + v0 + 16 * j + r] : 0.f;
 
   // next chunk's tiles, loaded into registers while the current chunk computes
-  FlatTileRows<XTy, TK, C, XLD> tx, tx2;
+  FlatTileRows<OpT, TK, XW, XLD> tx, tx2;
   ColTile<OpT, Tin, C, YLD> ty, ty2;
   float egr = 0.f;
   auto fetch = [&](int i) {
     const int t0 = i * C, rows = min(C, T - t0);
-    const long xo = (((long)bh * N + i) * dk + k0) * C;
+    const long xo = (((long)bh * N + i) * dk + k0) * XW;
     tx.load(XT + xo);
     ty.load(Y + ((long)bh * T + t0) * dv + v0, dv, rows);
     if constexpr (CROSS) {
@@ -102,6 +91,11 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
   };
   if (N > 0) fetch(reverse ? N - 1 : 0);
 
+  // Stores are issued right after the step's first barrier and before the next chunk's
+  // loads: vector memory operations complete in order, so a store issued after the
+  // prefetch would make the next step wait for the write round trip.
+  float part_prev[4] = {0.f, 0.f, 0.f, 0.f};   // cross term of the previous chunk
+  int i_prev = -1;
   for (int step = 0; step < N; ++step) {
     const int i = reverse ? N - 1 - step : step;
     tx.store(xs);
@@ -124,7 +118,6 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
         }
     }
     __syncthreads();
-    if (step + 1 < N) fetch(reverse ? i - 1 : i + 1);
     if constexpr (STORE != 0) {
       constexpr int kPer = 16 / (int)sizeof(StT), kUnits = 64 * 64 / kPer;
       const long sb = ((long)bh * N + i) * dk * dv;
@@ -137,6 +130,13 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
             *reinterpret_cast<const u32x4*>(ss + a * SLD + b);
       }
     }
+    if constexpr (CROSS) {
+      if (i_prev >= 0 && r == 0) {
+        f32x4 o = {part_prev[0], part_prev[1], part_prev[2], part_prev[3]};
+        *reinterpret_cast<f32x4*>(cross + (((long)bh * N + i_prev) * nvt + vt) * dk + row0) = o;
+      }
+    }
+    if (step + 1 < N) fetch(reverse ? i - 1 : i + 1);
 
     if constexpr (CROSS) {
       f32x4 P[4];
@@ -144,8 +144,8 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
       for (int j = 0; j < 4; ++j) P[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < C / 32; ++kb) {
-        XFrag<OpT, XTy> fa;
-        fa.load(x2s + (16 * w + r) * XLD + kb * 32);
+        XFrag<OpT, SPLIT> fa;
+        fa.load(x2s + (16 * w + r) * XLD, kb, C);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           Frag<OpT> fb;
@@ -153,7 +153,6 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
           fa.apply(P[j], fb);
         }
       }
-      float part[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float sum = 0.f;
@@ -163,12 +162,9 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
         sum += __shfl_xor(sum, 2);
         sum += __shfl_xor(sum, 4);
         sum += __shfl_xor(sum, 8);
-        part[e] = sum;
+        part_prev[e] = sum;
       }
-      if (r == 0) {
-        f32x4 o = {part[0], part[1], part[2], part[3]};
-        *reinterpret_cast<f32x4*>(cross + (((long)bh * N + i) * nvt + vt) * dk + row0) = o;
-      }
+      i_prev = i;
     }
 
 #pragma unroll
@@ -179,8 +175,8 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
     }
 #pragma unroll
     for (int kb = 0; kb < C / 32; ++kb) {
-      XFrag<OpT, XTy> fa;
-      fa.load(xs + (16 * w + r) * XLD + kb * 32);
+      XFrag<OpT, SPLIT> fa;
+      fa.load(xs + (16 * w + r) * XLD, kb, C);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         Frag<OpT> fb;
@@ -189,6 +185,12 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
       }
     }
     __syncthreads();
+  }
+  if constexpr (CROSS) {
+    if (i_prev >= 0 && r == 0) {
+      f32x4 o = {part_prev[0], part_prev[1], part_prev[2], part_prev[3]};
+      *reinterpret_cast<f32x4*>(cross + (((long)bh * N + i_prev) * nvt + vt) * dk + row0) = o;
+    }
   }
   if (S_out) {
 #pragma unroll
@@ -199,26 +201,26 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
   }
 }
 
-template <typename Tin, typename OpT, typename XTy, int C, int STORE, bool CROSS>
+template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS>
 static void launch_scan_k(const ScanArgs& a, hipStream_t s) {
   dim3 grid((a.dv / 64) * (a.dk / 64) * a.BH);
-  hipLaunchKernelGGL((k_state_scan<Tin, OpT, XTy, C, STORE, CROSS>), grid, dim3(kThreads), 0, s,
-                     (const XTy*)a.XT, (const Tin*)a.Y, (const XTy*)a.X2T, (const Tin*)a.Y2,
+  hipLaunchKernelGGL((k_state_scan<Tin, OpT, SPLIT, C, STORE, CROSS>), grid, dim3(kThreads), 0, s,
+                     (const OpT*)a.XT, (const Tin*)a.Y, (const OpT*)a.X2T, (const Tin*)a.Y2,
                      a.cross, a.eg, a.S_in, a.states, a.S_out, a.T, a.dk, a.dv, a.N,
                      a.reverse ? 1 : 0);
 }
 
-template <typename Tin, typename OpT, typename XTy, int C>
+template <typename Tin, typename OpT, bool SPLIT, int C>
 static hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
   if (a.cross) {
     // the backward: operand-type states, [dk][dv]
-    launch_scan_k<Tin, OpT, XTy, C, 1, true>(a, s);
+    launch_scan_k<Tin, OpT, SPLIT, C, 1, true>(a, s);
   } else {
     switch (a.store) {
-      case 0: launch_scan_k<Tin, OpT, XTy, C, 0, false>(a, s); break;
-      case 1: launch_scan_k<Tin, OpT, XTy, C, 1, false>(a, s); break;
-      case 2: launch_scan_k<Tin, OpT, XTy, C, 2, false>(a, s); break;
-      default: launch_scan_k<Tin, OpT, XTy, C, 3, false>(a, s); break;
+      case 0: launch_scan_k<Tin, OpT, SPLIT, C, 0, false>(a, s); break;
+      case 1: launch_scan_k<Tin, OpT, SPLIT, C, 1, false>(a, s); break;
+      case 2: launch_scan_k<Tin, OpT, SPLIT, C, 2, false>(a, s); break;
+      default: launch_scan_k<Tin, OpT, SPLIT, C, 3, false>(a, s); break;
     }
   }
   return hipGetLastError();
@@ -227,13 +229,13 @@ static hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
 hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s) {
   if (a.BH == 0 || a.N == 0) return hipSuccess;
   if (a.cross && a.store != 1) return hipErrorInvalidValue;
-  if (a.dtype == 0) return launch_scan_t<float, float, float, 64>(a, s);
+  if (a.dtype == 0) return launch_scan_t<float, float, false, 64>(a, s);
   if (a.xt_f32) {
-    if (a.C == 64) return launch_scan_t<bf16, bf16, float, 64>(a, s);
-    return launch_scan_t<bf16, bf16, float, 128>(a, s);
+    if (a.C == 64) return launch_scan_t<bf16, bf16, true, 64>(a, s);
+    return launch_scan_t<bf16, bf16, true, 128>(a, s);
   }
-  if (a.C == 64) return launch_scan_t<bf16, bf16, bf16, 64>(a, s);
-  return launch_scan_t<bf16, bf16, bf16, 128>(a, s);
+  if (a.C == 64) return launch_scan_t<bf16, bf16, false, 64>(a, s);
+  return launch_scan_t<bf16, bf16, false, 128>(a, s);
 }
 
 }  // namespace gla
