@@ -43,7 +43,8 @@ STAGE_SOURCE = {
     "gate_cumsum": "k_gate.hip", "gate_tot": "k_gate.hip", "gate_grad": "k_gate.hip",
     "state_dot": "k_gate.hip", "intra": "k_intra.hip", "state_scan": "k_state.hip",
     "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip", "output": "k_fwd.hip",
-    "fwd_fused": "k_fwd.hip", "bwd_chunk": "k_bwd.hip",
+    "fwd_fused": "k_fwd.hip", "bwd_chunk": "k_bwd.hip", "bwd_dqk": "k_bwd.hip",
+    "bwd_dv": "k_bwd.hip",
 }
 
 
@@ -82,6 +83,13 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
         byt = (tok * (2 * dk * e + 2 * dv * e + dk * 4) + BH * N * C * C * e + tokp * dk * e
                + 2 * st + tok * (2 * dk * e + dv * e + dk * 4))
         return byt, tok * (6 * dk * dv + C * (2 * dk + 2 * dv))
+    if stage == "bwd_dqk":   # reads q, k, v, dO, g, S, dS; writes dq, dk, D
+        byt = (tok * (2 * dk * e + 2 * dv * e + dk * 4) + 2 * st
+               + tok * (2 * dk * e + dk * 4))
+        return byt, tok * (4 * dk * dv + C * dv + 2 * C * dk)
+    if stage == "bwd_dv":    # reads Kh, A, dS, dO; writes dv
+        byt = tokp * dk * e + BH * N * C * C * e + st + 2 * tok * dv * e
+        return byt, tok * (2 * dk * dv + C * dv)
     if stage == "gate_tot":
         return 2 * BH * N * (dv // 64) * dk * 4 + BH * N * dk * 4, 0
     if stage == "gate_grad":

@@ -130,7 +130,9 @@ struct Tracer {
 const char* const kFwdMat[] = {"gate_cumsum", "intra", "state_scan", "output"};
 const char* const kFwdRec[] = {"intra", "fwd_fused"};
 const char* const kBwd[] = {"intra", "state_scan_fwd", "state_scan_rev", "state_dot",
-                            "bwd_chunk", "gate_tot", "gate_grad"};
+                            "bwd_dqk", "bwd_dv", "gate_tot", "gate_grad"};
+const char* const kBwdOne[] = {"intra", "state_scan_fwd", "state_scan_rev", "state_dot",
+                               "bwd_chunk", "gate_tot", "gate_grad"};
 
 int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, int max) {
   const char* const* src;
@@ -138,8 +140,10 @@ int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, in
   if (pass == GLA_PASS_FWD) {
     if (d->state_mode == GLA_STATES_MATERIALIZED) { src = kFwdMat; n = 4; }
     else { src = kFwdRec; n = 2; }
+  } else if (gla::bwd_split(d->dtype, d->chunk)) {
+    src = kBwd; n = 8;
   } else {
-    src = kBwd; n = 7;
+    src = kBwdOne; n = 7;
   }
   int m = 0;
   for (int j = 0; j < n; ++j) {
@@ -374,6 +378,11 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   if ((rs = tr.mark()) != GLA_OK) return rs;
   rs = dev(gla::launch_bwd_chunk(ba, s));
   if (rs != GLA_OK) return rs;
+  if (gla::bwd_split(x.dtype, C)) {
+    if ((rs = tr.mark()) != GLA_OK) return rs;
+    rs = dev(gla::launch_bwd_dv(ba, s));
+    if (rs != GLA_OK) return rs;
+  }
   if ((rs = tr.mark()) != GLA_OK) return rs;
   rs = dev(gla::launch_gate_carry((const float*)(w + p.crossF), (const float*)(w + p.crossR),
                                   dS_T ? (const float*)(w + p.cT) : nullptr, (float*)(w + p.carry),

@@ -74,6 +74,10 @@ struct BwdArgs {
   void *dq, *dk_out, *dv_out;
   float* Dloc;
 };
+// The backward chunk work: with bf16 operands and chunk 64 it is two kernels (dq/dk/D,
+// then dv: launch_bwd_chunk and launch_bwd_dv); otherwise one (launch_bwd_chunk).
+bool bwd_split(int dtype, int C);
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dv(const BwdArgs& a, hipStream_t s);
 
 }  // namespace gla

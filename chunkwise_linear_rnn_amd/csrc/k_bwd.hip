@@ -22,11 +22,13 @@
 // chunk totals that the two state scans form from their fp32 states.
 //
 // Kernels
-//   k_bwd_dqk  (chunk 64) dq, dk and D.  One pass over 64-wide dv blocks accumulates dA,
-//              dO S^T and V dS^T together: dO and V tiles go through LDS (shared by the 4
-//              waves), each wave's S / dS fragments are prefetched straight into registers
-//              (double-buffered); then the intra-chunk part runs per 64-wide dk block.
-//   k_bwd_dv   (chunk 64) dv = Kh dS + A^T dO per (chunk, 64 values), XCD-aware.
+//   k_bwd_dqk  (chunk 64) dq, dk and D per (chunk, 64-wide dk block).  One pass over
+//              64-wide dv blocks accumulates dA, dO S^T and V dS^T together: dO and V
+//              tiles go through LDS (shared by the 4 waves), each wave's S / dS fragments
+//              are prefetched straight into registers (double-buffered); then the
+//              intra-chunk part of the block.
+//   k_bwd_dv   (chunk 64) dv = A^T dO + Kh dS per (chunk, 64 values), looping over
+//              64-wide dk blocks, XCD-aware.
 //   k_bwd_chunk (chunk 128, and fp32 operands) all of the above in one workgroup per
 //              chunk, operands read straight from memory.
 #include "gla_common.cuh"
@@ -212,67 +214,68 @@ __device__ __forceinline__ void bwd_finish_block(const IntraLds<C, DB, Tin>& L,
 }
 
 // =====================================================================================
-// chunk 64: k_bwd_dqk
+// chunk 64: k_bwd_dqk, one workgroup per (batch*head, chunk, 64-wide dk block)
 // =====================================================================================
-template <typename Tin, typename OpT, int DK>
+// Wave w owns columns 16w .. 16w+15 of the block for all 64 rows of the chunk (four
+// accumulator tiles each for dq and dk).  dA = tril(dO V^T) is formed by every dk block of
+// the chunk (it is cheap next to the dO S^T and V dS^T products, and keeps the blocks
+// independent).  Three workgroups fit on a CU, so one's loads overlap another's math.
+template <typename Tin, typename OpT>
 __global__ __launch_bounds__(kThreads) void k_bwd_dqk(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dO, const float* __restrict__ g, const OpT* __restrict__ S,
     const OpT* __restrict__ dS, Tin* __restrict__ dq, Tin* __restrict__ dk_out,
-    float* __restrict__ Dloc, int T, int dv, int N) {
+    float* __restrict__ Dloc, int T, int dk, int dv, int N) {
   static_assert(sizeof(Tin) == sizeof(OpT), "input and operand types match");
-  constexpr int C = 64, NM = 4, NJ = DK / 64, DB = 64, YLD = 64 + 8;
-  using IL = IntraLds<C, DB, Tin>;
-  constexpr int o_dA = 0;
-  constexpr int o_p = C * IL::FLD * 4;
-  constexpr int b1 = 2 * C * YLD * (int)sizeof(OpT);
-  constexpr int bytes = o_p + (b1 > IL::bytes_blk ? b1 : IL::bytes_blk);
+  constexpr int C = 64, NM = 4, NS = C / 16, YLD = 64 + 8;
+  constexpr int FLD = C + 4, GLD = 64 + 4, XLD = 64 + 8;
+  // LDS: dA [C][FLD] fp32, then a region that holds the dO / V tiles during the dv loop
+  // and g [C][GLD] fp32, q, k [C][XLD] afterwards.  53248 bytes: three workgroups per CU.
+  constexpr int o_u = C * FLD * 4, o_q = o_u + C * GLD * 4, o_k = o_q + C * XLD * 2;
+  constexpr int bytes = o_k + C * XLD * 2;
+  static_assert(2 * C * YLD * 2 <= bytes - o_u, "dO / V tiles fit the shared region");
   __shared__ __attribute__((aligned(16))) char arena[bytes];
-  OpT* dOs = (OpT*)(arena + o_p);
+  float* dAs = (float*)arena;
+  OpT* dOs = (OpT*)(arena + o_u);
   OpT* Vs = dOs + C * YLD;
-  IL L;
-  L.dAs = (float*)(arena + o_dA);
-  L.gs = (float*)(arena + o_p);
-  L.qs = (Tin*)(arena + o_p + C * IL::GLD * 4);
-  L.ks = L.qs + C * IL::XLD;
-  L.dqd = (float*)(L.ks + C * IL::XLD);
-  L.dkd = L.dqd + C * IL::GLD;
+  float* gs = (float*)(arena + o_u);
+  Tin* qs = (Tin*)(arena + o_q);
+  Tin* ks = (Tin*)(arena + o_k);
 
-  const int i = blockIdx.x, bh = blockIdx.y;
-  const int t0 = i * C, rows = min(C, T - t0);
+  // XCD-aware: the dk blocks of one chunk (same dO and V tiles) are consecutive
+  const int NJ = dk / 64;
+  const int lt = xcd_logical(blockIdx.x, gridDim.x);
+  const int jb = lt % NJ, i = (lt / NJ) % N, bh = lt / (NJ * N);
+  const int d0 = 64 * jb, t0 = i * C, rows = min(C, T - t0);
   const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
+  const int c = 16 * w + r;   // this lane's column in the block
   const long tok0 = (long)bh * T + t0;
-  const OpT* Si = S + ((long)bh * N + i) * DK * dv;
-  const OpT* dSi = dS + ((long)bh * N + i) * DK * dv;
+  const OpT* Si = S + ((long)bh * N + i) * dk * dv;
+  const OpT* dSi = dS + ((long)bh * N + i) * dk * dv;
   const int NV = dv / 64;
 
-  f32x4 adq[NJ][NM], adk[NJ][NM], adA[NM];   // adA[n] = dA tile (w, n), n <= w
+  f32x4 adq[NM], adk[NM], adA[NM];   // adA[n] = dA tile (w, n), n <= w
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      adq[j][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-      adk[j][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-  for (int n = 0; n < NM; ++n) adA[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < NM; ++m) {
+    adq[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    adk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    adA[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   RowTile<OpT, C, 64, YLD> tdO, tV;
-  Frag<OpT> sA[NJ][2], dsA[NJ][2], sB[NJ][2], dsB[NJ][2];
-  auto fetch = [&](int vb, Frag<OpT> (&fs)[NJ][2], Frag<OpT> (&fds)[NJ][2]) {
+  Frag<OpT> sA[2], dsA[2], sB[2], dsB[2];
+  auto fetch = [&](int vb, Frag<OpT> (&fs)[2], Frag<OpT> (&fds)[2]) {
     tdO.load((const OpT*)dO + tok0 * dv + vb * 64, dv, rows);
     tV.load((const OpT*)v + tok0 * dv + vb * 64, dv, rows);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const long off = (long)(64 * j + 16 * w + r) * dv + vb * 64 + kb * 32;
-        load_frag_c(fs[j][kb], Si + off);
-        load_frag_c(fds[j][kb], dSi + off);
-      }
+    for (int kb = 0; kb < 2; ++kb) {
+      const long off = (long)(d0 + c) * dv + vb * 64 + kb * 32;
+      load_frag_c(fs[kb], Si + off);
+      load_frag_c(fds[kb], dSi + off);
+    }
   };
-  auto body = [&](int vb, Frag<OpT> (&fs)[NJ][2], Frag<OpT> (&fds)[NJ][2],
-                  Frag<OpT> (&ns)[NJ][2], Frag<OpT> (&nds)[NJ][2]) {
+  auto body = [&](int vb, Frag<OpT> (&fs)[2], Frag<OpT> (&fds)[2], Frag<OpT> (&ns)[2],
+                  Frag<OpT> (&nds)[2]) {
     tdO.store(dOs);
     tV.store(Vs);
     __syncthreads();
@@ -287,12 +290,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dqk(
       }
       load_frag_c(fOw, dOs + (16 * w + r) * YLD + kb * 32);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          mma(adq[j][m], fO[m], fs[j][kb]);
-          mma(adk[j][m], fV[m], fds[j][kb]);
-        }
+      for (int m = 0; m < NM; ++m) {
+        mma(adq[m], fO[m], fs[kb]);
+        mma(adk[m], fV[m], fds[kb]);
+      }
 #pragma unroll
       for (int n = 0; n < NM; ++n)
         if (n <= w) mma(adA[n], fOw, fV[n]);
@@ -307,106 +308,259 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dqk(
   }
   if (vb < NV) body(vb, sA, dsA, sB, dsB);
 
-  // dA tiles (w, n <= w) to LDS, diagonal tile masked above the diagonal
+  // dA tiles (w, n <= w) to LDS, the diagonal tile masked above the diagonal; the
+  // block's g, q, k into the region the dO / V tiles used
 #pragma unroll
   for (int n = 0; n < NM; ++n)
     if (n <= w) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tl = 4 * qd + e;
-        L.dAs[(16 * w + tl) * IL::FLD + 16 * n + r] = (n == w && r > tl) ? 0.f : adA[n][e];
+        dAs[(16 * w + tl) * FLD + 16 * n + r] = (n == w && r > tl) ? 0.f : adA[n][e];
       }
     }
-
-  // intra-chunk part and D, per 64-wide dk block (wave w: columns 16w.. of each block)
+  // g (times log2 e; rows past T continue the last valid row), q, k of the block
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    bwd_stage_block<C, DB, DK, Tin>(L, q, k, g, tok0, rows, 64 * j);
-    bwd_finish_block<C, DB, DK, NM, 1, Tin, OpT>(L, adq[j], adk[j], dq, dk_out, Dloc, tok0, rows,
-                                                 64 * j, w, 0);
+  for (int u = 0; u < 4; ++u) {
+    const int idx = threadIdx.x + kThreads * u, rr = idx / 16, cc = (idx % 16) * 4;
+    *reinterpret_cast<f32x4*>(gs + rr * GLD + cc) =
+        *reinterpret_cast<const f32x4*>(g + (tok0 + min(rr, rows - 1)) * dk + d0 + cc);
+  }
+  {
+    RowTile<Tin, C, 64, XLD> tq, tk;
+    tq.load(q + tok0 * dk + d0, dk, rows);
+    tk.load(k + tok0 * dk + d0, dk, rows);
+    tq.store(qs);
+    tk.store(ks);
+  }
+  __syncthreads();
+
+  // inter-chunk parts: dq *= exp(g_t), dk *= exp(gamma - g_t)
+  const float gl = gs[(C - 1) * GLD + c];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float gt = gs[(16 * m + 4 * qd + e) * GLD + c];
+      adq[m][e] *= __builtin_amdgcn_exp2f(gt);
+      adk[m][e] *= __builtin_amdgcn_exp2f(gl - gt);
+    }
+  // intra-chunk, off-diagonal sub-blocks (split bf16 operands, three MFMAs each)
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    if (m > 0) {   // dq rows of sub-chunk I = m, sources J < I, rebased on rho = 16 m
+      const int rho = 16 * m;
+      const float gr = gs[rho * GLD + c];
+      f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < (16 * m + 31) / 32; ++kb) {
+        SFrag<OpT> fa, fb;
+        float xa[8];
+        load8(xa, dAs + (16 * m + r) * FLD + kb * 32 + 8 * qd);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int s = kb * 32 + 8 * qd + e;
+          // dA is only written below its diagonal: mask the rest on both operands
+          fa.set(e, s < rho ? xa[e] : 0.f);
+          fb.set(e, s < rho ? to_f32(ks[s * XLD + c]) * __builtin_amdgcn_exp2f(gr - gs[s * GLD + c])
+                            : 0.f);
+        }
+        mma_split(tmp, fa, fb);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        adq[m][e] += tmp[e] * __builtin_amdgcn_exp2f(gs[(rho + 4 * qd + e) * GLD + c] - gr);
+    }
+    if (m < NS - 1) {   // dk rows of sub-chunk J = m, sources I > J, rebased on rho' = 16 m + 15
+      const int rho = 16 * m + 15;
+      const float gr = gs[rho * GLD + c];
+      f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = (16 * m + 16) / 32; kb < C / 32; ++kb) {
+        SFrag<OpT> fa, fb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = kb * 32 + 8 * qd + e;
+          const bool on = t > rho;
+          fa.set(e, on ? dAs[t * FLD + 16 * m + r] : 0.f);
+          fb.set(e, on ? to_f32(qs[t * XLD + c]) * __builtin_amdgcn_exp2f(gs[t * GLD + c] - gr) : 0.f);
+        }
+        mma_split(tmp, fa, fb);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        adk[m][e] += tmp[e] * __builtin_amdgcn_exp2f(gr - gs[(16 * m + 4 * qd + e) * GLD + c]);
+    }
+  }
+  // intra-chunk, diagonal sub-blocks in fp32 log space: thread (sub-chunk md, column cd)
+  float aq[16], ak[16];
+  const int md = threadIdx.x / 64, cd = threadIdx.x % 64, base = 16 * md;
+  {
+    float gt[16], qv[16], kv[16];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      gt[jj] = gs[(base + jj) * GLD + cd];
+      qv[jj] = to_f32(qs[(base + jj) * XLD + cd]);
+      kv[jj] = to_f32(ks[(base + jj) * XLD + cd]);
+      aq[jj] = 0.f;
+      ak[jj] = 0.f;
+    }
+    const float* dAm = dAs + base * FLD + base;
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+#pragma unroll
+      for (int s = 0; s <= t; ++s) {
+        const float ex = __builtin_amdgcn_exp2f(gt[t] - gt[s]) * dAm[t * FLD + s];
+        aq[t] += ex * kv[s];
+        ak[s] += ex * qv[t];
+      }
+  }
+  __syncthreads();   // dA and g are dead from here: their regions carry the diagonal terms
+  float* dqd = dAs;   // [C][FLD]
+  float* dkd = gs;    // [C][GLD]
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    dqd[(base + jj) * FLD + cd] = aq[jj];
+    dkd[(base + jj) * GLD + cd] = ak[jj];
+  }
+  __syncthreads();
+  // finish dq, dk; D = q*dq - k*dk and its chunk-local suffix sums, in registers
+  float Dv[NM][4];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * m + 4 * qd + e;
+      const float vq = adq[m][e] + dqd[t * FLD + c];
+      const float vk = adk[m][e] + dkd[t * GLD + c];
+      if (t < rows) {
+        dq[(tok0 + t) * dk + d0 + c] = from_f32<Tin>(vq);
+        dk_out[(tok0 + t) * dk + d0 + c] = from_f32<Tin>(vk);
+      }
+      Dv[m][e] = to_f32(qs[t * XLD + c]) * vq - to_f32(ks[t * XLD + c]) * vk;
+    }
+  // rows of this lane: 16 m + 4 qd + e.  Suffix sums within the lane, then across the
+  // four lane groups of the column (lanes r + 16 q') and the later sub-chunks.
+  float tot[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    Dv[m][2] += Dv[m][3];
+    Dv[m][1] += Dv[m][2];
+    Dv[m][0] += Dv[m][1];
+    tot[m] = Dv[m][0];
+  }
+  float later = 0.f;   // sum over sub-chunks after m, all lane groups
+#pragma unroll
+  for (int m = NM - 1; m >= 0; --m) {
+    float after = later, all = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < 4; ++g2) {
+      const float x = __shfl(tot[m], r + 16 * g2);
+      all += x;
+      if (g2 > qd) after += x;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * m + 4 * qd + e;
+      if (t < rows) Dloc[(tok0 + t) * dk + d0 + c] = Dv[m][e] + after;
+    }
+    later += all;
   }
 }
 
 // =====================================================================================
-// chunk 64: k_bwd_dv
+// chunk 64: k_bwd_dv, one workgroup per (batch*head, chunk, 64 values)
 // =====================================================================================
-template <typename Tin, typename OpT, int DK>
+// dv = A^T dO + sum over 64-wide dk blocks of Kh_blk dS_blk; the next block's Kh and
+// dS^T tiles are loaded into registers while the current one multiplies.
+template <typename Tin, typename OpT>
 __global__ __launch_bounds__(kThreads) void k_bwd_dv(const OpT* __restrict__ Kh,
                                                      const OpT* __restrict__ A,
                                                      const OpT* __restrict__ dS,
                                                      const Tin* __restrict__ dO,
-                                                     Tin* __restrict__ dv_out, int T, int dv,
-                                                     int N) {
-  constexpr int C = 64, NM = 4, KLD = DK + 8, ALD = C + 8, SLD = DK + 8, OLD = C + 8,
-                ULD = 64 + 8;
-  __shared__ __attribute__((aligned(16))) OpT ksh[C * KLD];
-  __shared__ __attribute__((aligned(16))) OpT aT[C * ALD];
-  __shared__ __attribute__((aligned(16))) OpT dsT[64 * SLD];
-  __shared__ __attribute__((aligned(16))) OpT doT[64 * OLD];
+                                                     Tin* __restrict__ dv_out, int T, int dk,
+                                                     int dv, int N) {
+  constexpr int C = 64, NM = 4, LD = 64 + 8;
+  __shared__ __attribute__((aligned(16))) OpT ksh[C * LD];   // Kh block [t][k]
+  __shared__ __attribute__((aligned(16))) OpT dsT[64 * LD];  // dS block transposed [v][k]
+  __shared__ __attribute__((aligned(16))) OpT aT[C * LD];    // A^T [t][s]
+  __shared__ __attribute__((aligned(16))) OpT doT[64 * LD];  // dO^T [v][t]
   // XCD-aware: the dv tiles of one chunk share Kh and A
-  const int nvt = dv / 64;
+  const int nvt = dv / 64, NJ = dk / 64;
   const int lt = xcd_logical(blockIdx.x, gridDim.x);
   const int vt = lt % nvt, i = (lt / nvt) % N, bh = lt / (nvt * N);
   const int v0 = vt * 64, t0 = i * C, rows = min(C, T - t0);
-  const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
+  const int w = wave_id(), l = lane_id(), r = l & 15;
+  const OpT* Khc = Kh + ((long)bh * N * C + t0) * dk;
+  const OpT* dSc = dS + ((long)bh * N + i) * dk * dv + v0;
+  RowTile<OpT, C, 64, LD> tk;
+  ColTile<OpT, OpT, 64, LD> ts;
   {
-    FlatTile<OpT, C, DK, KLD> tk;
-    tk.load(Kh + ((long)bh * N * C + t0) * DK);
-    ColTile<OpT, OpT, C, ALD> ta;
+    ColTile<OpT, OpT, C, LD> ta;
+    ColTile<OpT, Tin, C, LD> to;
     ta.load(A + ((long)bh * N + i) * C * C, C, C);
-    tk.store(ksh);
-    ta.store(aT);
-  }
-  {
-    ColTile<OpT, OpT, DK, SLD> ts;
-    ts.load(dS + ((long)bh * N + i) * DK * dv + v0, dv, DK);
-    ColTile<OpT, Tin, C, OLD> to;
     to.load(dO + ((long)bh * T + t0) * dv + v0, dv, rows);
-    ts.store(dsT);
+    tk.load(Khc, dk, C);
+    ts.load(dSc, dv, 64);
+    ta.store(aT);
     to.store(doT);
+    tk.store(ksh);
+    ts.store(dsT);
   }
   __syncthreads();
   f32x4 acc[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kb = 0; kb < DK / 32; ++kb) {
-    Frag<OpT> fb;
-    load_frag_c(fb, dsT + (16 * w + r) * SLD + kb * 32);
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      Frag<OpT> fa;
-      load_frag_c(fa, ksh + (16 * m + r) * KLD + kb * 32);
-      mma(acc[m], fa, fb);
-    }
-  }
-#pragma unroll
   for (int kb = 0; kb < C / 32; ++kb) {
     Frag<OpT> fb;
-    load_frag_c(fb, doT + (16 * w + r) * OLD + kb * 32);
+    load_frag_c(fb, doT + (16 * w + r) * LD + kb * 32);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       if (32 * kb + 31 >= 16 * m) {
         Frag<OpT> fa;
-        load_frag_c(fa, aT + (16 * m + r) * ALD + kb * 32);
+        load_frag_c(fa, aT + (16 * m + r) * LD + kb * 32);
         mma(acc[m], fa, fb);
       }
     }
   }
-  __syncthreads();
-  Tin* outs = (Tin*)ksh;   // reuse as [C][ULD]
+  for (int jb = 0; jb < NJ; ++jb) {
+    if (jb + 1 < NJ) {
+      tk.load(Khc + 64 * (jb + 1), dk, C);
+      ts.load(dSc + (long)64 * (jb + 1) * dv, dv, 64);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      Frag<OpT> fb;
+      load_frag_c(fb, dsT + (16 * w + r) * LD + kb * 32);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        Frag<OpT> fa;
+        load_frag_c(fa, ksh + (16 * m + r) * LD + kb * 32);
+        mma(acc[m], fa, fb);
+      }
+    }
+    __syncthreads();
+    if (jb + 1 < NJ) {
+      tk.store(ksh);
+      ts.store(dsT);
+      __syncthreads();
+    }
+  }
+  Tin* outs = (Tin*)ksh;   // [C][LD]
+  const int qd = l >> 4;
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      outs[(16 * m + 4 * qd + e) * ULD + 16 * w + r] = from_f32<Tin>(acc[m][e]);
+      outs[(16 * m + 4 * qd + e) * LD + 16 * w + r] = from_f32<Tin>(acc[m][e]);
   __syncthreads();
   constexpr int kPer = 16 / (int)sizeof(Tin), kUnits = C * 64 / kPer;
   for (int idx = threadIdx.x; idx < kUnits; idx += kThreads) {
     const int e0 = idx * kPer, rr = e0 / 64, cc = e0 % 64;
     if (rr < rows)
       *reinterpret_cast<u32x4*>(dv_out + ((long)bh * T + t0 + rr) * dv + v0 + cc) =
-          *reinterpret_cast<const u32x4*>(outs + rr * ULD + cc);
+          *reinterpret_cast<const u32x4*>(outs + rr * LD + cc);
   }
 }
 
@@ -568,23 +722,17 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(
 template <typename Tin, typename OpT, int C, int DK>
 static hipError_t launch_bwd_t2(const BwdArgs& a, hipStream_t s) {
   if constexpr (C == 64 && sizeof(OpT) == 2) {
-    hipLaunchKernelGGL((k_bwd_dqk<Tin, OpT, DK>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_bwd_dqk<Tin, OpT>), dim3((a.dk / 64) * a.N * a.BH), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,
                        (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq, (Tin*)a.dk_out, a.Dloc, a.T,
-                       a.dv, a.N);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bwd_dv<Tin, OpT, DK>), dim3((a.dv / 64) * a.N * a.BH), dim3(kThreads), 0,
-                       s, (const OpT*)a.Kh, (const OpT*)a.A, (const OpT*)a.dS, (const Tin*)a.dO,
-                       (Tin*)a.dv_out, a.T, a.dv, a.N);
-    return hipGetLastError();
+                       a.dk, a.dv, a.N);
   } else {
     hipLaunchKernelGGL((k_bwd_chunk<Tin, OpT, C, DK>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,
                        (const OpT*)a.A, (const OpT*)a.Kh, (const OpT*)a.S, (const OpT*)a.dS,
                        (Tin*)a.dq, (Tin*)a.dk_out, (Tin*)a.dv_out, a.Dloc, a.T, a.dv, a.N);
-    return hipGetLastError();
   }
+  return hipGetLastError();
 }
 template <typename Tin, typename OpT, int C>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
@@ -596,11 +744,22 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   }
 }
 
+bool bwd_split(int dtype, int C) { return dtype != 0 && C == 64; }
+
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s) {
   if (a.BH == 0 || a.N == 0) return hipSuccess;
   if (a.dtype == 0) return launch_bwd_t<float, float, 64>(a, s);
   if (a.C == 64) return launch_bwd_t<bf16, bf16, 64>(a, s);
   return launch_bwd_t<bf16, bf16, 128>(a, s);
+}
+
+hipError_t launch_bwd_dv(const BwdArgs& a, hipStream_t s) {
+  if (a.BH == 0 || a.N == 0) return hipSuccess;
+  if (!bwd_split(a.dtype, a.C)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_bwd_dv<bf16, bf16>), dim3((a.dv / 64) * a.N * a.BH), dim3(kThreads), 0, s,
+                     (const bf16*)a.Kh, (const bf16*)a.A, (const bf16*)a.dS, (const bf16*)a.dO,
+                     (bf16*)a.dv_out, a.T, a.dk, a.dv, a.N);
+  return hipGetLastError();
 }
 
 }  // namespace gla

@@ -19,11 +19,13 @@ import os
 import re
 import sys
 
-STAGE_KERNEL = {"bwd_chunk": "k_bwd_chunk", "fwd_fused": "k_fwd_fused", "intra": "k_intra",
+STAGE_KERNEL = {"bwd_chunk": "k_bwd_chunk", "bwd_dqk": "k_bwd_dqk", "bwd_dv": "k_bwd_dv",
+                "fwd_fused": "k_fwd_fused", "intra": "k_intra",
                 "state_scan_fwd": "k_state_scan", "state_scan_rev": "k_state_scan",
                 "output": "k_output", "gate_cumsum": "k_gate_cumsum", "gate_grad": "k_gate_grad",
                 "gate_tot": "k_gate_tot"}
-STAGE_SOURCE = {"bwd_chunk": "k_bwd.hip", "fwd_fused": "k_fwd.hip", "intra": "k_intra.hip",
+STAGE_SOURCE = {"bwd_chunk": "k_bwd.hip", "bwd_dqk": "k_bwd.hip", "bwd_dv": "k_bwd.hip",
+                "fwd_fused": "k_fwd.hip", "intra": "k_intra.hip",
                 "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip",
                 "output": "k_fwd.hip", "gate_cumsum": "k_gate.hip", "gate_grad": "k_gate.hip",
                 "gate_tot": "k_gate.hip"}
