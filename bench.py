@@ -42,7 +42,7 @@ METRIC = "GLA fwd+bwd tokens/s at 1.3B shape T=2K, 1 GPU; % of bf16 MFMA peak"
 STAGE_SOURCE = {
     "gate_cumsum": "k_gate.hip", "gate_tot": "k_gate.hip", "gate_grad": "k_gate.hip",
     "state_dot": "k_gate.hip", "intra": "k_intra.hip", "state_scan": "k_state.hip",
-    "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip", "output": "k_fwd.hip",
+    "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip", "state_scans": "k_state.hip", "output": "k_fwd.hip",
     "fwd_fused": "k_fwd.hip", "bwd_chunk": "k_bwd.hip", "bwd_dqk": "k_bwd.hip",
     "bwd_dv": "k_bwd.hip",
 }
@@ -69,9 +69,12 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
             byt = (3 * tok * dk * e + tok * dk * 4 + BH * N * C * C * e + 2 * tokp * dk * 4
                    + tokp * dk * e + BH * N * dk * 4)
         return byt, tok * C * dk
-    if stage in ("state_scan_fwd", "state_scan_rev"):
+    if stage in ("state_scan_fwd", "state_scan_rev", "state_scans"):
+        # one scan: reads Kh^T and Qh^T (fp32 as bf16 pairs), v and dO; writes the states
+        # and the cross-term tiles.  state_scans is both scans in one launch.
         byt = 2 * tokp * dk * 4 + 2 * tok * dv * e + st + BH * N * (dv // 64) * dk * 4
-        return byt, tok * 4 * dk * dv
+        n = 2 if stage == "state_scans" else 1
+        return n * byt, n * tok * 4 * dk * dv
     if stage == "state_scan":
         return tokp * dk * e + tok * dv * e + st + BH * dk * dv * 4, tok * 2 * dk * dv
     if stage == "output":

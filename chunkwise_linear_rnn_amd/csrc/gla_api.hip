@@ -129,10 +129,10 @@ struct Tracer {
 // Stage names of each pipeline, in launch order.
 const char* const kFwdMat[] = {"gate_cumsum", "intra", "state_scan", "output"};
 const char* const kFwdRec[] = {"intra", "fwd_fused"};
-const char* const kBwd[] = {"intra", "state_scan_fwd", "state_scan_rev", "state_dot",
-                            "bwd_dqk", "bwd_dv", "gate_tot", "gate_grad"};
-const char* const kBwdOne[] = {"intra", "state_scan_fwd", "state_scan_rev", "state_dot",
-                               "bwd_chunk", "gate_tot", "gate_grad"};
+const char* const kBwd[] = {"intra", "state_scans", "state_dot", "bwd_dqk", "bwd_dv",
+                            "gate_tot", "gate_grad"};
+const char* const kBwdOne[] = {"intra", "state_scans", "state_dot", "bwd_chunk", "gate_tot",
+                               "gate_grad"};
 
 int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, int max) {
   const char* const* src;
@@ -141,13 +141,13 @@ int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, in
     if (d->state_mode == GLA_STATES_MATERIALIZED) { src = kFwdMat; n = 4; }
     else { src = kFwdRec; n = 2; }
   } else if (gla::bwd_split(d->dtype, d->chunk)) {
-    src = kBwd; n = 8;
+    src = kBwd; n = 7;
   } else {
-    src = kBwdOne; n = 7;
+    src = kBwdOne; n = 6;
   }
   int m = 0;
   for (int j = 0; j < n; ++j) {
-    if (pass == GLA_PASS_BWD && j == 3 && !with_dST) continue;
+    if (pass == GLA_PASS_BWD && j == 2 && !with_dST) continue;
     if (out && m < max) out[m] = src[j];
     ++m;
   }
@@ -354,15 +354,13 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   sa.XT = w + p.KhT; sa.Y = v; sa.X2T = w + p.QhT; sa.Y2 = dO; sa.cross = (float*)(w + p.crossF);
   sa.eg = (const float*)(w + p.eg); sa.S_in = S0; sa.states = w + p.st;
   sa.S_out = dS_T ? (float*)(w + p.ST) : nullptr;
-  if ((rs = tr.mark()) != GLA_OK) return rs;
-  rs = dev(gla::launch_state_scan(sa, s));
-  if (rs != GLA_OK) return rs;
   // reverse scan: dS_[i+1]; cross term rowsum(dS_[i+1] * Kh_i^T V_i)
   gla::ScanArgs ra = sa;
   ra.reverse = true; ra.XT = w + p.QhT; ra.Y = dO; ra.X2T = w + p.KhT; ra.Y2 = v;
   ra.cross = (float*)(w + p.crossR); ra.S_in = dS_T; ra.states = w + p.dst; ra.S_out = dS0;
+  // both scans in one launch
   if ((rs = tr.mark()) != GLA_OK) return rs;
-  rs = dev(gla::launch_state_scan(ra, s));
+  rs = dev(gla::launch_state_scan2(sa, ra, s));
   if (rs != GLA_OK) return rs;
   if (dS_T) {
     if ((rs = tr.mark()) != GLA_OK) return rs;

@@ -48,6 +48,18 @@ struct ScanArgs {
   float* S_out;          // [BH][dk][dv] or NULL
 };
 hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s);
+// Two scans of the same shape and kind (the backward's forward and reverse scans) in one
+// launch, so that their workgroups share the machine.
+hipError_t launch_state_scan2(const ScanArgs& a, const ScanArgs& b, hipStream_t s);
+// Per-direction kernel arguments of the scan kernel.
+struct ScanDir {
+  const void *XT, *Y, *X2T, *Y2;
+  float* cross;
+  const float* S_in;
+  void* states;
+  float* S_out;
+  int reverse;
+};
 
 struct OutArgs {
   int dtype, C, BH, T, dk, dv, N;

@@ -8,8 +8,9 @@
 //     reverse:  dS_[i]   = diag(exp(gamma_i)) dS_[i+1] + Qh_i^T dO_i,  Qh = q*exp(g)
 // Before each chunk the tile is written out (the chunk-start state S_[i], or dS_[i+1]).
 // The product is a k32 MFMA over the chunk's tokens: the transposed decayed operand
-// comes ready-made from the intra-chunk kernel, the value-side tile is staged into LDS
-// transposed so both operands are token-contiguous.  The tile stays in fp32 accumulators
+// comes ready-made from the intra-chunk kernel and each wave loads its own rows of it
+// straight into MFMA fragments; the value-side tile, shared by the four waves, is staged
+// into LDS transposed so both operands are token-contiguous.  The tile stays in fp32 accumulators
 // across the whole sequence.  In the backward the transposed operand arrives as a bf16
 // high part plus bf16 remainder (two MFMAs), so the state carries no operand rounding;
 // the kernel is bound by the state writes, not by the matrix units.
@@ -27,42 +28,68 @@
 
 namespace gla {
 
-// Transposed decayed operand in LDS: rows of C tokens in the operand type, or (SPLIT) a
+// This wave's 16 rows of a per-chunk transposed operand ([rows][XW], XW = C or 2C), as
+// MFMA A fragments held in registers: rows of C tokens in the operand type, or (SPLIT) a
 // bf16 high part in [0, C) and its bf16 remainder in [C, 2C) of each row.
-template <typename OpT, bool SPLIT>
-struct XFrag {
-  Frag<OpT> hi, lo;
-  __device__ __forceinline__ void load(const OpT* row, int kb, int C) {
-    load_frag_c(hi, row + kb * 32);
-    if constexpr (SPLIT) load_frag_c(lo, row + C + kb * 32);
+template <typename OpT, bool SPLIT, int C>
+struct XRegs {
+  static constexpr int KB = C / 32;
+  Frag<OpT> hi[KB], lo[SPLIT ? KB : 1];
+  __device__ __forceinline__ void load(const OpT* __restrict__ row) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      load_frag_c(hi[kb], row + kb * 32);
+      if constexpr (SPLIT) load_frag_c(lo[kb], row + C + kb * 32);
+    }
   }
-  __device__ __forceinline__ void apply(f32x4& acc, const Frag<OpT>& b) const {
-    mma(acc, hi, b);
-    if constexpr (SPLIT) mma(acc, lo, b);
+  __device__ __forceinline__ void apply(f32x4& acc, int kb, const Frag<OpT>& b) const {
+    mma(acc, hi[kb], b);
+    if constexpr (SPLIT) mma(acc, lo[kb], b);
   }
 };
 
+// Sum over the 16 lanes of a DPP row (lanes with the same l / 16), result in every lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_f<0x124>(x);   // row_ror 4
+  x += dpp_f<0x128>(x);   // row_ror 8
+  return x;
+}
+
 template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS>
-__global__ __launch_bounds__(kThreads) void k_state_scan(
-    const OpT* __restrict__ XT, const Tin* __restrict__ Y, const OpT* __restrict__ X2T,
-    const Tin* __restrict__ Y2, float* __restrict__ cross, const float* __restrict__ eg,
-    const float* __restrict__ S_in, void* __restrict__ states, float* __restrict__ S_out,
-    int T, int dk, int dv, int N, int reverse) {
-  constexpr int TV = 64, TK = 64, YLD = C + 8, XW = SPLIT ? 2 * C : C, XLD = XW + 8;
+__global__ __launch_bounds__(kThreads, 4) void k_state_scan(ScanDir d0, ScanDir d1, int ndir,
+                                                            const float* __restrict__ eg, int T,
+                                                            int dk, int dv, int N) {
+  constexpr int TV = 64, YLD = C + 8, XW = SPLIT ? 2 * C : C;
   constexpr int SLD = 64 + 8;   // state tile staging for 16-byte row stores
   using StT = typename std::conditional<STORE == 3, float, OpT>::type;
+  using XR = XRegs<OpT, SPLIT, C>;
   __shared__ __attribute__((aligned(16))) OpT ys[TV * YLD];
   __shared__ __attribute__((aligned(16))) OpT y2s[CROSS ? TV * YLD : 8];
-  __shared__ __attribute__((aligned(16))) OpT xs[TK * XLD];
-  __shared__ __attribute__((aligned(16))) OpT x2s[CROSS ? TK * XLD : 8];
   __shared__ __attribute__((aligned(16))) StT ss[STORE != 0 ? 64 * SLD : 8];
-  __shared__ float egs[TK];
-  // 1-D grid, XCD-aware: the dv tiles of one (bh, dk tile) share the Kh^T / Qh^T tiles
-  // and the dk tiles of one bh share the value-side tiles, so they run on one XCD.
-  const int nvt = dv / TV, nkt = dk / TK;
-  const int lt = xcd_logical(blockIdx.x, gridDim.x);
+  // 1-D grid, XCD-aware: the dv tiles of one (bh, dk tile) share the transposed operand
+  // tiles and the dk tiles of one bh share the value-side tiles, so they run on one XCD.
+  // With two scans in the launch, the first half of the logical ids runs the first.
+  const int nvt = dv / TV, nkt = dk / 64, tiles = (int)gridDim.x / ndir;
+  int lt = xcd_logical(blockIdx.x, gridDim.x);
+  const bool second = lt >= tiles;
+  if (second) lt -= tiles;
+  const OpT* __restrict__ XT = (const OpT*)(second ? d1.XT : d0.XT);
+  const Tin* __restrict__ Y = (const Tin*)(second ? d1.Y : d0.Y);
+  const OpT* __restrict__ X2T = (const OpT*)(second ? d1.X2T : d0.X2T);
+  const Tin* __restrict__ Y2 = (const Tin*)(second ? d1.Y2 : d0.Y2);
+  float* __restrict__ cross = second ? d1.cross : d0.cross;
+  const float* __restrict__ S_in = second ? d1.S_in : d0.S_in;
+  void* __restrict__ states = second ? d1.states : d0.states;
+  float* __restrict__ S_out = second ? d1.S_out : d0.S_out;
+  const int reverse = second ? d1.reverse : d0.reverse;
   const int vt = lt % nvt, kt = (lt / nvt) % nkt, bh = lt / (nvt * nkt);
-  const int v0 = vt * TV, k0 = kt * TK;
+  const int v0 = vt * TV, k0 = kt * 64;
   const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
   const int rl = 16 * w + 4 * qd;          // tile-local accumulator rows rl .. rl+3
   const int row0 = k0 + rl;
@@ -74,22 +101,28 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
     for (int e = 0; e < 4; ++e)
       acc[j][e] = S_in ? S_in[((long)bh * dk + row0 + e) * dv + v0 + 16 * j + r] : 0.f;
 
-  // next chunk's tiles, loaded into registers while the current chunk computes
-  FlatTileRows<OpT, TK, XW, XLD> tx, tx2;
+  // The value-side tiles of the next chunk are loaded into registers (then LDS,
+  // transposed) while the current chunk computes.  This wave's rows of the transposed
+  // operands go straight into MFMA fragments, each reloaded for the next chunk as soon as
+  // the current chunk's products have consumed it (one set of registers, so four
+  // workgroups fit on a CU).
   ColTile<OpT, Tin, C, YLD> ty, ty2;
-  float egr = 0.f;
-  auto fetch = [&](int i) {
+  f32x4 egr;   // exp(gamma) of this lane's rows, for the chunk about to be applied
+  XR cx, cx2;
+  auto xrow = [&](int i) { return (((long)bh * N + i) * dk + k0 + 16 * w + r) * XW; };
+  auto fetch_y = [&](int i) {
     const int t0 = i * C, rows = min(C, T - t0);
-    const long xo = (((long)bh * N + i) * dk + k0) * XW;
-    tx.load(XT + xo);
     ty.load(Y + ((long)bh * T + t0) * dv + v0, dv, rows);
-    if constexpr (CROSS) {
-      tx2.load(X2T + xo);
-      ty2.load(Y2 + ((long)bh * T + t0) * dv + v0, dv, rows);
-    }
-    if (threadIdx.x < TK) egr = eg[((long)bh * N + i) * dk + k0 + threadIdx.x];
+    if constexpr (CROSS) ty2.load(Y2 + ((long)bh * T + t0) * dv + v0, dv, rows);
   };
-  if (N > 0) fetch(reverse ? N - 1 : 0);
+  auto fetch_eg = [&](int i) { egr = *reinterpret_cast<const f32x4*>(eg + ((long)bh * N + i) * dk + row0); };
+  if (N > 0) {
+    const int i0 = reverse ? N - 1 : 0;
+    fetch_y(i0);
+    fetch_eg(i0);
+    cx.load(XT + xrow(i0));
+    if constexpr (CROSS) cx2.load(X2T + xrow(i0));
+  }
 
   // Stores are issued right after the step's first barrier and before the next chunk's
   // loads: vector memory operations complete in order, so a store issued after the
@@ -98,13 +131,10 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
   int i_prev = -1;
   for (int step = 0; step < N; ++step) {
     const int i = reverse ? N - 1 - step : step;
-    tx.store(xs);
+    const int inext = reverse ? i - 1 : i + 1;
+    const bool more = step + 1 < N;
     ty.store(ys);
-    if constexpr (CROSS) {
-      tx2.store(x2s);
-      ty2.store(y2s);
-    }
-    if (threadIdx.x < TK) egs[threadIdx.x] = egr;
+    if constexpr (CROSS) ty2.store(y2s);
     if constexpr (STORE != 0) {
       // the state before this chunk, through LDS
 #pragma unroll
@@ -136,54 +166,43 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
         *reinterpret_cast<f32x4*>(cross + (((long)bh * N + i_prev) * nvt + vt) * dk + row0) = o;
       }
     }
-    if (step + 1 < N) fetch(reverse ? i - 1 : i + 1);
+    if (more) fetch_y(inext);
 
     if constexpr (CROSS) {
-      f32x4 P[4];
+      // P_j = X2^T Y2 for column tile j, folded into the row sums one tile at a time
+      float sum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) P[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4; ++j) {
+        f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < C / 32; ++kb) {
-        XFrag<OpT, SPLIT> fa;
-        fa.load(x2s + (16 * w + r) * XLD, kb, C);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int kb = 0; kb < C / 32; ++kb) {
           Frag<OpT> fb;
           load_frag_c(fb, y2s + (16 * j + r) * YLD + kb * 32);
-          fa.apply(P[j], fb);
+          cx2.apply(P, kb, fb);
         }
-      }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float sum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sum += acc[j][e] * P[j][e];
-        sum += __shfl_xor(sum, 1);
-        sum += __shfl_xor(sum, 2);
-        sum += __shfl_xor(sum, 4);
-        sum += __shfl_xor(sum, 8);
-        part_prev[e] = sum;
+        for (int e = 0; e < 4; ++e) sum[e] += acc[j][e] * P[e];
       }
+      if (more) cx2.load(X2T + xrow(inext));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part_prev[e] = row16_sum(sum[e]);
       i_prev = i;
     }
 
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float dec = egs[rl + e];
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j][e] *= dec;
-    }
+      for (int j = 0; j < 4; ++j) acc[j][e] *= egr[e];
+    if (more) fetch_eg(inext);
 #pragma unroll
-    for (int kb = 0; kb < C / 32; ++kb) {
-      XFrag<OpT, SPLIT> fa;
-      fa.load(xs + (16 * w + r) * XLD, kb, C);
+    for (int kb = 0; kb < C / 32; ++kb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         Frag<OpT> fb;
         load_frag_c(fb, ys + (16 * j + r) * YLD + kb * 32);
-        fa.apply(acc[j], fb);
+        cx.apply(acc[j], kb, fb);
       }
-    }
+    if (more) cx.load(XT + xrow(inext));
     __syncthreads();
   }
   if constexpr (CROSS) {
@@ -202,40 +221,54 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(
 }
 
 template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS>
-static void launch_scan_k(const ScanArgs& a, hipStream_t s) {
-  dim3 grid((a.dv / 64) * (a.dk / 64) * a.BH);
+static void launch_scan_k(const ScanArgs& a, const ScanArgs* b, hipStream_t s) {
+  auto dir = [](const ScanArgs& x) {
+    ScanDir d;
+    d.XT = x.XT; d.Y = x.Y; d.X2T = x.X2T; d.Y2 = x.Y2; d.cross = x.cross; d.S_in = x.S_in;
+    d.states = x.states; d.S_out = x.S_out; d.reverse = x.reverse ? 1 : 0;
+    return d;
+  };
+  const int ndir = b ? 2 : 1;
+  dim3 grid(ndir * (a.dv / 64) * (a.dk / 64) * a.BH);
   hipLaunchKernelGGL((k_state_scan<Tin, OpT, SPLIT, C, STORE, CROSS>), grid, dim3(kThreads), 0, s,
-                     (const OpT*)a.XT, (const Tin*)a.Y, (const OpT*)a.X2T, (const Tin*)a.Y2,
-                     a.cross, a.eg, a.S_in, a.states, a.S_out, a.T, a.dk, a.dv, a.N,
-                     a.reverse ? 1 : 0);
+                     dir(a), dir(b ? *b : a), ndir, a.eg, a.T, a.dk, a.dv, a.N);
 }
 
 template <typename Tin, typename OpT, bool SPLIT, int C>
-static hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
+static hipError_t launch_scan_t(const ScanArgs& a, const ScanArgs* b, hipStream_t s) {
   if (a.cross) {
     // the backward: operand-type states, [dk][dv]
-    launch_scan_k<Tin, OpT, SPLIT, C, 1, true>(a, s);
+    launch_scan_k<Tin, OpT, SPLIT, C, 1, true>(a, b, s);
   } else {
     switch (a.store) {
-      case 0: launch_scan_k<Tin, OpT, SPLIT, C, 0, false>(a, s); break;
-      case 1: launch_scan_k<Tin, OpT, SPLIT, C, 1, false>(a, s); break;
-      case 2: launch_scan_k<Tin, OpT, SPLIT, C, 2, false>(a, s); break;
-      default: launch_scan_k<Tin, OpT, SPLIT, C, 3, false>(a, s); break;
+      case 0: launch_scan_k<Tin, OpT, SPLIT, C, 0, false>(a, b, s); break;
+      case 1: launch_scan_k<Tin, OpT, SPLIT, C, 1, false>(a, b, s); break;
+      case 2: launch_scan_k<Tin, OpT, SPLIT, C, 2, false>(a, b, s); break;
+      default: launch_scan_k<Tin, OpT, SPLIT, C, 3, false>(a, b, s); break;
     }
   }
   return hipGetLastError();
 }
 
-hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s) {
+static hipError_t launch_scans(const ScanArgs& a, const ScanArgs* b, hipStream_t s) {
   if (a.BH == 0 || a.N == 0) return hipSuccess;
   if (a.cross && a.store != 1) return hipErrorInvalidValue;
-  if (a.dtype == 0) return launch_scan_t<float, float, false, 64>(a, s);
+  if (b && (b->dtype != a.dtype || b->C != a.C || b->BH != a.BH || b->T != a.T ||
+            b->dk != a.dk || b->dv != a.dv || b->N != a.N || b->xt_f32 != a.xt_f32 ||
+            b->store != a.store || (b->cross != nullptr) != (a.cross != nullptr) || b->eg != a.eg))
+    return hipErrorInvalidValue;
+  if (a.dtype == 0) return launch_scan_t<float, float, false, 64>(a, b, s);
   if (a.xt_f32) {
-    if (a.C == 64) return launch_scan_t<bf16, bf16, true, 64>(a, s);
-    return launch_scan_t<bf16, bf16, true, 128>(a, s);
+    if (a.C == 64) return launch_scan_t<bf16, bf16, true, 64>(a, b, s);
+    return launch_scan_t<bf16, bf16, true, 128>(a, b, s);
   }
-  if (a.C == 64) return launch_scan_t<bf16, bf16, false, 64>(a, s);
-  return launch_scan_t<bf16, bf16, false, 128>(a, s);
+  if (a.C == 64) return launch_scan_t<bf16, bf16, false, 64>(a, b, s);
+  return launch_scan_t<bf16, bf16, false, 128>(a, b, s);
+}
+
+hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s) { return launch_scans(a, nullptr, s); }
+hipError_t launch_state_scan2(const ScanArgs& a, const ScanArgs& b, hipStream_t s) {
+  return launch_scans(a, &b, s);
 }
 
 }  // namespace gla

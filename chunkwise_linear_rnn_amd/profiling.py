@@ -22,11 +22,13 @@ import sys
 STAGE_KERNEL = {"bwd_chunk": "k_bwd_chunk", "bwd_dqk": "k_bwd_dqk", "bwd_dv": "k_bwd_dv",
                 "fwd_fused": "k_fwd_fused", "intra": "k_intra",
                 "state_scan_fwd": "k_state_scan", "state_scan_rev": "k_state_scan",
+                "state_scans": "k_state_scan",
                 "output": "k_output", "gate_cumsum": "k_gate_cumsum", "gate_grad": "k_gate_grad",
                 "gate_tot": "k_gate_tot"}
 STAGE_SOURCE = {"bwd_chunk": "k_bwd.hip", "bwd_dqk": "k_bwd.hip", "bwd_dv": "k_bwd.hip",
                 "fwd_fused": "k_fwd.hip", "intra": "k_intra.hip",
                 "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip",
+                "state_scans": "k_state.hip",
                 "output": "k_fwd.hip", "gate_cumsum": "k_gate.hip", "gate_grad": "k_gate.hip",
                 "gate_tot": "k_gate.hip"}
 
@@ -63,7 +65,7 @@ def counters(fetch_csv, write_csv, copy_bytes, stage, workload, command, root):
     sel = STAGE_KERNEL[stage]
     kf = [v for n, v in f if sel in n]
     kw = [v for n, v in w if sel in n]
-    if stage.startswith("state_scan"):   # two scans per step, same kernel: keep one of each pair
+    if stage in ("state_scan_fwd", "state_scan_rev"):   # two launches per step: keep one of each pair
         kf, kw = kf[0::2] if stage.endswith("fwd") else kf[1::2], kw[0::2] if stage.endswith("fwd") else kw[1::2]
     sf = copy_bytes / (1024.0 * (sum(copy_f) / len(copy_f)))
     sw = copy_bytes / (1024.0 * (sum(copy_w) / len(copy_w)))
