@@ -211,31 +211,32 @@ __device__ __forceinline__ void mma_split(f32x4& acc, const SFrag<OpT>& a, const
 
 // ---------------------------------------------------------------------------------
 // Register-staged tile copies (global -> registers now, registers -> LDS later), so
-// the next chunk's loads are in flight while the current chunk computes.
+// the next chunk's loads are in flight while the current chunk computes.  NT is the
+// workgroup size (all of its threads take part).
 // ---------------------------------------------------------------------------------
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // A contiguous global tile of ROWS x COLS elements (row-major, COLS contiguous) moved as
 // 16-byte units into an LDS tile with row stride LD (elements).
-template <typename T, int ROWS, int COLS, int LD>
+template <typename T, int ROWS, int COLS, int LD, int NT = kThreads>
 struct FlatTile {
   static constexpr int kPer = 16 / (int)sizeof(T);            // elements per unit
   static constexpr int kUnits = ROWS * COLS / kPer;
-  static constexpr int kPerThread = (kUnits + kThreads - 1) / kThreads;
+  static constexpr int kPerThread = (kUnits + NT - 1) / NT;
   u32x4 u[kPerThread];
   __device__ __forceinline__ void load(const T* __restrict__ g) {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      const int idx = threadIdx.x + j * kThreads;
-      if (kUnits % kThreads == 0 || idx < kUnits)
+      const int idx = threadIdx.x + j * NT;
+      if (kUnits % NT == 0 || idx < kUnits)
         u[j] = *reinterpret_cast<const u32x4*>(g + (long)idx * kPer);
     }
   }
   __device__ __forceinline__ void store(T* lds) const {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      const int idx = threadIdx.x + j * kThreads;
-      if (kUnits % kThreads == 0 || idx < kUnits) {
+      const int idx = threadIdx.x + j * NT;
+      if (kUnits % NT == 0 || idx < kUnits) {
         const int e = idx * kPer, r = e / COLS, c = e % COLS;
         *reinterpret_cast<u32x4*>(lds + r * LD + c) = u[j];
       }
@@ -245,28 +246,28 @@ struct FlatTile {
 
 // ROWS x COLS tile of a row-major [*, gld] matrix (rows beyond `rows` zero) moved as
 // 16-byte units into an LDS tile with row stride LD, same orientation.
-template <typename T, int ROWS, int COLS, int LD>
+template <typename T, int ROWS, int COLS, int LD, int NT = kThreads>
 struct RowTile {
   static constexpr int kPer = 16 / (int)sizeof(T);
   static constexpr int kUnitsRow = COLS / kPer;
   static constexpr int kUnits = ROWS * kUnitsRow;
-  static constexpr int kPerThread = (kUnits + kThreads - 1) / kThreads;
+  static constexpr int kPerThread = (kUnits + NT - 1) / NT;
   u32x4 u[kPerThread];
   __device__ __forceinline__ void load(const T* __restrict__ g, long gld, int rows) {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      const int idx = threadIdx.x + j * kThreads;
+      const int idx = threadIdx.x + j * NT;
       const int r = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
-      if (kUnits % kThreads == 0 || idx < kUnits)
+      if (kUnits % NT == 0 || idx < kUnits)
         u[j] = r < rows ? *reinterpret_cast<const u32x4*>(g + r * gld + c) : u32x4{0u, 0u, 0u, 0u};
     }
   }
   __device__ __forceinline__ void store(T* lds) const {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      const int idx = threadIdx.x + j * kThreads;
+      const int idx = threadIdx.x + j * NT;
       const int r = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
-      if (kUnits % kThreads == 0 || idx < kUnits)
+      if (kUnits % NT == 0 || idx < kUnits)
         *reinterpret_cast<u32x4*>(lds + r * LD + c) = u[j];
     }
   }
@@ -281,19 +282,19 @@ using FlatTileRows = FlatTile<T, ROWS, COLS, LD>;
 // transposed (lds[c * LD + r]) through 2-row x 8-column units.  The loads keep the raw
 // 16-byte words (no use of the data until store), so they stay in flight.  Input and
 // LDS element types are the same (bf16 or fp32).
-template <typename OpT, typename Tin, int ROWS, int LD>
+template <typename OpT, typename Tin, int ROWS, int LD, int NT = kThreads>
 struct ColTile {
   static_assert(sizeof(OpT) == sizeof(Tin), "same element type in and out");
   static constexpr int kWords = sizeof(Tin) == 2 ? 1 : 2;   // 16-byte words per 8 elements
   static constexpr int kUnits = (ROWS / 2) * 8;
-  static constexpr int kPerThread = (kUnits + kThreads - 1) / kThreads;
+  static constexpr int kPerThread = (kUnits + NT - 1) / NT;
   u32x4 x0[kPerThread][kWords], x1[kPerThread][kWords];
   __device__ __forceinline__ void load(const Tin* __restrict__ g, long gld, int rows) {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      const int idx = threadIdx.x + j * kThreads;
+      const int idx = threadIdx.x + j * NT;
       const int r = (idx / 8) * 2, c = (idx % 8) * 8;
-      if (kUnits % kThreads == 0 || idx < kUnits) {
+      if (kUnits % NT == 0 || idx < kUnits) {
 #pragma unroll
         for (int h = 0; h < kWords; ++h) {
           const int ce = c + h * (8 / kWords);
@@ -307,9 +308,9 @@ struct ColTile {
   __device__ __forceinline__ void store(OpT* lds) const {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      const int idx = threadIdx.x + j * kThreads;
+      const int idx = threadIdx.x + j * NT;
       const int r = (idx / 8) * 2, c = (idx % 8) * 8;
-      if (kUnits % kThreads == 0 || idx < kUnits) {
+      if (kUnits % NT == 0 || idx < kUnits) {
         if constexpr (sizeof(OpT) == 2) {
           // word w of a row holds elements 2w (low half) and 2w+1 (high half)
 #pragma unroll

@@ -10,15 +10,19 @@
 //                O_i = Qh_i S + A_i V_i, then S <- diag(exp(gamma_i)) S + Kh_i^T V_i.  No
 //                per-chunk state ever reaches memory.  The state accumulators feed the
 //                Qh S product directly as the MFMA B operand (acc-order fragments).
-//                Chunk 64: each chunk's Qh, Kh^T, A and V^T tiles are staged into LDS
-//                with cooperative 16-byte loads, the next chunk's tiles are loaded into
-//                registers while the current one computes, and O leaves through LDS as
-//                16-byte row stores.  Chunk 128 and fp32 operands (tiles too large for
+//                Chunk 64: eight waves, wave w holding the 16 value columns w % 4 of the
+//                state rows of dk half w / 4; O is the sum of the two halves' partial
+//                products (added through LDS).  Each chunk's Qh, Kh^T, A and V^T tiles are
+//                staged into LDS with cooperative 16-byte loads, the next chunk's tiles
+//                are loaded into registers while the current one computes, and O leaves
+//                through LDS as 16-byte row stores.  Chunk 128 and fp32 operands (tiles too large for
 //                LDS) read the operand fragments straight from memory.
 #include "gla_common.cuh"
 #include "gla_internal.h"
 
 namespace gla {
+
+constexpr int kFusedThreads = 512;   // eight waves: two per SIMD on the one CU a tile gets
 
 template <typename Tin, typename OpT, int C>
 __global__ __launch_bounds__(kThreads) void k_output(const OpT* __restrict__ Qh,
@@ -79,36 +83,39 @@ __global__ __launch_bounds__(kThreads) void k_output(const OpT* __restrict__ Qh,
 }
 
 template <typename Tin, typename OpT, int C, int DK>
-__global__ __launch_bounds__(kThreads) void k_fwd_fused_staged(
+__global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
     const OpT* __restrict__ Qh, const OpT* __restrict__ KhT, const OpT* __restrict__ A,
     const float* __restrict__ eg, const Tin* __restrict__ V, const float* __restrict__ S0,
     Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N) {
-  constexpr int TV = 64, NM = C / 16, NP = DK / 16;
-  constexpr int QLD = DK + 8, KLD = C + 8, ALD = C + 8, VLD = C + 8, OLD = TV + 8;
+  constexpr int NT = kFusedThreads, TV = 64, NM = C / 16, KH = DK / 2, NP = KH / 16;
+  constexpr int QLD = DK + 8, KLD = C + 8, ALD = C + 8, VLD = C + 8, OLD = TV + 8, RLD = TV + 4;
   __shared__ __attribute__((aligned(16))) OpT qs[C * QLD];
   __shared__ __attribute__((aligned(16))) OpT ks[DK * KLD];
   __shared__ __attribute__((aligned(16))) OpT as_[C * ALD];
   __shared__ __attribute__((aligned(16))) OpT vs[TV * VLD];
   __shared__ __attribute__((aligned(16))) Tin os_[2][C * OLD];   // O tile, double-buffered
+  __shared__ __attribute__((aligned(16))) float red[C * RLD];     // partial O of the upper dk half
   __shared__ float egs[DK];
   // 1-D grid, XCD-aware: the dv tiles of one bh share every Qh / Kh^T / A tile
   const int nvt = dv / TV;
   const int lt = xcd_logical(blockIdx.x, gridDim.x);
   const int v0 = (lt % nvt) * TV, bh = lt / nvt;
-  const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
-  const int col = v0 + 16 * w + r;
+  // wave w: value columns 16 (w % 4) .. +15, state rows kh*KH .. kh*KH + KH-1 (kh = w / 4)
+  const int w = threadIdx.x >> 6, vc = w & 3, kh = w >> 2;
+  const int l = lane_id(), r = l & 15, qd = l >> 4;
+  const int c16 = 16 * vc + r, col = v0 + c16, k0 = kh * KH;
 
-  f32x4 S[NP];   // S[p][e] = state[16p + 4qd + e][col]
+  f32x4 S[NP];   // S[p][e] = state[k0 + 16p + 4qd + e][col]
 #pragma unroll
   for (int p = 0; p < NP; ++p)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      S[p][e] = S0 ? S0[((long)bh * DK + 16 * p + 4 * qd + e) * dv + col] : 0.f;
+      S[p][e] = S0 ? S0[((long)bh * DK + k0 + 16 * p + 4 * qd + e) * dv + col] : 0.f;
 
-  FlatTile<OpT, C, DK, QLD> tq;
-  FlatTile<OpT, DK, C, KLD> tk;
-  FlatTile<OpT, C, C, ALD> ta;
-  ColTile<OpT, Tin, C, VLD> tv;
+  FlatTile<OpT, C, DK, QLD, NT> tq;
+  FlatTile<OpT, DK, C, KLD, NT> tk;
+  FlatTile<OpT, C, C, ALD, NT> ta;
+  ColTile<OpT, Tin, C, VLD, NT> tv;
   float egr = 0.f;
   auto fetch = [&](int i) {
     const int t0 = i * C;
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd_fused_staged(
   auto store_o = [&](int ip) {
     const int tp = ip * C, rp = min(C, T - tp);
     const Tin* ob = os_[ip & 1];
-    for (int idx = threadIdx.x; idx < kUnits; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < kUnits; idx += NT) {
       const int e0 = idx * kPer, rr = e0 / TV, cc = e0 % TV;
       if (rr < rp)
         *reinterpret_cast<u32x4*>(O + ((long)bh * T + tp + rr) * dv + v0 + cc) =
@@ -143,55 +150,68 @@ __global__ __launch_bounds__(kThreads) void k_fwd_fused_staged(
     if (i > 0) store_o(i - 1);
     if (i + 1 < N) fetch(i + 1);
 
-    // O_i = Qh_i S + A_i V_i
+    // O_i = Qh_i S + A_i V_i as two partial sums, one per dk half; the A V rows are split
+    // between the halves
     f32x4 acc[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) {
+    for (int kb = 0; kb < KH / 32; ++kb) {
       Frag<OpT> fb;
       frag_from_acc(fb, S[2 * kb], S[2 * kb + 1]);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         Frag<OpT> fa;
-        load_frag_a(fa, qs + (16 * m + r) * QLD + kb * 32);
+        load_frag_a(fa, qs + (16 * m + r) * QLD + k0 + kb * 32);
         mma(acc[m], fa, fb);
       }
     }
 #pragma unroll
     for (int kb = 0; kb < C / 32; ++kb) {
       Frag<OpT> fb;
-      load_frag_c(fb, vs + (16 * w + r) * VLD + kb * 32);
+      load_frag_c(fb, vs + c16 * VLD + kb * 32);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        if (32 * kb <= 16 * m + 15) {
+        if ((m < NM / 2) == (kh == 0) && 32 * kb <= 16 * m + 15) {
           Frag<OpT> fa;
           load_frag_c(fa, as_ + (16 * m + r) * ALD + kb * 32);
           mma(acc[m], fa, fb);
         }
       }
     }
-    Tin* ob = os_[i & 1];
+    if (kh == 1) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+      for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ob[(16 * m + 4 * qd + e) * OLD + 16 * w + r] = from_f32<Tin>(acc[m][e]);
+        for (int e = 0; e < 4; ++e) red[(16 * m + 4 * qd + e) * RLD + c16] = acc[m][e];
+    }
+    __syncthreads();
+    if (kh == 0) {
+      Tin* ob = os_[i & 1];
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * m + 4 * qd + e;
+          ob[t * OLD + c16] = from_f32<Tin>(acc[m][e] + red[t * RLD + c16]);
+        }
+    }
 
-    // S <- diag(exp(gamma_i)) S + Kh_i^T V_i
+    // S <- diag(exp(gamma_i)) S + Kh_i^T V_i, this wave's dk half
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const f32x4 dec = *reinterpret_cast<const f32x4*>(egs + 16 * p + 4 * qd);
+      const f32x4 dec = *reinterpret_cast<const f32x4*>(egs + k0 + 16 * p + 4 * qd);
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[p][e] *= dec[e];
     }
 #pragma unroll
     for (int kb = 0; kb < C / 32; ++kb) {
       Frag<OpT> fb;
-      load_frag_c(fb, vs + (16 * w + r) * VLD + kb * 32);
+      load_frag_c(fb, vs + c16 * VLD + kb * 32);
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         Frag<OpT> fa;
-        load_frag_c(fa, ks + (16 * p + r) * KLD + kb * 32);
+        load_frag_c(fa, ks + (k0 + 16 * p + r) * KLD + kb * 32);
         mma(S[p], fa, fb);
       }
     }
@@ -202,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd_fused_staged(
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S_T[((long)bh * DK + 16 * p + 4 * qd + e) * dv + col] = S[p][e];
+      for (int e = 0; e < 4; ++e) S_T[((long)bh * DK + k0 + 16 * p + 4 * qd + e) * dv + col] = S[p][e];
   }
 }
 
@@ -323,7 +343,7 @@ template <typename Tin, typename OpT, int C, int DK>
 static hipError_t launch_fused_t2(const FusedArgs& a, hipStream_t s) {
   dim3 grid((a.dv / 64) * a.BH);
   if constexpr (C == 64 && sizeof(OpT) == 2) {
-    hipLaunchKernelGGL((k_fwd_fused_staged<Tin, OpT, C, DK>), grid, dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_fwd_fused_staged<Tin, OpT, C, DK>), grid, dim3(kFusedThreads), 0, s,
                        (const OpT*)a.Qh, (const OpT*)a.KhT, (const OpT*)a.A, a.eg,
                        (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N);
     return hipGetLastError();
