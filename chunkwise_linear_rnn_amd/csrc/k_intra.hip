@@ -21,6 +21,8 @@
 // g either comes from the gate-cumsum kernel (G_WS) or is computed here from log_alpha
 // by a segmented column scan.  Internally g is held multiplied by log2(e) so every decay
 // is one v_exp_f32; g2_out (nullable) receives it for the backward chunk kernel.
+#include <type_traits>
+
 #include "gla_common.cuh"
 #include "gla_internal.h"
 
@@ -43,6 +45,42 @@ __device__ __forceinline__ void pair_decode(int p, int& I, int& J) {
   J = p - ii * (ii - 1) / 2;
 }
 
+// A C x DB block of g (fp32) or log_alpha (SrcT) in registers as 16-byte units, written to
+// LDS as fp32 times log2 e.  Rows at and past `rows`: the last valid row repeated (clamp)
+// or zero.
+template <typename SrcT, int C, int DB>
+struct GBlock {
+  static constexpr int kPer = 16 / (int)sizeof(SrcT), kUnitsRow = DB / kPer;
+  static constexpr int kUnits = C * kUnitsRow, kPerThread = kUnits / kThreads;
+  static_assert(kUnits % kThreads == 0, "whole units per thread");
+  u32x4 u[kPerThread];
+  __device__ __forceinline__ void load(const SrcT* __restrict__ src, long ld, int rows, bool clamp) {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int idx = threadIdx.x + j * kThreads, rr = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
+      if (clamp) u[j] = *reinterpret_cast<const u32x4*>(src + (long)min(rr, rows - 1) * ld + c);
+      else u[j] = rr < rows ? *reinterpret_cast<const u32x4*>(src + (long)rr * ld + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(float* gs, int gld) const {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int idx = threadIdx.x + j * kThreads, rr = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
+      if constexpr (sizeof(SrcT) == 2) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, u[j]);
+        f32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { lo[e] = (float)b[e] * kLog2e; hi[e] = (float)b[4 + e] * kLog2e; }
+        *reinterpret_cast<f32x4*>(gs + rr * gld + c) = lo;
+        *reinterpret_cast<f32x4*>(gs + rr * gld + c + 4) = hi;
+      } else {
+        const f32x4 f = __builtin_bit_cast(f32x4, u[j]);
+        *reinterpret_cast<f32x4*>(gs + rr * gld + c) = f * kLog2e;
+      }
+    }
+  }
+};
+
 template <typename Tin, typename OpT, typename XT, int C, bool G_WS, bool WANT_A>
 __global__ __launch_bounds__(kThreads) void k_intra(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ la,
@@ -58,60 +96,63 @@ __global__ __launch_bounds__(kThreads) void k_intra(
   constexpr int GLD = DB + 4;
   constexpr int XLD = DB + 8;
 
-  __shared__ float gs[C * GLD];
+  __shared__ __attribute__((aligned(16))) float gs[C * GLD];
   __shared__ __attribute__((aligned(16))) Tin qs[C * XLD];
   __shared__ __attribute__((aligned(16))) Tin ks[C * XLD];
   __shared__ float segtot[4 * DB];
+  __shared__ float dacc[WANT_A ? NITEM : 1];
 
   const int i = blockIdx.x, bh = blockIdx.y;
   const int t0 = i * C, rows = min(C, T - t0);
   const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
   const long in_base = ((long)bh * T + t0) * dk;
 
+  // off-diagonal sub-blocks accumulate in registers, the diagonal items (each owned by
+  // one thread across the dk blocks) in LDS
   f32x4 accp[PPW > 0 ? PPW : 1];
-  float accd[IPT];
 #pragma unroll
   for (int p = 0; p < (PPW > 0 ? PPW : 1); ++p) accp[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < IPT; ++j) accd[j] = 0.f;
+  if constexpr (WANT_A)
+    for (int item = threadIdx.x; item < NITEM; item += kThreads) dacc[item] = 0.f;
+
+  // The next dk block's g (or log_alpha), q and k are loaded into registers while the
+  // current block computes.
+  using GSrc = typename std::conditional<G_WS, float, Tin>::type;
+  GBlock<GSrc, C, DB> pg;
+  RowTile<Tin, C, DB, XLD> tq, tk;
+  auto fetch = [&](int d0) {
+    // g from the gate kernel: rows past T continue the last valid row; log_alpha: zero
+    if constexpr (G_WS) pg.load(gws + in_base + d0, dk, rows, true);
+    else pg.load(la + in_base + d0, dk, rows, false);
+    tq.load(q + in_base + d0, dk, rows);
+    tk.load(k + in_base + d0, dk, rows);
+  };
+  fetch(0);
 
   for (int d0 = 0; d0 < dk; d0 += DB) {
-    // ---- g block (times log2 e); rows past T continue the last valid row -------------
-    if constexpr (G_WS) {
-      for (int idx = threadIdx.x; idx < C * (DB / 8); idx += kThreads) {
-        const int rr = idx / (DB / 8), c = (idx % (DB / 8)) * 8;
-        float x[8];
-        load8(x, gws + in_base + (long)min(rr, rows - 1) * dk + d0 + c);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gs[rr * GLD + c + e] = x[e] * kLog2e;
-      }
-    } else {
-      for (int idx = threadIdx.x; idx < C * (DB / 8); idx += kThreads) {
-        const int rr = idx / (DB / 8), c = (idx % (DB / 8)) * 8;
-        float x[8];
-        if (rr < rows) load8(x, la + in_base + (long)rr * dk + d0 + c); else zero8(x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gs[rr * GLD + c + e] = x[e] * kLog2e;
-      }
+    // ---- g block (times log2 e), q, k -------------------------------------------------
+    pg.store(gs, GLD);
+    tq.store(qs);
+    tk.store(ks);
+    if (d0 + DB < dk) fetch(d0 + DB);
+    if constexpr (!G_WS) {
+      // chunk-local cumsum down each column: four 16-row segments per column, each
+      // summed in registers, then offset by the totals of the segments above it
       __syncthreads();
-      {
-        constexpr int L = C / 4;
-        const int col = threadIdx.x % DB, seg = threadIdx.x / DB;
-        float run = 0.f;
-        for (int rr = seg * L; rr < seg * L + L; ++rr) {
-          run += gs[rr * GLD + col];
-          gs[rr * GLD + col] = run;
-        }
-        segtot[seg * DB + col] = run;
-        __syncthreads();
-        float off = 0.f;
-        for (int s2 = 0; s2 < seg; ++s2) off += segtot[s2 * DB + col];
-        if (seg > 0)
-          for (int rr = seg * L; rr < seg * L + L; ++rr) gs[rr * GLD + col] += off;
-      }
+      constexpr int L = C / 4;
+      const int col = threadIdx.x % DB, seg = threadIdx.x / DB;
+      float run[L];
+#pragma unroll
+      for (int rr = 0; rr < L; ++rr) run[rr] = gs[(seg * L + rr) * GLD + col];
+#pragma unroll
+      for (int rr = 1; rr < L; ++rr) run[rr] += run[rr - 1];
+      segtot[seg * DB + col] = run[L - 1];
+      __syncthreads();
+      float off = 0.f;
+      for (int s2 = 0; s2 < seg; ++s2) off += segtot[s2 * DB + col];
+#pragma unroll
+      for (int rr = 0; rr < L; ++rr) gs[(seg * L + rr) * GLD + col] = run[rr] + off;
     }
-    stage_rows<Tin, Tin, C, DB>(qs, XLD, q + in_base + d0, dk, rows);
-    stage_rows<Tin, Tin, C, DB>(ks, XLD, k + in_base + d0, dk, rows);
     __syncthreads();
     if (g2_out) {   // g * log2 e for the backward chunk kernel
       for (int idx = threadIdx.x; idx < C * (DB / 8); idx += kThreads) {
@@ -197,28 +238,30 @@ __global__ __launch_bounds__(kThreads) void k_intra(
         if (p < NPAIR) {
           int I, J;
           pair_decode(p, I, J);
-          const int rho = 16 * I, tq = 16 * I + r, sk = 16 * J + r;
-#pragma unroll
+          const int rho = 16 * I, tr = 16 * I + r, sk = 16 * J + r;
+#pragma unroll 1
           for (int kb = 0; kb < DB / 32; ++kb) {
             const int c0 = kb * 32 + 8 * qd;
             Frag<OpT> fa, fb;
+            float gr[8], gq[8], gk[8], xq[8], xk[8];
+            load8(gr, gs + rho * GLD + c0);
+            load8(gq, gs + tr * GLD + c0);
+            load8(gk, gs + sk * GLD + c0);
+            load8(xq, qs + tr * XLD + c0);
+            load8(xk, ks + sk * XLD + c0);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float gr = gs[rho * GLD + c0 + e];
-              fa.set(e, to_f32(qs[tq * XLD + c0 + e]) *
-                            __builtin_amdgcn_exp2f(gs[tq * GLD + c0 + e] - gr));
-              fb.set(e, to_f32(ks[sk * XLD + c0 + e]) *
-                            __builtin_amdgcn_exp2f(gr - gs[sk * GLD + c0 + e]));
+              fa.set(e, xq[e] * __builtin_amdgcn_exp2f(gq[e] - gr[e]));
+              fb.set(e, xk[e] * __builtin_amdgcn_exp2f(gr[e] - gk[e]));
             }
             mma(accp[pi], fa, fb);
           }
         }
       }
       // ---- diagonal sub-blocks: fp32, log-space ---------------------------------------
-#pragma unroll
-      for (int j = 0; j < IPT; ++j) {
-        const int item = threadIdx.x + kThreads * j;
-        if (item < NITEM) {
+#pragma unroll 1
+      for (int item = threadIdx.x; item < NITEM; item += kThreads) {
+        {
           const int quarter = item & 3, pr = item >> 2;
           const int I = pr / 136;
           int tt, ss;
@@ -227,16 +270,15 @@ __global__ __launch_bounds__(kThreads) void k_intra(
           float acc = 0.f;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            float xq[8], xk[8];
+            float xq[8], xk[8], gt[8], gsr[8];
             load8(xq, qs + t * XLD + cb + 8 * h);
             load8(xk, ks + s * XLD + cb + 8 * h);
+            load8(gt, gs + t * GLD + cb + 8 * h);
+            load8(gsr, gs + s * GLD + cb + 8 * h);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int c = cb + 8 * h + e;
-              acc += xq[e] * xk[e] * __builtin_amdgcn_exp2f(gs[t * GLD + c] - gs[s * GLD + c]);
-            }
+            for (int e = 0; e < 8; ++e) acc += xq[e] * xk[e] * __builtin_amdgcn_exp2f(gt[e] - gsr[e]);
           }
-          accd[j] += acc;
+          dacc[item] += acc;
         }
       }
     }
@@ -256,12 +298,13 @@ __global__ __launch_bounds__(kThreads) void k_intra(
           Ab[(16 * I + 4 * qd + e) * C + 16 * J + r] = from_f32<OpT>(accp[pi][e]);
       }
     }
+    // four column-quarter partials of each diagonal entry sit in adjacent lanes
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
-      float v = accd[j];
+      const int item = threadIdx.x + kThreads * j;
+      float v = item < NITEM ? dacc[item] : 0.f;
       v += __shfl_xor(v, 1);
       v += __shfl_xor(v, 2);
-      const int item = threadIdx.x + kThreads * j;
       if (item < NITEM && (item & 3) == 0) {
         const int pr = item >> 2, I = pr / 136;
         int tt, ss;
