@@ -214,7 +214,7 @@ def main():
     ap.add_argument("--workload", default="gla1p3b_t2k")
     ap.add_argument("--state-mode", default="recompute", choices=["recompute", "materialized"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024,
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens per (batch, head) in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration runs)")

@@ -60,8 +60,13 @@ def _counter_rows(path, counter):
 def counters(fetch_csv, write_csv, copy_bytes, stage, workload, command, root):
     f = _counter_rows(fetch_csv, "FETCH_SIZE")
     w = _counter_rows(write_csv, "WRITE_SIZE")
-    copy_f = [v for n, v in f if "copy" in n.lower() or "elementwise" in n.lower()]
-    copy_w = [v for n, v in w if "copy" in n.lower() or "elementwise" in n.lower()]
+    # the calibration copy (a device-to-device buffer copy); the fill that initializes its
+    # source writes but reads nothing, so it is not a calibration point
+    def is_copy(n):
+        n = n.lower()
+        return "copy" in n and "fill" not in n
+    copy_f = [v for n, v in f if is_copy(n)]
+    copy_w = [v for n, v in w if is_copy(n)]
     sel = STAGE_KERNEL[stage]
     kf = [v for n, v in f if sel in n]
     kw = [v for n, v in w if sel in n]
