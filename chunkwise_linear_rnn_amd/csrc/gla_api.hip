@@ -84,7 +84,7 @@ Plan plan_of(const gla_desc_t* d, int pass) {
     p.dst = take(stB);
     p.ST = take((size_t)x.BH * x.dk * x.dv * 4);
     p.cT = take((size_t)x.BH * x.dk * 4);
-    p.Dloc = take(gB);
+    if (!gla::bwd_split(x.dtype, (int)x.C)) p.Dloc = take(gB);   // the split path writes dla directly
     p.crossF = take(crossB);
     p.crossR = take(crossB);
     p.carry = take(egB);
@@ -129,8 +129,8 @@ struct Tracer {
 // Stage names of each pipeline, in launch order.
 const char* const kFwdMat[] = {"gate_cumsum", "intra", "state_scan", "output"};
 const char* const kFwdRec[] = {"intra", "fwd_fused"};
-const char* const kBwd[] = {"intra", "state_scans", "state_dot", "bwd_dqk", "bwd_dv",
-                            "gate_tot", "gate_grad"};
+const char* const kBwd[] = {"intra", "state_scans", "state_dot", "gate_tot", "bwd_dqk",
+                            "bwd_dv"};
 const char* const kBwdOne[] = {"intra", "state_scans", "state_dot", "bwd_chunk", "gate_tot",
                                "gate_grad"};
 
@@ -141,7 +141,7 @@ int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, in
     if (d->state_mode == GLA_STATES_MATERIALIZED) { src = kFwdMat; n = 4; }
     else { src = kFwdRec; n = 2; }
   } else if (gla::bwd_split(d->dtype, d->chunk)) {
-    src = kBwd; n = 7;
+    src = kBwd; n = 6;
   } else {
     src = kBwdOne; n = 6;
   }
@@ -372,20 +372,30 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   ba.dtype = x.dtype; ba.C = C; ba.BH = BH; ba.T = T; ba.dk = DK; ba.dv = DV; ba.N = N;
   ba.q = q; ba.k = k; ba.v = v; ba.dO = dO; ba.g = (const float*)(w + p.g); ba.gamma = nullptr;
   ba.A = w + p.A; ba.Kh = w + p.Kh; ba.S = w + p.st; ba.dS = w + p.dst;
-  ba.dq = dq; ba.dk_out = dk; ba.dv_out = dv; ba.Dloc = (float*)(w + p.Dloc);
-  if ((rs = tr.mark()) != GLA_OK) return rs;
-  rs = dev(gla::launch_bwd_chunk(ba, s));
-  if (rs != GLA_OK) return rs;
+  ba.dq = dq; ba.dk_out = dk; ba.dv_out = dv;
+  ba.Dloc = p.Dloc ? (float*)(w + p.Dloc) : nullptr;
+  ba.tot = (const float*)(w + p.carry); ba.cT = dS_T ? (const float*)(w + p.cT) : nullptr;
+  ba.dla = dlog_alpha;
+  // chunk totals of D from the scans' cross terms
+  auto totals = [&]() {
+    return dev(gla::launch_gate_tot((const float*)(w + p.crossF), (const float*)(w + p.crossR),
+                                    dS_T ? (const float*)(w + p.cT) : nullptr,
+                                    (float*)(w + p.carry), BH, T, DK, DV, C, s));
+  };
   if (gla::bwd_split(x.dtype, C)) {
+    // totals first: the dq / dk kernel finishes the gate gradient itself
     if ((rs = tr.mark()) != GLA_OK) return rs;
-    rs = dev(gla::launch_bwd_dv(ba, s));
-    if (rs != GLA_OK) return rs;
+    if ((rs = totals()) != GLA_OK) return rs;
+    if ((rs = tr.mark()) != GLA_OK) return rs;
+    if ((rs = dev(gla::launch_bwd_chunk(ba, s))) != GLA_OK) return rs;
+    if ((rs = tr.mark()) != GLA_OK) return rs;
+    if ((rs = dev(gla::launch_bwd_dv(ba, s))) != GLA_OK) return rs;
+    return tr.mark();
   }
   if ((rs = tr.mark()) != GLA_OK) return rs;
-  rs = dev(gla::launch_gate_carry((const float*)(w + p.crossF), (const float*)(w + p.crossR),
-                                  dS_T ? (const float*)(w + p.cT) : nullptr, (float*)(w + p.carry),
-                                  BH, T, DK, DV, C, s));
-  if (rs != GLA_OK) return rs;
+  if ((rs = dev(gla::launch_bwd_chunk(ba, s))) != GLA_OK) return rs;
+  if ((rs = tr.mark()) != GLA_OK) return rs;
+  if ((rs = totals()) != GLA_OK) return rs;
   if ((rs = tr.mark()) != GLA_OK) return rs;
   rs = dev(gla::launch_gate_grad(x.dtype, (const float*)(w + p.Dloc), (const float*)(w + p.carry),
                                  dS_T ? (const float*)(w + p.cT) : nullptr, dlog_alpha, BH, T, DK,

@@ -23,7 +23,7 @@ hipError_t launch_gate_cumsum(int dtype, const void* la, float* g, float* gamma,
 hipError_t launch_state_dot(const float* dST, const float* ST, float* cT, int BH, int dk, int dv,
                             hipStream_t s);
 // chunk totals of D from the scans' cross terms -> tot [BH][N][dk]
-hipError_t launch_gate_carry(const float* crossF, const float* crossR, const float* cT,
+hipError_t launch_gate_tot(const float* crossF, const float* crossR, const float* cT,
                              float* tot, int BH, int T, int dk, int dv, int C, hipStream_t s);
 hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* tot, const float* cT,
                             void* dla, int BH, int T, int dk, int C, hipStream_t s);
@@ -84,10 +84,13 @@ struct BwdArgs {
   const float *g, *gamma;   // g: g * log2(e) [BH][T][dk] (from the intra-chunk kernel)
   const void *A, *Kh, *S, *dS;
   void *dq, *dk_out, *dv_out;
-  float* Dloc;
+  float* Dloc;             // chunk-local suffix sums of D (single-kernel path)
+  const float *tot, *cT;   // chunk totals of D, rowsum(dS_T * S_T) or NULL (split path)
+  void* dla;               // dlog_alpha, written directly (split path)
 };
-// The backward chunk work: with bf16 operands and chunk 64 it is two kernels (dq/dk/D,
-// then dv: launch_bwd_chunk and launch_bwd_dv); otherwise one (launch_bwd_chunk).
+// The backward chunk work: with bf16 operands and chunk 64 it is two kernels (dq, dk and
+// dlog_alpha, after the chunk totals are formed; then dv: launch_bwd_chunk and
+// launch_bwd_dv); otherwise one (launch_bwd_chunk), followed by the gate-gradient kernel.
 bool bwd_split(int dtype, int C);
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dv(const BwdArgs& a, hipStream_t s);

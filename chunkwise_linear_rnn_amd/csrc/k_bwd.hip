@@ -22,7 +22,9 @@
 // chunk totals that the two state scans form from their fp32 states.
 //
 // Kernels
-//   k_bwd_dqk  (chunk 64) dq, dk and D per (chunk, 64-wide dk block).  One pass over
+//   k_bwd_dqk  (chunk 64) dq, dk and dlog_alpha per (chunk, 64-wide dk block): D as
+//              chunk-local suffix sums plus the carry from the later chunks' totals
+//              (formed by the gate-total kernel from the scans).  One pass over
 //              64-wide dv blocks accumulates dA, dO S^T and V dS^T together: dO and V
 //              tiles go through LDS (shared by the 4 waves), each wave's S / dS fragments
 //              are prefetched straight into registers (double-buffered); then the
@@ -225,7 +227,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dqk(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dO, const float* __restrict__ g, const OpT* __restrict__ S,
     const OpT* __restrict__ dS, Tin* __restrict__ dq, Tin* __restrict__ dk_out,
-    float* __restrict__ Dloc, int T, int dk, int dv, int N) {
+    const float* __restrict__ tot, const float* __restrict__ cT, Tin* __restrict__ dla, int T,
+    int dk, int dv, int N) {
   static_assert(sizeof(Tin) == sizeof(OpT), "input and operand types match");
   constexpr int C = 64, NM = 4, NS = C / 16, YLD = 64 + 8;
   constexpr int FLD = C + 4, GLD = 64 + 4, XLD = 64 + 8;
@@ -253,6 +256,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dqk(
   const OpT* Si = S + ((long)bh * N + i) * dk * dv;
   const OpT* dSi = dS + ((long)bh * N + i) * dk * dv;
   const int NV = dv / 64;
+
+  // gate gradient carried into this chunk for column c: the chunk totals of D over the
+  // later chunks (lane group qd takes every fourth chunk), plus c_T
+  float carry = 0.f;
+  for (int j = i + 1 + qd; j < N; j += 4) carry += tot[((long)bh * N + j) * dk + d0 + c];
 
   f32x4 adq[NM], adk[NM], adA[NM];   // adA[n] = dA tile (w, n), n <= w
 #pragma unroll
@@ -440,29 +448,33 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dqk(
       Dv[m][e] = to_f32(qs[t * XLD + c]) * vq - to_f32(ks[t * XLD + c]) * vk;
     }
   // rows of this lane: 16 m + 4 qd + e.  Suffix sums within the lane, then across the
-  // four lane groups of the column (lanes r + 16 q') and the later sub-chunks.
-  float tot[NM];
+  // four lane groups of the column (lanes r + 16 q') and the later sub-chunks, on top of
+  // the carry from the later chunks: the closed-form gate gradient.
+  carry += __shfl_xor(carry, 16);
+  carry += __shfl_xor(carry, 32);
+  if (cT) carry += cT[(long)bh * dk + d0 + c];
+  float ptot[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     Dv[m][2] += Dv[m][3];
     Dv[m][1] += Dv[m][2];
     Dv[m][0] += Dv[m][1];
-    tot[m] = Dv[m][0];
+    ptot[m] = Dv[m][0];
   }
-  float later = 0.f;   // sum over sub-chunks after m, all lane groups
+  float later = carry;   // carry plus the sum over sub-chunks after m, all lane groups
 #pragma unroll
   for (int m = NM - 1; m >= 0; --m) {
     float after = later, all = 0.f;
 #pragma unroll
     for (int g2 = 0; g2 < 4; ++g2) {
-      const float x = __shfl(tot[m], r + 16 * g2);
+      const float x = __shfl(ptot[m], r + 16 * g2);
       all += x;
       if (g2 > qd) after += x;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 16 * m + 4 * qd + e;
-      if (t < rows) Dloc[(tok0 + t) * dk + d0 + c] = Dv[m][e] + after;
+      if (t < rows) dla[(tok0 + t) * dk + d0 + c] = from_f32<Tin>(Dv[m][e] + after);
     }
     later += all;
   }
@@ -724,8 +736,8 @@ static hipError_t launch_bwd_t2(const BwdArgs& a, hipStream_t s) {
   if constexpr (C == 64 && sizeof(OpT) == 2) {
     hipLaunchKernelGGL((k_bwd_dqk<Tin, OpT>), dim3((a.dk / 64) * a.N * a.BH), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,
-                       (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq, (Tin*)a.dk_out, a.Dloc, a.T,
-                       a.dk, a.dv, a.N);
+                       (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq, (Tin*)a.dk_out, a.tot, a.cT,
+                       (Tin*)a.dla, a.T, a.dk, a.dv, a.N);
   } else {
     hipLaunchKernelGGL((k_bwd_chunk<Tin, OpT, C, DK>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,

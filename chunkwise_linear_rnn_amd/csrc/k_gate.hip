@@ -120,7 +120,7 @@ hipError_t launch_state_dot(const float* dST, const float* ST, float* cT, int BH
   return hipGetLastError();
 }
 
-hipError_t launch_gate_carry(const float* crossF, const float* crossR, const float* cT,
+hipError_t launch_gate_tot(const float* crossF, const float* crossR, const float* cT,
                              float* tot, int BH, int T, int dk, int dv, int C, hipStream_t s) {
   (void)cT;
   const int N = (T + C - 1) / C;

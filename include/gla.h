@@ -142,9 +142,9 @@ gla_status_t gla_chunk_bwd(const gla_desc_t* desc, const void* q, const void* k,
  *   forward, materialized: gate_cumsum, intra, state_scan, output
  *   forward, recompute:    intra, fwd_fused
  *   backward:              intra, state_scans (the forward and the reverse scan, one
- *                          launch), [state_dot when dS_T is given], then bwd_dqk, bwd_dv
- *                          (bf16, chunk 64) or bwd_chunk (otherwise), then gate_tot,
- *                          gate_grad */
+ *                          launch), [state_dot when dS_T is given], then gate_tot, bwd_dqk,
+ *                          bwd_dv (bf16, chunk 64) or bwd_chunk, gate_tot, gate_grad
+ *                          (otherwise) */
 int32_t gla_trace_stages(const gla_desc_t* desc, int32_t pass, int32_t with_dS_T,
                          const char** names, int32_t max_names);
 
