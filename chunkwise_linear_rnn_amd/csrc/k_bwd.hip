@@ -223,7 +223,7 @@ __device__ __forceinline__ void bwd_finish_block(const IntraLds<C, DB, Tin>& L,
 // the chunk (it is cheap next to the dO S^T and V dS^T products, and keeps the blocks
 // independent).  Three workgroups fit on a CU, so one's loads overlap another's math.
 template <typename Tin, typename OpT>
-__global__ __launch_bounds__(kThreads) void k_bwd_dqk(
+__global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dO, const float* __restrict__ g, const OpT* __restrict__ S,
     const OpT* __restrict__ dS, Tin* __restrict__ dq, Tin* __restrict__ dk_out,
@@ -439,13 +439,22 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dqk(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 16 * m + 4 * qd + e;
-      const float vq = adq[m][e] + dqd[t * FLD + c];
-      const float vk = adk[m][e] + dkd[t * GLD + c];
-      if (t < rows) {
-        dq[(tok0 + t) * dk + d0 + c] = from_f32<Tin>(vq);
-        dk_out[(tok0 + t) * dk + d0 + c] = from_f32<Tin>(vk);
-      }
-      Dv[m][e] = to_f32(qs[t * XLD + c]) * vq - to_f32(ks[t * XLD + c]) * vk;
+      adq[m][e] += dqd[t * FLD + c];
+      adk[m][e] += dkd[t * GLD + c];
+      Dv[m][e] = to_f32(qs[t * XLD + c]) * adq[m][e] - to_f32(ks[t * XLD + c]) * adk[m][e];
+    }
+  // dq, dk, dlog_alpha of the block leave as 16-byte rows through LDS (the dA and g
+  // regions are dead once every wave has read the diagonal terms)
+  constexpr int SLD = 64 + 8;
+  Tin* st = (Tin*)arena;   // three [C][SLD] tiles: dq, dk, dlog_alpha
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * m + 4 * qd + e;
+      st[t * SLD + c] = from_f32<Tin>(adq[m][e]);
+      st[C * SLD + t * SLD + c] = from_f32<Tin>(adk[m][e]);
     }
   // rows of this lane: 16 m + 4 qd + e.  Suffix sums within the lane, then across the
   // four lane groups of the column (lanes r + 16 q') and the later sub-chunks, on top of
@@ -472,11 +481,20 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dqk(
       if (g2 > qd) after += x;
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 16 * m + 4 * qd + e;
-      if (t < rows) dla[(tok0 + t) * dk + d0 + c] = from_f32<Tin>(Dv[m][e] + after);
-    }
+    for (int e = 0; e < 4; ++e)
+      st[2 * C * SLD + (16 * m + 4 * qd + e) * SLD + c] = from_f32<Tin>(Dv[m][e] + after);
     later += all;
+  }
+  __syncthreads();
+  constexpr int kPer = 16 / (int)sizeof(Tin), kRowUnits = 64 / kPer, kUnits = 3 * C * kRowUnits;
+  static_assert(3 * C * SLD * (int)sizeof(Tin) <= o_q, "staging stays clear of q / k");
+  for (int idx = threadIdx.x; idx < kUnits; idx += kThreads) {
+    const int tile = idx / (C * kRowUnits), u = idx % (C * kRowUnits);
+    const int rr = u / kRowUnits, cc = (u % kRowUnits) * kPer;
+    Tin* dst = tile == 0 ? dq : (tile == 1 ? dk_out : dla);
+    if (rr < rows)
+      *reinterpret_cast<u32x4*>(dst + (tok0 + rr) * dk + d0 + cc) =
+          *reinterpret_cast<const u32x4*>(st + (tile * C + rr) * SLD + cc);
   }
 }
 
