@@ -12,12 +12,16 @@ goes to stdout; a per-stage table goes to stderr.
 
 The roofline object describes the stage with the largest time per step, against the
 MI355X peak for its bound (HBM 8 TB/s, or dense bf16 MFMA 2.5 PFLOP/s); its `achieved`
-uses the algorithmic bytes or flops per launch listed in STAGE_WORK below.  `traffic`
+uses the algorithmic bytes or flops per launch from stage_work() below.  `traffic`
 is the measured HBM bytes per launch of that stage from the committed rocprofv3 counter
 summary, or null when no summary matches the current kernel source.
 
-The CPU baseline times the fp64 oracle (step recurrence + direct backward) on a bounded
-sample of the same workload with a process pool on the host cores.
+`cache_flushed` repeats the step after a 512 MiB write that evicts the 256 MiB Infinity
+Cache, with HIP events around the step only (the headline `value` is the warm rate).
+
+The CPU baseline times the fp64 oracle (step recurrence, then direct backward, each
+timed separately) on a bounded sample of the same workload with a process pool on the
+host cores.
 """
 from __future__ import annotations
 
@@ -118,6 +122,11 @@ class HipEvents:
         self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                ctypes.c_void_p]
         self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, ev, stream):
+        if self.h.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def create(self, n):
         arr = (ctypes.c_void_p * n)()
@@ -149,14 +158,27 @@ def _oracle_warm(_):
     return 0
 
 
-def _oracle_head(args):
-    os.environ.setdefault("OMP_NUM_THREADS", "1")
+def _oracle_fwd(args):
     q, k, v, la, dO = args
-    from oracle import recurrence_fwd, recurrence_bwd
-    t0 = time.perf_counter()
+    from oracle import recurrence_fwd
     recurrence_fwd(q, k, v, la)
+
+
+def _oracle_bwd(args):
+    q, k, v, la, dO = args
+    from oracle import recurrence_bwd
     recurrence_bwd(q, k, v, la, dO)
-    return time.perf_counter() - t0
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(d, cfg, T_sample):
@@ -177,8 +199,12 @@ def cpu_baseline(d, cfg, T_sample):
     with ctx.Pool(workers) as pool:
         pool.map(_oracle_warm, range(workers))      # process start-up is not timed
         t0 = time.perf_counter()
-        pool.map(_oracle_head, jobs, chunksize=1)
-        wall = time.perf_counter() - t0
+        pool.map(_oracle_fwd, jobs, chunksize=1)
+        t1 = time.perf_counter()
+        pool.map(_oracle_bwd, jobs, chunksize=1)
+        t2 = time.perf_counter()
+    wall_f, wall_b = t1 - t0, t2 - t1
+    wall = wall_f + wall_b
     for k, val in env_before.items():
         if val is None:
             os.environ.pop(k, None)
@@ -188,7 +214,8 @@ def cpu_baseline(d, cfg, T_sample):
     return {"value": tokens / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
             "sample": (f"fp64 step recurrence + direct backward, {workers} (batch, head) pairs x "
                        f"first {T_sample} tokens of {cfg.name}, one process per head, "
-                       f"{wall:.2f} s wall")}
+                       f"{wall:.2f} s wall (fwd {wall_f:.2f} s, bwd {wall_b:.2f} s)"),
+            "fwd_s": wall_f, "bwd_s": wall_b, "cpu_model": _cpu_model()}
 
 
 def counter_traffic(stage, workload):
@@ -216,6 +243,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens per (batch, head) in the oracle sample")
+    ap.add_argument("--flush-steps", type=int, default=10,
+                    help="extra steps timed after a 512 MiB write that evicts the Infinity Cache")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
     args = ap.parse_args()
@@ -307,6 +336,26 @@ def main():
         stages[key] /= args.steps
     gpu_ms_from_events = sum(stages.values())
 
+    # Cache-cold steps: a 512 MiB write before each step evicts the 256 MiB Infinity Cache,
+    # and HIP events bracket only the step itself.
+    flushed = None
+    if args.flush_steps > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        evs = hip.create(2)
+        total = 0.0
+        for j in range(args.flush_steps):
+            scratch.fill_(j & 0xFF)
+            hip.record(evs[0], sp)
+            step(args.warmup)
+            hip.record(evs[1], sp)
+            torch.cuda.synchronize()
+            total += hip.elapsed_ms(evs[0], evs[1])
+        hip.destroy(evs)
+        del scratch
+        fms = total / args.flush_steps
+        flushed = {"ms_per_step": fms, "value": B * T / (fms * 1e-3), "steps": args.flush_steps,
+                   "flush_bytes": 512 << 20}
+
     if args.copy_calibration:
         nbytes = 1 << 30
         a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1)
@@ -343,6 +392,7 @@ def main():
     roof["avg_launch_us"] = dom_ms * 1e3
     roof["algorithmic_bytes_per_launch"] = byt
     roof["algorithmic_flops_per_launch"] = fl
+    roof["ai_flop_per_byte"] = ai
 
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)
@@ -357,6 +407,7 @@ def main():
                    "seq_len": T, "parallelism": "none (1 GPU)"},
         "tflops": tflops, "mfma_peak_frac": flops / (ms_per_step * 1e-3) / PEAK_BF16,
         "roofline": roof,
+        "cache_flushed": flushed,
     }
     for arr in evf + evb:
         hip.destroy(arr)
