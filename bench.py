@@ -16,6 +16,10 @@ uses the algorithmic bytes or flops per launch from stage_work() below.  `traffi
 is the measured HBM bytes per launch of that stage from the committed rocprofv3 counter
 summary, or null when no summary matches the current kernel source.
 
+`decode_step` times the recurrent entry point (one token per sequence, float32 state
+read and written in place) at the workload's head shape for a small and a serving-size
+batch, against the HBM roofline.
+
 `cache_flushed` repeats the step after a 512 MiB write that evicts the 256 MiB Infinity
 Cache, with HIP events around the step only (the headline `value` is the warm rate).
 
@@ -233,6 +237,42 @@ def counter_traffic(stage, workload):
     return rec.get("traffic_bytes_per_launch")
 
 
+def decode_measure(L, nat, hip, dev, sp, H, dk, dv, batches=(4, 64), calls=200):
+    """One-token recurrent steps (gla_decode, T = 1, bf16, float32 state in place) at a few
+    batch sizes: microseconds per step from HIP events around `calls` back-to-back steps;
+    the algorithmic bytes are the state read and written plus the token's q, k, v,
+    log_alpha and o."""
+    import torch
+    out = []
+    for B in batches:
+        g = torch.Generator(device="cpu").manual_seed(B)
+        mk = lambda *s: (torch.randn(*s, generator=g) * 0.1).to(torch.bfloat16).to(dev)  # noqa: E731
+        q, k, la = mk(B, H, 1, dk), mk(B, H, 1, dk), -mk(B, H, 1, dk).abs()
+        v = mk(B, H, 1, dv)
+        S = torch.zeros((B, H, dk, dv), dtype=torch.float32, device=dev)
+        o = torch.empty((B, H, 1, dv), dtype=torch.bfloat16, device=dev)
+        desc = nat.make_desc(B, H, 1, dk, dv, 64, 16, nat.BF16, nat.RECOMPUTE)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        args = (ctypes.byref(desc), P(q), P(k), P(v), P(la), P(S), P(o), sp)
+        for _ in range(20):
+            if L.gla_decode(*args):
+                raise nat.GlaError(L.gla_decode(*args), "gla_decode")
+        evs = hip.create(2)
+        hip.record(evs[0], sp)
+        for _ in range(calls):
+            L.gla_decode(*args)
+        hip.record(evs[1], sp)
+        torch.cuda.synchronize()
+        us = hip.elapsed_ms(evs[0], evs[1]) * 1e3 / calls
+        hip.destroy(evs)
+        byt = 2 * B * H * dk * dv * 4 + B * H * (3 * dk + 2 * dv) * 2
+        out.append({"B": B, "H": H, "dk": dk, "dv": dv, "us_per_step": us,
+                    "tokens_per_s": B / (us * 1e-6), "algorithmic_bytes": byt,
+                    "achieved_GBps": byt / (us * 1e-6) / 1e9,
+                    "hbm_frac": byt / (us * 1e-6) / PEAK_HBM})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +281,8 @@ def main():
     ap.add_argument("--workload", default="gla1p3b_t2k")
     ap.add_argument("--state-mode", default="recompute", choices=["recompute", "materialized"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the one-token recurrent step measurement")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens per (batch, head) in the oracle sample")
     ap.add_argument("--flush-steps", type=int, default=10,
@@ -411,6 +453,8 @@ def main():
     }
     for arr in evf + evb:
         hip.destroy(arr)
+    if not args.no_decode:
+        out["decode_step"] = decode_measure(L, nat, hip, dev, sp, H, dk, dv)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(d, cfg, min(args.cpu_tokens, T))

@@ -19,8 +19,8 @@ from __future__ import annotations
 from ._native import (GlaDesc, GlaError, F32, BF16, MATERIALIZED, RECOMPUTE, PASS_FWD,  # noqa: F401
                       PASS_BWD, PASS_STATES, lib, lib_path, make_desc, status_string, trace_stages,
                       validate, version, workspace_bytes)
-from .ops import fwd, bwd, gate_cumsum, chunk_states, GLAFunction, gla  # noqa: F401
+from .ops import fwd, bwd, gate_cumsum, chunk_states, decode, GLAFunction, gla  # noqa: F401
 
-__all__ = ["fwd", "bwd", "gate_cumsum", "chunk_states", "GLAFunction", "gla", "GlaDesc",
+__all__ = ["fwd", "bwd", "gate_cumsum", "chunk_states", "decode", "GLAFunction", "gla", "GlaDesc",
            "GlaError", "make_desc", "workspace_bytes", "validate", "status_string", "version",
            "lib", "lib_path"]

@@ -39,6 +39,7 @@ SIGNATURES = {
     "gla_chunk_fwd": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "gla_chunk_bwd": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp, _sz, _vp]),
+    "gla_decode": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "gla_trace_stages": (_i32, [_PDESC, _i32, _i32, ctypes.POINTER(ctypes.c_char_p), _i32]),
     "gla_chunk_fwd_traced": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
                                     ctypes.POINTER(_vp), _i32]),

@@ -412,4 +412,24 @@ gla_status_t gla_chunk_bwd(const gla_desc_t* d, const void* q, const void* k, co
                               ws_bytes, stream, nullptr, 0);
 }
 
+gla_status_t gla_decode(const gla_desc_t* d, const void* q, const void* k, const void* v,
+                        const void* log_alpha, float* S, void* o, void* stream) {
+  if (!d) return GLA_ERR_INVALID_ARG;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->dk < 0 || d->dv < 0) return GLA_ERR_INVALID_ARG;
+  if (d->dtype != GLA_F32 && d->dtype != GLA_BF16) return GLA_ERR_INVALID_ARG;
+  if (d->dk < 32 || d->dk > 256 || d->dk % 32 != 0) return GLA_ERR_UNSUPPORTED;
+  if (d->dv < 32 || d->dv > 1024 || d->dv % 32 != 0) return GLA_ERR_UNSUPPORTED;
+  const long long bh = (long long)d->B * d->H;
+  if (bh * (d->dv / 32) > (1LL << 31) - 1) return GLA_ERR_UNSUPPORTED;
+  if (bh * (long long)d->T > (1LL << 31) - 1) return GLA_ERR_UNSUPPORTED;
+  if (bh == 0 || d->T == 0) return GLA_OK;   // nothing to do; S is left as it is
+  if (!q || !k || !v || !log_alpha || !S || !o) return GLA_ERR_INVALID_ARG;
+  for (const void* p : std::initializer_list<const void*>{q, k, v, log_alpha, S, o})
+    if (!aligned16(p)) return GLA_ERR_INVALID_ARG;
+  gla::DecodeArgs a{};
+  a.dtype = d->dtype; a.BH = (int)bh; a.T = d->T; a.dk = d->dk; a.dv = d->dv;
+  a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.S = S; a.o = o;
+  return dev(gla::launch_decode(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -95,4 +95,13 @@ bool bwd_split(int dtype, int C);
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dv(const BwdArgs& a, hipStream_t s);
 
+// Recurrent evaluation (decoding): T tokens in order, state updated in place.
+struct DecodeArgs {
+  int dtype, BH, T, dk, dv;
+  const void *q, *k, *v, *la;
+  float* S;   // [BH][dk][dv]
+  void* o;    // [BH][T][dv]
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
 }  // namespace gla

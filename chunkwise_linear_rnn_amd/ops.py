@@ -165,6 +165,28 @@ class GLAFunction(torch.autograd.Function):
         return dq, dk, dv, dla, dS0, None, None, None
 
 
+def decode(q, k, v, log_alpha, S):
+    """o = the recurrent evaluation of T tokens (T typically 1), S (float32
+    [B, H, dk, dv]) updated in place: S <- diag(exp(log_alpha_t)) S + k_t^T v_t,
+    o_t = q_t S, for t in order."""
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be [B, H, T, d]")
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)),
+                      (v, "v", (B, H, T, dv)), (log_alpha, "log_alpha", (B, H, T, dk))):
+        _check(t, n, shp, dt, dev)
+    _check(S, "S", (B, H, dk, dv), torch.float32, dev)
+    desc = make_desc(B, H, T, dk, dv, 64, 16, _DT[dt], RECOMPUTE)
+    o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    _call("gla_decode", lib().gla_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(log_alpha), _ptr(S), _ptr(o), _stream(dev)))
+    return o
+
+
 def gla(q, k, v, log_alpha, S0=None, chunk=64, subchunk=16, state_mode="recompute"):
     """Differentiable GLA layer: returns (o, S_T)."""
     return GLAFunction.apply(q, k, v, log_alpha, S0, chunk, subchunk, state_mode)

@@ -129,6 +129,23 @@ gla_status_t gla_chunk_bwd(const gla_desc_t* desc, const void* q, const void* k,
                            void* dv, void* dlog_alpha, float* dS0, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* Recurrent evaluation, for decoding (Approach section: the same state in its
+ * recurrent form, the layer's inference side).  For every (b, h) and t = 0 .. T-1 in
+ * order:
+ *     S <- diag(exp(log_alpha[b,h,t,:])) S + k[b,h,t,:]^T v[b,h,t,:],
+ *     o[b,h,t,:] = q[b,h,t,:] S,
+ * with S float32 [B,H,dk,dv], read and updated in place (required; it is both input and
+ * output, the one exception to the no-alias rule).  q, k, log_alpha [B,H,T,dk] and v
+ * [B,H,T,dv] are inputs, o [B,H,T,dv] the output (all desc->dtype).  T is typically 1:
+ * one new token per sequence; the state is read and written once per call whatever T
+ * is, every step in fp32.  desc->chunk, subchunk and state_mode are not used, and no
+ * workspace is needed.  B*H == 0 or T == 0 is a no-op.
+ * Supported: dk a multiple of 32 in [32, 256]; dv a multiple of 32 in [32, 1024];
+ * B*H*(dv/32) and B*H*T below 2^31 (else GLA_ERR_UNSUPPORTED).  A NULL or misaligned
+ * pointer is GLA_ERR_INVALID_ARG. */
+gla_status_t gla_decode(const gla_desc_t* desc, const void* q, const void* k, const void* v,
+                        const void* log_alpha, float* S, void* o, void* stream);
+
 /* Stage tracing, for profiling.  The *_traced variants behave exactly like
  * gla_chunk_fwd / gla_chunk_bwd and additionally record caller-created hipEvent_t
  * handles on `stream`: events[j] right before the j-th kernel launch and events[n] after

@@ -102,3 +102,28 @@ def test_errors_before_any_launch(native):
     assert L.gla_chunk_bwd(ctypes.byref(good), p, p, p, p, None, None, None, p, p, p, p, None,
                            p, 1 << 30, None) == 1
     assert L.gla_gate_cumsum(ctypes.byref(good), None, p, p, None) == 1
+
+
+def test_decode_validation_before_any_launch(native):
+    """gla_decode checks its own shape rules on the host (chunk fields are not used)."""
+    L = native.lib()
+    D = native.make_desc
+    p = ctypes.c_void_p(16)
+    # supported: dk, dv multiples of 32
+    for dk, dv, code in ((48, 64, 2), (64, 48, 2), (288, 64, 2), (64, 1056, 2), (0, 64, 2)):
+        d = D(1, 1, 1, dk, dv)
+        assert L.gla_decode(ctypes.byref(d), p, p, p, p, p, p, None) == code, (dk, dv)
+    d = D(1, 1, 1, 96, 96)
+    assert L.gla_decode(None, p, p, p, p, p, p, None) == 1
+    assert L.gla_decode(ctypes.byref(d), p, p, p, p, None, p, None) == 1     # S required
+    assert L.gla_decode(ctypes.byref(d), p, p, p, p, p, None, None) == 1     # o required
+    assert L.gla_decode(ctypes.byref(d), ctypes.c_void_p(20), p, p, p, p, p, None) == 1
+    bad_dtype = D(1, 1, 1, 96, 96, 64, 16, 7)
+    assert L.gla_decode(ctypes.byref(bad_dtype), p, p, p, p, p, p, None) == 1
+    neg = D(1, -1, 1, 96, 96)
+    assert L.gla_decode(ctypes.byref(neg), p, p, p, p, p, p, None) == 1
+    # nothing to do: no pointer is looked at
+    assert L.gla_decode(ctypes.byref(D(1, 1, 0, 96, 96)), None, None, None, None, None, None,
+                        None) == 0
+    assert L.gla_decode(ctypes.byref(D(0, 3, 5, 96, 96)), None, None, None, None, None, None,
+                        None) == 0
