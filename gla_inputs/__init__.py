@@ -110,7 +110,8 @@ def generate(cfg: GlaConfig, *, with_dO: bool = True, T: int | None = None):
     q = rng.standard_normal((B, H, T, dk)) * inv
     k = rng.standard_normal((B, H, T, dk)) * inv
     v = rng.standard_normal((B, H, T, dv)) * inv
-    items = [("log_alpha", la), ("q", q), ("k", k), ("v", v)]
+    # the raw gate logits too, for the gate front-end (log_alpha formed from them)
+    items = [("log_alpha", la), ("gate_logits", g), ("q", q), ("k", k), ("v", v)]
     if with_dO:
         items.append(("dO", rng.standard_normal((B, H, T, dv))))
     for name, arr in items:
