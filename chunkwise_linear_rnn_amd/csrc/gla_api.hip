@@ -100,6 +100,17 @@ bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0
 
 gla_status_t dev(hipError_t e) { return e == hipSuccess ? GLA_OK : GLA_ERR_DEVICE; }
 
+bool gate_ok(const gla_desc_t* d) {
+  if (d->gate == GLA_GATE_LOG_ALPHA) return true;
+  return d->gate == GLA_GATE_LOGITS && d->gate_tau > 0.f && d->gate_tau <= 3.0e38f;
+}
+gla::GateFn gate_of(const gla_desc_t* d) {
+  gla::GateFn g;
+  g.on = d->gate == GLA_GATE_LOGITS ? 1 : 0;
+  g.inv_tau = g.on ? 1.f / d->gate_tau : 1.f;
+  return g;
+}
+
 // Zero or copy a [BH,dk,dv] fp32 state with a kernel (safe under stream capture).
 __global__ void k_state_copy(const float* __restrict__ src, float* __restrict__ dst, long n) {
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
@@ -185,6 +196,7 @@ gla_status_t gla_validate(const gla_desc_t* d, int32_t pass) {
   if (d->dtype != GLA_F32 && d->dtype != GLA_BF16) return GLA_ERR_INVALID_ARG;
   if (d->state_mode != GLA_STATES_MATERIALIZED && d->state_mode != GLA_STATES_RECOMPUTE)
     return GLA_ERR_INVALID_ARG;
+  if (!gate_ok(d)) return GLA_ERR_INVALID_ARG;
   if (d->chunk != 64 && d->chunk != 128) return GLA_ERR_UNSUPPORTED;
   if (d->subchunk != 16) return GLA_ERR_UNSUPPORTED;
   if (d->dtype == GLA_F32 && d->chunk != 64) return GLA_ERR_UNSUPPORTED;
@@ -213,7 +225,7 @@ gla_status_t gla_gate_cumsum(const gla_desc_t* d, const void* log_alpha, float* 
   if (x.BH * x.T == 0) return GLA_OK;
   if (!log_alpha || (!g && !gamma)) return GLA_ERR_INVALID_ARG;
   if (!aligned16(log_alpha) || !aligned16(g) || !aligned16(gamma)) return GLA_ERR_INVALID_ARG;
-  return dev(gla::launch_gate_cumsum(x.dtype, log_alpha, g, gamma, (int)x.BH, (int)x.T,
+  return dev(gla::launch_gate_cumsum(x.dtype, log_alpha, gate_of(d), g, gamma, (int)x.BH, (int)x.T,
                                      (int)x.dk, (int)x.C, (hipStream_t)stream));
 }
 
@@ -234,7 +246,7 @@ gla_status_t gla_chunk_states(const gla_desc_t* d, const void* k, const void* v,
   char* w = (char*)ws;
   gla::IntraArgs ia{};
   ia.dtype = x.dtype; ia.C = (int)x.C; ia.BH = (int)x.BH; ia.T = (int)x.T; ia.dk = (int)x.dk;
-  ia.N = (int)x.N; ia.want_A = false; ia.q = k; ia.k = k; ia.la = log_alpha; ia.g = nullptr;
+  ia.N = (int)x.N; ia.want_A = false; ia.q = k; ia.k = k; ia.la = log_alpha; ia.g = nullptr; ia.gate = gate_of(d);
   ia.KhT = w + p.KhT; ia.eg = (float*)(w + p.eg);
   gla_status_t rs = dev(gla::launch_intra(ia, s));
   if (rs != GLA_OK) return rs;
@@ -269,13 +281,13 @@ gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void
   gla_status_t rs = GLA_OK;
   if (mat) {
     if ((rs = tr.mark()) != GLA_OK) return rs;
-    rs = dev(gla::launch_gate_cumsum(x.dtype, log_alpha, (float*)(w + p.g), nullptr, (int)x.BH,
+    rs = dev(gla::launch_gate_cumsum(x.dtype, log_alpha, gate_of(d), (float*)(w + p.g), nullptr, (int)x.BH,
                                      (int)x.T, (int)x.dk, (int)x.C, s));
     if (rs != GLA_OK) return rs;
   }
   gla::IntraArgs ia{};
   ia.dtype = x.dtype; ia.C = (int)x.C; ia.BH = (int)x.BH; ia.T = (int)x.T; ia.dk = (int)x.dk;
-  ia.N = (int)x.N; ia.want_A = true; ia.q = q; ia.k = k; ia.la = log_alpha;
+  ia.N = (int)x.N; ia.want_A = true; ia.q = q; ia.k = k; ia.la = log_alpha; ia.gate = gate_of(d);
   ia.g = mat ? (const float*)(w + p.g) : nullptr;
   ia.A = w + p.A; ia.Qh = w + p.Qh; ia.KhT = w + p.KhT; ia.eg = (float*)(w + p.eg);
   if ((rs = tr.mark()) != GLA_OK) return rs;
@@ -342,6 +354,7 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   ia.dtype = x.dtype; ia.C = C; ia.BH = BH; ia.T = T; ia.dk = DK; ia.N = N; ia.want_A = true;
   ia.xt_f32 = x.dtype == GLA_BF16;
   ia.q = q; ia.k = k; ia.la = log_alpha; ia.g = nullptr; ia.g2_out = (float*)(w + p.g);
+  ia.gate = gate_of(d);
   ia.A = w + p.A; ia.QhT = w + p.QhT; ia.Kh = w + p.Kh; ia.KhT = w + p.KhT;
   ia.eg = (float*)(w + p.eg);
   if ((rs = tr.mark()) != GLA_OK) return rs;
@@ -375,7 +388,7 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   ba.dq = dq; ba.dk_out = dk; ba.dv_out = dv;
   ba.Dloc = p.Dloc ? (float*)(w + p.Dloc) : nullptr;
   ba.tot = (const float*)(w + p.carry); ba.cT = dS_T ? (const float*)(w + p.cT) : nullptr;
-  ba.dla = dlog_alpha;
+  ba.dla = dlog_alpha; ba.la = log_alpha; ba.gate = gate_of(d);
   // chunk totals of D from the scans' cross terms
   auto totals = [&]() {
     return dev(gla::launch_gate_tot((const float*)(w + p.crossF), (const float*)(w + p.crossR),
@@ -398,8 +411,8 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   if ((rs = totals()) != GLA_OK) return rs;
   if ((rs = tr.mark()) != GLA_OK) return rs;
   rs = dev(gla::launch_gate_grad(x.dtype, (const float*)(w + p.Dloc), (const float*)(w + p.carry),
-                                 dS_T ? (const float*)(w + p.cT) : nullptr, dlog_alpha, BH, T, DK,
-                                 C, s));
+                                 dS_T ? (const float*)(w + p.cT) : nullptr, log_alpha, gate_of(d),
+                                 dlog_alpha, BH, T, DK, C, s));
   if (rs != GLA_OK) return rs;
   return tr.mark();
 }
@@ -417,6 +430,7 @@ gla_status_t gla_decode(const gla_desc_t* d, const void* q, const void* k, const
   if (!d) return GLA_ERR_INVALID_ARG;
   if (d->B < 0 || d->H < 0 || d->T < 0 || d->dk < 0 || d->dv < 0) return GLA_ERR_INVALID_ARG;
   if (d->dtype != GLA_F32 && d->dtype != GLA_BF16) return GLA_ERR_INVALID_ARG;
+  if (!gate_ok(d)) return GLA_ERR_INVALID_ARG;
   if (d->dk < 32 || d->dk > 256 || d->dk % 32 != 0) return GLA_ERR_UNSUPPORTED;
   if (d->dv < 32 || d->dv > 1024 || d->dv % 32 != 0) return GLA_ERR_UNSUPPORTED;
   const long long bh = (long long)d->B * d->H;
@@ -428,7 +442,7 @@ gla_status_t gla_decode(const gla_desc_t* d, const void* q, const void* k, const
     if (!aligned16(p)) return GLA_ERR_INVALID_ARG;
   gla::DecodeArgs a{};
   a.dtype = d->dtype; a.BH = (int)bh; a.T = d->T; a.dk = d->dk; a.dv = d->dv;
-  a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.S = S; a.o = o;
+  a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.S = S; a.o = o; a.gate = gate_of(d);
   return dev(gla::launch_decode(a, (hipStream_t)stream));
 }
 

@@ -5,6 +5,24 @@
 
 namespace gla {
 
+// Gate front-end (page "Gated Linear Attention Transformers with Hardware-Efficient
+// Training", atlas.scime.ai summary, section Approach: a data-dependent gate).  With `on`
+// the log_alpha operand holds gate logits x and the layer uses logsigmoid(x) * inv_tau;
+// otherwise the operand is log_alpha itself.
+struct GateFn {
+  int on;
+  float inv_tau;
+  __device__ __forceinline__ float operator()(float x) const {
+    return on ? (fminf(x, 0.f) - log1pf(__expf(-fabsf(x)))) * inv_tau : x;
+  }
+  // d log_alpha / dx: sigmoid(-x) * inv_tau, or 1 for log_alpha given directly
+  __device__ __forceinline__ float slope(float x) const {
+    if (!on) return 1.f;
+    const float e = __expf(-fabsf(x));
+    return (x >= 0.f ? e : 1.f) / (1.f + e) * inv_tau;
+  }
+};
+
 struct IntraArgs {
   int dtype, C, BH, T, dk, N;
   bool want_A;
@@ -15,18 +33,20 @@ struct IntraArgs {
   void *Qh, *QhT, *Kh, *KhT;
   float* eg;             // [BH][N][dk]
   float* g2_out;         // [BH][T][dk] g * log2(e), or NULL
+  GateFn gate;           // applied to la (not to g, which is already a cumsum)
 };
 hipError_t launch_intra(const IntraArgs& a, hipStream_t s);
 
-hipError_t launch_gate_cumsum(int dtype, const void* la, float* g, float* gamma, int BH, int T,
-                              int dk, int C, hipStream_t s);
+hipError_t launch_gate_cumsum(int dtype, const void* la, GateFn gate, float* g, float* gamma,
+                              int BH, int T, int dk, int C, hipStream_t s);
 hipError_t launch_state_dot(const float* dST, const float* ST, float* cT, int BH, int dk, int dv,
                             hipStream_t s);
 // chunk totals of D from the scans' cross terms -> tot [BH][N][dk]
 hipError_t launch_gate_tot(const float* crossF, const float* crossR, const float* cT,
                              float* tot, int BH, int T, int dk, int dv, int C, hipStream_t s);
 hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* tot, const float* cT,
-                            void* dla, int BH, int T, int dk, int C, hipStream_t s);
+                            const void* la, GateFn gate, void* dla, int BH, int T, int dk,
+                            int C, hipStream_t s);
 
 // Inter-chunk state scan.  store: 0 = none, 1 = operand type [dk][dv], 2 = operand type
 // [dv][dk], 3 = fp32 [dk][dv].  With X2T/Y2/cross set, every step also forms the
@@ -87,6 +107,8 @@ struct BwdArgs {
   float* Dloc;             // chunk-local suffix sums of D (single-kernel path)
   const float *tot, *cT;   // chunk totals of D, rowsum(dS_T * S_T) or NULL (split path)
   void* dla;               // dlog_alpha, written directly (split path)
+  const void* la;          // the gate operand, for the gate front-end's chain rule
+  GateFn gate;
 };
 // The backward chunk work: with bf16 operands and chunk 64 it is two kernels (dq, dk and
 // dlog_alpha, after the chunk totals are formed; then dv: launch_bwd_chunk and
@@ -101,6 +123,7 @@ struct DecodeArgs {
   const void *q, *k, *v, *la;
   float* S;   // [BH][dk][dv]
   void* o;    // [BH][T][dv]
+  GateFn gate;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 

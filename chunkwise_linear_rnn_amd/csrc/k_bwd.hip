@@ -227,8 +227,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dO, const float* __restrict__ g, const OpT* __restrict__ S,
     const OpT* __restrict__ dS, Tin* __restrict__ dq, Tin* __restrict__ dk_out,
-    const float* __restrict__ tot, const float* __restrict__ cT, Tin* __restrict__ dla, int T,
-    int dk, int dv, int N) {
+    const float* __restrict__ tot, const float* __restrict__ cT, const Tin* __restrict__ la,
+    GateFn gf, Tin* __restrict__ dla, int T, int dk, int dv, int N) {
   static_assert(sizeof(Tin) == sizeof(OpT), "input and operand types match");
   constexpr int C = 64, NM = 4, NS = C / 16, YLD = 64 + 8;
   constexpr int FLD = C + 4, GLD = 64 + 4, XLD = 64 + 8;
@@ -481,8 +481,12 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk(
       if (g2 > qd) after += x;
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      st[2 * C * SLD + (16 * m + 4 * qd + e) * SLD + c] = from_f32<Tin>(Dv[m][e] + after);
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * m + 4 * qd + e;
+      // gates given as logits: chain rule to the logit (rows past T hold no logit)
+      const float sl = gf.on && t < rows ? gf.slope(to_f32(la[(tok0 + t) * dk + d0 + c])) : 1.f;
+      st[2 * C * SLD + t * SLD + c] = from_f32<Tin>((Dv[m][e] + after) * sl);
+    }
     later += all;
   }
   __syncthreads();
@@ -755,7 +759,7 @@ static hipError_t launch_bwd_t2(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((k_bwd_dqk<Tin, OpT>), dim3((a.dk / 64) * a.N * a.BH), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,
                        (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq, (Tin*)a.dk_out, a.tot, a.cT,
-                       (Tin*)a.dla, a.T, a.dk, a.dv, a.N);
+                       (const Tin*)a.la, a.gate, (Tin*)a.dla, a.T, a.dk, a.dv, a.N);
   } else {
     hipLaunchKernelGGL((k_bwd_chunk<Tin, OpT, C, DK>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,

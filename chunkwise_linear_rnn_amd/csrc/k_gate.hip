@@ -16,7 +16,7 @@ namespace gla {
 
 template <typename Tin>
 __global__ __launch_bounds__(kThreads) void k_gate_cumsum(const Tin* __restrict__ la,
-                                                          float* __restrict__ g,
+                                                          GateFn gf, float* __restrict__ g,
                                                           float* __restrict__ gamma, int T,
                                                           int dk, int C, int N) {
   constexpr int U = 16;   // rows loaded per batch, so the loads are in flight together
@@ -28,7 +28,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_cumsum(const Tin* __restrict_
     for (int tb = t0; tb < t1; tb += U) {
       float x[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) x[u] = tb + u < t1 ? to_f32(la[base + (long)(tb + u) * dk + d]) : 0.f;
+      for (int u = 0; u < U; ++u)
+        x[u] = tb + u < t1 ? gf(to_f32(la[base + (long)(tb + u) * dk + d])) : 0.f;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         acc += x[u];
@@ -71,11 +72,12 @@ __global__ __launch_bounds__(kThreads) void k_gate_tot(const float* __restrict__
 }
 
 // dlog_alpha[t] = (chunk-local suffix sum of D at t) + c_T + sum of chunk totals of the
-// later chunks.
+// later chunks (times the gate front-end's slope when the gates come as logits).
 template <typename Tin>
 __global__ __launch_bounds__(kThreads) void k_gate_grad(const float* __restrict__ Dloc,
                                                         const float* __restrict__ tot,
                                                         const float* __restrict__ cT,
+                                                        const Tin* __restrict__ la, GateFn gf,
                                                         Tin* __restrict__ dla, int T, int dk,
                                                         int C, int N) {
   constexpr int U = 16;
@@ -91,7 +93,11 @@ __global__ __launch_bounds__(kThreads) void k_gate_grad(const float* __restrict_
       for (int u = 0; u < U; ++u) x[u] = tb + u < t1 ? Dloc[base + (long)(tb + u) * dk + d] : 0.f;
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (tb + u < t1) dla[base + (long)(tb + u) * dk + d] = from_f32<Tin>(x[u] + cr);
+        if (tb + u < t1) {
+          const long at = base + (long)(tb + u) * dk + d;
+          const float sl = gf.on ? gf.slope(to_f32(la[at])) : 1.f;
+          dla[at] = from_f32<Tin>((x[u] + cr) * sl);
+        }
     }
   }
 }
@@ -99,17 +105,17 @@ __global__ __launch_bounds__(kThreads) void k_gate_grad(const float* __restrict_
 // ---------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------
-hipError_t launch_gate_cumsum(int dtype, const void* la, float* g, float* gamma, int BH, int T,
-                              int dk, int C, hipStream_t s) {
+hipError_t launch_gate_cumsum(int dtype, const void* la, GateFn gate, float* g, float* gamma,
+                              int BH, int T, int dk, int C, hipStream_t s) {
   const int N = (T + C - 1) / C;
   if (BH == 0 || N == 0) return hipSuccess;
   dim3 grid(N, BH);
   if (dtype == 0)
-    hipLaunchKernelGGL(k_gate_cumsum<float>, grid, dim3(kThreads), 0, s, (const float*)la, g,
-                       gamma, T, dk, C, N);
+    hipLaunchKernelGGL(k_gate_cumsum<float>, grid, dim3(kThreads), 0, s, (const float*)la, gate,
+                       g, gamma, T, dk, C, N);
   else
-    hipLaunchKernelGGL(k_gate_cumsum<bf16>, grid, dim3(kThreads), 0, s, (const bf16*)la, g,
-                       gamma, T, dk, C, N);
+    hipLaunchKernelGGL(k_gate_cumsum<bf16>, grid, dim3(kThreads), 0, s, (const bf16*)la, gate,
+                       g, gamma, T, dk, C, N);
   return hipGetLastError();
 }
 
@@ -131,16 +137,17 @@ hipError_t launch_gate_tot(const float* crossF, const float* crossR, const float
 }
 
 hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* tot, const float* cT,
-                            void* dla, int BH, int T, int dk, int C, hipStream_t s) {
+                            const void* la, GateFn gate, void* dla, int BH, int T, int dk,
+                            int C, hipStream_t s) {
   const int N = (T + C - 1) / C;
   if (BH == 0 || N == 0) return hipSuccess;
   dim3 grid(N, BH);
   if (dtype == 0)
     hipLaunchKernelGGL(k_gate_grad<float>, grid, dim3(kThreads), 0, s, Dloc, tot, cT,
-                       (float*)dla, T, dk, C, N);
+                       (const float*)la, gate, (float*)dla, T, dk, C, N);
   else
-    hipLaunchKernelGGL(k_gate_grad<bf16>, grid, dim3(kThreads), 0, s, Dloc, tot, cT, (bf16*)dla,
-                       T, dk, C, N);
+    hipLaunchKernelGGL(k_gate_grad<bf16>, grid, dim3(kThreads), 0, s, Dloc, tot, cT,
+                       (const bf16*)la, gate, (bf16*)dla, T, dk, C, N);
   return hipGetLastError();
 }
 

@@ -46,15 +46,18 @@ __device__ __forceinline__ void pair_decode(int p, int& I, int& J) {
 }
 
 // A C x DB block of g (fp32) or log_alpha (SrcT) in registers as 16-byte units, written to
-// LDS as fp32 times log2 e.  Rows at and past `rows`: the last valid row repeated (clamp)
-// or zero.
+// LDS as fp32 times log2 e (through the gate front-end).  Rows at and past `rows`: the last
+// valid row repeated (clamp) or zero (after the front-end too, so padded rows never
+// decay the chunk).
 template <typename SrcT, int C, int DB>
 struct GBlock {
   static constexpr int kPer = 16 / (int)sizeof(SrcT), kUnitsRow = DB / kPer;
   static constexpr int kUnits = C * kUnitsRow, kPerThread = kUnits / kThreads;
   static_assert(kUnits % kThreads == 0, "whole units per thread");
   u32x4 u[kPerThread];
+  int zero_from;   // first row stored as zero
   __device__ __forceinline__ void load(const SrcT* __restrict__ src, long ld, int rows, bool clamp) {
+    zero_from = clamp ? 1 << 30 : rows;
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       const int idx = threadIdx.x + j * kThreads, rr = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
@@ -62,20 +65,26 @@ struct GBlock {
       else u[j] = rr < rows ? *reinterpret_cast<const u32x4*>(src + (long)rr * ld + c) : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  __device__ __forceinline__ void store(float* gs, int gld) const {
+  __device__ __forceinline__ void store(float* gs, int gld, GateFn gf) const {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       const int idx = threadIdx.x + j * kThreads, rr = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
+      const float keep = rr < zero_from ? 1.f : 0.f;
       if constexpr (sizeof(SrcT) == 2) {
         const bf16x8 b = __builtin_bit_cast(bf16x8, u[j]);
         f32x4 lo, hi;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { lo[e] = (float)b[e] * kLog2e; hi[e] = (float)b[4 + e] * kLog2e; }
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = gf((float)b[e]) * kLog2e * keep;
+          hi[e] = gf((float)b[4 + e]) * kLog2e * keep;
+        }
         *reinterpret_cast<f32x4*>(gs + rr * gld + c) = lo;
         *reinterpret_cast<f32x4*>(gs + rr * gld + c + 4) = hi;
       } else {
-        const f32x4 f = __builtin_bit_cast(f32x4, u[j]);
-        *reinterpret_cast<f32x4*>(gs + rr * gld + c) = f * kLog2e;
+        f32x4 f = __builtin_bit_cast(f32x4, u[j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = gf(f[e]) * kLog2e * keep;
+        *reinterpret_cast<f32x4*>(gs + rr * gld + c) = f;
       }
     }
   }
@@ -86,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ la,
     const float* __restrict__ gws, OpT* __restrict__ A_out, OpT* __restrict__ Qh_out,
     XT* __restrict__ QhT_out, OpT* __restrict__ Kh_out, XT* __restrict__ KhT_out,
-    float* __restrict__ eg_out, float* __restrict__ g2_out, int T, int dk, int N) {
+    float* __restrict__ eg_out, float* __restrict__ g2_out, GateFn gf, int T, int dk, int N) {
   constexpr int DB = 64;                    // dk columns per pass
   constexpr int NS = C / 16;                // sub-chunks
   constexpr int NPAIR = NS * (NS - 1) / 2;  // off-diagonal sub-block pairs
@@ -131,7 +140,8 @@ __global__ __launch_bounds__(kThreads) void k_intra(
 
   for (int d0 = 0; d0 < dk; d0 += DB) {
     // ---- g block (times log2 e), q, k -------------------------------------------------
-    pg.store(gs, GLD);
+    // g from the gate kernel is already transformed; log_alpha (or logits) goes through gf
+    pg.store(gs, GLD, G_WS ? GateFn{0, 1.f} : gf);
     tq.store(qs);
     tk.store(ks);
     if (d0 + DB < dk) fetch(d0 + DB);
@@ -324,8 +334,8 @@ template <typename Tin, typename OpT, typename XT, int C, bool GW, bool WA>
 static void launch_intra_k(const IntraArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_intra<Tin, OpT, XT, C, GW, WA>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
                      (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.la, a.g, (OpT*)a.A,
-                     (OpT*)a.Qh, (XT*)a.QhT, (OpT*)a.Kh, (XT*)a.KhT, a.eg, a.g2_out, a.T, a.dk,
-                     a.N);
+                     (OpT*)a.Qh, (XT*)a.QhT, (OpT*)a.Kh, (XT*)a.KhT, a.eg, a.g2_out, a.gate, a.T,
+                     a.dk, a.N);
 }
 template <typename Tin, typename OpT, typename XT, int C>
 static hipError_t launch_intra_t(const IntraArgs& a, hipStream_t s) {

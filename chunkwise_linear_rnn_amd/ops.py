@@ -7,8 +7,9 @@ import ctypes
 
 import torch
 
-from ._native import (BF16, F32, MATERIALIZED, RECOMPUTE, PASS_BWD, PASS_FWD, PASS_STATES,
-                      GlaError, lib, make_desc, workspace_bytes)
+from ._native import (BF16, F32, GATE_LOG_ALPHA, GATE_LOGITS, MATERIALIZED, RECOMPUTE,
+                      PASS_BWD, PASS_FWD, PASS_STATES, GlaError, lib, make_desc,
+                      workspace_bytes)
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 _MODES = {"materialized": MATERIALIZED, "recompute": RECOMPUTE}
@@ -35,7 +36,9 @@ def _check(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _desc_from(q, v, chunk, subchunk, state_mode):
+def _desc_from(q, v, chunk, subchunk, state_mode, gate_tau=None):
+    """gate_tau: None when the log_alpha argument is log_alpha itself, else the temperature
+    of gate logits (log_alpha = logsigmoid(x) / gate_tau)."""
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q and v must be [B, H, T, d]")
     if q.dtype not in _DT:
@@ -43,7 +46,10 @@ def _desc_from(q, v, chunk, subchunk, state_mode):
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     mode = _MODES[state_mode] if isinstance(state_mode, str) else int(state_mode)
-    return make_desc(B, H, T, dk, dv, chunk, subchunk, _DT[q.dtype], mode)
+    if gate_tau is None:
+        return make_desc(B, H, T, dk, dv, chunk, subchunk, _DT[q.dtype], mode)
+    return make_desc(B, H, T, dk, dv, chunk, subchunk, _DT[q.dtype], mode, GATE_LOGITS,
+                     float(gate_tau))
 
 
 def _workspace(desc, pass_, device, workspace):
@@ -61,9 +67,11 @@ def _call(name, st):
 
 
 def fwd(q, k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, state_mode="recompute",
-        final_state=True, workspace=None):
-    """o, S_T = the GLA layer forward (S_T is None when final_state is False)."""
-    desc = _desc_from(q, v, chunk, subchunk, state_mode)
+        final_state=True, workspace=None, gate_tau=None):
+    """o, S_T = the GLA layer forward (S_T is None when final_state is False).
+    gate_tau: when set, log_alpha holds gate logits x and the layer uses
+    logsigmoid(x) / gate_tau."""
+    desc = _desc_from(q, v, chunk, subchunk, state_mode, gate_tau)
     dev, dt = q.device, q.dtype
     B, H, T, dk, dv = desc.B, desc.H, desc.T, desc.dk, desc.dv
     for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)),
@@ -81,9 +89,10 @@ def fwd(q, k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, state_mode="recom
 
 
 def bwd(q, k, v, log_alpha, dO, S0=None, dS_T=None, *, chunk=64, subchunk=16,
-        want_dS0=True, workspace=None):
-    """dq, dk, dv, dlog_alpha, dS0 for the loss gradient (dO, dS_T)."""
-    desc = _desc_from(q, v, chunk, subchunk, RECOMPUTE)
+        want_dS0=True, workspace=None, gate_tau=None):
+    """dq, dk, dv, dlog_alpha, dS0 for the loss gradient (dO, dS_T).  With gate_tau set
+    (gate logits in log_alpha) the fourth output is the gradient with respect to them."""
+    desc = _desc_from(q, v, chunk, subchunk, RECOMPUTE, gate_tau)
     dev, dt = q.device, q.dtype
     B, H, T, dk, dv = desc.B, desc.H, desc.T, desc.dk, desc.dv
     for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)),
@@ -106,12 +115,16 @@ def bwd(q, k, v, log_alpha, dO, S0=None, dS_T=None, *, chunk=64, subchunk=16,
     return dq, dk_, dv_, dla, dS0
 
 
-def gate_cumsum(log_alpha, chunk=64):
+def gate_cumsum(log_alpha, chunk=64, gate_tau=None):
     """g (chunk-local inclusive cumsum, fp32) and gamma (chunk totals, fp32)."""
     if log_alpha.dim() != 4 or log_alpha.dtype not in _DT:
         raise ValueError("log_alpha must be [B,H,T,dk] float32/bfloat16")
     B, H, T, dk = log_alpha.shape
-    desc = make_desc(B, H, T, dk, 64, chunk, 16, _DT[log_alpha.dtype], RECOMPUTE)
+    if gate_tau is None:
+        desc = make_desc(B, H, T, dk, 64, chunk, 16, _DT[log_alpha.dtype], RECOMPUTE)
+    else:
+        desc = make_desc(B, H, T, dk, 64, chunk, 16, _DT[log_alpha.dtype], RECOMPUTE,
+                         GATE_LOGITS, float(gate_tau))
     _check(log_alpha, "log_alpha", (B, H, T, dk), log_alpha.dtype, log_alpha.device)
     N = (T + chunk - 1) // chunk
     g = torch.empty((B, H, T, dk), dtype=torch.float32, device=log_alpha.device)
@@ -121,9 +134,10 @@ def gate_cumsum(log_alpha, chunk=64):
     return g, gamma
 
 
-def chunk_states(k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, workspace=None):
+def chunk_states(k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, workspace=None,
+                 gate_tau=None):
     """states [B,H,N,dk,dv] (state before every chunk, fp32) and S_T."""
-    desc = _desc_from(k, v, chunk, subchunk, MATERIALIZED)
+    desc = _desc_from(k, v, chunk, subchunk, MATERIALIZED, gate_tau)
     dev, dt = k.device, k.dtype
     B, H, T, dk, dv = desc.B, desc.H, desc.T, desc.dk, desc.dv
     for t, n, shp in ((k, "k", (B, H, T, dk)), (v, "v", (B, H, T, dv)),
@@ -165,10 +179,10 @@ class GLAFunction(torch.autograd.Function):
         return dq, dk, dv, dla, dS0, None, None, None
 
 
-def decode(q, k, v, log_alpha, S):
+def decode(q, k, v, log_alpha, S, *, gate_tau=None):
     """o = the recurrent evaluation of T tokens (T typically 1), S (float32
     [B, H, dk, dv]) updated in place: S <- diag(exp(log_alpha_t)) S + k_t^T v_t,
-    o_t = q_t S, for t in order."""
+    o_t = q_t S, for t in order.  gate_tau: log_alpha holds gate logits (see fwd)."""
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q and v must be [B, H, T, d]")
     if q.dtype not in _DT:
@@ -180,7 +194,7 @@ def decode(q, k, v, log_alpha, S):
                       (v, "v", (B, H, T, dv)), (log_alpha, "log_alpha", (B, H, T, dk))):
         _check(t, n, shp, dt, dev)
     _check(S, "S", (B, H, dk, dv), torch.float32, dev)
-    desc = make_desc(B, H, T, dk, dv, 64, 16, _DT[dt], RECOMPUTE)
+    desc = _desc_from(q, v, 64, 16, RECOMPUTE, gate_tau)
     o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
     _call("gla_decode", lib().gla_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                          _ptr(log_alpha), _ptr(S), _ptr(o), _stream(dev)))

@@ -69,6 +69,15 @@ typedef enum { GLA_STATES_MATERIALIZED = 0, GLA_STATES_RECOMPUTE = 1 } gla_state
 
 typedef enum { GLA_PASS_FWD = 0, GLA_PASS_BWD = 1 } gla_pass_t;
 
+/* What the log_alpha argument of every entry point holds (Approach section: the gate is
+ * data-dependent).
+ *  GLA_GATE_LOG_ALPHA: log_alpha itself (finite, <= 0).
+ *  GLA_GATE_LOGITS: gate logits x; the layer uses log_alpha = logsigmoid(x) / gate_tau
+ *    (alpha = sigmoid(x)^(1/gate_tau), gate_tau > 0), formed inside the kernels that read
+ *    the gates, and the backward's dlog_alpha output is the gradient with respect to x,
+ *    dL/dlog_alpha * sigmoid(-x) / gate_tau. */
+typedef enum { GLA_GATE_LOG_ALPHA = 0, GLA_GATE_LOGITS = 1 } gla_gate_t;
+
 typedef struct {
   int32_t B, H, T;     /* batch, heads, sequence length (any of them may be 0)          */
   int32_t dk, dv;      /* key and value head dimensions                                  */
@@ -76,6 +85,8 @@ typedef struct {
   int32_t subchunk;    /* secondary (sub-)chunk size c of the intra-chunk part           */
   int32_t dtype;       /* gla_dtype_t                                                    */
   int32_t state_mode;  /* gla_state_mode_t                                               */
+  int32_t gate;        /* gla_gate_t (zero: log_alpha given directly)                      */
+  float gate_tau;      /* temperature of GLA_GATE_LOGITS (> 0, finite); unused otherwise   */
 } gla_desc_t;
 
 /* Supported by this build (else GLA_ERR_UNSUPPORTED):
@@ -91,7 +102,8 @@ int32_t gla_version(void);
 
 /* Host-only validation of a descriptor for a pass (no device call).  Returns GLA_OK,
  * GLA_ERR_INVALID_ARG (desc NULL, a negative size, chunk or subchunk < 1,
- * chunk % subchunk != 0, unknown dtype/mode/pass) or GLA_ERR_UNSUPPORTED. */
+ * chunk % subchunk != 0, unknown dtype/mode/pass/gate, GLA_GATE_LOGITS with gate_tau not
+ * a positive finite number) or GLA_ERR_UNSUPPORTED. */
 gla_status_t gla_validate(const gla_desc_t* desc, int32_t pass);
 
 /* Workspace bytes needed by gla_chunk_fwd (pass = GLA_PASS_FWD), gla_chunk_bwd

@@ -127,3 +127,18 @@ def test_decode_validation_before_any_launch(native):
                         None) == 0
     assert L.gla_decode(ctypes.byref(D(0, 3, 5, 96, 96)), None, None, None, None, None, None,
                         None) == 0
+
+
+def test_gate_front_end_fields(native):
+    """gate: 0 (log_alpha given) or 1 (logits, temperature gate_tau > 0 and finite)."""
+    D = native.make_desc
+    ok = D(1, 1, 64, 64, 64, 64, 16, native.BF16, native.RECOMPUTE, native.GATE_LOGITS, 16.0)
+    assert native.validate(ok) == 0 and native.validate(ok, native.PASS_BWD) == 0
+    for gate, tau in ((2, 1.0), (-1, 1.0), (1, 0.0), (1, -3.0), (1, float("nan")),
+                      (1, float("inf"))):
+        d = D(1, 1, 64, 64, 64, 64, 16, native.BF16, native.RECOMPUTE, gate, tau)
+        assert native.validate(d) == 1, (gate, tau)
+        p = ctypes.c_void_p(16)
+        assert native.lib().gla_decode(ctypes.byref(d), p, p, p, p, p, p, None) == 1
+    # the temperature is ignored when the gates are given as log_alpha
+    assert native.validate(D(1, 1, 64, 64, 64, 64, 16, native.BF16, native.RECOMPUTE, 0, 0.0)) == 0
