@@ -20,6 +20,9 @@ summary, or null when no summary matches the current kernel source.
 read and written in place) at the workload's head shape for a small and a serving-size
 batch, against the HBM roofline.
 
+`gate_logits_step` times the same step fed gate logits (the gate front-end: log_alpha =
+logsigmoid(x)/16 formed inside the kernels, the gradient returned for x).
+
 `cache_flushed` repeats the step after a 512 MiB write that evicts the 256 MiB Infinity
 Cache, with HIP events around the step only (the headline `value` is the warm rate).
 
@@ -398,6 +401,37 @@ def main():
         flushed = {"ms_per_step": fms, "value": B * T / (fms * 1e-3), "steps": args.flush_steps,
                    "flush_bytes": 512 << 20}
 
+    # The same steps fed gate logits (log_alpha = logsigmoid(x)/16 formed in the kernels,
+    # the gradient returned for x): what the gate front-end costs.
+    gate_fe = None
+    if not args.no_decode:
+        xg = up("gate_logits")
+        desc_g = nat.make_desc(B, H, T, dk, dv, C, cfg.subchunk,
+                               nat.BF16 if cfg.dtype == "bf16" else nat.F32, mode,
+                               nat.GATE_LOGITS, 16.0)
+        evs = hip.create(2)
+
+        def step_g():
+            for st in (L.gla_chunk_fwd(ctypes.byref(desc_g), P(q), P(k), P(v), P(xg), None, P(o),
+                                       P(S_T), P(wsf), wsf_n, sp),
+                       L.gla_chunk_bwd(ctypes.byref(desc_g), P(q), P(k), P(v), P(xg), None, P(dO),
+                                       None, P(dq), P(dk_), P(dv_), P(dla), None, P(wsb), wsb_n,
+                                       sp)):
+                if st:
+                    raise nat.GlaError(st, "gla_chunk_fwd/bwd with gate logits")
+        for _ in range(3):
+            step_g()
+        n_g = max(5, args.steps // 2)
+        hip.record(evs[0], sp)
+        for _ in range(n_g):
+            step_g()
+        hip.record(evs[1], sp)
+        torch.cuda.synchronize()
+        gms = hip.elapsed_ms(evs[0], evs[1]) / n_g
+        hip.destroy(evs)
+        gate_fe = {"ms_per_step": gms, "value": B * T / (gms * 1e-3), "gate_tau": 16.0,
+                   "steps": n_g}
+
     if args.copy_calibration:
         nbytes = 1 << 30
         a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1)
@@ -450,6 +484,7 @@ def main():
         "tflops": tflops, "mfma_peak_frac": flops / (ms_per_step * 1e-3) / PEAK_BF16,
         "roofline": roof,
         "cache_flushed": flushed,
+        "gate_logits_step": gate_fe,
     }
     for arr in evf + evb:
         hip.destroy(arr)

@@ -12,14 +12,19 @@ namespace gla {
 struct GateFn {
   int on;
   float inv_tau;
+  // logsigmoid(x) = min(x, 0) - log(1 + exp(-|x|)), with the hardware base-2 exp and log
+  // (1 + exp(-|x|) is in (1, 2], so its log has no cancellation; for x beyond ~17 the
+  // exp term drops below fp32 resolution next to 1 and the gate rounds to exactly 1)
   __device__ __forceinline__ float operator()(float x) const {
-    return on ? (fminf(x, 0.f) - log1pf(__expf(-fabsf(x)))) * inv_tau : x;
+    if (!on) return x;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f);
+    return (fminf(x, 0.f) - 0.6931471805599453f * __builtin_amdgcn_logf(1.f + e)) * inv_tau;
   }
   // d log_alpha / dx: sigmoid(-x) * inv_tau, or 1 for log_alpha given directly
   __device__ __forceinline__ float slope(float x) const {
     if (!on) return 1.f;
-    const float e = __expf(-fabsf(x));
-    return (x >= 0.f ? e : 1.f) / (1.f + e) * inv_tau;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f);
+    return (x >= 0.f ? e : 1.f) * __builtin_amdgcn_rcpf(1.f + e) * inv_tau;
   }
 };
 
