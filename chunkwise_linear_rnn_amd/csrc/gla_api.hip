@@ -393,7 +393,8 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   auto totals = [&]() {
     return dev(gla::launch_gate_tot((const float*)(w + p.crossF), (const float*)(w + p.crossR),
                                     dS_T ? (const float*)(w + p.cT) : nullptr,
-                                    (float*)(w + p.carry), BH, T, DK, DV, C, s));
+                                    (float*)(w + p.carry), BH, T, DK,
+                                    DV / gla::scan_tile_v(sa), C, s));
   };
   if (gla::bwd_split(x.dtype, C)) {
     // totals first: the dq / dk kernel finishes the gate gradient itself

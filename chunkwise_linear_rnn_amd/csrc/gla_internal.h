@@ -48,7 +48,7 @@ hipError_t launch_state_dot(const float* dST, const float* ST, float* cT, int BH
                             hipStream_t s);
 // chunk totals of D from the scans' cross terms -> tot [BH][N][dk]
 hipError_t launch_gate_tot(const float* crossF, const float* crossR, const float* cT,
-                             float* tot, int BH, int T, int dk, int dv, int C, hipStream_t s);
+                             float* tot, int BH, int T, int dk, int ntile, int C, hipStream_t s);
 hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* tot, const float* cT,
                             const void* la, GateFn gate, void* dla, int BH, int T, int dk,
                             int C, hipStream_t s);
@@ -76,6 +76,8 @@ hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s);
 // Two scans of the same shape and kind (the backward's forward and reverse scans) in one
 // launch, so that their workgroups share the machine.
 hipError_t launch_state_scan2(const ScanArgs& a, const ScanArgs& b, hipStream_t s);
+// Value columns per scan workgroup (the cross-term tiles come in dv / this many).
+int scan_tile_v(const ScanArgs& a);
 // Per-direction kernel arguments of the scan kernel.
 struct ScanDir {
   const void *XT, *Y, *X2T, *Y2;

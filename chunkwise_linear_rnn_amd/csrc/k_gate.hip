@@ -127,12 +127,12 @@ hipError_t launch_state_dot(const float* dST, const float* ST, float* cT, int BH
 }
 
 hipError_t launch_gate_tot(const float* crossF, const float* crossR, const float* cT,
-                             float* tot, int BH, int T, int dk, int dv, int C, hipStream_t s) {
+                             float* tot, int BH, int T, int dk, int ntile, int C, hipStream_t s) {
   (void)cT;
   const int N = (T + C - 1) / C;
   if (BH == 0 || N == 0) return hipSuccess;
   hipLaunchKernelGGL(k_gate_tot, dim3(N, BH), dim3(kThreads), 0, s, crossF, crossR, tot, dk,
-                     dv / 64, N);
+                     ntile, N);
   return hipGetLastError();
 }
 

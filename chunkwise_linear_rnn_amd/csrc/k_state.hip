@@ -61,17 +61,21 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS>
-__global__ __launch_bounds__(kThreads, 4) void k_state_scan(ScanDir d0, ScanDir d1, int ndir,
+template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS, int TV>
+__global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, ScanDir d1, int ndir,
                                                             const float* __restrict__ eg, int T,
                                                             int dk, int dv, int N) {
-  constexpr int TV = 64, YLD = C + 8, XW = SPLIT ? 2 * C : C;
-  constexpr int SLD = 64 + 8;   // state tile staging for 16-byte row stores
+  // TV value columns per workgroup: NJ accumulator tiles per wave, NY 64-column
+  // value-side tiles per operand
+  constexpr int NJ = TV / 16, NY = TV / 64, YLD = C + 8, XW = SPLIT ? 2 * C : C;
+  static_assert(TV == 64 || (TV == 128 && STORE != 2), "[v][k] staging is 64 columns wide");
+  constexpr int SLD = (STORE == 2 ? 64 : TV) + 8;   // state tile staging for 16-byte row stores
+  constexpr int SROWS = STORE == 2 ? TV : 64;
   using StT = typename std::conditional<STORE == 3, float, OpT>::type;
   using XR = XRegs<OpT, SPLIT, C>;
   __shared__ __attribute__((aligned(16))) OpT ys[TV * YLD];
   __shared__ __attribute__((aligned(16))) OpT y2s[CROSS ? TV * YLD : 8];
-  __shared__ __attribute__((aligned(16))) StT ss[STORE != 0 ? 64 * SLD : 8];
+  __shared__ __attribute__((aligned(16))) StT ss[STORE != 0 ? SROWS * SLD : 8];
   // 1-D grid, XCD-aware: the dv tiles of one (bh, dk tile) share the transposed operand
   // tiles and the dk tiles of one bh share the value-side tiles, so they run on one XCD.
   // With two scans in the launch, the first half of the logical ids runs the first.
@@ -94,9 +98,9 @@ __global__ __launch_bounds__(kThreads, 4) void k_state_scan(ScanDir d0, ScanDir 
   const int rl = 16 * w + 4 * qd;          // tile-local accumulator rows rl .. rl+3
   const int row0 = k0 + rl;
 
-  f32x4 acc[4];   // acc[j][e] = S[row0 + e][v0 + 16 j + r]
+  f32x4 acc[NJ];   // acc[j][e] = S[row0 + e][v0 + 16 j + r]
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       acc[j][e] = S_in ? S_in[((long)bh * dk + row0 + e) * dv + v0 + 16 * j + r] : 0.f;
@@ -106,14 +110,17 @@ __global__ __launch_bounds__(kThreads, 4) void k_state_scan(ScanDir d0, ScanDir 
   // operands go straight into MFMA fragments, each reloaded for the next chunk as soon as
   // the current chunk's products have consumed it (one set of registers, so four
   // workgroups fit on a CU).
-  ColTile<OpT, Tin, C, YLD> ty, ty2;
+  ColTile<OpT, Tin, C, YLD> ty[NY], ty2[NY];
   f32x4 egr;   // exp(gamma) of this lane's rows, for the chunk about to be applied
   XR cx, cx2;
   auto xrow = [&](int i) { return (((long)bh * N + i) * dk + k0 + 16 * w + r) * XW; };
   auto fetch_y = [&](int i) {
     const int t0 = i * C, rows = min(C, T - t0);
-    ty.load(Y + ((long)bh * T + t0) * dv + v0, dv, rows);
-    if constexpr (CROSS) ty2.load(Y2 + ((long)bh * T + t0) * dv + v0, dv, rows);
+#pragma unroll
+    for (int h = 0; h < NY; ++h) {
+      ty[h].load(Y + ((long)bh * T + t0) * dv + v0 + 64 * h, dv, rows);
+      if constexpr (CROSS) ty2[h].load(Y2 + ((long)bh * T + t0) * dv + v0 + 64 * h, dv, rows);
+    }
   };
   auto fetch_eg = [&](int i) { egr = *reinterpret_cast<const f32x4*>(eg + ((long)bh * N + i) * dk + row0); };
   if (N > 0) {
@@ -133,12 +140,15 @@ __global__ __launch_bounds__(kThreads, 4) void k_state_scan(ScanDir d0, ScanDir 
     const int i = reverse ? N - 1 - step : step;
     const int inext = reverse ? i - 1 : i + 1;
     const bool more = step + 1 < N;
-    ty.store(ys);
-    if constexpr (CROSS) ty2.store(y2s);
+#pragma unroll
+    for (int h = 0; h < NY; ++h) {
+      ty[h].store(ys + 64 * h * YLD);
+      if constexpr (CROSS) ty2[h].store(y2s + 64 * h * YLD);
+    }
     if constexpr (STORE != 0) {
       // the state before this chunk, through LDS
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if constexpr (STORE == 2)
@@ -149,10 +159,11 @@ __global__ __launch_bounds__(kThreads, 4) void k_state_scan(ScanDir d0, ScanDir 
     }
     __syncthreads();
     if constexpr (STORE != 0) {
-      constexpr int kPer = 16 / (int)sizeof(StT), kUnits = 64 * 64 / kPer;
+      constexpr int kPer = 16 / (int)sizeof(StT), kCols = STORE == 2 ? 64 : TV;
+      constexpr int kUnits = 64 * TV / kPer;
       const long sb = ((long)bh * N + i) * dk * dv;
       for (int idx = threadIdx.x; idx < kUnits; idx += kThreads) {
-        const int e0 = idx * kPer, a = e0 / 64, b = e0 % 64;
+        const int e0 = idx * kPer, a = e0 / kCols, b = e0 % kCols;
         long off;
         if constexpr (STORE == 2) off = sb + (long)(v0 + a) * dk + k0 + b;
         else off = sb + (long)(k0 + a) * dv + v0 + b;
@@ -172,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_state_scan(ScanDir d0, ScanDir 
       // P_j = X2^T Y2 for column tile j, folded into the row sums one tile at a time
       float sum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < C / 32; ++kb) {
@@ -192,12 +203,12 @@ __global__ __launch_bounds__(kThreads, 4) void k_state_scan(ScanDir d0, ScanDir 
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j][e] *= egr[e];
+      for (int j = 0; j < NJ; ++j) acc[j][e] *= egr[e];
     if (more) fetch_eg(inext);
 #pragma unroll
     for (int kb = 0; kb < C / 32; ++kb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         Frag<OpT> fb;
         load_frag_c(fb, ys + (16 * j + r) * YLD + kb * 32);
         cx.apply(acc[j], kb, fb);
@@ -213,14 +224,14 @@ __global__ __launch_bounds__(kThreads, 4) void k_state_scan(ScanDir d0, ScanDir 
   }
   if (S_out) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         S_out[((long)bh * dk + row0 + e) * dv + v0 + 16 * j + r] = acc[j][e];
   }
 }
 
-template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS>
+template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS, int TV>
 static void launch_scan_k(const ScanArgs& a, const ScanArgs* b, hipStream_t s) {
   auto dir = [](const ScanArgs& x) {
     ScanDir d;
@@ -229,22 +240,32 @@ static void launch_scan_k(const ScanArgs& a, const ScanArgs* b, hipStream_t s) {
     return d;
   };
   const int ndir = b ? 2 : 1;
-  dim3 grid(ndir * (a.dv / 64) * (a.dk / 64) * a.BH);
-  hipLaunchKernelGGL((k_state_scan<Tin, OpT, SPLIT, C, STORE, CROSS>), grid, dim3(kThreads), 0, s,
-                     dir(a), dir(b ? *b : a), ndir, a.eg, a.T, a.dk, a.dv, a.N);
+  dim3 grid(ndir * (a.dv / TV) * (a.dk / 64) * a.BH);
+  hipLaunchKernelGGL((k_state_scan<Tin, OpT, SPLIT, C, STORE, CROSS, TV>), grid, dim3(kThreads), 0,
+                     s, dir(a), dir(b ? *b : a), ndir, a.eg, a.T, a.dk, a.dv, a.N);
+}
+
+int scan_tile_v(const ScanArgs& a) {
+  return (a.cross && a.dtype != 0 && a.C == 64 && a.dv % 128 == 0) ? 128 : 64;
 }
 
 template <typename Tin, typename OpT, bool SPLIT, int C>
 static hipError_t launch_scan_t(const ScanArgs& a, const ScanArgs* b, hipStream_t s) {
   if (a.cross) {
     // the backward: operand-type states, [dk][dv]
-    launch_scan_k<Tin, OpT, SPLIT, C, 1, true>(a, b, s);
+    if constexpr (C == 64 && sizeof(OpT) == 2) {
+      if (scan_tile_v(a) == 128) {
+        launch_scan_k<Tin, OpT, SPLIT, C, 1, true, 128>(a, b, s);
+        return hipGetLastError();
+      }
+    }
+    launch_scan_k<Tin, OpT, SPLIT, C, 1, true, 64>(a, b, s);
   } else {
     switch (a.store) {
-      case 0: launch_scan_k<Tin, OpT, SPLIT, C, 0, false>(a, b, s); break;
-      case 1: launch_scan_k<Tin, OpT, SPLIT, C, 1, false>(a, b, s); break;
-      case 2: launch_scan_k<Tin, OpT, SPLIT, C, 2, false>(a, b, s); break;
-      default: launch_scan_k<Tin, OpT, SPLIT, C, 3, false>(a, b, s); break;
+      case 0: launch_scan_k<Tin, OpT, SPLIT, C, 0, false, 64>(a, b, s); break;
+      case 1: launch_scan_k<Tin, OpT, SPLIT, C, 1, false, 64>(a, b, s); break;
+      case 2: launch_scan_k<Tin, OpT, SPLIT, C, 2, false, 64>(a, b, s); break;
+      default: launch_scan_k<Tin, OpT, SPLIT, C, 3, false, 64>(a, b, s); break;
     }
   }
   return hipGetLastError();
