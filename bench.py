@@ -54,7 +54,7 @@ STAGE_SOURCE = {
     "gate_cumsum": "k_gate.hip", "gate_tot": "k_gate.hip", "gate_grad": "k_gate.hip",
     "state_dot": "k_gate.hip", "intra": "k_intra.hip", "state_scan": "k_state.hip",
     "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip", "state_scans": "k_state.hip", "output": "k_fwd.hip",
-    "fwd_fused": "k_fwd.hip", "bwd_chunk": "k_bwd.hip", "bwd_dqk": "k_bwd.hip",
+    "fwd_fused": "k_fwd.hip", "seg_state": "k_state.hip", "bwd_chunk": "k_bwd.hip", "bwd_dqk": "k_bwd.hip",
     "bwd_dv": "k_bwd.hip",
 }
 
@@ -90,6 +90,9 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
         return tokp * dk * e + tok * dv * e + st + BH * dk * dv * 4, tok * 2 * dk * dv
     if stage == "output":
         return tokp * dk * e + BH * N * C * C * e + st + 2 * tok * dv * e, tok * (2 * dk * dv + C * dv)
+    if stage == "seg_state":   # the state at the midpoint chunk: first half of Kh^T and v
+        h = BH * (N // 2) * C
+        return h * dk * e + h * dv * e + BH * (N // 2) * dk * 4 + BH * dk * dv * 4, h * 2 * dk * dv
     if stage == "fwd_fused":
         byt = 2 * tokp * dk * e + BH * N * C * C * e + 2 * tok * dv * e + BH * dk * dv * 4
         return byt, tok * (4 * dk * dv + C * dv)
@@ -448,6 +451,8 @@ def main():
     print(f"{'pass':4s} {'stage':16s} {'us':>9s} {'GB/s':>8s} {'TFLOP/s':>8s}", file=sys.stderr)
     dom_key, dom_ms = None, -1.0
     for (tag, name), ms in stages.items():
+        if ms <= 0.0:   # a stage with no launch for this shape
+            continue
         byt, fl = stage_work(name, tag, mode_s, B, H, T, dk, dv, C, e)
         print(f"{tag:4s} {name:16s} {ms * 1e3:9.2f} {byt / ms / 1e6:8.0f} {fl / ms / 1e9:8.1f}",
               file=sys.stderr)

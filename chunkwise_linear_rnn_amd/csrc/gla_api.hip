@@ -44,7 +44,7 @@ Dims dims_of(const gla_desc_t* d) {
 // Workspace carving.  Every region is 256-byte aligned.
 struct Plan {
   size_t g = 0, A = 0, Qh = 0, QhT = 0, Kh = 0, KhT = 0, eg = 0, st = 0, dst = 0, ST = 0,
-         cT = 0, Dloc = 0, crossF = 0, crossR = 0, carry = 0, total = 0;
+         cT = 0, Dloc = 0, crossF = 0, crossR = 0, carry = 0, smid = 0, total = 0;
 };
 
 Plan plan_of(const gla_desc_t* d, int pass) {
@@ -70,6 +70,8 @@ Plan plan_of(const gla_desc_t* d, int pass) {
     p.KhT = take(opB);
     p.eg = take(egB);
     if (mat) p.st = take(stB);
+    if (!mat && gla::fused_split(x.dtype, (int)x.C, (int)x.N) > 0)
+      p.smid = take((size_t)x.BH * x.dk * x.dv * 4);
   } else if (pass == GLA_PASS_BWD) {
     // the scans' transposed operands are kept in fp32 (split into two bf16 halves)
     const size_t op32 = rowsP * x.dk * 4;
@@ -139,7 +141,7 @@ struct Tracer {
 
 // Stage names of each pipeline, in launch order.
 const char* const kFwdMat[] = {"gate_cumsum", "intra", "state_scan", "output"};
-const char* const kFwdRec[] = {"intra", "fwd_fused"};
+const char* const kFwdRec[] = {"intra", "seg_state", "fwd_fused"};
 const char* const kBwd[] = {"intra", "state_scans", "state_dot", "gate_tot", "bwd_dqk",
                             "bwd_dv"};
 const char* const kBwdOne[] = {"intra", "state_scans", "state_dot", "bwd_chunk", "gate_tot",
@@ -150,7 +152,7 @@ int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, in
   int n;
   if (pass == GLA_PASS_FWD) {
     if (d->state_mode == GLA_STATES_MATERIALIZED) { src = kFwdMat; n = 4; }
-    else { src = kFwdRec; n = 2; }
+    else { src = kFwdRec; n = 3; }
   } else if (gla::bwd_split(d->dtype, d->chunk)) {
     src = kBwd; n = 6;
   } else {
@@ -314,6 +316,19 @@ gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void
   fa.dtype = x.dtype; fa.C = (int)x.C; fa.BH = (int)x.BH; fa.T = (int)x.T; fa.dk = (int)x.dk;
   fa.dv = (int)x.dv; fa.N = (int)x.N; fa.Qh = w + p.Qh; fa.KhT = w + p.KhT; fa.A = w + p.A;
   fa.v = v; fa.eg = (const float*)(w + p.eg); fa.S0 = S0; fa.o = o; fa.S_T = S_T;
+  fa.split = gla::fused_split(x.dtype, (int)x.C, (int)x.N);
+  // with a split, the state before the midpoint chunk comes first: a state scan over the
+  // first half of the chunks (no per-chunk states written)
+  if ((rs = tr.mark()) != GLA_OK) return rs;
+  if (fa.split > 0) {
+    gla::ScanArgs sa{};
+    sa.dtype = x.dtype; sa.C = (int)x.C; sa.BH = (int)x.BH; sa.T = (int)x.T; sa.dk = (int)x.dk;
+    sa.dv = (int)x.dv; sa.N = (int)x.N; sa.reverse = false; sa.store = 0; sa.nsteps = fa.split;
+    sa.XT = w + p.KhT; sa.Y = v; sa.eg = (const float*)(w + p.eg); sa.S_in = S0;
+    sa.S_out = (float*)(w + p.smid);
+    if ((rs = dev(gla::launch_state_scan(sa, s))) != GLA_OK) return rs;
+    fa.S_mid = (const float*)(w + p.smid);
+  }
   if ((rs = tr.mark()) != GLA_OK) return rs;
   if ((rs = dev(gla::launch_fwd_fused(fa, s))) != GLA_OK) return rs;
   return tr.mark();

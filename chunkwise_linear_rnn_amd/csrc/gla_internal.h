@@ -71,6 +71,7 @@ struct ScanArgs {
   const float* S_in;     // [BH][dk][dv] or NULL
   void* states;          // see store
   float* S_out;          // [BH][dk][dv] or NULL
+  int nsteps;            // chunks to walk (0: all N); the layout strides still use N
 };
 hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s);
 // Two scans of the same shape and kind (the backward's forward and reverse scans) in one
@@ -102,7 +103,14 @@ struct FusedArgs {
   const float* S0;
   void* o;
   float* S_T;
+  // sequence split: chunks [0, split) and [split, N) walk in parallel, the second from
+  // S_mid = the state before chunk `split` (0: one walk over all chunks)
+  int split;
+  const float* S_mid;
 };
+// The split point of the fused forward for a shape (0: no split).  With a split, the
+// state before that chunk must be formed first (a state scan over chunks [0, split)).
+int fused_split(int dtype, int C, int N);
 hipError_t launch_fwd_fused(const FusedArgs& a, hipStream_t s);
 
 struct BwdArgs {

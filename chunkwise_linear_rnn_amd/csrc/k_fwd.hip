@@ -86,7 +86,8 @@ template <typename Tin, typename OpT, int C, int DK>
 __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
     const OpT* __restrict__ Qh, const OpT* __restrict__ KhT, const OpT* __restrict__ A,
     const float* __restrict__ eg, const Tin* __restrict__ V, const float* __restrict__ S0,
-    Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N) {
+    Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N, int split,
+    const float* __restrict__ S_mid) {
   constexpr int NT = kFusedThreads, TV = 64, NM = C / 16, KH = DK / 2, NP = KH / 16;
   constexpr int QLD = DK + 8, KLD = C + 8, ALD = C + 8, VLD = C + 8, OLD = TV + 8, RLD = TV + 4;
   __shared__ __attribute__((aligned(16))) OpT qs[C * QLD];
@@ -96,10 +97,14 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
   __shared__ __attribute__((aligned(16))) Tin os_[2][C * OLD];   // O tile, double-buffered
   __shared__ __attribute__((aligned(16))) float red[C * RLD];     // partial O of the upper dk half
   __shared__ float egs[DK];
-  // 1-D grid, XCD-aware: the dv tiles of one bh share every Qh / Kh^T / A tile
-  const int nvt = dv / TV;
-  const int lt = xcd_logical(blockIdx.x, gridDim.x);
+  // 1-D grid, XCD-aware: the dv tiles of one bh share every Qh / Kh^T / A tile.  With a
+  // sequence split the second half of the logical ids walks chunks [split, N) from S_mid.
+  const int nvt = dv / TV, nseg = split > 0 ? 2 : 1, per_seg = (int)gridDim.x / nseg;
+  const int lg = xcd_logical(blockIdx.x, gridDim.x);
+  const int seg = lg / per_seg, lt = lg % per_seg;
   const int v0 = (lt % nvt) * TV, bh = lt / nvt;
+  const int ib = seg == 1 ? split : 0, ie = (nseg == 2 && seg == 0) ? split : N;
+  const float* __restrict__ Sinit = seg == 1 ? S_mid : S0;
   // wave w: value columns 16 (w % 4) .. +15, state rows kh*KH .. kh*KH + KH-1 (kh = w / 4)
   const int w = threadIdx.x >> 6, vc = w & 3, kh = w >> 2;
   const int l = lane_id(), r = l & 15, qd = l >> 4;
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
   for (int p = 0; p < NP; ++p)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      S[p][e] = S0 ? S0[((long)bh * DK + k0 + 16 * p + 4 * qd + e) * dv + col] : 0.f;
+      S[p][e] = Sinit ? Sinit[((long)bh * DK + k0 + 16 * p + 4 * qd + e) * dv + col] : 0.f;
 
   FlatTile<OpT, C, DK, QLD, NT> tq;
   FlatTile<OpT, DK, C, KLD, NT> tk;
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
     tv.load(V + ((long)bh * T + t0) * dv + v0, dv, min(C, T - t0));
     if (threadIdx.x < DK) egr = eg[((long)bh * N + i) * DK + threadIdx.x];
   };
-  if (N > 0) fetch(0);
+  if (ie > ib) fetch(ib);
 
   // O tile of the previous chunk leaves right after the first barrier of the next chunk,
   // before that chunk's prefetch (vector memory operations complete in order).
@@ -140,15 +145,15 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
             *reinterpret_cast<const u32x4*>(ob + rr * OLD + cc);
     }
   };
-  for (int i = 0; i < N; ++i) {
+  for (int i = ib; i < ie; ++i) {
     tq.store(qs);
     tk.store(ks);
     ta.store(as_);
     tv.store(vs);
     if (threadIdx.x < DK) egs[threadIdx.x] = egr;
     __syncthreads();
-    if (i > 0) store_o(i - 1);
-    if (i + 1 < N) fetch(i + 1);
+    if (i > ib) store_o(i - 1);
+    if (i + 1 < ie) fetch(i + 1);
 
     // O_i = Qh_i S + A_i V_i as two partial sums, one per dk half; the A V rows are split
     // between the halves
@@ -217,8 +222,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
     }
     __syncthreads();
   }
-  if (N > 0) store_o(N - 1);
-  if (S_T) {
+  if (ie > ib) store_o(ie - 1);
+  if (S_T && seg == nseg - 1) {
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
@@ -339,15 +344,19 @@ hipError_t launch_output(const OutArgs& a, hipStream_t s) {
   return launch_output_t<bf16, bf16, 128>(a, s);
 }
 
+int fused_split(int dtype, int C, int N) { return (dtype != 0 && C == 64 && N >= 4) ? N / 2 : 0; }
+
 template <typename Tin, typename OpT, int C, int DK>
 static hipError_t launch_fused_t2(const FusedArgs& a, hipStream_t s) {
-  dim3 grid((a.dv / 64) * a.BH);
   if constexpr (C == 64 && sizeof(OpT) == 2) {
+    const int split = a.S_mid ? a.split : 0;
+    dim3 grid((a.dv / 64) * a.BH * (split > 0 ? 2 : 1));
     hipLaunchKernelGGL((k_fwd_fused_staged<Tin, OpT, C, DK>), grid, dim3(kFusedThreads), 0, s,
                        (const OpT*)a.Qh, (const OpT*)a.KhT, (const OpT*)a.A, a.eg,
-                       (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N);
+                       (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N, split, a.S_mid);
     return hipGetLastError();
   }
+  dim3 grid((a.dv / 64) * a.BH);
   hipLaunchKernelGGL((k_fwd_fused<Tin, OpT, C, DK>), grid, dim3(kThreads), 0, s,
                      (const OpT*)a.Qh, (const OpT*)a.KhT, (const OpT*)a.A, a.eg,
                      (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N);

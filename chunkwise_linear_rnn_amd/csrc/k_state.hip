@@ -64,7 +64,7 @@ __device__ __forceinline__ float row16_sum(float x) {
 template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS, int TV>
 __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, ScanDir d1, int ndir,
                                                             const float* __restrict__ eg, int T,
-                                                            int dk, int dv, int N) {
+                                                            int dk, int dv, int N, int nsteps) {
   // TV value columns per workgroup: NJ accumulator tiles per wave, NY 64-column
   // value-side tiles per operand
   constexpr int NJ = TV / 16, NY = TV / 64, YLD = C + 8, XW = SPLIT ? 2 * C : C;
@@ -136,10 +136,10 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // prefetch would make the next step wait for the write round trip.
   float part_prev[4] = {0.f, 0.f, 0.f, 0.f};   // cross term of the previous chunk
   int i_prev = -1;
-  for (int step = 0; step < N; ++step) {
+  for (int step = 0; step < nsteps; ++step) {
     const int i = reverse ? N - 1 - step : step;
     const int inext = reverse ? i - 1 : i + 1;
-    const bool more = step + 1 < N;
+    const bool more = step + 1 < nsteps;
 #pragma unroll
     for (int h = 0; h < NY; ++h) {
       ty[h].store(ys + 64 * h * YLD);
@@ -242,7 +242,8 @@ static void launch_scan_k(const ScanArgs& a, const ScanArgs* b, hipStream_t s) {
   const int ndir = b ? 2 : 1;
   dim3 grid(ndir * (a.dv / TV) * (a.dk / 64) * a.BH);
   hipLaunchKernelGGL((k_state_scan<Tin, OpT, SPLIT, C, STORE, CROSS, TV>), grid, dim3(kThreads), 0,
-                     s, dir(a), dir(b ? *b : a), ndir, a.eg, a.T, a.dk, a.dv, a.N);
+                     s, dir(a), dir(b ? *b : a), ndir, a.eg, a.T, a.dk, a.dv, a.N,
+                     a.nsteps > 0 && a.nsteps < a.N ? a.nsteps : a.N);
 }
 
 int scan_tile_v(const ScanArgs& a) {
@@ -276,7 +277,8 @@ static hipError_t launch_scans(const ScanArgs& a, const ScanArgs* b, hipStream_t
   if (a.cross && a.store != 1) return hipErrorInvalidValue;
   if (b && (b->dtype != a.dtype || b->C != a.C || b->BH != a.BH || b->T != a.T ||
             b->dk != a.dk || b->dv != a.dv || b->N != a.N || b->xt_f32 != a.xt_f32 ||
-            b->store != a.store || (b->cross != nullptr) != (a.cross != nullptr) || b->eg != a.eg))
+            b->store != a.store || (b->cross != nullptr) != (a.cross != nullptr) || b->eg != a.eg ||
+            b->nsteps != a.nsteps))
     return hipErrorInvalidValue;
   if (a.dtype == 0) return launch_scan_t<float, float, false, 64>(a, b, s);
   if (a.xt_f32) {

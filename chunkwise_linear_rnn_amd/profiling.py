@@ -22,13 +22,13 @@ import sys
 STAGE_KERNEL = {"bwd_chunk": "k_bwd_chunk", "bwd_dqk": "k_bwd_dqk", "bwd_dv": "k_bwd_dv",
                 "fwd_fused": "k_fwd_fused", "intra": "k_intra",
                 "state_scan_fwd": "k_state_scan", "state_scan_rev": "k_state_scan",
-                "state_scans": "k_state_scan",
+                "state_scans": "k_state_scan", "seg_state": "k_state_scan",
                 "output": "k_output", "gate_cumsum": "k_gate_cumsum", "gate_grad": "k_gate_grad",
                 "gate_tot": "k_gate_tot"}
 STAGE_SOURCE = {"bwd_chunk": "k_bwd.hip", "bwd_dqk": "k_bwd.hip", "bwd_dv": "k_bwd.hip",
                 "fwd_fused": "k_fwd.hip", "intra": "k_intra.hip",
                 "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip",
-                "state_scans": "k_state.hip",
+                "state_scans": "k_state.hip", "seg_state": "k_state.hip",
                 "output": "k_fwd.hip", "gate_cumsum": "k_gate.hip", "gate_grad": "k_gate.hip",
                 "gate_tot": "k_gate.hip"}
 

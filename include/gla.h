@@ -169,7 +169,9 @@ gla_status_t gla_decode(const gla_desc_t* desc, const void* q, const void* k, co
  * writes up to max_names static stage names to `names` (nullable); -1 on a NULL desc or a
  * bad pass.  The stages are
  *   forward, materialized: gate_cumsum, intra, state_scan, output
- *   forward, recompute:    intra, fwd_fused
+ *   forward, recompute:    intra, seg_state (bf16, chunk 64, at least 4 chunks: the state
+ *                          at the midpoint chunk, so that the two halves of the sequence
+ *                          run in parallel; no launch otherwise), fwd_fused
  *   backward:              intra, state_scans (the forward and the reverse scan, one
  *                          launch), [state_dot when dS_T is given], then gate_tot, bwd_dqk,
  *                          bwd_dv (bf16, chunk 64) or bwd_chunk, gate_tot, gate_grad
