@@ -278,12 +278,28 @@ struct RowTile {
 template <typename T, int ROWS, int COLS, int LD>
 using FlatTileRows = FlatTile<T, ROWS, COLS, LD>;
 
+// Position of element (column c, row r) of a transposed tile kept with the swizzle of
+// ColTile<..., SWZ = true>: each LDS row (one column c of the source) is made of 8-element
+// chunks, and chunk r / 8 sits at chunk (r / 8) ^ ((c / 8) & 6).  With LD = 72 (bf16) the
+// transposing stores of a wave then fall on distinct banks (64 banks of 4 bytes) instead
+// of four to a bank, and 16-byte fragment reads of 16 consecutive columns stay
+// conflict-free (the XOR is the same for all of them).
+__device__ __forceinline__ int swz_chunk(int c, int chunk) { return chunk ^ ((c >> 3) & 6); }
+// Fragment read from such a tile: row `c`, elements 32 kb + 8 (lane / 16) .. + 7.
+__device__ __forceinline__ void load_frag_cs(Frag<bf16>& f, const bf16* tile, int LD, int c,
+                                             int kb) {
+  const int ch = swz_chunk(c, 4 * kb + (lane_id() >> 4));
+  f.v = *reinterpret_cast<const bf16x8*>(tile + c * LD + 8 * ch);
+}
+
 // ROWS x 64 slice of a row-major [*, gld] matrix, rows beyond `rows` zero, staged
 // transposed (lds[c * LD + r]) through 2-row x 8-column units.  The loads keep the raw
 // 16-byte words (no use of the data until store), so they stay in flight.  Input and
-// LDS element types are the same (bf16 or fp32).
-template <typename OpT, typename Tin, int ROWS, int LD, int NT = kThreads>
+// LDS element types are the same (bf16 or fp32).  SWZ (bf16 only): rows of the staged
+// tile are chunk-swizzled as described at swz_chunk.
+template <typename OpT, typename Tin, int ROWS, int LD, int NT = kThreads, bool SWZ = false>
 struct ColTile {
+  static_assert(!SWZ || sizeof(OpT) == 2, "swizzled staging is for 16-bit elements");
   static_assert(sizeof(OpT) == sizeof(Tin), "same element type in and out");
   static constexpr int kWords = sizeof(Tin) == 2 ? 1 : 2;   // 16-byte words per 8 elements
   static constexpr int kUnits = (ROWS / 2) * 8;
@@ -316,8 +332,12 @@ struct ColTile {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const uint32_t a = x0[j][0][w], b = x1[j][0][w];
-            *reinterpret_cast<uint32_t*>(lds + (c + 2 * w) * LD + r) = (a & 0xFFFFu) | (b << 16);
-            *reinterpret_cast<uint32_t*>(lds + (c + 2 * w + 1) * LD + r) = (a >> 16) | (b & 0xFFFF0000u);
+            const int c0 = c + 2 * w, c1 = c0 + 1;
+            // r is even: the word holding rows r, r + 1 stays inside one 8-row chunk
+            const int r0 = SWZ ? 8 * swz_chunk(c0, r >> 3) + (r & 7) : r;
+            const int r1 = SWZ ? 8 * swz_chunk(c1, r >> 3) + (r & 7) : r;
+            *reinterpret_cast<uint32_t*>(lds + c0 * LD + r0) = (a & 0xFFFFu) | (b << 16);
+            *reinterpret_cast<uint32_t*>(lds + c1 * LD + r1) = (a >> 16) | (b & 0xFFFF0000u);
           }
         } else {
 #pragma unroll

@@ -110,7 +110,13 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // operands go straight into MFMA fragments, each reloaded for the next chunk as soon as
   // the current chunk's products have consumed it (one set of registers, so four
   // workgroups fit on a CU).
-  ColTile<OpT, Tin, C, YLD> ty[NY], ty2[NY];
+  // bf16 value-side tiles are staged chunk-swizzled (conflict-free transposing stores)
+  constexpr bool SWZ = sizeof(OpT) == 2;
+  ColTile<OpT, Tin, C, YLD, kThreads, SWZ> ty[NY], ty2[NY];
+  auto yfrag = [&](Frag<OpT>& fb, const OpT* tile, int c, int kb) {
+    if constexpr (SWZ) load_frag_cs(fb, tile, YLD, c, kb);
+    else load_frag_c(fb, tile + c * YLD + kb * 32);
+  };
   f32x4 egr;   // exp(gamma) of this lane's rows, for the chunk about to be applied
   XR cx, cx2;
   auto xrow = [&](int i) { return (((long)bh * N + i) * dk + k0 + 16 * w + r) * XW; };
@@ -188,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
 #pragma unroll
         for (int kb = 0; kb < C / 32; ++kb) {
           Frag<OpT> fb;
-          load_frag_c(fb, y2s + (16 * j + r) * YLD + kb * 32);
+          yfrag(fb, y2s, 16 * j + r, kb);
           cx2.apply(P, kb, fb);
         }
 #pragma unroll
@@ -210,7 +216,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         Frag<OpT> fb;
-        load_frag_c(fb, ys + (16 * j + r) * YLD + kb * 32);
+        yfrag(fb, ys, 16 * j + r, kb);
         cx.apply(acc[j], kb, fb);
       }
     if (more) cx.load(XT + xrow(inext));
