@@ -528,10 +528,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dv(const OpT* __restrict__ Kh,
   const OpT* Khc = Kh + ((long)bh * N * C + t0) * dk;
   const OpT* dSc = dS + ((long)bh * N + i) * dk * dv + v0;
   RowTile<OpT, C, 64, LD> tk;
-  ColTile<OpT, OpT, 64, LD> ts;
+  // transposed tiles are staged chunk-swizzled (conflict-free stores)
+  ColTile<OpT, OpT, 64, LD, kThreads, true> ts;
   {
-    ColTile<OpT, OpT, C, LD> ta;
-    ColTile<OpT, Tin, C, LD> to;
+    ColTile<OpT, OpT, C, LD, kThreads, true> ta;
+    ColTile<OpT, Tin, C, LD, kThreads, true> to;
     ta.load(A + ((long)bh * N + i) * C * C, C, C);
     to.load(dO + ((long)bh * T + t0) * dv + v0, dv, rows);
     tk.load(Khc, dk, C);
@@ -548,12 +549,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dv(const OpT* __restrict__ Kh,
 #pragma unroll
   for (int kb = 0; kb < C / 32; ++kb) {
     Frag<OpT> fb;
-    load_frag_c(fb, doT + (16 * w + r) * LD + kb * 32);
+    load_frag_cs(fb, doT, LD, 16 * w + r, kb);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       if (32 * kb + 31 >= 16 * m) {
         Frag<OpT> fa;
-        load_frag_c(fa, aT + (16 * m + r) * LD + kb * 32);
+        load_frag_cs(fa, aT, LD, 16 * m + r, kb);
         mma(acc[m], fa, fb);
       }
     }
@@ -566,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dv(const OpT* __restrict__ Kh,
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       Frag<OpT> fb;
-      load_frag_c(fb, dsT + (16 * w + r) * LD + kb * 32);
+      load_frag_cs(fb, dsT, LD, 16 * w + r, kb);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         Frag<OpT> fa;

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
   FlatTile<OpT, C, DK, QLD, NT> tq;
   FlatTile<OpT, DK, C, KLD, NT> tk;
   FlatTile<OpT, C, C, ALD, NT> ta;
-  ColTile<OpT, Tin, C, VLD, NT> tv;
+  ColTile<OpT, Tin, C, VLD, NT, true> tv;   // chunk-swizzled (conflict-free stores)
   float egr = 0.f;
   auto fetch = [&](int i) {
     const int t0 = i * C;
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
 #pragma unroll
     for (int kb = 0; kb < C / 32; ++kb) {
       Frag<OpT> fb;
-      load_frag_c(fb, vs + c16 * VLD + kb * 32);
+      load_frag_cs(fb, vs, VLD, c16, kb);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         if ((m < NM / 2) == (kh == 0) && 32 * kb <= 16 * m + 15) {
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
 #pragma unroll
     for (int kb = 0; kb < C / 32; ++kb) {
       Frag<OpT> fb;
-      load_frag_c(fb, vs + c16 * VLD + kb * 32);
+      load_frag_cs(fb, vs, VLD, c16, kb);
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         Frag<OpT> fa;
