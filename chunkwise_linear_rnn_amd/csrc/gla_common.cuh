@@ -244,7 +244,21 @@ struct FlatTile {
   }
 };
 
-// ROWS x COLS tile of a row-major [*, gld] matrix (rows beyond `rows` zero) moved as
+// Row-bounded tile loads: every lane issues its 16-byte load (rows at or beyond `rows`,
+// which must be >= 1, read the last valid row instead), and the words of rows beyond are
+// zeroed only when the tile is stored to LDS.  With no branch around the loads and no use
+// of their data before the store, the compiler's counts of loads in flight stay exact and
+// the loads of a prefetched tile stay in flight until then.
+template <typename T>
+__device__ __forceinline__ u32x4 load16_clamped(const T* __restrict__ g, long gld, int r, int c,
+                                                int rows) {
+  return *reinterpret_cast<const u32x4*>(g + (long)min(r, rows - 1) * gld + c);
+}
+__device__ __forceinline__ u32x4 keep_if(const u32x4& v, bool ok) {
+  return u32x4{ok ? v[0] : 0u, ok ? v[1] : 0u, ok ? v[2] : 0u, ok ? v[3] : 0u};
+}
+
+// ROWS x COLS tile of a row-major [*, gld] matrix (rows beyond `rows` zero, rows >= 1) moved as
 // 16-byte units into an LDS tile with row stride LD, same orientation.
 template <typename T, int ROWS, int COLS, int LD, int NT = kThreads>
 struct RowTile {
@@ -253,13 +267,15 @@ struct RowTile {
   static constexpr int kUnits = ROWS * kUnitsRow;
   static constexpr int kPerThread = (kUnits + NT - 1) / NT;
   u32x4 u[kPerThread];
+  int nrows;
   __device__ __forceinline__ void load(const T* __restrict__ g, long gld, int rows) {
+    nrows = rows;
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       const int idx = threadIdx.x + j * NT;
       const int r = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
       if (kUnits % NT == 0 || idx < kUnits)
-        u[j] = r < rows ? *reinterpret_cast<const u32x4*>(g + r * gld + c) : u32x4{0u, 0u, 0u, 0u};
+        u[j] = load16_clamped(g, gld, r, c, rows);
     }
   }
   __device__ __forceinline__ void store(T* lds) const {
@@ -268,7 +284,7 @@ struct RowTile {
       const int idx = threadIdx.x + j * NT;
       const int r = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
       if (kUnits % NT == 0 || idx < kUnits)
-        *reinterpret_cast<u32x4*>(lds + r * LD + c) = u[j];
+        *reinterpret_cast<u32x4*>(lds + r * LD + c) = keep_if(u[j], r < nrows);
     }
   }
 };
@@ -292,7 +308,7 @@ __device__ __forceinline__ void load_frag_cs(Frag<bf16>& f, const bf16* tile, in
   f.v = *reinterpret_cast<const bf16x8*>(tile + c * LD + 8 * ch);
 }
 
-// ROWS x 64 slice of a row-major [*, gld] matrix, rows beyond `rows` zero, staged
+// ROWS x 64 slice of a row-major [*, gld] matrix, rows beyond `rows` (>= 1) zero, staged
 // transposed (lds[c * LD + r]) through 2-row x 8-column units.  The loads keep the raw
 // 16-byte words (no use of the data until store), so they stay in flight.  Input and
 // LDS element types are the same (bf16 or fp32).  SWZ (bf16 only): rows of the staged
@@ -305,7 +321,9 @@ struct ColTile {
   static constexpr int kUnits = (ROWS / 2) * 8;
   static constexpr int kPerThread = (kUnits + NT - 1) / NT;
   u32x4 x0[kPerThread][kWords], x1[kPerThread][kWords];
+  int nrows;
   __device__ __forceinline__ void load(const Tin* __restrict__ g, long gld, int rows) {
+    nrows = rows;
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       const int idx = threadIdx.x + j * NT;
@@ -314,9 +332,8 @@ struct ColTile {
 #pragma unroll
         for (int h = 0; h < kWords; ++h) {
           const int ce = c + h * (8 / kWords);
-          x0[j][h] = r < rows ? *reinterpret_cast<const u32x4*>(g + r * gld + ce) : u32x4{0u, 0u, 0u, 0u};
-          x1[j][h] = r + 1 < rows ? *reinterpret_cast<const u32x4*>(g + (r + 1) * gld + ce)
-                                  : u32x4{0u, 0u, 0u, 0u};
+          x0[j][h] = load16_clamped(g, gld, r, ce, rows);
+          x1[j][h] = load16_clamped(g, gld, r + 1, ce, rows);
         }
       }
     }
@@ -327,11 +344,12 @@ struct ColTile {
       const int idx = threadIdx.x + j * NT;
       const int r = (idx / 8) * 2, c = (idx % 8) * 8;
       if (kUnits % NT == 0 || idx < kUnits) {
+        const bool ok0 = r < nrows, ok1 = r + 1 < nrows;
         if constexpr (sizeof(OpT) == 2) {
           // word w of a row holds elements 2w (low half) and 2w+1 (high half)
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            const uint32_t a = x0[j][0][w], b = x1[j][0][w];
+            const uint32_t a = ok0 ? x0[j][0][w] : 0u, b = ok1 ? x1[j][0][w] : 0u;
             const int c0 = c + 2 * w, c1 = c0 + 1;
             // r is even: the word holding rows r, r + 1 stays inside one 8-row chunk
             const int r0 = SWZ ? 8 * swz_chunk(c0, r >> 3) + (r & 7) : r;
@@ -344,7 +362,7 @@ struct ColTile {
           for (int e = 0; e < 8; ++e) {
             u32x4 const& A = x0[j][e / 4];
             u32x4 const& B = x1[j][e / 4];
-            uint32_t pr[2] = {A[e % 4], B[e % 4]};
+            uint32_t pr[2] = {ok0 ? A[e % 4] : 0u, ok1 ? B[e % 4] : 0u};
             *reinterpret_cast<uint2*>(lds + (c + e) * LD + r) = *reinterpret_cast<uint2*>(pr);
           }
         }

@@ -104,6 +104,10 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       acc[j][e] = S_in ? S_in[((long)bh * dk + row0 + e) * dv + v0 + 16 * j + r] : 0.f;
+  // Settle the initial-state loads before the loop: otherwise the compiler, merging the
+  // loop's entry with its back edge, treats the state registers as possibly still being
+  // loaded and waits for nearly every prefetch in flight at each step.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
   // The value-side tiles of the next chunk are loaded into registers (then LDS,
   // transposed) while the current chunk computes.  This wave's rows of the transposed
@@ -117,7 +121,6 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
     if constexpr (SWZ) load_frag_cs(fb, tile, YLD, c, kb);
     else load_frag_c(fb, tile + c * YLD + kb * 32);
   };
-  f32x4 egr;   // exp(gamma) of this lane's rows, for the chunk about to be applied
   XR cx, cx2;
   auto xrow = [&](int i) { return (((long)bh * N + i) * dk + k0 + 16 * w + r) * XW; };
   auto fetch_y = [&](int i) {
@@ -128,11 +131,9 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
       if constexpr (CROSS) ty2[h].load(Y2 + ((long)bh * T + t0) * dv + v0 + 64 * h, dv, rows);
     }
   };
-  auto fetch_eg = [&](int i) { egr = *reinterpret_cast<const f32x4*>(eg + ((long)bh * N + i) * dk + row0); };
   if (N > 0) {
     const int i0 = reverse ? N - 1 : 0;
     fetch_y(i0);
-    fetch_eg(i0);
     cx.load(XT + xrow(i0));
     if constexpr (CROSS) cx2.load(X2T + xrow(i0));
   }
@@ -144,8 +145,14 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   int i_prev = -1;
   for (int step = 0; step < nsteps; ++step) {
     const int i = reverse ? N - 1 - step : step;
-    const int inext = reverse ? i - 1 : i + 1;
+    // the next chunk's operands are fetched unconditionally (the last step refetches its
+    // own chunk), so that the compiler's wait counts stay exact along the loop
     const bool more = step + 1 < nsteps;
+    const int inext = more ? (reverse ? i - 1 : i + 1) : i;
+    // exp(gamma) of this lane's rows for this chunk, loaded here and first used after the
+    // cross term: a value carried over from the previous step would make the compiler
+    // wait for every load in flight at the loop's back edge
+    const f32x4 egr = *reinterpret_cast<const f32x4*>(eg + ((long)bh * N + i) * dk + row0);
 #pragma unroll
     for (int h = 0; h < NY; ++h) {
       ty[h].store(ys + 64 * h * YLD);
@@ -183,7 +190,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
         *reinterpret_cast<f32x4*>(cross + (((long)bh * N + i_prev) * nvt + vt) * dk + row0) = o;
       }
     }
-    if (more) fetch_y(inext);
+    fetch_y(inext);
 
     if constexpr (CROSS) {
       // P_j = X2^T Y2 for column tile j, folded into the row sums one tile at a time
@@ -200,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
 #pragma unroll
         for (int e = 0; e < 4; ++e) sum[e] += acc[j][e] * P[e];
       }
-      if (more) cx2.load(X2T + xrow(inext));
+      cx2.load(X2T + xrow(inext));
 #pragma unroll
       for (int e = 0; e < 4; ++e) part_prev[e] = row16_sum(sum[e]);
       i_prev = i;
@@ -210,7 +217,6 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
     for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[j][e] *= egr[e];
-    if (more) fetch_eg(inext);
 #pragma unroll
     for (int kb = 0; kb < C / 32; ++kb)
 #pragma unroll
@@ -219,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
         yfrag(fb, ys, 16 * j + r, kb);
         cx.apply(acc[j], kb, fb);
       }
-    if (more) cx.load(XT + xrow(inext));
+    cx.load(XT + xrow(inext));
     __syncthreads();
   }
   if constexpr (CROSS) {
