@@ -259,8 +259,16 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk(
 
   // gate gradient carried into this chunk for column c: the chunk totals of D over the
   // later chunks (lane group qd takes every fourth chunk), plus c_T
+  // (eight chunk totals per lane in flight at once; out-of-range ones read a valid entry
+  // and are dropped)
   float carry = 0.f;
-  for (int j = i + 1 + qd; j < N; j += 4) carry += tot[((long)bh * N + j) * dk + d0 + c];
+  for (int j0 = i + 1 + qd; j0 < N; j0 += 32) {
+    float tv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) tv[u] = tot[((long)bh * N + min(j0 + 4 * u, N - 1)) * dk + d0 + c];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) carry += j0 + 4 * u < N ? tv[u] : 0.f;
+  }
 
   f32x4 adq[NM], adk[NM], adA[NM];   // adA[n] = dA tile (w, n), n <= w
 #pragma unroll
@@ -287,7 +295,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk(
     tdO.store(dOs);
     tV.store(Vs);
     __syncthreads();
-    if (vb + 1 < NV) fetch(vb + 1, ns, nds);
+    // unconditional (the last block refetches itself): exact wait counts for the compiler
+    fetch(min(vb + 1, NV - 1), ns, nds);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       Frag<OpT> fO[NM], fV[NM], fOw;

@@ -138,7 +138,10 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
   auto store_o = [&](int ip) {
     const int tp = ip * C, rp = min(C, T - tp);
     const Tin* ob = os_[ip & 1];
-    for (int idx = threadIdx.x; idx < kUnits; idx += NT) {
+#pragma unroll
+    for (int u_ = 0; u_ < (kUnits + NT - 1) / NT; ++u_) {   // fixed trip count
+      const int idx = threadIdx.x + u_ * NT;
+      if ((kUnits) % NT != 0 && idx >= kUnits) continue;
       const int e0 = idx * kPer, rr = e0 / TV, cc = e0 % TV;
       if (rr < rp)
         *reinterpret_cast<u32x4*>(O + ((long)bh * T + tp + rr) * dv + v0 + cc) =

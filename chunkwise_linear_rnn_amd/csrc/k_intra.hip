@@ -61,29 +61,30 @@ struct GBlock {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       const int idx = threadIdx.x + j * kThreads, rr = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
-      if (clamp) u[j] = *reinterpret_cast<const u32x4*>(src + (long)min(rr, rows - 1) * ld + c);
-      else u[j] = rr < rows ? *reinterpret_cast<const u32x4*>(src + (long)rr * ld + c) : u32x4{0u, 0u, 0u, 0u};
+      // always a load (of the last valid row past `rows`): no branch around it, and the
+      // rows past `rows` are zeroed at store time when not clamped
+      u[j] = *reinterpret_cast<const u32x4*>(src + (long)min(rr, rows - 1) * ld + c);
     }
   }
   __device__ __forceinline__ void store(float* gs, int gld, GateFn gf) const {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       const int idx = threadIdx.x + j * kThreads, rr = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
-      const float keep = rr < zero_from ? 1.f : 0.f;
+      const bool keep = rr < zero_from;
       if constexpr (sizeof(SrcT) == 2) {
         const bf16x8 b = __builtin_bit_cast(bf16x8, u[j]);
         f32x4 lo, hi;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          lo[e] = gf((float)b[e]) * kLog2e * keep;
-          hi[e] = gf((float)b[4 + e]) * kLog2e * keep;
+          lo[e] = keep ? gf((float)b[e]) * kLog2e : 0.f;
+          hi[e] = keep ? gf((float)b[4 + e]) * kLog2e : 0.f;
         }
         *reinterpret_cast<f32x4*>(gs + rr * gld + c) = lo;
         *reinterpret_cast<f32x4*>(gs + rr * gld + c + 4) = hi;
       } else {
         f32x4 f = __builtin_bit_cast(f32x4, u[j]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = gf(f[e]) * kLog2e * keep;
+        for (int e = 0; e < 4; ++e) f[e] = keep ? gf(f[e]) * kLog2e : 0.f;
         *reinterpret_cast<f32x4*>(gs + rr * gld + c) = f;
       }
     }
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(
     pg.store(gs, GLD, G_WS ? GateFn{0, 1.f} : gf);
     tq.store(qs);
     tk.store(ks);
-    if (d0 + DB < dk) fetch(d0 + DB);
+    fetch(min(d0 + DB, dk - DB));   // unconditional (exact wait counts); the last refetches
     if constexpr (!G_WS) {
       // chunk-local cumsum down each column: four 16-row segments per column, each
       // summed in registers, then offset by the totals of the segments above it
@@ -165,7 +166,10 @@ __global__ __launch_bounds__(kThreads) void k_intra(
     }
     __syncthreads();
     if (g2_out) {   // g * log2 e for the backward chunk kernel
-      for (int idx = threadIdx.x; idx < C * (DB / 8); idx += kThreads) {
+#pragma unroll
+      for (int u_ = 0; u_ < (C * (DB / 8) + kThreads - 1) / kThreads; ++u_) {   // fixed trip count
+        const int idx = threadIdx.x + u_ * kThreads;
+        if ((C * (DB / 8)) % kThreads != 0 && idx >= C * (DB / 8)) continue;
         const int rr = idx / (DB / 8), c = (idx % (DB / 8)) * 8;
         if (rr < rows) {
           float x[8];
@@ -181,7 +185,10 @@ __global__ __launch_bounds__(kThreads) void k_intra(
     if (eg_out && threadIdx.x < DB)
       eg_out[((long)bh * N + i) * dk + d0 + threadIdx.x] = __builtin_amdgcn_exp2f(glast[threadIdx.x]);
     if (Qh_out || Kh_out) {
-      for (int idx = threadIdx.x; idx < C * (DB / 8); idx += kThreads) {
+#pragma unroll
+      for (int u_ = 0; u_ < (C * (DB / 8) + kThreads - 1) / kThreads; ++u_) {   // fixed trip count
+        const int idx = threadIdx.x + u_ * kThreads;
+        if ((C * (DB / 8)) % kThreads != 0 && idx >= C * (DB / 8)) continue;
         const int rr = idx / (DB / 8), c = (idx % (DB / 8)) * 8;
         const long o = ((long)bh * N * C + t0 + rr) * dk + d0 + c;
         float x[8];
@@ -204,7 +211,10 @@ __global__ __launch_bounds__(kThreads) void k_intra(
       // transposed per chunk: [dk][C] in the operand type, or (XT = float) as a bf16 high
       // part [dk][0..C) followed by its bf16 remainder [dk][C..2C) in the same bytes
       constexpr bool kSplit = sizeof(XT) == 4 && sizeof(OpT) == 2;
-      for (int idx = threadIdx.x; idx < DB * (C / 8); idx += kThreads) {
+#pragma unroll
+      for (int u_ = 0; u_ < (DB * (C / 8) + kThreads - 1) / kThreads; ++u_) {   // fixed trip count
+        const int idx = threadIdx.x + u_ * kThreads;
+        if ((DB * (C / 8)) % kThreads != 0 && idx >= DB * (C / 8)) continue;
         const int c = idx / (C / 8), r8 = (idx % (C / 8)) * 8;
         const long rowi = ((long)bh * N + i) * dk + d0 + c;
         float x[8];

@@ -175,7 +175,10 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
       constexpr int kPer = 16 / (int)sizeof(StT), kCols = STORE == 2 ? 64 : TV;
       constexpr int kUnits = 64 * TV / kPer;
       const long sb = ((long)bh * N + i) * dk * dv;
-      for (int idx = threadIdx.x; idx < kUnits; idx += kThreads) {
+#pragma unroll
+      for (int u_ = 0; u_ < (kUnits + kThreads - 1) / kThreads; ++u_) {   // fixed trip count
+        const int idx = threadIdx.x + u_ * kThreads;
+        if ((kUnits) % kThreads != 0 && idx >= kUnits) continue;
         const int e0 = idx * kPer, a = e0 / kCols, b = e0 % kCols;
         long off;
         if constexpr (STORE == 2) off = sb + (long)(v0 + a) * dk + k0 + b;
