@@ -109,33 +109,47 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // loaded and waits for nearly every prefetch in flight at each step.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
-  // The value-side tiles of the next chunk are loaded into registers (then LDS,
-  // transposed) while the current chunk computes.  This wave's rows of the transposed
-  // operands go straight into MFMA fragments, each reloaded for the next chunk as soon as
-  // the current chunk's products have consumed it (one set of registers, so four
-  // workgroups fit on a CU).
+  // The operands of later chunks are loaded into registers while the current chunk
+  // computes: the value-side tiles (then LDS, transposed) and this wave's rows of the
+  // transposed operands (straight into MFMA fragments), each set reloaded as soon as the
+  // current chunk has consumed it.  DEPTH sets of registers keep DEPTH chunks in flight
+  // (one set where the register budget of four workgroups per CU leaves no room).
+  constexpr int DEPTH = (TV == 128 || (!CROSS && C == 64 && sizeof(OpT) == 2)) ? 2 : 1;
   // bf16 value-side tiles are staged chunk-swizzled (conflict-free transposing stores)
   constexpr bool SWZ = sizeof(OpT) == 2;
-  ColTile<OpT, Tin, C, YLD, kThreads, SWZ> ty[NY], ty2[NY];
+  using YT = ColTile<OpT, Tin, C, YLD, kThreads, SWZ>;
+  struct Set {
+    YT ty[NY], ty2[NY];
+    XR cx, cx2;
+  };
+  Set sets[DEPTH];
   auto yfrag = [&](Frag<OpT>& fb, const OpT* tile, int c, int kb) {
     if constexpr (SWZ) load_frag_cs(fb, tile, YLD, c, kb);
     else load_frag_c(fb, tile + c * YLD + kb * 32);
   };
-  XR cx, cx2;
   auto xrow = [&](int i) { return (((long)bh * N + i) * dk + k0 + 16 * w + r) * XW; };
-  auto fetch_y = [&](int i) {
+  auto fetch_y = [&](Set& st, int i) {
     const int t0 = i * C, rows = min(C, T - t0);
 #pragma unroll
     for (int h = 0; h < NY; ++h) {
-      ty[h].load(Y + ((long)bh * T + t0) * dv + v0 + 64 * h, dv, rows);
-      if constexpr (CROSS) ty2[h].load(Y2 + ((long)bh * T + t0) * dv + v0 + 64 * h, dv, rows);
+      st.ty[h].load(Y + ((long)bh * T + t0) * dv + v0 + 64 * h, dv, rows);
+      if constexpr (CROSS) st.ty2[h].load(Y2 + ((long)bh * T + t0) * dv + v0 + 64 * h, dv, rows);
     }
   };
-  if (N > 0) {
-    const int i0 = reverse ? N - 1 : 0;
-    fetch_y(i0);
-    cx.load(XT + xrow(i0));
-    if constexpr (CROSS) cx2.load(X2T + xrow(i0));
+  // chunk of a step; steps past the end map to the last one (refetched, never used), so
+  // that every prefetch is unconditional and the compiler's wait counts stay exact
+  auto chunk_of = [&](int step) {
+    const int sc = min(step, nsteps - 1);
+    return reverse ? N - 1 - sc : sc;
+  };
+  if (nsteps > 0) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int i0 = chunk_of(d);
+      fetch_y(sets[d], i0);
+      sets[d].cx.load(XT + xrow(i0));
+      if constexpr (CROSS) sets[d].cx2.load(X2T + xrow(i0));
+    }
   }
 
   // Stores are issued right after the step's first barrier and before the next chunk's
@@ -143,20 +157,16 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // prefetch would make the next step wait for the write round trip.
   float part_prev[4] = {0.f, 0.f, 0.f, 0.f};   // cross term of the previous chunk
   int i_prev = -1;
-  for (int step = 0; step < nsteps; ++step) {
-    const int i = reverse ? N - 1 - step : step;
-    // the next chunk's operands are fetched unconditionally (the last step refetches its
-    // own chunk), so that the compiler's wait counts stay exact along the loop
-    const bool more = step + 1 < nsteps;
-    const int inext = more ? (reverse ? i - 1 : i + 1) : i;
+  auto body = [&](int step, Set& st) {
+    const int i = chunk_of(step), ipre = chunk_of(step + DEPTH);
     // exp(gamma) of this lane's rows for this chunk, loaded here and first used after the
     // cross term: a value carried over from the previous step would make the compiler
     // wait for every load in flight at the loop's back edge
     const f32x4 egr = *reinterpret_cast<const f32x4*>(eg + ((long)bh * N + i) * dk + row0);
 #pragma unroll
     for (int h = 0; h < NY; ++h) {
-      ty[h].store(ys + 64 * h * YLD);
-      if constexpr (CROSS) ty2[h].store(y2s + 64 * h * YLD);
+      st.ty[h].store(ys + 64 * h * YLD);
+      if constexpr (CROSS) st.ty2[h].store(y2s + 64 * h * YLD);
     }
     if constexpr (STORE != 0) {
       // the state before this chunk, through LDS
@@ -193,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
         *reinterpret_cast<f32x4*>(cross + (((long)bh * N + i_prev) * nvt + vt) * dk + row0) = o;
       }
     }
-    fetch_y(inext);
+    fetch_y(st, ipre);
 
     if constexpr (CROSS) {
       // P_j = X2^T Y2 for column tile j, folded into the row sums one tile at a time
@@ -205,12 +215,12 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
         for (int kb = 0; kb < C / 32; ++kb) {
           Frag<OpT> fb;
           yfrag(fb, y2s, 16 * j + r, kb);
-          cx2.apply(P, kb, fb);
+          st.cx2.apply(P, kb, fb);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) sum[e] += acc[j][e] * P[e];
       }
-      cx2.load(X2T + xrow(inext));
+      st.cx2.load(X2T + xrow(ipre));
 #pragma unroll
       for (int e = 0; e < 4; ++e) part_prev[e] = row16_sum(sum[e]);
       i_prev = i;
@@ -226,11 +236,19 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
       for (int j = 0; j < NJ; ++j) {
         Frag<OpT> fb;
         yfrag(fb, ys, 16 * j + r, kb);
-        cx.apply(acc[j], kb, fb);
+        st.cx.apply(acc[j], kb, fb);
       }
-    cx.load(XT + xrow(inext));
+    st.cx.load(XT + xrow(ipre));
     __syncthreads();
+  };
+  int step = 0;
+  if constexpr (DEPTH == 2) {
+    for (; step + 1 < nsteps; step += 2) {
+      body(step, sets[0]);
+      body(step + 1, sets[DEPTH - 1]);
+    }
   }
+  for (; step < nsteps; ++step) body(step, sets[0]);
   if constexpr (CROSS) {
     if (i_prev >= 0 && r == 0) {
       f32x4 o = {part_prev[0], part_prev[1], part_prev[2], part_prev[3]};
