@@ -15,6 +15,10 @@ Draw order (one numpy PCG64 stream per config): g, q, k, v, dO, each drawn in fl
 over its full [B,H,T,d] shape; q, k, v are scaled by 1/sqrt(dk); all values are cast
 to float32 and then, for bf16 configs, rounded to bf16 (round-to-nearest-even).
 The float64 views returned here hold exactly the values the device sees.
+
+Scalar gates (one per token and head, the pages' scalar-gate ablation) come from a second
+stream seeded (seed, 1), so that adding them changes none of the draws above: logits
+g_s ~ N(gate_mean, 1) over [B,H,T], log_alpha_scalar = logsigmoid(g_s) / 16.
 """
 from __future__ import annotations
 
@@ -114,6 +118,9 @@ def generate(cfg: GlaConfig, *, with_dO: bool = True, T: int | None = None):
     items = [("log_alpha", la), ("gate_logits", g), ("q", q), ("k", k), ("v", v)]
     if with_dO:
         items.append(("dO", rng.standard_normal((B, H, T, dv))))
+    rng_s = np.random.default_rng([cfg.seed, 1])
+    gsc = rng_s.standard_normal((B, H, T)) + cfg.gate_mean
+    items += [("log_alpha_scalar", logsigmoid(gsc) / 16.0), ("gate_logits_scalar", gsc)]
     for name, arr in items:
         store, exact = _quantize(arr, cfg.dtype)
         out[name + "_store"] = store

@@ -21,12 +21,15 @@ Modules
               intermediates for per-stage checks.
   gates       the gate front-end: log_alpha = logsigmoid(x) / tau from gate logits x, and
               the chain rule back to x.
+  scalar      scalar-gate variants (one gate per token, or a constant decay per head):
+              the layer with the gate repeated over the key dimension, its gradient
+              summed back, and the parallel decay-matrix form used to pin it.
   compare     error metrics used by the parity tests.
 
 Every function is pinned by the CPU tests in tests/test_oracle_*.py against facts that do
 not come from the oracle itself (closed forms, a library routine, finite differences,
 torch autograd on an independent fp64 graph, exact rational arithmetic).
 """
-from . import recurrence, chunkwise, compare, gates  # noqa: F401
+from . import recurrence, chunkwise, compare, gates, scalar  # noqa: F401
 from .recurrence import (recurrence_fwd, recurrence_bwd, quadratic_fwd,  # noqa: F401
                          closed_form_gate_grad)
