@@ -17,7 +17,8 @@ and GLAFunction, a torch.autograd.Function over fwd/bwd.
 from __future__ import annotations
 
 from ._native import (GlaDesc, GlaError, F32, BF16, MATERIALIZED, RECOMPUTE, PASS_FWD,  # noqa: F401
-                      PASS_BWD, PASS_STATES, GATE_LOG_ALPHA, GATE_LOGITS, lib, lib_path, make_desc, status_string, trace_stages,
+                      PASS_BWD, PASS_STATES, GATE_LOG_ALPHA, GATE_LOGITS, GATE_PER_KEY, GATE_SCALAR,
+                      lib, lib_path, make_desc, status_string, trace_stages,
                       validate, version, workspace_bytes)
 from .ops import fwd, bwd, gate_cumsum, chunk_states, decode, GLAFunction, gla  # noqa: F401
 

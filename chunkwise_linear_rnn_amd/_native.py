@@ -14,6 +14,7 @@ _LIB_NAME = "libgla_mi355x.so"
 
 F32, BF16 = 0, 1
 GATE_LOG_ALPHA, GATE_LOGITS = 0, 1
+GATE_PER_KEY, GATE_SCALAR = 0, 1
 MATERIALIZED, RECOMPUTE = 0, 1
 PASS_FWD, PASS_BWD, PASS_STATES = 0, 1, 2
 
@@ -24,7 +25,7 @@ _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 class GlaDesc(ctypes.Structure):
     _fields_ = [("B", _i32), ("H", _i32), ("T", _i32), ("dk", _i32), ("dv", _i32),
                 ("chunk", _i32), ("subchunk", _i32), ("dtype", _i32), ("state_mode", _i32),
-                ("gate", _i32), ("gate_tau", ctypes.c_float)]
+                ("gate", _i32), ("gate_tau", ctypes.c_float), ("gate_shape", _i32)]
 
     def __repr__(self):
         return "GlaDesc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -88,8 +89,9 @@ def version() -> int:
 
 
 def make_desc(B, H, T, dk, dv, chunk=64, subchunk=16, dtype=BF16, state_mode=RECOMPUTE,
-              gate=GATE_LOG_ALPHA, gate_tau=1.0) -> GlaDesc:
-    return GlaDesc(B, H, T, dk, dv, chunk, subchunk, dtype, state_mode, gate, gate_tau)
+              gate=GATE_LOG_ALPHA, gate_tau=1.0, gate_shape=GATE_PER_KEY) -> GlaDesc:
+    return GlaDesc(B, H, T, dk, dv, chunk, subchunk, dtype, state_mode, gate, gate_tau,
+                   gate_shape)
 
 
 def validate(desc: GlaDesc, pass_: int = PASS_FWD) -> int:

@@ -44,7 +44,7 @@ Dims dims_of(const gla_desc_t* d) {
 // Workspace carving.  Every region is 256-byte aligned.
 struct Plan {
   size_t g = 0, A = 0, Qh = 0, QhT = 0, Kh = 0, KhT = 0, eg = 0, st = 0, dst = 0, ST = 0,
-         cT = 0, Dloc = 0, crossF = 0, crossR = 0, carry = 0, smid = 0, total = 0;
+         cT = 0, Dloc = 0, crossF = 0, crossR = 0, carry = 0, smid = 0, dpart = 0, total = 0;
 };
 
 Plan plan_of(const gla_desc_t* d, int pass) {
@@ -90,6 +90,8 @@ Plan plan_of(const gla_desc_t* d, int pass) {
     p.crossF = take(crossB);
     p.crossR = take(crossB);
     p.carry = take(egB);
+    if (d->gate_shape == GLA_GATE_SCALAR && gla::bwd_split(x.dtype, (int)x.C))
+      p.dpart = take((size_t)x.BH * x.T * (x.dk / 64) * 4);
   } else {
     p.KhT = take(opB);
     p.eg = take(egB);
@@ -103,9 +105,11 @@ bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0
 gla_status_t dev(hipError_t e) { return e == hipSuccess ? GLA_OK : GLA_ERR_DEVICE; }
 
 bool gate_ok(const gla_desc_t* d) {
+  if (d->gate_shape != GLA_GATE_PER_KEY && d->gate_shape != GLA_GATE_SCALAR) return false;
   if (d->gate == GLA_GATE_LOG_ALPHA) return true;
   return d->gate == GLA_GATE_LOGITS && d->gate_tau > 0.f && d->gate_tau <= 3.0e38f;
 }
+bool scalar_gate(const gla_desc_t* d) { return d->gate_shape == GLA_GATE_SCALAR; }
 gla::GateFn gate_of(const gla_desc_t* d) {
   gla::GateFn g;
   g.on = d->gate == GLA_GATE_LOGITS ? 1 : 0;
@@ -164,6 +168,10 @@ int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, in
     if (out && m < max) out[m] = src[j];
     ++m;
   }
+  if (pass == GLA_PASS_BWD && d->gate_shape == GLA_GATE_SCALAR) {   // the sum over d
+    if (out && m < max) out[m] = "gate_reduce";
+    ++m;
+  }
   return m;
 }
 
@@ -188,7 +196,7 @@ const char* gla_status_string(gla_status_t s) {
   return "GLA_ERR_UNKNOWN";
 }
 
-int32_t gla_version(void) { return 10000 * 0 + 100 * 1 + 0; }
+int32_t gla_version(void) { return 10000 * 0 + 100 * 2 + 0; }
 
 gla_status_t gla_validate(const gla_desc_t* d, int32_t pass) {
   if (!d) return GLA_ERR_INVALID_ARG;
@@ -227,8 +235,9 @@ gla_status_t gla_gate_cumsum(const gla_desc_t* d, const void* log_alpha, float* 
   if (x.BH * x.T == 0) return GLA_OK;
   if (!log_alpha || (!g && !gamma)) return GLA_ERR_INVALID_ARG;
   if (!aligned16(log_alpha) || !aligned16(g) || !aligned16(gamma)) return GLA_ERR_INVALID_ARG;
-  return dev(gla::launch_gate_cumsum(x.dtype, log_alpha, gate_of(d), g, gamma, (int)x.BH, (int)x.T,
-                                     (int)x.dk, (int)x.C, (hipStream_t)stream));
+  return dev(gla::launch_gate_cumsum(x.dtype, log_alpha, gate_of(d), scalar_gate(d), g, gamma,
+                                     (int)x.BH, (int)x.T, (int)x.dk, (int)x.C,
+                                     (hipStream_t)stream));
 }
 
 gla_status_t gla_chunk_states(const gla_desc_t* d, const void* k, const void* v,
@@ -249,6 +258,7 @@ gla_status_t gla_chunk_states(const gla_desc_t* d, const void* k, const void* v,
   gla::IntraArgs ia{};
   ia.dtype = x.dtype; ia.C = (int)x.C; ia.BH = (int)x.BH; ia.T = (int)x.T; ia.dk = (int)x.dk;
   ia.N = (int)x.N; ia.want_A = false; ia.q = k; ia.k = k; ia.la = log_alpha; ia.g = nullptr; ia.gate = gate_of(d);
+  ia.gscalar = scalar_gate(d);
   ia.KhT = w + p.KhT; ia.eg = (float*)(w + p.eg);
   gla_status_t rs = dev(gla::launch_intra(ia, s));
   if (rs != GLA_OK) return rs;
@@ -283,13 +293,15 @@ gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void
   gla_status_t rs = GLA_OK;
   if (mat) {
     if ((rs = tr.mark()) != GLA_OK) return rs;
-    rs = dev(gla::launch_gate_cumsum(x.dtype, log_alpha, gate_of(d), (float*)(w + p.g), nullptr, (int)x.BH,
-                                     (int)x.T, (int)x.dk, (int)x.C, s));
+    rs = dev(gla::launch_gate_cumsum(x.dtype, log_alpha, gate_of(d), scalar_gate(d),
+                                     (float*)(w + p.g), nullptr, (int)x.BH, (int)x.T, (int)x.dk,
+                                     (int)x.C, s));
     if (rs != GLA_OK) return rs;
   }
   gla::IntraArgs ia{};
   ia.dtype = x.dtype; ia.C = (int)x.C; ia.BH = (int)x.BH; ia.T = (int)x.T; ia.dk = (int)x.dk;
   ia.N = (int)x.N; ia.want_A = true; ia.q = q; ia.k = k; ia.la = log_alpha; ia.gate = gate_of(d);
+  ia.gscalar = scalar_gate(d);
   ia.g = mat ? (const float*)(w + p.g) : nullptr;
   ia.A = w + p.A; ia.Qh = w + p.Qh; ia.KhT = w + p.KhT; ia.eg = (float*)(w + p.eg);
   if ((rs = tr.mark()) != GLA_OK) return rs;
@@ -369,7 +381,7 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   ia.dtype = x.dtype; ia.C = C; ia.BH = BH; ia.T = T; ia.dk = DK; ia.N = N; ia.want_A = true;
   ia.xt_f32 = x.dtype == GLA_BF16;
   ia.q = q; ia.k = k; ia.la = log_alpha; ia.g = nullptr; ia.g2_out = (float*)(w + p.g);
-  ia.gate = gate_of(d);
+  ia.gate = gate_of(d); ia.gscalar = scalar_gate(d);
   ia.A = w + p.A; ia.QhT = w + p.QhT; ia.Kh = w + p.Kh; ia.KhT = w + p.KhT;
   ia.eg = (float*)(w + p.eg);
   if ((rs = tr.mark()) != GLA_OK) return rs;
@@ -404,6 +416,17 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   ba.Dloc = p.Dloc ? (float*)(w + p.Dloc) : nullptr;
   ba.tot = (const float*)(w + p.carry); ba.cT = dS_T ? (const float*)(w + p.cT) : nullptr;
   ba.dla = dlog_alpha; ba.la = log_alpha; ba.gate = gate_of(d);
+  // scalar gates: the per-key gradient is summed over the key dimension afterwards, and
+  // the front-end slope (one per token) applied there
+  const bool sg = scalar_gate(d);
+  if (sg) {
+    ba.gate = gla::GateFn{0, 1.f};
+    ba.dla_part = p.dpart ? (float*)(w + p.dpart) : nullptr;
+  }
+  auto reduce = [&](const float* part, int nparts) {
+    return dev(gla::launch_gate_reduce(x.dtype, part, nparts, log_alpha, gate_of(d), dlog_alpha,
+                                       (long)BH * T, s));
+  };
   // chunk totals of D from the scans' cross terms
   auto totals = [&]() {
     return dev(gla::launch_gate_tot((const float*)(w + p.crossF), (const float*)(w + p.crossR),
@@ -419,6 +442,10 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
     if ((rs = dev(gla::launch_bwd_chunk(ba, s))) != GLA_OK) return rs;
     if ((rs = tr.mark()) != GLA_OK) return rs;
     if ((rs = dev(gla::launch_bwd_dv(ba, s))) != GLA_OK) return rs;
+    if (sg) {
+      if ((rs = tr.mark()) != GLA_OK) return rs;
+      if ((rs = reduce((const float*)(w + p.dpart), DK / 64)) != GLA_OK) return rs;
+    }
     return tr.mark();
   }
   if ((rs = tr.mark()) != GLA_OK) return rs;
@@ -426,10 +453,16 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   if ((rs = tr.mark()) != GLA_OK) return rs;
   if ((rs = totals()) != GLA_OK) return rs;
   if ((rs = tr.mark()) != GLA_OK) return rs;
+  // scalar gates: the per-key gradient overwrites D in place, then the sum over d
   rs = dev(gla::launch_gate_grad(x.dtype, (const float*)(w + p.Dloc), (const float*)(w + p.carry),
                                  dS_T ? (const float*)(w + p.cT) : nullptr, log_alpha, gate_of(d),
-                                 dlog_alpha, BH, T, DK, C, s));
+                                 dlog_alpha, sg ? (float*)(w + p.Dloc) : nullptr, BH, T, DK, C,
+                                 s));
   if (rs != GLA_OK) return rs;
+  if (sg) {
+    if ((rs = tr.mark()) != GLA_OK) return rs;
+    if ((rs = reduce((const float*)(w + p.Dloc), DK)) != GLA_OK) return rs;
+  }
   return tr.mark();
 }
 
@@ -459,6 +492,7 @@ gla_status_t gla_decode(const gla_desc_t* d, const void* q, const void* k, const
   gla::DecodeArgs a{};
   a.dtype = d->dtype; a.BH = (int)bh; a.T = d->T; a.dk = d->dk; a.dv = d->dv;
   a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.S = S; a.o = o; a.gate = gate_of(d);
+  a.gscalar = scalar_gate(d) ? 1 : 0;
   return dev(gla::launch_decode(a, (hipStream_t)stream));
 }
 

@@ -39,19 +39,26 @@ struct IntraArgs {
   float* eg;             // [BH][N][dk]
   float* g2_out;         // [BH][T][dk] g * log2(e), or NULL
   GateFn gate;           // applied to la (not to g, which is already a cumsum)
+  bool gscalar;          // la holds one gate per token: [BH][T], broadcast over dk
 };
 hipError_t launch_intra(const IntraArgs& a, hipStream_t s);
 
-hipError_t launch_gate_cumsum(int dtype, const void* la, GateFn gate, float* g, float* gamma,
-                              int BH, int T, int dk, int C, hipStream_t s);
+hipError_t launch_gate_cumsum(int dtype, const void* la, GateFn gate, int gscalar, float* g,
+                              float* gamma, int BH, int T, int dk, int C, hipStream_t s);
 hipError_t launch_state_dot(const float* dST, const float* ST, float* cT, int BH, int dk, int dv,
                             hipStream_t s);
 // chunk totals of D from the scans' cross terms -> tot [BH][N][dk]
 hipError_t launch_gate_tot(const float* crossF, const float* crossR, const float* cT,
                              float* tot, int BH, int T, int dk, int ntile, int C, hipStream_t s);
+// part != NULL (scalar gates): the per-(t, d) gradient goes to part [BH][T][dk] in fp32,
+// without the front-end slope (it may alias Dloc), and dla is not written.
 hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* tot, const float* cT,
-                            const void* la, GateFn gate, void* dla, int BH, int T, int dk,
-                            int C, hipStream_t s);
+                            const void* la, GateFn gate, void* dla, float* part, int BH,
+                            int T, int dk, int C, hipStream_t s);
+// Scalar gates: dla[row] = slope(la[row]) * sum of part[row][0 .. nparts) for the rows
+// row < nrows = BH * T (dla and la [BH][T] in the input type).
+hipError_t launch_gate_reduce(int dtype, const float* part, int nparts, const void* la,
+                              GateFn gate, void* dla, long nrows, hipStream_t s);
 
 // Inter-chunk state scan.  store: 0 = none, 1 = operand type [dk][dv], 2 = operand type
 // [dv][dk], 3 = fp32 [dk][dv].  With X2T/Y2/cross set, every step also forms the
@@ -124,6 +131,8 @@ struct BwdArgs {
   void* dla;               // dlog_alpha, written directly (split path)
   const void* la;          // the gate operand, for the gate front-end's chain rule
   GateFn gate;
+  float* dla_part;         // scalar gates (split path): fp32 sums of the per-(t, d) gradient
+                           // over each 64-wide d block, [BH][T][dk/64], instead of dla
 };
 // The backward chunk work: with bf16 operands and chunk 64 it is two kernels (dq, dk and
 // dlog_alpha, after the chunk totals are formed; then dv: launch_bwd_chunk and
@@ -139,6 +148,7 @@ struct DecodeArgs {
   float* S;   // [BH][dk][dv]
   void* o;    // [BH][T][dv]
   GateFn gate;
+  int gscalar;   // la is [BH][T] (one gate per token), else [BH][T][dk]
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 

@@ -228,7 +228,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk(
     const Tin* __restrict__ dO, const float* __restrict__ g, const OpT* __restrict__ S,
     const OpT* __restrict__ dS, Tin* __restrict__ dq, Tin* __restrict__ dk_out,
     const float* __restrict__ tot, const float* __restrict__ cT, const Tin* __restrict__ la,
-    GateFn gf, Tin* __restrict__ dla, int T, int dk, int dv, int N) {
+    GateFn gf, Tin* __restrict__ dla, float* __restrict__ dla_part, int T, int dk, int dv,
+    int N) {
   static_assert(sizeof(Tin) == sizeof(OpT), "input and operand types match");
   constexpr int C = 64, NM = 4, NS = C / 16, YLD = 64 + 8;
   constexpr int FLD = C + 4, GLD = 64 + 4, XLD = 64 + 8;
@@ -480,6 +481,9 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk(
     ptot[m] = Dv[m][0];
   }
   float later = carry;   // carry plus the sum over sub-chunks after m, all lane groups
+  // scalar gates: the row sums over this block's 64 columns, per wave (its 16 columns),
+  // in the region of the third staging tile
+  float* wsum = (float*)(st + 2 * C * SLD);   // [4 waves][C]
 #pragma unroll
   for (int m = NM - 1; m >= 0; --m) {
     float after = later, all = 0.f;
@@ -492,22 +496,33 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 16 * m + 4 * qd + e;
-      // gates given as logits: chain rule to the logit (rows past T hold no logit)
-      const float sl = gf.on && t < rows ? gf.slope(to_f32(la[(tok0 + t) * dk + d0 + c])) : 1.f;
-      st[2 * C * SLD + t * SLD + c] = from_f32<Tin>((Dv[m][e] + after) * sl);
+      if (dla_part) {
+        const float rs = row16_sum(Dv[m][e] + after);
+        if (r == 0) wsum[w * C + t] = rs;
+      } else {
+        // gates given as logits: chain rule to the logit (rows past T hold no logit)
+        const float sl = gf.on && t < rows ? gf.slope(to_f32(la[(tok0 + t) * dk + d0 + c])) : 1.f;
+        st[2 * C * SLD + t * SLD + c] = from_f32<Tin>((Dv[m][e] + after) * sl);
+      }
     }
     later += all;
   }
   __syncthreads();
   constexpr int kPer = 16 / (int)sizeof(Tin), kRowUnits = 64 / kPer, kUnits = 3 * C * kRowUnits;
   static_assert(3 * C * SLD * (int)sizeof(Tin) <= o_q, "staging stays clear of q / k");
+  static_assert(4 * C * 4 <= C * SLD * (int)sizeof(Tin), "row sums fit the third tile");
+  const int ntile_out = dla_part ? 2 : 3;
   for (int idx = threadIdx.x; idx < kUnits; idx += kThreads) {
     const int tile = idx / (C * kRowUnits), u = idx % (C * kRowUnits);
     const int rr = u / kRowUnits, cc = (u % kRowUnits) * kPer;
     Tin* dst = tile == 0 ? dq : (tile == 1 ? dk_out : dla);
-    if (rr < rows)
+    if (tile < ntile_out && rr < rows)
       *reinterpret_cast<u32x4*>(dst + (tok0 + rr) * dk + d0 + cc) =
           *reinterpret_cast<const u32x4*>(st + (tile * C + rr) * SLD + cc);
+  }
+  if (dla_part && threadIdx.x < rows) {
+    const int t = threadIdx.x;
+    dla_part[(tok0 + t) * NJ + jb] = (wsum[t] + wsum[C + t]) + (wsum[2 * C + t] + wsum[3 * C + t]);
   }
 }
 
@@ -769,7 +784,7 @@ static hipError_t launch_bwd_t2(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((k_bwd_dqk<Tin, OpT>), dim3((a.dk / 64) * a.N * a.BH), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,
                        (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq, (Tin*)a.dk_out, a.tot, a.cT,
-                       (const Tin*)a.la, a.gate, (Tin*)a.dla, a.T, a.dk, a.dv, a.N);
+                       (const Tin*)a.la, a.gate, (Tin*)a.dla, a.dla_part, a.T, a.dk, a.dv, a.N);
   } else {
     hipLaunchKernelGGL((k_bwd_chunk<Tin, OpT, C, DK>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,

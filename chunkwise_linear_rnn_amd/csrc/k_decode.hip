@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(const Tin* __restrict__ q,
                                                      const Tin* __restrict__ v,
                                                      const Tin* __restrict__ la,
                                                      float* __restrict__ S, Tin* __restrict__ o,
-                                                     GateFn gf, int T, int dv) {
+                                                     GateFn gf, int gscalar, int T, int dv) {
   constexpr int DK = 32 * NR, TV = 32;
   __shared__ float red[2][32][TV + 1];
   const int nvt = dv / TV;
@@ -51,11 +51,13 @@ __global__ __launch_bounds__(kThreads) void k_decode(const Tin* __restrict__ q,
   for (int t = 0; t < T; ++t) {
     const long tk = ((long)bh * T + t) * DK;
     const f32x4 vv = load4<Tin>(v + ((long)bh * T + t) * dv + c0);
+    // scalar gates: one decay for every row of the state
+    const float as = gscalar ? __builtin_amdgcn_exp2f(gf(to_f32(la[(long)bh * T + t])) * kLog2e) : 0.f;
     f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
       const int row = rg + 32 * j;
-      const float a = __builtin_amdgcn_exp2f(gf(to_f32(la[tk + row])) * kLog2e);
+      const float a = gscalar ? as : __builtin_amdgcn_exp2f(gf(to_f32(la[tk + row])) * kLog2e);
       const float kk = to_f32(k[tk + row]), qq = to_f32(q[tk + row]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -82,14 +84,14 @@ template <typename Tin>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((long)a.BH * (a.dv / 32)));
   switch (a.dk / 32) {
-    case 1: hipLaunchKernelGGL((k_decode<Tin, 1>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.T, a.dv); break;
-    case 2: hipLaunchKernelGGL((k_decode<Tin, 2>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.T, a.dv); break;
-    case 3: hipLaunchKernelGGL((k_decode<Tin, 3>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.T, a.dv); break;
-    case 4: hipLaunchKernelGGL((k_decode<Tin, 4>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.T, a.dv); break;
-    case 5: hipLaunchKernelGGL((k_decode<Tin, 5>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.T, a.dv); break;
-    case 6: hipLaunchKernelGGL((k_decode<Tin, 6>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.T, a.dv); break;
-    case 7: hipLaunchKernelGGL((k_decode<Tin, 7>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.T, a.dv); break;
-    case 8: hipLaunchKernelGGL((k_decode<Tin, 8>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.T, a.dv); break;
+    case 1: hipLaunchKernelGGL((k_decode<Tin, 1>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.gscalar, a.T, a.dv); break;
+    case 2: hipLaunchKernelGGL((k_decode<Tin, 2>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.gscalar, a.T, a.dv); break;
+    case 3: hipLaunchKernelGGL((k_decode<Tin, 3>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.gscalar, a.T, a.dv); break;
+    case 4: hipLaunchKernelGGL((k_decode<Tin, 4>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.gscalar, a.T, a.dv); break;
+    case 5: hipLaunchKernelGGL((k_decode<Tin, 5>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.gscalar, a.T, a.dv); break;
+    case 6: hipLaunchKernelGGL((k_decode<Tin, 6>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.gscalar, a.T, a.dv); break;
+    case 7: hipLaunchKernelGGL((k_decode<Tin, 7>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.gscalar, a.T, a.dv); break;
+    case 8: hipLaunchKernelGGL((k_decode<Tin, 8>), grid, dim3(kThreads), 0, s, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.la, a.S, (Tin*)a.o, a.gate, a.gscalar, a.T, a.dv); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

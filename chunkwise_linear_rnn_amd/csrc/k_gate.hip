@@ -16,20 +16,23 @@ namespace gla {
 
 template <typename Tin>
 __global__ __launch_bounds__(kThreads) void k_gate_cumsum(const Tin* __restrict__ la,
-                                                          GateFn gf, float* __restrict__ g,
+                                                          GateFn gf, int gscalar,
+                                                          float* __restrict__ g,
                                                           float* __restrict__ gamma, int T,
                                                           int dk, int C, int N) {
   constexpr int U = 16;   // rows loaded per batch, so the loads are in flight together
   const int i = blockIdx.x, bh = blockIdx.y;
   const int t0 = i * C, t1 = min(T, t0 + C);
   const long base = (long)bh * T * dk;
+  // element (t, d) of the gate: [T][dk], or [T] shared by every d (scalar gates)
+  const long ls_t = gscalar ? 1 : dk, ls_d = gscalar ? 0 : 1, lbase = gscalar ? (long)bh * T : base;
   for (int d = threadIdx.x; d < dk; d += kThreads) {
     float acc = 0.f;
     for (int tb = t0; tb < t1; tb += U) {
       float x[U];
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        x[u] = tb + u < t1 ? gf(to_f32(la[base + (long)(tb + u) * dk + d])) : 0.f;
+        x[u] = tb + u < t1 ? gf(to_f32(la[lbase + (long)(tb + u) * ls_t + d * ls_d])) : 0.f;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         acc += x[u];
@@ -74,12 +77,13 @@ __global__ __launch_bounds__(kThreads) void k_gate_tot(const float* __restrict__
 // dlog_alpha[t] = (chunk-local suffix sum of D at t) + c_T + sum of chunk totals of the
 // later chunks (times the gate front-end's slope when the gates come as logits).
 template <typename Tin>
-__global__ __launch_bounds__(kThreads) void k_gate_grad(const float* __restrict__ Dloc,
+__global__ __launch_bounds__(kThreads) void k_gate_grad(const float* Dloc,   // may alias part
                                                         const float* __restrict__ tot,
                                                         const float* __restrict__ cT,
                                                         const Tin* __restrict__ la, GateFn gf,
-                                                        Tin* __restrict__ dla, int T, int dk,
-                                                        int C, int N) {
+                                                        Tin* __restrict__ dla,
+                                                        float* part, int T,
+                                                        int dk, int C, int N) {
   constexpr int U = 16;
   const int i = blockIdx.x, bh = blockIdx.y;
   const int t0 = i * C, t1 = min(T, t0 + C);
@@ -95,27 +99,69 @@ __global__ __launch_bounds__(kThreads) void k_gate_grad(const float* __restrict_
       for (int u = 0; u < U; ++u)
         if (tb + u < t1) {
           const long at = base + (long)(tb + u) * dk + d;
-          const float sl = gf.on ? gf.slope(to_f32(la[at])) : 1.f;
-          dla[at] = from_f32<Tin>((x[u] + cr) * sl);
+          if (part) {   // scalar gates: reduced over d afterwards (x[u] was read first)
+            part[at] = x[u] + cr;
+          } else {
+            const float sl = gf.on ? gf.slope(to_f32(la[at])) : 1.f;
+            dla[at] = from_f32<Tin>((x[u] + cr) * sl);
+          }
         }
     }
   }
 }
 
+// Scalar gates (one per token): the gradient of log_alpha_t is the sum over the key
+// dimension of the per-key gradient, times the front-end slope of its logit.  One thread
+// per row; nparts partial sums per row (64-wide d blocks, or every d).
+template <typename Tin>
+__global__ __launch_bounds__(kThreads) void k_gate_reduce(const float* __restrict__ part,
+                                                          int nparts,
+                                                          const Tin* __restrict__ la,
+                                                          GateFn gf, Tin* __restrict__ dla,
+                                                          long nrows) {
+  const long row = (long)blockIdx.x * kThreads + threadIdx.x;
+  if (row >= nrows) return;
+  const float* p = part + row * nparts;
+  float s = 0.f;
+  if (nparts % 4 == 0) {
+    for (int j = 0; j < nparts; j += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(p + j);
+      s += (x[0] + x[1]) + (x[2] + x[3]);
+    }
+  } else {
+    for (int j = 0; j < nparts; ++j) s += p[j];
+  }
+  if (gf.on) s *= gf.slope(to_f32(la[row]));
+  dla[row] = from_f32<Tin>(s);
+}
+
 // ---------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------
-hipError_t launch_gate_cumsum(int dtype, const void* la, GateFn gate, float* g, float* gamma,
-                              int BH, int T, int dk, int C, hipStream_t s) {
+hipError_t launch_gate_cumsum(int dtype, const void* la, GateFn gate, int gscalar, float* g,
+                              float* gamma, int BH, int T, int dk, int C, hipStream_t s) {
   const int N = (T + C - 1) / C;
   if (BH == 0 || N == 0) return hipSuccess;
   dim3 grid(N, BH);
   if (dtype == 0)
     hipLaunchKernelGGL(k_gate_cumsum<float>, grid, dim3(kThreads), 0, s, (const float*)la, gate,
-                       g, gamma, T, dk, C, N);
+                       gscalar, g, gamma, T, dk, C, N);
   else
     hipLaunchKernelGGL(k_gate_cumsum<bf16>, grid, dim3(kThreads), 0, s, (const bf16*)la, gate,
-                       g, gamma, T, dk, C, N);
+                       gscalar, g, gamma, T, dk, C, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_reduce(int dtype, const float* part, int nparts, const void* la,
+                              GateFn gate, void* dla, long nrows, hipStream_t s) {
+  if (nrows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((nrows + kThreads - 1) / kThreads));
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_gate_reduce<float>, grid, dim3(kThreads), 0, s, part, nparts,
+                       (const float*)la, gate, (float*)dla, nrows);
+  else
+    hipLaunchKernelGGL(k_gate_reduce<bf16>, grid, dim3(kThreads), 0, s, part, nparts,
+                       (const bf16*)la, gate, (bf16*)dla, nrows);
   return hipGetLastError();
 }
 
@@ -137,17 +183,17 @@ hipError_t launch_gate_tot(const float* crossF, const float* crossR, const float
 }
 
 hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* tot, const float* cT,
-                            const void* la, GateFn gate, void* dla, int BH, int T, int dk,
-                            int C, hipStream_t s) {
+                            const void* la, GateFn gate, void* dla, float* part, int BH,
+                            int T, int dk, int C, hipStream_t s) {
   const int N = (T + C - 1) / C;
   if (BH == 0 || N == 0) return hipSuccess;
   dim3 grid(N, BH);
   if (dtype == 0)
     hipLaunchKernelGGL(k_gate_grad<float>, grid, dim3(kThreads), 0, s, Dloc, tot, cT,
-                       (const float*)la, gate, (float*)dla, T, dk, C, N);
+                       (const float*)la, gate, (float*)dla, part, T, dk, C, N);
   else
     hipLaunchKernelGGL(k_gate_grad<bf16>, grid, dim3(kThreads), 0, s, Dloc, tot, cT,
-                       (const bf16*)la, gate, (bf16*)dla, T, dk, C, N);
+                       (const bf16*)la, gate, (bf16*)dla, part, T, dk, C, N);
   return hipGetLastError();
 }
 

@@ -66,6 +66,23 @@ struct GBlock {
       u[j] = *reinterpret_cast<const u32x4*>(src + (long)min(rr, rows - 1) * ld + c);
     }
   }
+  // one gate per row, src[row] (rows past `rows` zero), the same for every column
+  __device__ __forceinline__ void load_scalar(const SrcT* __restrict__ src, int rows) {
+    zero_from = rows;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int idx = threadIdx.x + j * kThreads, rr = idx / kUnitsRow;
+      const SrcT x = src[min(rr, rows - 1)];
+      uint32_t wd;
+      if constexpr (sizeof(SrcT) == 2) {
+        const uint32_t b = __builtin_bit_cast(uint16_t, x);
+        wd = b | (b << 16);
+      } else {
+        wd = __builtin_bit_cast(uint32_t, x);
+      }
+      u[j] = u32x4{wd, wd, wd, wd};
+    }
+  }
   __device__ __forceinline__ void store(float* gs, int gld, GateFn gf) const {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
@@ -91,7 +108,7 @@ struct GBlock {
   }
 };
 
-template <typename Tin, typename OpT, typename XT, int C, bool G_WS, bool WANT_A>
+template <typename Tin, typename OpT, typename XT, int C, bool G_WS, bool WANT_A, bool SG>
 __global__ __launch_bounds__(kThreads) void k_intra(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ la,
     const float* __restrict__ gws, OpT* __restrict__ A_out, OpT* __restrict__ Qh_out,
@@ -133,6 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(
   auto fetch = [&](int d0) {
     // g from the gate kernel: rows past T continue the last valid row; log_alpha: zero
     if constexpr (G_WS) pg.load(gws + in_base + d0, dk, rows, true);
+    else if constexpr (SG) pg.load_scalar(la + (long)bh * T + t0, rows);   // one gate per token
     else pg.load(la + in_base + d0, dk, rows, false);
     tq.load(q + in_base + d0, dk, rows);
     tk.load(k + in_base + d0, dk, rows);
@@ -340,9 +358,9 @@ __global__ __launch_bounds__(kThreads) void k_intra(
 }
 
 // ---------------------------------------------------------------------------------
-template <typename Tin, typename OpT, typename XT, int C, bool GW, bool WA>
+template <typename Tin, typename OpT, typename XT, int C, bool GW, bool WA, bool SG = false>
 static void launch_intra_k(const IntraArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_intra<Tin, OpT, XT, C, GW, WA>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((k_intra<Tin, OpT, XT, C, GW, WA, SG>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
                      (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.la, a.g, (OpT*)a.A,
                      (OpT*)a.Qh, (XT*)a.QhT, (OpT*)a.Kh, (XT*)a.KhT, a.eg, a.g2_out, a.gate, a.T,
                      a.dk, a.N);
@@ -351,9 +369,11 @@ template <typename Tin, typename OpT, typename XT, int C>
 static hipError_t launch_intra_t(const IntraArgs& a, hipStream_t s) {
   if (a.want_A) {
     if (a.g) launch_intra_k<Tin, OpT, XT, C, true, true>(a, s);
+    else if (a.gscalar) launch_intra_k<Tin, OpT, XT, C, false, true, true>(a, s);
     else launch_intra_k<Tin, OpT, XT, C, false, true>(a, s);
   } else {
     if (a.g) launch_intra_k<Tin, OpT, XT, C, true, false>(a, s);
+    else if (a.gscalar) launch_intra_k<Tin, OpT, XT, C, false, false, true>(a, s);
     else launch_intra_k<Tin, OpT, XT, C, false, false>(a, s);
   }
   return hipGetLastError();

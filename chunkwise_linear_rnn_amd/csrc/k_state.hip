@@ -48,19 +48,6 @@ struct XRegs {
   }
 };
 
-// Sum over the 16 lanes of a DPP row (lanes with the same l / 16), result in every lane.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_f<0xB1>(x);    // quad_perm [1,0,3,2]
-  x += dpp_f<0x4E>(x);    // quad_perm [2,3,0,1]
-  x += dpp_f<0x124>(x);   // row_ror 4
-  x += dpp_f<0x128>(x);   // row_ror 8
-  return x;
-}
-
 template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS, int TV>
 __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, ScanDir d1, int ndir,
                                                             const float* __restrict__ eg, int T,

@@ -7,9 +7,9 @@ import ctypes
 
 import torch
 
-from ._native import (BF16, F32, GATE_LOG_ALPHA, GATE_LOGITS, MATERIALIZED, RECOMPUTE,
-                      PASS_BWD, PASS_FWD, PASS_STATES, GlaError, lib, make_desc,
-                      workspace_bytes)
+from ._native import (BF16, F32, GATE_LOG_ALPHA, GATE_LOGITS, GATE_PER_KEY, GATE_SCALAR,
+                      MATERIALIZED, RECOMPUTE, PASS_BWD, PASS_FWD, PASS_STATES, GlaError, lib,
+                      make_desc, workspace_bytes)
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 _MODES = {"materialized": MATERIALIZED, "recompute": RECOMPUTE}
@@ -36,9 +36,10 @@ def _check(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _desc_from(q, v, chunk, subchunk, state_mode, gate_tau=None):
+def _desc_from(q, v, chunk, subchunk, state_mode, gate_tau=None, scalar=False):
     """gate_tau: None when the log_alpha argument is log_alpha itself, else the temperature
-    of gate logits (log_alpha = logsigmoid(x) / gate_tau)."""
+    of gate logits (log_alpha = logsigmoid(x) / gate_tau).  scalar: one gate per token
+    ([B, H, T]) instead of one per key dimension."""
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q and v must be [B, H, T, d]")
     if q.dtype not in _DT:
@@ -46,10 +47,21 @@ def _desc_from(q, v, chunk, subchunk, state_mode, gate_tau=None):
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     mode = _MODES[state_mode] if isinstance(state_mode, str) else int(state_mode)
+    shape = GATE_SCALAR if scalar else GATE_PER_KEY
     if gate_tau is None:
-        return make_desc(B, H, T, dk, dv, chunk, subchunk, _DT[q.dtype], mode)
+        return make_desc(B, H, T, dk, dv, chunk, subchunk, _DT[q.dtype], mode,
+                         gate_shape=shape)
     return make_desc(B, H, T, dk, dv, chunk, subchunk, _DT[q.dtype], mode, GATE_LOGITS,
-                     float(gate_tau))
+                     float(gate_tau), shape)
+
+
+def _is_scalar(log_alpha):
+    """A [B, H, T] gate (one per token) rather than [B, H, T, dk]."""
+    return isinstance(log_alpha, torch.Tensor) and log_alpha.dim() == 3
+
+
+def _gate_shape(log_alpha, B, H, T, dk):
+    return (B, H, T) if _is_scalar(log_alpha) else (B, H, T, dk)
 
 
 def _workspace(desc, pass_, device, workspace):
@@ -70,12 +82,14 @@ def fwd(q, k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, state_mode="recom
         final_state=True, workspace=None, gate_tau=None):
     """o, S_T = the GLA layer forward (S_T is None when final_state is False).
     gate_tau: when set, log_alpha holds gate logits x and the layer uses
-    logsigmoid(x) / gate_tau."""
-    desc = _desc_from(q, v, chunk, subchunk, state_mode, gate_tau)
+    logsigmoid(x) / gate_tau.  log_alpha [B, H, T] (instead of [B, H, T, dk]) is a scalar
+    gate per token, shared by every key dimension."""
+    desc = _desc_from(q, v, chunk, subchunk, state_mode, gate_tau, _is_scalar(log_alpha))
     dev, dt = q.device, q.dtype
     B, H, T, dk, dv = desc.B, desc.H, desc.T, desc.dk, desc.dv
     for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)),
-                      (v, "v", (B, H, T, dv)), (log_alpha, "log_alpha", (B, H, T, dk))):
+                      (v, "v", (B, H, T, dv)),
+                      (log_alpha, "log_alpha", _gate_shape(log_alpha, B, H, T, dk))):
         _check(t, n, shp, dt, dev)
     if S0 is not None:
         _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
@@ -91,12 +105,14 @@ def fwd(q, k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, state_mode="recom
 def bwd(q, k, v, log_alpha, dO, S0=None, dS_T=None, *, chunk=64, subchunk=16,
         want_dS0=True, workspace=None, gate_tau=None):
     """dq, dk, dv, dlog_alpha, dS0 for the loss gradient (dO, dS_T).  With gate_tau set
-    (gate logits in log_alpha) the fourth output is the gradient with respect to them."""
-    desc = _desc_from(q, v, chunk, subchunk, RECOMPUTE, gate_tau)
+    (gate logits in log_alpha) the fourth output is the gradient with respect to them.
+    A scalar gate (log_alpha [B, H, T]) gets its gradient summed over the key dimension."""
+    desc = _desc_from(q, v, chunk, subchunk, RECOMPUTE, gate_tau, _is_scalar(log_alpha))
     dev, dt = q.device, q.dtype
     B, H, T, dk, dv = desc.B, desc.H, desc.T, desc.dk, desc.dv
     for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)),
-                      (v, "v", (B, H, T, dv)), (log_alpha, "log_alpha", (B, H, T, dk)),
+                      (v, "v", (B, H, T, dv)),
+                      (log_alpha, "log_alpha", _gate_shape(log_alpha, B, H, T, dk)),
                       (dO, "dO", (B, H, T, dv))):
         _check(t, n, shp, dt, dev)
     for t, n in ((S0, "S0"), (dS_T, "dS_T")):
@@ -115,17 +131,26 @@ def bwd(q, k, v, log_alpha, dO, S0=None, dS_T=None, *, chunk=64, subchunk=16,
     return dq, dk_, dv_, dla, dS0
 
 
-def gate_cumsum(log_alpha, chunk=64, gate_tau=None):
-    """g (chunk-local inclusive cumsum, fp32) and gamma (chunk totals, fp32)."""
-    if log_alpha.dim() != 4 or log_alpha.dtype not in _DT:
-        raise ValueError("log_alpha must be [B,H,T,dk] float32/bfloat16")
-    B, H, T, dk = log_alpha.shape
+def gate_cumsum(log_alpha, chunk=64, gate_tau=None, dk=None):
+    """g (chunk-local inclusive cumsum, fp32) and gamma (chunk totals, fp32).  A scalar
+    gate (log_alpha [B, H, T]) needs dk: g and gamma are broadcast over it."""
+    if log_alpha.dim() not in (3, 4) or log_alpha.dtype not in _DT:
+        raise ValueError("log_alpha must be [B,H,T,dk] or [B,H,T] float32/bfloat16")
+    scalar = log_alpha.dim() == 3
+    if scalar:
+        if dk is None:
+            raise ValueError("a scalar gate needs dk")
+        B, H, T = log_alpha.shape
+    else:
+        B, H, T, dk = log_alpha.shape
+    shape = GATE_SCALAR if scalar else GATE_PER_KEY
     if gate_tau is None:
-        desc = make_desc(B, H, T, dk, 64, chunk, 16, _DT[log_alpha.dtype], RECOMPUTE)
+        desc = make_desc(B, H, T, dk, 64, chunk, 16, _DT[log_alpha.dtype], RECOMPUTE,
+                         gate_shape=shape)
     else:
         desc = make_desc(B, H, T, dk, 64, chunk, 16, _DT[log_alpha.dtype], RECOMPUTE,
-                         GATE_LOGITS, float(gate_tau))
-    _check(log_alpha, "log_alpha", (B, H, T, dk), log_alpha.dtype, log_alpha.device)
+                         GATE_LOGITS, float(gate_tau), shape)
+    _check(log_alpha, "log_alpha", tuple(log_alpha.shape), log_alpha.dtype, log_alpha.device)
     N = (T + chunk - 1) // chunk
     g = torch.empty((B, H, T, dk), dtype=torch.float32, device=log_alpha.device)
     gamma = torch.empty((B, H, N, dk), dtype=torch.float32, device=log_alpha.device)
@@ -137,11 +162,11 @@ def gate_cumsum(log_alpha, chunk=64, gate_tau=None):
 def chunk_states(k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, workspace=None,
                  gate_tau=None):
     """states [B,H,N,dk,dv] (state before every chunk, fp32) and S_T."""
-    desc = _desc_from(k, v, chunk, subchunk, MATERIALIZED, gate_tau)
+    desc = _desc_from(k, v, chunk, subchunk, MATERIALIZED, gate_tau, _is_scalar(log_alpha))
     dev, dt = k.device, k.dtype
     B, H, T, dk, dv = desc.B, desc.H, desc.T, desc.dk, desc.dv
     for t, n, shp in ((k, "k", (B, H, T, dk)), (v, "v", (B, H, T, dv)),
-                      (log_alpha, "log_alpha", (B, H, T, dk))):
+                      (log_alpha, "log_alpha", _gate_shape(log_alpha, B, H, T, dk))):
         _check(t, n, shp, dt, dev)
     if S0 is not None:
         _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
@@ -191,10 +216,11 @@ def decode(q, k, v, log_alpha, S, *, gate_tau=None):
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
     for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)),
-                      (v, "v", (B, H, T, dv)), (log_alpha, "log_alpha", (B, H, T, dk))):
+                      (v, "v", (B, H, T, dv)),
+                      (log_alpha, "log_alpha", _gate_shape(log_alpha, B, H, T, dk))):
         _check(t, n, shp, dt, dev)
     _check(S, "S", (B, H, dk, dv), torch.float32, dev)
-    desc = _desc_from(q, v, 64, 16, RECOMPUTE, gate_tau)
+    desc = _desc_from(q, v, 64, 16, RECOMPUTE, gate_tau, _is_scalar(log_alpha))
     o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
     _call("gla_decode", lib().gla_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                          _ptr(log_alpha), _ptr(S), _ptr(o), _stream(dev)))

@@ -17,7 +17,9 @@
  *
  * Conventions shared by every entry point
  *  - Tensors are dense, row-major, contiguous device buffers:
- *      q, k, log_alpha, dq, dk, dlog_alpha  [B, H, T, dk]
+ *      q, k, dq, dk                          [B, H, T, dk]
+ *      log_alpha, dlog_alpha                 [B, H, T, dk], or [B, H, T] with
+ *                                            gate_shape GLA_GATE_SCALAR
  *      v, o, dO, dv                          [B, H, T, dv]
  *      S0, S_T, dS_T, dS0                    [B, H, dk, dv]   always float32
  *    The element type of the [B,H,T,*] tensors is desc->dtype (GLA_F32 or GLA_BF16).
@@ -78,6 +80,18 @@ typedef enum { GLA_PASS_FWD = 0, GLA_PASS_BWD = 1 } gla_pass_t;
  *    dL/dlog_alpha * sigmoid(-x) / gate_tau. */
 typedef enum { GLA_GATE_LOG_ALPHA = 0, GLA_GATE_LOGITS = 1 } gla_gate_t;
 
+/* Shape of the gate (Experiments section of the same summary: its ablations compare the
+ * fine-grained gate with a data-dependent scalar gate and with a data-independent scalar
+ * decay, RetNet-style).
+ *  GLA_GATE_PER_KEY: one gate per key dimension, log_alpha [B, H, T, dk] (the layer).
+ *  GLA_GATE_SCALAR: one gate per token and head, log_alpha [B, H, T], shared by every
+ *    row of the state: S_t = alpha_t S_{t-1} + k_t^T v_t.  A data-independent decay
+ *    (RetNet-style, one constant per head) is the case of a value constant along t.
+ *    dlog_alpha is [B, H, T]: the sum over the key dimension of the per-key gradient
+ *    (times sigmoid(-x) / gate_tau with GLA_GATE_LOGITS).
+ * gate (the meaning of the values) and gate_shape combine freely. */
+typedef enum { GLA_GATE_PER_KEY = 0, GLA_GATE_SCALAR = 1 } gla_gate_shape_t;
+
 typedef struct {
   int32_t B, H, T;     /* batch, heads, sequence length (any of them may be 0)          */
   int32_t dk, dv;      /* key and value head dimensions                                  */
@@ -87,6 +101,7 @@ typedef struct {
   int32_t state_mode;  /* gla_state_mode_t                                               */
   int32_t gate;        /* gla_gate_t (zero: log_alpha given directly)                      */
   float gate_tau;      /* temperature of GLA_GATE_LOGITS (> 0, finite); unused otherwise   */
+  int32_t gate_shape;  /* gla_gate_shape_t (zero: one gate per key dimension)              */
 } gla_desc_t;
 
 /* Supported by this build (else GLA_ERR_UNSUPPORTED):
@@ -102,8 +117,8 @@ int32_t gla_version(void);
 
 /* Host-only validation of a descriptor for a pass (no device call).  Returns GLA_OK,
  * GLA_ERR_INVALID_ARG (desc NULL, a negative size, chunk or subchunk < 1,
- * chunk % subchunk != 0, unknown dtype/mode/pass/gate, GLA_GATE_LOGITS with gate_tau not
- * a positive finite number) or GLA_ERR_UNSUPPORTED. */
+ * chunk % subchunk != 0, unknown dtype/mode/pass/gate/gate_shape, GLA_GATE_LOGITS with
+ * gate_tau not a positive finite number) or GLA_ERR_UNSUPPORTED. */
 gla_status_t gla_validate(const gla_desc_t* desc, int32_t pass);
 
 /* Workspace bytes needed by gla_chunk_fwd (pass = GLA_PASS_FWD), gla_chunk_bwd
@@ -114,7 +129,8 @@ gla_status_t gla_workspace_bytes(const gla_desc_t* desc, int32_t pass, size_t* b
 /* Gate log-cumsum (the first step of the chunkwise form, Approach section):
  *   g[b,h,t,:] = sum of log_alpha[b,h,u,:] over u from the start of t's chunk to t,
  *   gamma[b,h,i,:] = g at the last row of chunk i (a ragged last chunk ends at T-1).
- * g: float32 [B,H,T,dk]; gamma: float32 [B,H,ceil(T/chunk),dk]. */
+ * g: float32 [B,H,T,dk]; gamma: float32 [B,H,ceil(T/chunk),dk] (with a scalar gate the
+ * dk entries of a row are equal). */
 gla_status_t gla_gate_cumsum(const gla_desc_t* desc, const void* log_alpha,
                              float* g, float* gamma, void* stream);
 
@@ -147,8 +163,9 @@ gla_status_t gla_chunk_bwd(const gla_desc_t* desc, const void* q, const void* k,
  *     S <- diag(exp(log_alpha[b,h,t,:])) S + k[b,h,t,:]^T v[b,h,t,:],
  *     o[b,h,t,:] = q[b,h,t,:] S,
  * with S float32 [B,H,dk,dv], read and updated in place (required; it is both input and
- * output, the one exception to the no-alias rule).  q, k, log_alpha [B,H,T,dk] and v
- * [B,H,T,dv] are inputs, o [B,H,T,dv] the output (all desc->dtype).  T is typically 1:
+ * output, the one exception to the no-alias rule).  q, k, log_alpha [B,H,T,dk] ([B,H,T]
+ * with a scalar gate) and v [B,H,T,dv] are inputs, o [B,H,T,dv] the output (all
+ * desc->dtype).  T is typically 1:
  * one new token per sequence; the state is read and written once per call whatever T
  * is, every step in fp32.  desc->chunk, subchunk and state_mode are not used, and no
  * workspace is needed.  B*H == 0 or T == 0 is a no-op.

@@ -142,3 +142,29 @@ def test_gate_front_end_fields(native):
         assert native.lib().gla_decode(ctypes.byref(d), p, p, p, p, p, p, None) == 1
     # the temperature is ignored when the gates are given as log_alpha
     assert native.validate(D(1, 1, 64, 64, 64, 64, 16, native.BF16, native.RECOMPUTE, 0, 0.0)) == 0
+
+
+def test_gate_shape_field(native):
+    """gate_shape: 0 (one gate per key dimension) or 1 (one gate per token); anything else
+    is an invalid argument.  Scalar gates add the sum over d as a last backward stage and,
+    on the bf16 chunk-64 path, a small workspace for its per-block partial sums."""
+    D = native.make_desc
+    base = dict(chunk=64, subchunk=16, dtype=native.BF16, state_mode=native.RECOMPUTE)
+    for shape in (native.GATE_PER_KEY, native.GATE_SCALAR):
+        for gate, tau in ((native.GATE_LOG_ALPHA, 1.0), (native.GATE_LOGITS, 8.0)):
+            d = D(2, 2, 300, 128, 64, gate=gate, gate_tau=tau, gate_shape=shape, **base)
+            assert native.validate(d) == 0 and native.validate(d, native.PASS_BWD) == 0
+    for bad in (2, -1, 7):
+        d = D(1, 1, 64, 64, 64, gate_shape=bad, **base)
+        assert native.validate(d) == 1, bad
+        p = ctypes.c_void_p(16)
+        assert native.lib().gla_decode(ctypes.byref(d), p, p, p, p, p, p, None) == 1
+    per_key = D(4, 4, 2048, 256, 512, **base)
+    sc = D(4, 4, 2048, 256, 512, gate_shape=native.GATE_SCALAR, **base)
+    assert native.workspace_bytes(sc, native.PASS_BWD) == (
+        native.workspace_bytes(per_key, native.PASS_BWD) + 4 * 4 * 2048 * (256 // 64) * 4)
+    assert native.workspace_bytes(sc, native.PASS_FWD) == native.workspace_bytes(per_key, native.PASS_FWD)
+    assert native.trace_stages(sc, native.PASS_BWD)[-1] == "gate_reduce"
+    assert "gate_reduce" not in native.trace_stages(per_key, native.PASS_BWD)
+    f32 = D(1, 2, 100, 64, 64, 64, 16, native.F32, native.RECOMPUTE, gate_shape=native.GATE_SCALAR)
+    assert native.trace_stages(f32, native.PASS_BWD)[-2:] == ["gate_grad", "gate_reduce"]
