@@ -21,7 +21,9 @@ read and written in place) at the workload's head shape for a small and a servin
 batch, against the HBM roofline.
 
 `gate_logits_step` times the same step fed gate logits (the gate front-end: log_alpha =
-logsigmoid(x)/16 formed inside the kernels, the gradient returned for x).
+logsigmoid(x)/16 formed inside the kernels, the gradient returned for x), and
+`scalar_gate_step` fed scalar gates (one per token and head, [B, H, T]; the gradient is
+summed over the key dimension).
 
 `cache_flushed` repeats the step after a 512 MiB write that evicts the 256 MiB Infinity
 Cache, with HIP events around the step only (the headline `value` is the warm rate).
@@ -404,36 +406,49 @@ def main():
         flushed = {"ms_per_step": fms, "value": B * T / (fms * 1e-3), "steps": args.flush_steps,
                    "flush_bytes": 512 << 20}
 
-    # The same steps fed gate logits (log_alpha = logsigmoid(x)/16 formed in the kernels,
-    # the gradient returned for x): what the gate front-end costs.
-    gate_fe = None
-    if not args.no_decode:
-        xg = up("gate_logits")
-        desc_g = nat.make_desc(B, H, T, dk, dv, C, cfg.subchunk,
-                               nat.BF16 if cfg.dtype == "bf16" else nat.F32, mode,
-                               nat.GATE_LOGITS, 16.0)
+    # The same steps with other gate inputs: gate logits (log_alpha = logsigmoid(x)/16
+    # formed in the kernels, the gradient returned for x), and scalar gates (one per token,
+    # [B, H, T], gradient summed over the key dimension).
+    def time_variant(desc_v, gate_t, dla_t, what):
+        ws_f = torch.empty(max(1, nat.workspace_bytes(desc_v, nat.PASS_FWD)), dtype=torch.uint8,
+                           device=dev)
+        ws_b = torch.empty(max(1, nat.workspace_bytes(desc_v, nat.PASS_BWD)), dtype=torch.uint8,
+                           device=dev)
         evs = hip.create(2)
 
-        def step_g():
-            for st in (L.gla_chunk_fwd(ctypes.byref(desc_g), P(q), P(k), P(v), P(xg), None, P(o),
-                                       P(S_T), P(wsf), wsf_n, sp),
-                       L.gla_chunk_bwd(ctypes.byref(desc_g), P(q), P(k), P(v), P(xg), None, P(dO),
-                                       None, P(dq), P(dk_), P(dv_), P(dla), None, P(wsb), wsb_n,
-                                       sp)):
+        def step_v():
+            for st in (L.gla_chunk_fwd(ctypes.byref(desc_v), P(q), P(k), P(v), P(gate_t), None,
+                                       P(o), P(S_T), P(ws_f), ws_f.numel(), sp),
+                       L.gla_chunk_bwd(ctypes.byref(desc_v), P(q), P(k), P(v), P(gate_t), None,
+                                       P(dO), None, P(dq), P(dk_), P(dv_), P(dla_t), None,
+                                       P(ws_b), ws_b.numel(), sp)):
                 if st:
-                    raise nat.GlaError(st, "gla_chunk_fwd/bwd with gate logits")
+                    raise nat.GlaError(st, f"gla_chunk_fwd/bwd with {what}")
         for _ in range(3):
-            step_g()
-        n_g = max(5, args.steps // 2)
+            step_v()
+        n_v = max(5, args.steps // 2)
         hip.record(evs[0], sp)
-        for _ in range(n_g):
-            step_g()
+        for _ in range(n_v):
+            step_v()
         hip.record(evs[1], sp)
         torch.cuda.synchronize()
-        gms = hip.elapsed_ms(evs[0], evs[1]) / n_g
+        vms = hip.elapsed_ms(evs[0], evs[1]) / n_v
         hip.destroy(evs)
-        gate_fe = {"ms_per_step": gms, "value": B * T / (gms * 1e-3), "gate_tau": 16.0,
-                   "steps": n_g}
+        del ws_f, ws_b
+        return {"ms_per_step": vms, "value": B * T / (vms * 1e-3), "steps": n_v}
+
+    gate_fe = scalar_fe = None
+    if not args.no_decode:
+        dt_code = nat.BF16 if cfg.dtype == "bf16" else nat.F32
+        desc_g = nat.make_desc(B, H, T, dk, dv, C, cfg.subchunk, dt_code, mode, nat.GATE_LOGITS,
+                               16.0)
+        gate_fe = time_variant(desc_g, up("gate_logits"), dla, "gate logits")
+        gate_fe["gate_tau"] = 16.0
+        desc_s = nat.make_desc(B, H, T, dk, dv, C, cfg.subchunk, dt_code, mode,
+                               gate_shape=nat.GATE_SCALAR)
+        la_s = up("log_alpha_scalar")
+        dla_s = torch.empty_like(la_s)
+        scalar_fe = time_variant(desc_s, la_s, dla_s, "scalar gates")
 
     if args.copy_calibration:
         nbytes = 1 << 30
@@ -490,6 +505,7 @@ def main():
         "roofline": roof,
         "cache_flushed": flushed,
         "gate_logits_step": gate_fe,
+        "scalar_gate_step": scalar_fe,
     }
     for arr in evf + evb:
         hip.destroy(arr)
