@@ -36,7 +36,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -51,14 +50,6 @@ PEAK_BF16 = 2.5e15         # dense bf16 MFMA flop/s
 PEAK_F32 = 157.3e12        # fp32 (MFMA / packed vector) flop/s
 METRIC = "GLA fwd+bwd tokens/s at 1.3B shape T=2K, 1 GPU; % of bf16 MFMA peak"
 
-# Kernel source of each stage (for matching committed counter summaries).
-STAGE_SOURCE = {
-    "gate_cumsum": "k_gate.hip", "gate_tot": "k_gate.hip", "gate_grad": "k_gate.hip",
-    "state_dot": "k_gate.hip", "intra": "k_intra.hip", "state_scan": "k_state.hip",
-    "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip", "state_scans": "k_state.hip", "output": "k_fwd.hip",
-    "fwd_fused": "k_fwd.hip", "seg_state": "k_state.hip", "bwd_chunk": "k_bwd.hip", "bwd_dqk": "k_bwd.hip",
-    "bwd_dv": "k_bwd.hip",
-}
 
 
 def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
@@ -238,9 +229,8 @@ def counter_traffic(stage, workload):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    src = os.path.join(ROOT, "chunkwise_linear_rnn_amd", "csrc", STAGE_SOURCE[stage])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    from chunkwise_linear_rnn_amd.profiling import STAGE_SOURCE, source_digest
+    if stage not in STAGE_SOURCE or rec.get("source_sha256") != source_digest(stage, ROOT):
         return None
     return rec.get("traffic_bytes_per_launch")
 

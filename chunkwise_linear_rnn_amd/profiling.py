@@ -24,13 +24,37 @@ STAGE_KERNEL = {"bwd_chunk": "k_bwd_chunk", "bwd_dqk": "k_bwd_dqk", "bwd_dv": "k
                 "state_scan_fwd": "k_state_scan", "state_scan_rev": "k_state_scan",
                 "state_scans": "k_state_scan", "seg_state": "k_state_scan",
                 "output": "k_output", "gate_cumsum": "k_gate_cumsum", "gate_grad": "k_gate_grad",
-                "gate_tot": "k_gate_tot"}
+                "gate_tot": "k_gate_tot", "gate_reduce": "k_gate_reduce", "state_dot": "k_state_dot",
+                "state_scan": "k_state_scan"}
 STAGE_SOURCE = {"bwd_chunk": "k_bwd.hip", "bwd_dqk": "k_bwd.hip", "bwd_dv": "k_bwd.hip",
                 "fwd_fused": "k_fwd.hip", "intra": "k_intra.hip",
                 "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip",
                 "state_scans": "k_state.hip", "seg_state": "k_state.hip",
                 "output": "k_fwd.hip", "gate_cumsum": "k_gate.hip", "gate_grad": "k_gate.hip",
-                "gate_tot": "k_gate.hip"}
+                "gate_tot": "k_gate.hip", "gate_reduce": "k_gate.hip", "state_dot": "k_gate.hip",
+                "state_scan": "k_state.hip"}
+
+
+# Stages whose kernel name is shared by several launches of a step: the template
+# arguments that pick the stage's instance (mangled, or demangled, symbol text).
+STAGE_SYMBOL = {"state_scans": ("ELi1ELb1E", ", 1, true"),     # stores states, cross terms
+                "seg_state": ("ELi0ELb0E", ", 0, false")}      # midpoint state only
+
+
+def matches(stage: str, name: str) -> bool:
+    if STAGE_KERNEL[stage] not in name:
+        return False
+    keys = STAGE_SYMBOL.get(stage)
+    return keys is None or any(k in name for k in keys)
+
+
+def source_digest(stage: str, root: str) -> str:
+    """sha256 over the stage's kernel source and the shared device headers it includes."""
+    h = hashlib.sha256()
+    csrc = os.path.join(root, "chunkwise_linear_rnn_amd", "csrc")
+    for f in (STAGE_SOURCE[stage], "gla_common.cuh", "gla_internal.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
 
 
 def short(name: str) -> str:
@@ -67,18 +91,16 @@ def counters(fetch_csv, write_csv, copy_bytes, stage, workload, command, root):
         return "copy" in n and "fill" not in n
     copy_f = [v for n, v in f if is_copy(n)]
     copy_w = [v for n, v in w if is_copy(n)]
-    sel = STAGE_KERNEL[stage]
-    kf = [v for n, v in f if sel in n]
-    kw = [v for n, v in w if sel in n]
+    kf = [v for n, v in f if matches(stage, n)]
+    kw = [v for n, v in w if matches(stage, n)]
     if stage in ("state_scan_fwd", "state_scan_rev"):   # two launches per step: keep one of each pair
         kf, kw = kf[0::2] if stage.endswith("fwd") else kf[1::2], kw[0::2] if stage.endswith("fwd") else kw[1::2]
     sf = copy_bytes / (1024.0 * (sum(copy_f) / len(copy_f)))
     sw = copy_bytes / (1024.0 * (sum(copy_w) / len(copy_w)))
     fetch = sum(kf) / len(kf) * 1024.0 * sf
     write = sum(kw) / len(kw) * 1024.0 * sw
-    src = os.path.join(root, "chunkwise_linear_rnn_amd", "csrc", STAGE_SOURCE[stage])
     return {"stage": stage, "workload": workload,
-            "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+            "source_sha256": source_digest(stage, root),
             "fetch_kib_raw": sum(kf) / len(kf), "write_kib_raw": sum(kw) / len(kw),
             "copy_scale_fetch": sf, "copy_scale_write": sw,
             "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
