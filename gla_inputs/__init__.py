@@ -27,7 +27,7 @@ import math
 
 import numpy as np
 
-__all__ = ["GlaConfig", "CONFIGS", "generate", "round_to_bf16_bits", "bf16_bits_to_f64",
+__all__ = ["GlaConfig", "CONFIGS", "generate", "generate_gsa", "round_to_bf16_bits", "bf16_bits_to_f64",
            "logsigmoid"]
 
 
@@ -125,4 +125,17 @@ def generate(cfg: GlaConfig, *, with_dO: bool = True, T: int | None = None):
         store, exact = _quantize(arr, cfg.dtype)
         out[name + "_store"] = store
         out[name] = exact
+    return out
+
+
+def generate_gsa(cfg: GlaConfig, m: int, *, with_dO: bool = True):
+    """Inputs of Gated Slot Attention with m slots: q, k, v (and dO) exactly as `generate`
+    draws them, plus per-slot gates from a third stream seeded (seed, 2): logits
+    g_slot ~ N(gate_mean, 1) over [B,H,T,m] and log_alpha_slot = logsigmoid(g_slot) / 8."""
+    out = generate(cfg, with_dO=with_dO)
+    rng = np.random.default_rng([cfg.seed, 2])
+    g = rng.standard_normal((cfg.B, cfg.H, cfg.T, m)) + cfg.gate_mean
+    store, exact = _quantize(logsigmoid(g) / 8.0, cfg.dtype)
+    out["log_alpha_slot_store"] = store
+    out["log_alpha_slot"] = exact
     return out

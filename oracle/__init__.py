@@ -24,12 +24,14 @@ Modules
   scalar      scalar-gate variants (one gate per token, or a constant decay per head):
               the layer with the gate repeated over the key dimension, its gradient
               summed back, and the parallel decay-matrix form used to pin it.
+  gsa         Gated Slot Attention: the slot recurrence with a softmax read, its gradient
+              by fp64 autograd of that recurrence, and the two-GLA-pass form.
   compare     error metrics used by the parity tests.
 
 Every function is pinned by the CPU tests in tests/test_oracle_*.py against facts that do
 not come from the oracle itself (closed forms, a library routine, finite differences,
 torch autograd on an independent fp64 graph, exact rational arithmetic).
 """
-from . import recurrence, chunkwise, compare, gates, scalar  # noqa: F401
+from . import recurrence, chunkwise, compare, gates, scalar, gsa  # noqa: F401
 from .recurrence import (recurrence_fwd, recurrence_bwd, quadratic_fwd,  # noqa: F401
                          closed_form_gate_grad)
