@@ -18,10 +18,12 @@ from __future__ import annotations
 
 from ._native import (GlaDesc, GlaError, F32, BF16, MATERIALIZED, RECOMPUTE, PASS_FWD,  # noqa: F401
                       PASS_BWD, PASS_STATES, GATE_LOG_ALPHA, GATE_LOGITS, GATE_PER_KEY, GATE_SCALAR,
-                      lib, lib_path, make_desc, status_string, trace_stages,
+                      lib, lib_path, make_desc, make_gsa_desc, gsa_workspace_bytes, status_string,
+                      trace_stages,
                       validate, version, workspace_bytes)
-from .ops import fwd, bwd, gate_cumsum, chunk_states, decode, GLAFunction, gla  # noqa: F401
+from .ops import fwd, bwd, gate_cumsum, chunk_states, decode, GLAFunction, gla, gsa_fwd, gsa_bwd  # noqa: F401
 
 __all__ = ["fwd", "bwd", "gate_cumsum", "chunk_states", "decode", "GLAFunction", "gla", "GlaDesc",
+           "gsa_fwd", "gsa_bwd", "make_gsa_desc", "gsa_workspace_bytes",
            "GlaError", "make_desc", "workspace_bytes", "validate", "status_string", "version",
            "lib", "lib_path"]

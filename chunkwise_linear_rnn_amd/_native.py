@@ -31,7 +31,16 @@ class GlaDesc(ctypes.Structure):
         return "GlaDesc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
 
 
+class GsaDesc(ctypes.Structure):
+    _fields_ = [("B", _i32), ("H", _i32), ("T", _i32), ("dk", _i32), ("dv", _i32),
+                ("slots", _i32), ("dtype", _i32)]
+
+    def __repr__(self):
+        return "GsaDesc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
 _PDESC = ctypes.POINTER(GlaDesc)
+_PGSA = ctypes.POINTER(GsaDesc)
 SIGNATURES = {
     "gla_status_string": (ctypes.c_char_p, [_i32]),
     "gla_version": (_i32, []),
@@ -43,6 +52,10 @@ SIGNATURES = {
     "gla_chunk_bwd": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp, _sz, _vp]),
     "gla_decode": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "gla_gsa_validate": (_i32, [_PGSA]),
+    "gla_gsa_workspace_bytes": (_i32, [_PGSA, _i32, ctypes.POINTER(_sz)]),
+    "gla_gsa_fwd": (_i32, [_PGSA, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "gla_gsa_bwd": (_i32, [_PGSA, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "gla_trace_stages": (_i32, [_PDESC, _i32, _i32, ctypes.POINTER(ctypes.c_char_p), _i32]),
     "gla_chunk_fwd_traced": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
                                     ctypes.POINTER(_vp), _i32]),
@@ -113,3 +126,15 @@ def workspace_bytes(desc: GlaDesc, pass_: int = PASS_FWD) -> int:
     if st != 0:
         raise GlaError(st, "gla_workspace_bytes")
     return int(out.value)
+
+
+def make_gsa_desc(B, H, T, dk, dv, slots, dtype=F32) -> GsaDesc:
+    return GsaDesc(B, H, T, dk, dv, slots, dtype)
+
+
+def gsa_workspace_bytes(desc: GsaDesc, pass_: int = PASS_FWD) -> int:
+    n = _sz()
+    st = int(lib().gla_gsa_workspace_bytes(ctypes.byref(desc), int(pass_), ctypes.byref(n)))
+    if st != 0:
+        raise GlaError(st, "gla_gsa_workspace_bytes")
+    return int(n.value)

@@ -497,3 +497,197 @@ gla_status_t gla_decode(const gla_desc_t* d, const void* q, const void* k, const
 }
 
 }  // extern "C"
+
+// =====================================================================================
+// Gated Slot Attention (page "Gated Slot Attention for Efficient Linear-Time Sequence
+// Modeling", Abstract): two GLA passes joined by a softmax.  Pipeline (fp32, chunk 64):
+//   w = 1 - exp(log_alpha)
+//   first pass  : intra-chunk kernel on (w, log_alpha) -> (w * e^(gamma - g))^T, e^gamma, g;
+//                 state scan with values k -> key slots S1_[i] [m][dk]; k_vg_out -> s
+//   p = softmax(s)
+//   second pass : gla_chunk_fwd with queries p, keys w, values v, gates log_alpha -> o
+// backward: the forward again up to p, gla_chunk_bwd of the second pass (dp, dw2, dv,
+// dlog_alpha2), ds = softmax backward, the intra-chunk kernel on (ds, log_alpha) ->
+// (ds * e^g)^T, the reverse scan with values q -> dS1, k_vg_bwd -> dq, dk, dw1 and the
+// gate terms, the closed-form gate scan, and dlog_alpha = dla1 + dla2 - (dw1 + dw2) e^la.
+// =====================================================================================
+namespace {
+
+struct GsaPlan {
+  size_t w = 0, g2 = 0, KhT = 0, eg = 0, S1 = 0, s = 0, p = 0, ws2 = 0, dp = 0, dw2 = 0,
+         dla2 = 0, ds = 0, QhT = 0, dS1 = 0, dw1 = 0, Dloc = 0, tot = 0, dla1 = 0, total = 0;
+  size_t ws2_bytes = 0;
+};
+
+gla_desc_t gsa_layer2(const gla_gsa_desc_t* d) {
+  gla_desc_t x{};
+  x.B = d->B; x.H = d->H; x.T = d->T; x.dk = d->slots; x.dv = d->dv; x.chunk = 64;
+  x.subchunk = 16; x.dtype = GLA_F32; x.state_mode = GLA_STATES_RECOMPUTE;
+  x.gate = GLA_GATE_LOG_ALPHA; x.gate_tau = 1.f; x.gate_shape = GLA_GATE_PER_KEY;
+  return x;
+}
+
+GsaPlan gsa_plan(const gla_gsa_desc_t* d, int pass) {
+  GsaPlan p;
+  const size_t BH = (size_t)d->B * d->H, T = d->T, m = d->slots, dk = d->dk;
+  const size_t N = (T + 63) / 64;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  const size_t TM = BH * T * m * 4;
+  p.w = take(TM); p.g2 = take(TM); p.KhT = take(BH * N * m * 64 * 4); p.eg = take(BH * N * m * 4);
+  p.S1 = take(BH * N * m * dk * 4); p.s = take(TM); p.p = take(TM);
+  const gla_desc_t l2 = gsa_layer2(d);
+  const size_t b2 = plan_of(&l2, pass == GLA_PASS_BWD ? GLA_PASS_BWD : GLA_PASS_FWD).total;
+  p.ws2 = take(b2); p.ws2_bytes = b2;
+  if (pass == GLA_PASS_BWD) {
+    p.dp = take(TM); p.dw2 = take(TM); p.dla2 = take(TM); p.ds = take(TM);
+    p.QhT = take(BH * N * m * 64 * 4); p.dS1 = take(BH * N * m * dk * 4); p.dw1 = take(TM);
+    p.Dloc = take(TM); p.tot = take(BH * N * m * 4); p.dla1 = take(TM);
+  }
+  p.total = off;
+  return p;
+}
+
+struct GsaFwd {   // the forward up to p (and o when asked)
+  gla_status_t run(const gla_gsa_desc_t* d, const float* q, const float* k, const float* v,
+                   const float* la, float* o, char* w, const GsaPlan& p, hipStream_t s) {
+    const int BH = d->B * d->H, T = d->T, m = d->slots, DK = d->dk, N = (T + 63) / 64;
+    gla_status_t rs;
+    if ((rs = dev(gla::launch_gsa_w(la, (float*)(w + p.w), (long)BH * T * m, s))) != GLA_OK) return rs;
+    gla::IntraArgs ia{};
+    ia.dtype = 0; ia.C = 64; ia.BH = BH; ia.T = T; ia.dk = m; ia.N = N; ia.want_A = false;
+    ia.q = w + p.w; ia.k = w + p.w; ia.la = la; ia.g = nullptr;
+    ia.KhT = w + p.KhT; ia.eg = (float*)(w + p.eg); ia.g2_out = (float*)(w + p.g2);
+    ia.gate = gla::GateFn{0, 1.f};
+    if ((rs = dev(gla::launch_intra(ia, s))) != GLA_OK) return rs;
+    gla::ScanArgs sa{};
+    sa.dtype = 0; sa.C = 64; sa.BH = BH; sa.T = T; sa.dk = m; sa.dv = DK; sa.N = N;
+    sa.reverse = false; sa.store = 3; sa.XT = w + p.KhT; sa.Y = k; sa.eg = (const float*)(w + p.eg);
+    sa.states = w + p.S1;
+    if ((rs = dev(gla::launch_state_scan(sa, s))) != GLA_OK) return rs;
+    if ((rs = dev(gla::launch_vg_out(q, k, (const float*)(w + p.w), (const float*)(w + p.g2),
+                                     (const float*)(w + p.S1), (float*)(w + p.s), BH, T, DK, m,
+                                     s))) != GLA_OK)
+      return rs;
+    if ((rs = dev(gla::launch_softmax_rows((const float*)(w + p.s), (float*)(w + p.p),
+                                           (long)BH * T, m, s))) != GLA_OK)
+      return rs;
+    if (!o) return GLA_OK;
+    const gla_desc_t l2 = gsa_layer2(d);
+    return gla_chunk_fwd(&l2, w + p.p, w + p.w, v, la, nullptr, o, nullptr, w + p.ws2, p.ws2_bytes,
+                         s);
+  }
+};
+
+gla_status_t gsa_common_checks(const gla_gsa_desc_t* d, int pass) {
+  const gla_status_t st = gla_gsa_validate(d);
+  if (st != GLA_OK) return st;
+  if (pass != GLA_PASS_FWD && pass != GLA_PASS_BWD) return GLA_ERR_INVALID_ARG;
+  return GLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gla_status_t gla_gsa_validate(const gla_gsa_desc_t* d) {
+  if (!d) return GLA_ERR_INVALID_ARG;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->dk < 0 || d->dv < 0 || d->slots < 0)
+    return GLA_ERR_INVALID_ARG;
+  if (d->dtype != GLA_F32 && d->dtype != GLA_BF16) return GLA_ERR_INVALID_ARG;
+  if (d->dtype != GLA_F32) return GLA_ERR_UNSUPPORTED;
+  if (d->dk < 64 || d->dk > 256 || d->dk % 64 != 0) return GLA_ERR_UNSUPPORTED;
+  if (d->slots < 64 || d->slots > 256 || d->slots % 64 != 0) return GLA_ERR_UNSUPPORTED;
+  if (d->dv < 64 || d->dv > 1024 || d->dv % 64 != 0) return GLA_ERR_UNSUPPORTED;
+  const long long bh = (long long)d->B * d->H;
+  if (bh > 65535) return GLA_ERR_UNSUPPORTED;
+  if (bh * (long long)d->T > (1LL << 31) - 1) return GLA_ERR_UNSUPPORTED;
+  if (((long long)d->T + 63) / 64 > 65535) return GLA_ERR_UNSUPPORTED;
+  return GLA_OK;
+}
+
+gla_status_t gla_gsa_workspace_bytes(const gla_gsa_desc_t* d, int32_t pass, size_t* bytes) {
+  if (!bytes) return GLA_ERR_INVALID_ARG;
+  const gla_status_t st = gsa_common_checks(d, pass);
+  if (st != GLA_OK) return st;
+  *bytes = (size_t)d->B * d->H * d->T == 0 ? 0 : gsa_plan(d, pass).total;
+  return GLA_OK;
+}
+
+gla_status_t gla_gsa_fwd(const gla_gsa_desc_t* d, const void* q, const void* k, const void* v,
+                         const void* log_alpha, void* o, void* ws, size_t ws_bytes,
+                         void* stream) {
+  const gla_status_t st = gsa_common_checks(d, GLA_PASS_FWD);
+  if (st != GLA_OK) return st;
+  if ((long long)d->B * d->H * d->T == 0) return GLA_OK;
+  if (!q || !k || !v || !log_alpha || !o) return GLA_ERR_INVALID_ARG;
+  for (const void* ptr : std::initializer_list<const void*>{q, k, v, log_alpha, o, ws})
+    if (!aligned16(ptr)) return GLA_ERR_INVALID_ARG;
+  const GsaPlan p = gsa_plan(d, GLA_PASS_FWD);
+  if (!ws || ws_bytes < p.total) return GLA_ERR_WORKSPACE;
+  GsaFwd f;
+  return f.run(d, (const float*)q, (const float*)k, (const float*)v, (const float*)log_alpha,
+               (float*)o, (char*)ws, p, (hipStream_t)stream);
+}
+
+gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* d, const void* q, const void* k, const void* v,
+                         const void* log_alpha, const void* dO, void* dq, void* dk, void* dv,
+                         void* dlog_alpha, void* ws, size_t ws_bytes, void* stream) {
+  const gla_status_t st = gsa_common_checks(d, GLA_PASS_BWD);
+  if (st != GLA_OK) return st;
+  if ((long long)d->B * d->H * d->T == 0) return GLA_OK;
+  if (!q || !k || !v || !log_alpha || !dO || !dq || !dk || !dv || !dlog_alpha)
+    return GLA_ERR_INVALID_ARG;
+  for (const void* ptr : std::initializer_list<const void*>{q, k, v, log_alpha, dO, dq, dk, dv,
+                                                            dlog_alpha, ws})
+    if (!aligned16(ptr)) return GLA_ERR_INVALID_ARG;
+  const GsaPlan p = gsa_plan(d, GLA_PASS_BWD);
+  if (!ws || ws_bytes < p.total) return GLA_ERR_WORKSPACE;
+  char* w = (char*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  const float* la = (const float*)log_alpha;
+  const int BH = d->B * d->H, T = d->T, m = d->slots, DK = d->dk, N = (T + 63) / 64;
+  const long TM = (long)BH * T * m;
+  GsaFwd f;
+  gla_status_t rs = f.run(d, (const float*)q, (const float*)k, (const float*)v, la, nullptr, w, p, s);
+  if (rs != GLA_OK) return rs;
+  // second pass backward: gradients for p, w (as keys), v and log_alpha
+  const gla_desc_t l2 = gsa_layer2(d);
+  rs = gla_chunk_bwd(&l2, w + p.p, w + p.w, v, la, nullptr, dO, nullptr, w + p.dp, w + p.dw2, dv,
+                     w + p.dla2, nullptr, w + p.ws2, p.ws2_bytes, s);
+  if (rs != GLA_OK) return rs;
+  if ((rs = dev(gla::launch_softmax_bwd((const float*)(w + p.p), (const float*)(w + p.dp),
+                                        (float*)(w + p.ds), (long)BH * T, m, s))) != GLA_OK)
+    return rs;
+  // first pass backward: (ds * e^g)^T per chunk, the reverse scan of the key slots
+  gla::IntraArgs ia{};
+  ia.dtype = 0; ia.C = 64; ia.BH = BH; ia.T = T; ia.dk = m; ia.N = N; ia.want_A = false;
+  ia.q = w + p.ds; ia.k = w + p.w; ia.la = la; ia.g = nullptr; ia.QhT = w + p.QhT;
+  ia.eg = (float*)(w + p.eg); ia.gate = gla::GateFn{0, 1.f};
+  if ((rs = dev(gla::launch_intra(ia, s))) != GLA_OK) return rs;
+  gla::ScanArgs ra{};
+  ra.dtype = 0; ra.C = 64; ra.BH = BH; ra.T = T; ra.dk = m; ra.dv = DK; ra.N = N;
+  ra.reverse = true; ra.store = 3; ra.XT = w + p.QhT; ra.Y = q; ra.eg = (const float*)(w + p.eg);
+  ra.states = w + p.dS1;
+  if ((rs = dev(gla::launch_state_scan(ra, s))) != GLA_OK) return rs;
+  if ((rs = dev(gla::launch_vg_bwd((const float*)q, (const float*)k, (const float*)(w + p.w),
+                                   (const float*)(w + p.g2), (const float*)(w + p.ds),
+                                   (const float*)(w + p.s), (const float*)(w + p.S1),
+                                   (const float*)(w + p.dS1), (float*)dq, (float*)dk,
+                                   (float*)(w + p.dw1), (float*)(w + p.Dloc), (float*)(w + p.tot),
+                                   BH, T, DK, m, s))) != GLA_OK)
+    return rs;
+  if ((rs = dev(gla::launch_gate_grad(0, (const float*)(w + p.Dloc), (const float*)(w + p.tot),
+                                      nullptr, la, gla::GateFn{0, 1.f}, w + p.dla1, nullptr, BH, T,
+                                      m, 64, s))) != GLA_OK)
+    return rs;
+  return dev(gla::launch_gsa_combine(la, (const float*)(w + p.dla1), (const float*)(w + p.dla2),
+                                     (const float*)(w + p.dw1), (const float*)(w + p.dw2),
+                                     (float*)dlog_alpha, TM, s));
+}
+
+}  // extern "C"

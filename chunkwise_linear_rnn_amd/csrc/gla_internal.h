@@ -152,4 +152,24 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
+// Gated Slot Attention (fp32): w = 1 - exp(log_alpha); the first (slot-gated) pass's chunk
+// output and chunk backward; row softmax and its backward; the gate-gradient combination.
+// Layouts: q, k [BH][T][dk]; w, g2 (chunk-local cumsum * log2 e), s, ds, dw, Dloc [BH][T][m];
+// S1, dS1 [BH][N][m][dk] (dS1 of chunk i = the gradient flowing in from chunk i + 1);
+// tot [BH][N][m].
+hipError_t launch_gsa_w(const float* la, float* w, long n, hipStream_t s);
+hipError_t launch_vg_out(const float* q, const float* k, const float* w, const float* g2,
+                         const float* S1, float* s_out, int BH, int T, int dk, int m,
+                         hipStream_t s);
+hipError_t launch_vg_bwd(const float* q, const float* k, const float* w, const float* g2,
+                         const float* ds, const float* s_in, const float* S1, const float* dS1,
+                         float* dq, float* dk, float* dw, float* Dloc, float* tot, int BH, int T,
+                         int dkh, int m, hipStream_t s);
+hipError_t launch_softmax_rows(const float* x, float* p, long nrows, int m, hipStream_t s);
+hipError_t launch_softmax_bwd(const float* p, const float* dp, float* ds, long nrows, int m,
+                              hipStream_t s);
+hipError_t launch_gsa_combine(const float* la, const float* dla1, const float* dla2,
+                              const float* dw1, const float* dw2, float* dla, long n,
+                              hipStream_t s);
+
 }  // namespace gla

@@ -9,7 +9,7 @@ import torch
 
 from ._native import (BF16, F32, GATE_LOG_ALPHA, GATE_LOGITS, GATE_PER_KEY, GATE_SCALAR,
                       MATERIALIZED, RECOMPUTE, PASS_BWD, PASS_FWD, PASS_STATES, GlaError, lib,
-                      make_desc, workspace_bytes)
+                      make_desc, make_gsa_desc, gsa_workspace_bytes, workspace_bytes)
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 _MODES = {"materialized": MATERIALIZED, "recompute": RECOMPUTE}
@@ -230,3 +230,47 @@ def decode(q, k, v, log_alpha, S, *, gate_tau=None):
 def gla(q, k, v, log_alpha, S0=None, chunk=64, subchunk=16, state_mode="recompute"):
     """Differentiable GLA layer: returns (o, S_T)."""
     return GLAFunction.apply(q, k, v, log_alpha, S0, chunk, subchunk, state_mode)
+
+
+def _gsa_desc(q, v, log_alpha):
+    if q.dim() != 4 or v.dim() != 4 or log_alpha.dim() != 4:
+        raise ValueError("q, v and log_alpha must be [B, H, T, d]")
+    if q.dtype != torch.float32:
+        raise ValueError("Gated Slot Attention is float32 in this build")
+    B, H, T, dk = q.shape
+    return make_gsa_desc(B, H, T, dk, v.shape[-1], log_alpha.shape[-1], F32)
+
+
+def gsa_fwd(q, k, v, log_alpha, *, workspace=None):
+    """o of Gated Slot Attention: key/value slots [slots, d] forgotten by the per-slot
+    gates exp(log_alpha) [B, H, T, slots], written with weight 1 - alpha, read by
+    softmax(slots_k q) (float32)."""
+    desc = _gsa_desc(q, v, log_alpha)
+    dev = q.device
+    B, H, T, dk, dv, m = desc.B, desc.H, desc.T, desc.dk, desc.dv, desc.slots
+    for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)), (v, "v", (B, H, T, dv)),
+                      (log_alpha, "log_alpha", (B, H, T, m))):
+        _check(t, n, shp, torch.float32, dev)
+    o = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+    need = gsa_workspace_bytes(desc, PASS_FWD)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _call("gla_gsa_fwd", lib().gla_gsa_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(log_alpha), _ptr(o), _ptr(ws), need, _stream(dev)))
+    return o
+
+
+def gsa_bwd(q, k, v, log_alpha, dO, *, workspace=None):
+    """dq, dk, dv, dlog_alpha of Gated Slot Attention for the loss gradient dO."""
+    desc = _gsa_desc(q, v, log_alpha)
+    dev = q.device
+    B, H, T, dk, dv, m = desc.B, desc.H, desc.T, desc.dk, desc.dv, desc.slots
+    for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)), (v, "v", (B, H, T, dv)),
+                      (log_alpha, "log_alpha", (B, H, T, m)), (dO, "dO", (B, H, T, dv))):
+        _check(t, n, shp, torch.float32, dev)
+    dq, dk_, dv_, dla = (torch.empty_like(x) for x in (q, k, v, log_alpha))
+    need = gsa_workspace_bytes(desc, PASS_BWD)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _call("gla_gsa_bwd", lib().gla_gsa_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(log_alpha), _ptr(dO), _ptr(dq), _ptr(dk_),
+                                           _ptr(dv_), _ptr(dla), _ptr(ws), need, _stream(dev)))
+    return dq, dk_, dv_, dla

@@ -175,6 +175,40 @@ gla_status_t gla_chunk_bwd(const gla_desc_t* desc, const void* q, const void* k,
 gla_status_t gla_decode(const gla_desc_t* desc, const void* q, const void* k, const void* v,
                         const void* log_alpha, float* S, void* o, void* stream);
 
+/* Gated Slot Attention (page "Gated Slot Attention for Efficient Linear-Time Sequence
+ * Modeling", mlsanity.com summary, Abstract: m memory slots forgotten by a GLA-style gate,
+ * read with a softmax; two GLA passes joined by a softmax).  Per batch b and head h, with
+ * per-slot gates alpha_t = exp(log_alpha[b,h,t,:]) in (0,1]^m and w_t = 1 - alpha_t:
+ *
+ *     Kt_t = diag(alpha_t) Kt_{t-1} + w_t^T k_t,   Vt_t = diag(alpha_t) Vt_{t-1} + w_t^T v_t,
+ *     o_t  = softmax(Kt_t q_t)^T Vt_t     (softmax over the m slots; Kt, Vt start at zero)
+ *
+ * q, k [B,H,T,dk], v, o, dO, dv [B,H,T,dv], log_alpha, dlog_alpha [B,H,T,slots], all float32
+ * (bf16 is GLA_ERR_UNSUPPORTED in this build), contiguous, 16-byte aligned, caller-owned.
+ * Scratch comes from `ws` (gla_gsa_workspace_bytes); no state is carried in or out.
+ * Supported: dk and slots in {64, 128, 192, 256}, dv a multiple of 64 up to 1024,
+ * B*H <= 65535, B*H*T < 2^31; B*H*T == 0 is a no-op.  Errors as for the layer's entry
+ * points; everything is checked on the host before any launch. */
+typedef struct {
+  int32_t B, H, T;
+  int32_t dk, dv;
+  int32_t slots;   /* m, the number of memory slots */
+  int32_t dtype;   /* gla_dtype_t; GLA_F32 */
+} gla_gsa_desc_t;
+
+gla_status_t gla_gsa_validate(const gla_gsa_desc_t* desc);
+/* pass: GLA_PASS_FWD or GLA_PASS_BWD. */
+gla_status_t gla_gsa_workspace_bytes(const gla_gsa_desc_t* desc, int32_t pass, size_t* bytes);
+/* o (required) from q, k, v, log_alpha. */
+gla_status_t gla_gsa_fwd(const gla_gsa_desc_t* desc, const void* q, const void* k,
+                         const void* v, const void* log_alpha, void* o, void* ws,
+                         size_t ws_bytes, void* stream);
+/* dq, dk, dv, dlog_alpha (all required) for the loss gradient dO; recomputes the forward. */
+gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* desc, const void* q, const void* k,
+                         const void* v, const void* log_alpha, const void* dO, void* dq,
+                         void* dk, void* dv, void* dlog_alpha, void* ws, size_t ws_bytes,
+                         void* stream);
+
 /* Stage tracing, for profiling.  The *_traced variants behave exactly like
  * gla_chunk_fwd / gla_chunk_bwd and additionally record caller-created hipEvent_t
  * handles on `stream`: events[j] right before the j-th kernel launch and events[n] after

@@ -168,3 +168,23 @@ def test_gate_shape_field(native):
     assert "gate_reduce" not in native.trace_stages(per_key, native.PASS_BWD)
     f32 = D(1, 2, 100, 64, 64, 64, 16, native.F32, native.RECOMPUTE, gate_shape=native.GATE_SCALAR)
     assert native.trace_stages(f32, native.PASS_BWD)[-2:] == ["gate_grad", "gate_reduce"]
+
+
+def test_gsa_descriptor_validation(native):
+    """Gated Slot Attention: float32 only in this build; dk and slots in {64..256} by 64."""
+    G = native.make_gsa_desc
+    L = native.lib()
+    assert L.gla_gsa_validate(ctypes.byref(G(2, 2, 300, 128, 192, 64))) == 0
+    assert L.gla_gsa_validate(ctypes.byref(G(2, 2, 300, 128, 192, 64, native.BF16))) == 2
+    assert L.gla_gsa_validate(ctypes.byref(G(2, 2, 300, 128, 192, 64, 7))) == 1
+    for bad in ((1, 1, 64, 96, 64, 64), (1, 1, 64, 64, 64, 32), (1, 1, 64, 64, 96, 64),
+                (1, 1, 64, 64, 64, 320)):
+        assert L.gla_gsa_validate(ctypes.byref(G(*bad))) == 2, bad
+    assert L.gla_gsa_validate(ctypes.byref(G(-1, 1, 64, 64, 64, 64))) == 1
+    assert L.gla_gsa_validate(None) == 1
+    assert native.gsa_workspace_bytes(G(0, 2, 64, 64, 64, 64)) == 0
+    assert native.gsa_workspace_bytes(G(1, 2, 64, 64, 64, 64), native.PASS_BWD) > \
+        native.gsa_workspace_bytes(G(1, 2, 64, 64, 64, 64), native.PASS_FWD) > 0
+    p = ctypes.c_void_p(16)
+    # a missing workspace is reported before any launch
+    assert L.gla_gsa_fwd(ctypes.byref(G(1, 1, 64, 64, 64, 64)), p, p, p, p, p, None, 0, None) == 3
