@@ -25,6 +25,9 @@ logsigmoid(x)/16 formed inside the kernels, the gradient returned for x), and
 `scalar_gate_step` fed scalar gates (one per token and head, [B, H, T]; the gradient is
 summed over the key dimension).
 
+`gsa_step` times Gated Slot Attention (float32, fwd + bwd, --gsa-slots memory slots,
+default 64) at the workload's B, H, T, dk, dv.
+
 `cache_flushed` repeats the step after a 512 MiB write that evicts the 256 MiB Infinity
 Cache, with HIP events around the step only (the headline `value` is the warm rate).
 
@@ -235,6 +238,45 @@ def counter_traffic(stage, workload):
     return rec.get("traffic_bytes_per_launch")
 
 
+def gsa_measure(L, nat, hip, dev, sp, cfg, slots, steps):
+    """Gated Slot Attention fwd + bwd (gla_gsa_fwd, gla_gsa_bwd; float32) on the workload's
+    B, H, T, dk, dv with `slots` memory slots: ms per step from HIP events around `steps`
+    back-to-back steps after 2 warm-up steps.  Inputs: gla_inputs.generate_gsa."""
+    import torch
+    from gla_inputs import generate_gsa
+    c32 = cfg.replace(dtype="f32")
+    d = generate_gsa(c32, slots)
+    t = {n: torch.from_numpy(d[n + "_store"]).to(dev) for n in ("q", "k", "v", "dO", "log_alpha_slot")}
+    desc = nat.make_gsa_desc(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, slots, nat.F32)
+    o = torch.empty_like(t["v"])
+    grads = [torch.empty_like(t[n]) for n in ("q", "k", "v", "log_alpha_slot")]
+    need_f = nat.gsa_workspace_bytes(desc, nat.PASS_FWD)
+    need_b = nat.gsa_workspace_bytes(desc, nat.PASS_BWD)
+    ws = torch.empty(max(need_f, need_b), dtype=torch.uint8, device=dev)
+    P = lambda x: ctypes.c_void_p(x.data_ptr())  # noqa: E731
+
+    def step():
+        for st in (L.gla_gsa_fwd(ctypes.byref(desc), P(t["q"]), P(t["k"]), P(t["v"]),
+                                 P(t["log_alpha_slot"]), P(o), P(ws), need_f, sp),
+                   L.gla_gsa_bwd(ctypes.byref(desc), P(t["q"]), P(t["k"]), P(t["v"]),
+                                 P(t["log_alpha_slot"]), P(t["dO"]), *(P(g) for g in grads),
+                                 P(ws), need_b, sp)):
+            if st:
+                raise nat.GlaError(st, "gla_gsa_fwd/bwd")
+    for _ in range(2):
+        step()
+    evs = hip.create(2)
+    hip.record(evs[0], sp)
+    for _ in range(steps):
+        step()
+    hip.record(evs[1], sp)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(evs[0], evs[1]) / steps
+    hip.destroy(evs)
+    return {"ms_per_step": ms, "value": cfg.B * cfg.T / (ms * 1e-3), "unit": "tokens/s",
+            "slots": slots, "dtype": "f32", "steps": steps}
+
+
 def decode_measure(L, nat, hip, dev, sp, H, dk, dv, batches=(4, 64), calls=200):
     """One-token recurrent steps (gla_decode, T = 1, bf16, float32 state in place) at a few
     batch sizes: microseconds per step from HIP events around `calls` back-to-back steps;
@@ -280,7 +322,10 @@ def main():
     ap.add_argument("--state-mode", default="recompute", choices=["recompute", "materialized"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
-                    help="skip the one-token recurrent step measurement")
+                    help="skip the side measurements: decode step, gate-logit and scalar-gate "
+                         "steps, Gated Slot Attention step")
+    ap.add_argument("--gsa-slots", type=int, default=64,
+                    help="memory slots of the Gated Slot Attention step")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens per (batch, head) in the oracle sample")
     ap.add_argument("--flush-steps", type=int, default=10,
@@ -440,6 +485,11 @@ def main():
         dla_s = torch.empty_like(la_s)
         scalar_fe = time_variant(desc_s, la_s, dla_s, "scalar gates")
 
+    # Gated Slot Attention (float32) at the workload's head shape: one fwd + bwd step
+    gsa_step = None
+    if not args.no_decode:
+        gsa_step = gsa_measure(L, nat, hip, dev, sp, cfg, args.gsa_slots, max(5, args.steps // 5))
+
     if args.copy_calibration:
         nbytes = 1 << 30
         a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1)
@@ -496,6 +546,7 @@ def main():
         "cache_flushed": flushed,
         "gate_logits_step": gate_fe,
         "scalar_gate_step": scalar_fe,
+        "gsa_step": gsa_step,
     }
     for arr in evf + evb:
         hip.destroy(arr)

@@ -522,7 +522,7 @@ struct GsaPlan {
 gla_desc_t gsa_layer2(const gla_gsa_desc_t* d) {
   gla_desc_t x{};
   x.B = d->B; x.H = d->H; x.T = d->T; x.dk = d->slots; x.dv = d->dv; x.chunk = 64;
-  x.subchunk = 16; x.dtype = GLA_F32; x.state_mode = GLA_STATES_RECOMPUTE;
+  x.subchunk = 16; x.dtype = GLA_F32; x.state_mode = GLA_STATES_MATERIALIZED;
   x.gate = GLA_GATE_LOG_ALPHA; x.gate_tau = 1.f; x.gate_shape = GLA_GATE_PER_KEY;
   return x;
 }
