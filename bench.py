@@ -326,6 +326,9 @@ def main():
                          "steps, Gated Slot Attention step")
     ap.add_argument("--gsa-slots", type=int, default=64,
                     help="memory slots of the Gated Slot Attention step")
+    ap.add_argument("--gsa-only", action="store_true",
+                    help="time only the Gated Slot Attention step and print its JSON (for "
+                         "profiling its kernels on their own)")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens per (batch, head) in the oracle sample")
     ap.add_argument("--flush-steps", type=int, default=10,
@@ -353,6 +356,15 @@ def main():
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.gsa_only:
+        L = nat.lib()
+        sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        rec = gsa_measure(L, nat, HipEvents(), dev, sp, cfg, args.gsa_slots, args.steps)
+        rec.update({"metric": "Gated Slot Attention fwd+bwd tokens/s", "n_gpus": 1,
+                    "config": {"workload": cfg.name + f"_gsa{args.gsa_slots}", "B": cfg.B,
+                               "H": cfg.H, "T": cfg.T, "dk": cfg.dk, "dv": cfg.dv}})
+        print(json.dumps(rec), flush=True)
+        return
     print(f"[bench] generating {cfg}", file=sys.stderr, flush=True)
     d = generate(cfg)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
