@@ -119,6 +119,10 @@ __global__ __launch_bounds__(kThreads) void k_intra(
   constexpr int NPAIR = NS * (NS - 1) / 2;  // off-diagonal sub-block pairs
   constexpr int PPW = (NPAIR + 3) / 4;      // pairs per wave
   constexpr int NITEM = NS * 136 * 4;       // diagonal (pair, 16-column quarter) items
+  constexpr int NDW = (NS + 3) / 4;         // diagonal sub-blocks per wave (MFMA path)
+  // largest spread of g * log2 e inside a 16-row sub-block for which the diagonal
+  // sub-blocks take the rebased MFMA path (factors within 2^+-kDiagRange of the inputs)
+  constexpr float kDiagRange = 96.f;
   constexpr int IPT = (NITEM + kThreads - 1) / kThreads;
   constexpr int GLD = DB + 4;
   constexpr int XLD = DB + 8;
@@ -136,9 +140,11 @@ __global__ __launch_bounds__(kThreads) void k_intra(
 
   // off-diagonal sub-blocks accumulate in registers, the diagonal items (each owned by
   // one thread across the dk blocks) in LDS
-  f32x4 accp[PPW > 0 ? PPW : 1];
+  f32x4 accp[PPW > 0 ? PPW : 1], accd[NDW];
 #pragma unroll
   for (int p = 0; p < (PPW > 0 ? PPW : 1); ++p) accp[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < NDW; ++p) accd[p] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (WANT_A)
     for (int item = threadIdx.x; item < NITEM; item += kThreads) dacc[item] = 0.f;
 
@@ -296,7 +302,45 @@ __global__ __launch_bounds__(kThreads) void k_intra(
           }
         }
       }
-      // ---- diagonal sub-blocks: fp32, log-space ---------------------------------------
+      // ---- diagonal sub-blocks ------------------------------------------------------
+      // When the gates' spread inside every 16-row sub-block is moderate (the usual
+      // case), the same MFMA on operands rebased at the sub-block's first row (entries
+      // above the diagonal are dropped when the block is written); otherwise the exact
+      // fp32 log-space sum per (t, s, column).
+      bool wide = false;
+      for (int idx = threadIdx.x; idx < NS * DB; idx += kThreads) {
+        const int I = idx / DB, col = idx % DB;
+        const float g0 = gs[16 * I * GLD + col];
+        float mx = 0.f;
+#pragma unroll
+        for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, fabsf(gs[(16 * I + rr) * GLD + col] - g0));
+        wide = wide || !(mx <= kDiagRange);
+      }
+      if (!__syncthreads_or(wide)) {
+#pragma unroll
+        for (int dI = 0; dI < NDW; ++dI) {
+          const int I = w + 4 * dI;
+          if (I < NS) {
+            const int rho = 16 * I, tr = 16 * I + r;
+#pragma unroll 1
+            for (int kb = 0; kb < DB / 32; ++kb) {
+              const int c0 = kb * 32 + 8 * qd;
+              Frag<OpT> fa, fb;
+              float gr[8], gq[8], xq[8], xk[8];
+              load8(gr, gs + rho * GLD + c0);
+              load8(gq, gs + tr * GLD + c0);
+              load8(xq, qs + tr * XLD + c0);
+              load8(xk, ks + tr * XLD + c0);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                fa.set(e, xq[e] * __builtin_amdgcn_exp2f(gq[e] - gr[e]));
+                fb.set(e, xk[e] * __builtin_amdgcn_exp2f(gr[e] - gq[e]));
+              }
+              mma(accd[dI], fa, fb);
+            }
+          }
+        }
+      } else {
 #pragma unroll 1
       for (int item = threadIdx.x; item < NITEM; item += kThreads) {
         {
@@ -319,11 +363,26 @@ __global__ __launch_bounds__(kThreads) void k_intra(
           dacc[item] += acc;
         }
       }
+      }
     }
     __syncthreads();
   }
 
   if constexpr (WANT_A) {
+    // the MFMA part of the diagonal entries (t = 4 qd + e, s = r in sub-block I) joins
+    // the fp32 part on the first column-quarter item of the entry
+#pragma unroll
+    for (int dI = 0; dI < NDW; ++dI) {
+      const int I = w + 4 * dI;
+      if (I < NS) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tt = 4 * qd + e;
+          if (r <= tt) dacc[(I * 136 + tt * (tt + 1) / 2 + r) << 2] += accd[dI][e];
+        }
+      }
+    }
+    __syncthreads();
     OpT* Ab = A_out + ((long)bh * N + i) * C * C;
 #pragma unroll
     for (int pi = 0; pi < PPW; ++pi) {

@@ -268,3 +268,31 @@ def test_invalid_arguments_raise(gla):
         gla.fwd(y, y, y, y, chunk=32)
     with pytest.raises(ValueError):
         gla.fwd(y, y, y.double(), y)
+
+
+def test_diagonal_paths_bf16(gla):
+    """The intra-chunk diagonal sub-blocks take an MFMA path on rebased operands when the
+    gates' spread inside every 16-row sub-block is moderate and an exact fp32 path
+    otherwise; here chunks 0 and 2 decay strongly in one key column (log_alpha = -12 there:
+    a spread far past the MFMA path's range) and chunks 1 and 3 are ordinary, so both
+    paths run in one call, forward and backward."""
+    cfg = GlaConfig("diag", "bf16", 1, 2, 256, 128, 64, 64, seed=12)
+    say(f"[edge] diagonal paths {cfg}")
+    d = generate(cfg)
+    la = d["log_alpha"].copy()
+    la[:, :, 0:64, 5] = -12.0
+    la[:, :, 128:192, 70] = -12.0
+    from gla_inputs import round_to_bf16_bits, bf16_bits_to_f64
+    bits = round_to_bf16_bits(la)
+    d2 = dict(d)
+    d2["log_alpha"], d2["log_alpha_store"] = bf16_bits_to_f64(bits), bits
+    x = dev_inputs(d2, "bf16", DEV)
+    o, ST = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"])
+    g = gla.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["dO"])
+    torch.cuda.synchronize()
+    heads = [(0, 0), (0, 1)]
+    ref = oracle_heads(d2, heads)
+    check("o", pick(host(o), heads), ref["o"], "bf16")
+    check("S_T", pick(host(ST), heads), ref["S_T"], "bf16")
+    for k, t in zip(("dq", "dk", "dv", "dla"), g[:4]):
+        check(k, pick(host(t), heads), ref[k], "bf16")
