@@ -42,9 +42,12 @@ struct XRegs {
       if constexpr (SPLIT) load_frag_c(lo[kb], row + C + kb * 32);
     }
   }
-  __device__ __forceinline__ void apply(f32x4& acc, int kb, const Frag<OpT>& b) const {
-    mma(acc, hi[kb], b);
-    if constexpr (SPLIT) mma(acc, lo[kb], b);
+  // acc += (the value-side fragment b as the A operand) x (these rows as the B operand):
+  // the product lands with this wave's rows as output columns, i.e. each lane holds one
+  // state row (its r) and four consecutive value columns (4 qd .. 4 qd + 3)
+  __device__ __forceinline__ void apply_t(f32x4& acc, int kb, const Frag<OpT>& b) const {
+    mma(acc, b, hi[kb]);
+    if constexpr (SPLIT) mma(acc, b, lo[kb]);
   }
 };
 
@@ -56,7 +59,8 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // value-side tiles per operand
   constexpr int NJ = TV / 16, NY = TV / 64, YLD = C + 8, XW = SPLIT ? 2 * C : C;
   static_assert(TV == 64 || (TV == 128 && STORE != 2), "[v][k] staging is 64 columns wide");
-  constexpr int SLD = (STORE == 2 ? 64 : TV) + 8;   // state tile staging for 16-byte row stores
+  // state tile staging for 16-byte row stores: [v][k] (STORE 2) or [k][v]
+  constexpr int SLD = (STORE == 2 ? 64 : TV) + 8;
   constexpr int SROWS = STORE == 2 ? TV : 64;
   using StT = typename std::conditional<STORE == 3, float, OpT>::type;
   using XR = XRegs<OpT, SPLIT, C>;
@@ -82,15 +86,13 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   const int vt = lt % nvt, kt = (lt / nvt) % nkt, bh = lt / (nvt * nkt);
   const int v0 = vt * TV, k0 = kt * 64;
   const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
-  const int rl = 16 * w + 4 * qd;          // tile-local accumulator rows rl .. rl+3
-  const int row0 = k0 + rl;
+  const int krow = k0 + 16 * w + r;        // this lane's state row
 
-  f32x4 acc[NJ];   // acc[j][e] = S[row0 + e][v0 + 16 j + r]
+  f32x4 acc[NJ];   // acc[j][e] = S[krow][v0 + 16 j + 4 qd + e]
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc[j][e] = S_in ? S_in[((long)bh * dk + row0 + e) * dv + v0 + 16 * j + r] : 0.f;
+    acc[j] = S_in ? *reinterpret_cast<const f32x4*>(S_in + ((long)bh * dk + krow) * dv + v0 + 16 * j + 4 * qd)
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
   // Settle the initial-state loads before the loop: otherwise the compiler, merging the
   // loop's entry with its back edge, treats the state registers as possibly still being
   // loaded and waits for nearly every prefetch in flight at each step.
@@ -142,30 +144,40 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // Stores are issued right after the step's first barrier and before the next chunk's
   // loads: vector memory operations complete in order, so a store issued after the
   // prefetch would make the next step wait for the write round trip.
-  float part_prev[4] = {0.f, 0.f, 0.f, 0.f};   // cross term of the previous chunk
+  float part_prev = 0.f;   // cross term of the previous chunk for row krow
   int i_prev = -1;
   auto body = [&](int step, Set& st) {
     const int i = chunk_of(step), ipre = chunk_of(step + DEPTH);
-    // exp(gamma) of this lane's rows for this chunk, loaded here and first used after the
+    // exp(gamma) of this lane's row for this chunk, loaded here and first used after the
     // cross term: a value carried over from the previous step would make the compiler
     // wait for every load in flight at the loop's back edge
-    const f32x4 egr = *reinterpret_cast<const f32x4*>(eg + ((long)bh * N + i) * dk + row0);
+    const float egr = eg[((long)bh * N + i) * dk + krow];
 #pragma unroll
     for (int h = 0; h < NY; ++h) {
       st.ty[h].store(ys + 64 * h * YLD);
       if constexpr (CROSS) st.ty2[h].store(y2s + 64 * h * YLD);
     }
-    if constexpr (STORE != 0) {
-      // the state before this chunk, through LDS
+    if constexpr (STORE == 2) {
+      // the state before this chunk, [v][k], through LDS
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (STORE == 2)
-            ss[(16 * j + r) * SLD + rl + e] = (StT)acc[j][e];    // [v][k]
-          else
-            ss[(rl + e) * SLD + 16 * j + r] = (StT)acc[j][e];    // [k][v]
+        for (int e = 0; e < 4; ++e) ss[(16 * j + 4 * qd + e) * SLD + 16 * w + r] = (StT)acc[j][e];
+    } else if constexpr (STORE != 0) {
+      // the state before this chunk, [k][v], through LDS: this lane's four consecutive
+      // values of row krow in each column tile as one 8- or 16-byte write
+      StT* srow = ss + (16 * w + r) * SLD + 4 * qd;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if constexpr (sizeof(StT) == 2) {
+          bf16x4 b;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[e] = (bf16)acc[j][e];
+          *reinterpret_cast<bf16x4*>(srow + 16 * j) = b;
+        } else {
+          *reinterpret_cast<f32x4*>(srow + 16 * j) = acc[j];
         }
+      }
     }
     __syncthreads();
     if constexpr (STORE != 0) {
@@ -185,16 +197,15 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
       }
     }
     if constexpr (CROSS) {
-      if (i_prev >= 0 && r == 0) {
-        f32x4 o = {part_prev[0], part_prev[1], part_prev[2], part_prev[3]};
-        *reinterpret_cast<f32x4*>(cross + (((long)bh * N + i_prev) * nvt + vt) * dk + row0) = o;
-      }
+      if (i_prev >= 0 && qd == 0)
+        cross[(((long)bh * N + i_prev) * nvt + vt) * dk + krow] = part_prev;
     }
     fetch_y(st, ipre);
 
     if constexpr (CROSS) {
-      // P_j = X2^T Y2 for column tile j, folded into the row sums one tile at a time
-      float sum[4] = {0.f, 0.f, 0.f, 0.f};
+      // P_j = X2^T Y2 for column tile j (same layout as the state), folded into the row
+      // sum one tile at a time; the four lanes of a row (qd) then add their partial sums
+      float sum = 0.f;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         f32x4 P = {0.f, 0.f, 0.f, 0.f};
@@ -202,28 +213,29 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
         for (int kb = 0; kb < C / 32; ++kb) {
           Frag<OpT> fb;
           yfrag(fb, y2s, 16 * j + r, kb);
-          st.cx2.apply(P, kb, fb);
+          st.cx2.apply_t(P, kb, fb);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sum[e] += acc[j][e] * P[e];
+        for (int e = 0; e < 4; ++e) sum += acc[j][e] * P[e];
       }
       st.cx2.load(X2T + xrow(ipre));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) part_prev[e] = row16_sum(sum[e]);
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      part_prev = sum;
       i_prev = i;
     }
 
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[j][e] *= egr[e];
+      for (int e = 0; e < 4; ++e) acc[j][e] *= egr;
 #pragma unroll
     for (int kb = 0; kb < C / 32; ++kb)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         Frag<OpT> fb;
         yfrag(fb, ys, 16 * j + r, kb);
-        st.cx.apply(acc[j], kb, fb);
+        st.cx.apply_t(acc[j], kb, fb);
       }
     st.cx.load(XT + xrow(ipre));
     __syncthreads();
@@ -237,17 +249,12 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   }
   for (; step < nsteps; ++step) body(step, sets[0]);
   if constexpr (CROSS) {
-    if (i_prev >= 0 && r == 0) {
-      f32x4 o = {part_prev[0], part_prev[1], part_prev[2], part_prev[3]};
-      *reinterpret_cast<f32x4*>(cross + (((long)bh * N + i_prev) * nvt + vt) * dk + row0) = o;
-    }
+    if (i_prev >= 0 && qd == 0) cross[(((long)bh * N + i_prev) * nvt + vt) * dk + krow] = part_prev;
   }
   if (S_out) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        S_out[((long)bh * dk + row0 + e) * dv + v0 + 16 * j + r] = acc[j][e];
+      *reinterpret_cast<f32x4*>(S_out + ((long)bh * dk + krow) * dv + v0 + 16 * j + 4 * qd) = acc[j];
   }
 }
 
