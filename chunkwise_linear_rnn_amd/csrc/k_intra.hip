@@ -239,7 +239,10 @@ __global__ __launch_bounds__(kThreads) void k_intra(
       for (int u_ = 0; u_ < (DB * (C / 8) + kThreads - 1) / kThreads; ++u_) {   // fixed trip count
         const int idx = threadIdx.x + u_ * kThreads;
         if ((DB * (C / 8)) % kThreads != 0 && idx >= DB * (C / 8)) continue;
-        const int c = idx / (C / 8), r8 = (idx % (C / 8)) * 8;
+        // a wave takes 32 columns x two 8-row groups of opposite parity, so that its
+        // column reads of the g, q, k tiles fall on distinct LDS banks
+        const int lw = idx & 63, wv = idx >> 6;
+        const int c = 32 * (wv & 1) + (lw & 31), r8 = 8 * (2 * (wv >> 1) + (lw >> 5));
         const long rowi = ((long)bh * N + i) * dk + d0 + c;
         float x[8];
 #pragma unroll
