@@ -96,13 +96,15 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
         byt = (tok * (2 * dk * e + 2 * dv * e + dk * 4) + BH * N * C * C * e + tokp * dk * e
                + 2 * st + tok * (2 * dk * e + dv * e + dk * 4))
         return byt, tok * (6 * dk * dv + C * (2 * dk + 2 * dv))
-    if stage == "bwd_dqk":   # reads q, k, v, dO, g, S, dS, chunk totals; writes dq, dk, dla
+    if stage == "bwd_dqk_dv":
+        # dq/dk part: reads q, k, v, dO, g, S, dS, chunk totals; writes dq, dk, dla
         byt = (tok * (2 * dk * e + 2 * dv * e + dk * 4) + 2 * st + BH * N * dk * 4
                + tok * 3 * dk * e)
-        return byt, tok * (4 * dk * dv + C * dv + 2 * C * dk)
-    if stage == "bwd_dv":    # reads Kh, A, dS, dO; writes dv
-        byt = tokp * dk * e + BH * N * C * C * e + st + 2 * tok * dv * e
-        return byt, tok * (2 * dk * dv + C * dv)
+        fl = tok * (4 * dk * dv + C * dv + 2 * C * dk)
+        # dv part: reads Kh, A, dS, dO; writes dv
+        byt += tokp * dk * e + BH * N * C * C * e + st + 2 * tok * dv * e
+        fl += tok * (2 * dk * dv + C * dv)
+        return byt, fl
     if stage == "gate_tot":
         return 2 * BH * N * (dv // 64) * dk * 4 + BH * N * dk * 4, 0
     if stage == "gate_grad":

@@ -146,8 +146,7 @@ struct Tracer {
 // Stage names of each pipeline, in launch order.
 const char* const kFwdMat[] = {"gate_cumsum", "intra", "state_scan", "output"};
 const char* const kFwdRec[] = {"intra", "seg_state", "fwd_fused"};
-const char* const kBwd[] = {"intra", "state_scans", "state_dot", "gate_tot", "bwd_dqk",
-                            "bwd_dv"};
+const char* const kBwd[] = {"intra", "state_scans", "state_dot", "gate_tot", "bwd_dqk_dv"};
 const char* const kBwdOne[] = {"intra", "state_scans", "state_dot", "bwd_chunk", "gate_tot",
                                "gate_grad"};
 
@@ -158,7 +157,7 @@ int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, in
     if (d->state_mode == GLA_STATES_MATERIALIZED) { src = kFwdMat; n = 4; }
     else { src = kFwdRec; n = 3; }
   } else if (gla::bwd_split(d->dtype, d->chunk)) {
-    src = kBwd; n = 6;
+    src = kBwd; n = 5;
   } else {
     src = kBwdOne; n = 6;
   }
@@ -440,8 +439,6 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
     if ((rs = totals()) != GLA_OK) return rs;
     if ((rs = tr.mark()) != GLA_OK) return rs;
     if ((rs = dev(gla::launch_bwd_chunk(ba, s))) != GLA_OK) return rs;
-    if ((rs = tr.mark()) != GLA_OK) return rs;
-    if ((rs = dev(gla::launch_bwd_dv(ba, s))) != GLA_OK) return rs;
     if (sg) {
       if ((rs = tr.mark()) != GLA_OK) return rs;
       if ((rs = reduce((const float*)(w + p.dpart), DK / 64)) != GLA_OK) return rs;

@@ -134,12 +134,11 @@ struct BwdArgs {
   float* dla_part;         // scalar gates (split path): fp32 sums of the per-(t, d) gradient
                            // over each 64-wide d block, [BH][T][dk/64], instead of dla
 };
-// The backward chunk work: with bf16 operands and chunk 64 it is two kernels (dq, dk and
-// dlog_alpha, after the chunk totals are formed; then dv: launch_bwd_chunk and
-// launch_bwd_dv); otherwise one (launch_bwd_chunk), followed by the gate-gradient kernel.
+// The backward chunk work (launch_bwd_chunk): with bf16 operands and chunk 64 one launch of
+// dq / dk / dlog_alpha workgroups (after the chunk totals are formed) interleaved with dv
+// workgroups; otherwise one workgroup per chunk, followed by the gate-gradient kernel.
 bool bwd_split(int dtype, int C);
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s);
-hipError_t launch_bwd_dv(const BwdArgs& a, hipStream_t s);
 
 // Recurrent evaluation (decoding): T tokens in order, state updated in place.
 struct DecodeArgs {

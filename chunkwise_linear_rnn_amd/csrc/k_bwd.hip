@@ -22,15 +22,16 @@
 // chunk totals that the two state scans form from their fp32 states.
 //
 // Kernels
-//   k_bwd_dqk  (chunk 64) dq, dk and dlog_alpha per (chunk, 64-wide dk block): D as
+//   k_bwd_dqk_dv (chunk 64) one launch holding two kinds of workgroup, interleaved:
+//   dq/dk part  dq, dk and dlog_alpha per (chunk, 64-wide dk block): D as
 //              chunk-local suffix sums plus the carry from the later chunks' totals
 //              (formed by the gate-total kernel from the scans).  One pass over
 //              64-wide dv blocks accumulates dA, dO S^T and V dS^T together: dO and V
 //              tiles go through LDS (shared by the 4 waves), each wave's S / dS fragments
 //              are prefetched straight into registers (double-buffered); then the
 //              intra-chunk part of the block.
-//   k_bwd_dv   (chunk 64) dv = A^T dO + Kh dS per (chunk, 64 values), looping over
-//              64-wide dk blocks, XCD-aware.
+//   dv part     dv = A^T dO + Kh dS per (chunk, 64 values), looping over 64-wide dk
+//              blocks.
 //   k_bwd_chunk (chunk 128, and fp32 operands) all of the above in one workgroup per
 //              chunk, operands read straight from memory.
 #include "gla_common.cuh"
@@ -216,15 +217,16 @@ __device__ __forceinline__ void bwd_finish_block(const IntraLds<C, DB, Tin>& L,
 }
 
 // =====================================================================================
-// chunk 64: k_bwd_dqk, one workgroup per (batch*head, chunk, 64-wide dk block)
+// chunk 64, dq/dk part: one workgroup per (batch*head, chunk, 64-wide dk block)
 // =====================================================================================
 // Wave w owns columns 16w .. 16w+15 of the block for all 64 rows of the chunk (four
 // accumulator tiles each for dq and dk).  dA = tril(dO V^T) is formed by every dk block of
 // the chunk (it is cheap next to the dO S^T and V dS^T products, and keeps the blocks
 // independent).  Three workgroups fit on a CU, so one's loads overlap another's math.
+constexpr int kDqkLds = 64 * (64 + 4) * 4 + 64 * (64 + 4) * 4 + 2 * 64 * (64 + 8) * 2;
 template <typename Tin, typename OpT>
-__global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk(
-    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+__device__ __forceinline__ void bwd_dqk_body(
+    char* __restrict__ arena, int lt, const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dO, const float* __restrict__ g, const OpT* __restrict__ S,
     const OpT* __restrict__ dS, Tin* __restrict__ dq, Tin* __restrict__ dk_out,
     const float* __restrict__ tot, const float* __restrict__ cT, const Tin* __restrict__ la,
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk(
   constexpr int o_u = C * FLD * 4, o_q = o_u + C * GLD * 4, o_k = o_q + C * XLD * 2;
   constexpr int bytes = o_k + C * XLD * 2;
   static_assert(2 * C * YLD * 2 <= bytes - o_u, "dO / V tiles fit the shared region");
-  __shared__ __attribute__((aligned(16))) char arena[bytes];
+  static_assert(bytes == kDqkLds, "arena size");
   float* dAs = (float*)arena;
   OpT* dOs = (OpT*)(arena + o_u);
   OpT* Vs = dOs + C * YLD;
@@ -248,7 +250,6 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk(
 
   // XCD-aware: the dk blocks of one chunk (same dO and V tiles) are consecutive
   const int NJ = dk / 64;
-  const int lt = xcd_logical(blockIdx.x, gridDim.x);
   const int jb = lt % NJ, i = (lt / NJ) % N, bh = lt / (NJ * N);
   const int d0 = 64 * jb, t0 = i * C, rows = min(C, T - t0);
   const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
@@ -527,25 +528,26 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk(
 }
 
 // =====================================================================================
-// chunk 64: k_bwd_dv, one workgroup per (batch*head, chunk, 64 values)
+// chunk 64, dv part: one workgroup per (batch*head, chunk, 64 values)
 // =====================================================================================
 // dv = A^T dO + sum over 64-wide dk blocks of Kh_blk dS_blk; the next block's Kh and
 // dS^T tiles are loaded into registers while the current one multiplies.
 template <typename Tin, typename OpT>
-__global__ __launch_bounds__(kThreads) void k_bwd_dv(const OpT* __restrict__ Kh,
-                                                     const OpT* __restrict__ A,
-                                                     const OpT* __restrict__ dS,
-                                                     const Tin* __restrict__ dO,
-                                                     Tin* __restrict__ dv_out, int T, int dk,
-                                                     int dv, int N) {
+__device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
+                                            const OpT* __restrict__ Kh,
+                                            const OpT* __restrict__ A,
+                                            const OpT* __restrict__ dS,
+                                            const Tin* __restrict__ dO,
+                                            Tin* __restrict__ dv_out, int T, int dk, int dv,
+                                            int N) {
   constexpr int C = 64, NM = 4, LD = 64 + 8;
-  __shared__ __attribute__((aligned(16))) OpT ksh[C * LD];   // Kh block [t][k]
-  __shared__ __attribute__((aligned(16))) OpT dsT[64 * LD];  // dS block transposed [v][k]
-  __shared__ __attribute__((aligned(16))) OpT aT[C * LD];    // A^T [t][s]
-  __shared__ __attribute__((aligned(16))) OpT doT[64 * LD];  // dO^T [v][t]
-  // XCD-aware: the dv tiles of one chunk share Kh and A
+  static_assert(4 * 64 * LD * 2 <= kDqkLds, "the dv tiles fit the shared arena");
+  OpT* ksh = (OpT*)arena;        // Kh block [t][k]
+  OpT* dsT = ksh + C * LD;       // dS block transposed [v][k]
+  OpT* aT = dsT + 64 * LD;       // A^T [t][s]
+  OpT* doT = aT + C * LD;        // dO^T [v][t]
+  // the dv tiles of one chunk share Kh and A (consecutive logical ids)
   const int nvt = dv / 64, NJ = dk / 64;
-  const int lt = xcd_logical(blockIdx.x, gridDim.x);
   const int vt = lt % nvt, i = (lt / nvt) % N, bh = lt / (nvt * N);
   const int v0 = vt * 64, t0 = i * C, rows = min(C, T - t0);
   const int w = wave_id(), l = lane_id(), r = l & 15;
@@ -777,14 +779,40 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(
   }
 }
 
+// The two chunk-64 backward kernels as one launch: dq / dk / dlog_alpha workgroups and dv
+// workgroups interleaved in proportion (a dv workgroup needs neither the chunk totals nor
+// anything the dq / dk workgroups write), so that their memory phases overlap on each CU.
+template <typename Tin, typename OpT>
+__global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk_dv(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const Tin* __restrict__ dO, const float* __restrict__ g, const OpT* __restrict__ S,
+    const OpT* __restrict__ dS, Tin* __restrict__ dq, Tin* __restrict__ dk_out,
+    const float* __restrict__ tot, const float* __restrict__ cT, const Tin* __restrict__ la,
+    GateFn gf, Tin* __restrict__ dla, float* __restrict__ dla_part, const OpT* __restrict__ Kh,
+    const OpT* __restrict__ A, Tin* __restrict__ dv_out, int T, int dk, int dv, int N,
+    int n_dqk) {
+  __shared__ __attribute__((aligned(16))) char arena[kDqkLds];
+  const int L = xcd_logical(blockIdx.x, gridDim.x);
+  const long total = gridDim.x;
+  // Bresenham split: logical id L is a dq/dk workgroup when the count of them up to L grows
+  const int before = (int)(((long)L * n_dqk) / total), upto = (int)(((long)(L + 1) * n_dqk) / total);
+  if (upto > before)
+    bwd_dqk_body<Tin, OpT>(arena, before, q, k, v, dO, g, S, dS, dq, dk_out, tot, cT, la, gf,
+                           dla, dla_part, T, dk, dv, N);
+  else
+    bwd_dv_body<Tin, OpT>(arena, L - before, Kh, A, dS, dO, dv_out, T, dk, dv, N);
+}
+
 // ---------------------------------------------------------------------------------
 template <typename Tin, typename OpT, int C, int DK>
 static hipError_t launch_bwd_t2(const BwdArgs& a, hipStream_t s) {
   if constexpr (C == 64 && sizeof(OpT) == 2) {
-    hipLaunchKernelGGL((k_bwd_dqk<Tin, OpT>), dim3((a.dk / 64) * a.N * a.BH), dim3(kThreads), 0, s,
+    const int n_dqk = (a.dk / 64) * a.N * a.BH, n_dv = (a.dv / 64) * a.N * a.BH;
+    hipLaunchKernelGGL((k_bwd_dqk_dv<Tin, OpT>), dim3(n_dqk + n_dv), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,
                        (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq, (Tin*)a.dk_out, a.tot, a.cT,
-                       (const Tin*)a.la, a.gate, (Tin*)a.dla, a.dla_part, a.T, a.dk, a.dv, a.N);
+                       (const Tin*)a.la, a.gate, (Tin*)a.dla, a.dla_part, (const OpT*)a.Kh,
+                       (const OpT*)a.A, (Tin*)a.dv_out, a.T, a.dk, a.dv, a.N, n_dqk);
   } else {
     hipLaunchKernelGGL((k_bwd_chunk<Tin, OpT, C, DK>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,
@@ -812,13 +840,5 @@ hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s) {
   return launch_bwd_t<bf16, bf16, 128>(a, s);
 }
 
-hipError_t launch_bwd_dv(const BwdArgs& a, hipStream_t s) {
-  if (a.BH == 0 || a.N == 0) return hipSuccess;
-  if (!bwd_split(a.dtype, a.C)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_bwd_dv<bf16, bf16>), dim3((a.dv / 64) * a.N * a.BH), dim3(kThreads), 0, s,
-                     (const bf16*)a.Kh, (const bf16*)a.A, (const bf16*)a.dS, (const bf16*)a.dO,
-                     (bf16*)a.dv_out, a.T, a.dk, a.dv, a.N);
-  return hipGetLastError();
-}
 
 }  // namespace gla

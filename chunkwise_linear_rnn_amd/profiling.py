@@ -19,14 +19,14 @@ import os
 import re
 import sys
 
-STAGE_KERNEL = {"bwd_chunk": "k_bwd_chunk", "bwd_dqk": "k_bwd_dqk", "bwd_dv": "k_bwd_dv",
+STAGE_KERNEL = {"bwd_chunk": "k_bwd_chunk", "bwd_dqk_dv": "k_bwd_dqk_dv",
                 "fwd_fused": "k_fwd_fused", "intra": "k_intra",
                 "state_scan_fwd": "k_state_scan", "state_scan_rev": "k_state_scan",
                 "state_scans": "k_state_scan", "seg_state": "k_state_scan",
                 "output": "k_output", "gate_cumsum": "k_gate_cumsum", "gate_grad": "k_gate_grad",
                 "gate_tot": "k_gate_tot", "gate_reduce": "k_gate_reduce", "state_dot": "k_state_dot",
                 "state_scan": "k_state_scan"}
-STAGE_SOURCE = {"bwd_chunk": "k_bwd.hip", "bwd_dqk": "k_bwd.hip", "bwd_dv": "k_bwd.hip",
+STAGE_SOURCE = {"bwd_chunk": "k_bwd.hip", "bwd_dqk_dv": "k_bwd.hip",
                 "fwd_fused": "k_fwd.hip", "intra": "k_intra.hip",
                 "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip",
                 "state_scans": "k_state.hip", "seg_state": "k_state.hip",

@@ -224,9 +224,9 @@ gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* desc, const void* q, const void* 
  *                          at the midpoint chunk, so that the two halves of the sequence
  *                          run in parallel; no launch otherwise), fwd_fused
  *   backward:              intra, state_scans (the forward and the reverse scan, one
- *                          launch), [state_dot when dS_T is given], then gate_tot, bwd_dqk,
- *                          bwd_dv (bf16, chunk 64) or bwd_chunk, gate_tot, gate_grad
- *                          (otherwise) */
+ *                          launch), [state_dot when dS_T is given], then gate_tot,
+ *                          bwd_dqk_dv (bf16, chunk 64: dq/dk/dlog_alpha and dv workgroups
+ *                          in one launch) or bwd_chunk, gate_tot, gate_grad (otherwise) */
 int32_t gla_trace_stages(const gla_desc_t* desc, int32_t pass, int32_t with_dS_T,
                          const char** names, int32_t max_names);
 
