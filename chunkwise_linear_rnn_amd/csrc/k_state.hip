@@ -67,6 +67,9 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   __shared__ __attribute__((aligned(16))) OpT ys[TV * YLD];
   __shared__ __attribute__((aligned(16))) OpT y2s[CROSS ? TV * YLD : 8];
   __shared__ __attribute__((aligned(16))) StT ss[STORE != 0 ? SROWS * SLD : 8];
+  // per-row decays exp(gamma) of EB consecutive steps, [step][row]
+  constexpr int EB = 32;
+  __shared__ float egs[EB * 64];
   // 1-D grid, XCD-aware: the dv tiles of one (bh, dk tile) share the transposed operand
   // tiles and the dk tiles of one bh share the value-side tiles, so they run on one XCD.
   // With two scans in the launch, the first half of the logical ids runs the first.
@@ -96,7 +99,24 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // Settle the initial-state loads before the loop: otherwise the compiler, merging the
   // loop's entry with its back edge, treats the state registers as possibly still being
   // loaded and waits for nearly every prefetch in flight at each step.
+  // chunk of a step; steps past the end map to the last one (refetched, never used), so
+  // that every prefetch is unconditional and the compiler's wait counts stay exact
+  auto chunk_of = [&](int step) {
+    const int sc = min(step, nsteps - 1);
+    return reverse ? N - 1 - sc : sc;
+  };
+  // the decays of steps [sb, sb + EB) into LDS: read there at each step, they put no
+  // global-memory round trip on the chain of dependent steps
+  auto stage_eg = [&](int sb) {
+#pragma unroll
+    for (int u_ = 0; u_ < EB * 64 / kThreads; ++u_) {
+      const int idx = threadIdx.x + u_ * kThreads;
+      egs[idx] = eg[((long)bh * N + chunk_of(sb + (idx >> 6))) * dk + k0 + (idx & 63)];
+    }
+  };
+  if (nsteps > 0) stage_eg(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
 
   // The operands of later chunks are loaded into registers while the current chunk
   // computes: the value-side tiles (then LDS, transposed) and this wave's rows of the
@@ -125,12 +145,6 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
       if constexpr (CROSS) st.ty2[h].load(Y2 + ((long)bh * T + t0) * dv + v0 + 64 * h, dv, rows);
     }
   };
-  // chunk of a step; steps past the end map to the last one (refetched, never used), so
-  // that every prefetch is unconditional and the compiler's wait counts stay exact
-  auto chunk_of = [&](int step) {
-    const int sc = min(step, nsteps - 1);
-    return reverse ? N - 1 - sc : sc;
-  };
   if (nsteps > 0) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
@@ -148,10 +162,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   int i_prev = -1;
   auto body = [&](int step, Set& st) {
     const int i = chunk_of(step), ipre = chunk_of(step + DEPTH);
-    // exp(gamma) of this lane's row for this chunk, loaded here and first used after the
-    // cross term: a value carried over from the previous step would make the compiler
-    // wait for every load in flight at the loop's back edge
-    const float egr = eg[((long)bh * N + i) * dk + krow];
+    const float egr = egs[(step % EB) * 64 + 16 * w + r];   // exp(gamma) of row krow
 #pragma unroll
     for (int h = 0; h < NY; ++h) {
       st.ty[h].store(ys + 64 * h * YLD);
@@ -240,14 +251,24 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
     st.cx.load(XT + xrow(ipre));
     __syncthreads();
   };
+  // blocks of EB steps (EB even: step s runs on set s % DEPTH throughout); each step ends
+  // with a barrier, so the previous block's decays are no longer read when restaged
+  static_assert(EB % 2 == 0 && EB * 64 % kThreads == 0, "decay staging");
   int step = 0;
-  if constexpr (DEPTH == 2) {
-    for (; step + 1 < nsteps; step += 2) {
-      body(step, sets[0]);
-      body(step + 1, sets[DEPTH - 1]);
+  for (int sb = 0; sb < nsteps; sb += EB) {
+    if (sb > 0) {
+      stage_eg(sb);
+      __syncthreads();
     }
+    const int se = min(sb + EB, nsteps);
+    if constexpr (DEPTH == 2) {
+      for (; step + 1 < se; step += 2) {
+        body(step, sets[0]);
+        body(step + 1, sets[DEPTH - 1]);
+      }
+    }
+    for (; step < se; ++step) body(step, sets[0]);
   }
-  for (; step < nsteps; ++step) body(step, sets[0]);
   if constexpr (CROSS) {
     if (i_prev >= 0 && qd == 0) cross[(((long)bh * N + i_prev) * nvt + vt) * dk + krow] = part_prev;
   }
@@ -288,6 +309,8 @@ static hipError_t launch_scan_t(const ScanArgs& a, const ScanArgs* b, hipStream_
       }
     }
     launch_scan_k<Tin, OpT, SPLIT, C, 1, true, 64>(a, b, s);
+  } else if constexpr (SPLIT) {
+    return hipErrorInvalidValue;   // split operands come with the backward's cross term only
   } else {
     switch (a.store) {
       case 0: launch_scan_k<Tin, OpT, SPLIT, C, 0, false, 64>(a, b, s); break;
