@@ -385,6 +385,60 @@ struct ColTile {
 };
 
 // ---------------------------------------------------------------------------------
+// Transposed 64 x 64 bf16 tiles without padding (row stride 64 elements = 8 chunks of 8),
+// chunk k of row c kept at chunk k ^ g(c), g(c) = 2 ((c / 8) % 4) ^ 4 ((c / 2) % 2).
+// Banks of the LDS as measured on gfx950: 16-byte reads serve 16 lanes per cycle from 64
+// banks (the lanes of each half wave split by the parity of lane bits 2..4); 16-byte
+// writes serve 8 consecutive lanes per cycle from 32 banks.  With this swizzle the
+// fragment reads below (16 consecutive rows, one chunk column per 16 lanes) and the block
+// writes of WaveColTile (eight lanes: two chunk rows x four column blocks) both touch
+// distinct banks in every cycle.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ int swz64(int c, int chunk) {
+  return chunk ^ ((c >> 2) & 6) ^ ((c << 1) & 4);
+}
+// Fragment read: row `c`, elements 32 kb + 8 (lane / 16) .. + 7.
+__device__ __forceinline__ void load_frag_x64(Frag<bf16>& f, const bf16* tile, int c, int kb) {
+  f.v = *reinterpret_cast<const bf16x8*>(tile + c * 64 + 8 * swz64(c, 4 * kb + (lane_id() >> 4)));
+}
+// A 64 x 64 slice of a row-major bf16 [*, gld] matrix (rows beyond `rows` >= 1 zero),
+// staged by ONE wave into a transposed swizzled tile as above: lane l holds the 8 x 8 block
+// at rows 8 rb .., columns 8 cb .. with rb = (l / 4) % 8, cb = l % 4 + 4 (l / 32) (eight
+// 16-byte loads; the four lanes of a quad read 64 contiguous bytes of one row), transposes
+// it in registers and writes its eight columns as 16-byte words.
+struct WaveColTile {
+  u32x4 x[8];
+  int nrows;
+  __device__ __forceinline__ void load(const bf16* __restrict__ g, long gld, int rows) {
+    nrows = rows;
+    const int l = lane_id(), rb = (l >> 2) & 7, cb = (l & 3) + 4 * (l >> 5);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = load16_clamped(g, gld, 8 * rb + i, 8 * cb, rows);
+  }
+  __device__ __forceinline__ void store(bf16* lds) const {
+    const int l = lane_id(), rb = (l >> 2) & 7, cb = (l & 3) + 4 * (l >> 5);
+    // rows at or beyond nrows are zeroed after the transposition: word w of every column
+    // holds rows 2w and 2w + 1 of the block
+    uint32_t m[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      m[w] = (8 * rb + 2 * w < nrows ? 0x0000FFFFu : 0u) | (8 * rb + 2 * w + 1 < nrows ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // column 8 cb + e: word w holds rows 2w (low half) and 2w + 1 (high half), taken from
+      // the low (even e) or high (odd e) half of word e / 2 of those rows (v_perm_b32 byte
+      // selectors: 0-3 pick bytes of the second source, 4-7 of the first)
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 o;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(x[2 * w + 1][e / 2], x[2 * w][e / 2], sel) & m[w];
+      const int c = 8 * cb + e;
+      *reinterpret_cast<u32x4*>(lds + c * 64 + 8 * swz64(c, rb)) = o;
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------------
 // Transposing fragment reads (CDNA4 ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane i receives element i % 4 of the four 16-bit words addressed by lanes
 // i / 4 + 4e, e = 0..3 (checked on the device).  A tile kept in LDS in its global

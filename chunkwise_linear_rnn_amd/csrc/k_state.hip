@@ -57,12 +57,20 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
                                                             int dk, int dv, int N, int nsteps) {
   // TV value columns per workgroup: NJ accumulator tiles per wave, NY 64-column
   // value-side tiles per operand
-  constexpr int NJ = TV / 16, NY = TV / 64, YLD = C + 8, XW = SPLIT ? 2 * C : C;
+  constexpr int NJ = TV / 16, NY = TV / 64, XW = SPLIT ? 2 * C : C;
   static_assert(TV == 64 || (TV == 128 && STORE != 2), "[v][k] staging is 64 columns wide");
-  // state tile staging for 16-byte row stores: [v][k] (STORE 2) or [k][v]
-  constexpr int SLD = (STORE == 2 ? 64 : TV) + 8;
-  constexpr int SROWS = STORE == 2 ? TV : 64;
+  // WT: bf16, chunk 64 and four 64-column value-side tiles per chunk (two operands of 128
+  // columns): wave w stages tile w alone into unpadded swizzled tiles (conflict-free
+  // 16-byte writes and fragment reads); otherwise all threads stage every tile
+  constexpr bool WT = sizeof(OpT) == 2 && C == 64 && NY * (CROSS ? 2 : 1) == 4;
+  constexpr int YLD = WT ? 64 : C + 8;
   using StT = typename std::conditional<STORE == 3, float, OpT>::type;
+  // state tile staging for 16-byte row stores: [v][k] (STORE 2) or [k][v].  bf16 rows of
+  // 128 columns take a stride of 132: the 8-byte writes of 16 consecutive rows, and the
+  // 8-byte reads of two rows by 32 lanes, then fall on distinct banks.
+  constexpr bool SPAD4 = STORE == 1 && sizeof(StT) == 2 && TV == 128;
+  constexpr int SLD = STORE == 2 ? 64 + 8 : SPAD4 ? TV + 4 : TV + 8;
+  constexpr int SROWS = STORE == 2 ? TV : 64;
   using XR = XRegs<OpT, SPLIT, C>;
   __shared__ __attribute__((aligned(16))) OpT ys[TV * YLD];
   __shared__ __attribute__((aligned(16))) OpT y2s[CROSS ? TV * YLD : 8];
@@ -123,33 +131,45 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // transposed operands (straight into MFMA fragments), each set reloaded as soon as the
   // current chunk has consumed it.  DEPTH sets of registers keep DEPTH chunks in flight
   // (one set where the register budget of four workgroups per CU leaves no room).
-  constexpr int DEPTH = (TV == 128 || (!CROSS && C == 64 && sizeof(OpT) == 2)) ? 2 : 1;
+  constexpr int DEPTH = WT ? 1 : (TV == 128 || (!CROSS && C == 64 && sizeof(OpT) == 2)) ? 2 : 1;
   // bf16 value-side tiles are staged chunk-swizzled (conflict-free transposing stores)
   constexpr bool SWZ = sizeof(OpT) == 2;
   using YT = ColTile<OpT, Tin, C, YLD, kThreads, SWZ>;
-  struct Set {
+  struct SetAll {
     YT ty[NY], ty2[NY];
     XR cx, cx2;
   };
+  struct SetWave {   // the value-side tile is held once (below), one chunk ahead
+    XR cx, cx2;
+  };
+  using Set = typename std::conditional<WT, SetWave, SetAll>::type;
   Set sets[DEPTH];
+  WaveColTile ywt;
   auto yfrag = [&](Frag<OpT>& fb, const OpT* tile, int c, int kb) {
-    if constexpr (SWZ) load_frag_cs(fb, tile, YLD, c, kb);
+    if constexpr (WT) load_frag_x64(fb, tile, c, kb);
+    else if constexpr (SWZ) load_frag_cs(fb, tile, YLD, c, kb);
     else load_frag_c(fb, tile + c * YLD + kb * 32);
   };
+  // WT: wave w stages 64 columns at 64 (w % 2) of the first (w < 2) or second operand
+  const int wu = __builtin_amdgcn_readfirstlane(w), wh = wu & 1, wsec = wu >> 1;
   auto xrow = [&](int i) { return (((long)bh * N + i) * dk + k0 + 16 * w + r) * XW; };
   auto fetch_y = [&](Set& st, int i) {
     const int t0 = i * C, rows = min(C, T - t0);
+    if constexpr (WT) {
+      ywt.load((wsec ? Y2 : Y) + ((long)bh * T + t0) * dv + v0 + 64 * wh, dv, rows);
+    } else {
 #pragma unroll
-    for (int h = 0; h < NY; ++h) {
-      st.ty[h].load(Y + ((long)bh * T + t0) * dv + v0 + 64 * h, dv, rows);
-      if constexpr (CROSS) st.ty2[h].load(Y2 + ((long)bh * T + t0) * dv + v0 + 64 * h, dv, rows);
+      for (int h = 0; h < NY; ++h) {
+        st.ty[h].load(Y + ((long)bh * T + t0) * dv + v0 + 64 * h, dv, rows);
+        if constexpr (CROSS) st.ty2[h].load(Y2 + ((long)bh * T + t0) * dv + v0 + 64 * h, dv, rows);
+      }
     }
   };
   if (nsteps > 0) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int i0 = chunk_of(d);
-      fetch_y(sets[d], i0);
+      if (!WT || d == 0) fetch_y(sets[d], i0);
       sets[d].cx.load(XT + xrow(i0));
       if constexpr (CROSS) sets[d].cx2.load(X2T + xrow(i0));
     }
@@ -163,10 +183,14 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   auto body = [&](int step, Set& st) {
     const int i = chunk_of(step), ipre = chunk_of(step + DEPTH);
     const float egr = egs[(step % EB) * 64 + 16 * w + r];   // exp(gamma) of row krow
+    if constexpr (WT) {
+      ywt.store((wsec ? y2s : ys) + 64 * wh * YLD);
+    } else {
 #pragma unroll
-    for (int h = 0; h < NY; ++h) {
-      st.ty[h].store(ys + 64 * h * YLD);
-      if constexpr (CROSS) st.ty2[h].store(y2s + 64 * h * YLD);
+      for (int h = 0; h < NY; ++h) {
+        st.ty[h].store(ys + 64 * h * YLD);
+        if constexpr (CROSS) st.ty2[h].store(y2s + 64 * h * YLD);
+      }
     }
     if constexpr (STORE == 2) {
       // the state before this chunk, [v][k], through LDS
@@ -203,15 +227,22 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
         long off;
         if constexpr (STORE == 2) off = sb + (long)(v0 + a) * dk + k0 + b;
         else off = sb + (long)(k0 + a) * dv + v0 + b;
-        *reinterpret_cast<u32x4*>((StT*)states + off) =
-            *reinterpret_cast<const u32x4*>(ss + a * SLD + b);
+        u32x4 v;
+        if constexpr (SPAD4) {   // rows are 8-byte aligned only
+          const uint2* p = reinterpret_cast<const uint2*>(ss + a * SLD + b);
+          const uint2 p0 = p[0], p1 = p[1];
+          v = u32x4{p0.x, p0.y, p1.x, p1.y};
+        } else {
+          v = *reinterpret_cast<const u32x4*>(ss + a * SLD + b);
+        }
+        *reinterpret_cast<u32x4*>((StT*)states + off) = v;
       }
     }
     if constexpr (CROSS) {
       if (i_prev >= 0 && qd == 0)
         cross[(((long)bh * N + i_prev) * nvt + vt) * dk + krow] = part_prev;
     }
-    fetch_y(st, ipre);
+    fetch_y(st, WT ? chunk_of(step + 1) : ipre);
 
     if constexpr (CROSS) {
       // P_j = X2^T Y2 for column tile j (same layout as the state), folded into the row
