@@ -43,6 +43,10 @@ SMALL = [
     ("bf16_c128", "bf16", 1, 2, 333, 64, 128, 128, -3.0),
     ("bf16_dk192_slow", "bf16", 1, 1, 257, 192, 192, 64, 2.0),
     ("bf16_dk256", "bf16", 1, 1, 190, 256, 256, 128, 0.0),
+    # value width a multiple of 128 at chunk 64: the backward scans' 128-column tiles, with
+    # a ragged last chunk, and a sequence shorter than one chunk
+    ("bf16_c64_dv256", "bf16", 1, 2, 301, 128, 256, 64, 0.0),
+    ("bf16_short_dv128", "bf16", 1, 1, 37, 64, 128, 64, 0.0),
 ]
 
 
