@@ -309,11 +309,15 @@ using FlatTileRows = FlatTile<T, ROWS, COLS, LD>;
 
 // Position of element (column c, row r) of a transposed tile kept with the swizzle of
 // ColTile<..., SWZ = true>: each LDS row (one column c of the source) is made of 8-element
-// chunks, and chunk r / 8 sits at chunk (r / 8) ^ ((c / 8) & 6).  With LD = 72 (bf16) the
-// transposing stores of a wave then fall on distinct banks (64 banks of 4 bytes) instead
-// of four to a bank, and 16-byte fragment reads of 16 consecutive columns stay
-// conflict-free (the XOR is the same for all of them).
-__device__ __forceinline__ int swz_chunk(int c, int chunk) { return chunk ^ ((c >> 3) & 6); }
+// chunks, and chunk r / 8 sits at chunk (r / 8) ^ ((c / 8) % 8) ^ ((c / 4) % 2).  Banks as
+// measured on gfx950: 4-byte writes serve 32 lanes per cycle from 32 banks; 16-byte reads
+// serve 16 lanes per cycle from 64 banks (each half wave split by the parity of lane bits
+// 2..4).  With row strides of 72 (chunk 64) or 136 (chunk 128) bf16 elements, the
+// transposing 4-byte stores of ColTile (eight column blocks of a 2-row unit per 32 lanes)
+// and the 16-byte fragment reads of 16 consecutive rows both touch distinct banks.
+__device__ __forceinline__ int swz_chunk(int c, int chunk) {
+  return chunk ^ ((c >> 3) & 7) ^ ((c >> 2) & 1);
+}
 // Fragment read from such a tile: row `c`, elements 32 kb + 8 (lane / 16) .. + 7.
 __device__ __forceinline__ void load_frag_cs(Frag<bf16>& f, const bf16* tile, int LD, int c,
                                              int kb) {

@@ -89,7 +89,10 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
     Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N, int split,
     const float* __restrict__ S_mid) {
   constexpr int NT = kFusedThreads, TV = 64, NM = C / 16, KH = DK / 2, NP = KH / 16;
-  constexpr int QLD = DK + 8, KLD = C + 8, ALD = C + 8, VLD = C + 8, OLD = TV + 8, RLD = TV + 4;
+  // K^T and A rows padded to 80 elements: 16-byte fragment reads of 16 consecutive rows
+  // then fall on distinct banks (a stride of 72 pairs rows up on gfx950's 64 banks); the
+  // Qh rows are read as 8-byte halves, conflict-free at DK + 8
+  constexpr int QLD = DK + 8, KLD = C + 16, ALD = C + 16, VLD = C + 8, OLD = TV + 8, RLD = TV + 4;
   __shared__ __attribute__((aligned(16))) OpT qs[C * QLD];
   __shared__ __attribute__((aligned(16))) OpT ks[DK * KLD];
   __shared__ __attribute__((aligned(16))) OpT as_[C * ALD];
