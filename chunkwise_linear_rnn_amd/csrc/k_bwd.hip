@@ -233,7 +233,9 @@ __device__ __forceinline__ void bwd_dqk_body(
     GateFn gf, Tin* __restrict__ dla, float* __restrict__ dla_part, int T, int dk, int dv,
     int N) {
   static_assert(sizeof(Tin) == sizeof(OpT), "input and operand types match");
-  constexpr int C = 64, NM = 4, NS = C / 16, YLD = 64 + 8;
+  // dO / V rows padded to 80: their 16-byte fragment reads (16 consecutive rows) then fall
+  // on distinct banks
+  constexpr int C = 64, NM = 4, NS = C / 16, YLD = 64 + 16;
   constexpr int FLD = C + 4, GLD = 64 + 4, XLD = 64 + 8;
   // LDS: dA [C][FLD] fp32, then a region that holds the dO / V tiles during the dv loop
   // and g [C][GLD] fp32, q, k [C][XLD] afterwards.  53248 bytes: three workgroups per CU.
@@ -540,10 +542,12 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
                                             const Tin* __restrict__ dO,
                                             Tin* __restrict__ dv_out, int T, int dk, int dv,
                                             int N) {
-  constexpr int C = 64, NM = 4, LD = 64 + 8;
-  static_assert(4 * 64 * LD * 2 <= kDqkLds, "the dv tiles fit the shared arena");
+  // the Kh block is read row-major (rows padded to 80 for conflict-free fragment reads),
+  // the transposed tiles through the swizzle of ColTile (rows of 72)
+  constexpr int C = 64, NM = 4, LD = 64 + 8, KLD = 64 + 16;
+  static_assert(C * KLD * 2 + 3 * 64 * LD * 2 <= kDqkLds, "the dv tiles fit the shared arena");
   OpT* ksh = (OpT*)arena;        // Kh block [t][k]
-  OpT* dsT = ksh + C * LD;       // dS block transposed [v][k]
+  OpT* dsT = ksh + C * KLD;      // dS block transposed [v][k]
   OpT* aT = dsT + 64 * LD;       // A^T [t][s]
   OpT* doT = aT + C * LD;        // dO^T [v][t]
   // the dv tiles of one chunk share Kh and A (consecutive logical ids)
@@ -553,7 +557,7 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
   const int w = wave_id(), l = lane_id(), r = l & 15;
   const OpT* Khc = Kh + ((long)bh * N * C + t0) * dk;
   const OpT* dSc = dS + ((long)bh * N + i) * dk * dv + v0;
-  RowTile<OpT, C, 64, LD> tk;
+  RowTile<OpT, C, 64, KLD> tk;
   // transposed tiles are staged chunk-swizzled (conflict-free stores)
   ColTile<OpT, OpT, 64, LD, kThreads, true> ts;
   {
@@ -597,7 +601,7 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         Frag<OpT> fa;
-        load_frag_c(fa, ksh + (16 * m + r) * LD + kb * 32);
+        load_frag_c(fa, ksh + (16 * m + r) * KLD + kb * 32);
         mma(acc[m], fa, fb);
       }
     }
@@ -608,7 +612,7 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
       __syncthreads();
     }
   }
-  Tin* outs = (Tin*)ksh;   // [C][LD]
+  Tin* outs = (Tin*)ksh;   // [C][LD], inside the Kh block's space
   const int qd = l >> 4;
 #pragma unroll
   for (int m = 0; m < NM; ++m)
