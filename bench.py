@@ -72,9 +72,11 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
             byt = 3 * tok * dk * e + 2 * tokp * dk * e + BH * N * C * C * e + BH * N * dk * 4
             if mode == "materialized":
                 byt += tok * dk * (4 - e)  # reads fp32 g instead of log_alpha
-        else:   # reads log_alpha, q, k; writes g (fp32), A, Qh^T, Kh^T (fp32), Kh, e^gamma
-            byt = (3 * tok * dk * e + tok * dk * 4 + BH * N * C * C * e + 2 * tokp * dk * 4
-                   + tokp * dk * e + BH * N * dk * 4)
+        else:   # reads log_alpha, q, k; writes A, Qh^T, Kh^T (fp32), Kh, e^gamma, and g (fp32)
+            # for the single-kernel chunk backward (bf16 at chunk 64 rebuilds g itself)
+            split = e == 2 and C == 64
+            byt = (3 * tok * dk * e + (0 if split else tok * dk * 4) + BH * N * C * C * e
+                   + 2 * tokp * dk * 4 + tokp * dk * e + BH * N * dk * 4)
         return byt, tok * C * dk
     if stage in ("state_scan_fwd", "state_scan_rev", "state_scans"):
         # one scan: reads Kh^T and Qh^T (fp32 as bf16 pairs), v and dO; writes the states
@@ -97,8 +99,8 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
                + 2 * st + tok * (2 * dk * e + dv * e + dk * 4))
         return byt, tok * (6 * dk * dv + C * (2 * dk + 2 * dv))
     if stage == "bwd_dqk_dv":
-        # dq/dk part: reads q, k, v, dO, g, S, dS, chunk totals; writes dq, dk, dla
-        byt = (tok * (2 * dk * e + 2 * dv * e + dk * 4) + 2 * st + BH * N * dk * 4
+        # dq/dk part: reads q, k, v, dO, log_alpha, S, dS, chunk totals; writes dq, dk, dla
+        byt = (tok * (2 * dk * e + 2 * dv * e + dk * e) + 2 * st + BH * N * dk * 4
                + tok * 3 * dk * e)
         fl = tok * (4 * dk * dv + C * dv + 2 * C * dk)
         # dv part: reads Kh, A, dS, dO; writes dv

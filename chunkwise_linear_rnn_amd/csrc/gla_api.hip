@@ -76,7 +76,8 @@ Plan plan_of(const gla_desc_t* d, int pass) {
     // the scans' transposed operands are kept in fp32 (split into two bf16 halves)
     const size_t op32 = rowsP * x.dk * 4;
     const size_t crossB = (size_t)x.BH * x.N * (x.dv / 64) * x.dk * 4;
-    p.g = take(gB);
+    // g for the single-kernel chunk backward (the split path rebuilds it from the gates)
+    if (!gla::bwd_split(x.dtype, (int)x.C)) p.g = take(gB);
     p.A = take(AB);
     p.QhT = take(op32);
     p.Kh = take(opB);
@@ -379,7 +380,9 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   gla::IntraArgs ia{};
   ia.dtype = x.dtype; ia.C = C; ia.BH = BH; ia.T = T; ia.dk = DK; ia.N = N; ia.want_A = true;
   ia.xt_f32 = x.dtype == GLA_BF16;
-  ia.q = q; ia.k = k; ia.la = log_alpha; ia.g = nullptr; ia.g2_out = (float*)(w + p.g);
+  const bool split = gla::bwd_split(x.dtype, C);
+  ia.q = q; ia.k = k; ia.la = log_alpha; ia.g = nullptr;
+  ia.g2_out = split ? nullptr : (float*)(w + p.g);
   ia.gate = gate_of(d); ia.gscalar = scalar_gate(d);
   ia.A = w + p.A; ia.QhT = w + p.QhT; ia.Kh = w + p.Kh; ia.KhT = w + p.KhT;
   ia.eg = (float*)(w + p.eg);
@@ -409,19 +412,19 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   }
   gla::BwdArgs ba{};
   ba.dtype = x.dtype; ba.C = C; ba.BH = BH; ba.T = T; ba.dk = DK; ba.dv = DV; ba.N = N;
-  ba.q = q; ba.k = k; ba.v = v; ba.dO = dO; ba.g = (const float*)(w + p.g); ba.gamma = nullptr;
+  ba.q = q; ba.k = k; ba.v = v; ba.dO = dO; ba.gamma = nullptr;
+  ba.g = split ? nullptr : (const float*)(w + p.g);
+  ba.gscalar = scalar_gate(d);
   ba.A = w + p.A; ba.Kh = w + p.Kh; ba.S = w + p.st; ba.dS = w + p.dst;
   ba.dq = dq; ba.dk_out = dk; ba.dv_out = dv;
   ba.Dloc = p.Dloc ? (float*)(w + p.Dloc) : nullptr;
   ba.tot = (const float*)(w + p.carry); ba.cT = dS_T ? (const float*)(w + p.cT) : nullptr;
   ba.dla = dlog_alpha; ba.la = log_alpha; ba.gate = gate_of(d);
   // scalar gates: the per-key gradient is summed over the key dimension afterwards, and
-  // the front-end slope (one per token) applied there
+  // the front-end slope (one per token) applied there (the chunk kernel writes partial
+  // sums without it; it still takes the gate function, to rebuild g from the gates)
   const bool sg = scalar_gate(d);
-  if (sg) {
-    ba.gate = gla::GateFn{0, 1.f};
-    ba.dla_part = p.dpart ? (float*)(w + p.dpart) : nullptr;
-  }
+  if (sg) ba.dla_part = p.dpart ? (float*)(w + p.dpart) : nullptr;
   auto reduce = [&](const float* part, int nparts) {
     return dev(gla::launch_gate_reduce(x.dtype, part, nparts, log_alpha, gate_of(d), dlog_alpha,
                                        (long)BH * T, s));

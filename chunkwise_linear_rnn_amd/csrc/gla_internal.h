@@ -123,7 +123,8 @@ hipError_t launch_fwd_fused(const FusedArgs& a, hipStream_t s);
 struct BwdArgs {
   int dtype, C, BH, T, dk, dv, N;
   const void *q, *k, *v, *dO;
-  const float *g, *gamma;   // g: g * log2(e) [BH][T][dk] (from the intra-chunk kernel)
+  const float *g, *gamma;   // g: g * log2(e) [BH][T][dk] (from the intra-chunk kernel; the
+                            // split path rebuilds it from la and does not read it)
   const void *A, *Kh, *S, *dS;
   void *dq, *dk_out, *dv_out;
   float* Dloc;             // chunk-local suffix sums of D (single-kernel path)
@@ -133,6 +134,7 @@ struct BwdArgs {
   GateFn gate;
   float* dla_part;         // scalar gates (split path): fp32 sums of the per-(t, d) gradient
                            // over each 64-wide d block, [BH][T][dk/64], instead of dla
+  bool gscalar;            // la holds one gate per token: [BH][T]
 };
 // The backward chunk work (launch_bwd_chunk): with bf16 operands and chunk 64 one launch of
 // dq / dk / dlog_alpha workgroups (after the chunk totals are formed) interleaved with dv

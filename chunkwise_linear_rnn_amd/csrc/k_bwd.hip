@@ -35,6 +35,7 @@
 //   k_bwd_chunk (chunk 128, and fp32 operands) all of the above in one workgroup per
 //              chunk, operands read straight from memory.
 #include "gla_common.cuh"
+#include "gla_gate.cuh"
 #include "gla_internal.h"
 
 namespace gla {
@@ -227,7 +228,7 @@ constexpr int kDqkLds = 64 * (64 + 4) * 4 + 64 * (64 + 4) * 4 + 2 * 64 * (64 + 8
 template <typename Tin, typename OpT>
 __device__ __forceinline__ void bwd_dqk_body(
     char* __restrict__ arena, int lt, const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
-    const Tin* __restrict__ dO, const float* __restrict__ g, const OpT* __restrict__ S,
+    const Tin* __restrict__ dO, int gscalar, const OpT* __restrict__ S,
     const OpT* __restrict__ dS, Tin* __restrict__ dq, Tin* __restrict__ dk_out,
     const float* __restrict__ tot, const float* __restrict__ cT, const Tin* __restrict__ la,
     GateFn gf, Tin* __restrict__ dla, float* __restrict__ dla_part, int T, int dk, int dv,
@@ -340,17 +341,20 @@ __device__ __forceinline__ void bwd_dqk_body(
         dAs[(16 * w + tl) * FLD + 16 * n + r] = (n == w && r > tl) ? 0.f : adA[n][e];
       }
     }
-  // g (times log2 e; rows past T continue the last valid row), q, k of the block
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int idx = threadIdx.x + kThreads * u, rr = idx / 16, cc = (idx % 16) * 4;
-    *reinterpret_cast<f32x4*>(gs + rr * GLD + cc) =
-        *reinterpret_cast<const f32x4*>(g + (tok0 + min(rr, rows - 1)) * dk + d0 + cc);
-  }
+  // g * log2 e of the block (rows past T continue the last valid row), rebuilt from the
+  // gate operand with the intra-chunk kernel's staging and column cumsum (the same bits),
+  // then q, k of the block; the k tile's space holds the cumsum's segment totals first
   {
+    GBlock<Tin, C, 64> pg;
+    if (gscalar) pg.load_scalar(la + tok0, rows);
+    else pg.load(la + tok0 * dk + d0, dk, rows, false);
     RowTile<Tin, C, 64, XLD> tq, tk;
     tq.load(q + tok0 * dk + d0, dk, rows);
     tk.load(k + tok0 * dk + d0, dk, rows);
+    pg.store(gs, GLD, gf);
+    __syncthreads();
+    chunk_cumsum_cols<C, 64>(gs, GLD, reinterpret_cast<float*>(ks));
+    __syncthreads();
     tq.store(qs);
     tk.store(ks);
   }
@@ -789,7 +793,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(
 template <typename Tin, typename OpT>
 __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk_dv(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
-    const Tin* __restrict__ dO, const float* __restrict__ g, const OpT* __restrict__ S,
+    const Tin* __restrict__ dO, int gscalar, const OpT* __restrict__ S,
     const OpT* __restrict__ dS, Tin* __restrict__ dq, Tin* __restrict__ dk_out,
     const float* __restrict__ tot, const float* __restrict__ cT, const Tin* __restrict__ la,
     GateFn gf, Tin* __restrict__ dla, float* __restrict__ dla_part, const OpT* __restrict__ Kh,
@@ -801,7 +805,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk_dv(
   // Bresenham split: logical id L is a dq/dk workgroup when the count of them up to L grows
   const int before = (int)(((long)L * n_dqk) / total), upto = (int)(((long)(L + 1) * n_dqk) / total);
   if (upto > before)
-    bwd_dqk_body<Tin, OpT>(arena, before, q, k, v, dO, g, S, dS, dq, dk_out, tot, cT, la, gf,
+    bwd_dqk_body<Tin, OpT>(arena, before, q, k, v, dO, gscalar, S, dS, dq, dk_out, tot, cT, la, gf,
                            dla, dla_part, T, dk, dv, N);
   else
     bwd_dv_body<Tin, OpT>(arena, L - before, Kh, A, dS, dO, dv_out, T, dk, dv, N);
@@ -813,8 +817,9 @@ static hipError_t launch_bwd_t2(const BwdArgs& a, hipStream_t s) {
   if constexpr (C == 64 && sizeof(OpT) == 2) {
     const int n_dqk = (a.dk / 64) * a.N * a.BH, n_dv = (a.dv / 64) * a.N * a.BH;
     hipLaunchKernelGGL((k_bwd_dqk_dv<Tin, OpT>), dim3(n_dqk + n_dv), dim3(kThreads), 0, s,
-                       (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,
-                       (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq, (Tin*)a.dk_out, a.tot, a.cT,
+                       (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO,
+                       a.gscalar ? 1 : 0, (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq,
+                       (Tin*)a.dk_out, a.tot, a.cT,
                        (const Tin*)a.la, a.gate, (Tin*)a.dla, a.dla_part, (const OpT*)a.Kh,
                        (const OpT*)a.A, (Tin*)a.dv_out, a.T, a.dk, a.dv, a.N, n_dqk);
   } else {

@@ -24,6 +24,7 @@
 #include <type_traits>
 
 #include "gla_common.cuh"
+#include "gla_gate.cuh"
 #include "gla_internal.h"
 
 namespace gla {
@@ -44,69 +45,6 @@ __device__ __forceinline__ void pair_decode(int p, int& I, int& J) {
   I = ii;
   J = p - ii * (ii - 1) / 2;
 }
-
-// A C x DB block of g (fp32) or log_alpha (SrcT) in registers as 16-byte units, written to
-// LDS as fp32 times log2 e (through the gate front-end).  Rows at and past `rows`: the last
-// valid row repeated (clamp) or zero (after the front-end too, so padded rows never
-// decay the chunk).
-template <typename SrcT, int C, int DB>
-struct GBlock {
-  static constexpr int kPer = 16 / (int)sizeof(SrcT), kUnitsRow = DB / kPer;
-  static constexpr int kUnits = C * kUnitsRow, kPerThread = kUnits / kThreads;
-  static_assert(kUnits % kThreads == 0, "whole units per thread");
-  u32x4 u[kPerThread];
-  int zero_from;   // first row stored as zero
-  __device__ __forceinline__ void load(const SrcT* __restrict__ src, long ld, int rows, bool clamp) {
-    zero_from = clamp ? 1 << 30 : rows;
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int idx = threadIdx.x + j * kThreads, rr = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
-      // always a load (of the last valid row past `rows`): no branch around it, and the
-      // rows past `rows` are zeroed at store time when not clamped
-      u[j] = *reinterpret_cast<const u32x4*>(src + (long)min(rr, rows - 1) * ld + c);
-    }
-  }
-  // one gate per row, src[row] (rows past `rows` zero), the same for every column
-  __device__ __forceinline__ void load_scalar(const SrcT* __restrict__ src, int rows) {
-    zero_from = rows;
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int idx = threadIdx.x + j * kThreads, rr = idx / kUnitsRow;
-      const SrcT x = src[min(rr, rows - 1)];
-      uint32_t wd;
-      if constexpr (sizeof(SrcT) == 2) {
-        const uint32_t b = __builtin_bit_cast(uint16_t, x);
-        wd = b | (b << 16);
-      } else {
-        wd = __builtin_bit_cast(uint32_t, x);
-      }
-      u[j] = u32x4{wd, wd, wd, wd};
-    }
-  }
-  __device__ __forceinline__ void store(float* gs, int gld, GateFn gf) const {
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int idx = threadIdx.x + j * kThreads, rr = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
-      const bool keep = rr < zero_from;
-      if constexpr (sizeof(SrcT) == 2) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, u[j]);
-        f32x4 lo, hi;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lo[e] = keep ? gf((float)b[e]) * kLog2e : 0.f;
-          hi[e] = keep ? gf((float)b[4 + e]) * kLog2e : 0.f;
-        }
-        *reinterpret_cast<f32x4*>(gs + rr * gld + c) = lo;
-        *reinterpret_cast<f32x4*>(gs + rr * gld + c + 4) = hi;
-      } else {
-        f32x4 f = __builtin_bit_cast(f32x4, u[j]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = keep ? gf(f[e]) * kLog2e : 0.f;
-        *reinterpret_cast<f32x4*>(gs + rr * gld + c) = f;
-      }
-    }
-  }
-};
 
 template <typename Tin, typename OpT, typename XT, int C, bool G_WS, bool WANT_A, bool SG>
 __global__ __launch_bounds__(kThreads) void k_intra(
@@ -171,22 +109,9 @@ __global__ __launch_bounds__(kThreads) void k_intra(
     tk.store(ks);
     fetch(min(d0 + DB, dk - DB));   // unconditional (exact wait counts); the last refetches
     if constexpr (!G_WS) {
-      // chunk-local cumsum down each column: four 16-row segments per column, each
-      // summed in registers, then offset by the totals of the segments above it
+      // chunk-local cumsum down each column
       __syncthreads();
-      constexpr int L = C / 4;
-      const int col = threadIdx.x % DB, seg = threadIdx.x / DB;
-      float run[L];
-#pragma unroll
-      for (int rr = 0; rr < L; ++rr) run[rr] = gs[(seg * L + rr) * GLD + col];
-#pragma unroll
-      for (int rr = 1; rr < L; ++rr) run[rr] += run[rr - 1];
-      segtot[seg * DB + col] = run[L - 1];
-      __syncthreads();
-      float off = 0.f;
-      for (int s2 = 0; s2 < seg; ++s2) off += segtot[s2 * DB + col];
-#pragma unroll
-      for (int rr = 0; rr < L; ++rr) gs[(seg * L + rr) * GLD + col] = run[rr] + off;
+      chunk_cumsum_cols<C, DB>(gs, GLD, segtot);
     }
     __syncthreads();
     if (g2_out) {   // g * log2 e for the backward chunk kernel

@@ -52,7 +52,7 @@ def source_digest(stage: str, root: str) -> str:
     """sha256 over the stage's kernel source and the shared device headers it includes."""
     h = hashlib.sha256()
     csrc = os.path.join(root, "chunkwise_linear_rnn_amd", "csrc")
-    for f in (STAGE_SOURCE[stage], "gla_common.cuh", "gla_internal.h"):
+    for f in (STAGE_SOURCE[stage], "gla_common.cuh", "gla_gate.cuh", "gla_internal.h"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
 
