@@ -262,19 +262,6 @@ __device__ __forceinline__ void bwd_dqk_body(
   const OpT* dSi = dS + ((long)bh * N + i) * dk * dv;
   const int NV = dv / 64;
 
-  // gate gradient carried into this chunk for column c: the chunk totals of D over the
-  // later chunks (lane group qd takes every fourth chunk), plus c_T
-  // (eight chunk totals per lane in flight at once; out-of-range ones read a valid entry
-  // and are dropped)
-  float carry = 0.f;
-  for (int j0 = i + 1 + qd; j0 < N; j0 += 32) {
-    float tv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) tv[u] = tot[((long)bh * N + min(j0 + 4 * u, N - 1)) * dk + d0 + c];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) carry += j0 + 4 * u < N ? tv[u] : 0.f;
-  }
-
   f32x4 adq[NM], adk[NM], adA[NM];   // adA[n] = dA tile (w, n), n <= w
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
@@ -323,6 +310,18 @@ __device__ __forceinline__ void bwd_dqk_body(
     __syncthreads();
   };
   fetch(0, sA, dsA);
+  // gate gradient carried into this chunk for column c: the chunk totals of D over the
+  // later chunks (lane group qd takes every fourth chunk), plus c_T (eight chunk totals
+  // per lane in flight at once; out-of-range ones read a valid entry and are dropped).
+  // Loaded after the first block's operands, so that both round trips overlap.
+  float carry = 0.f;
+  for (int j0 = i + 1 + qd; j0 < N; j0 += 32) {
+    float tv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) tv[u] = tot[((long)bh * N + min(j0 + 4 * u, N - 1)) * dk + d0 + c];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) carry += j0 + 4 * u < N ? tv[u] : 0.f;
+  }
   int vb = 0;
   for (; vb + 1 < NV; vb += 2) {
     body(vb, sA, dsA, sB, dsB);
