@@ -329,20 +329,11 @@ __device__ __forceinline__ void bwd_dqk_body(
   }
   if (vb < NV) body(vb, sA, dsA, sB, dsB);
 
-  // dA tiles (w, n <= w) to LDS, the diagonal tile masked above the diagonal; the
-  // block's g, q, k into the region the dO / V tiles used
-#pragma unroll
-  for (int n = 0; n < NM; ++n)
-    if (n <= w) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tl = 4 * qd + e;
-        dAs[(16 * w + tl) * FLD + 16 * n + r] = (n == w && r > tl) ? 0.f : adA[n][e];
-      }
-    }
   // g * log2 e of the block (rows past T continue the last valid row), rebuilt from the
   // gate operand with the intra-chunk kernel's staging and column cumsum (the same bits),
-  // then q, k of the block; the k tile's space holds the cumsum's segment totals first
+  // then q, k of the block, into the region the dO / V tiles used; the k tile's space
+  // holds the cumsum's segment totals first.  Their loads are issued before the dA tiles
+  // (w, n <= w; the diagonal tile masked above the diagonal) go to LDS.
   {
     GBlock<Tin, C, 64> pg;
     if (gscalar) pg.load_scalar(la + tok0, rows);
@@ -350,6 +341,15 @@ __device__ __forceinline__ void bwd_dqk_body(
     RowTile<Tin, C, 64, XLD> tq, tk;
     tq.load(q + tok0 * dk + d0, dk, rows);
     tk.load(k + tok0 * dk + d0, dk, rows);
+#pragma unroll
+    for (int n = 0; n < NM; ++n)
+      if (n <= w) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tl = 4 * qd + e;
+          dAs[(16 * w + tl) * FLD + 16 * n + r] = (n == w && r > tl) ? 0.f : adA[n][e];
+        }
+      }
     pg.store(gs, GLD, gf);
     __syncthreads();
     chunk_cumsum_cols<C, 64>(gs, GLD, reinterpret_cast<float*>(ks));
