@@ -235,7 +235,9 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
         } else {
           v = *reinterpret_cast<const u32x4*>(ss + a * SLD + b);
         }
-        *reinterpret_cast<u32x4*>((StT*)states + off) = v;
+        // written once, read by a later kernel: a streaming store, so that the tiles
+        // the neighbouring workgroups share stay in L2
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>((StT*)states + off));
       }
     }
     if constexpr (CROSS) {
