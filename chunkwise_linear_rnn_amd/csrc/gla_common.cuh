@@ -24,6 +24,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kThreads = 256;   // 4 waves per workgroup everywhere
@@ -134,6 +135,25 @@ __device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
   reinterpret_cast<f32x4*>(p)[0] = a;
   reinterpret_cast<f32x4*>(p)[1] = b;
 }
+// Streaming (nontemporal) 16-byte stores, for outputs written once and read only by a
+// later kernel: they do not hold L2 lines that the workgroups still share.
+template <typename T>
+__device__ __forceinline__ void stream16(T* p, const u32x4& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void stream8(bf16* p, const float (&x)[8]) {
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (bf16)x[e];
+  stream16(p, __builtin_bit_cast(u32x4, v));
+}
+__device__ __forceinline__ void stream8(float* p, const float (&x)[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { a[e] = x[e]; b[e] = x[4 + e]; }
+  stream16(p, __builtin_bit_cast(u32x4, a));
+  stream16(p + 4, __builtin_bit_cast(u32x4, b));
+}
 __device__ __forceinline__ void zero8(float (&x)[8]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) x[e] = 0.f;
@@ -214,7 +234,6 @@ __device__ __forceinline__ void mma_split(f32x4& acc, const SFrag<OpT>& a, const
 // the next chunk's loads are in flight while the current chunk computes.  NT is the
 // workgroup size (all of its threads take part).
 // ---------------------------------------------------------------------------------
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // A contiguous global tile of ROWS x COLS elements (row-major, COLS contiguous) moved as
 // 16-byte units into an LDS tile with row stride LD (elements).

@@ -523,8 +523,8 @@ __device__ __forceinline__ void bwd_dqk_body(
     const int rr = u / kRowUnits, cc = (u % kRowUnits) * kPer;
     Tin* dst = tile == 0 ? dq : (tile == 1 ? dk_out : dla);
     if (tile < ntile_out && rr < rows)
-      *reinterpret_cast<u32x4*>(dst + (tok0 + rr) * dk + d0 + cc) =
-          *reinterpret_cast<const u32x4*>(st + (tile * C + rr) * SLD + cc);
+      stream16(dst + (tok0 + rr) * dk + d0 + cc,
+               *reinterpret_cast<const u32x4*>(st + (tile * C + rr) * SLD + cc));
   }
   if (dla_part && threadIdx.x < rows) {
     const int t = threadIdx.x;
@@ -627,8 +627,8 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
   for (int idx = threadIdx.x; idx < kUnits; idx += kThreads) {
     const int e0 = idx * kPer, rr = e0 / 64, cc = e0 % 64;
     if (rr < rows)
-      *reinterpret_cast<u32x4*>(dv_out + ((long)bh * T + t0 + rr) * dv + v0 + cc) =
-          *reinterpret_cast<const u32x4*>(outs + rr * LD + cc);
+      stream16(dv_out + ((long)bh * T + t0 + rr) * dv + v0 + cc,
+               *reinterpret_cast<const u32x4*>(outs + rr * LD + cc));
   }
 }
 

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(
           float x[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = gs[rr * GLD + c + e];
-          store8(g2_out + in_base + (long)rr * dk + d0 + c, x);
+          stream8(g2_out + in_base + (long)rr * dk + d0 + c, x);
         }
       }
     }
@@ -145,14 +145,14 @@ __global__ __launch_bounds__(kThreads) void k_intra(
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             x[e] = to_f32(qs[rr * XLD + c + e]) * __builtin_amdgcn_exp2f(gs[rr * GLD + c + e]);
-          store8(Qh_out + o, x);
+          store8(Qh_out + o, x);   // re-read at once by the fused forward: kept cacheable
         }
         if (Kh_out) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             x[e] = to_f32(ks[rr * XLD + c + e]) *
                    __builtin_amdgcn_exp2f(glast[c + e] - gs[rr * GLD + c + e]);
-          store8(Kh_out + o, x);
+          stream8(Kh_out + o, x);
         }
       }
     }
