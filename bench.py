@@ -103,8 +103,9 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
         byt = (tok * (2 * dk * e + 2 * dv * e + dk * e) + 2 * st + BH * N * dk * 4
                + tok * 3 * dk * e)
         fl = tok * (4 * dk * dv + C * dv + 2 * C * dk)
-        # dv part: reads Kh, A, dS, dO; writes dv
-        byt += tokp * dk * e + BH * N * C * C * e + st + 2 * tok * dv * e
+        # dv part: reads Kh, A (dS and dO are the dq/dk part's, read once by the launch);
+        # writes dv
+        byt += tokp * dk * e + BH * N * C * C * e + tok * dv * e
         fl += tok * (2 * dk * dv + C * dv)
         return byt, fl
     if stage == "gate_tot":
