@@ -131,7 +131,7 @@ gla_status_t state_copy(const float* src, float* dst, long n, hipStream_t s) {
 }
 
 // Records caller-provided events between kernel launches (profiling); inert when the
-// caller passes none.
+// caller passes none, and a NULL entry skips its boundary.
 struct Tracer {
   void** ev;
   int n;
@@ -140,7 +140,8 @@ struct Tracer {
   gla_status_t mark() {
     if (!ev) return GLA_OK;
     if (k >= n) return GLA_ERR_INVALID_ARG;
-    return dev(hipEventRecord((hipEvent_t)ev[k++], s));
+    void* e = ev[k++];
+    return e ? dev(hipEventRecord((hipEvent_t)e, s)) : GLA_OK;
   }
 };
 

@@ -213,8 +213,10 @@ gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* desc, const void* q, const void* 
  * gla_chunk_fwd / gla_chunk_bwd and additionally record caller-created hipEvent_t
  * handles on `stream`: events[j] right before the j-th kernel launch and events[n] after
  * the last, where n is the stage count from gla_trace_stages (events == NULL records
- * nothing).  The elapsed time between events[j] and events[j+1] is the duration of stage
- * j.  n_events smaller than n + 1 is GLA_ERR_INVALID_ARG (checked before any launch).
+ * nothing; a NULL entry records nothing at its boundary, so two events time one stage
+ * with the least disturbance).  The elapsed time between events[j] and events[j+1] is the
+ * duration of stage j.  n_events smaller than n + 1 is GLA_ERR_INVALID_ARG (checked
+ * before any launch).
  *
  * gla_trace_stages returns n for a pass (with_dS_T: whether the backward gets a dS_T) and
  * writes up to max_names static stage names to `names` (nullable); -1 on a NULL desc or a
