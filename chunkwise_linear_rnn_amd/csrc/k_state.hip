@@ -2,18 +2,21 @@
 // Linear Attention Transformers with Hardware-Efficient Training", atlas.scime.ai
 // summary, section Approach: materialized inter-chunk states).
 //
-// One workgroup owns a 64 x 64 fp32 tile (dk rows x dv columns) of one (batch, head)
-// state and walks the chunks in order (forward) or in reverse (the state gradient):
+// One workgroup owns a 64 x TV fp32 tile (dk rows x dv columns, TV = 64, or 128 in the
+// backward at chunk 64) of one (batch, head) state and walks the chunks in order
+// (forward) or in reverse (the state gradient):
 //     forward:  S_[i+1]  = diag(exp(gamma_i)) S_[i]    + Kh_i^T V_i,   Kh = k*exp(gamma-g)
 //     reverse:  dS_[i]   = diag(exp(gamma_i)) dS_[i+1] + Qh_i^T dO_i,  Qh = q*exp(g)
 // Before each chunk the tile is written out (the chunk-start state S_[i], or dS_[i+1]).
 // The product is a k32 MFMA over the chunk's tokens: the transposed decayed operand
 // comes ready-made from the intra-chunk kernel and each wave loads its own rows of it
 // straight into MFMA fragments; the value-side tile, shared by the four waves, is staged
-// into LDS transposed so both operands are token-contiguous.  The tile stays in fp32 accumulators
-// across the whole sequence.  In the backward the transposed operand arrives as a bf16
-// high part plus bf16 remainder (two MFMAs), so the state carries no operand rounding;
-// the kernel is bound by the state writes, not by the matrix units.
+// into LDS transposed so both operands are token-contiguous.  The tile stays in fp32
+// accumulators across the whole sequence; the per-row decays of 32 steps at a time wait
+// in LDS.  In the backward the transposed operand arrives as a bf16 high part plus bf16
+// remainder (two MFMAs), so the state carries no operand rounding.  The states leave
+// through LDS as 16-byte streaming stores (they are read only by a later kernel); the
+// kernel is bound by memory traffic and LDS staging, not by the matrix units.
 //
 // Chunk totals of the closed-form gate gradient (optional cross term): summed over one
 // chunk, the intra-chunk parts of q*dq - k*dk cancel pairwise, so the chunk total is
@@ -130,7 +133,9 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // computes: the value-side tiles (then LDS, transposed) and this wave's rows of the
   // transposed operands (straight into MFMA fragments), each set reloaded as soon as the
   // current chunk has consumed it.  DEPTH sets of registers keep DEPTH chunks in flight
-  // (one set where the register budget of four workgroups per CU leaves no room).
+  // (one set where the register budget of four workgroups per CU leaves no room, and on
+  // the WT path, where the registers freed let the compiler keep several fragment reads
+  // in flight: measured faster than two chunks ahead).
   constexpr int DEPTH = WT ? 1 : (TV == 128 || (!CROSS && C == 64 && sizeof(OpT) == 2)) ? 2 : 1;
   // bf16 value-side tiles are staged chunk-swizzled (conflict-free transposing stores)
   constexpr bool SWZ = sizeof(OpT) == 2;

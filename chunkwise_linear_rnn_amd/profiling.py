@@ -48,12 +48,20 @@ def matches(stage: str, name: str) -> bool:
     return keys is None or any(k in name for k in keys)
 
 
+def code_text(src: str) -> bytes:
+    """The source with comments removed and whitespace collapsed: what the compiler sees."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return " ".join(src.split()).encode()
+
+
 def source_digest(stage: str, root: str) -> str:
-    """sha256 over the stage's kernel source and the shared device headers it includes."""
+    """sha256 over the code (comments aside) of the stage's kernel source and the shared
+    device headers it includes."""
     h = hashlib.sha256()
     csrc = os.path.join(root, "chunkwise_linear_rnn_amd", "csrc")
     for f in (STAGE_SOURCE[stage], "gla_common.cuh", "gla_gate.cuh", "gla_internal.h"):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        h.update(code_text(open(os.path.join(csrc, f)).read()))
     return h.hexdigest()
 
 
