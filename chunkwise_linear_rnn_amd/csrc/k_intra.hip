@@ -185,7 +185,12 @@ __global__ __launch_bounds__(kThreads) void k_intra(
                      __builtin_amdgcn_exp2f(glast[c] - gs[(r8 + e) * GLD + c]);
           }
           if constexpr (kSplit) {
-            bf16* b = reinterpret_cast<bf16*>(dst) + rowi * 2 * C + r8;
+            // fragment order (the backward scans' MFMA operand): for 16-row block d / 16
+            // and 32-token block kb of this chunk, the 64 lanes' 16-byte pieces of the high
+            // part, then of the remainder; this piece belongs to lane 16 qd + d % 16
+            const int d = d0 + c, j = r8 / 8, kb = j / 4, qd = j % 4;
+            const long f = (((long)bh * N + i) * (dk / 16) + d / 16) * (C / 32) + kb;
+            bf16* b = reinterpret_cast<bf16*>(dst) + ((f * 2) * 64 + 16 * qd + d % 16) * 8;
             float lo[8];
             bf16x8 hv;
 #pragma unroll
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(
               lo[e] = x[e] - (float)hv[e];
             }
             *reinterpret_cast<bf16x8*>(b) = hv;
-            store8(b + C, lo);
+            store8(b + 64 * 8, lo);
           } else {
             store8(dst + rowi * C + r8, x);
           }

@@ -31,18 +31,25 @@
 
 namespace gla {
 
-// This wave's 16 rows of a per-chunk transposed operand ([rows][XW], XW = C or 2C), as
-// MFMA A fragments held in registers: rows of C tokens in the operand type, or (SPLIT) a
-// bf16 high part in [0, C) and its bf16 remainder in [C, 2C) of each row.
+// This wave's 16 rows of a per-chunk transposed operand, as MFMA A fragments held in
+// registers.  Unsplit: rows of C tokens in the operand type ([rows][C]), `at` = the lane's
+// row.  SPLIT: a bf16 high part and its bf16 remainder stored in fragment order (as the
+// intra-chunk kernel writes them): for each 16-row block and 32-token block kb, the 64
+// lanes' 16-byte high-part pieces, then their remainders (2 KB); `at` = the row block's
+// first piece plus the lane's, so that every load reads 1 KB of whole cache lines.
 template <typename OpT, bool SPLIT, int C>
 struct XRegs {
   static constexpr int KB = C / 32;
   Frag<OpT> hi[KB], lo[SPLIT ? KB : 1];
-  __device__ __forceinline__ void load(const OpT* __restrict__ row) {
+  __device__ __forceinline__ void load(const OpT* __restrict__ at) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      load_frag_c(hi[kb], row + kb * 32);
-      if constexpr (SPLIT) load_frag_c(lo[kb], row + C + kb * 32);
+      if constexpr (SPLIT) {
+        hi[kb].v = *reinterpret_cast<const bf16x8*>(at + (2 * kb) * 64 * 8);
+        lo[kb].v = *reinterpret_cast<const bf16x8*>(at + (2 * kb + 1) * 64 * 8);
+      } else {
+        load_frag_c(hi[kb], at + kb * 32);
+      }
     }
   }
   // acc += (the value-side fragment b as the A operand) x (these rows as the B operand):
@@ -60,7 +67,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
                                                             int dk, int dv, int N, int nsteps) {
   // TV value columns per workgroup: NJ accumulator tiles per wave, NY 64-column
   // value-side tiles per operand
-  constexpr int NJ = TV / 16, NY = TV / 64, XW = SPLIT ? 2 * C : C;
+  constexpr int NJ = TV / 16, NY = TV / 64;
   static_assert(TV == 64 || (TV == 128 && STORE != 2), "[v][k] staging is 64 columns wide");
   // WT: bf16, chunk 64 and four 64-column value-side tiles per chunk (two operands of 128
   // columns): wave w stages tile w alone into unpadded swizzled tiles (conflict-free
@@ -157,7 +164,13 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   };
   // WT: wave w stages 64 columns at 64 (w % 2) of the first (w < 2) or second operand
   const int wu = __builtin_amdgcn_readfirstlane(w), wh = wu & 1, wsec = wu >> 1;
-  auto xrow = [&](int i) { return (((long)bh * N + i) * dk + k0 + 16 * w + r) * XW; };
+  // where this lane's rows of a chunk's transposed operand start (see XRegs)
+  auto xrow = [&](int i) {
+    if constexpr (SPLIT)
+      return ((((long)bh * N + i) * (dk / 16) + (k0 / 16 + w)) * (2 * (C / 32)) * 64 + l) * 8;
+    else
+      return (((long)bh * N + i) * dk + k0 + 16 * w + r) * (long)C;
+  };
   auto fetch_y = [&](Set& st, int i) {
     const int t0 = i * C, rows = min(C, T - t0);
     if constexpr (WT) {
