@@ -401,6 +401,11 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   gla::ScanArgs ra = sa;
   ra.reverse = true; ra.XT = w + p.QhT; ra.Y = dO; ra.X2T = w + p.KhT; ra.Y2 = v;
   ra.cross = (float*)(w + p.crossR); ra.S_in = dS_T; ra.states = w + p.dst; ra.S_out = dS0;
+  // the forward states go to the backward chunk kernel in MFMA fragment order when the
+  // scans run 128-column tiles (split path); dS stays row-major (its dv workgroups
+  // stage it transposed)
+  sa.frag_states = split && gla::scan_tile_v(sa) == 128;
+  ra.frag_states = false;
   // both scans in one launch
   if ((rs = tr.mark()) != GLA_OK) return rs;
   rs = dev(gla::launch_state_scan2(sa, ra, s));
@@ -416,6 +421,7 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   ba.q = q; ba.k = k; ba.v = v; ba.dO = dO; ba.gamma = nullptr;
   ba.g = split ? nullptr : (const float*)(w + p.g);
   ba.gscalar = scalar_gate(d);
+  ba.s_frag = sa.frag_states;
   ba.A = w + p.A; ba.Kh = w + p.Kh; ba.S = w + p.st; ba.dS = w + p.dst;
   ba.dq = dq; ba.dk_out = dk; ba.dv_out = dv;
   ba.Dloc = p.Dloc ? (float*)(w + p.Dloc) : nullptr;

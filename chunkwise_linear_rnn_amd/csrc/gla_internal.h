@@ -77,6 +77,8 @@ struct ScanArgs {
   const float* eg;       // [BH][N][dk]
   const float* S_in;     // [BH][dk][dv] or NULL
   void* states;          // see store
+  bool frag_states;      // store 1, bf16, 128-column tiles only: states in MFMA fragment
+                         // order (see the scan kernel), for the backward chunk kernel
   float* S_out;          // [BH][dk][dv] or NULL
   int nsteps;            // chunks to walk (0: all N); the layout strides still use N
 };
@@ -94,6 +96,7 @@ struct ScanDir {
   void* states;
   float* S_out;
   int reverse;
+  int frag_states;
 };
 
 struct OutArgs {
@@ -135,6 +138,7 @@ struct BwdArgs {
   float* dla_part;         // scalar gates (split path): fp32 sums of the per-(t, d) gradient
                            // over each 64-wide d block, [BH][T][dk/64], instead of dla
   bool gscalar;            // la holds one gate per token: [BH][T]
+  bool s_frag;             // S (split path) in MFMA fragment order, as the scan wrote it
 };
 // The backward chunk work (launch_bwd_chunk): with bf16 operands and chunk 64 one launch of
 // dq / dk / dlog_alpha workgroups (after the chunk totals are formed) interleaved with dv

@@ -225,7 +225,10 @@ __device__ __forceinline__ void bwd_finish_block(const IntraLds<C, DB, Tin>& L,
 // the chunk (it is cheap next to the dO S^T and V dS^T products, and keeps the blocks
 // independent).  Three workgroups fit on a CU, so one's loads overlap another's math.
 constexpr int kDqkLds = 64 * (64 + 4) * 4 + 64 * (64 + 4) * 4 + 2 * 64 * (64 + 8) * 2;
-template <typename Tin, typename OpT>
+// SFRAG: S in MFMA fragment order (fragment (16-row block, 32-column block) of a chunk's
+// [dk][dv] state: lane 16 q + r holds row r, columns 8 q .. 8 q + 7), as the forward scan
+// writes it for 128-column tiles; otherwise row-major.
+template <typename Tin, typename OpT, bool SFRAG>
 __device__ __forceinline__ void bwd_dqk_body(
     char* __restrict__ arena, int lt, const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dO, int gscalar, const OpT* __restrict__ S,
@@ -278,7 +281,11 @@ __device__ __forceinline__ void bwd_dqk_body(
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const long off = (long)(d0 + c) * dv + vb * 64 + kb * 32;
-      load_frag_c(fs[kb], Si + off);
+      if constexpr (SFRAG)
+        fs[kb].v = *reinterpret_cast<const bf16x8*>(
+            Si + (((long)(d0 / 16 + w) * (dv / 32) + (vb * 2 + kb)) * 64 + l) * 8);
+      else
+        load_frag_c(fs[kb], Si + off);
       load_frag_c(fds[kb], dSi + off);
     }
   };
@@ -789,7 +796,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(
 // The two chunk-64 backward kernels as one launch: dq / dk / dlog_alpha workgroups and dv
 // workgroups interleaved in proportion (a dv workgroup needs neither the chunk totals nor
 // anything the dq / dk workgroups write), so that their memory phases overlap on each CU.
-template <typename Tin, typename OpT>
+template <typename Tin, typename OpT, bool SFRAG>
 __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk_dv(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dO, int gscalar, const OpT* __restrict__ S,
@@ -804,7 +811,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk_dv(
   // Bresenham split: logical id L is a dq/dk workgroup when the count of them up to L grows
   const int before = (int)(((long)L * n_dqk) / total), upto = (int)(((long)(L + 1) * n_dqk) / total);
   if (upto > before)
-    bwd_dqk_body<Tin, OpT>(arena, before, q, k, v, dO, gscalar, S, dS, dq, dk_out, tot, cT, la, gf,
+    bwd_dqk_body<Tin, OpT, SFRAG>(arena, before, q, k, v, dO, gscalar, S, dS, dq, dk_out, tot, cT, la, gf,
                            dla, dla_part, T, dk, dv, N);
   else
     bwd_dv_body<Tin, OpT>(arena, L - before, Kh, A, dS, dO, dv_out, T, dk, dv, N);
@@ -815,7 +822,8 @@ template <typename Tin, typename OpT, int C, int DK>
 static hipError_t launch_bwd_t2(const BwdArgs& a, hipStream_t s) {
   if constexpr (C == 64 && sizeof(OpT) == 2) {
     const int n_dqk = (a.dk / 64) * a.N * a.BH, n_dv = (a.dv / 64) * a.N * a.BH;
-    hipLaunchKernelGGL((k_bwd_dqk_dv<Tin, OpT>), dim3(n_dqk + n_dv), dim3(kThreads), 0, s,
+    auto kern = a.s_frag ? k_bwd_dqk_dv<Tin, OpT, true> : k_bwd_dqk_dv<Tin, OpT, false>;
+    hipLaunchKernelGGL(kern, dim3(n_dqk + n_dv), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO,
                        a.gscalar ? 1 : 0, (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq,
                        (Tin*)a.dk_out, a.tot, a.cT,

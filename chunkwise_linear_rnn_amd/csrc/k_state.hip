@@ -104,6 +104,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   void* __restrict__ states = second ? d1.states : d0.states;
   float* __restrict__ S_out = second ? d1.S_out : d0.S_out;
   const int reverse = second ? d1.reverse : d0.reverse;
+  const int frag_states = second ? d1.frag_states : d0.frag_states;
   const int vt = lt % nvt, kt = (lt / nvt) % nkt, bh = lt / (nvt * nkt);
   const int v0 = vt * TV, k0 = kt * 64;
   const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
@@ -241,10 +242,23 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
       for (int u_ = 0; u_ < (kUnits + kThreads - 1) / kThreads; ++u_) {   // fixed trip count
         const int idx = threadIdx.x + u_ * kThreads;
         if ((kUnits) % kThreads != 0 && idx >= kUnits) continue;
-        const int e0 = idx * kPer, a = e0 / kCols, b = e0 % kCols;
+        const int e0 = idx * kPer;
+        int a = e0 / kCols, b = e0 % kCols;
         long off;
         if constexpr (STORE == 2) off = sb + (long)(v0 + a) * dk + k0 + b;
         else off = sb + (long)(k0 + a) * dv + v0 + b;
+        if constexpr (SPAD4) {
+          if (frag_states) {
+            // MFMA fragment order of the chunk's [dk][dv] state, as B operands of
+            // products over dv: fragment (16-row block, 32-column block) holds, for lane
+            // 16 q + r, row r and columns 8 q .. 8 q + 7 (16 bytes); units run through
+            // this tile's 4 x 4 fragments lane by lane, so the stores stay contiguous
+            const int fi = idx / 64, ln = idx % 64;
+            a = 16 * (fi / 4) + ln % 16;
+            b = 32 * (fi % 4) + 8 * (ln / 16);
+            off = sb + (((long)(k0 / 16 + fi / 4) * (dv / 32) + (v0 / 32 + fi % 4)) * 64 + ln) * 8;
+          }
+        }
         u32x4 v;
         if constexpr (SPAD4) {   // rows are 8-byte aligned only
           const uint2* p = reinterpret_cast<const uint2*>(ss + a * SLD + b);
@@ -336,6 +350,7 @@ static void launch_scan_k(const ScanArgs& a, const ScanArgs* b, hipStream_t s) {
     ScanDir d;
     d.XT = x.XT; d.Y = x.Y; d.X2T = x.X2T; d.Y2 = x.Y2; d.cross = x.cross; d.S_in = x.S_in;
     d.states = x.states; d.S_out = x.S_out; d.reverse = x.reverse ? 1 : 0;
+    d.frag_states = x.frag_states ? 1 : 0;
     return d;
   };
   const int ndir = b ? 2 : 1;
@@ -376,6 +391,12 @@ static hipError_t launch_scan_t(const ScanArgs& a, const ScanArgs* b, hipStream_
 static hipError_t launch_scans(const ScanArgs& a, const ScanArgs* b, hipStream_t s) {
   if (a.BH == 0 || a.N == 0) return hipSuccess;
   if (a.cross && a.store != 1) return hipErrorInvalidValue;
+  // fragment-ordered states: bf16, chunk 64, 128-column tiles (the backward's scans)
+  auto frag_ok = [](const ScanArgs& x) {
+    return !x.frag_states || (x.dtype != 0 && x.C == 64 && x.store == 1 && x.cross &&
+                              scan_tile_v(x) == 128);
+  };
+  if (!frag_ok(a) || (b && !frag_ok(*b))) return hipErrorInvalidValue;
   if (b && (b->dtype != a.dtype || b->C != a.C || b->BH != a.BH || b->T != a.T ||
             b->dk != a.dk || b->dv != a.dv || b->N != a.N || b->xt_f32 != a.xt_f32 ||
             b->store != a.store || (b->cross != nullptr) != (a.cross != nullptr) || b->eg != a.eg ||
