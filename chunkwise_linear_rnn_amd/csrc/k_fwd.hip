@@ -89,10 +89,12 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
     Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N, int split,
     const float* __restrict__ S_mid) {
   constexpr int NT = kFusedThreads, TV = 64, NM = C / 16, KH = DK / 2, NP = KH / 16;
-  // K^T and A rows padded to 80 elements: 16-byte fragment reads of 16 consecutive rows
-  // then fall on distinct banks (a stride of 72 pairs rows up on gfx950's 64 banks); the
-  // Qh rows are read as 8-byte halves, conflict-free at DK + 8
-  constexpr int QLD = DK + 8, KLD = C + 16, ALD = C + 16, VLD = C + 8, OLD = TV + 8, RLD = TV + 4;
+  // Kh^T arrives in MFMA fragment order (lane 16 q + r of fragment (16-row block, 32-token
+  // block) holds row r, tokens 8 q ..) and is copied to LDS as is: each fragment read is 1 KB
+  // of consecutive lanes.  A rows padded to 80 elements: 16-byte fragment reads of 16
+  // consecutive rows then fall on distinct banks (a stride of 72 pairs rows up on gfx950's
+  // 64 banks); the Qh rows are read as 8-byte halves, conflict-free at DK + 8.
+  constexpr int QLD = DK + 8, KLD = C, ALD = C + 16, VLD = C + 8, OLD = TV + 8, RLD = TV + 4;
   __shared__ __attribute__((aligned(16))) OpT qs[C * QLD];
   __shared__ __attribute__((aligned(16))) OpT ks[DK * KLD];
   __shared__ __attribute__((aligned(16))) OpT as_[C * ALD];
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         Frag<OpT> fa;
-        load_frag_c(fa, ks + (k0 + 16 * p + r) * KLD + kb * 32);
+        fa.v = *reinterpret_cast<const bf16x8*>(ks + (((k0 / 16 + p) * (C / 32) + kb) * 64 + l) * 8);
         mma(S[p], fa, fb);
       }
     }
@@ -316,7 +318,10 @@ __global__ __launch_bounds__(kThreads) void k_fwd_fused(
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         Frag<OpT> fa;
-        load_frag_c(fa, kp + (16 * p + r) * C + kb * 32);
+        if constexpr (sizeof(OpT) == 2)   // bf16 Kh^T in fragment order
+          fa.v = *reinterpret_cast<const bf16x8*>(kp + ((p * (C / 32) + kb) * 64 + l) * 8);
+        else
+          load_frag_c(fa, kp + (16 * p + r) * C + kb * 32);
         mma(S[p], fa, fb);
       }
     }

@@ -200,6 +200,11 @@ __global__ __launch_bounds__(kThreads) void k_intra(
             }
             *reinterpret_cast<bf16x8*>(b) = hv;
             store8(b + 64 * 8, lo);
+          } else if constexpr (sizeof(XT) == 2) {
+            // bf16: fragment order, one plane (see the split case)
+            const int d = d0 + c, j = r8 / 8, kb = j / 4, qd = j % 4;
+            const long f = (((long)bh * N + i) * (dk / 16) + d / 16) * (C / 32) + kb;
+            store8(dst + (f * 64 + 16 * qd + d % 16) * 8, x);
           } else {
             store8(dst + rowi * C + r8, x);
           }

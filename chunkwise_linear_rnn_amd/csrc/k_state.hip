@@ -32,11 +32,11 @@
 namespace gla {
 
 // This wave's 16 rows of a per-chunk transposed operand, as MFMA A fragments held in
-// registers.  Unsplit: rows of C tokens in the operand type ([rows][C]), `at` = the lane's
-// row.  SPLIT: a bf16 high part and its bf16 remainder stored in fragment order (as the
-// intra-chunk kernel writes them): for each 16-row block and 32-token block kb, the 64
-// lanes' 16-byte high-part pieces, then their remainders (2 KB); `at` = the row block's
-// first piece plus the lane's, so that every load reads 1 KB of whole cache lines.
+// registers.  fp32: rows of C tokens ([rows][C]), `at` = the lane's row.  bf16: fragment
+// order, as the intra-chunk kernel writes it: for each 16-row block and 32-token block kb,
+// the 64 lanes' 16-byte pieces (lane 16 q + r: row r, tokens 32 kb + 8 q ..), and with
+// SPLIT the high-part fragment followed by the remainder's; `at` = the row block's first
+// piece plus the lane's, so that every load reads 1 KB of whole cache lines.
 template <typename OpT, bool SPLIT, int C>
 struct XRegs {
   static constexpr int KB = C / 32;
@@ -47,6 +47,8 @@ struct XRegs {
       if constexpr (SPLIT) {
         hi[kb].v = *reinterpret_cast<const bf16x8*>(at + (2 * kb) * 64 * 8);
         lo[kb].v = *reinterpret_cast<const bf16x8*>(at + (2 * kb + 1) * 64 * 8);
+      } else if constexpr (sizeof(OpT) == 2) {
+        hi[kb].v = *reinterpret_cast<const bf16x8*>(at + kb * 64 * 8);
       } else {
         load_frag_c(hi[kb], at + kb * 32);
       }
@@ -167,8 +169,8 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   const int wu = __builtin_amdgcn_readfirstlane(w), wh = wu & 1, wsec = wu >> 1;
   // where this lane's rows of a chunk's transposed operand start (see XRegs)
   auto xrow = [&](int i) {
-    if constexpr (SPLIT)
-      return ((((long)bh * N + i) * (dk / 16) + (k0 / 16 + w)) * (2 * (C / 32)) * 64 + l) * 8;
+    if constexpr (sizeof(OpT) == 2)
+      return ((((long)bh * N + i) * (dk / 16) + (k0 / 16 + w)) * ((SPLIT ? 2 : 1) * (C / 32)) * 64 + l) * 8;
     else
       return (((long)bh * N + i) * dk + k0 + 16 * w + r) * (long)C;
   };
