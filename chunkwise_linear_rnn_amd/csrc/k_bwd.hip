@@ -17,7 +17,8 @@
 // rho' the last row of J (all exponents <= 0).  Those MFMA products take dA and the
 // rebased operand each as a bf16 high part plus a bf16 remainder (three MFMAs), since the
 // gate gradient sums q*dq - k*dk with heavy cancellation.  Diagonal sub-blocks are summed
-// in fp32 from log-space differences, each exp(g_t - g_s) shared by its dQ and dK terms.
+// in fp32, each exp(g_t - g_s) (a product of per-row decays, all at most 1) shared by its
+// dQ and dK terms.
 // The chunk-local suffix sums of D are completed by the gate-gradient kernel with the
 // chunk totals that the two state scans form from their fp32 states.
 //
@@ -39,6 +40,31 @@
 #include "gla_internal.h"
 
 namespace gla {
+
+// Diagonal 16 x 16 sub-block of the intra-chunk terms for one column, in fp32: with
+// a_ts = exp(g_t - g_s) dA_ts (t >= s, g already times log2 e),
+//   aq_t += sum_{s <= t} a_ts k_s,   ak_s += sum_{t >= s} a_ts q_t.
+// exp(g_t - g_s) is the running product of the per-row decays exp(g_u - g_{u-1}),
+// u = s + 1 .. t: 15 exponentials instead of 136, every factor at most 1 (nothing
+// overflows), and each a_ts shared by its two sums.
+__device__ __forceinline__ void diag_block16(const float (&gt)[16], const float (&qv)[16],
+                                             const float (&kv)[16], const float* dAm, int ld,
+                                             float (&aq)[16], float (&ak)[16]) {
+  float dec[16];
+#pragma unroll
+  for (int u = 1; u < 16; ++u) dec[u] = __builtin_amdgcn_exp2f(gt[u] - gt[u - 1]);
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    float ex = 1.f;
+#pragma unroll
+    for (int s = t; s >= 0; --s) {
+      if (s < t) ex *= dec[s + 1];
+      const float a = ex * dAm[t * ld + s];
+      aq[t] += a * kv[s];
+      ak[s] += a * qv[t];
+    }
+  }
+}
 
 // LDS of the intra-chunk / D phase for one dk block of DB columns.
 template <int C, int DB, typename Tin>
@@ -155,15 +181,7 @@ __device__ __forceinline__ void bwd_finish_block(const IntraLds<C, DB, Tin>& L,
       aq[j] = 0.f;
       ak[j] = 0.f;
     }
-    const float* dAm = L.dAs + base * FLD + base;
-#pragma unroll
-    for (int t = 0; t < 16; ++t)
-#pragma unroll
-      for (int s = 0; s <= t; ++s) {
-        const float ex = __builtin_amdgcn_exp2f(gt[t] - gt[s]) * dAm[t * FLD + s];
-        aq[t] += ex * kv[s];
-        ak[s] += ex * qv[t];
-      }
+    diag_block16(gt, qv, kv, L.dAs + base * FLD + base, FLD, aq, ak);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       L.dqd[(base + j) * GLD + cc] = aq[j];
@@ -423,7 +441,7 @@ __device__ __forceinline__ void bwd_dqk_body(
         adk[m][e] += tmp[e] * __builtin_amdgcn_exp2f(gr - gs[(16 * m + 4 * qd + e) * GLD + c]);
     }
   }
-  // intra-chunk, diagonal sub-blocks in fp32 log space: thread (sub-chunk md, column cd)
+  // intra-chunk, diagonal sub-blocks in fp32: thread (sub-chunk md, column cd)
   float aq[16], ak[16];
   const int md = threadIdx.x / 64, cd = threadIdx.x % 64, base = 16 * md;
   {
@@ -436,15 +454,7 @@ __device__ __forceinline__ void bwd_dqk_body(
       aq[jj] = 0.f;
       ak[jj] = 0.f;
     }
-    const float* dAm = dAs + base * FLD + base;
-#pragma unroll
-    for (int t = 0; t < 16; ++t)
-#pragma unroll
-      for (int s = 0; s <= t; ++s) {
-        const float ex = __builtin_amdgcn_exp2f(gt[t] - gt[s]) * dAm[t * FLD + s];
-        aq[t] += ex * kv[s];
-        ak[s] += ex * qv[t];
-      }
+    diag_block16(gt, qv, kv, dAs + base * FLD + base, FLD, aq, ak);
   }
   __syncthreads();   // dA and g are dead from here: their regions carry the diagonal terms
   float* dqd = dAs;   // [C][FLD]
