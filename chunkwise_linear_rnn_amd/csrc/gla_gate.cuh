@@ -75,11 +75,14 @@ struct GBlock {
 // Chunk-local inclusive cumsum down each of the DB columns of gs ([C][gld] fp32, already
 // staged; the caller synchronizes before and after): thread t takes column t % DB and
 // the t / DB-th quarter of the rows, sums it in registers, then adds the totals of the
-// quarters above it (in order).  segtot: 4 x DB floats of LDS scratch.
+// quarters above it (in order).  segtot: 4 x DB floats of LDS scratch.  Returns the
+// largest |g_t - g_rho| over the thread's rows, rho the first row of each 16-row
+// sub-chunk (the spread that decides how a diagonal sub-block can be summed).
 template <int C, int DB>
-__device__ __forceinline__ void chunk_cumsum_cols(float* gs, int gld, float* segtot) {
+__device__ __forceinline__ float chunk_cumsum_cols(float* gs, int gld, float* segtot) {
   static_assert(kThreads == 4 * DB, "four row quarters per column");
   constexpr int L = C / 4;
+  static_assert(L % 16 == 0, "row quarters hold whole sub-chunks");
   const int col = threadIdx.x % DB, seg = threadIdx.x / DB;
   float run[L];
 #pragma unroll
@@ -90,8 +93,15 @@ __device__ __forceinline__ void chunk_cumsum_cols(float* gs, int gld, float* seg
   __syncthreads();
   float off = 0.f;
   for (int s2 = 0; s2 < seg; ++s2) off += segtot[s2 * DB + col];
+  float spread = 0.f, first = 0.f;
 #pragma unroll
-  for (int rr = 0; rr < L; ++rr) gs[(seg * L + rr) * gld + col] = run[rr] + off;
+  for (int rr = 0; rr < L; ++rr) {
+    const float x = run[rr] + off;
+    gs[(seg * L + rr) * gld + col] = x;
+    if (rr % 16 == 0) first = x;
+    else spread = fmaxf(spread, fabsf(x - first));
+  }
+  return spread;
 }
 
 }  // namespace gla

@@ -108,12 +108,15 @@ __global__ __launch_bounds__(kThreads) void k_intra(
     tq.store(qs);
     tk.store(ks);
     fetch(min(d0 + DB, dk - DB));   // unconditional (exact wait counts); the last refetches
+    // wide: some 16-row sub-block of this block has a spread of g beyond kDiagRange
+    bool wide = false;
     if constexpr (!G_WS) {
-      // chunk-local cumsum down each column
+      // chunk-local cumsum down each column; its spread decides at the barrier after it
       __syncthreads();
-      chunk_cumsum_cols<C, DB>(gs, GLD, segtot);
+      wide = __syncthreads_or(!(chunk_cumsum_cols<C, DB>(gs, GLD, segtot) <= kDiagRange));
+    } else {
+      __syncthreads();
     }
-    __syncthreads();
     if (g2_out) {   // g * log2 e for the backward chunk kernel
 #pragma unroll
       for (int u_ = 0; u_ < (C * (DB / 8) + kThreads - 1) / kThreads; ++u_) {   // fixed trip count
@@ -245,16 +248,18 @@ __global__ __launch_bounds__(kThreads) void k_intra(
       // case), the same MFMA on operands rebased at the sub-block's first row (entries
       // above the diagonal are dropped when the block is written); otherwise the exact
       // fp32 log-space sum per (t, s, column).
-      bool wide = false;
-      for (int idx = threadIdx.x; idx < NS * DB; idx += kThreads) {
-        const int I = idx / DB, col = idx % DB;
-        const float g0 = gs[16 * I * GLD + col];
-        float mx = 0.f;
+      if constexpr (G_WS) {   // g from the gate kernel: measure the spread here
+        for (int idx = threadIdx.x; idx < NS * DB; idx += kThreads) {
+          const int I = idx / DB, col = idx % DB;
+          const float g0 = gs[16 * I * GLD + col];
+          float mx = 0.f;
 #pragma unroll
-        for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, fabsf(gs[(16 * I + rr) * GLD + col] - g0));
-        wide = wide || !(mx <= kDiagRange);
+          for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, fabsf(gs[(16 * I + rr) * GLD + col] - g0));
+          wide = wide || !(mx <= kDiagRange);
+        }
+        wide = __syncthreads_or(wide);
       }
-      if (!__syncthreads_or(wide)) {
+      if (!wide) {
 #pragma unroll
         for (int dI = 0; dI < NDW; ++dI) {
           const int I = w + 4 * dI;
@@ -320,8 +325,17 @@ __global__ __launch_bounds__(kThreads) void k_intra(
         }
       }
     }
-    __syncthreads();
+    // The block is assembled in LDS (in the g tile, dead after the last pass) when it fits
+    // there, and leaves as 16-byte rows; otherwise it is written entry by entry.
     OpT* Ab = A_out + ((long)bh * N + i) * C * C;
+    constexpr int ALD = C + 8;
+    constexpr bool kStageA = C * ALD * (int)sizeof(OpT) <= C * GLD * 4;
+    OpT* At = kStageA ? reinterpret_cast<OpT*>(gs) : Ab;
+    const int ald = kStageA ? ALD : C;
+    for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {   // zero above the diagonal
+      const int t = idx / C, s = idx % C;
+      if (s > t) At[t * ald + s] = from_f32<OpT>(0.f);
+    }
 #pragma unroll
     for (int pi = 0; pi < PPW; ++pi) {
       const int p = w + 4 * pi;
@@ -330,9 +344,10 @@ __global__ __launch_bounds__(kThreads) void k_intra(
         pair_decode(p, I, J);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          Ab[(16 * I + 4 * qd + e) * C + 16 * J + r] = from_f32<OpT>(accp[pi][e]);
+          At[(16 * I + 4 * qd + e) * ald + 16 * J + r] = from_f32<OpT>(accp[pi][e]);
       }
     }
+    __syncthreads();
     // four column-quarter partials of each diagonal entry sit in adjacent lanes
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
@@ -344,12 +359,18 @@ __global__ __launch_bounds__(kThreads) void k_intra(
         const int pr = item >> 2, I = pr / 136;
         int tt, ss;
         tri_decode(pr % 136, tt, ss);
-        Ab[(16 * I + tt) * C + 16 * I + ss] = from_f32<OpT>(v);
+        At[(16 * I + tt) * ald + 16 * I + ss] = from_f32<OpT>(v);
       }
     }
-    for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
-      const int t = idx / C, s = idx % C;
-      if (s > t) Ab[idx] = from_f32<OpT>(0.f);
+    if constexpr (kStageA) {
+      constexpr int kPer = 16 / (int)sizeof(OpT), kRowUnits = C / kPer;
+      static_assert(C * kRowUnits % kThreads == 0, "whole 16-byte units per thread");
+      __syncthreads();
+#pragma unroll
+      for (int u_ = 0; u_ < C * kRowUnits / kThreads; ++u_) {
+        const int idx = threadIdx.x + u_ * kThreads, rr = idx / kRowUnits, cc = (idx % kRowUnits) * kPer;
+        *reinterpret_cast<u32x4*>(Ab + rr * C + cc) = *reinterpret_cast<const u32x4*>(At + rr * ALD + cc);
+      }
     }
   }
 }
