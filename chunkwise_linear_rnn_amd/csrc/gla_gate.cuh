@@ -47,26 +47,38 @@ struct GBlock {
       u[j] = u32x4{wd, wd, wd, wd};
     }
   }
+  // The loaded units are unpacked first, in straight-line code, and rows are zeroed with
+  // selects: a branch around the first use of a load makes the compiler wait for every
+  // memory operation in flight (the previous block's output stores included).
   __device__ __forceinline__ void store(float* gs, int gld, GateFn gf) const {
+    constexpr int kF = sizeof(SrcT) == 2 ? 8 : 4;   // floats per unit
+    float x[kPerThread][kF];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      if constexpr (sizeof(SrcT) == 2) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, u[j]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[j][e] = (float)b[e];
+      } else {
+        const f32x4 f = __builtin_bit_cast(f32x4, u[j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[j][e] = f[e];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+#pragma unroll
+      for (int e = 0; e < kF; ++e) x[j][e] = gf(x[j][e]) * kLog2e;
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       const int idx = threadIdx.x + j * kThreads, rr = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;
       const bool keep = rr < zero_from;
-      if constexpr (sizeof(SrcT) == 2) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, u[j]);
-        f32x4 lo, hi;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lo[e] = keep ? gf((float)b[e]) * kLog2e : 0.f;
-          hi[e] = keep ? gf((float)b[4 + e]) * kLog2e : 0.f;
-        }
-        *reinterpret_cast<f32x4*>(gs + rr * gld + c) = lo;
-        *reinterpret_cast<f32x4*>(gs + rr * gld + c + 4) = hi;
-      } else {
-        f32x4 f = __builtin_bit_cast(f32x4, u[j]);
+      for (int h = 0; h < kF / 4; ++h) {
+        f32x4 f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = keep ? gf(f[e]) * kLog2e : 0.f;
-        *reinterpret_cast<f32x4*>(gs + rr * gld + c) = f;
+        for (int e = 0; e < 4; ++e) f[e] = keep ? x[j][4 * h + e] : 0.f;
+        *reinterpret_cast<f32x4*>(gs + rr * gld + c + 4 * h) = f;
       }
     }
   }
