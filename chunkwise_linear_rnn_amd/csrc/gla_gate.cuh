@@ -90,7 +90,9 @@ struct GBlock {
 // quarters above it (in order).  segtot: 4 x DB floats of LDS scratch.  Returns the
 // largest |g_t - g_rho| over the thread's rows, rho the first row of each 16-row
 // sub-chunk (the spread that decides how a diagonal sub-block can be summed).
-template <int C, int DB>
+// TRANS: the sums go to gs transposed, gs[col * gld + row] (in place: every read of the
+// staged rows happens before the internal barrier), as 16-byte pieces of 4 rows.
+template <int C, int DB, bool TRANS = false>
 __device__ __forceinline__ float chunk_cumsum_cols(float* gs, int gld, float* segtot) {
   static_assert(kThreads == 4 * DB, "four row quarters per column");
   constexpr int L = C / 4;
@@ -108,10 +110,18 @@ __device__ __forceinline__ float chunk_cumsum_cols(float* gs, int gld, float* se
   float spread = 0.f, first = 0.f;
 #pragma unroll
   for (int rr = 0; rr < L; ++rr) {
-    const float x = run[rr] + off;
-    gs[(seg * L + rr) * gld + col] = x;
-    if (rr % 16 == 0) first = x;
-    else spread = fmaxf(spread, fabsf(x - first));
+    run[rr] += off;
+    if (rr % 16 == 0) first = run[rr];
+    else spread = fmaxf(spread, fabsf(run[rr] - first));
+  }
+  if constexpr (TRANS) {
+#pragma unroll
+    for (int rr = 0; rr < L; rr += 4)
+      *reinterpret_cast<f32x4*>(gs + col * gld + seg * L + rr) =
+          f32x4{run[rr], run[rr + 1], run[rr + 2], run[rr + 3]};
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < L; ++rr) gs[(seg * L + rr) * gld + col] = run[rr];
   }
   return spread;
 }

@@ -260,7 +260,9 @@ __device__ __forceinline__ void bwd_dqk_body(
   constexpr int C = 64, NM = 4, NS = C / 16, YLD = 64 + 16;
   constexpr int FLD = C + 4, GLD = 64 + 4, XLD = 64 + 8;
   // LDS: dA [C][FLD] fp32, then a region that holds the dO / V tiles during the dv loop
-  // and g [C][GLD] fp32, q, k [C][XLD] afterwards.  53248 bytes: three workgroups per CU.
+  // and g^T [64 columns][GLD] fp32 (a column's rows contiguous: the post-loop phases read
+  // 4 to 16 consecutive rows of one column), q, k [C][XLD] afterwards.  53248 bytes: three
+  // workgroups per CU.
   constexpr int o_u = C * FLD * 4, o_q = o_u + C * GLD * 4, o_k = o_q + C * XLD * 2;
   constexpr int bytes = o_k + C * XLD * 2;
   static_assert(2 * C * YLD * 2 <= bytes - o_u, "dO / V tiles fit the shared region");
@@ -377,7 +379,7 @@ __device__ __forceinline__ void bwd_dqk_body(
       }
     pg.store(gs, GLD, gf);
     __syncthreads();
-    chunk_cumsum_cols<C, 64>(gs, GLD, reinterpret_cast<float*>(ks));
+    chunk_cumsum_cols<C, 64, true>(gs, GLD, reinterpret_cast<float*>(ks));   // g^T
     __syncthreads();
     tq.store(qs);
     tk.store(ks);
@@ -385,60 +387,65 @@ __device__ __forceinline__ void bwd_dqk_body(
   __syncthreads();
 
   // inter-chunk parts: dq *= exp(g_t), dk *= exp(gamma - g_t)
-  const float gl = gs[(C - 1) * GLD + c];
+  const float* gc = gs + c * GLD;   // g of this lane's column, by row
+  const float gl = gc[C - 1];
 #pragma unroll
-  for (int m = 0; m < NM; ++m)
+  for (int m = 0; m < NM; ++m) {
+    const f32x4 gt = *reinterpret_cast<const f32x4*>(gc + 16 * m + 4 * qd);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float gt = gs[(16 * m + 4 * qd + e) * GLD + c];
-      adq[m][e] *= __builtin_amdgcn_exp2f(gt);
-      adk[m][e] *= __builtin_amdgcn_exp2f(gl - gt);
+      adq[m][e] *= __builtin_amdgcn_exp2f(gt[e]);
+      adk[m][e] *= __builtin_amdgcn_exp2f(gl - gt[e]);
     }
+  }
   // intra-chunk, off-diagonal sub-blocks (split bf16 operands, three MFMAs each)
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     if (m > 0) {   // dq rows of sub-chunk I = m, sources J < I, rebased on rho = 16 m
       const int rho = 16 * m;
-      const float gr = gs[rho * GLD + c];
+      const float gr = gc[rho];
       f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < (16 * m + 31) / 32; ++kb) {
         SFrag<OpT> fa, fb;
-        float xa[8];
+        float xa[8], gv[8];
         load8(xa, dAs + (16 * m + r) * FLD + kb * 32 + 8 * qd);
+        load8(gv, gc + kb * 32 + 8 * qd);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int s = kb * 32 + 8 * qd + e;
           // dA is only written below its diagonal: mask the rest on both operands
           fa.set(e, s < rho ? xa[e] : 0.f);
-          fb.set(e, s < rho ? to_f32(ks[s * XLD + c]) * __builtin_amdgcn_exp2f(gr - gs[s * GLD + c])
+          fb.set(e, s < rho ? to_f32(ks[s * XLD + c]) * __builtin_amdgcn_exp2f(gr - gv[e])
                             : 0.f);
         }
         mma_split(tmp, fa, fb);
       }
+      const f32x4 gt = *reinterpret_cast<const f32x4*>(gc + rho + 4 * qd);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        adq[m][e] += tmp[e] * __builtin_amdgcn_exp2f(gs[(rho + 4 * qd + e) * GLD + c] - gr);
+      for (int e = 0; e < 4; ++e) adq[m][e] += tmp[e] * __builtin_amdgcn_exp2f(gt[e] - gr);
     }
     if (m < NS - 1) {   // dk rows of sub-chunk J = m, sources I > J, rebased on rho' = 16 m + 15
       const int rho = 16 * m + 15;
-      const float gr = gs[rho * GLD + c];
+      const float gr = gc[rho];
       f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = (16 * m + 16) / 32; kb < C / 32; ++kb) {
         SFrag<OpT> fa, fb;
+        float gv[8];
+        load8(gv, gc + kb * 32 + 8 * qd);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int t = kb * 32 + 8 * qd + e;
           const bool on = t > rho;
           fa.set(e, on ? dAs[t * FLD + 16 * m + r] : 0.f);
-          fb.set(e, on ? to_f32(qs[t * XLD + c]) * __builtin_amdgcn_exp2f(gs[t * GLD + c] - gr) : 0.f);
+          fb.set(e, on ? to_f32(qs[t * XLD + c]) * __builtin_amdgcn_exp2f(gv[e] - gr) : 0.f);
         }
         mma_split(tmp, fa, fb);
       }
+      const f32x4 gt = *reinterpret_cast<const f32x4*>(gc + 16 * m + 4 * qd);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        adk[m][e] += tmp[e] * __builtin_amdgcn_exp2f(gr - gs[(16 * m + 4 * qd + e) * GLD + c]);
+      for (int e = 0; e < 4; ++e) adk[m][e] += tmp[e] * __builtin_amdgcn_exp2f(gr - gt[e]);
     }
   }
   // intra-chunk, diagonal sub-blocks in fp32: thread (sub-chunk md, column cd)
@@ -447,8 +454,13 @@ __device__ __forceinline__ void bwd_dqk_body(
   {
     float gt[16], qv[16], kv[16];
 #pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(gs + cd * GLD + base + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gt[4 * h + e] = x[e];
+    }
+#pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
-      gt[jj] = gs[(base + jj) * GLD + cd];
       qv[jj] = to_f32(qs[(base + jj) * XLD + cd]);
       kv[jj] = to_f32(ks[(base + jj) * XLD + cd]);
       aq[jj] = 0.f;
