@@ -401,11 +401,11 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   gla::ScanArgs ra = sa;
   ra.reverse = true; ra.XT = w + p.QhT; ra.Y = dO; ra.X2T = w + p.KhT; ra.Y2 = v;
   ra.cross = (float*)(w + p.crossR); ra.S_in = dS_T; ra.states = w + p.dst; ra.S_out = dS0;
-  // the forward states go to the backward chunk kernel in MFMA fragment order when the
-  // scans run 128-column tiles (split path); dS stays row-major (its dv workgroups
-  // stage it transposed)
+  // S and dS go to the backward chunk kernel in MFMA fragment order when the scans run
+  // 128-column tiles (split path): its dq / dk workgroups load whole fragments, its dv
+  // workgroups stage dS transposed from them
   sa.frag_states = split && gla::scan_tile_v(sa) == 128;
-  ra.frag_states = false;
+  ra.frag_states = sa.frag_states;
   // both scans in one launch
   if ((rs = tr.mark()) != GLA_OK) return rs;
   rs = dev(gla::launch_state_scan2(sa, ra, s));

@@ -374,6 +374,27 @@ struct ColTile {
       }
     }
   }
+  // The same units from a [*][ncols] matrix kept in MFMA fragment order (16-row x
+  // 32-column fragments of 1 KB, row-block major; lane 16 q + r of a fragment holds row r,
+  // columns 8 q .. 8 q + 7): rows r0 + [0, ROWS), columns c0 + [0, 64), all valid.  The
+  // two rows of a unit are adjacent 16-byte pieces; a wave reads two whole fragments.
+  __device__ __forceinline__ void load_frag(const Tin* __restrict__ g, int ncols, int r0,
+                                            int c0) {
+    static_assert(sizeof(Tin) == 2, "fragment order is kept for 16-bit states");
+    nrows = ROWS;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int idx = threadIdx.x + j * NT;
+      const int r = (idx / 8) * 2, c = (idx % 8) * 8;
+      if (kUnits % NT == 0 || idx < kUnits) {
+        const int d = r0 + r, v = c0 + c;
+        const Tin* p = g + (((long)(d >> 4) * (ncols >> 5) + (v >> 5)) * 64 +
+                            16 * ((v & 31) >> 3) + (d & 15)) * 8;
+        x0[j][0] = *reinterpret_cast<const u32x4*>(p);
+        x1[j][0] = *reinterpret_cast<const u32x4*>(p + 8);
+      }
+    }
+  }
   __device__ __forceinline__ void store(OpT* lds) const {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {

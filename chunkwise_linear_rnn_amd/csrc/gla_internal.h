@@ -138,7 +138,7 @@ struct BwdArgs {
   float* dla_part;         // scalar gates (split path): fp32 sums of the per-(t, d) gradient
                            // over each 64-wide d block, [BH][T][dk/64], instead of dla
   bool gscalar;            // la holds one gate per token: [BH][T]
-  bool s_frag;             // S (split path) in MFMA fragment order, as the scan wrote it
+  bool s_frag;             // S and dS (split path) in MFMA fragment order, as the scans wrote them
 };
 // The backward chunk work (launch_bwd_chunk): with bf16 operands and chunk 64 one launch of
 // dq / dk / dlog_alpha workgroups (after the chunk totals are formed) interleaved with dv

@@ -243,9 +243,9 @@ __device__ __forceinline__ void bwd_finish_block(const IntraLds<C, DB, Tin>& L,
 // the chunk (it is cheap next to the dO S^T and V dS^T products, and keeps the blocks
 // independent).  Three workgroups fit on a CU, so one's loads overlap another's math.
 constexpr int kDqkLds = 64 * (64 + 4) * 4 + 64 * (64 + 4) * 4 + 2 * 64 * (64 + 8) * 2;
-// SFRAG: S in MFMA fragment order (fragment (16-row block, 32-column block) of a chunk's
-// [dk][dv] state: lane 16 q + r holds row r, columns 8 q .. 8 q + 7), as the forward scan
-// writes it for 128-column tiles; otherwise row-major.
+// SFRAG: S and dS in MFMA fragment order (fragment (16-row block, 32-column block) of a
+// chunk's [dk][dv] state: lane 16 q + r holds row r, columns 8 q .. 8 q + 7), as the scans
+// write them for 128-column tiles; otherwise row-major.
 template <typename Tin, typename OpT, bool SFRAG>
 __device__ __forceinline__ void bwd_dqk_body(
     char* __restrict__ arena, int lt, const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
@@ -301,12 +301,14 @@ __device__ __forceinline__ void bwd_dqk_body(
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const long off = (long)(d0 + c) * dv + vb * 64 + kb * 32;
-      if constexpr (SFRAG)
-        fs[kb].v = *reinterpret_cast<const bf16x8*>(
-            Si + (((long)(d0 / 16 + w) * (dv / 32) + (vb * 2 + kb)) * 64 + l) * 8);
-      else
+      if constexpr (SFRAG) {
+        const long fo = (((long)(d0 / 16 + w) * (dv / 32) + (vb * 2 + kb)) * 64 + l) * 8;
+        fs[kb].v = *reinterpret_cast<const bf16x8*>(Si + fo);
+        fds[kb].v = *reinterpret_cast<const bf16x8*>(dSi + fo);
+      } else {
         load_frag_c(fs[kb], Si + off);
-      load_frag_c(fds[kb], dSi + off);
+        load_frag_c(fds[kb], dSi + off);
+      }
     }
   };
   auto body = [&](int vb, Frag<OpT> (&fs)[2], Frag<OpT> (&fds)[2], Frag<OpT> (&ns)[2],
@@ -566,7 +568,7 @@ __device__ __forceinline__ void bwd_dqk_body(
 // =====================================================================================
 // dv = A^T dO + sum over 64-wide dk blocks of Kh_blk dS_blk; the next block's Kh and
 // dS^T tiles are loaded into registers while the current one multiplies.
-template <typename Tin, typename OpT>
+template <typename Tin, typename OpT, bool SFRAG>
 __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
                                             const OpT* __restrict__ Kh,
                                             const OpT* __restrict__ A,
@@ -588,7 +590,8 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
   const int v0 = vt * 64, t0 = i * C, rows = min(C, T - t0);
   const int w = wave_id(), l = lane_id(), r = l & 15;
   const OpT* Khc = Kh + ((long)bh * N * C + t0) * dk;
-  const OpT* dSc = dS + ((long)bh * N + i) * dk * dv + v0;
+  const OpT* dSb = dS + ((long)bh * N + i) * dk * dv;   // the chunk's dS (SFRAG: fragment order)
+  const OpT* dSc = dSb + v0;
   RowTile<OpT, C, 64, KLD> tk;
   // transposed tiles are staged chunk-swizzled (conflict-free stores)
   ColTile<OpT, OpT, 64, LD, kThreads, true> ts;
@@ -598,7 +601,8 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
     ta.load(A + ((long)bh * N + i) * C * C, C, C);
     to.load(dO + ((long)bh * T + t0) * dv + v0, dv, rows);
     tk.load(Khc, dk, C);
-    ts.load(dSc, dv, 64);
+    if constexpr (SFRAG) ts.load_frag(dSb, dv, 0, v0);
+    else ts.load(dSc, dv, 64);
     ta.store(aT);
     to.store(doT);
     tk.store(ksh);
@@ -624,7 +628,8 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
   for (int jb = 0; jb < NJ; ++jb) {
     if (jb + 1 < NJ) {
       tk.load(Khc + 64 * (jb + 1), dk, C);
-      ts.load(dSc + (long)64 * (jb + 1) * dv, dv, 64);
+      if constexpr (SFRAG) ts.load_frag(dSb, dv, 64 * (jb + 1), v0);
+      else ts.load(dSc + (long)64 * (jb + 1) * dv, dv, 64);
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -836,7 +841,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk_dv(
     bwd_dqk_body<Tin, OpT, SFRAG>(arena, before, q, k, v, dO, gscalar, S, dS, dq, dk_out, tot, cT, la, gf,
                            dla, dla_part, T, dk, dv, N);
   else
-    bwd_dv_body<Tin, OpT>(arena, L - before, Kh, A, dS, dO, dv_out, T, dk, dv, N);
+    bwd_dv_body<Tin, OpT, SFRAG>(arena, L - before, Kh, A, dS, dO, dv_out, T, dk, dv, N);
 }
 
 // ---------------------------------------------------------------------------------
