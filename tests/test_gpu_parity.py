@@ -47,6 +47,10 @@ SMALL = [
     # a ragged last chunk, and a sequence shorter than one chunk
     ("bf16_c64_dv256", "bf16", 1, 2, 301, 128, 256, 64, 0.0),
     ("bf16_short_dv128", "bf16", 1, 1, 37, 64, 128, 64, 0.0),
+    # the recompute forward's sequence split at chunk N / 2: 9 chunks (halves of 4 and 5,
+    # ragged last chunk) and 7 chunks (halves of 3 and 4)
+    ("bf16_c64_n9", "bf16", 1, 2, 520, 128, 128, 64, -1.0),
+    ("bf16_c64_n7", "bf16", 2, 1, 400, 64, 128, 64, 0.5),
 ]
 
 
