@@ -592,21 +592,31 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
   const OpT* Khc = Kh + ((long)bh * N * C + t0) * dk;
   const OpT* dSb = dS + ((long)bh * N + i) * dk * dv;   // the chunk's dS (SFRAG: fragment order)
   const OpT* dSc = dSb + v0;
-  RowTile<OpT, C, 64, KLD> tk;
+  // Every dk block's Kh and dS^T tiles (dk <= 256: at most four) are loaded into registers
+  // up front, in the order they are used, so that their latency is paid once rather than
+  // once per block (a block's products are far shorter than a load's round trip).  Block
+  // indices past the last are clamped (loaded, staged, never used): no branch around a
+  // load or its first use, so the compiler's wait counts stay exact.
+  constexpr int MJ = 4;
+  RowTile<OpT, C, 64, KLD> tk[MJ];
   // transposed tiles are staged chunk-swizzled (conflict-free stores)
-  ColTile<OpT, OpT, 64, LD, kThreads, true> ts;
+  ColTile<OpT, OpT, 64, LD, kThreads, true> ts[MJ];
   {
     ColTile<OpT, OpT, C, LD, kThreads, true> ta;
     ColTile<OpT, Tin, C, LD, kThreads, true> to;
     ta.load(A + ((long)bh * N + i) * C * C, C, C);
     to.load(dO + ((long)bh * T + t0) * dv + v0, dv, rows);
-    tk.load(Khc, dk, C);
-    if constexpr (SFRAG) ts.load_frag(dSb, dv, 0, v0);
-    else ts.load(dSc, dv, 64);
+#pragma unroll
+    for (int jb = 0; jb < MJ; ++jb) {
+      const int jc = min(jb, NJ - 1);
+      tk[jb].load(Khc + 64 * jc, dk, C);
+      if constexpr (SFRAG) ts[jb].load_frag(dSb, dv, 64 * jc, v0);
+      else ts[jb].load(dSc + (long)64 * jc * dv, dv, 64);
+    }
     ta.store(aT);
     to.store(doT);
-    tk.store(ksh);
-    ts.store(dsT);
+    tk[0].store(ksh);
+    ts[0].store(dsT);
   }
   __syncthreads();
   f32x4 acc[NM];
@@ -625,27 +635,25 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
       }
     }
   }
-  for (int jb = 0; jb < NJ; ++jb) {
-    if (jb + 1 < NJ) {
-      tk.load(Khc + 64 * (jb + 1), dk, C);
-      if constexpr (SFRAG) ts.load_frag(dSb, dv, 64 * (jb + 1), v0);
-      else ts.load(dSc + (long)64 * (jb + 1) * dv, dv, 64);
-    }
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      Frag<OpT> fb;
-      load_frag_cs(fb, dsT, LD, 16 * w + r, kb);
+  for (int jb = 0; jb < MJ; ++jb) {
+    if (jb < NJ) {
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        Frag<OpT> fa;
-        load_frag_c(fa, ksh + (16 * m + r) * KLD + kb * 32);
-        mma(acc[m], fa, fb);
+      for (int kb = 0; kb < 2; ++kb) {
+        Frag<OpT> fb;
+        load_frag_cs(fb, dsT, LD, 16 * w + r, kb);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          Frag<OpT> fa;
+          load_frag_c(fa, ksh + (16 * m + r) * KLD + kb * 32);
+          mma(acc[m], fa, fb);
+        }
       }
     }
     __syncthreads();
-    if (jb + 1 < NJ) {
-      tk.store(ksh);
-      ts.store(dsT);
+    if (jb + 1 < MJ) {
+      tk[jb + 1].store(ksh);
+      ts[jb + 1].store(dsT);
       __syncthreads();
     }
   }
