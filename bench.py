@@ -40,6 +40,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import json
+import statistics
 import os
 import sys
 import time
@@ -417,19 +418,20 @@ def main():
         if st:
             raise nat.GlaError(st, "gla_chunk_bwd_traced")
 
-    def stage_means(evs_f, evs_b, n_steps):
+    def stage_means(evs_f, evs_b, n_steps, agg=statistics.fmean):
         acc = {}
         for j in range(n_steps):
             for names, evs, tag in ((fwd_stages, evs_f[j], "fwd"), (bwd_stages, evs_b[j], "bwd")):
                 for s_i, name in enumerate(names):
-                    acc[(tag, name)] = acc.get((tag, name), 0.0) + hip.elapsed_ms(evs[s_i], evs[s_i + 1])
-        return {key: ms / n_steps for key, ms in acc.items()}
+                    acc.setdefault((tag, name), []).append(hip.elapsed_ms(evs[s_i], evs[s_i + 1]))
+        return {key: agg(ms) for key, ms in acc.items()}
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for j in range(args.warmup):
         step(evf[j], evb[j])
     torch.cuda.synchronize()
-    warm = stage_means(evf, evb, args.warmup) if args.warmup > 0 else {}
+    # per-stage medians: the first steps carry one-off costs (first launches, cold caches)
+    warm = stage_means(evf, evb, args.warmup, statistics.median) if args.warmup > 0 else {}
     # the stage the roofline describes: the longest in the warm-up (a stage with no launch
     # for this shape reads ~0)
     dom_key = max(warm, key=warm.get) if warm else ("bwd", bwd_stages[-1])
