@@ -592,27 +592,28 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
   const OpT* Khc = Kh + ((long)bh * N * C + t0) * dk;
   const OpT* dSb = dS + ((long)bh * N + i) * dk * dv;   // the chunk's dS (SFRAG: fragment order)
   const OpT* dSc = dSb + v0;
-  // Every dk block's Kh and dS^T tiles (dk <= 256: at most four) are loaded into registers
-  // up front, in the order they are used, so that their latency is paid once rather than
-  // once per block (a block's products are far shorter than a load's round trip).  Block
+  // The dk blocks' Kh and dS^T tiles (dk <= 256: at most four) are loaded into registers
+  // two blocks ahead of their use, so that a block's round trip overlaps two blocks of
+  // products rather than one (all four at once cost more L2 hits than it saved).  Block
   // indices past the last are clamped (loaded, staged, never used): no branch around a
   // load or its first use, so the compiler's wait counts stay exact.
   constexpr int MJ = 4;
   RowTile<OpT, C, 64, KLD> tk[MJ];
   // transposed tiles are staged chunk-swizzled (conflict-free stores)
   ColTile<OpT, OpT, 64, LD, kThreads, true> ts[MJ];
+  auto load_blk = [&](int jb) {
+    const int jc = min(jb, NJ - 1);
+    tk[jb].load(Khc + 64 * jc, dk, C);
+    if constexpr (SFRAG) ts[jb].load_frag(dSb, dv, 64 * jc, v0);
+    else ts[jb].load(dSc + (long)64 * jc * dv, dv, 64);
+  };
   {
     ColTile<OpT, OpT, C, LD, kThreads, true> ta;
     ColTile<OpT, Tin, C, LD, kThreads, true> to;
     ta.load(A + ((long)bh * N + i) * C * C, C, C);
     to.load(dO + ((long)bh * T + t0) * dv + v0, dv, rows);
 #pragma unroll
-    for (int jb = 0; jb < MJ; ++jb) {
-      const int jc = min(jb, NJ - 1);
-      tk[jb].load(Khc + 64 * jc, dk, C);
-      if constexpr (SFRAG) ts[jb].load_frag(dSb, dv, 64 * jc, v0);
-      else ts[jb].load(dSc + (long)64 * jc * dv, dv, 64);
-    }
+    for (int jb = 0; jb < 2; ++jb) load_blk(jb);
     ta.store(aT);
     to.store(doT);
     tk[0].store(ksh);
@@ -637,6 +638,7 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
   }
 #pragma unroll
   for (int jb = 0; jb < MJ; ++jb) {
+    if (jb + 2 < MJ) load_blk(jb + 2);
     if (jb < NJ) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
