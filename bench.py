@@ -28,8 +28,11 @@ summed over the key dimension).
 `gsa_step` times Gated Slot Attention (float32, fwd + bwd, --gsa-slots memory slots,
 default 64) at the workload's B, H, T, dk, dv.
 
-`cache_flushed` repeats the step after a 512 MiB write that evicts the 256 MiB Infinity
-Cache, with HIP events around the step only (the headline `value` is the warm rate).
+Every timed step runs after a 512 MiB device write that evicts the 256 MiB Infinity
+Cache, with HIP events around the step only (the write is not timed): the headline
+`value` is the cache-flushed rate, the inputs resident in HBM but not in any cache.
+`warm_cache` repeats the steps back to back without the write (inputs and workspaces
+partly served from the Infinity Cache), for context.
 
 The CPU baseline times the fp64 oracle (step recurrence, then direct backward, each
 timed separately) on a bounded sample of the same workload with a process pool on the
@@ -223,7 +226,10 @@ def cpu_baseline(d, cfg, T_sample):
         else:
             os.environ[k] = val
     tokens = workers * T_sample / cfg.H     # head-tokens -> tokens (each token has H heads)
-    return {"value": tokens / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+    # cores: the worker processes (one thread each) that ran the oracle; host_cores: the
+    # cores available to this process on the host
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": workers,
+            "host_cores": cores, "workers": workers, "kind": "oracle",
             "sample": (f"fp64 step recurrence + direct backward, {workers} (batch, head) pairs x "
                        f"first {T_sample} tokens of {cfg.name}, one process per head, "
                        f"{wall:.2f} s wall (fwd {wall_f:.2f} s, bwd {wall_b:.2f} s)"),
@@ -337,8 +343,9 @@ def main():
                          "profiling its kernels on their own)")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens per (batch, head) in the oracle sample")
-    ap.add_argument("--flush-steps", type=int, default=10,
-                    help="extra steps timed after a 512 MiB write that evicts the Infinity Cache")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="time the steps back to back without the cache-evicting write "
+                         "(then `value` is the warm-cache rate)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
     args = ap.parse_args()
@@ -443,18 +450,38 @@ def main():
         arr[dom_i], arr[dom_i + 1] = ev_dom[j][0], ev_dom[j][1]
         sparse.append(arr)
 
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    # The timed steps: each after a 512 MiB write that evicts the Infinity Cache (untimed),
+    # HIP events around the step itself, and the two events around the longest stage.
+    flush = not args.no_flush
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if flush else None
+    ev_step = [hip.create(2) for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps{' (cache flushed before each)' if flush else ''}",
+          file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for j in range(args.steps):
+        if flush:
+            scratch.fill_(j & 0xFF)
+        hip.record(ev_step[j][0], sp)
         if dom_pass == "fwd":
             step(sparse[j], None)
         else:
             step(None, sparse[j])
+        hip.record(ev_step[j][1], sp)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = sum(hip.elapsed_ms(e0, e1) for e0, e1 in ev_step) / args.steps
     dom_ms = sum(hip.elapsed_ms(ev_dom[j][0], ev_dom[j][1]) for j in range(args.steps)) / args.steps
+    del scratch
+
+    # The same steps back to back without the write (warm Infinity Cache), for context.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        step(None, None)
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    warm_rec = {"ms_per_step": warm_ms, "value": B * T / (warm_ms * 1e-3), "steps": args.steps}
 
     # per-stage means from a profiling pass of the same steps with every boundary recorded
     n_prof = args.steps
@@ -469,26 +496,6 @@ def main():
     gpu_ms_from_events = sum(stages.values())
     evf += pf
     evb += pb
-
-    # Cache-cold steps: a 512 MiB write before each step evicts the 256 MiB Infinity Cache,
-    # and HIP events bracket only the step itself.
-    flushed = None
-    if args.flush_steps > 0:
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        evs = hip.create(2)
-        total = 0.0
-        for j in range(args.flush_steps):
-            scratch.fill_(j & 0xFF)
-            hip.record(evs[0], sp)
-            step(None, None)
-            hip.record(evs[1], sp)
-            torch.cuda.synchronize()
-            total += hip.elapsed_ms(evs[0], evs[1])
-        hip.destroy(evs)
-        del scratch
-        fms = total / args.flush_steps
-        flushed = {"ms_per_step": fms, "value": B * T / (fms * 1e-3), "steps": args.flush_steps,
-                   "flush_bytes": 512 << 20}
 
     # The same steps with other gate inputs: gate logits (log_alpha = logsigmoid(x)/16
     # formed in the kernels, the gradient returned for x), and scalar gates (one per token,
@@ -550,7 +557,9 @@ def main():
 
     e = 2 if cfg.dtype == "bf16" else 4
     mode_s = args.state_mode
-    print(f"[bench] {cfg.name}: {ms_per_step:.4f} ms/step (wall, timed steps); profiling pass "
+    print(f"[bench] {cfg.name}: {ms_per_step:.4f} ms/step (HIP events, timed steps; "
+          f"{wall * 1e3 / args.steps:.4f} ms wall incl. the cache flush), warm cache "
+          f"{warm_ms:.4f} ms/step; profiling pass "
           f"with every stage boundary recorded: {traced_ms:.4f} ms/step wall, "
           f"{gpu_ms_from_events:.4f} ms (sum of stage events)", file=sys.stderr)
     print(f"{'pass':4s} {'stage':16s} {'us':>9s} {'GB/s':>8s} {'TFLOP/s':>8s}", file=sys.stderr)
@@ -592,12 +601,13 @@ def main():
                    "seq_len": T, "parallelism": "none (1 GPU)"},
         "tflops": tflops, "mfma_peak_frac": flops / (ms_per_step * 1e-3) / PEAK_BF16,
         "roofline": roof,
-        "cache_flushed": flushed,
+        "cache_flushed": flush,
+        "warm_cache": warm_rec,
         "gate_logits_step": gate_fe,
         "scalar_gate_step": scalar_fe,
         "gsa_step": gsa_step,
     }
-    for arr in evf + evb + ev_dom:
+    for arr in evf + evb + ev_dom + ev_step:
         hip.destroy(arr)
     if not args.no_decode:
         out["decode_step"] = decode_measure(L, nat, hip, dev, sp, H, dk, dv)

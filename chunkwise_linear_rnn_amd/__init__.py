@@ -18,6 +18,7 @@ from __future__ import annotations
 
 from ._native import (GlaDesc, GlaError, F32, BF16, MATERIALIZED, RECOMPUTE, PASS_FWD,  # noqa: F401
                       PASS_BWD, PASS_STATES, GATE_LOG_ALPHA, GATE_LOGITS, GATE_PER_KEY, GATE_SCALAR,
+                      DIAG_F32, DIAG_BF16,
                       lib, lib_path, make_desc, make_gsa_desc, gsa_workspace_bytes, status_string,
                       trace_stages,
                       validate, version, workspace_bytes)

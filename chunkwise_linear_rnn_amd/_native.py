@@ -16,6 +16,7 @@ F32, BF16 = 0, 1
 GATE_LOG_ALPHA, GATE_LOGITS = 0, 1
 GATE_PER_KEY, GATE_SCALAR = 0, 1
 MATERIALIZED, RECOMPUTE = 0, 1
+DIAG_F32, DIAG_BF16 = 0, 1
 PASS_FWD, PASS_BWD, PASS_STATES = 0, 1, 2
 
 # Every function include/gla.h declares, with its ctypes signature.
@@ -25,7 +26,8 @@ _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 class GlaDesc(ctypes.Structure):
     _fields_ = [("B", _i32), ("H", _i32), ("T", _i32), ("dk", _i32), ("dv", _i32),
                 ("chunk", _i32), ("subchunk", _i32), ("dtype", _i32), ("state_mode", _i32),
-                ("gate", _i32), ("gate_tau", ctypes.c_float), ("gate_shape", _i32)]
+                ("gate", _i32), ("gate_tau", ctypes.c_float), ("gate_shape", _i32),
+                ("diag", _i32)]
 
     def __repr__(self):
         return "GlaDesc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -102,9 +104,10 @@ def version() -> int:
 
 
 def make_desc(B, H, T, dk, dv, chunk=64, subchunk=16, dtype=BF16, state_mode=RECOMPUTE,
-              gate=GATE_LOG_ALPHA, gate_tau=1.0, gate_shape=GATE_PER_KEY) -> GlaDesc:
+              gate=GATE_LOG_ALPHA, gate_tau=1.0, gate_shape=GATE_PER_KEY,
+              diag=DIAG_F32) -> GlaDesc:
     return GlaDesc(B, H, T, dk, dv, chunk, subchunk, dtype, state_mode, gate, gate_tau,
-                   gate_shape)
+                   gate_shape, diag)
 
 
 def validate(desc: GlaDesc, pass_: int = PASS_FWD) -> int:

@@ -208,6 +208,7 @@ gla_status_t gla_validate(const gla_desc_t* d, int32_t pass) {
   if (d->state_mode != GLA_STATES_MATERIALIZED && d->state_mode != GLA_STATES_RECOMPUTE)
     return GLA_ERR_INVALID_ARG;
   if (!gate_ok(d)) return GLA_ERR_INVALID_ARG;
+  if (d->diag != GLA_DIAG_F32 && d->diag != GLA_DIAG_BF16) return GLA_ERR_INVALID_ARG;
   if (d->chunk != 64 && d->chunk != 128) return GLA_ERR_UNSUPPORTED;
   if (d->subchunk != 16) return GLA_ERR_UNSUPPORTED;
   if (d->dtype == GLA_F32 && d->chunk != 64) return GLA_ERR_UNSUPPORTED;
@@ -302,7 +303,7 @@ gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void
   gla::IntraArgs ia{};
   ia.dtype = x.dtype; ia.C = (int)x.C; ia.BH = (int)x.BH; ia.T = (int)x.T; ia.dk = (int)x.dk;
   ia.N = (int)x.N; ia.want_A = true; ia.q = q; ia.k = k; ia.la = log_alpha; ia.gate = gate_of(d);
-  ia.gscalar = scalar_gate(d);
+  ia.gscalar = scalar_gate(d); ia.diag_bf16 = d->diag == GLA_DIAG_BF16;
   ia.g = mat ? (const float*)(w + p.g) : nullptr;
   ia.A = w + p.A; ia.Qh = w + p.Qh; ia.KhT = w + p.KhT; ia.eg = (float*)(w + p.eg);
   if ((rs = tr.mark()) != GLA_OK) return rs;
@@ -384,7 +385,7 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   const bool split = gla::bwd_split(x.dtype, C);
   ia.q = q; ia.k = k; ia.la = log_alpha; ia.g = nullptr;
   ia.g2_out = split ? nullptr : (float*)(w + p.g);
-  ia.gate = gate_of(d); ia.gscalar = scalar_gate(d);
+  ia.gate = gate_of(d); ia.gscalar = scalar_gate(d); ia.diag_bf16 = d->diag == GLA_DIAG_BF16;
   ia.A = w + p.A; ia.QhT = w + p.QhT; ia.Kh = w + p.Kh; ia.KhT = w + p.KhT;
   ia.eg = (float*)(w + p.eg);
   if ((rs = tr.mark()) != GLA_OK) return rs;

@@ -40,6 +40,7 @@ struct IntraArgs {
   float* g2_out;         // [BH][T][dk] g * log2(e), or NULL
   GateFn gate;           // applied to la (not to g, which is already a cumsum)
   bool gscalar;          // la holds one gate per token: [BH][T], broadcast over dk
+  bool diag_bf16;        // rebased diagonal sub-blocks with bf16 operands (else fp32)
 };
 hipError_t launch_intra(const IntraArgs& a, hipStream_t s);
 

@@ -9,8 +9,15 @@
 //   - a sub-block with t in sub-chunk I and s in an earlier sub-chunk J is the MFMA
 //     product (Q_I * exp(g_I - g_rho)) (K_J * exp(g_rho - g_J))^T, rho = first row of I;
 //     both exponents are <= 0, so the rounded (bf16) operands stay in [0, |x|];
-//   - a diagonal sub-block is summed element by element in fp32 from log-space
-//     differences exp(g_t - g_s), which is in [0,1] for any finite gates.
+//   - a diagonal sub-block stays in fp32 (most, not all, intra-chunk products run on
+//     the half-precision units).  When the spread of g inside the sub-block is moderate
+//     (at most kDiagRange in log2 units, in every column) it is the same product on q and
+//     k rebased at the sub-block's first row, with fp32 operands and fp32 MFMA: the key
+//     factor exp(g_rho - g_s) is at most 2^96 and the query factor at least 2^-96, both
+//     normal fp32 numbers, so each term carries fp32 rounding only.  Otherwise it is
+//     summed element by element in fp32 from log-space differences exp(g_t - g_s), which
+//     is in [0,1] for any finite gates.  DIAG_BF16 (opt-in) takes the rebased product
+//     with bf16 operands instead, at the off-diagonal sub-blocks' operand rounding.
 // Alongside it emits, for the chunk, the decayed operands the inter-chunk kernels
 // consume (each nullable): Qh = q*exp(g) token-major, its transpose QhT, Kh =
 // k*exp(gamma - g) token-major, its transpose KhT, and exp(gamma).  The transposed
@@ -46,7 +53,8 @@ __device__ __forceinline__ void pair_decode(int p, int& I, int& J) {
   J = p - ii * (ii - 1) / 2;
 }
 
-template <typename Tin, typename OpT, typename XT, int C, bool G_WS, bool WANT_A, bool SG>
+template <typename Tin, typename OpT, typename XT, int C, bool G_WS, bool WANT_A, bool SG,
+          bool DIAG_BF16>
 __global__ __launch_bounds__(kThreads) void k_intra(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ la,
     const float* __restrict__ gws, OpT* __restrict__ A_out, OpT* __restrict__ Qh_out,
@@ -61,6 +69,8 @@ __global__ __launch_bounds__(kThreads) void k_intra(
   // largest spread of g * log2 e inside a 16-row sub-block for which the diagonal
   // sub-blocks take the rebased MFMA path (factors within 2^+-kDiagRange of the inputs)
   constexpr float kDiagRange = 96.f;
+  // operands of the rebased diagonal product: fp32 (fp32 MFMA), or bf16 when opted in
+  using DFrag = typename std::conditional<DIAG_BF16, Frag<OpT>, Frag<float>>::type;
   constexpr int IPT = (NITEM + kThreads - 1) / kThreads;
   constexpr int GLD = DB + 4;
   constexpr int XLD = DB + 8;
@@ -245,9 +255,9 @@ __global__ __launch_bounds__(kThreads) void k_intra(
       }
       // ---- diagonal sub-blocks ------------------------------------------------------
       // When the gates' spread inside every 16-row sub-block is moderate (the usual
-      // case), the same MFMA on operands rebased at the sub-block's first row (entries
-      // above the diagonal are dropped when the block is written); otherwise the exact
-      // fp32 log-space sum per (t, s, column).
+      // case), an MFMA on operands rebased at the sub-block's first row, fp32 unless
+      // opted into bf16 (entries above the diagonal are dropped when the block is
+      // written); otherwise the exact fp32 log-space sum per (t, s, column).
       if constexpr (G_WS) {   // g from the gate kernel: measure the spread here
         for (int idx = threadIdx.x; idx < NS * DB; idx += kThreads) {
           const int I = idx / DB, col = idx % DB;
@@ -268,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(
 #pragma unroll 1
             for (int kb = 0; kb < DB / 32; ++kb) {
               const int c0 = kb * 32 + 8 * qd;
-              Frag<OpT> fa, fb;
+              DFrag fa, fb;
               float gr[8], gq[8], xq[8], xk[8];
               load8(gr, gs + rho * GLD + c0);
               load8(gq, gs + tr * GLD + c0);
@@ -376,9 +386,10 @@ __global__ __launch_bounds__(kThreads) void k_intra(
 }
 
 // ---------------------------------------------------------------------------------
-template <typename Tin, typename OpT, typename XT, int C, bool GW, bool WA, bool SG = false>
+template <typename Tin, typename OpT, typename XT, int C, bool GW, bool WA, bool SG = false,
+          bool DB16 = false>
 static void launch_intra_k(const IntraArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_intra<Tin, OpT, XT, C, GW, WA, SG>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((k_intra<Tin, OpT, XT, C, GW, WA, SG, DB16>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
                      (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.la, a.g, (OpT*)a.A,
                      (OpT*)a.Qh, (XT*)a.QhT, (OpT*)a.Kh, (XT*)a.KhT, a.eg, a.g2_out, a.gate, a.T,
                      a.dk, a.N);
@@ -386,9 +397,18 @@ static void launch_intra_k(const IntraArgs& a, hipStream_t s) {
 template <typename Tin, typename OpT, typename XT, int C>
 static hipError_t launch_intra_t(const IntraArgs& a, hipStream_t s) {
   if (a.want_A) {
-    if (a.g) launch_intra_k<Tin, OpT, XT, C, true, true>(a, s);
-    else if (a.gscalar) launch_intra_k<Tin, OpT, XT, C, false, true, true>(a, s);
-    else launch_intra_k<Tin, OpT, XT, C, false, true>(a, s);
+    // the bf16 diagonal is an option of bf16 operands only
+    const bool db16 = a.diag_bf16 && sizeof(OpT) == 2;
+    if (a.g) {
+      if (db16) launch_intra_k<Tin, OpT, XT, C, true, true, false, true>(a, s);
+      else launch_intra_k<Tin, OpT, XT, C, true, true>(a, s);
+    } else if (a.gscalar) {
+      if (db16) launch_intra_k<Tin, OpT, XT, C, false, true, true, true>(a, s);
+      else launch_intra_k<Tin, OpT, XT, C, false, true, true>(a, s);
+    } else {
+      if (db16) launch_intra_k<Tin, OpT, XT, C, false, true, false, true>(a, s);
+      else launch_intra_k<Tin, OpT, XT, C, false, true>(a, s);
+    }
   } else {
     if (a.g) launch_intra_k<Tin, OpT, XT, C, true, false>(a, s);
     else if (a.gscalar) launch_intra_k<Tin, OpT, XT, C, false, false, true>(a, s);

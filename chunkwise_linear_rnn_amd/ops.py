@@ -7,12 +7,14 @@ import ctypes
 
 import torch
 
-from ._native import (BF16, F32, GATE_LOG_ALPHA, GATE_LOGITS, GATE_PER_KEY, GATE_SCALAR,
+from ._native import (BF16, DIAG_BF16, DIAG_F32, F32, GATE_LOG_ALPHA, GATE_LOGITS,
+                      GATE_PER_KEY, GATE_SCALAR,
                       MATERIALIZED, RECOMPUTE, PASS_BWD, PASS_FWD, PASS_STATES, GlaError, lib,
                       make_desc, make_gsa_desc, gsa_workspace_bytes, workspace_bytes)
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 _MODES = {"materialized": MATERIALIZED, "recompute": RECOMPUTE}
+_DIAGS = {"f32": DIAG_F32, "bf16": DIAG_BF16}
 
 
 def _ptr(t):
@@ -36,10 +38,13 @@ def _check(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _desc_from(q, v, chunk, subchunk, state_mode, gate_tau=None, scalar=False):
+def _desc_from(q, v, chunk, subchunk, state_mode, gate_tau=None, scalar=False, diag="f32"):
     """gate_tau: None when the log_alpha argument is log_alpha itself, else the temperature
     of gate logits (log_alpha = logsigmoid(x) / gate_tau).  scalar: one gate per token
-    ([B, H, T]) instead of one per key dimension."""
+    ([B, H, T]) instead of one per key dimension.  diag: arithmetic of the diagonal
+    intra-chunk sub-blocks, "f32" (default) or "bf16" (opt-in, bf16 inputs)."""
+    if diag not in _DIAGS:
+        raise ValueError(f"diag must be one of {sorted(_DIAGS)}")
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q and v must be [B, H, T, d]")
     if q.dtype not in _DT:
@@ -50,9 +55,9 @@ def _desc_from(q, v, chunk, subchunk, state_mode, gate_tau=None, scalar=False):
     shape = GATE_SCALAR if scalar else GATE_PER_KEY
     if gate_tau is None:
         return make_desc(B, H, T, dk, dv, chunk, subchunk, _DT[q.dtype], mode,
-                         gate_shape=shape)
+                         gate_shape=shape, diag=_DIAGS[diag])
     return make_desc(B, H, T, dk, dv, chunk, subchunk, _DT[q.dtype], mode, GATE_LOGITS,
-                     float(gate_tau), shape)
+                     float(gate_tau), shape, _DIAGS[diag])
 
 
 def _is_scalar(log_alpha):
@@ -64,13 +69,25 @@ def _gate_shape(log_alpha, B, H, T, dk):
     return (B, H, T) if _is_scalar(log_alpha) else (B, H, T, dk)
 
 
-def _workspace(desc, pass_, device, workspace):
-    need = workspace_bytes(desc, pass_)
+def _ws_buffer(need, device, workspace):
+    """(buffer, its size in bytes): the caller's workspace after checking its device,
+    layout and size, or a fresh one of `need` bytes.  The real size goes to the C ABI,
+    which checks it against what the call needs."""
     if workspace is not None:
-        if workspace.device != device or workspace.numel() * workspace.element_size() < need:
-            raise ValueError(f"workspace must hold at least {need} bytes on {device}")
-        return workspace, need
+        if not isinstance(workspace, torch.Tensor) or workspace.device != device:
+            raise ValueError(f"workspace must be a tensor on {device}")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        size = workspace.numel() * workspace.element_size()
+        if size < need:
+            raise ValueError(f"workspace must hold at least {need} bytes on {device} "
+                             f"(it holds {size})")
+        return workspace, size
     return torch.empty(max(need, 1), dtype=torch.uint8, device=device), need
+
+
+def _workspace(desc, pass_, device, workspace):
+    return _ws_buffer(workspace_bytes(desc, pass_), device, workspace)
 
 
 def _call(name, st):
@@ -79,12 +96,13 @@ def _call(name, st):
 
 
 def fwd(q, k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, state_mode="recompute",
-        final_state=True, workspace=None, gate_tau=None):
+        final_state=True, workspace=None, gate_tau=None, diag="f32"):
     """o, S_T = the GLA layer forward (S_T is None when final_state is False).
     gate_tau: when set, log_alpha holds gate logits x and the layer uses
     logsigmoid(x) / gate_tau.  log_alpha [B, H, T] (instead of [B, H, T, dk]) is a scalar
-    gate per token, shared by every key dimension."""
-    desc = _desc_from(q, v, chunk, subchunk, state_mode, gate_tau, _is_scalar(log_alpha))
+    gate per token, shared by every key dimension.  diag: "f32" or "bf16" diagonal
+    intra-chunk sub-blocks."""
+    desc = _desc_from(q, v, chunk, subchunk, state_mode, gate_tau, _is_scalar(log_alpha), diag)
     dev, dt = q.device, q.dtype
     B, H, T, dk, dv = desc.B, desc.H, desc.T, desc.dk, desc.dv
     for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)),
@@ -103,11 +121,11 @@ def fwd(q, k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, state_mode="recom
 
 
 def bwd(q, k, v, log_alpha, dO, S0=None, dS_T=None, *, chunk=64, subchunk=16,
-        want_dS0=True, workspace=None, gate_tau=None):
+        want_dS0=True, workspace=None, gate_tau=None, diag="f32"):
     """dq, dk, dv, dlog_alpha, dS0 for the loss gradient (dO, dS_T).  With gate_tau set
     (gate logits in log_alpha) the fourth output is the gradient with respect to them.
     A scalar gate (log_alpha [B, H, T]) gets its gradient summed over the key dimension."""
-    desc = _desc_from(q, v, chunk, subchunk, RECOMPUTE, gate_tau, _is_scalar(log_alpha))
+    desc = _desc_from(q, v, chunk, subchunk, RECOMPUTE, gate_tau, _is_scalar(log_alpha), diag)
     dev, dt = q.device, q.dtype
     B, H, T, dk, dv = desc.B, desc.H, desc.T, desc.dk, desc.dv
     for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)),
@@ -252,8 +270,7 @@ def gsa_fwd(q, k, v, log_alpha, *, workspace=None):
                       (log_alpha, "log_alpha", (B, H, T, m))):
         _check(t, n, shp, torch.float32, dev)
     o = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
-    need = gsa_workspace_bytes(desc, PASS_FWD)
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws, need = _ws_buffer(gsa_workspace_bytes(desc, PASS_FWD), dev, workspace)
     _call("gla_gsa_fwd", lib().gla_gsa_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                            _ptr(log_alpha), _ptr(o), _ptr(ws), need, _stream(dev)))
     return o
@@ -268,8 +285,7 @@ def gsa_bwd(q, k, v, log_alpha, dO, *, workspace=None):
                       (log_alpha, "log_alpha", (B, H, T, m)), (dO, "dO", (B, H, T, dv))):
         _check(t, n, shp, torch.float32, dev)
     dq, dk_, dv_, dla = (torch.empty_like(x) for x in (q, k, v, log_alpha))
-    need = gsa_workspace_bytes(desc, PASS_BWD)
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws, need = _ws_buffer(gsa_workspace_bytes(desc, PASS_BWD), dev, workspace)
     _call("gla_gsa_bwd", lib().gla_gsa_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                            _ptr(log_alpha), _ptr(dO), _ptr(dq), _ptr(dk_),
                                            _ptr(dv_), _ptr(dla), _ptr(ws), need, _stream(dev)))

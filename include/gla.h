@@ -92,6 +92,22 @@ typedef enum { GLA_GATE_LOG_ALPHA = 0, GLA_GATE_LOGITS = 1 } gla_gate_t;
  * gate (the meaning of the values) and gate_shape combine freely. */
 typedef enum { GLA_GATE_PER_KEY = 0, GLA_GATE_SCALAR = 1 } gla_gate_shape_t;
 
+/* Arithmetic of the diagonal 16 x 16 sub-blocks of the intra-chunk matrix A (Approach
+ * section: with two-level chunking *most* intra-chunk products run on the half-precision
+ * matrix units; the plainest reading of "most" is that the products between different
+ * sub-chunks do, while the sub-blocks on the diagonal stay in full precision).
+ *  GLA_DIAG_F32: fp32 throughout.  When the spread of the chunk-local cumulative log-gate
+ *    inside every 16-row sub-block is at most 96 (in log2 units, per key dimension) the
+ *    sub-block is an fp32 matrix product (v_mfma_f32_16x16x4_f32) of q and k rebased at
+ *    the sub-block's first row: every factor exp(g_t - g_rho), exp(g_rho - g_s) is then a
+ *    normal fp32 number, so each term carries fp32 rounding only.  Otherwise the exact
+ *    log-space sum of q_td k_sd exp(g_td - g_sd) per (t, s, d) in fp32.  The default.
+ *  GLA_DIAG_BF16: the same rebased product with bf16 operands (one bf16 MFMA per 32 key
+ *    dimensions instead of eight fp32 ones); the operand rounding (2^-9 relative per
+ *    factor) matches that of the off-diagonal sub-blocks.  Opt-in, for speed; bf16
+ *    inputs only (fp32 inputs always take GLA_DIAG_F32). */
+typedef enum { GLA_DIAG_F32 = 0, GLA_DIAG_BF16 = 1 } gla_diag_t;
+
 typedef struct {
   int32_t B, H, T;     /* batch, heads, sequence length (any of them may be 0)          */
   int32_t dk, dv;      /* key and value head dimensions                                  */
@@ -102,6 +118,7 @@ typedef struct {
   int32_t gate;        /* gla_gate_t (zero: log_alpha given directly)                      */
   float gate_tau;      /* temperature of GLA_GATE_LOGITS (> 0, finite); unused otherwise   */
   int32_t gate_shape;  /* gla_gate_shape_t (zero: one gate per key dimension)              */
+  int32_t diag;        /* gla_diag_t (zero: fp32 diagonal sub-blocks)                      */
 } gla_desc_t;
 
 /* Supported by this build (else GLA_ERR_UNSUPPORTED):
@@ -117,7 +134,7 @@ int32_t gla_version(void);
 
 /* Host-only validation of a descriptor for a pass (no device call).  Returns GLA_OK,
  * GLA_ERR_INVALID_ARG (desc NULL, a negative size, chunk or subchunk < 1,
- * chunk % subchunk != 0, unknown dtype/mode/pass/gate/gate_shape, GLA_GATE_LOGITS with
+ * chunk % subchunk != 0, unknown dtype/mode/pass/gate/gate_shape/diag, GLA_GATE_LOGITS with
  * gate_tau not a positive finite number) or GLA_ERR_UNSUPPORTED. */
 gla_status_t gla_validate(const gla_desc_t* desc, int32_t pass);
 

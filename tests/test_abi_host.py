@@ -188,3 +188,31 @@ def test_gsa_descriptor_validation(native):
     p = ctypes.c_void_p(16)
     # a missing workspace is reported before any launch
     assert L.gla_gsa_fwd(ctypes.byref(G(1, 1, 64, 64, 64, 64)), p, p, p, p, p, None, 0, None) == 3
+
+
+def test_caller_workspace_is_checked(native):
+    """A caller-provided workspace that is too small, on another device, or not contiguous
+    is refused before any call (the real byte size goes to the C ABI otherwise)."""
+    import torch
+    from chunkwise_linear_rnn_amd.ops import _ws_buffer
+    cpu = torch.device("cpu")
+    with pytest.raises(ValueError):
+        _ws_buffer(100, cpu, torch.empty(99, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        _ws_buffer(100, torch.device("cuda", 0), torch.empty(200, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        _ws_buffer(100, cpu, torch.empty(400, dtype=torch.uint8)[::2])
+    buf, size = _ws_buffer(100, cpu, torch.empty(64, dtype=torch.float32))
+    assert size == 256
+    buf, size = _ws_buffer(100, cpu, None)
+    assert size == 100 and buf.numel() == 100
+
+
+def test_diag_field_validation(native):
+    D = native.make_desc
+    d = D(1, 1, 64, 64, 64, 64, 16, native.BF16, native.RECOMPUTE, diag=native.DIAG_BF16)
+    assert native.validate(d) == 0
+    d.diag = 2
+    assert native.validate(d) == 1
+    d.diag = -1
+    assert native.validate(d) == 1

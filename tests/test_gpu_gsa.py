@@ -85,3 +85,26 @@ def test_gsa_full_size_sampled(gla):
     a = (d2["q"][b, h], d2["k"][b, h], d2["v"][b, h], d2["log_alpha_slot"][b, h])
     for kname, t, r in zip(("dq", "dk", "dv", "dla"), g, gsa.gsa_bwd(*a, d2["dO"][b, h])):
         check(f"{kname}[1,0]", host(t)[b, h], r, "f32")
+
+
+def test_gsa_caller_workspace(gla):
+    """A caller workspace is checked for size before the call (ValueError when short) and
+    a large enough one gives the same output as the library-sized one."""
+    cfg = GlaConfig(name="gsaws", dtype="f32", B=1, H=1, T=100, dk=64, dv=64, chunk=64)
+    say(f"[gsa] caller workspace {cfg}")
+    d = generate_gsa(cfg, 64)
+    x = _dev(d)
+    desc = gla.make_gsa_desc(1, 1, 100, 64, 64, 64, gla.F32)
+    need_f = gla.gsa_workspace_bytes(desc, gla.PASS_FWD)
+    need_b = gla.gsa_workspace_bytes(desc, gla.PASS_BWD)
+    with pytest.raises(ValueError):
+        gla.gsa_fwd(x["q"], x["k"], x["v"], x["log_alpha_slot"],
+                    workspace=torch.empty(need_f - 1, dtype=torch.uint8, device=DEV))
+    with pytest.raises(ValueError):
+        gla.gsa_bwd(x["q"], x["k"], x["v"], x["log_alpha_slot"], x["dO"],
+                    workspace=torch.empty(need_b // 2, dtype=torch.uint8, device=DEV))
+    ws = torch.empty(need_b + 4096, dtype=torch.uint8, device=DEV)
+    a = gla.gsa_fwd(x["q"], x["k"], x["v"], x["log_alpha_slot"], workspace=ws)
+    b = gla.gsa_fwd(x["q"], x["k"], x["v"], x["log_alpha_slot"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

@@ -2,13 +2,15 @@
 
 Small cases (several chunks, ragged tails, initial and final state gradients) are
 compared element by element on every output.  The full-size workloads are compared on
-sampled (batch, head) pairs, for which the oracle runs the whole sequence."""
+every (batch, head) pair, each head on its own and all together: the oracle runs the
+whole sequence of each head in a pool of worker processes."""
 import numpy as np
 import pytest
 
 from gla_inputs import CONFIGS, GlaConfig, generate
 from oracle import chunkwise
-from tests.gpu_util import TOL, check, dev_inputs, host, oracle_heads, pick, say
+from tests.gpu_util import (TOL, check, check_heads, dev_inputs, host, oracle_heads,
+                            oracle_heads_pool, pick, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -95,27 +97,61 @@ def test_tiny_f32_config(gla):
             check(k, host(t)[0:1, 0], ref[k], "f32")
 
 
-@pytest.mark.parametrize("cfg_name,heads", [
-    ("gla340m_t2k", [(0, 0), (7, 3)]),
-    ("gla1p3b_t2k", [(0, 1), (3, 3)]),
-])
-def test_full_size_configs_sampled_heads(gla, cfg_name, heads):
+def _all_heads(cfg):
+    return [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+
+
+def _check_all(ref, heads, dtype, o=None, ST=None, grads=None):
+    if o is not None:
+        check_heads("o", host(o), ref["o"], heads, dtype)
+    if ST is not None:
+        check_heads("S_T", host(ST), ref["S_T"], heads, dtype)
+    if grads is not None:
+        for kname, t in zip(("dq", "dk", "dv", "dla", "dS0"), grads):
+            check_heads(kname, host(t), ref[kname], heads, dtype)
+
+
+@pytest.mark.parametrize("cfg_name", ["gla340m_t2k", "gla1p3b_t2k"])
+def test_full_size_configs_all_heads(gla, cfg_name):
+    """The 340M and 1.3B head shapes at T = 2048: every output of every (batch, head)."""
     cfg = CONFIGS[cfg_name]
-    say(f"[config] {cfg} heads={heads}")
+    heads = _all_heads(cfg)
+    say(f"[config] {cfg} all {len(heads)} heads")
     d = generate(cfg)
     x = dev_inputs(d, cfg.dtype, DEV)
     o, ST = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], chunk=cfg.chunk)
     g = gla.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["dO"], chunk=cfg.chunk)
     torch.cuda.synchronize()
-    ref = oracle_heads(d, heads)
-    check("o", pick(host(o), heads), ref["o"], cfg.dtype)
-    check("S_T", pick(host(ST), heads), ref["S_T"], cfg.dtype)
-    for k, t in zip(("dq", "dk", "dv", "dla", "dS0"), g):
-        check(k, pick(host(t), heads), ref[k], cfg.dtype)
+    say("    oracle on every head")
+    ref = oracle_heads_pool(d, heads)
+    _check_all(ref, heads, cfg.dtype, o, ST, g)
+
+
+def test_materialized_full_shape(gla):
+    """The materialized-states forward at the 1.3B head shape (dk 256, dv 512, chunk 64),
+    every head against the oracle, and against the recompute forward."""
+    cfg = CONFIGS["gla1p3b_t2k"]
+    heads = _all_heads(cfg)
+    say(f"[config] {cfg} materialized forward, all {len(heads)} heads")
+    d = generate(cfg, with_dO=False)
+    x = dev_inputs(d, cfg.dtype, DEV, names=("q", "k", "v", "log_alpha"))
+    o_m, ST_m = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], chunk=cfg.chunk,
+                        state_mode="materialized")
+    o_r, ST_r = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], chunk=cfg.chunk,
+                        state_mode="recompute")
+    torch.cuda.synchronize()
+    from oracle.compare import normwise
+    nw = normwise(host(o_m), host(o_r))
+    say(f"    materialized vs recompute o: normwise={nw:.3e}")
+    assert nw <= TOL["bf16"]["normwise"]
+    say("    oracle on every head")
+    ref = oracle_heads_pool(d, heads, bwd=False)
+    _check_all(ref, heads, cfg.dtype, o_m, ST_m)
 
 
 def test_long_sequence_chained(gla):
-    """T = 20480 as one call and as 10 chained 2048-token calls (S_T -> S0)."""
+    """T = 20480 as one call and as 10 chained 2048-token calls (S_T -> S0); every head
+    against the oracle."""
     cfg = CONFIGS["long_t20k"]
     say(f"[config] {cfg}")
     d = generate(cfg, with_dO=False)
@@ -137,28 +173,28 @@ def test_long_sequence_chained(gla):
     say(f"    chained vs single: normwise={nw:.3e} bitwise={np.array_equal(a, b)}")
     assert nw <= 1e-6
     assert normwise(host(S), host(S1)) <= 1e-6
-    heads = [(0, 2)]
-    ref = oracle_heads(d, heads, bwd=False)
-    check("o", pick(a, heads), ref["o"], cfg.dtype)
-    check("S_T", pick(host(S1), heads), ref["S_T"], cfg.dtype)
+    heads = _all_heads(cfg)
+    say(f"    oracle on all {len(heads)} heads")
+    ref = oracle_heads_pool(d, heads, bwd=False)
+    _check_all(ref, heads, cfg.dtype, o1, S1)
+    check_heads("o chained", b, ref["o"], heads, cfg.dtype)
 
 
 @pytest.mark.parametrize("T,C", [(1024, 64), (1024, 128), (4096, 64), (4096, 128),
                                  (8192, 64), (8192, 128)])
 def test_sweep_configs(gla, T, C):
+    """The training-throughput sweep (fast-decay gates), every head of every run."""
     cfg = CONFIGS[f"sweep_t{T}_c{C}"]
-    heads = [(cfg.B - 1, 1)]
-    say(f"[config] {cfg} heads={heads}")
+    heads = _all_heads(cfg)
+    say(f"[config] {cfg} all {len(heads)} heads")
     d = generate(cfg)
     x = dev_inputs(d, cfg.dtype, DEV)
     o, ST = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], chunk=C)
     g = gla.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["dO"], chunk=C)
     torch.cuda.synchronize()
-    ref = oracle_heads(d, heads)
-    check("o", pick(host(o), heads), ref["o"], cfg.dtype)
-    check("S_T", pick(host(ST), heads), ref["S_T"], cfg.dtype)
-    for k, t in zip(("dq", "dk", "dv", "dla", "dS0"), g):
-        check(k, pick(host(t), heads), ref[k], cfg.dtype)
+    say("    oracle on every head")
+    ref = oracle_heads_pool(d, heads)
+    _check_all(ref, heads, cfg.dtype, o, ST, g)
 
 
 def test_gate_cumsum_kernel(gla):
@@ -304,3 +340,59 @@ def test_diagonal_paths_bf16(gla):
     check("S_T", pick(host(ST), heads), ref["S_T"], "bf16")
     for k, t in zip(("dq", "dk", "dv", "dla"), g[:4]):
         check(k, pick(host(t), heads), ref[k], "bf16")
+
+
+@pytest.mark.parametrize("diag", ["f32", "bf16"])
+def test_diagonal_rebased_band(gla, diag):
+    """The rebased diagonal sub-block product where its factors are largest: a few key
+    columns decay by log_alpha in [-4, -1] at every step, so the cumulative gate spreads by
+    about 21 to 87 (log2 units) inside each 16-row sub-block, below the 96 that switches to
+    the log-space sum.  The key factors exp(g_rho - g_s) reach ~2^87 and the query factors
+    ~2^-87.  Default fp32 diagonal and the opt-in bf16 diagonal, forward and backward, at
+    chunk 64 and 128."""
+    for C, T, dk in ((64, 320, 128), (128, 300, 256)):
+        cfg = GlaConfig("diagband", "bf16", 1, 2, T, dk, 128, C, seed=21)
+        say(f"[edge] diagonal band diag={diag} {cfg}")
+        d = generate(cfg)
+        la = d["log_alpha"].copy()
+        rng = np.random.default_rng(5)
+        cols = [3, 17, dk - 9]
+        la[..., cols] = -rng.uniform(1.0, 4.0, size=la[..., cols].shape)
+        from gla_inputs import round_to_bf16_bits, bf16_bits_to_f64
+        bits = round_to_bf16_bits(la)
+        d2 = dict(d)
+        d2["log_alpha"], d2["log_alpha_store"] = bf16_bits_to_f64(bits), bits
+        # the spread per 16-row sub-block of the strongly decaying columns, in log2 units
+        L = np.cumsum(d2["log_alpha"][0, 0, :(T // 16) * 16, cols].reshape(len(cols), -1, 16),
+                      axis=-1) / np.log(2.0)
+        spread = L[..., -1] - L[..., 0]
+        say(f"    spread (log2) of the decaying columns: {(-spread).min():.1f} .. {(-spread).max():.1f}")
+        assert (-spread).max() < 96.0 and (-spread).min() > 15.0
+        x = dev_inputs(d2, "bf16", DEV)
+        o, ST = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], chunk=C, diag=diag)
+        om, _ = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], chunk=C, diag=diag,
+                        state_mode="materialized")
+        g = gla.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["dO"], chunk=C, diag=diag)
+        torch.cuda.synchronize()
+        heads = [(0, 0), (0, 1)]
+        ref = oracle_heads(d2, heads)
+        check_heads("o", host(o), ref["o"], heads, "bf16")
+        check_heads("o mat", host(om), ref["o"], heads, "bf16")
+        check_heads("S_T", host(ST), ref["S_T"], heads, "bf16")
+        for kname, t in zip(("dq", "dk", "dv", "dla", "dS0"), g):
+            check_heads(kname, host(t), ref[kname], heads, "bf16")
+
+
+def test_diag_option_fp32_inputs_and_invalid(gla):
+    """fp32 inputs ignore the bf16-diagonal option (they are fp32 throughout) and an
+    unknown diagonal mode is an invalid argument."""
+    cfg = GlaConfig("diagf32", "f32", 1, 1, 130, 64, 64, 64, seed=2)
+    say(f"[edge] diagonal option with fp32 inputs {cfg}")
+    d = generate(cfg)
+    x = dev_inputs(d, "f32", DEV)
+    a, _ = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], diag="f32")
+    b, _ = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], diag="bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    with pytest.raises(ValueError):
+        gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], diag="fp8")
