@@ -53,6 +53,7 @@ SIGNATURES = {
     "gla_chunk_fwd": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "gla_chunk_bwd": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp, _sz, _vp]),
+    "gla_chunk_fwd_noalloc": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "gla_decode": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "gla_gsa_validate": (_i32, [_PGSA]),
     "gla_gsa_workspace_bytes": (_i32, [_PGSA, _i32, ctypes.POINTER(_sz)]),

@@ -29,8 +29,10 @@
  *    bytes (16-byte aligned; its contents on entry do not matter).
  *  - Outputs are overwritten, never accumulated, and must not alias any input.
  *  - Calls enqueue kernels on `stream` (a hipStream_t; NULL is the default stream) and
- *    return before they finish.  The library keeps no global mutable state, so calls
- *    are reentrant; two calls that share a workspace must be ordered on one stream.
+ *    return before they finish.  The library keeps no global mutable state (apart from
+ *    the scratch array of gla_chunk_fwd_noalloc and its per-device address, set once),
+ *    so calls are reentrant; two calls that share a workspace must be ordered on one
+ *    stream.
  *  - Nullable pointers (marked) mean "zero" for inputs and "not wanted" for outputs.
  *  - Errors are reported by status code; no C++ exception crosses this boundary.  All
  *    argument checks run on the host before any launch, and on an error no output is
@@ -164,6 +166,23 @@ gla_status_t gla_chunk_states(const gla_desc_t* desc, const void* k, const void*
 gla_status_t gla_chunk_fwd(const gla_desc_t* desc, const void* q, const void* k,
                            const void* v, const void* log_alpha, const float* S0,
                            void* o, float* S_T, void* ws, size_t ws_bytes, void* stream);
+
+/* Allocation-free forward, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation and kernels as gla_chunk_fwd, with its scratch space taken from a fixed
+ * device array of GLA_NOALLOC_SCRATCH_BYTES inside the library instead of a workspace.
+ * The caller still passes every input and output.  The array is placed on a device at
+ * the first call there and held until the process ends; every call on one device uses
+ * that device's array, so calls that overlap on one device (other streams, other host
+ * threads) race on it and must be ordered by the caller.  Its contents on entry do not
+ * matter (every byte the kernels read is written first in the same call).  A problem
+ * whose gla_workspace_bytes(desc, GLA_PASS_FWD) exceeds GLA_NOALLOC_SCRATCH_BYTES is
+ * GLA_ERR_WORKSPACE, returned before the device is touched; other errors as for
+ * gla_chunk_fwd.  No device memory is allocated or freed by this call. */
+#define GLA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gla_status_t gla_chunk_fwd_noalloc(const gla_desc_t* desc, const void* q, const void* k,
+                                   const void* v, const void* log_alpha, const float* S0,
+                                   void* o, float* S_T, void* stream);
 
 /* Backward of the layer for the loss gradient (dO, dS_T).  Inputs q, k, v, log_alpha,
  * S0 (nullable), dO (required), dS_T (nullable: zero).  Outputs dq, dk, dv,

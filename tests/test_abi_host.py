@@ -216,3 +216,18 @@ def test_diag_field_validation(native):
     assert native.validate(d) == 1
     d.diag = -1
     assert native.validate(d) == 1
+
+
+def test_noalloc_refuses_oversized_problem_on_host(native):
+    """gla_chunk_fwd_noalloc refuses a forward whose workspace would exceed its fixed
+    scratch array (GLA_ERR_WORKSPACE) before touching the device, and an invalid
+    descriptor as gla_chunk_fwd does; the pointers below are never dereferenced."""
+    D = native.make_desc
+    big = D(16, 4, 8192, 256, 512, 64, 16, native.BF16, native.MATERIALIZED)
+    assert native.workspace_bytes(big, native.PASS_FWD) > (128 << 20)
+    p = ctypes.c_void_p(1 << 20)
+    L = native.lib()
+    assert L.gla_chunk_fwd_noalloc(ctypes.byref(big), p, p, p, p, None, p, None, None) == 3
+    bad = D(1, 1, 64, 96, 64)
+    assert L.gla_chunk_fwd_noalloc(ctypes.byref(bad), p, p, p, p, None, p, None, None) == 2
+    assert L.gla_chunk_fwd_noalloc(None, p, p, p, p, None, p, None, None) == 1
