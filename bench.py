@@ -332,6 +332,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gla1p3b_t2k")
     ap.add_argument("--state-mode", default="recompute", choices=["recompute", "materialized"])
+    ap.add_argument("--scalar-gates", action="store_true",
+                    help="time the step with scalar gates (one per token and head, [B, H, T]) "
+                         "as the main measurement, with its per-stage table")
+    ap.add_argument("--diag", default="f32", choices=["f32", "bf16"],
+                    help="arithmetic of the diagonal intra-chunk sub-blocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the side measurements: decode step, gate-logit and scalar-gate "
@@ -389,9 +394,13 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     q, k, v, la, dO = (up(n) for n in ("q", "k", "v", "log_alpha", "dO"))
+    if args.scalar_gates:
+        la = up("log_alpha_scalar")
     B, H, T, dk, dv, C = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.chunk
     mode = nat.RECOMPUTE if args.state_mode == "recompute" else nat.MATERIALIZED
-    desc = nat.make_desc(B, H, T, dk, dv, C, cfg.subchunk, nat.BF16 if cfg.dtype == "bf16" else nat.F32, mode)
+    desc = nat.make_desc(B, H, T, dk, dv, C, cfg.subchunk, nat.BF16 if cfg.dtype == "bf16" else nat.F32, mode,
+                         gate_shape=nat.GATE_SCALAR if args.scalar_gates else nat.GATE_PER_KEY,
+                         diag=nat.DIAG_BF16 if args.diag == "bf16" else nat.DIAG_F32)
     o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
     S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     dq, dk_, dv_, dla = (torch.empty_like(x) for x in (q, k, v, la))
@@ -596,7 +605,9 @@ def main():
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": cfg.name, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": C,
+        "config": {"workload": cfg.name + ("_scalar_gates" if args.scalar_gates else "")
+                   + ("_diag_bf16" if args.diag == "bf16" else ""),
+                   "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": C,
                    "subchunk": cfg.subchunk, "state_mode": mode_s, "global_batch": B,
                    "seq_len": T, "parallelism": "none (1 GPU)"},
         "tflops": tflops, "mfma_peak_frac": flops / (ms_per_step * 1e-3) / PEAK_BF16,

@@ -246,7 +246,7 @@ constexpr int kDqkLds = 64 * (64 + 4) * 4 + 64 * (64 + 4) * 4 + 2 * 64 * (64 + 8
 // SFRAG: S and dS in MFMA fragment order (fragment (16-row block, 32-column block) of a
 // chunk's [dk][dv] state: lane 16 q + r holds row r, columns 8 q .. 8 q + 7), as the scans
 // write them for 128-column tiles; otherwise row-major.
-template <typename Tin, typename OpT, bool SFRAG>
+template <typename Tin, typename OpT, bool SFRAG, bool SG>
 __device__ __forceinline__ void bwd_dqk_body(
     char* __restrict__ arena, int lt, const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dO, int gscalar, const OpT* __restrict__ S,
@@ -400,6 +400,65 @@ __device__ __forceinline__ void bwd_dqk_body(
       adk[m][e] *= __builtin_amdgcn_exp2f(gl - gt[e]);
     }
   }
+  if constexpr (SG) {
+    // Scalar gates: exp(g_t - g_s) is the same for every column (g of column 0 stands for
+    // all), so the intra-chunk terms are two MFMA products with the C x C matrix
+    // P = dA * D, D[t][s] = exp(g_t - g_s) (s <= t), formed in fp32 in place of dA:
+    //     dq[t] += sum_{s <= t} P[t][s] k_s,     dk[s] += sum_{t >= s} P[t][s] q_t,
+    // P entering as three bf16 parts (high, middle, low: fp32-exact) against the exact
+    // bf16 q and k.  Tiles above the diagonal tile row are never read.
+    for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
+      const int t = idx / C, s2 = idx % C;
+      if (s2 <= t) dAs[t * FLD + s2] *= __builtin_amdgcn_exp2f(gs[t] - gs[s2]);
+    }
+    __syncthreads();
+    auto split3 = [](float x, Frag<OpT>& h, Frag<OpT>& md, Frag<OpT>& lo, int e) {
+      h.set(e, x);
+      const float r1 = x - h.get(e);
+      md.set(e, r1);
+      lo.set(e, r1 - md.get(e));
+    };
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      f32x4 tq = {0.f, 0.f, 0.f, 0.f}, tk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < C / 32; ++kb) {
+        if (32 * kb < 16 * (m + 1)) {   // dq rows of tile m: sources s < 16 (m + 1)
+          Frag<OpT> h, md, lo, fb;
+          float xa[8];
+          load8(xa, dAs + (16 * m + r) * FLD + kb * 32 + 8 * qd);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int s2 = kb * 32 + 8 * qd + e;
+            const bool on = s2 < 16 * (m + 1);
+            split3(on ? xa[e] : 0.f, h, md, lo, e);
+            fb.set(e, on ? to_f32(ks[s2 * XLD + c]) : 0.f);
+          }
+          mma(tq, h, fb);
+          mma(tq, md, fb);
+          mma(tq, lo, fb);
+        }
+        if (32 * kb + 31 >= 16 * m) {   // dk rows of tile m: sources t >= 16 m
+          Frag<OpT> h, md, lo, fb;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int t = kb * 32 + 8 * qd + e;
+            const bool on = t >= 16 * m;
+            split3(on ? dAs[t * FLD + 16 * m + r] : 0.f, h, md, lo, e);
+            fb.set(e, on ? to_f32(qs[t * XLD + c]) : 0.f);
+          }
+          mma(tk, h, fb);
+          mma(tk, md, fb);
+          mma(tk, lo, fb);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        adq[m][e] += tq[e];
+        adk[m][e] += tk[e];
+      }
+    }
+  } else {
   // intra-chunk, off-diagonal sub-blocks (split bf16 operands, three MFMAs each)
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
@@ -479,8 +538,6 @@ __device__ __forceinline__ void bwd_dqk_body(
     dkd[(base + jj) * GLD + cd] = ak[jj];
   }
   __syncthreads();
-  // finish dq, dk; D = q*dq - k*dk and its chunk-local suffix sums, in registers
-  float Dv[NM][4];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -488,6 +545,15 @@ __device__ __forceinline__ void bwd_dqk_body(
       const int t = 16 * m + 4 * qd + e;
       adq[m][e] += dqd[t * FLD + c];
       adk[m][e] += dkd[t * GLD + c];
+    }
+  }
+  // finish dq, dk; D = q*dq - k*dk and its chunk-local suffix sums, in registers
+  float Dv[NM][4];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * m + 4 * qd + e;
       Dv[m][e] = to_f32(qs[t * XLD + c]) * adq[m][e] - to_f32(ks[t * XLD + c]) * adk[m][e];
     }
   // dq, dk, dlog_alpha of the block leave as 16-byte rows through LDS (the dA and g
@@ -833,7 +899,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(
 // The two chunk-64 backward kernels as one launch: dq / dk / dlog_alpha workgroups and dv
 // workgroups interleaved in proportion (a dv workgroup needs neither the chunk totals nor
 // anything the dq / dk workgroups write), so that their memory phases overlap on each CU.
-template <typename Tin, typename OpT, bool SFRAG>
+template <typename Tin, typename OpT, bool SFRAG, bool SG>
 __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk_dv(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dO, int gscalar, const OpT* __restrict__ S,
@@ -848,7 +914,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk_dv(
   // Bresenham split: logical id L is a dq/dk workgroup when the count of them up to L grows
   const int before = (int)(((long)L * n_dqk) / total), upto = (int)(((long)(L + 1) * n_dqk) / total);
   if (upto > before)
-    bwd_dqk_body<Tin, OpT, SFRAG>(arena, before, q, k, v, dO, gscalar, S, dS, dq, dk_out, tot, cT, la, gf,
+    bwd_dqk_body<Tin, OpT, SFRAG, SG>(arena, before, q, k, v, dO, gscalar, S, dS, dq, dk_out, tot, cT, la, gf,
                            dla, dla_part, T, dk, dv, N);
   else
     bwd_dv_body<Tin, OpT, SFRAG>(arena, L - before, Kh, A, dS, dO, dv_out, T, dk, dv, N);
@@ -859,7 +925,9 @@ template <typename Tin, typename OpT, int C, int DK>
 static hipError_t launch_bwd_t2(const BwdArgs& a, hipStream_t s) {
   if constexpr (C == 64 && sizeof(OpT) == 2) {
     const int n_dqk = (a.dk / 64) * a.N * a.BH, n_dv = (a.dv / 64) * a.N * a.BH;
-    auto kern = a.s_frag ? k_bwd_dqk_dv<Tin, OpT, true> : k_bwd_dqk_dv<Tin, OpT, false>;
+    // scalar gates: the C x C decay-matrix form of the intra-chunk terms
+    auto kern = a.gscalar ? (a.s_frag ? k_bwd_dqk_dv<Tin, OpT, true, true> : k_bwd_dqk_dv<Tin, OpT, false, true>)
+                          : (a.s_frag ? k_bwd_dqk_dv<Tin, OpT, true, false> : k_bwd_dqk_dv<Tin, OpT, false, false>);
     hipLaunchKernelGGL(kern, dim3(n_dqk + n_dv), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO,
                        a.gscalar ? 1 : 0, (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq,

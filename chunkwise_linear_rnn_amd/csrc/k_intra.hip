@@ -53,6 +53,40 @@ __device__ __forceinline__ void pair_decode(int p, int& I, int& J) {
   J = p - ii * (ii - 1) / 2;
 }
 
+// One 8-token piece x[0..8) (tokens r8 .. r8 + 7 of the chunk, key dimension d) of a
+// chunk's transposed decayed operand, in the layout the inter-chunk kernels read:
+//  - XT = float with bf16 operands (the backward's scans): MFMA fragment order, for 16-row
+//    block d / 16 and 32-token block kb of the chunk the 64 lanes' 16-byte pieces of the
+//    bf16 high part, then of the bf16 remainder; this piece belongs to lane 16 q + d % 16;
+//  - XT = bf16: the same fragment order, one plane;
+//  - XT = float with fp32 operands: rows [dk][C], token-contiguous.
+// bhi = batch*head * N + chunk.
+template <typename OpT, typename XT, int C>
+__device__ __forceinline__ void store_xt(XT* __restrict__ dst, long bhi, int dk, int d, int r8,
+                                         const float (&x)[8]) {
+  constexpr bool kSplit = sizeof(XT) == 4 && sizeof(OpT) == 2;
+  if constexpr (kSplit || sizeof(XT) == 2) {
+    const int j = r8 / 8, kb = j / 4, qd = j % 4;
+    const long f = (bhi * (dk / 16) + d / 16) * (C / 32) + kb;
+    if constexpr (kSplit) {
+      bf16* b = reinterpret_cast<bf16*>(dst) + ((f * 2) * 64 + 16 * qd + d % 16) * 8;
+      float lo[8];
+      bf16x8 hv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hv[e] = (bf16)x[e];
+        lo[e] = x[e] - (float)hv[e];
+      }
+      *reinterpret_cast<bf16x8*>(b) = hv;
+      store8(b + 64 * 8, lo);
+    } else {
+      store8(dst + (f * 64 + 16 * qd + d % 16) * 8, x);
+    }
+  } else {
+    store8(dst + (bhi * dk + d) * C + r8, x);
+  }
+}
+
 template <typename Tin, typename OpT, typename XT, int C, bool G_WS, bool WANT_A, bool SG,
           bool DIAG_BF16>
 __global__ __launch_bounds__(kThreads) void k_intra(
@@ -170,9 +204,6 @@ __global__ __launch_bounds__(kThreads) void k_intra(
       }
     }
     if (QhT_out || KhT_out) {
-      // transposed per chunk: [dk][C] in the operand type, or (XT = float) as a bf16 high
-      // part [dk][0..C) followed by its bf16 remainder [dk][C..2C) in the same bytes
-      constexpr bool kSplit = sizeof(XT) == 4 && sizeof(OpT) == 2;
 #pragma unroll
       for (int u_ = 0; u_ < (DB * (C / 8) + kThreads - 1) / kThreads; ++u_) {   // fixed trip count
         const int idx = threadIdx.x + u_ * kThreads;
@@ -181,7 +212,6 @@ __global__ __launch_bounds__(kThreads) void k_intra(
         // column reads of the g, q, k tiles fall on distinct LDS banks
         const int lw = idx & 63, wv = idx >> 6;
         const int c = 32 * (wv & 1) + (lw & 31), r8 = 8 * (2 * (wv >> 1) + (lw >> 5));
-        const long rowi = ((long)bh * N + i) * dk + d0 + c;
         float x[8];
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
@@ -197,30 +227,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(
               x[e] = to_f32(ks[(r8 + e) * XLD + c]) *
                      __builtin_amdgcn_exp2f(glast[c] - gs[(r8 + e) * GLD + c]);
           }
-          if constexpr (kSplit) {
-            // fragment order (the backward scans' MFMA operand): for 16-row block d / 16
-            // and 32-token block kb of this chunk, the 64 lanes' 16-byte pieces of the high
-            // part, then of the remainder; this piece belongs to lane 16 qd + d % 16
-            const int d = d0 + c, j = r8 / 8, kb = j / 4, qd = j % 4;
-            const long f = (((long)bh * N + i) * (dk / 16) + d / 16) * (C / 32) + kb;
-            bf16* b = reinterpret_cast<bf16*>(dst) + ((f * 2) * 64 + 16 * qd + d % 16) * 8;
-            float lo[8];
-            bf16x8 hv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              hv[e] = (bf16)x[e];
-              lo[e] = x[e] - (float)hv[e];
-            }
-            *reinterpret_cast<bf16x8*>(b) = hv;
-            store8(b + 64 * 8, lo);
-          } else if constexpr (sizeof(XT) == 2) {
-            // bf16: fragment order, one plane (see the split case)
-            const int d = d0 + c, j = r8 / 8, kb = j / 4, qd = j % 4;
-            const long f = (((long)bh * N + i) * (dk / 16) + d / 16) * (C / 32) + kb;
-            store8(dst + (f * 64 + 16 * qd + d % 16) * 8, x);
-          } else {
-            store8(dst + rowi * C + r8, x);
-          }
+          store_xt<OpT, XT, C>(dst, (long)bh * N + i, dk, d0 + c, r8, x);
         }
       }
     }
@@ -385,6 +392,190 @@ __global__ __launch_bounds__(kThreads) void k_intra(
   }
 }
 
+
+// Scalar gates: one gate per token and head, shared by every key dimension (the
+// data-dependent scalar gate and the data-independent scalar decay that the same summary
+// compares with the fine-grained gate, Measured effects and Surprising findings).  The
+// decay exp(g_t - g_s) then no longer depends on d and leaves the sum over it:
+//     A = tril((Q K^T) * D),   D[t][s] = exp(g_t - g_s),
+// one MFMA product of the chunk's q and k over every key dimension (exact products of the
+// bf16 inputs, fp32 accumulation; the diagonal sub-blocks included) times the C x C decay
+// matrix in fp32: no sub-chunk rebasing and no exponential per element.  The decayed
+// operands scale whole rows: Qh = q * exp(g_t), Kh = k * exp(gamma - g_t); exp(gamma) is
+// the same for every key dimension.  Same outputs and layouts as k_intra.
+template <typename Tin, typename OpT, typename XT, int C, bool WANT_A>
+__global__ __launch_bounds__(kThreads) void k_intra_scalar(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ la,
+    OpT* __restrict__ A_out, OpT* __restrict__ Qh_out, XT* __restrict__ QhT_out,
+    OpT* __restrict__ Kh_out, XT* __restrict__ KhT_out, float* __restrict__ eg_out,
+    float* __restrict__ g2_out, GateFn gf, int T, int dk, int N) {
+  static_assert(sizeof(Tin) == sizeof(OpT), "operands in the input type");
+  constexpr int DB = 64, NS = C / 16, XLD = DB + 8;
+  constexpr int NIW = (NS + 3) / 4;   // row tiles of A per wave: I = w + 4 ii
+  __shared__ __attribute__((aligned(16))) Tin qs[C * XLD];
+  __shared__ __attribute__((aligned(16))) Tin ks[C * XLD];
+  __shared__ float gsc[C], pq[C], pk[C], wtot[4];
+  const int i = blockIdx.x, bh = blockIdx.y;
+  const int t0 = i * C, rows = min(C, T - t0);
+  const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
+  const long in_base = ((long)bh * T + t0) * dk;
+
+  RowTile<Tin, C, DB, XLD> tq, tk;
+  auto fetch = [&](int d0) {
+    tq.load(q + in_base + d0, dk, rows);
+    tk.load(k + in_base + d0, dk, rows);
+  };
+  fetch(0);
+
+  // g * log2 e per row: the gate front-end (zero past T, so padded rows never decay the
+  // chunk), then an inclusive scan over the chunk's rows: shuffles within each wave, then
+  // the totals of the waves before
+  float x = 0.f;
+  if (threadIdx.x < C) {
+    const int t = threadIdx.x;
+    x = t < rows ? gf(to_f32(la[(long)bh * T + t0 + min(t, rows - 1)])) * kLog2e : 0.f;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float y = __shfl_up(x, off);
+      if (l >= off) x += y;
+    }
+    if (l == kWave - 1) wtot[w] = x;
+  }
+  __syncthreads();
+  if (threadIdx.x < C) {
+    for (int u = 0; u < w; ++u) x += wtot[u];
+    gsc[threadIdx.x] = x;
+  }
+  __syncthreads();
+  const float gam = gsc[C - 1];
+  if (threadIdx.x < C) {
+    pq[threadIdx.x] = __builtin_amdgcn_exp2f(gsc[threadIdx.x]);
+    pk[threadIdx.x] = __builtin_amdgcn_exp2f(gam - gsc[threadIdx.x]);
+  }
+  if (eg_out) {
+    const float eg = __builtin_amdgcn_exp2f(gam);
+    for (int d = threadIdx.x; d < dk; d += kThreads) eg_out[((long)bh * N + i) * dk + d] = eg;
+  }
+
+  f32x4 acc[NIW][NS];
+#pragma unroll
+  for (int ii = 0; ii < NIW; ++ii)
+#pragma unroll
+    for (int J = 0; J < NS; ++J) acc[ii][J] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int d0 = 0; d0 < dk; d0 += DB) {
+    tq.store(qs);
+    tk.store(ks);
+    fetch(min(d0 + DB, dk - DB));   // unconditional (exact wait counts); the last refetches
+    __syncthreads();
+    if constexpr (WANT_A) {
+      // (Q K^T) over this block's key dimensions, the row tiles of this wave, J <= I
+#pragma unroll
+      for (int ii = 0; ii < NIW; ++ii) {
+        const int I = w + 4 * ii;
+        if (I < NS) {
+#pragma unroll
+          for (int kb = 0; kb < DB / 32; ++kb) {
+            Frag<OpT> fa;
+            load_frag_c(fa, qs + (16 * I + r) * XLD + kb * 32);
+#pragma unroll
+            for (int J = 0; J < NS; ++J) {
+              if (J <= I) {
+                Frag<OpT> fb;
+                load_frag_c(fb, ks + (16 * J + r) * XLD + kb * 32);
+                mma(acc[ii][J], fa, fb);
+              }
+            }
+          }
+        }
+      }
+    }
+    if (g2_out) {   // g * log2 e, the same for every key dimension
+#pragma unroll
+      for (int u_ = 0; u_ < (C * (DB / 8) + kThreads - 1) / kThreads; ++u_) {   // fixed trip count
+        const int idx = threadIdx.x + u_ * kThreads;
+        if ((C * (DB / 8)) % kThreads != 0 && idx >= C * (DB / 8)) continue;
+        const int rr = idx / (DB / 8), c = (idx % (DB / 8)) * 8;
+        if (rr < rows) {
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = gsc[rr];
+          stream8(g2_out + in_base + (long)rr * dk + d0 + c, y);
+        }
+      }
+    }
+    if (Qh_out || Kh_out) {
+#pragma unroll
+      for (int u_ = 0; u_ < (C * (DB / 8) + kThreads - 1) / kThreads; ++u_) {   // fixed trip count
+        const int idx = threadIdx.x + u_ * kThreads;
+        if ((C * (DB / 8)) % kThreads != 0 && idx >= C * (DB / 8)) continue;
+        const int rr = idx / (DB / 8), c = (idx % (DB / 8)) * 8;
+        const long o = ((long)bh * N * C + t0 + rr) * dk + d0 + c;
+        float y[8];
+        if (Qh_out) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = to_f32(qs[rr * XLD + c + e]) * pq[rr];
+          store8(Qh_out + o, y);
+        }
+        if (Kh_out) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = to_f32(ks[rr * XLD + c + e]) * pk[rr];
+          stream8(Kh_out + o, y);
+        }
+      }
+    }
+    if (QhT_out || KhT_out) {
+#pragma unroll
+      for (int u_ = 0; u_ < (DB * (C / 8) + kThreads - 1) / kThreads; ++u_) {   // fixed trip count
+        const int idx = threadIdx.x + u_ * kThreads;
+        if ((DB * (C / 8)) % kThreads != 0 && idx >= DB * (C / 8)) continue;
+        const int lw = idx & 63, wv = idx >> 6;
+        const int c = 32 * (wv & 1) + (lw & 31), r8 = 8 * (2 * (wv >> 1) + (lw >> 5));
+        float y[8];
+        if (QhT_out) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = to_f32(qs[(r8 + e) * XLD + c]) * pq[r8 + e];
+          store_xt<OpT, XT, C>(QhT_out, (long)bh * N + i, dk, d0 + c, r8, y);
+        }
+        if (KhT_out) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = to_f32(ks[(r8 + e) * XLD + c]) * pk[r8 + e];
+          store_xt<OpT, XT, C>(KhT_out, (long)bh * N + i, dk, d0 + c, r8, y);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if constexpr (WANT_A) {
+    // A[t][s] = (Q K^T)[t][s] * exp(g_t - g_s) for s <= t, zero above the diagonal
+    OpT* Ab = A_out + ((long)bh * N + i) * C * C;
+    for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
+      const int t = idx / C, s2 = idx % C;
+      if (s2 > t) Ab[idx] = from_f32<OpT>(0.f);
+    }
+#pragma unroll
+    for (int ii = 0; ii < NIW; ++ii) {
+      const int I = w + 4 * ii;
+      if (I < NS) {
+#pragma unroll
+        for (int J = 0; J < NS; ++J) {
+          if (J <= I) {
+            const int s2 = 16 * J + r;
+            const float gs2 = gsc[s2];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int t = 16 * I + 4 * qd + e;
+              if (s2 <= t)
+                Ab[t * C + s2] = from_f32<OpT>(acc[ii][J][e] * __builtin_amdgcn_exp2f(gsc[t] - gs2));
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------
 template <typename Tin, typename OpT, typename XT, int C, bool GW, bool WA, bool SG = false,
           bool DB16 = false>
@@ -396,6 +587,13 @@ static void launch_intra_k(const IntraArgs& a, hipStream_t s) {
 }
 template <typename Tin, typename OpT, typename XT, int C>
 static hipError_t launch_intra_t(const IntraArgs& a, hipStream_t s) {
+  if (a.gscalar) {   // scalar gates: the C x C decay-matrix kernel (g formed from the gates)
+    auto kern = a.want_A ? k_intra_scalar<Tin, OpT, XT, C, true> : k_intra_scalar<Tin, OpT, XT, C, false>;
+    hipLaunchKernelGGL(kern, dim3(a.N, a.BH), dim3(kThreads), 0, s, (const Tin*)a.q,
+                       (const Tin*)a.k, (const Tin*)a.la, (OpT*)a.A, (OpT*)a.Qh, (XT*)a.QhT,
+                       (OpT*)a.Kh, (XT*)a.KhT, a.eg, a.g2_out, a.gate, a.T, a.dk, a.N);
+    return hipGetLastError();
+  }
   if (a.want_A) {
     // the bf16 diagonal is an option of bf16 operands only
     const bool db16 = a.diag_bf16 && sizeof(OpT) == 2;
