@@ -121,10 +121,12 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
     return 0, 0
 
 
-def path_flops(B, H, T, dk, dv, C):
-    """Algorithmic flops of one forward + backward (causal intra counted at C/2)."""
+def path_flops(B, H, T, dk, dv, C, fwd_only=False):
+    """Algorithmic flops of one forward + backward, or of the forward alone (causal intra
+    counted at C/2)."""
     tok = B * H * T
-    return tok * (4 * dk * dv + C * (dk + dv)) + tok * (8 * dk * dv + C * (3 * dk + 2 * dv))
+    fwd = tok * (4 * dk * dv + C * (dk + dv))
+    return fwd if fwd_only else fwd + tok * (8 * dk * dv + C * (3 * dk + 2 * dv))
 
 
 # ---------------------------------------------------------------------------------
@@ -408,8 +410,10 @@ def main():
     wsb_n = nat.workspace_bytes(desc, nat.PASS_BWD)
     wsf = torch.empty(wsf_n, dtype=torch.uint8, device=dev)
     wsb = torch.empty(wsb_n, dtype=torch.uint8, device=dev)
+    # a forward-only workload (the long sequence with state carry) times gla_chunk_fwd alone
+    fwd_only = not cfg.bwd
     fwd_stages = nat.trace_stages(desc, nat.PASS_FWD)
-    bwd_stages = nat.trace_stages(desc, nat.PASS_BWD, False)
+    bwd_stages = [] if fwd_only else nat.trace_stages(desc, nat.PASS_BWD, False)
     nf, nb = len(fwd_stages) + 1, len(bwd_stages) + 1
     L = nat.lib()
     stream = torch.cuda.current_stream(dev)
@@ -428,6 +432,8 @@ def main():
                                     P(wsf), wsf_n, sp, ef, nf if ef is not None else 0)
         if st:
             raise nat.GlaError(st, "gla_chunk_fwd_traced")
+        if fwd_only:
+            return
         st = L.gla_chunk_bwd_traced(ctypes.byref(desc), P(q), P(k), P(v), P(la), None, P(dO), None,
                                     P(dq), P(dk_), P(dv_), P(dla), None, P(wsb), wsb_n, sp, eb,
                                     nb if eb is not None else 0)
@@ -538,7 +544,7 @@ def main():
         return {"ms_per_step": vms, "value": B * T / (vms * 1e-3), "steps": n_v}
 
     gate_fe = scalar_fe = None
-    if not args.no_decode:
+    if not args.no_decode and not fwd_only:
         dt_code = nat.BF16 if cfg.dtype == "bf16" else nat.F32
         desc_g = nat.make_desc(B, H, T, dk, dv, C, cfg.subchunk, dt_code, mode, nat.GATE_LOGITS,
                                16.0)
@@ -552,7 +558,7 @@ def main():
 
     # Gated Slot Attention (float32) at the workload's head shape: one fwd + bwd step
     gsa_step = None
-    if not args.no_decode:
+    if not args.no_decode and not fwd_only:
         gsa_step = gsa_measure(L, nat, hip, dev, sp, cfg, args.gsa_slots, max(5, args.steps // 5))
 
     if args.copy_calibration:
@@ -599,10 +605,10 @@ def main():
 
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)
-    flops = path_flops(B, H, T, dk, dv, C)
+    flops = path_flops(B, H, T, dk, dv, C, fwd_only)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     out = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC if not fwd_only else METRIC.replace("fwd+bwd", "fwd"), "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name + ("_scalar_gates" if args.scalar_gates else "")

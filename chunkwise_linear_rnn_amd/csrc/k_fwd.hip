@@ -239,6 +239,212 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
   }
 }
 
+
+// Chunk 128, bf16: the same walk in half-chunk steps of 64 rows, so that every staged tile
+// stays the size of the chunk-64 kernel's (a whole chunk-128 tile set would need ~260 KB
+// of LDS).  Within chunk i the state stays S_[i] for both halves:
+//     O_0 = Qh_0 S + A_00 V_0,    O_1 = Qh_1 S + A_10 V_0 + A_11 V_1
+// (Qh rows and A taken against the chunk-128 cumulative gate), and the update
+//     S <- diag(exp(gamma_i)) S + Kh_0^T V_0 + Kh_1^T V_1
+// is formed in two parts: the first half's product goes to a side accumulator while the
+// first half runs, and joins the decayed state in the second.  The first half's V^T tile
+// stays in LDS for the second half's A_10 V_0.  Eight waves as in the chunk-64 kernel.
+template <typename Tin, int DK>
+__global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_c128(
+    const bf16* __restrict__ Qh, const bf16* __restrict__ KhT, const bf16* __restrict__ A,
+    const float* __restrict__ eg, const Tin* __restrict__ V, const float* __restrict__ S0,
+    Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N, int split,
+    const float* __restrict__ S_mid) {
+  using OpT = bf16;
+  constexpr int C = 128, H = 64;   // chunk, half-step rows
+  constexpr int NT = kFusedThreads, TV = 64, NM = H / 16, KH = DK / 2, NP = KH / 16;
+  constexpr int QLD = DK + 8, KLD = H, ALD = C + 16, VLD = H + 8, OLD = TV + 8, RLD = TV + 4;
+  __shared__ __attribute__((aligned(16))) OpT qs[H * QLD];
+  __shared__ __attribute__((aligned(16))) OpT ks[DK * KLD];       // Kh^T of the half, fragment order
+  __shared__ __attribute__((aligned(16))) OpT as_[H * ALD];       // A rows of the half, all columns
+  __shared__ __attribute__((aligned(16))) OpT vs[2][TV * VLD];    // V^T of both halves
+  __shared__ __attribute__((aligned(16))) Tin os_[2][H * OLD];    // O of a half, double-buffered
+  __shared__ __attribute__((aligned(16))) float red[H * RLD];
+  __shared__ float egs[DK];
+  const int nvt = dv / TV, nseg = split > 0 ? 2 : 1, per_seg = (int)gridDim.x / nseg;
+  const int lg = xcd_logical(blockIdx.x, gridDim.x);
+  const int seg = lg / per_seg, lt = lg % per_seg;
+  const int v0 = (lt % nvt) * TV, bh = lt / nvt;
+  const int ib = seg == 1 ? split : 0, ie = (nseg == 2 && seg == 0) ? split : N;
+  const float* __restrict__ Sinit = seg == 1 ? S_mid : S0;
+  const int w = threadIdx.x >> 6, vc = w & 3, kh = w >> 2;
+  const int l = lane_id(), r = l & 15, qd = l >> 4;
+  const int c16 = 16 * vc + r, col = v0 + c16, k0 = kh * KH;
+
+  f32x4 S[NP], Dl[NP];   // state rows k0 + 16 p + 4 qd + e of column col; Dl: Kh_0^T V_0
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      S[p][e] = Sinit ? Sinit[((long)bh * DK + k0 + 16 * p + 4 * qd + e) * dv + col] : 0.f;
+
+  FlatTile<OpT, H, DK, QLD, NT> tq;
+  FlatTile<OpT, H, C, ALD, NT> ta;
+  ColTile<OpT, Tin, H, VLD, NT, true> tv;
+  // Kh^T of one half: for each 16-row block, its two 32-token fragments of that half
+  // (2 KB of every 4 KB), copied to LDS as fragments (p, kb local)
+  constexpr int kKUnits = DK * H / 8, kKPer = (kKUnits + NT - 1) / NT;
+  u32x4 ku[kKPer];
+  float egr = 0.f;
+  auto fetch = [&](int i, int h) {
+    // the second half of a ragged last chunk may lie past T: its V rows are all zero
+    const int t0 = i * C + h * H, rows = min(H, T - t0);
+    tq.load(Qh + ((long)bh * N * C + t0) * DK);
+    ta.load(A + (((long)bh * N + i) * C + h * H) * C);
+    tv.load(V + ((long)bh * T + min(t0, T - 1)) * dv + v0, dv, max(rows, 1));
+    tv.nrows = max(rows, 0);
+    const bf16* kb0 = KhT + ((long)bh * N + i) * DK * C;
+#pragma unroll
+    for (int j = 0; j < kKPer; ++j) {
+      const int u = threadIdx.x + j * NT;   // unit: (row block p, local fragment f, lane piece)
+      const int pb = u / 128, f = (u / 64) % 2, pc = u % 64;
+      if (kKUnits % NT == 0 || u < kKUnits)
+        ku[j] = *reinterpret_cast<const u32x4*>(kb0 + ((pb * 4 + 2 * h + f) * 64 + pc) * 8);
+    }
+    egr = eg[((long)bh * N + i) * DK + min((int)threadIdx.x, DK - 1)];
+  };
+  auto store_k = [&]() {
+#pragma unroll
+    for (int j = 0; j < kKPer; ++j) {
+      const int u = threadIdx.x + j * NT;
+      if (kKUnits % NT == 0 || u < kKUnits) *reinterpret_cast<u32x4*>(ks + u * 8) = ku[j];
+    }
+  };
+  if (ie > ib) fetch(ib, 0);
+
+  constexpr int kPer = 16 / (int)sizeof(Tin), kUnits = H * TV / kPer;
+  auto store_o = [&](int ip, int hp, int buf) {
+    const int tp = ip * C + hp * H, rp = min(H, T - tp);
+    const Tin* ob = os_[buf];
+#pragma unroll
+    for (int u_ = 0; u_ < (kUnits + NT - 1) / NT; ++u_) {   // fixed trip count
+      const int idx = threadIdx.x + u_ * NT;
+      if ((kUnits) % NT != 0 && idx >= kUnits) continue;
+      const int e0 = idx * kPer, rr = e0 / TV, cc = e0 % TV;
+      if (rr < rp)
+        *reinterpret_cast<u32x4*>(O + ((long)bh * T + tp + rr) * dv + v0 + cc) =
+            *reinterpret_cast<const u32x4*>(ob + rr * OLD + cc);
+    }
+  };
+  int step = 0;
+  for (int i = ib; i < ie; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h, ++step) {
+      tq.store(qs);
+      store_k();
+      ta.store(as_);
+      tv.store(vs[h]);
+      if (h == 1 && threadIdx.x < DK) egs[threadIdx.x] = egr;
+      __syncthreads();
+      if (step > 0) store_o(h == 0 ? i - 1 : i, h ^ 1, (step - 1) & 1);
+      // next half-step (unconditional: past the end the last one is refetched, unused)
+      const int ni = h == 0 ? i : min(i + 1, ie - 1), nh = h == 0 ? 1 : (i + 1 < ie ? 0 : 1);
+      fetch(ni, nh);
+
+      // O_h = Qh_h S + (A V) of the half, as two partial sums (dk halves)
+      f32x4 acc[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KH / 32; ++kb) {
+        Frag<OpT> fb;
+        frag_from_acc(fb, S[2 * kb], S[2 * kb + 1]);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          Frag<OpT> fa;
+          load_frag_a(fa, qs + (16 * m + r) * QLD + k0 + kb * 32);
+          mma(acc[m], fa, fb);
+        }
+      }
+      // A columns of the first half (all of them for the second half's rows, causal for
+      // the first half's), then for the second half its own causal block
+#pragma unroll
+      for (int kb = 0; kb < H / 32; ++kb) {
+        Frag<OpT> fb;
+        load_frag_cs(fb, vs[0], VLD, c16, kb);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          if ((m < NM / 2) == (kh == 0) && (h == 1 || 32 * kb <= 16 * m + 15)) {
+            Frag<OpT> fa;
+            load_frag_c(fa, as_ + (16 * m + r) * ALD + kb * 32);
+            mma(acc[m], fa, fb);
+          }
+        }
+      }
+      if (h == 1) {
+#pragma unroll
+        for (int kb = 0; kb < H / 32; ++kb) {
+          Frag<OpT> fb;
+          load_frag_cs(fb, vs[1], VLD, c16, kb);
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            if ((m < NM / 2) == (kh == 0) && 32 * kb <= 16 * m + 15) {
+              Frag<OpT> fa;
+              load_frag_c(fa, as_ + (16 * m + r) * ALD + H + kb * 32);
+              mma(acc[m], fa, fb);
+            }
+          }
+        }
+      }
+      if (kh == 1) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) red[(16 * m + 4 * qd + e) * RLD + c16] = acc[m][e];
+      }
+      __syncthreads();
+      if (kh == 0) {
+        Tin* ob = os_[step & 1];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * m + 4 * qd + e;
+            ob[t * OLD + c16] = from_f32<Tin>(acc[m][e] + red[t * RLD + c16]);
+          }
+      }
+
+      // state: Kh_0^T V_0 aside in the first half; decay, add it, and Kh_1^T V_1 in the second
+      if (h == 0) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) Dl[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const f32x4 dec = *reinterpret_cast<const f32x4*>(egs + k0 + 16 * p + 4 * qd);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[p][e] = S[p][e] * dec[e] + Dl[p][e];
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < H / 32; ++kb) {
+        Frag<OpT> fb;
+        load_frag_cs(fb, vs[h], VLD, c16, kb);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          Frag<OpT> fa;
+          fa.v = *reinterpret_cast<const bf16x8*>(ks + (((k0 / 16 + p) * 2 + kb) * 64 + l) * 8);
+          if (h == 0) mma(Dl[p], fa, fb);
+          else mma(S[p], fa, fb);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (ie > ib) store_o(ie - 1, 1, (step - 1) & 1);
+  if (S_T && seg == nseg - 1) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S_T[((long)bh * DK + k0 + 16 * p + 4 * qd + e) * dv + col] = S[p][e];
+  }
+}
+
 template <typename Tin, typename OpT, int C, int DK>
 __global__ __launch_bounds__(kThreads) void k_fwd_fused(
     const OpT* __restrict__ Qh, const OpT* __restrict__ KhT, const OpT* __restrict__ A,
@@ -355,10 +561,18 @@ hipError_t launch_output(const OutArgs& a, hipStream_t s) {
   return launch_output_t<bf16, bf16, 128>(a, s);
 }
 
-int fused_split(int dtype, int C, int N) { return (dtype != 0 && C == 64 && N >= 4) ? N / 2 : 0; }
+int fused_split(int dtype, int C, int N) { return (dtype != 0 && N >= 4) ? N / 2 : 0; }
 
 template <typename Tin, typename OpT, int C, int DK>
 static hipError_t launch_fused_t2(const FusedArgs& a, hipStream_t s) {
+  if constexpr (C == 128 && sizeof(OpT) == 2) {
+    const int split = a.S_mid ? a.split : 0;
+    dim3 grid((a.dv / 64) * a.BH * (split > 0 ? 2 : 1));
+    hipLaunchKernelGGL((k_fwd_fused_c128<Tin, DK>), grid, dim3(kFusedThreads), 0, s,
+                       (const bf16*)a.Qh, (const bf16*)a.KhT, (const bf16*)a.A, a.eg,
+                       (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N, split, a.S_mid);
+    return hipGetLastError();
+  }
   if constexpr (C == 64 && sizeof(OpT) == 2) {
     const int split = a.S_mid ? a.split : 0;
     dim3 grid((a.dv / 64) * a.BH * (split > 0 ? 2 : 1));

@@ -53,6 +53,10 @@ SMALL = [
     # ragged last chunk) and 7 chunks (halves of 3 and 4)
     ("bf16_c64_n9", "bf16", 1, 2, 520, 128, 128, 64, -1.0),
     ("bf16_c64_n7", "bf16", 2, 1, 400, 64, 128, 64, 0.5),
+    # chunk 128 walked in 64-row halves with the sequence split: 5 chunks (halves of 2 and
+    # 3), the last one's second half partly (T = 600) or wholly (T = 540) past T
+    ("bf16_c128_n5", "bf16", 1, 2, 600, 128, 128, 128, 0.5),
+    ("bf16_c128_n5_tail", "bf16", 2, 1, 540, 64, 192, 128, -1.0),
 ]
 
 
