@@ -90,9 +90,10 @@ struct GBlock {
 // quarters above it (in order).  segtot: 4 x DB floats of LDS scratch.  Returns the
 // largest |g_t - g_rho| over the thread's rows, rho the first row of each 16-row
 // sub-chunk (the spread that decides how a diagonal sub-block can be summed).
-// TRANS: the sums go to gs transposed, gs[col * gld + row] (in place: every read of the
+// TRANS: the sums go to gs transposed, gs[col * OLD + row] (in place: every read of the
 // staged rows happens before the internal barrier), as 16-byte pieces of 4 rows.
-template <int C, int DB, bool TRANS = false>
+// OLD: the row stride of the transposed output (0: gld).
+template <int C, int DB, bool TRANS = false, int OLD = 0>
 __device__ __forceinline__ float chunk_cumsum_cols(float* gs, int gld, float* segtot) {
   static_assert(kThreads == 4 * DB, "four row quarters per column");
   constexpr int L = C / 4;
@@ -115,9 +116,11 @@ __device__ __forceinline__ float chunk_cumsum_cols(float* gs, int gld, float* se
     else spread = fmaxf(spread, fabsf(run[rr] - first));
   }
   if constexpr (TRANS) {
+    constexpr int kOld = OLD;
+    const int old = kOld ? kOld : gld;
 #pragma unroll
     for (int rr = 0; rr < L; rr += 4)
-      *reinterpret_cast<f32x4*>(gs + col * gld + seg * L + rr) =
+      *reinterpret_cast<f32x4*>(gs + col * old + seg * L + rr) =
           f32x4{run[rr], run[rr + 1], run[rr + 2], run[rr + 3]};
   } else {
 #pragma unroll

@@ -242,11 +242,16 @@ __device__ __forceinline__ void bwd_finish_block(const IntraLds<C, DB, Tin>& L,
 // accumulator tiles each for dq and dk).  dA = tril(dO V^T) is formed by every dk block of
 // the chunk (it is cheap next to the dO S^T and V dS^T products, and keeps the blocks
 // independent).  Three workgroups fit on a CU, so one's loads overlap another's math.
-constexpr int kDqkLds = 64 * (64 + 4) * 4 + 64 * (64 + 4) * 4 + 2 * 64 * (64 + 8) * 2;
+// LDS of a dq/dk workgroup for chunk C: dA [C][C + 4] fp32, the region of the staged g
+// block [C][68] and of g^T [64][C + 4] fp32, q and k [C][72]
+constexpr int dqk_lds_bytes(int C) {
+  return C * (C + 4) * 4 + (C * 68 > 64 * (C + 4) ? C * 68 : 64 * (C + 4)) * 4 + 2 * C * 72 * 2;
+}
+constexpr int kDqkLds = dqk_lds_bytes(64);
 // SFRAG: S and dS in MFMA fragment order (fragment (16-row block, 32-column block) of a
 // chunk's [dk][dv] state: lane 16 q + r holds row r, columns 8 q .. 8 q + 7), as the scans
 // write them for 128-column tiles; otherwise row-major.
-template <typename Tin, typename OpT, bool SFRAG, bool SG>
+template <typename Tin, typename OpT, bool SFRAG, bool SG, int C>
 __device__ __forceinline__ void bwd_dqk_body(
     char* __restrict__ arena, int lt, const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dO, int gscalar, const OpT* __restrict__ S,
@@ -257,16 +262,23 @@ __device__ __forceinline__ void bwd_dqk_body(
   static_assert(sizeof(Tin) == sizeof(OpT), "input and operand types match");
   // dO / V rows padded to 80: their 16-byte fragment reads (16 consecutive rows) then fall
   // on distinct banks
-  constexpr int C = 64, NM = 4, NS = C / 16, YLD = 64 + 16;
+  constexpr int NM = C / 16, NS = C / 16, YLD = 64 + 16;
+  constexpr int NRT = NM / 4;   // dA row tiles per wave: w, w + 4, ...
   constexpr int FLD = C + 4, GLD = 64 + 4, XLD = 64 + 8;
-  // LDS: dA [C][FLD] fp32, then a region that holds the dO / V tiles during the dv loop
-  // and g^T [64 columns][GLD] fp32 (a column's rows contiguous: the post-loop phases read
-  // 4 to 16 consecutive rows of one column), q, k [C][XLD] afterwards.  53248 bytes: three
-  // workgroups per CU.
-  constexpr int o_u = C * FLD * 4, o_q = o_u + C * GLD * 4, o_k = o_q + C * XLD * 2;
+  constexpr int GTLD = C + 4;   // g^T rows (a column's C rows)
+  // LDS: dA [C][FLD] fp32, then a region that holds the dO / V tiles during the dv loop,
+  // then the staged g block [C][GLD] and in its place g^T [64 columns][GTLD] fp32 (a
+  // column's rows contiguous: the post-loop phases read 4 to 16 consecutive rows of one
+  // column), q, k [C][XLD] afterwards.  Chunk 64: 53248 bytes, three workgroups per CU;
+  // chunk 128: 139264 bytes, one.
+  constexpr int GBYTES = (C * GLD > 64 * GTLD ? C * GLD : 64 * GTLD) * 4;
+  constexpr int o_u = C * FLD * 4, o_q = o_u + GBYTES, o_k = o_q + C * XLD * 2;
   constexpr int bytes = o_k + C * XLD * 2;
   static_assert(2 * C * YLD * 2 <= bytes - o_u, "dO / V tiles fit the shared region");
-  static_assert(bytes == kDqkLds, "arena size");
+  static_assert(bytes == dqk_lds_bytes(C), "arena size");
+  // the first-pass diagonal terms of dk go to dA's columns 64 .. (chunk 128) or to g's
+  // region (chunk 64)
+  constexpr int DKLD = C == 64 ? GLD : FLD;
   float* dAs = (float*)arena;
   OpT* dOs = (OpT*)(arena + o_u);
   OpT* Vs = dOs + C * YLD;
@@ -285,12 +297,13 @@ __device__ __forceinline__ void bwd_dqk_body(
   const OpT* dSi = dS + ((long)bh * N + i) * dk * dv;
   const int NV = dv / 64;
 
-  f32x4 adq[NM], adk[NM], adA[NM];   // adA[n] = dA tile (w, n), n <= w
+  f32x4 adq[NM], adk[NM], adA[NRT][NM];   // adA[j][n] = dA tile (w + 4 j, n), n <= w + 4 j
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     adq[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     adk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    adA[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NRT; ++j) adA[j][m] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   RowTile<OpT, C, 64, YLD> tdO, tV;
@@ -320,21 +333,25 @@ __device__ __forceinline__ void bwd_dqk_body(
     fetch(min(vb + 1, NV - 1), ns, nds);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      Frag<OpT> fO[NM], fV[NM], fOw;
+      Frag<OpT> fO[NM], fV[NM];
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         load_frag_c(fO[m], dOs + (16 * m + r) * YLD + kb * 32);
         load_frag_c(fV[m], Vs + (16 * m + r) * YLD + kb * 32);
       }
-      load_frag_c(fOw, dOs + (16 * w + r) * YLD + kb * 32);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         mma(adq[m], fO[m], fs[kb]);
         mma(adk[m], fV[m], fds[kb]);
       }
 #pragma unroll
-      for (int n = 0; n < NM; ++n)
-        if (n <= w) mma(adA[n], fOw, fV[n]);
+      for (int j = 0; j < NRT; ++j) {
+        Frag<OpT> fOw;
+        load_frag_c(fOw, dOs + (16 * (w + 4 * j) + r) * YLD + kb * 32);
+#pragma unroll
+        for (int n = 0; n < NM; ++n)
+          if (n <= w + 4 * j) mma(adA[j][n], fOw, fV[n]);
+      }
     }
     __syncthreads();
   };
@@ -371,17 +388,21 @@ __device__ __forceinline__ void bwd_dqk_body(
     tq.load(q + tok0 * dk + d0, dk, rows);
     tk.load(k + tok0 * dk + d0, dk, rows);
 #pragma unroll
-    for (int n = 0; n < NM; ++n)
-      if (n <= w) {
+    for (int j = 0; j < NRT; ++j) {
+      const int wr = w + 4 * j;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tl = 4 * qd + e;
-          dAs[(16 * w + tl) * FLD + 16 * n + r] = (n == w && r > tl) ? 0.f : adA[n][e];
+      for (int n = 0; n < NM; ++n)
+        if (n <= wr) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int tl = 4 * qd + e;
+            dAs[(16 * wr + tl) * FLD + 16 * n + r] = (n == wr && r > tl) ? 0.f : adA[j][n][e];
+          }
         }
-      }
+    }
     pg.store(gs, GLD, gf);
     __syncthreads();
-    chunk_cumsum_cols<C, 64, true>(gs, GLD, reinterpret_cast<float*>(ks));   // g^T
+    chunk_cumsum_cols<C, 64, true, GTLD>(gs, GLD, reinterpret_cast<float*>(ks));   // g^T
     __syncthreads();
     tq.store(qs);
     tk.store(ks);
@@ -389,7 +410,7 @@ __device__ __forceinline__ void bwd_dqk_body(
   __syncthreads();
 
   // inter-chunk parts: dq *= exp(g_t), dk *= exp(gamma - g_t)
-  const float* gc = gs + c * GLD;   // g of this lane's column, by row
+  const float* gc = gs + c * GTLD;   // g of this lane's column, by row
   const float gl = gc[C - 1];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
@@ -509,14 +530,18 @@ __device__ __forceinline__ void bwd_dqk_body(
       for (int e = 0; e < 4; ++e) adk[m][e] += tmp[e] * __builtin_amdgcn_exp2f(gr - gt[e]);
     }
   }
-  // intra-chunk, diagonal sub-blocks in fp32: thread (sub-chunk md, column cd)
-  float aq[16], ak[16];
-  const int md = threadIdx.x / 64, cd = threadIdx.x % 64, base = 16 * md;
-  {
+  // intra-chunk, diagonal sub-blocks in fp32: thread (sub-chunk md, column cd), four
+  // sub-chunks per pass
+  constexpr int NPD = NS / 4;
+  float aq[NPD][16], ak[NPD][16];
+  const int cd = threadIdx.x % 64;
+#pragma unroll
+  for (int pd = 0; pd < NPD; ++pd) {
+    const int base = 16 * (threadIdx.x / 64 + 4 * pd);
     float gt[16], qv[16], kv[16];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(gs + cd * GLD + base + 4 * h);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(gs + cd * GTLD + base + 4 * h);
 #pragma unroll
       for (int e = 0; e < 4; ++e) gt[4 * h + e] = x[e];
     }
@@ -524,18 +549,22 @@ __device__ __forceinline__ void bwd_dqk_body(
     for (int jj = 0; jj < 16; ++jj) {
       qv[jj] = to_f32(qs[(base + jj) * XLD + cd]);
       kv[jj] = to_f32(ks[(base + jj) * XLD + cd]);
-      aq[jj] = 0.f;
-      ak[jj] = 0.f;
+      aq[pd][jj] = 0.f;
+      ak[pd][jj] = 0.f;
     }
-    diag_block16(gt, qv, kv, dAs + base * FLD + base, FLD, aq, ak);
+    diag_block16(gt, qv, kv, dAs + base * FLD + base, FLD, aq[pd], ak[pd]);
   }
   __syncthreads();   // dA and g are dead from here: their regions carry the diagonal terms
-  float* dqd = dAs;   // [C][FLD]
-  float* dkd = gs;    // [C][GLD]
+  float* dqd = dAs;                          // [C][FLD], columns 0 .. 63
+  float* dkd = C == 64 ? gs : dAs + 64;      // [C][DKLD]
 #pragma unroll
-  for (int jj = 0; jj < 16; ++jj) {
-    dqd[(base + jj) * FLD + cd] = aq[jj];
-    dkd[(base + jj) * GLD + cd] = ak[jj];
+  for (int pd = 0; pd < NPD; ++pd) {
+    const int base = 16 * (threadIdx.x / 64 + 4 * pd);
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      dqd[(base + jj) * FLD + cd] = aq[pd][jj];
+      dkd[(base + jj) * DKLD + cd] = ak[pd][jj];
+    }
   }
   __syncthreads();
 #pragma unroll
@@ -544,7 +573,7 @@ __device__ __forceinline__ void bwd_dqk_body(
     for (int e = 0; e < 4; ++e) {
       const int t = 16 * m + 4 * qd + e;
       adq[m][e] += dqd[t * FLD + c];
-      adk[m][e] += dkd[t * GLD + c];
+      adk[m][e] += dkd[t * DKLD + c];
     }
   }
   // finish dq, dk; D = q*dq - k*dk and its chunk-local suffix sums, in registers
@@ -634,7 +663,7 @@ __device__ __forceinline__ void bwd_dqk_body(
 // =====================================================================================
 // dv = A^T dO + sum over 64-wide dk blocks of Kh_blk dS_blk; the next block's Kh and
 // dS^T tiles are loaded into registers while the current one multiplies.
-template <typename Tin, typename OpT, bool SFRAG>
+template <typename Tin, typename OpT, bool SFRAG, int C>
 __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
                                             const OpT* __restrict__ Kh,
                                             const OpT* __restrict__ A,
@@ -644,12 +673,15 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
                                             int N) {
   // the Kh block is read row-major (rows padded to 80 for conflict-free fragment reads),
   // the transposed tiles through the swizzle of ColTile (rows of 72)
-  constexpr int C = 64, NM = 4, LD = 64 + 8, KLD = 64 + 16;
-  static_assert(C * KLD * 2 + 3 * 64 * LD * 2 <= kDqkLds, "the dv tiles fit the shared arena");
+  // LD: rows of 64 (the dS^T tile, the output staging); TLD: rows of C tokens (A^T, dO^T)
+  constexpr int NM = C / 16, LD = 64 + 8, TLD = C + 8, KLD = 64 + 16;
+  static_assert(C * KLD * 2 + 64 * LD * 2 + (C + 64) * TLD * 2 <= dqk_lds_bytes(C),
+                "the dv tiles fit the shared arena");
+  static_assert(C * LD <= C * KLD, "the output staging fits the Kh block's space");
   OpT* ksh = (OpT*)arena;        // Kh block [t][k]
   OpT* dsT = ksh + C * KLD;      // dS block transposed [v][k]
-  OpT* aT = dsT + 64 * LD;       // A^T [t][s]
-  OpT* doT = aT + C * LD;        // dO^T [v][t]
+  OpT* aT = dsT + 64 * LD;       // A^T [s][t]
+  OpT* doT = aT + C * TLD;       // dO^T [v][t]
   // the dv tiles of one chunk share Kh and A (consecutive logical ids)
   const int nvt = dv / 64, NJ = dk / 64;
   const int vt = lt % nvt, i = (lt / nvt) % N, bh = lt / (nvt * N);
@@ -674,13 +706,16 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
     else ts[jb].load(dSc + (long)64 * jc * dv, dv, 64);
   };
   {
-    ColTile<OpT, OpT, C, LD, kThreads, true> ta;
-    ColTile<OpT, Tin, C, LD, kThreads, true> to;
-    ta.load(A + ((long)bh * N + i) * C * C, C, C);
+    // A^T in 64-column slices of A (its s index), dO^T
+    ColTile<OpT, OpT, C, TLD, kThreads, true> ta[C / 64];
+    ColTile<OpT, Tin, C, TLD, kThreads, true> to;
+#pragma unroll
+    for (int h = 0; h < C / 64; ++h) ta[h].load(A + ((long)bh * N + i) * C * C + 64 * h, C, C);
     to.load(dO + ((long)bh * T + t0) * dv + v0, dv, rows);
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) load_blk(jb);
-    ta.store(aT);
+#pragma unroll
+    for (int h = 0; h < C / 64; ++h) ta[h].store(aT + 64 * h * TLD);
     to.store(doT);
     tk[0].store(ksh);
     ts[0].store(dsT);
@@ -692,12 +727,12 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
 #pragma unroll
   for (int kb = 0; kb < C / 32; ++kb) {
     Frag<OpT> fb;
-    load_frag_cs(fb, doT, LD, 16 * w + r, kb);
+    load_frag_cs(fb, doT, TLD, 16 * w + r, kb);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       if (32 * kb + 31 >= 16 * m) {
         Frag<OpT> fa;
-        load_frag_cs(fa, aT, LD, 16 * m + r, kb);
+        load_frag_cs(fa, aT, TLD, 16 * m + r, kb);
         mma(acc[m], fa, fb);
       }
     }
@@ -899,8 +934,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(
 // The two chunk-64 backward kernels as one launch: dq / dk / dlog_alpha workgroups and dv
 // workgroups interleaved in proportion (a dv workgroup needs neither the chunk totals nor
 // anything the dq / dk workgroups write), so that their memory phases overlap on each CU.
-template <typename Tin, typename OpT, bool SFRAG, bool SG>
-__global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk_dv(
+template <typename Tin, typename OpT, bool SFRAG, bool SG, int C>
+__global__ __launch_bounds__(kThreads, C == 64 ? 3 : 1) void k_bwd_dqk_dv(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dO, int gscalar, const OpT* __restrict__ S,
     const OpT* __restrict__ dS, Tin* __restrict__ dq, Tin* __restrict__ dk_out,
@@ -908,26 +943,27 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_dqk_dv(
     GateFn gf, Tin* __restrict__ dla, float* __restrict__ dla_part, const OpT* __restrict__ Kh,
     const OpT* __restrict__ A, Tin* __restrict__ dv_out, int T, int dk, int dv, int N,
     int n_dqk) {
-  __shared__ __attribute__((aligned(16))) char arena[kDqkLds];
+  __shared__ __attribute__((aligned(16))) char arena[dqk_lds_bytes(C)];
   const int L = xcd_logical(blockIdx.x, gridDim.x);
   const long total = gridDim.x;
   // Bresenham split: logical id L is a dq/dk workgroup when the count of them up to L grows
   const int before = (int)(((long)L * n_dqk) / total), upto = (int)(((long)(L + 1) * n_dqk) / total);
   if (upto > before)
-    bwd_dqk_body<Tin, OpT, SFRAG, SG>(arena, before, q, k, v, dO, gscalar, S, dS, dq, dk_out, tot, cT, la, gf,
+    bwd_dqk_body<Tin, OpT, SFRAG, SG, C>(arena, before, q, k, v, dO, gscalar, S, dS, dq, dk_out, tot, cT, la, gf,
                            dla, dla_part, T, dk, dv, N);
   else
-    bwd_dv_body<Tin, OpT, SFRAG>(arena, L - before, Kh, A, dS, dO, dv_out, T, dk, dv, N);
+    bwd_dv_body<Tin, OpT, SFRAG, C>(arena, L - before, Kh, A, dS, dO, dv_out, T, dk, dv, N);
 }
 
 // ---------------------------------------------------------------------------------
 template <typename Tin, typename OpT, int C, int DK>
 static hipError_t launch_bwd_t2(const BwdArgs& a, hipStream_t s) {
-  if constexpr (C == 64 && sizeof(OpT) == 2) {
+  if constexpr (sizeof(OpT) == 2) {
     const int n_dqk = (a.dk / 64) * a.N * a.BH, n_dv = (a.dv / 64) * a.N * a.BH;
-    // scalar gates: the C x C decay-matrix form of the intra-chunk terms
-    auto kern = a.gscalar ? (a.s_frag ? k_bwd_dqk_dv<Tin, OpT, true, true> : k_bwd_dqk_dv<Tin, OpT, false, true>)
-                          : (a.s_frag ? k_bwd_dqk_dv<Tin, OpT, true, false> : k_bwd_dqk_dv<Tin, OpT, false, false>);
+    // scalar gates: the C x C decay-matrix form of the intra-chunk terms; fragment-order
+    // states come with chunk 64 only (the scans' 128-column tiles)
+    auto kern = a.gscalar ? (a.s_frag ? k_bwd_dqk_dv<Tin, OpT, C == 64, true, C> : k_bwd_dqk_dv<Tin, OpT, false, true, C>)
+                          : (a.s_frag ? k_bwd_dqk_dv<Tin, OpT, C == 64, false, C> : k_bwd_dqk_dv<Tin, OpT, false, false, C>);
     hipLaunchKernelGGL(kern, dim3(n_dqk + n_dv), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO,
                        a.gscalar ? 1 : 0, (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq,
@@ -952,7 +988,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   }
 }
 
-bool bwd_split(int dtype, int C) { return dtype != 0 && C == 64; }
+bool bwd_split(int dtype, int C) { return dtype != 0 && (C == 64 || C == 128); }
 
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s) {
   if (a.BH == 0 || a.N == 0) return hipSuccess;
