@@ -238,10 +238,15 @@ def cpu_baseline(d, cfg, T_sample):
             "fwd_s": wall_f, "bwd_s": wall_b, "cpu_model": _cpu_model()}
 
 
-def counter_traffic(stage, workload):
+def counter_traffic(stage, workload, state_mode="recompute"):
     """HBM bytes per launch from a committed counter summary that matches the current
-    kernel source, else None."""
+    kernel source, else None.  A summary taken in materialized state mode carries that
+    suffix; the backward's kernels are the same in both modes."""
     path = os.path.join(ROOT, "profiles", f"counters_{stage}_{workload}.json")
+    if state_mode == "materialized":
+        mpath = os.path.join(ROOT, "profiles", f"counters_{stage}_{workload}_materialized.json")
+        if os.path.exists(mpath):
+            path = mpath
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -250,6 +255,30 @@ def counter_traffic(stage, workload):
     if stage not in STAGE_SOURCE or rec.get("source_sha256") != source_digest(stage, ROOT):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def counter_mfma(workload, state_mode):
+    """Matrix-unit figures per stage from the committed `rocprofv3 --pmc
+    SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE` summary of this
+    workload and state mode: {stage: {mfma_busy_frac, bf16_peak_frac, ...}} for the stages
+    whose kernel source still matches the summary's hash; {} when there is none."""
+    suffix = "_materialized" if state_mode == "materialized" else ""
+    path = os.path.join(ROOT, "profiles", f"mfma_{workload}{suffix}.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as fh:
+        rec = json.load(fh)
+    from chunkwise_linear_rnn_amd.profiling import source_digest
+    out = {}
+    for kr in rec.get("kernels", []):
+        for st in kr.get("stages", []):
+            if rec.get("source_sha256", {}).get(st) != source_digest(st, ROOT):
+                continue
+            out[st] = {"mfma_busy_frac": kr["mfma_busy_frac"],
+                       "bf16_peak_frac": kr["bf16_peak_frac"],
+                       "bf16_gflop_per_launch": kr["bf16_gflop_per_launch"],
+                       "summary": os.path.relpath(path, ROOT)}
+    return out
 
 
 def gsa_measure(L, nat, hip, dev, sp, cfg, slots, steps):
@@ -596,12 +625,18 @@ def main():
         roof = {"bound": "mfma", "achieved": fl / (dom_ms * 1e-3) / 1e12, "peak": PEAK_BF16 / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = counter_traffic(dom_key[1], cfg.name)
+    stage_key = {"intra": f"intra_{dom_key[0]}"}.get(dom_key[1], dom_key[1])
+    roof["traffic"] = counter_traffic(stage_key, cfg.name, mode_s)
     roof["kernel"] = f"{dom_key[0]}:{dom_key[1]}"
     roof["avg_launch_us"] = dom_ms * 1e3
     roof["algorithmic_bytes_per_launch"] = byt
     roof["algorithmic_flops_per_launch"] = fl
     roof["ai_flop_per_byte"] = ai
+    # measured matrix-unit use (committed counter summary of the default gate options):
+    # the dominant stage's busy fraction, and every MFMA stage's alongside
+    mf = counter_mfma(cfg.name, mode_s) if not (args.scalar_gates or args.diag == "bf16") else {}
+    roof["mfma_busy_frac"] = mf.get(stage_key, {}).get("mfma_busy_frac")
+    roof["mfma_counters"] = mf or None
 
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)

@@ -9,6 +9,15 @@
 `bench.py --copy-calibration` into HBM bytes per launch of one stage: the counters are
 scaled so that the plain 1 GiB device copy in the same run reads and writes exactly its
 size; the result is written as JSON (matched by bench.py against the kernel source hash).
+
+    python -m chunkwise_linear_rnn_amd.profiling mfma <counter csv> <workload> "<command>"
+
+`mfma` turns one `rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16
+GRBM_GUI_ACTIVE` run into per-kernel matrix-unit figures (JSON, keyed by stage where the
+kernel belongs to one, with the kernel source hash): bf16 MFMA work per launch
+(MOPS x 512 flop), the busy fraction of the 1024 SIMDs' matrix units over the launch
+(busy cycles / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs)) and the achieved fraction of the
+2.5 PFLOP/s bf16 peak at 2.4 GHz.
 """
 from __future__ import annotations
 
@@ -25,20 +34,24 @@ STAGE_KERNEL = {"bwd_chunk": "k_bwd_chunk", "bwd_dqk_dv": "k_bwd_dqk_dv",
                 "state_scans": "k_state_scan", "seg_state": "k_state_scan",
                 "output": "k_output", "gate_cumsum": "k_gate_cumsum", "gate_grad": "k_gate_grad",
                 "gate_tot": "k_gate_tot", "gate_reduce": "k_gate_reduce", "state_dot": "k_state_dot",
-                "state_scan": "k_state_scan"}
+                "state_scan": "k_state_scan", "intra_fwd": "k_intra", "intra_bwd": "k_intra"}
 STAGE_SOURCE = {"bwd_chunk": "k_bwd.hip", "bwd_dqk_dv": "k_bwd.hip",
                 "fwd_fused": "k_fwd.hip", "intra": "k_intra.hip",
                 "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip",
                 "state_scans": "k_state.hip", "seg_state": "k_state.hip",
                 "output": "k_fwd.hip", "gate_cumsum": "k_gate.hip", "gate_grad": "k_gate.hip",
                 "gate_tot": "k_gate.hip", "gate_reduce": "k_gate.hip", "state_dot": "k_gate.hip",
-                "state_scan": "k_state.hip"}
+                "state_scan": "k_state.hip", "intra_fwd": "k_intra.hip", "intra_bwd": "k_intra.hip"}
 
 
 # Stages whose kernel name is shared by several launches of a step: the template
 # arguments that pick the stage's instance (mangled, or demangled, symbol text).
 STAGE_SYMBOL = {"state_scans": ("ELi1ELb1E", ", 1, true"),     # stores states, cross terms
-                "seg_state": ("ELi0ELb0E", ", 0, false")}      # midpoint state only
+                "seg_state": ("ELi0ELb0E", ", 0, false"),      # midpoint state only
+                "state_scan": ("ELi2ELb0E", ", 2, false"),     # materialized forward states
+                # the forward's intra-chunk kernel writes Kh^T in bf16, the backward's in fp32
+                "intra_fwd": ("DF16bDF16bDF16bLi", "bf16, bf16, bf16,"),
+                "intra_bwd": ("DF16bDF16bfLi", "bf16, bf16, float,")}
 
 
 def matches(stage: str, name: str) -> bool:
@@ -115,6 +128,41 @@ def counters(fetch_csv, write_csv, copy_bytes, stage, workload, command, root):
             "traffic_bytes_per_launch": fetch + write, "launches": len(kf), "command": command}
 
 
+MFMA_STAGES = ("fwd_fused", "bwd_dqk_dv", "state_scans", "seg_state", "bwd_chunk", "output",
+               "state_scan", "intra_fwd", "intra_bwd")
+SIMDS, XCDS, CLOCK_HZ, PEAK_BF16 = 1024, 8, 2.4e9, 2.5e15
+
+
+def mfma(path, workload, command, root):
+    """Per-kernel MFMA figures (averages per launch) from one counter run."""
+    rows = list(csv.DictReader(open(path)))
+    agg = {}
+    for r in rows:
+        d = agg.setdefault(r["Kernel_Name"], {})
+        d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    kernels = []
+    for name, d in agg.items():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in d or "GRBM_GUI_ACTIVE" not in d:
+            continue
+        mean = {c: sum(v) / len(v) for c, v in d.items()}
+        cycles = mean["GRBM_GUI_ACTIVE"] / XCDS
+        busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"]
+        flop = mean.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512.0
+        secs = cycles / CLOCK_HZ
+        kernels.append({"kernel": short(name), "symbol": name[:120],
+                        "launches": len(d["GRBM_GUI_ACTIVE"]),
+                        "gpu_cycles_per_launch": cycles, "mfma_busy_cycles": busy,
+                        "mfma_busy_frac": busy / (cycles * SIMDS) if cycles else 0.0,
+                        "bf16_gflop_per_launch": flop / 1e9,
+                        "bf16_tflops": flop / secs / 1e12 if secs else 0.0,
+                        "bf16_peak_frac": flop / secs / PEAK_BF16 if secs else 0.0,
+                        "stages": [st for st in MFMA_STAGES if matches(st, name)]})
+    kernels.sort(key=lambda k: -k["gpu_cycles_per_launch"] * k["launches"])
+    digests = {st: source_digest(st, root) for st in MFMA_STAGES}
+    return {"workload": workload, "command": command, "source_sha256": digests,
+            "kernels": kernels}
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         sys.stdout.write(stats_table(sys.argv[2], sys.argv[3]))
@@ -123,3 +171,6 @@ if __name__ == "__main__":
         rec = counters(sys.argv[2], sys.argv[3], float(sys.argv[4]), sys.argv[5], sys.argv[6],
                        sys.argv[7], root)
         print(json.dumps(rec, indent=1))
+    elif sys.argv[1] == "mfma":
+        root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+        print(json.dumps(mfma(sys.argv[2], sys.argv[3], sys.argv[4], root), indent=1))

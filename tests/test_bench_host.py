@@ -61,3 +61,26 @@ def test_counter_summaries_match_sources(bench, stage):
     if bench.counter_traffic(stage, "gla1p3b_t2k") is None:
         pytest.skip(f"{os.path.basename(path)} predates the current kernel sources "
                     "(bench.py reports its traffic as null)")
+
+
+def test_mfma_summary_is_well_formed(bench):
+    """The committed matrix-unit summary at the 1.3B shape: fractions within [0, 1], the
+    MFMA stages present, and bench.py reading them back while the sources match."""
+    import json
+    path = os.path.join(ROOT, "profiles", "mfma_gla1p3b_t2k.json")
+    if not os.path.exists(path):
+        pytest.skip("no matrix-unit summary")
+    with open(path) as fh:
+        rec = json.load(fh)
+    stages = set()
+    for k in rec["kernels"]:
+        assert 0.0 <= k["mfma_busy_frac"] <= 1.0, k["kernel"]
+        assert 0.0 <= k["bf16_peak_frac"] <= 1.0, k["kernel"]
+        assert k["gpu_cycles_per_launch"] > 0, k["kernel"]
+        stages.update(k["stages"])
+    assert {"bwd_dqk_dv", "fwd_fused", "state_scans", "intra_fwd", "intra_bwd"} <= stages
+    got = bench.counter_mfma("gla1p3b_t2k", "recompute")
+    if not got:
+        pytest.skip("mfma_gla1p3b_t2k.json predates the current kernel sources")
+    for st, v in got.items():
+        assert st in stages and 0.0 <= v["mfma_busy_frac"] <= 1.0
