@@ -1,7 +1,7 @@
 // Recurrent (token by token) evaluation of the gated linear-attention state, for decoding
-// (page "Gated Linear Attention Transformers with Hardware-Efficient Training",
-// atlas.scime.ai summary, section Approach: the recurrent form of the same layer, its
-// inference side).  For each (batch, head) and each of the call's T tokens in order:
+// (page "Gated Slot Attention for Efficient Linear-Time Sequence Modeling", mlsanity.com
+// summary, Abstract: linear attention and its gated variants infer recurrently; here the
+// layer's own recurrence).  For each (batch, head) and each of the call's T tokens in order:
 //     S <- diag(exp(log_alpha_t)) S + k_t^T v_t,     o_t = q_t S
 // with S the caller's float32 state, updated in place.
 //

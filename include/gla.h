@@ -193,9 +193,10 @@ gla_status_t gla_chunk_bwd(const gla_desc_t* desc, const void* q, const void* k,
                            void* dv, void* dlog_alpha, float* dS0, void* ws,
                            size_t ws_bytes, void* stream);
 
-/* Recurrent evaluation, for decoding (Approach section: the same state in its
- * recurrent form, the layer's inference side).  For every (b, h) and t = 0 .. T-1 in
- * order:
+/* Recurrent evaluation, for decoding (page "Gated Slot Attention for Efficient
+ * Linear-Time Sequence Modeling", mlsanity.com summary, Abstract: linear attention and its
+ * gated variants infer recurrently; here the layer's own recurrence, one state per
+ * (b, h) carried from token to token).  For every (b, h) and t = 0 .. T-1 in order:
  *     S <- diag(exp(log_alpha[b,h,t,:])) S + k[b,h,t,:]^T v[b,h,t,:],
  *     o[b,h,t,:] = q[b,h,t,:] S,
  * with S float32 [B,H,dk,dv], read and updated in place (required; it is both input and
