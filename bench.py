@@ -637,6 +637,16 @@ def main():
     mf = counter_mfma(cfg.name, mode_s) if not (args.scalar_gates or args.diag == "bf16") else {}
     roof["mfma_busy_frac"] = mf.get(stage_key, {}).get("mfma_busy_frac")
     roof["mfma_counters"] = mf or None
+    # the intra-chunk kernel against the bf16 MFMA peak: its algorithmic flops over its live
+    # duration (profiling pass), and the counters' busy fraction where they match
+    intra_mfma = {}
+    for tag in ("fwd", "bwd"):
+        ms_i = stages.get((tag, "intra"), 0.0)
+        if ms_i > 0.0:
+            _, fl_i = stage_work("intra", tag, mode_s, B, H, T, dk, dv, C, e)
+            intra_mfma[tag] = {"us": ms_i * 1e3, "tflops": fl_i / ms_i / 1e9,
+                               "bf16_peak_frac": fl_i / (ms_i * 1e-3) / PEAK_BF16,
+                               "mfma_busy_frac": mf.get(f"intra_{tag}", {}).get("mfma_busy_frac")}
 
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)
@@ -653,6 +663,7 @@ def main():
                    "seq_len": T, "parallelism": "none (1 GPU)"},
         "tflops": tflops, "mfma_peak_frac": flops / (ms_per_step * 1e-3) / PEAK_BF16,
         "roofline": roof,
+        "intra_mfma": intra_mfma or None,
         "cache_flushed": flush,
         "warm_cache": warm_rec,
         "gate_logits_step": gate_fe,

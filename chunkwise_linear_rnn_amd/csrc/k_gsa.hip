@@ -22,56 +22,83 @@ namespace gla {
 
 namespace {
 
-constexpr int kC = 64, kLD = 65;   // chunk rows; LDS row stride of a 64 x 64 fp32 tile
+// 64-row fp32 tiles in LDS with rows of kFL floats: the 16-byte halves of an MFMA
+// fragment read (16 consecutive rows, one 32-float k block) then fall on distinct banks.
+constexpr int kC = 64, kFL = 68;
 
-// 64 x 64 block of a row-major fp32 matrix (row stride ld) into LDS, rows >= `rows`
-// zero; `trans` stores element (r, c) at lds[c * kLD + r].
-__device__ __forceinline__ void load_blk(float* lds, const float* __restrict__ g, long ld,
-                                         int rows, bool trans) {
+// 64 x 64 block of a row-major fp32 matrix (row stride ld) into LDS rows; rows >= `rows`
+// (>= 1) zero, or with `clamp` the last valid row repeated (a gate cumsum continuing flat,
+// so that every decay factor between two rows stays at most 1).
+__device__ __forceinline__ void stage_rows(float* lds, const float* __restrict__ g, long ld,
+                                           int rows, bool clamp = false) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int idx = threadIdx.x + kThreads * u, r = idx >> 4, c = (idx & 15) * 4;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(g + (long)min(r, rows - 1) * ld + c);
+    f32x4 x = *reinterpret_cast<const f32x4*>(g + (long)min(r, rows - 1) * ld + c);
+    if (r >= rows && !clamp) x = f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4*>(lds + r * kFL + c) = x;
+  }
+}
+// The same block stored transposed, lds[c * kFL + r] (lanes run down the source rows, so
+// the 4-byte LDS writes of a wave are consecutive).
+__device__ __forceinline__ void stage_cols(float* lds, const float* __restrict__ g, long ld,
+                                           int rows) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float v = r < rows ? x[e] : 0.f;
-      if (trans) lds[(c + e) * kLD + r] = v;
-      else lds[r * kLD + c + e] = v;
+  for (int u = 0; u < 4; ++u) {
+    const int idx = threadIdx.x + kThreads * u, r = idx & 63, c = (idx >> 6) * 4;
+    f32x4 x = *reinterpret_cast<const f32x4*>(g + (long)min(r, rows - 1) * ld + c);
+    if (r >= rows) x = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lds[(c + e) * kFL + r] = x[e];
+  }
+}
+
+// Wave w's 16 output rows of a 64 x 64 product over k = 64:
+//     acc[j][e] += sum_k X[16 w + 4 q + e][k] * Y[16 j + r][k]
+// (lane: r = lane % 16, q = lane / 16), both operands row-major in k in LDS: fp32 MFMA
+// 16x16x4 in k32 steps.
+__device__ __forceinline__ void mm_rows(f32x4 (&acc)[4], const float* X, const float* Y, int w) {
+  const int r = lane_id() & 15;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    Frag<float> a;
+    load_frag_c(a, X + (16 * w + r) * kFL + 32 * kb);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      Frag<float> b;
+      load_frag_c(b, Y + (16 * j + r) * kFL + 32 * kb);
+      mma(acc[j], a, b);
     }
   }
 }
 
-// acc[a][b] += sum_{k < kn} X(r0 + a, k) * Y(c0 + b, k), with X(r, k) = X[r * xr + k * xk]
-// and Y likewise (strides give either orientation of an LDS tile).
-__device__ __forceinline__ void mm64(float (&acc)[4][4], const float* X, int xr, int xk,
-                                     const float* Y, int yr, int yk, int r0, int c0,
-                                     int kn = kC) {
-  for (int kk = 0; kk < kn; ++kk) {
-    float xa[4], yb[4];
+__device__ __forceinline__ void zero4(f32x4 (&x)[4]) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) xa[a] = X[(r0 + a) * xr + kk * xk];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) yb[b] = Y[(c0 + b) * yr + kk * yk];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] += xa[a] * yb[b];
+  for (int j = 0; j < 4; ++j) x[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// A = tril(Q K^T) of one chunk (rows of q and k past `rows` zero) into lds_a [t][u],
+// through the staging tiles x0, x1.  Ends with the staging tiles free.
+__device__ __forceinline__ void chunk_qk(float* lds_a, float* x0, float* x1,
+                                        const float* __restrict__ qb,
+                                        const float* __restrict__ kb, int dk, int rows) {
+  const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
+  f32x4 acc[4];
+  zero4(acc);
+  for (int d0 = 0; d0 < dk; d0 += kC) {
+    stage_rows(x0, qb + d0, dk, rows);
+    stage_rows(x1, kb + d0, dk, rows);
+    __syncthreads();
+    mm_rows(acc, x0, x1, w);
+    __syncthreads();
   }
-}
-
-__device__ __forceinline__ void zero44(float (&x)[4][4]) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) x[a][b] = 0.f;
-}
-
-__device__ __forceinline__ void store_rows(float* __restrict__ g, long ld, const float (&x)[4][4],
-                                           int r0, int c0, int rows) {
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-    if (r0 + a < rows)
-      *reinterpret_cast<f32x4*>(g + (long)(r0 + a) * ld + c0) = f32x4{x[a][0], x[a][1], x[a][2], x[a][3]};
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * w + 4 * qd + e, u = 16 * j + r;
+      lds_a[t * kFL + u] = u <= t ? acc[j][e] : 0.f;
+    }
 }
 
 }  // namespace
@@ -86,72 +113,109 @@ __global__ __launch_bounds__(kThreads) void k_gsa_w(const float* __restrict__ la
 // First pass, chunk i of head bh: s_t = e^{g_t} * (q_t S1_[i]^T) + sum_{u<=t} A_tu w_u e^{g_t - g_u}
 // with A = Q K^T (causal), g the chunk-local cumsum (given times log2 e), S1_[i] the key
 // slots before the chunk ([m][dk] fp32).
-__global__ __launch_bounds__(kThreads) void k_vg_out(const float* __restrict__ q,
-                                                     const float* __restrict__ k,
-                                                     const float* __restrict__ w,
-                                                     const float* __restrict__ g2,
-                                                     const float* __restrict__ S1,
-                                                     float* __restrict__ s_out, int T, int dk,
-                                                     int m, int N) {
-  __shared__ float L0[kC * kLD], L1[kC * kLD], LA[kC * kLD], LW[kC * kLD], LG[kC * kLD];
+//
+// Wave w owns output rows 16 w .. 16 w + 15 (sub-chunk I = w) for 64 slots at a time.  The
+// dense products (Q K^T, Q S1^T) are fp32 MFMAs.  The gate acts on the slot index j, so
+// the intra-chunk sum is rebased per sub-chunk as in the main layer: for sources u in
+// earlier sub-chunks, with rho = 16 I,
+//     sum_u A_tu w_uj e^{g_tj - g_uj} = e^{g_tj - g_rho,j} sum_u A_tu (w_uj e^{g_rho,j - g_uj})
+// (both factors at most 1), an MFMA with the rebased w as B operand; the diagonal
+// sub-block (u, t in I) is summed directly.
+__global__ __launch_bounds__(kThreads, 3) void k_vg_out(const float* __restrict__ q,
+                                                        const float* __restrict__ k,
+                                                        const float* __restrict__ w,
+                                                        const float* __restrict__ g2,
+                                                        const float* __restrict__ S1,
+                                                        float* __restrict__ s_out, int T, int dk,
+                                                        int m, int N) {
+  __shared__ __attribute__((aligned(16))) float X0[kC * kFL], X1[kC * kFL], XA[kC * kFL];
   const int i = blockIdx.x, bh = blockIdx.y, t0 = i * kC, rows = min(kC, T - t0);
-  const int r0 = 4 * (threadIdx.x >> 4), c0 = 4 * (threadIdx.x & 15);
-  const float* qb = q + ((long)bh * T + t0) * dk;
-  const float* kb = k + ((long)bh * T + t0) * dk;
-  const float* wb = w + ((long)bh * T + t0) * m;
-  const float* gb = g2 + ((long)bh * T + t0) * m;
+  const int wv = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4, rho = 16 * wv;
+  const long rowbase = (long)bh * T + t0;
+  const float* qb = q + rowbase * dk;
+  const float* kb = k + rowbase * dk;
   const float* Sb = S1 + ((long)bh * N + i) * m * dk;
 
-  float acc[4][4];
-  zero44(acc);
-  for (int d0 = 0; d0 < dk; d0 += kC) {
-    load_blk(L0, qb + d0, dk, rows, false);
-    load_blk(L1, kb + d0, dk, rows, false);
-    __syncthreads();
-    mm64(acc, L0, kLD, 1, L1, kLD, 1, r0, c0);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) LA[(r0 + a) * kLD + c0 + b] = c0 + b <= r0 + a ? acc[a][b] : 0.f;
+  chunk_qk(XA, X0, X1, qb, kb, dk, rows);
 
   for (int j0 = 0; j0 < m; j0 += kC) {
-    float o[4][4];
-    zero44(o);
+    // inter-chunk part: Q S1^T for 64 slots
+    f32x4 o[4];
+    zero4(o);
     for (int d0 = 0; d0 < dk; d0 += kC) {
-      load_blk(L0, qb + d0, dk, rows, false);
-      load_blk(L1, Sb + (long)j0 * dk + d0, dk, kC, false);
+      stage_rows(X0, qb + d0, dk, rows);
+      stage_rows(X1, Sb + (long)j0 * dk + d0, dk, kC);
       __syncthreads();
-      mm64(o, L0, kLD, 1, L1, kLD, 1, r0, c0);
+      mm_rows(o, X0, X1, wv);
       __syncthreads();
     }
-    load_blk(LW, wb + j0, m, rows, false);
-    load_blk(LG, gb + j0, m, rows, false);
+    // w [u][j] (zero past `rows`) and g [t][j] (flat past `rows`) of the block
+    stage_rows(X0, w + rowbase * m + j0, m, rows);
+    stage_rows(X1, g2 + rowbase * m + j0, m, rows, true);
     __syncthreads();
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) o[a][b] *= __builtin_amdgcn_exp2f(LG[(r0 + a) * kLD + c0 + b]);
-    for (int u = 0; u <= r0 + 3; ++u) {
-      float wu[4], gu[4];
+      for (int e = 0; e < 4; ++e)
+        o[jt][e] *= __builtin_amdgcn_exp2f(X1[(rho + 4 * qd + e) * kFL + 16 * jt + r]);
+    // earlier sub-chunks (u < rho), rebased on rho
+    if (wv > 0) {
+      f32x4 tmp[4];
+      zero4(tmp);
+      for (int kb2 = 0; kb2 < (rho + 31) / 32; ++kb2) {
+        Frag<float> fa;   // A[rho + r][u], u = 32 kb2 + 8 qd + e < rho
+        load_frag_c(fa, XA + (rho + r) * kFL + 32 * kb2);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        wu[b] = LW[u * kLD + c0 + b];
-        gu[b] = LG[u * kLD + c0 + b];
-      }
+        for (int e = 0; e < 8; ++e)
+          if (32 * kb2 + 8 * qd + e >= rho) fa.v[e] = 0.f;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int t = r0 + a;
-        if (u <= t) {
-          const float at = LA[t * kLD + u];
+        for (int jt = 0; jt < 4; ++jt) {
+          const int j = 16 * jt + r;
+          const float grho = X1[rho * kFL + j];
+          Frag<float> fb;   // w[u][j] exp(g[rho][j] - g[u][j])
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
-            o[a][b] += at * wu[b] * __builtin_amdgcn_exp2f(LG[t * kLD + c0 + b] - gu[b]);
+          for (int e = 0; e < 8; ++e) {
+            const int u = 32 * kb2 + 8 * qd + e;
+            fb.v[e] = u < rho ? X0[u * kFL + j] * __builtin_amdgcn_exp2f(grho - X1[u * kFL + j]) : 0.f;
+          }
+          mma(tmp[jt], fa, fb);
         }
       }
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int j = 16 * jt + r;
+        const float grho = X1[rho * kFL + j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[jt][e] += tmp[jt][e] * __builtin_amdgcn_exp2f(X1[(rho + 4 * qd + e) * kFL + j] - grho);
+      }
     }
-    store_rows(s_out + ((long)bh * T + t0) * m + j0, m, o, r0, c0, rows);
+    // the diagonal sub-block: sources u in [rho, t]
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = rho + 4 * qd + e;
+      float gt[4], sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) gt[jt] = X1[t * kFL + 16 * jt + r];
+      for (int u = rho; u <= t; ++u) {
+        const float at = XA[t * kFL + u];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const int j = 16 * jt + r;
+          sum[jt] += at * X0[u * kFL + j] * __builtin_amdgcn_exp2f(gt[jt] - X1[u * kFL + j]);
+        }
+      }
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) o[jt][e] += sum[jt];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = rho + 4 * qd + e;
+      if (t < rows) {
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) s_out[(rowbase + t) * m + j0 + 16 * jt + r] = o[jt][e];
+      }
+    }
     __syncthreads();
   }
 }
@@ -164,157 +228,266 @@ __global__ __launch_bounds__(kThreads) void k_vg_out(const float* __restrict__ q
 //   dw_uj = e^{gamma_j - g_uj} (dS1_[i+1] k_u)_j + sum_{t>=u} ds_tj A_tu e^{g_tj - g_uj}
 // and the closed-form gate gradient's terms D = s*ds - w*dw (its dependence on the
 // cumulative log-gate), as chunk-local suffix sums Dloc and chunk totals tot.
-__global__ __launch_bounds__(kThreads) void k_vg_bwd(
+//
+// Wave w owns rows 16 w .. 16 w + 15 (sub-chunk I = w) of every output tile.  The dense
+// products are fp32 MFMAs; the two gated sums over pairs of rows are rebased per
+// sub-chunk (dA on rho = 16 I for earlier sources, dw on rho' = 16 I + 15 for later
+// targets; every factor at most 1) with their diagonal sub-blocks summed directly.  Four
+// 64 x 64 fp32 tiles of LDS, reused phase by phase, keep two workgroups per CU.
+__global__ __launch_bounds__(kThreads, 2) void k_vg_bwd(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ g2, const float* __restrict__ ds, const float* __restrict__ s,
     const float* __restrict__ S1, const float* __restrict__ dS1, float* __restrict__ dq,
     float* __restrict__ dk_out, float* __restrict__ dw, float* __restrict__ Dloc,
     float* __restrict__ tot, int T, int dk, int m, int N) {
-  __shared__ float L0[kC * kLD], L1[kC * kLD], L2[kC * kLD], L3[kC * kLD], L4[kC * kLD],
-      LA[kC * kLD], LdA[kC * kLD];
+  __shared__ __attribute__((aligned(16))) float T0[kC * kFL], T1[kC * kFL], T2[kC * kFL],
+      T3[kC * kFL];
   const int i = blockIdx.x, bh = blockIdx.y, t0 = i * kC, rows = min(kC, T - t0);
-  const int r0 = 4 * (threadIdx.x >> 4), c0 = 4 * (threadIdx.x & 15);
+  const int wv = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4, rho = 16 * wv;
   const long rowbase = (long)bh * T + t0;
   const float* qb = q + rowbase * dk;
   const float* kb = k + rowbase * dk;
   const float* Sb = S1 + ((long)bh * N + i) * m * dk;
   const float* dSb = dS1 + ((long)bh * N + i) * m * dk;
 
-  // A = Q K^T (causal)
-  float acc[4][4];
-  zero44(acc);
-  for (int d0 = 0; d0 < dk; d0 += kC) {
-    load_blk(L0, qb + d0, dk, rows, false);
-    load_blk(L1, kb + d0, dk, rows, false);
-    __syncthreads();
-    mm64(acc, L0, kLD, 1, L1, kLD, 1, r0, c0);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) LA[(r0 + a) * kLD + c0 + b] = c0 + b <= r0 + a ? acc[a][b] : 0.f;
+  // A = tril(Q K^T) in T0
+  chunk_qk(T0, T1, T2, qb, kb, dk, rows);
 
-  float adA[4][4];   // dA, thread tile (t = r0 + a, u = c0 + b)
-  zero44(adA);
+  f32x4 adA[4];   // dA tile (row tile wv, column tile J): lane t = rho + 4 qd + e, u = 16 J + r
+  zero4(adA);
   for (int j0 = 0; j0 < m; j0 += kC) {
-    load_blk(L2, ds + rowbase * m + j0, m, rows, false);   // ds [t][j]
-    load_blk(L3, w + rowbase * m + j0, m, rows, false);    // w  [u][j]
-    load_blk(L4, g2 + rowbase * m + j0, m, rows, false);   // g  [t][j] (times log2 e)
-    __syncthreads();
-    for (int j = 0; j < kC; ++j) {
-      float dt[4], gt[4], wu[4], gu[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        dt[a] = L2[(r0 + a) * kLD + j];
-        gt[a] = L4[(r0 + a) * kLD + j];
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        wu[b] = L3[(c0 + b) * kLD + j];
-        gu[b] = L4[(c0 + b) * kLD + j];
-      }
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          if (c0 + b <= r0 + a) adA[a][b] += dt[a] * wu[b] * __builtin_amdgcn_exp2f(gt[a] - gu[b]);
-    }
-    // (K dS1^T)[u][j] over dk
-    float kds[4][4];
-    zero44(kds);
+    // (dS1 k_u)_j for this wave's rows u and 64 slots
+    f32x4 kds[4];
+    zero4(kds);
     for (int d0 = 0; d0 < dk; d0 += kC) {
-      load_blk(L0, kb + d0, dk, rows, false);
-      load_blk(L1, dSb + (long)j0 * dk + d0, dk, kC, false);
+      stage_rows(T1, kb + d0, dk, rows);
+      stage_rows(T2, dSb + (long)j0 * dk + d0, dk, kC);
       __syncthreads();
-      mm64(kds, L0, kLD, 1, L1, kLD, 1, r0, c0);
+      mm_rows(kds, T1, T2, wv);
       __syncthreads();
     }
-    // dw for (u = r0 + a, j = c0 + b); gamma = g at the chunk's last valid row
-    float dwv[4][4];
+    // ds [t][j], w [u][j] (zero past `rows`), g [t][j] (flat past `rows`)
+    stage_rows(T1, ds + rowbase * m + j0, m, rows);
+    stage_rows(T2, w + rowbase * m + j0, m, rows);
+    stage_rows(T3, g2 + rowbase * m + j0, m, rows, true);
+    __syncthreads();
+
+    // dA, earlier sub-chunks J < I: (ds_tj e^{g_tj - g_rho,j}) (w_uj e^{g_rho,j - g_uj})
+    if (wv > 0) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        Frag<float> fds, fgt, fgr, fa;
+        load_frag_c(fds, T1 + (rho + r) * kFL + 32 * kb2);
+        load_frag_c(fgt, T3 + (rho + r) * kFL + 32 * kb2);
+        load_frag_c(fgr, T3 + rho * kFL + 32 * kb2);
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        dwv[a][b] = __builtin_amdgcn_exp2f(L4[(rows - 1) * kLD + c0 + b] - L4[(r0 + a) * kLD + c0 + b]) *
-                    kds[a][b];
-    for (int t = r0; t < kC; ++t) {
-      float dt[4], gt[4];
+        for (int e = 0; e < 8; ++e) fa.v[e] = fds.v[e] * __builtin_amdgcn_exp2f(fgt.v[e] - fgr.v[e]);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        dt[b] = L2[t * kLD + c0 + b];
-        gt[b] = L4[t * kLD + c0 + b];
-      }
+        for (int J = 0; J < 3; ++J) {
+          if (J < wv) {
+            Frag<float> fw, fgu, fb;
+            load_frag_c(fw, T2 + (16 * J + r) * kFL + 32 * kb2);
+            load_frag_c(fgu, T3 + (16 * J + r) * kFL + 32 * kb2);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int u = r0 + a;
-        if (t >= u) {
-          const float at = LA[t * kLD + u];
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            dwv[a][b] += dt[b] * at * __builtin_amdgcn_exp2f(gt[b] - L4[u * kLD + c0 + b]);
+            for (int e = 0; e < 8; ++e) fb.v[e] = fw.v[e] * __builtin_amdgcn_exp2f(fgr.v[e] - fgu.v[e]);
+            mma(adA[J], fa, fb);
+          }
         }
       }
     }
-    store_rows(dw + rowbase * m + j0, m, dwv, r0, c0, rows);
-    // D = s*ds - w*dw into L1, then suffix sums down each column
+    // dA, the diagonal sub-block: (t = rho + 4 qd + e, u = rho + r), u <= t
+    {
+      const int u = rho + r;
+      float sum[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < kC; ++j) {
+        const float wu = T2[u * kFL + j], gu = T3[u * kFL + j];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int t = r0 + a;
-      const f32x4 sv = *reinterpret_cast<const f32x4*>(s + (rowbase + min(t, rows - 1)) * m + j0 + c0);
+        for (int e = 0; e < 4; ++e) {
+          const int t = rho + 4 * qd + e;
+          sum[e] += T1[t * kFL + j] * wu * __builtin_amdgcn_exp2f(T3[t * kFL + j] - gu);
+        }
+      }
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        L1[t * kLD + c0 + b] = t < rows ? sv[b] * L2[t * kLD + c0 + b] - L3[t * kLD + c0 + b] * dwv[a][b] : 0.f;
+      for (int e = 0; e < 4; ++e)
+        if (u <= rho + 4 * qd + e) adA[wv][e] += sum[e];
+    }
+
+    // dw for this wave's rows u = rho + 4 qd + e and slots j = 16 jt + r
+    float dwv[4][4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      const int j = 16 * jt + r;
+      const float gam = T3[(kC - 1) * kFL + j];   // g at the last valid row (flat past it)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dwv[jt][e] = __builtin_amdgcn_exp2f(gam - T3[(rho + 4 * qd + e) * kFL + j]) * kds[jt][e];
+    }
+    // later sub-chunks (t > rho' = rho + 15), rebased on rho'
+    if (wv < 3) {
+      const int rp = rho + 15;
+      f32x4 tmp[4];
+      zero4(tmp);
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        if (32 * kb2 + 31 > rp) {
+          Frag<float> fa;   // A[t][u], u = rho + r, t = 32 kb2 + 8 qd + e > rp
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int t = 32 * kb2 + 8 * qd + e;
+            fa.v[e] = t > rp ? T0[t * kFL + rho + r] : 0.f;
+          }
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt) {
+            const int j = 16 * jt + r;
+            const float grp = T3[rp * kFL + j];
+            Frag<float> fb;   // ds[t][j] e^{g_tj - g_rp,j}
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int t = 32 * kb2 + 8 * qd + e;
+              fb.v[e] = t > rp ? T1[t * kFL + j] * __builtin_amdgcn_exp2f(T3[t * kFL + j] - grp) : 0.f;
+            }
+            mma(tmp[jt], fa, fb);
+          }
+        }
+      }
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int j = 16 * jt + r;
+        const float grp = T3[rp * kFL + j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dwv[jt][e] += tmp[jt][e] * __builtin_amdgcn_exp2f(grp - T3[(rho + 4 * qd + e) * kFL + j]);
+      }
+    }
+    // the diagonal sub-block: targets t in [u, rho + 15]
+    {
+      float gu[4][4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) gu[e][jt] = T3[(rho + 4 * qd + e) * kFL + 16 * jt + r];
+      for (int t = rho; t < rho + 16; ++t) {
+        float dt[4], gt[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          dt[jt] = T1[t * kFL + 16 * jt + r];
+          gt[jt] = T3[t * kFL + 16 * jt + r];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int u = rho + 4 * qd + e;
+          if (t >= u) {
+            const float at = T0[t * kFL + u];
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt)
+              dwv[jt][e] += dt[jt] * at * __builtin_amdgcn_exp2f(gt[jt] - gu[e][jt]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int u = rho + 4 * qd + e;
+      if (u < rows) {
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) dw[(rowbase + u) * m + j0 + 16 * jt + r] = dwv[jt][e];
+      }
+    }
+    // D = s*ds - w*dw in place of w (each lane its own entries, after every read of w),
+    // then suffix sums down each slot column
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = rho + 4 * qd + e;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int j = 16 * jt + r;
+        const float sv = s[(rowbase + min(t, rows - 1)) * m + j0 + j];
+        T2[t * kFL + j] = t < rows ? sv * T1[t * kFL + j] - T2[t * kFL + j] * dwv[jt][e] : 0.f;
+      }
     }
     __syncthreads();
     if (threadIdx.x < kC) {
       const int j = threadIdx.x;
       float run = 0.f;
       for (int t = kC - 1; t >= 0; --t) {
-        run += L1[t * kLD + j];
+        run += T2[t * kFL + j];
         if (t < rows) Dloc[(rowbase + t) * m + j0 + j] = run;
       }
       tot[((long)bh * N + i) * m + j0 + j] = run;
     }
     __syncthreads();
   }
+
+  // dA (masked) into T3 as [t][u] and into T0 (A is dead) as [u][t]
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int J = 0; J < 4; ++J)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) LdA[(r0 + a) * kLD + c0 + b] = c0 + b <= r0 + a ? adA[a][b] : 0.f;
+    for (int e = 0; e < 4; ++e) {
+      const int t = rho + 4 * qd + e, u = 16 * J + r;
+      const float x = (J <= wv && u <= t) ? adA[J][e] : 0.f;
+      T3[t * kFL + u] = x;
+      T0[u * kFL + t] = x;
+    }
   __syncthreads();
 
   for (int d0 = 0; d0 < dk; d0 += kC) {
-    float aq[4][4], ak[4][4];   // (t, d) and (u, d)
-    zero44(aq);
-    zero44(ak);
+    f32x4 aq[4], ak[4];   // dq (rows t), dk (rows u) of this wave, columns d0 + 16 jt + r
+    zero4(aq);
+    zero4(ak);
     for (int j0 = 0; j0 < m; j0 += kC) {
-      load_blk(L2, ds + rowbase * m + j0, m, rows, false);
-      load_blk(L3, w + rowbase * m + j0, m, rows, false);
-      load_blk(L4, g2 + rowbase * m + j0, m, rows, false);
-      load_blk(L0, Sb + (long)j0 * dk + d0, dk, kC, false);    // S1   [j][d]
-      load_blk(L1, dSb + (long)j0 * dk + d0, dk, kC, false);   // dS1  [j][d]
-      __syncthreads();
-      // ds * e^g and w * e^(gamma - g), in place (each thread its own entries)
+      // ds e^{g} [t][j] and S1^T [d][j]
 #pragma unroll
-      for (int uu = 0; uu < 16; ++uu) {
-        const int idx = threadIdx.x + kThreads * uu, r = idx >> 6, c = idx & 63;
-        const float gv = L4[r * kLD + c];
-        L2[r * kLD + c] *= __builtin_amdgcn_exp2f(gv);
-        L3[r * kLD + c] *= __builtin_amdgcn_exp2f(L4[(rows - 1) * kLD + c] - gv);
+      for (int uu = 0; uu < 4; ++uu) {
+        const int idx = threadIdx.x + kThreads * uu, rr = idx >> 4, c = (idx & 15) * 4;
+        const long off = (rowbase + min(rr, rows - 1)) * m + j0 + c;
+        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(ds + off);
+        const f32x4 gv4 = *reinterpret_cast<const f32x4*>(g2 + off);
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = rr < rows ? dv4[e] * __builtin_amdgcn_exp2f(gv4[e]) : 0.f;
+        *reinterpret_cast<f32x4*>(T1 + rr * kFL + c) = x;
       }
+      stage_cols(T2, Sb + (long)j0 * dk + d0, dk, kC);
       __syncthreads();
-      mm64(aq, L2, kLD, 1, L0, 1, kLD, r0, c0);
-      mm64(ak, L3, kLD, 1, L1, 1, kLD, r0, c0);
+      mm_rows(aq, T1, T2, wv);
+      __syncthreads();
+      // w e^{gamma - g} [u][j] and dS1^T [d][j]
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu) {
+        const int idx = threadIdx.x + kThreads * uu, rr = idx >> 4, c = (idx & 15) * 4;
+        const long off = (rowbase + min(rr, rows - 1)) * m + j0 + c;
+        const f32x4 wv4 = *reinterpret_cast<const f32x4*>(w + off);
+        const f32x4 gv4 = *reinterpret_cast<const f32x4*>(g2 + off);
+        const f32x4 ga4 = *reinterpret_cast<const f32x4*>(g2 + (rowbase + rows - 1) * m + j0 + c);
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x[e] = rr < rows ? wv4[e] * __builtin_amdgcn_exp2f(ga4[e] - gv4[e]) : 0.f;
+        *reinterpret_cast<f32x4*>(T1 + rr * kFL + c) = x;
+      }
+      stage_cols(T2, dSb + (long)j0 * dk + d0, dk, kC);
+      __syncthreads();
+      mm_rows(ak, T1, T2, wv);
       __syncthreads();
     }
-    load_blk(L0, qb + d0, dk, rows, false);   // q [t][d]
-    load_blk(L1, kb + d0, dk, rows, false);   // k [u][d]
+    // + dA k and dA^T q: k^T, q^T [d][row]
+    stage_cols(T1, kb + d0, dk, rows);
+    stage_cols(T2, qb + d0, dk, rows);
     __syncthreads();
-    mm64(aq, LdA, kLD, 1, L1, 1, kLD, r0, c0);   // sum_u dA[t][u] k[u][d]
-    mm64(ak, LdA, 1, kLD, L0, 1, kLD, r0, c0);   // sum_t dA[t][u] q[t][d]
-    store_rows(dq + rowbase * dk + d0, dk, aq, r0, c0, rows);
-    store_rows(dk_out + rowbase * dk + d0, dk, ak, r0, c0, rows);
+    mm_rows(aq, T3, T1, wv);
+    mm_rows(ak, T0, T2, wv);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = rho + 4 * qd + e;
+      if (t < rows) {
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          dq[(rowbase + t) * dk + d0 + 16 * jt + r] = aq[jt][e];
+          dk_out[(rowbase + t) * dk + d0 + 16 * jt + r] = ak[jt][e];
+        }
+      }
+    }
     __syncthreads();
   }
 }
