@@ -98,10 +98,6 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
     if stage == "fwd_fused":
         byt = 2 * tokp * dk * e + BH * N * C * C * e + 2 * tok * dv * e + BH * dk * dv * 4
         return byt, tok * (4 * dk * dv + C * dv)
-    if stage == "bwd_chunk":
-        byt = (tok * (2 * dk * e + 2 * dv * e + dk * 4) + BH * N * C * C * e + tokp * dk * e
-               + 2 * st + tok * (2 * dk * e + dv * e + dk * 4))
-        return byt, tok * (6 * dk * dv + C * (2 * dk + 2 * dv))
     if stage == "bwd_dqk_dv":
         # dq/dk part: reads q, k, v, dO, log_alpha, S, dS, chunk totals; writes dq, dk, dla
         byt = (tok * (2 * dk * e + 2 * dv * e + dk * e) + 2 * st + BH * N * dk * 4
@@ -114,8 +110,6 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
         return byt, fl
     if stage == "gate_tot":
         return 2 * BH * N * (dv // 64) * dk * 4 + BH * N * dk * 4, 0
-    if stage == "gate_grad":
-        return tok * dk * (4 + e), tok * dk
     if stage == "state_dot":
         return 2 * BH * dk * dv * 4, 2 * BH * dk * dv
     return 0, 0

@@ -76,8 +76,7 @@ Plan plan_of(const gla_desc_t* d, int pass) {
     // the scans' transposed operands are kept in fp32 (split into two bf16 halves)
     const size_t op32 = rowsP * x.dk * 4;
     const size_t crossB = (size_t)x.BH * x.N * (x.dv / 64) * x.dk * 4;
-    // g for the single-kernel chunk backward (the split path rebuilds it from the gates)
-    if (!gla::bwd_split(x.dtype, (int)x.C)) p.g = take(gB);
+    // (the chunk kernel rebuilds g from the gates: no g in the workspace)
     p.A = take(AB);
     p.QhT = take(op32);
     p.Kh = take(opB);
@@ -87,11 +86,10 @@ Plan plan_of(const gla_desc_t* d, int pass) {
     p.dst = take(stB);
     p.ST = take((size_t)x.BH * x.dk * x.dv * 4);
     p.cT = take((size_t)x.BH * x.dk * 4);
-    if (!gla::bwd_split(x.dtype, (int)x.C)) p.Dloc = take(gB);   // the split path writes dla directly
     p.crossF = take(crossB);
     p.crossR = take(crossB);
     p.carry = take(egB);
-    if (d->gate_shape == GLA_GATE_SCALAR && gla::bwd_split(x.dtype, (int)x.C))
+    if (d->gate_shape == GLA_GATE_SCALAR)
       p.dpart = take((size_t)x.BH * x.T * (x.dk / 64) * 4);
   } else {
     p.KhT = take(opB);
@@ -149,8 +147,6 @@ struct Tracer {
 const char* const kFwdMat[] = {"gate_cumsum", "intra", "state_scan", "output"};
 const char* const kFwdRec[] = {"intra", "seg_state", "fwd_fused"};
 const char* const kBwd[] = {"intra", "state_scans", "state_dot", "gate_tot", "bwd_dqk_dv"};
-const char* const kBwdOne[] = {"intra", "state_scans", "state_dot", "bwd_chunk", "gate_tot",
-                               "gate_grad"};
 
 int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, int max) {
   const char* const* src;
@@ -158,10 +154,8 @@ int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, in
   if (pass == GLA_PASS_FWD) {
     if (d->state_mode == GLA_STATES_MATERIALIZED) { src = kFwdMat; n = 4; }
     else { src = kFwdRec; n = 3; }
-  } else if (gla::bwd_split(d->dtype, d->chunk)) {
-    src = kBwd; n = 5;
   } else {
-    src = kBwdOne; n = 6;
+    src = kBwd; n = 5;
   }
   int m = 0;
   for (int j = 0; j < n; ++j) {
@@ -382,9 +376,8 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   gla::IntraArgs ia{};
   ia.dtype = x.dtype; ia.C = C; ia.BH = BH; ia.T = T; ia.dk = DK; ia.N = N; ia.want_A = true;
   ia.xt_f32 = x.dtype == GLA_BF16;
-  const bool split = gla::bwd_split(x.dtype, C);
   ia.q = q; ia.k = k; ia.la = log_alpha; ia.g = nullptr;
-  ia.g2_out = split ? nullptr : (float*)(w + p.g);
+  ia.g2_out = nullptr;
   ia.gate = gate_of(d); ia.gscalar = scalar_gate(d); ia.diag_bf16 = d->diag == GLA_DIAG_BF16;
   ia.A = w + p.A; ia.QhT = w + p.QhT; ia.Kh = w + p.Kh; ia.KhT = w + p.KhT;
   ia.eg = (float*)(w + p.eg);
@@ -403,9 +396,9 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   ra.reverse = true; ra.XT = w + p.QhT; ra.Y = dO; ra.X2T = w + p.KhT; ra.Y2 = v;
   ra.cross = (float*)(w + p.crossR); ra.S_in = dS_T; ra.states = w + p.dst; ra.S_out = dS0;
   // S and dS go to the backward chunk kernel in MFMA fragment order when the scans run
-  // 128-column tiles (split path): its dq / dk workgroups load whole fragments, its dv
+  // 128-column tiles (bf16, chunk 64): its dq / dk workgroups load whole fragments, its dv
   // workgroups stage dS transposed from them
-  sa.frag_states = split && gla::scan_tile_v(sa) == 128;
+  sa.frag_states = gla::scan_tile_v(sa) == 128;
   ra.frag_states = sa.frag_states;
   // both scans in one launch
   if ((rs = tr.mark()) != GLA_OK) return rs;
@@ -419,13 +412,11 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   }
   gla::BwdArgs ba{};
   ba.dtype = x.dtype; ba.C = C; ba.BH = BH; ba.T = T; ba.dk = DK; ba.dv = DV; ba.N = N;
-  ba.q = q; ba.k = k; ba.v = v; ba.dO = dO; ba.gamma = nullptr;
-  ba.g = split ? nullptr : (const float*)(w + p.g);
+  ba.q = q; ba.k = k; ba.v = v; ba.dO = dO;
   ba.gscalar = scalar_gate(d);
   ba.s_frag = sa.frag_states;
   ba.A = w + p.A; ba.Kh = w + p.Kh; ba.S = w + p.st; ba.dS = w + p.dst;
   ba.dq = dq; ba.dk_out = dk; ba.dv_out = dv;
-  ba.Dloc = p.Dloc ? (float*)(w + p.Dloc) : nullptr;
   ba.tot = (const float*)(w + p.carry); ba.cT = dS_T ? (const float*)(w + p.cT) : nullptr;
   ba.dla = dlog_alpha; ba.la = log_alpha; ba.gate = gate_of(d);
   // scalar gates: the per-key gradient is summed over the key dimension afterwards, and
@@ -444,32 +435,14 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
                                     (float*)(w + p.carry), BH, T, DK,
                                     DV / gla::scan_tile_v(sa), C, s));
   };
-  if (gla::bwd_split(x.dtype, C)) {
-    // totals first: the dq / dk kernel finishes the gate gradient itself
-    if ((rs = tr.mark()) != GLA_OK) return rs;
-    if ((rs = totals()) != GLA_OK) return rs;
-    if ((rs = tr.mark()) != GLA_OK) return rs;
-    if ((rs = dev(gla::launch_bwd_chunk(ba, s))) != GLA_OK) return rs;
-    if (sg) {
-      if ((rs = tr.mark()) != GLA_OK) return rs;
-      if ((rs = reduce((const float*)(w + p.dpart), DK / 64)) != GLA_OK) return rs;
-    }
-    return tr.mark();
-  }
-  if ((rs = tr.mark()) != GLA_OK) return rs;
-  if ((rs = dev(gla::launch_bwd_chunk(ba, s))) != GLA_OK) return rs;
+  // totals first: the chunk kernel's dq / dk workgroups finish the gate gradient
   if ((rs = tr.mark()) != GLA_OK) return rs;
   if ((rs = totals()) != GLA_OK) return rs;
   if ((rs = tr.mark()) != GLA_OK) return rs;
-  // scalar gates: the per-key gradient overwrites D in place, then the sum over d
-  rs = dev(gla::launch_gate_grad(x.dtype, (const float*)(w + p.Dloc), (const float*)(w + p.carry),
-                                 dS_T ? (const float*)(w + p.cT) : nullptr, log_alpha, gate_of(d),
-                                 dlog_alpha, sg ? (float*)(w + p.Dloc) : nullptr, BH, T, DK, C,
-                                 s));
-  if (rs != GLA_OK) return rs;
+  if ((rs = dev(gla::launch_bwd_chunk(ba, s))) != GLA_OK) return rs;
   if (sg) {
     if ((rs = tr.mark()) != GLA_OK) return rs;
-    if ((rs = reduce((const float*)(w + p.Dloc), DK)) != GLA_OK) return rs;
+    if ((rs = reduce((const float*)(w + p.dpart), DK / 64)) != GLA_OK) return rs;
   }
   return tr.mark();
 }

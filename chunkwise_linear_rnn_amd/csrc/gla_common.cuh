@@ -201,16 +201,6 @@ __device__ __forceinline__ void stage_cols(OpT* lds, int lld, const Tin* src, lo
   }
 }
 
-// Fragment of 8 consecutive input elements (widened, then rounded to the operand type);
-// zero when !valid.
-template <typename OpT, typename Tin>
-__device__ __forceinline__ void load_frag_gc(Frag<OpT>& f, const Tin* p, bool valid) {
-  float x[8];
-  if (valid) load8(x, p + 8 * (lane_id() >> 4)); else zero8(x);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f.set(e, x[e]);
-}
-
 // An operand as high part + remainder in the MFMA type (bf16), or as is (fp32).
 template <typename OpT>
 struct SFrag {

@@ -127,24 +127,21 @@ hipError_t launch_fwd_fused(const FusedArgs& a, hipStream_t s);
 struct BwdArgs {
   int dtype, C, BH, T, dk, dv, N;
   const void *q, *k, *v, *dO;
-  const float *g, *gamma;   // g: g * log2(e) [BH][T][dk] (from the intra-chunk kernel; the
-                            // split path rebuilds it from la and does not read it)
   const void *A, *Kh, *S, *dS;
   void *dq, *dk_out, *dv_out;
-  float* Dloc;             // chunk-local suffix sums of D (single-kernel path)
-  const float *tot, *cT;   // chunk totals of D, rowsum(dS_T * S_T) or NULL (split path)
-  void* dla;               // dlog_alpha, written directly (split path)
-  const void* la;          // the gate operand, for the gate front-end's chain rule
+  const float *tot, *cT;   // chunk totals of D, rowsum(dS_T * S_T) or NULL
+  void* dla;               // dlog_alpha, written directly
+  const void* la;          // the gate operand: g is rebuilt from it, and the gate
+                           // front-end's chain rule applied
   GateFn gate;
-  float* dla_part;         // scalar gates (split path): fp32 sums of the per-(t, d) gradient
-                           // over each 64-wide d block, [BH][T][dk/64], instead of dla
+  float* dla_part;         // scalar gates: fp32 sums of the per-(t, d) gradient over each
+                           // 64-wide d block, [BH][T][dk/64], instead of dla
   bool gscalar;            // la holds one gate per token: [BH][T]
-  bool s_frag;             // S and dS (split path) in MFMA fragment order, as the scans wrote them
+  bool s_frag;             // S and dS in MFMA fragment order, as the scans wrote them
 };
-// The backward chunk work (launch_bwd_chunk): with bf16 operands and chunk 64 one launch of
-// dq / dk / dlog_alpha workgroups (after the chunk totals are formed) interleaved with dv
-// workgroups; otherwise one workgroup per chunk, followed by the gate-gradient kernel.
-bool bwd_split(int dtype, int C);
+// The backward chunk work (launch_bwd_chunk, after the chunk totals are formed): one
+// launch of dq / dk / dlog_alpha workgroups interleaved with dv workgroups (bf16 with
+// chunk 64 or 128, fp32 with chunk 64).
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s);
 
 // Recurrent evaluation (decoding): T tokens in order, state updated in place.

@@ -19,11 +19,13 @@
 // gate gradient sums q*dq - k*dk with heavy cancellation.  Diagonal sub-blocks are summed
 // in fp32, each exp(g_t - g_s) (a product of per-row decays, all at most 1) shared by its
 // dQ and dK terms.
-// The chunk-local suffix sums of D are completed by the gate-gradient kernel with the
-// chunk totals that the two state scans form from their fp32 states.
+// The dq/dk workgroups finish the gate gradient themselves: the chunk-local suffix sums
+// of D plus the carry of the later chunks' totals, which the two state scans form from
+// their fp32 states (summed by the gate-total kernel before this launch).
 //
-// Kernels
-//   k_bwd_dqk_dv (chunk 64) one launch holding two kinds of workgroup, interleaved:
+// Kernel
+//   k_bwd_dqk_dv (bf16 with chunk 64 or 128, fp32 with chunk 64) one launch holding two
+//   kinds of workgroup, interleaved:
 //   dq/dk part  dq, dk and dlog_alpha per (chunk, 64-wide dk block): D as
 //              chunk-local suffix sums plus the carry from the later chunks' totals
 //              (formed by the gate-total kernel from the scans).  One pass over
@@ -33,8 +35,9 @@
 //              intra-chunk part of the block.
 //   dv part     dv = A^T dO + Kh dS per (chunk, 64 values), looping over 64-wide dk
 //              blocks.
-//   k_bwd_chunk (chunk 128, and fp32 operands) all of the above in one workgroup per
-//              chunk, operands read straight from memory.
+//   fp32 operands take tiles with rows padded for 4-byte elements, unswizzled
+//   transposed staging and the off-diagonal products as plain fp32 MFMAs (two
+//   workgroups per CU); chunk 128 keeps two dA row tiles per wave (one per CU).
 #include "gla_common.cuh"
 #include "gla_gate.cuh"
 #include "gla_internal.h"
@@ -66,175 +69,6 @@ __device__ __forceinline__ void diag_block16(const float (&gt)[16], const float 
   }
 }
 
-// LDS of the intra-chunk / D phase for one dk block of DB columns.
-template <int C, int DB, typename Tin>
-struct IntraLds {
-  static constexpr int FLD = C + 4, GLD = DB + 4, XLD = DB + 8;
-  float* dAs;   // [C][FLD] dA in fp32 (written before the first block)
-  float* gs;    // [C][GLD] g * log2 e
-  Tin* qs;      // [C][XLD]
-  Tin* ks;
-  float* dqd;   // [C][GLD]
-  float* dkd;
-  static constexpr int bytes_blk = C * GLD * 4 * 3 + C * XLD * (int)sizeof(Tin) * 2;
-};
-
-// Stage g (already times log2 e; rows past T continue the last valid row), q, k for dk
-// columns [d0, d0 + DB) of the chunk.  Ends with a barrier.
-template <int C, int DB, int DK, typename Tin>
-__device__ __forceinline__ void bwd_stage_block(const IntraLds<C, DB, Tin>& L, const Tin* q,
-                                                const Tin* k, const float* g, long tok0,
-                                                int rows, int d0) {
-  constexpr int GLD = IntraLds<C, DB, Tin>::GLD, XLD = IntraLds<C, DB, Tin>::XLD;
-  for (int idx = threadIdx.x; idx < C * (DB / 8); idx += kThreads) {
-    const int rr = idx / (DB / 8), c = (idx % (DB / 8)) * 8;
-    float x[8];
-    load8(x, g + (tok0 + min(rr, rows - 1)) * DK + d0 + c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) L.gs[rr * GLD + c + e] = x[e];
-  }
-  stage_rows<Tin, Tin, C, DB>(L.qs, XLD, q + tok0 * DK + d0, DK, rows);
-  stage_rows<Tin, Tin, C, DB>(L.ks, XLD, k + tok0 * DK + d0, DK, rows);
-  __syncthreads();
-}
-
-// Given the inter-chunk products dO S^T (adq) and V dS^T (adk) of this block, unscaled,
-// in accumulator layout (wave column tile ct, M-tiles mg + MG*jj), finish dq, dk: decay
-// scaling, intra-chunk terms, output, D suffix sums.  Ends with a barrier.
-template <int C, int DB, int DK, int NMW, int MG, typename Tin, typename OpT>
-__device__ __forceinline__ void bwd_finish_block(const IntraLds<C, DB, Tin>& L,
-                                                 f32x4 (&adq)[NMW], f32x4 (&adk)[NMW],
-                                                 Tin* dq, Tin* dk_out, float* Dloc, long tok0,
-                                                 int rows, int d0, int ct, int mg) {
-  constexpr int NS = C / 16;
-  constexpr int FLD = IntraLds<C, DB, Tin>::FLD, GLD = IntraLds<C, DB, Tin>::GLD,
-                XLD = IntraLds<C, DB, Tin>::XLD;
-  const int l = lane_id(), r = l & 15, qd = l >> 4;
-  const int c = 16 * ct + r;   // column of this lane within the block
-  const float gl = L.gs[(C - 1) * GLD + c];   // gamma * log2 e
-#pragma unroll
-  for (int jj = 0; jj < NMW; ++jj) {
-    const int m = mg + MG * jj;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float gt = L.gs[(16 * m + 4 * qd + e) * GLD + c];
-      adq[jj][e] *= __builtin_amdgcn_exp2f(gt);
-      adk[jj][e] *= __builtin_amdgcn_exp2f(gl - gt);
-    }
-  }
-  // intra-chunk, off-diagonal sub-blocks
-#pragma unroll
-  for (int jj = 0; jj < NMW; ++jj) {
-    const int m = mg + MG * jj;
-    if (m > 0) {   // dq rows of sub-chunk I = m, sources J < I
-      const int rho = 16 * m;
-      const float gr = L.gs[rho * GLD + c];
-      f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
-      for (int kb = 0; kb < (16 * m + 31) / 32; ++kb) {
-        SFrag<OpT> fa, fb;
-        float xa[8];
-        load8(xa, L.dAs + (16 * m + r) * FLD + kb * 32 + 8 * qd);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int s = kb * 32 + 8 * qd + e;
-          fa.set(e, xa[e]);
-          fb.set(e, s < rho ? to_f32(L.ks[s * XLD + c]) *
-                                  __builtin_amdgcn_exp2f(gr - L.gs[s * GLD + c])
-                            : 0.f);
-        }
-        mma_split(tmp, fa, fb);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        adq[jj][e] += tmp[e] * __builtin_amdgcn_exp2f(L.gs[(rho + 4 * qd + e) * GLD + c] - gr);
-    }
-    if (m < NS - 1) {   // dk rows of sub-chunk J = m, sources I > J
-      const int rho = 16 * m + 15;
-      const float gr = L.gs[rho * GLD + c];
-      f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
-      for (int kb = (16 * m + 16) / 32; kb < C / 32; ++kb) {
-        SFrag<OpT> fa, fb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int t = kb * 32 + 8 * qd + e;
-          const bool on = t > rho;
-          fa.set(e, on ? L.dAs[t * FLD + 16 * m + r] : 0.f);
-          fb.set(e, on ? to_f32(L.qs[t * XLD + c]) * __builtin_amdgcn_exp2f(L.gs[t * GLD + c] - gr)
-                       : 0.f);
-        }
-        mma_split(tmp, fa, fb);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        adk[jj][e] += tmp[e] * __builtin_amdgcn_exp2f(gr - L.gs[(16 * m + 4 * qd + e) * GLD + c]);
-    }
-  }
-  // intra-chunk, diagonal sub-blocks: one thread per (sub-chunk, column)
-  {
-    const int m = threadIdx.x / DB, cc = threadIdx.x % DB, base = 16 * m;
-    float gt[16], qv[16], kv[16], aq[16], ak[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      gt[j] = L.gs[(base + j) * GLD + cc];
-      qv[j] = to_f32(L.qs[(base + j) * XLD + cc]);
-      kv[j] = to_f32(L.ks[(base + j) * XLD + cc]);
-      aq[j] = 0.f;
-      ak[j] = 0.f;
-    }
-    diag_block16(gt, qv, kv, L.dAs + base * FLD + base, FLD, aq, ak);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      L.dqd[(base + j) * GLD + cc] = aq[j];
-      L.dkd[(base + j) * GLD + cc] = ak[j];
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int jj = 0; jj < NMW; ++jj) {
-    const int m = mg + MG * jj;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 16 * m + 4 * qd + e;
-      adq[jj][e] += L.dqd[t * GLD + c];
-      adk[jj][e] += L.dkd[t * GLD + c];
-    }
-  }
-  __syncthreads();
-  // finish dq, dk; D = q*dq - k*dk into dqd
-#pragma unroll
-  for (int jj = 0; jj < NMW; ++jj) {
-    const int m = mg + MG * jj;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 16 * m + 4 * qd + e;
-      if (t < rows) {
-        dq[(tok0 + t) * DK + d0 + c] = from_f32<Tin>(adq[jj][e]);
-        dk_out[(tok0 + t) * DK + d0 + c] = from_f32<Tin>(adk[jj][e]);
-      }
-      L.dqd[t * GLD + c] =
-          to_f32(L.qs[t * XLD + c]) * adq[jj][e] - to_f32(L.ks[t * XLD + c]) * adk[jj][e];
-    }
-  }
-  __syncthreads();
-  // chunk-local suffix sums of D, column by column (segmented)
-  {
-    constexpr int NSEG = kThreads / DB, SL = C / NSEG;
-    const int col = threadIdx.x % DB, seg = threadIdx.x / DB;
-    float run = 0.f;
-    for (int rr = seg * SL + SL - 1; rr >= seg * SL; --rr) {
-      run += L.dqd[rr * GLD + col];
-      L.dqd[rr * GLD + col] = run;
-    }
-    L.dkd[seg * DB + col] = run;
-    __syncthreads();
-    float off = 0.f;
-    for (int s2 = seg + 1; s2 < NSEG; ++s2) off += L.dkd[s2 * DB + col];
-    for (int rr = seg * SL; rr < seg * SL + SL; ++rr)
-      if (rr < rows) Dloc[(tok0 + rr) * DK + d0 + col] = L.dqd[rr * GLD + col] + off;
-  }
-  __syncthreads();
-}
-
 // =====================================================================================
 // chunk 64, dq/dk part: one workgroup per (batch*head, chunk, 64-wide dk block)
 // =====================================================================================
@@ -242,12 +76,15 @@ __device__ __forceinline__ void bwd_finish_block(const IntraLds<C, DB, Tin>& L,
 // accumulator tiles each for dq and dk).  dA = tril(dO V^T) is formed by every dk block of
 // the chunk (it is cheap next to the dO S^T and V dS^T products, and keeps the blocks
 // independent).  Three workgroups fit on a CU, so one's loads overlap another's math.
-// LDS of a dq/dk workgroup for chunk C: dA [C][C + 4] fp32, the region of the staged g
-// block [C][68] and of g^T [64][C + 4] fp32, q and k [C][72]
-constexpr int dqk_lds_bytes(int C) {
-  return C * (C + 4) * 4 + (C * 68 > 64 * (C + 4) ? C * 68 : 64 * (C + 4)) * 4 + 2 * C * 72 * 2;
+// LDS of a dq/dk workgroup for chunk C and ES-byte elements: dA [C][C + 4] fp32, the
+// region of the staged g block [C][68] and of g^T [64][C + 4] fp32, q and k [C][72]
+constexpr int dqk_lds_bytes(int C, int ES = 2) {
+  return C * (C + 4) * 4 + (C * 68 > 64 * (C + 4) ? C * 68 : 64 * (C + 4)) * 4 + 2 * C * 72 * ES;
 }
 constexpr int kDqkLds = dqk_lds_bytes(64);
+// Row pad of a row-major 64-wide fragment-source tile in LDS: bf16 rows of 80 elements,
+// fp32 rows of 68 (16-byte fragment reads of 16 consecutive rows on distinct banks)
+template <typename T> constexpr int frag_row_ld() { return sizeof(T) == 2 ? 64 + 16 : 64 + 4; }
 // SFRAG: S and dS in MFMA fragment order (fragment (16-row block, 32-column block) of a
 // chunk's [dk][dv] state: lane 16 q + r holds row r, columns 8 q .. 8 q + 7), as the scans
 // write them for 128-column tiles; otherwise row-major.
@@ -262,20 +99,20 @@ __device__ __forceinline__ void bwd_dqk_body(
   static_assert(sizeof(Tin) == sizeof(OpT), "input and operand types match");
   // dO / V rows padded to 80: their 16-byte fragment reads (16 consecutive rows) then fall
   // on distinct banks
-  constexpr int NM = C / 16, NS = C / 16, YLD = 64 + 16;
+  constexpr int ES = sizeof(Tin), NM = C / 16, NS = C / 16, YLD = frag_row_ld<OpT>();
   constexpr int NRT = NM / 4;   // dA row tiles per wave: w, w + 4, ...
   constexpr int FLD = C + 4, GLD = 64 + 4, XLD = 64 + 8;
   constexpr int GTLD = C + 4;   // g^T rows (a column's C rows)
   // LDS: dA [C][FLD] fp32, then a region that holds the dO / V tiles during the dv loop,
   // then the staged g block [C][GLD] and in its place g^T [64 columns][GTLD] fp32 (a
   // column's rows contiguous: the post-loop phases read 4 to 16 consecutive rows of one
-  // column), q, k [C][XLD] afterwards.  Chunk 64: 53248 bytes, three workgroups per CU;
-  // chunk 128: 139264 bytes, one.
+  // column), q, k [C][XLD] afterwards.  Chunk 64: 53248 bytes (bf16), three workgroups per
+  // CU, or 71680 (fp32), two; chunk 128: 139264 bytes, one.
   constexpr int GBYTES = (C * GLD > 64 * GTLD ? C * GLD : 64 * GTLD) * 4;
-  constexpr int o_u = C * FLD * 4, o_q = o_u + GBYTES, o_k = o_q + C * XLD * 2;
-  constexpr int bytes = o_k + C * XLD * 2;
-  static_assert(2 * C * YLD * 2 <= bytes - o_u, "dO / V tiles fit the shared region");
-  static_assert(bytes == dqk_lds_bytes(C), "arena size");
+  constexpr int o_u = C * FLD * 4, o_q = o_u + GBYTES, o_k = o_q + C * XLD * ES;
+  constexpr int bytes = o_k + C * XLD * ES;
+  static_assert(2 * C * YLD * ES <= bytes - o_u, "dO / V tiles fit the shared region");
+  static_assert(bytes == dqk_lds_bytes(C, ES), "arena size");
   // the first-pass diagonal terms of dk go to dA's columns 64 .. (chunk 128) or to g's
   // region (chunk 64)
   constexpr int DKLD = C == 64 ? GLD : FLD;
@@ -433,11 +270,15 @@ __device__ __forceinline__ void bwd_dqk_body(
       if (s2 <= t) dAs[t * FLD + s2] *= __builtin_amdgcn_exp2f(gs[t] - gs[s2]);
     }
     __syncthreads();
+    // (fp32 operands: one exact part)
+    constexpr bool P3 = sizeof(OpT) == 2;
     auto split3 = [](float x, Frag<OpT>& h, Frag<OpT>& md, Frag<OpT>& lo, int e) {
       h.set(e, x);
-      const float r1 = x - h.get(e);
-      md.set(e, r1);
-      lo.set(e, r1 - md.get(e));
+      if constexpr (P3) {
+        const float r1 = x - h.get(e);
+        md.set(e, r1);
+        lo.set(e, r1 - md.get(e));
+      }
     };
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
@@ -456,8 +297,10 @@ __device__ __forceinline__ void bwd_dqk_body(
             fb.set(e, on ? to_f32(ks[s2 * XLD + c]) : 0.f);
           }
           mma(tq, h, fb);
-          mma(tq, md, fb);
-          mma(tq, lo, fb);
+          if constexpr (P3) {
+            mma(tq, md, fb);
+            mma(tq, lo, fb);
+          }
         }
         if (32 * kb + 31 >= 16 * m) {   // dk rows of tile m: sources t >= 16 m
           Frag<OpT> h, md, lo, fb;
@@ -469,8 +312,10 @@ __device__ __forceinline__ void bwd_dqk_body(
             fb.set(e, on ? to_f32(qs[t * XLD + c]) : 0.f);
           }
           mma(tk, h, fb);
-          mma(tk, md, fb);
-          mma(tk, lo, fb);
+          if constexpr (P3) {
+            mma(tk, md, fb);
+            mma(tk, lo, fb);
+          }
         }
       }
 #pragma unroll
@@ -641,7 +486,7 @@ __device__ __forceinline__ void bwd_dqk_body(
   }
   __syncthreads();
   constexpr int kPer = 16 / (int)sizeof(Tin), kRowUnits = 64 / kPer, kUnits = 3 * C * kRowUnits;
-  static_assert(3 * C * SLD * (int)sizeof(Tin) <= o_q, "staging stays clear of q / k");
+  static_assert(3 * C * SLD * (int)sizeof(Tin) <= bytes, "staging fits the arena (q, k dead)");
   static_assert(4 * C * 4 <= C * SLD * (int)sizeof(Tin), "row sums fit the third tile");
   const int ntile_out = dla_part ? 2 : 3;
   for (int idx = threadIdx.x; idx < kUnits; idx += kThreads) {
@@ -663,6 +508,15 @@ __device__ __forceinline__ void bwd_dqk_body(
 // =====================================================================================
 // dv = A^T dO + sum over 64-wide dk blocks of Kh_blk dS_blk; the next block's Kh and
 // dS^T tiles are loaded into registers while the current one multiplies.
+// Fragment read from a transposed tile staged by ColTile: row c, elements 32 kb + 8 q ..
+// (bf16: the chunk swizzle; fp32: plain rows)
+__device__ __forceinline__ void frag_t(Frag<bf16>& f, const bf16* t, int ld, int c, int kb) {
+  load_frag_cs(f, t, ld, c, kb);
+}
+__device__ __forceinline__ void frag_t(Frag<float>& f, const float* t, int ld, int c, int kb) {
+  load_frag_c(f, t + c * ld + kb * 32);
+}
+
 template <typename Tin, typename OpT, bool SFRAG, int C>
 __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
                                             const OpT* __restrict__ Kh,
@@ -671,11 +525,14 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
                                             const Tin* __restrict__ dO,
                                             Tin* __restrict__ dv_out, int T, int dk, int dv,
                                             int N) {
-  // the Kh block is read row-major (rows padded to 80 for conflict-free fragment reads),
-  // the transposed tiles through the swizzle of ColTile (rows of 72)
+  // the Kh block is read row-major (rows padded for conflict-free fragment reads); bf16
+  // transposed tiles through the swizzle of ColTile (rows of 72), fp32 ones unswizzled in
+  // rows of 68
   // LD: rows of 64 (the dS^T tile, the output staging); TLD: rows of C tokens (A^T, dO^T)
-  constexpr int NM = C / 16, LD = 64 + 8, TLD = C + 8, KLD = 64 + 16;
-  static_assert(C * KLD * 2 + 64 * LD * 2 + (C + 64) * TLD * 2 <= dqk_lds_bytes(C),
+  constexpr bool SW = sizeof(OpT) == 2;
+  constexpr int ES = sizeof(OpT), NM = C / 16, LD = SW ? 64 + 8 : 64 + 4, TLD = SW ? C + 8 : C + 4;
+  constexpr int KLD = frag_row_ld<OpT>();
+  static_assert(C * KLD * ES + 64 * LD * ES + (C + 64) * TLD * ES <= dqk_lds_bytes(C, ES),
                 "the dv tiles fit the shared arena");
   static_assert(C * LD <= C * KLD, "the output staging fits the Kh block's space");
   OpT* ksh = (OpT*)arena;        // Kh block [t][k]
@@ -698,7 +555,7 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
   constexpr int MJ = 4;
   RowTile<OpT, C, 64, KLD> tk[MJ];
   // transposed tiles are staged chunk-swizzled (conflict-free stores)
-  ColTile<OpT, OpT, 64, LD, kThreads, true> ts[MJ];
+  ColTile<OpT, OpT, 64, LD, kThreads, SW> ts[MJ];
   auto load_blk = [&](int jb) {
     const int jc = min(jb, NJ - 1);
     tk[jb].load(Khc + 64 * jc, dk, C);
@@ -707,8 +564,8 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
   };
   {
     // A^T in 64-column slices of A (its s index), dO^T
-    ColTile<OpT, OpT, C, TLD, kThreads, true> ta[C / 64];
-    ColTile<OpT, Tin, C, TLD, kThreads, true> to;
+    ColTile<OpT, OpT, C, TLD, kThreads, SW> ta[C / 64];
+    ColTile<OpT, Tin, C, TLD, kThreads, SW> to;
 #pragma unroll
     for (int h = 0; h < C / 64; ++h) ta[h].load(A + ((long)bh * N + i) * C * C + 64 * h, C, C);
     to.load(dO + ((long)bh * T + t0) * dv + v0, dv, rows);
@@ -727,12 +584,12 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
 #pragma unroll
   for (int kb = 0; kb < C / 32; ++kb) {
     Frag<OpT> fb;
-    load_frag_cs(fb, doT, TLD, 16 * w + r, kb);
+    frag_t(fb, doT, TLD, 16 * w + r, kb);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       if (32 * kb + 31 >= 16 * m) {
         Frag<OpT> fa;
-        load_frag_cs(fa, aT, TLD, 16 * m + r, kb);
+        frag_t(fa, aT, TLD, 16 * m + r, kb);
         mma(acc[m], fa, fb);
       }
     }
@@ -744,7 +601,7 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         Frag<OpT> fb;
-        load_frag_cs(fb, dsT, LD, 16 * w + r, kb);
+        frag_t(fb, dsT, LD, 16 * w + r, kb);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           Frag<OpT> fa;
@@ -777,165 +634,11 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
   }
 }
 
-// =====================================================================================
-// chunk 128: k_bwd_chunk (everything in one workgroup per chunk)
-// =====================================================================================
-template <int C, int DK, typename Tin, typename OpT>
-struct BwdLds {
-  static constexpr int DB = (C == 64) ? 64 : 32;
-  using IL = IntraLds<C, DB, Tin>;
-  static constexpr int ALD = C + 8;
-  static constexpr int o_dA = 0;
-  static constexpr int o_blk = o_dA + C * IL::FLD * 4;
-  static constexpr int end12 = o_blk + IL::bytes_blk;
-  static constexpr int o_AT = 0;
-  static constexpr int o_dOT = o_AT + C * ALD * (int)sizeof(OpT);
-  static constexpr int o_dST = o_dOT + 64 * ALD * (int)sizeof(OpT);
-  static constexpr int end3 = o_dST + 64 * (DK + 8) * (int)sizeof(OpT);
-  static constexpr int bytes = end12 > end3 ? end12 : end3;
-};
-
-template <typename Tin, typename OpT, int C, int DK>
-__global__ __launch_bounds__(kThreads) void k_bwd_chunk(
-    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
-    const Tin* __restrict__ dO, const float* __restrict__ g, const OpT* __restrict__ A,
-    const OpT* __restrict__ Kh, const OpT* __restrict__ S, const OpT* __restrict__ dS,
-    Tin* __restrict__ dq, Tin* __restrict__ dk_out, Tin* __restrict__ dv_out,
-    float* __restrict__ Dloc, int T, int dv, int N) {
-  using BL = BwdLds<C, DK, Tin, OpT>;
-  using IL = typename BL::IL;
-  constexpr int NM = C / 16, DB = BL::DB, ALD = BL::ALD, FLD = IL::FLD;
-  constexpr int CT = DB / 16, MG = 4 / CT, NMW = NM / MG;
-  __shared__ __attribute__((aligned(16))) char arena[BL::bytes];
-  IL L;
-  L.dAs = (float*)(arena + BL::o_dA);
-  L.gs = (float*)(arena + BL::o_blk);
-  L.qs = (Tin*)(arena + BL::o_blk + C * IL::GLD * 4);
-  L.ks = L.qs + C * IL::XLD;
-  L.dqd = (float*)(L.ks + C * IL::XLD);
-  L.dkd = L.dqd + C * IL::GLD;
-
-  const int i = blockIdx.x, bh = blockIdx.y;
-  const int t0 = i * C, rows = min(C, T - t0);
-  const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
-  const long tok0 = (long)bh * T + t0;
-
-  // phase 1: dA = tril(dO V^T)
-  {
-    constexpr int NT = NM * (NM + 1) / 2;
-    for (int p = w; p < NT; p += 4) {
-      int m = 0;
-      while ((m + 1) * (m + 2) / 2 <= p) ++m;
-      const int n = p - m * (m + 1) / 2;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const bool va = 16 * m + r < rows, vb = 16 * n + r < rows;
-      const Tin* ap = dO + (tok0 + 16 * m + r) * dv;
-      const Tin* bp = v + (tok0 + 16 * n + r) * dv;
-      for (int kb = 0; kb < dv / 32; ++kb) {
-        Frag<OpT> fa, fb;
-        load_frag_gc(fa, ap + kb * 32, va);
-        load_frag_gc(fb, bp + kb * 32, vb);
-        mma(acc, fa, fb);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tl = 4 * qd + e;
-        L.dAs[(16 * m + tl) * FLD + 16 * n + r] = (m == n && r > tl) ? 0.f : acc[e];
-      }
-    }
-  }
-
-  const int ct = w % CT, mg = w / CT;
-  const OpT* Si = S + ((long)bh * N + i) * DK * dv;
-  const OpT* dSi = dS + ((long)bh * N + i) * DK * dv;
-
-  // phase 2: dq, dk, D per dk block
-  for (int d0 = 0; d0 < DK; d0 += DB) {
-    bwd_stage_block<C, DB, DK, Tin>(L, q, k, g, tok0, rows, d0);
-    const int c = 16 * ct + r;
-    f32x4 adq[NMW], adk[NMW];
-#pragma unroll
-    for (int jj = 0; jj < NMW; ++jj) {
-      adq[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-      adk[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    const OpT* sp = Si + (long)(d0 + c) * dv;
-    const OpT* dsp = dSi + (long)(d0 + c) * dv;
-    for (int kb = 0; kb < dv / 32; ++kb) {
-      Frag<OpT> fS, fdS;
-      load_frag_c(fS, sp + kb * 32);
-      load_frag_c(fdS, dsp + kb * 32);
-#pragma unroll
-      for (int jj = 0; jj < NMW; ++jj) {
-        const int m = mg + MG * jj;
-        const bool valid = 16 * m + r < rows;
-        Frag<OpT> fa;
-        load_frag_gc(fa, dO + (tok0 + 16 * m + r) * dv + kb * 32, valid);
-        mma(adq[jj], fa, fS);
-        load_frag_gc(fa, v + (tok0 + 16 * m + r) * dv + kb * 32, valid);
-        mma(adk[jj], fa, fdS);
-      }
-    }
-    bwd_finish_block<C, DB, DK, NMW, MG, Tin, OpT>(L, adq, adk, dq, dk_out, Dloc, tok0, rows, d0,
-                                                   ct, mg);
-  }
-
-  // phase 3: dv = Kh dS_[i+1] + A^T dO
-  {
-    OpT* ATs = (OpT*)(arena + BL::o_AT);
-    OpT* dOT = (OpT*)(arena + BL::o_dOT);
-    OpT* dST = (OpT*)(arena + BL::o_dST);
-    constexpr int SLD = DK + 8;
-    stage_cols<OpT, OpT, C, C>(ATs, ALD, A + ((long)bh * N + i) * C * C, C, C);
-    const OpT* khp = Kh + ((long)bh * N * C + t0) * DK;
-    for (int vb0 = 0; vb0 < dv; vb0 += 64) {
-      stage_cols<OpT, Tin, C, 64>(dOT, ALD, dO + tok0 * dv + vb0, dv, rows);
-      stage_cols<OpT, OpT, DK, 64>(dST, SLD, dSi + vb0, dv, DK);
-      __syncthreads();
-      f32x4 adv[NM];
-#pragma unroll
-      for (int m = 0; m < NM; ++m) adv[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-      for (int kb = 0; kb < DK / 32; ++kb) {
-        Frag<OpT> fb;
-        load_frag_c(fb, dST + (16 * w + r) * SLD + kb * 32);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          Frag<OpT> fa;
-          load_frag_c(fa, khp + (long)(16 * m + r) * DK + kb * 32);
-          mma(adv[m], fa, fb);
-        }
-      }
-#pragma unroll
-      for (int kb = 0; kb < C / 32; ++kb) {
-        Frag<OpT> fb;
-        load_frag_c(fb, dOT + (16 * w + r) * ALD + kb * 32);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          if (32 * kb + 31 >= 16 * m) {
-            Frag<OpT> fa;
-            load_frag_c(fa, ATs + (16 * m + r) * ALD + kb * 32);
-            mma(adv[m], fa, fb);
-          }
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * m + 4 * qd + e;
-          if (t < rows) dv_out[(tok0 + t) * dv + vb0 + 16 * w + r] = from_f32<Tin>(adv[m][e]);
-        }
-      __syncthreads();
-    }
-  }
-}
-
-// The two chunk-64 backward kernels as one launch: dq / dk / dlog_alpha workgroups and dv
+// The two backward chunk kernels as one launch: dq / dk / dlog_alpha workgroups and dv
 // workgroups interleaved in proportion (a dv workgroup needs neither the chunk totals nor
 // anything the dq / dk workgroups write), so that their memory phases overlap on each CU.
 template <typename Tin, typename OpT, bool SFRAG, bool SG, int C>
-__global__ __launch_bounds__(kThreads, C == 64 ? 3 : 1) void k_bwd_dqk_dv(
+__global__ __launch_bounds__(kThreads, C == 128 ? 1 : sizeof(OpT) == 2 ? 3 : 2) void k_bwd_dqk_dv(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dO, int gscalar, const OpT* __restrict__ S,
     const OpT* __restrict__ dS, Tin* __restrict__ dq, Tin* __restrict__ dk_out,
@@ -943,7 +646,7 @@ __global__ __launch_bounds__(kThreads, C == 64 ? 3 : 1) void k_bwd_dqk_dv(
     GateFn gf, Tin* __restrict__ dla, float* __restrict__ dla_part, const OpT* __restrict__ Kh,
     const OpT* __restrict__ A, Tin* __restrict__ dv_out, int T, int dk, int dv, int N,
     int n_dqk) {
-  __shared__ __attribute__((aligned(16))) char arena[dqk_lds_bytes(C)];
+  __shared__ __attribute__((aligned(16))) char arena[dqk_lds_bytes(C, sizeof(OpT))];
   const int L = xcd_logical(blockIdx.x, gridDim.x);
   const long total = gridDim.x;
   // Bresenham split: logical id L is a dq/dk workgroup when the count of them up to L grows
@@ -956,45 +659,30 @@ __global__ __launch_bounds__(kThreads, C == 64 ? 3 : 1) void k_bwd_dqk_dv(
 }
 
 // ---------------------------------------------------------------------------------
-template <typename Tin, typename OpT, int C, int DK>
+template <typename Tin, typename OpT, int C>
 static hipError_t launch_bwd_t2(const BwdArgs& a, hipStream_t s) {
-  if constexpr (sizeof(OpT) == 2) {
+  {
     const int n_dqk = (a.dk / 64) * a.N * a.BH, n_dv = (a.dv / 64) * a.N * a.BH;
     // scalar gates: the C x C decay-matrix form of the intra-chunk terms; fragment-order
-    // states come with chunk 64 only (the scans' 128-column tiles)
-    auto kern = a.gscalar ? (a.s_frag ? k_bwd_dqk_dv<Tin, OpT, C == 64, true, C> : k_bwd_dqk_dv<Tin, OpT, false, true, C>)
-                          : (a.s_frag ? k_bwd_dqk_dv<Tin, OpT, C == 64, false, C> : k_bwd_dqk_dv<Tin, OpT, false, false, C>);
+    // states come with bf16 and chunk 64 only (the scans' 128-column tiles)
+    constexpr bool kSF = sizeof(OpT) == 2 && C == 64;
+    auto kern = a.gscalar ? (a.s_frag ? k_bwd_dqk_dv<Tin, OpT, kSF, true, C> : k_bwd_dqk_dv<Tin, OpT, false, true, C>)
+                          : (a.s_frag ? k_bwd_dqk_dv<Tin, OpT, kSF, false, C> : k_bwd_dqk_dv<Tin, OpT, false, false, C>);
     hipLaunchKernelGGL(kern, dim3(n_dqk + n_dv), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO,
                        a.gscalar ? 1 : 0, (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq,
                        (Tin*)a.dk_out, a.tot, a.cT,
                        (const Tin*)a.la, a.gate, (Tin*)a.dla, a.dla_part, (const OpT*)a.Kh,
                        (const OpT*)a.A, (Tin*)a.dv_out, a.T, a.dk, a.dv, a.N, n_dqk);
-  } else {
-    hipLaunchKernelGGL((k_bwd_chunk<Tin, OpT, C, DK>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
-                       (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO, a.g,
-                       (const OpT*)a.A, (const OpT*)a.Kh, (const OpT*)a.S, (const OpT*)a.dS,
-                       (Tin*)a.dq, (Tin*)a.dk_out, (Tin*)a.dv_out, a.Dloc, a.T, a.dv, a.N);
   }
   return hipGetLastError();
 }
-template <typename Tin, typename OpT, int C>
-static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
-  switch (a.dk) {
-    case 64: return launch_bwd_t2<Tin, OpT, C, 64>(a, s);
-    case 128: return launch_bwd_t2<Tin, OpT, C, 128>(a, s);
-    case 192: return launch_bwd_t2<Tin, OpT, C, 192>(a, s);
-    default: return launch_bwd_t2<Tin, OpT, C, 256>(a, s);
-  }
-}
-
-bool bwd_split(int dtype, int C) { return dtype != 0 && (C == 64 || C == 128); }
 
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s) {
   if (a.BH == 0 || a.N == 0) return hipSuccess;
-  if (a.dtype == 0) return launch_bwd_t<float, float, 64>(a, s);
-  if (a.C == 64) return launch_bwd_t<bf16, bf16, 64>(a, s);
-  return launch_bwd_t<bf16, bf16, 128>(a, s);
+  if (a.dtype == 0) return a.C == 64 ? launch_bwd_t2<float, float, 64>(a, s) : hipErrorInvalidValue;
+  if (a.C == 64) return launch_bwd_t2<bf16, bf16, 64>(a, s);
+  return launch_bwd_t2<bf16, bf16, 128>(a, s);
 }
 
 

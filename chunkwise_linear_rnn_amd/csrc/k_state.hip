@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // (one set where the register budget of four workgroups per CU leaves no room, and on
   // the WT path, where the registers freed let the compiler keep several fragment reads
   // in flight: measured faster than two chunks ahead).
-  constexpr int DEPTH = WT ? 1 : (TV == 128 || (!CROSS && C == 64 && sizeof(OpT) == 2)) ? 2 : 1;
+  constexpr int DEPTH = WT ? 1 : (TV == 128 || (!CROSS && C == 64)) ? 2 : 1;
   // bf16 value-side tiles are staged chunk-swizzled (conflict-free transposing stores)
   constexpr bool SWZ = sizeof(OpT) == 2;
   using YT = ColTile<OpT, Tin, C, YLD, kThreads, SWZ>;

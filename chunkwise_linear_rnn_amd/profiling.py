@@ -28,14 +28,14 @@ import os
 import re
 import sys
 
-STAGE_KERNEL = {"bwd_chunk": "k_bwd_chunk", "bwd_dqk_dv": "k_bwd_dqk_dv",
+STAGE_KERNEL = {"bwd_dqk_dv": "k_bwd_dqk_dv",
                 "fwd_fused": "k_fwd_fused", "intra": "k_intra",
                 "state_scan_fwd": "k_state_scan", "state_scan_rev": "k_state_scan",
                 "state_scans": "k_state_scan", "seg_state": "k_state_scan",
                 "output": "k_output", "gate_cumsum": "k_gate_cumsum", "gate_grad": "k_gate_grad",
                 "gate_tot": "k_gate_tot", "gate_reduce": "k_gate_reduce", "state_dot": "k_state_dot",
                 "state_scan": "k_state_scan", "intra_fwd": "k_intra", "intra_bwd": "k_intra"}
-STAGE_SOURCE = {"bwd_chunk": "k_bwd.hip", "bwd_dqk_dv": "k_bwd.hip",
+STAGE_SOURCE = {"bwd_dqk_dv": "k_bwd.hip",
                 "fwd_fused": "k_fwd.hip", "intra": "k_intra.hip",
                 "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip",
                 "state_scans": "k_state.hip", "seg_state": "k_state.hip",
@@ -128,7 +128,7 @@ def counters(fetch_csv, write_csv, copy_bytes, stage, workload, command, root):
             "traffic_bytes_per_launch": fetch + write, "launches": len(kf), "command": command}
 
 
-MFMA_STAGES = ("fwd_fused", "bwd_dqk_dv", "state_scans", "seg_state", "bwd_chunk", "output",
+MFMA_STAGES = ("fwd_fused", "bwd_dqk_dv", "state_scans", "seg_state", "output",
                "state_scan", "intra_fwd", "intra_bwd")
 SIMDS, XCDS, CLOCK_HZ, PEAK_BF16 = 1024, 8, 2.4e9, 2.5e15
 

@@ -167,7 +167,7 @@ def test_gate_shape_field(native):
     assert native.trace_stages(sc, native.PASS_BWD)[-1] == "gate_reduce"
     assert "gate_reduce" not in native.trace_stages(per_key, native.PASS_BWD)
     f32 = D(1, 2, 100, 64, 64, 64, 16, native.F32, native.RECOMPUTE, gate_shape=native.GATE_SCALAR)
-    assert native.trace_stages(f32, native.PASS_BWD)[-2:] == ["gate_grad", "gate_reduce"]
+    assert native.trace_stages(f32, native.PASS_BWD)[-2:] == ["bwd_dqk_dv", "gate_reduce"]
 
 
 def test_gsa_descriptor_validation(native):
