@@ -136,18 +136,46 @@ __global__ __launch_bounds__(kThreads, 3) void k_vg_out(const float* __restrict_
   const float* kb = k + rowbase * dk;
   const float* Sb = S1 + ((long)bh * N + i) * m * dk;
 
-  chunk_qk(XA, X0, X1, qb, kb, dk, rows);
+  // A = tril(Q K^T) and the first 64 slots' Q S1^T in one pass over dk (each q block
+  // staged once; XA holds the S1 block until A is written to it)
+  f32x4 o0[4];
+  zero4(o0);
+  {
+    f32x4 acc[4];
+    zero4(acc);
+    for (int d0 = 0; d0 < dk; d0 += kC) {
+      stage_rows(X0, qb + d0, dk, rows);
+      stage_rows(X1, kb + d0, dk, rows);
+      stage_rows(XA, Sb + d0, dk, kC);
+      __syncthreads();
+      mm_rows(acc, X0, X1, wv);
+      mm_rows(o0, X0, XA, wv);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = rho + 4 * qd + e, u = 16 * j + r;
+        XA[t * kFL + u] = u <= t ? acc[j][e] : 0.f;
+      }
+  }
 
   for (int j0 = 0; j0 < m; j0 += kC) {
     // inter-chunk part: Q S1^T for 64 slots
     f32x4 o[4];
-    zero4(o);
-    for (int d0 = 0; d0 < dk; d0 += kC) {
-      stage_rows(X0, qb + d0, dk, rows);
-      stage_rows(X1, Sb + (long)j0 * dk + d0, dk, kC);
-      __syncthreads();
-      mm_rows(o, X0, X1, wv);
-      __syncthreads();
+    if (j0 == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = o0[j];
+    } else {
+      zero4(o);
+      for (int d0 = 0; d0 < dk; d0 += kC) {
+        stage_rows(X0, qb + d0, dk, rows);
+        stage_rows(X1, Sb + (long)j0 * dk + d0, dk, kC);
+        __syncthreads();
+        mm_rows(o, X0, X1, wv);
+        __syncthreads();
+      }
     }
     // w [u][j] (zero past `rows`) and g [t][j] (flat past `rows`) of the block
     stage_rows(X0, w + rowbase * m + j0, m, rows);
