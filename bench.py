@@ -92,9 +92,17 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
         return tokp * dk * e + tok * dv * e + st + BH * dk * dv * 4, tok * 2 * dk * dv
     if stage == "output":
         return tokp * dk * e + BH * N * C * C * e + st + 2 * tok * dv * e, tok * (2 * dk * dv + C * dv)
-    if stage == "seg_state":   # the state at the midpoint chunk: first half of Kh^T and v
-        h = BH * (N // 2) * C
-        return h * dk * e + h * dv * e + BH * (N // 2) * dk * 4 + BH * dk * dv * 4, h * 2 * dk * dv
+    if stage == "seg_state":
+        # the states at the segment starts: Kh^T and v of every segment but the last, the
+        # end state of each scanned segment, and (more than two segments) their chaining
+        P = fused_segments(e, C, N, BH, dv)
+        ns = (P - 1) * N // P
+        h = BH * ns * C
+        st4 = BH * dk * dv * 4
+        byt = h * dk * e + h * dv * e + BH * ns * dk * 4 + (P - 1) * st4
+        if P > 2:
+            byt += 2 * (P - 2) * st4
+        return byt, h * 2 * dk * dv
     if stage == "fwd_fused":
         byt = 2 * tokp * dk * e + BH * N * C * C * e + 2 * tok * dv * e + BH * dk * dv * 4
         return byt, tok * (4 * dk * dv + C * dv)
@@ -113,6 +121,17 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
     if stage == "state_dot":
         return 2 * BH * dk * dv * 4, 2 * BH * dk * dv
     return 0, 0
+
+
+def fused_segments(e, C, N, BH, dv):
+    """Sequence segments of the non-materialized forward, as the library picks them: about
+    256 workgroups (one per CU) for small B*H*dv/64, at most 8, at least two chunks each;
+    none for fp32 or fewer than 4 chunks."""
+    if e == 4 or N < 4:
+        return 1
+    tiles = BH * (dv // 64)
+    P = 2 if tiles >= 128 else 256 // tiles
+    return max(2, min(P, 8, N // 2))
 
 
 def path_flops(B, H, T, dk, dv, C, fwd_only=False):

@@ -70,8 +70,8 @@ Plan plan_of(const gla_desc_t* d, int pass) {
     p.KhT = take(opB);
     p.eg = take(egB);
     if (mat) p.st = take(stB);
-    if (!mat && gla::fused_split(x.dtype, (int)x.C, (int)x.N) > 0)
-      p.smid = take((size_t)x.BH * x.dk * x.dv * 4);
+    const int nseg = mat ? 1 : gla::fused_segments(x.dtype, (int)x.C, (int)x.N, (int)x.BH, (int)x.dv);
+    if (nseg > 1) p.smid = take((size_t)(nseg - 1) * x.BH * x.dk * x.dv * 4);
   } else if (pass == GLA_PASS_BWD) {
     // the scans' transposed operands are kept in fp32 (split into two bf16 halves)
     const size_t op32 = rowsP * x.dk * 4;
@@ -324,17 +324,27 @@ gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void
   fa.dtype = x.dtype; fa.C = (int)x.C; fa.BH = (int)x.BH; fa.T = (int)x.T; fa.dk = (int)x.dk;
   fa.dv = (int)x.dv; fa.N = (int)x.N; fa.Qh = w + p.Qh; fa.KhT = w + p.KhT; fa.A = w + p.A;
   fa.v = v; fa.eg = (const float*)(w + p.eg); fa.S0 = S0; fa.o = o; fa.S_T = S_T;
-  fa.split = gla::fused_split(x.dtype, (int)x.C, (int)x.N);
-  // with a split, the state before the midpoint chunk comes first: a state scan over the
-  // first half of the chunks (no per-chunk states written)
+  fa.nseg = gla::fused_segments(x.dtype, (int)x.C, (int)x.N, (int)x.BH, (int)x.dv);
+  // with a split, the states at the segment starts come first (no per-chunk states
+  // written): two segments, a state scan over the first half; more, every segment but the
+  // last scanned from zero in one launch (the first from S0), then chained
   if ((rs = tr.mark()) != GLA_OK) return rs;
-  if (fa.split > 0) {
+  if (fa.nseg > 1) {
     gla::ScanArgs sa{};
     sa.dtype = x.dtype; sa.C = (int)x.C; sa.BH = (int)x.BH; sa.T = (int)x.T; sa.dk = (int)x.dk;
-    sa.dv = (int)x.dv; sa.N = (int)x.N; sa.reverse = false; sa.store = 0; sa.nsteps = fa.split;
+    sa.dv = (int)x.dv; sa.N = (int)x.N; sa.reverse = false; sa.store = 0;
+    if (fa.nseg == 2) {
+      sa.nsteps = (int)x.N / 2;
+    } else {
+      sa.nseg = fa.nseg - 1; sa.seg_p = fa.nseg;
+    }
     sa.XT = w + p.KhT; sa.Y = v; sa.eg = (const float*)(w + p.eg); sa.S_in = S0;
     sa.S_out = (float*)(w + p.smid);
     if ((rs = dev(gla::launch_state_scan(sa, s))) != GLA_OK) return rs;
+    if ((rs = dev(gla::launch_seg_combine((float*)(w + p.smid), (const float*)(w + p.eg),
+                                          (int)x.BH, (int)x.dk, (int)x.dv, (int)x.N, fa.nseg,
+                                          s))) != GLA_OK)
+      return rs;
     fa.S_mid = (const float*)(w + p.smid);
   }
   if ((rs = tr.mark()) != GLA_OK) return rs;

@@ -82,6 +82,11 @@ struct ScanArgs {
                          // order (see the scan kernel), for the backward chunk kernel
   float* S_out;          // [BH][dk][dv] or NULL
   int nsteps;            // chunks to walk (0: all N); the layout strides still use N
+  // sequence segments (forward, store 0, no cross term): nseg > 1 walks segments
+  // 0 .. nseg - 1 of the split into seg_p parts (chunks [s N / seg_p, (s + 1) N / seg_p))
+  // in one launch, each from zero except the first (from S_in), each end state to
+  // S_out + s * BH * dk * dv
+  int nseg, seg_p;
 };
 hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s);
 // Two scans of the same shape and kind (the backward's forward and reverse scans) in one
@@ -89,6 +94,11 @@ hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_state_scan2(const ScanArgs& a, const ScanArgs& b, hipStream_t s);
 // Value columns per scan workgroup (the cross-term tiles come in dv / this many).
 int scan_tile_v(const ScanArgs& a);
+// Chains the segment end states of a segmented scan into the states at the segment
+// starts: S[s] <- diag(prod of exp(gamma) over segment s) S[s - 1] + S[s], s = 1 .. P - 2,
+// in place on S [P - 1][BH][dk][dv] (slot 0 already the state at the first boundary).
+hipError_t launch_seg_combine(float* S, const float* eg, int BH, int dk, int dv, int N, int P,
+                              hipStream_t s);
 // Per-direction kernel arguments of the scan kernel.
 struct ScanDir {
   const void *XT, *Y, *X2T, *Y2;
@@ -114,14 +124,17 @@ struct FusedArgs {
   const float* S0;
   void* o;
   float* S_T;
-  // sequence split: chunks [0, split) and [split, N) walk in parallel, the second from
-  // S_mid = the state before chunk `split` (0: one walk over all chunks)
-  int split;
+  // sequence split: nseg segments, chunks [s N / nseg, (s + 1) N / nseg), walked in
+  // parallel, segment s > 0 from S_mid + (s - 1) * BH * dk * dv (the state at its first
+  // chunk); nseg = 1: one walk over all chunks
+  int nseg;
   const float* S_mid;
 };
-// The split point of the fused forward for a shape (0: no split).  With a split, the
-// state before that chunk must be formed first (a state scan over chunks [0, split)).
-int fused_split(int dtype, int C, int N);
+// The number of sequence segments of the fused forward for a shape (1: no split): enough
+// for about 256 workgroups (one per CU) when B*H*dv/64 is small, at most 8, and at least
+// two chunks per segment.  With a split, the states at the segment starts are formed first
+// (a segmented state scan and, for more than two segments, launch_seg_combine).
+int fused_segments(int dtype, int C, int N, int BH, int dv);
 hipError_t launch_fwd_fused(const FusedArgs& a, hipStream_t s);
 
 struct BwdArgs {

@@ -86,7 +86,7 @@ template <typename Tin, typename OpT, int C, int DK>
 __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
     const OpT* __restrict__ Qh, const OpT* __restrict__ KhT, const OpT* __restrict__ A,
     const float* __restrict__ eg, const Tin* __restrict__ V, const float* __restrict__ S0,
-    Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N, int split,
+    Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N, int nseg,
     const float* __restrict__ S_mid) {
   constexpr int NT = kFusedThreads, TV = 64, NM = C / 16, KH = DK / 2, NP = KH / 16;
   // Kh^T arrives in MFMA fragment order (lane 16 q + r of fragment (16-row block, 32-token
@@ -103,13 +103,16 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
   __shared__ __attribute__((aligned(16))) float red[C * RLD];     // partial O of the upper dk half
   __shared__ float egs[DK];
   // 1-D grid, XCD-aware: the dv tiles of one bh share every Qh / Kh^T / A tile.  With a
-  // sequence split the second half of the logical ids walks chunks [split, N) from S_mid.
-  const int nvt = dv / TV, nseg = split > 0 ? 2 : 1, per_seg = (int)gridDim.x / nseg;
+  // sequence split into nseg segments, the s-th part of the logical ids walks chunks
+  // [s N / nseg, (s + 1) N / nseg) from the state at its first chunk (S0, or slot s - 1 of
+  // S_mid).
+  const int nvt = dv / TV, per_seg = (int)gridDim.x / nseg;
   const int lg = xcd_logical(blockIdx.x, gridDim.x);
   const int seg = lg / per_seg, lt = lg % per_seg;
   const int v0 = (lt % nvt) * TV, bh = lt / nvt;
-  const int ib = seg == 1 ? split : 0, ie = (nseg == 2 && seg == 0) ? split : N;
-  const float* __restrict__ Sinit = seg == 1 ? S_mid : S0;
+  const int ib = seg * N / nseg, ie = (seg + 1) * N / nseg;
+  const float* __restrict__ Sinit =
+      seg == 0 ? S0 : S_mid + (long)(seg - 1) * (per_seg / nvt) * DK * dv;
   // wave w: value columns 16 (w % 4) .. +15, state rows kh*KH .. kh*KH + KH-1 (kh = w / 4)
   const int w = threadIdx.x >> 6, vc = w & 3, kh = w >> 2;
   const int l = lane_id(), r = l & 15, qd = l >> 4;
@@ -253,7 +256,7 @@ template <typename Tin, int DK>
 __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_c128(
     const bf16* __restrict__ Qh, const bf16* __restrict__ KhT, const bf16* __restrict__ A,
     const float* __restrict__ eg, const Tin* __restrict__ V, const float* __restrict__ S0,
-    Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N, int split,
+    Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N, int nseg,
     const float* __restrict__ S_mid) {
   using OpT = bf16;
   constexpr int C = 128, H = 64;   // chunk, half-step rows
@@ -266,12 +269,13 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_c128(
   __shared__ __attribute__((aligned(16))) Tin os_[2][H * OLD];    // O of a half, double-buffered
   __shared__ __attribute__((aligned(16))) float red[H * RLD];
   __shared__ float egs[DK];
-  const int nvt = dv / TV, nseg = split > 0 ? 2 : 1, per_seg = (int)gridDim.x / nseg;
+  const int nvt = dv / TV, per_seg = (int)gridDim.x / nseg;
   const int lg = xcd_logical(blockIdx.x, gridDim.x);
   const int seg = lg / per_seg, lt = lg % per_seg;
   const int v0 = (lt % nvt) * TV, bh = lt / nvt;
-  const int ib = seg == 1 ? split : 0, ie = (nseg == 2 && seg == 0) ? split : N;
-  const float* __restrict__ Sinit = seg == 1 ? S_mid : S0;
+  const int ib = seg * N / nseg, ie = (seg + 1) * N / nseg;
+  const float* __restrict__ Sinit =
+      seg == 0 ? S0 : S_mid + (long)(seg - 1) * (per_seg / nvt) * DK * dv;
   const int w = threadIdx.x >> 6, vc = w & 3, kh = w >> 2;
   const int l = lane_id(), r = l & 15, qd = l >> 4;
   const int c16 = 16 * vc + r, col = v0 + c16, k0 = kh * KH;
@@ -561,24 +565,31 @@ hipError_t launch_output(const OutArgs& a, hipStream_t s) {
   return launch_output_t<bf16, bf16, 128>(a, s);
 }
 
-int fused_split(int dtype, int C, int N) { return (dtype != 0 && N >= 4) ? N / 2 : 0; }
+int fused_segments(int dtype, int C, int N, int BH, int dv) {
+  if (dtype == 0 || N < 4) return 1;
+  const long tiles = (long)BH * (dv / 64);   // workgroups per segment
+  int P = tiles >= 128 ? 2 : (int)(256 / tiles);
+  P = P > 8 ? 8 : P;
+  P = P > N / 2 ? N / 2 : P;
+  return P < 2 ? 2 : P;
+}
 
 template <typename Tin, typename OpT, int C, int DK>
 static hipError_t launch_fused_t2(const FusedArgs& a, hipStream_t s) {
   if constexpr (C == 128 && sizeof(OpT) == 2) {
-    const int split = a.S_mid ? a.split : 0;
-    dim3 grid((a.dv / 64) * a.BH * (split > 0 ? 2 : 1));
+    const int nseg = a.S_mid && a.nseg > 1 ? a.nseg : 1;
+    dim3 grid((a.dv / 64) * a.BH * nseg);
     hipLaunchKernelGGL((k_fwd_fused_c128<Tin, DK>), grid, dim3(kFusedThreads), 0, s,
                        (const bf16*)a.Qh, (const bf16*)a.KhT, (const bf16*)a.A, a.eg,
-                       (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N, split, a.S_mid);
+                       (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N, nseg, a.S_mid);
     return hipGetLastError();
   }
   if constexpr (C == 64 && sizeof(OpT) == 2) {
-    const int split = a.S_mid ? a.split : 0;
-    dim3 grid((a.dv / 64) * a.BH * (split > 0 ? 2 : 1));
+    const int nseg = a.S_mid && a.nseg > 1 ? a.nseg : 1;
+    dim3 grid((a.dv / 64) * a.BH * nseg);
     hipLaunchKernelGGL((k_fwd_fused_staged<Tin, OpT, C, DK>), grid, dim3(kFusedThreads), 0, s,
                        (const OpT*)a.Qh, (const OpT*)a.KhT, (const OpT*)a.A, a.eg,
-                       (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N, split, a.S_mid);
+                       (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N, nseg, a.S_mid);
     return hipGetLastError();
   }
   dim3 grid((a.dv / 64) * a.BH);

@@ -66,7 +66,8 @@ struct XRegs {
 template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS, int TV>
 __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, ScanDir d1, int ndir,
                                                             const float* __restrict__ eg, int T,
-                                                            int dk, int dv, int N, int nsteps) {
+                                                            int dk, int dv, int N, int nsteps,
+                                                            int nseg, int segp) {
   // TV value columns per workgroup: NJ accumulator tiles per wave, NY 64-column
   // value-side tiles per operand
   constexpr int NJ = TV / 16, NY = TV / 64;
@@ -97,14 +98,22 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   int lt = xcd_logical(blockIdx.x, gridDim.x);
   const bool second = lt >= tiles;
   if (second) lt -= tiles;
+  // nseg > 1 (forward, no stores): segment sg of the sequence split into segp parts,
+  // chunks [sg N / segp, (sg + 1) N / segp), from S_in for the first and from zero for the
+  // others; its end state goes to S_out + sg * BH * dk * dv
+  const int base = tiles / nseg, sg = lt / base;
+  lt -= sg * base;
+  const int i0 = nseg > 1 ? sg * N / segp : 0;
+  const int nst = nseg > 1 ? (sg + 1) * N / segp - i0 : nsteps;
   const OpT* __restrict__ XT = (const OpT*)(second ? d1.XT : d0.XT);
   const Tin* __restrict__ Y = (const Tin*)(second ? d1.Y : d0.Y);
   const OpT* __restrict__ X2T = (const OpT*)(second ? d1.X2T : d0.X2T);
   const Tin* __restrict__ Y2 = (const Tin*)(second ? d1.Y2 : d0.Y2);
   float* __restrict__ cross = second ? d1.cross : d0.cross;
-  const float* __restrict__ S_in = second ? d1.S_in : d0.S_in;
+  const float* __restrict__ S_in = sg > 0 ? nullptr : second ? d1.S_in : d0.S_in;
   void* __restrict__ states = second ? d1.states : d0.states;
   float* __restrict__ S_out = second ? d1.S_out : d0.S_out;
+  if (S_out) S_out += (long)sg * (base / (nvt * nkt)) * dk * dv;
   const int reverse = second ? d1.reverse : d0.reverse;
   const int frag_states = second ? d1.frag_states : d0.frag_states;
   const int vt = lt % nvt, kt = (lt / nvt) % nkt, bh = lt / (nvt * nkt);
@@ -123,8 +132,8 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // chunk of a step; steps past the end map to the last one (refetched, never used), so
   // that every prefetch is unconditional and the compiler's wait counts stay exact
   auto chunk_of = [&](int step) {
-    const int sc = min(step, nsteps - 1);
-    return reverse ? N - 1 - sc : sc;
+    const int sc = min(step, nst - 1);
+    return reverse ? N - 1 - sc : i0 + sc;
   };
   // the decays of steps [sb, sb + EB) into LDS: read there at each step, they put no
   // global-memory round trip on the chain of dependent steps
@@ -135,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
       egs[idx] = eg[((long)bh * N + chunk_of(sb + (idx >> 6))) * dk + k0 + (idx & 63)];
     }
   };
-  if (nsteps > 0) stage_eg(0);
+  if (nst > 0) stage_eg(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
 
@@ -186,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
       }
     }
   };
-  if (nsteps > 0) {
+  if (nst > 0) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int i0 = chunk_of(d);
@@ -322,12 +331,12 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // with a barrier, so the previous block's decays are no longer read when restaged
   static_assert(EB % 2 == 0 && EB * 64 % kThreads == 0, "decay staging");
   int step = 0;
-  for (int sb = 0; sb < nsteps; sb += EB) {
+  for (int sb = 0; sb < nst; sb += EB) {
     if (sb > 0) {
       stage_eg(sb);
       __syncthreads();
     }
-    const int se = min(sb + EB, nsteps);
+    const int se = min(sb + EB, nst);
     if constexpr (DEPTH == 2) {
       for (; step + 1 < se; step += 2) {
         body(step, sets[0]);
@@ -355,11 +364,11 @@ static void launch_scan_k(const ScanArgs& a, const ScanArgs* b, hipStream_t s) {
     d.frag_states = x.frag_states ? 1 : 0;
     return d;
   };
-  const int ndir = b ? 2 : 1;
-  dim3 grid(ndir * (a.dv / TV) * (a.dk / 64) * a.BH);
+  const int ndir = b ? 2 : 1, nseg = a.nseg > 1 ? a.nseg : 1;
+  dim3 grid(ndir * nseg * (a.dv / TV) * (a.dk / 64) * a.BH);
   hipLaunchKernelGGL((k_state_scan<Tin, OpT, SPLIT, C, STORE, CROSS, TV>), grid, dim3(kThreads), 0,
                      s, dir(a), dir(b ? *b : a), ndir, a.eg, a.T, a.dk, a.dv, a.N,
-                     a.nsteps > 0 && a.nsteps < a.N ? a.nsteps : a.N);
+                     a.nsteps > 0 && a.nsteps < a.N ? a.nsteps : a.N, nseg, a.seg_p);
 }
 
 int scan_tile_v(const ScanArgs& a) {
@@ -399,6 +408,10 @@ static hipError_t launch_scans(const ScanArgs& a, const ScanArgs* b, hipStream_t
                               scan_tile_v(x) == 128);
   };
   if (!frag_ok(a) || (b && !frag_ok(*b))) return hipErrorInvalidValue;
+  // sequence segments: one forward scan without stores or cross terms, nseg < seg_p <= N
+  if (a.nseg > 1 && (b || a.store != 0 || a.cross || a.reverse || a.seg_p <= a.nseg ||
+                     a.seg_p > a.N || !a.S_out))
+    return hipErrorInvalidValue;
   if (b && (b->dtype != a.dtype || b->C != a.C || b->BH != a.BH || b->T != a.T ||
             b->dk != a.dk || b->dv != a.dv || b->N != a.N || b->xt_f32 != a.xt_f32 ||
             b->store != a.store || (b->cross != nullptr) != (a.cross != nullptr) || b->eg != a.eg ||
@@ -414,6 +427,54 @@ static hipError_t launch_scans(const ScanArgs& a, const ScanArgs* b, hipStream_t
 }
 
 hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s) { return launch_scans(a, nullptr, s); }
+
+// Segment end states -> states at the segment starts (see launch_seg_combine): one
+// workgroup per (64 state rows, 64 columns, bh).  The decay product of each (segment, row)
+// is formed by four threads over every fourth chunk (independent loads), joined through
+// LDS; then each thread loads all segment slots of its 16 elements at once and chains them.
+__global__ __launch_bounds__(kThreads) void k_seg_combine(float* __restrict__ S,
+                                                          const float* __restrict__ eg, int BH,
+                                                          int dk, int dv, int N, int P) {
+  __shared__ float Gp[4][8][64];
+  const int c0 = 64 * blockIdx.x, k0 = 64 * blockIdx.y, bh = blockIdx.z;
+  const int row = threadIdx.x & 63, part = threadIdx.x >> 6;
+  for (int sg = 1; sg < P - 1; ++sg) {
+    const int ia = sg * N / P, ib = (sg + 1) * N / P;
+    float g = 1.f;
+#pragma unroll 4
+    for (int i = ia + part; i < ib; i += 4) g *= eg[((long)bh * N + i) * dk + k0 + row];
+    Gp[part][sg][row] = g;
+  }
+  __syncthreads();
+  const long slot = (long)BH * dk * dv;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = threadIdx.x + kThreads * u, kr = idx >> 4, c = (idx & 15) * 4;
+    const long off = ((long)bh * dk + k0 + kr) * dv + c0 + c;
+    f32x4 x[8];
+#pragma unroll
+    for (int sg = 0; sg < 8; ++sg)
+      if (sg < P - 1) x[sg] = *reinterpret_cast<const f32x4*>(S + sg * slot + off);
+#pragma unroll
+    for (int sg = 1; sg < 8; ++sg) {
+      if (sg < P - 1) {
+        const float gs = (Gp[0][sg][kr] * Gp[1][sg][kr]) * (Gp[2][sg][kr] * Gp[3][sg][kr]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[sg][e] = gs * x[sg - 1][e] + x[sg][e];
+        *reinterpret_cast<f32x4*>(S + sg * slot + off) = x[sg];
+      }
+    }
+  }
+}
+
+hipError_t launch_seg_combine(float* S, const float* eg, int BH, int dk, int dv, int N, int P,
+                              hipStream_t s) {
+  if (P <= 2 || BH == 0) return hipSuccess;
+  if (P > 9 || dk % 64 != 0 || dv % 64 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_seg_combine, dim3(dv / 64, dk / 64, BH), dim3(kThreads), 0, s, S, eg, BH,
+                     dk, dv, N, P);
+  return hipGetLastError();
+}
 hipError_t launch_state_scan2(const ScanArgs& a, const ScanArgs& b, hipStream_t s) {
   return launch_scans(a, &b, s);
 }

@@ -40,6 +40,9 @@ def test_every_traced_stage_has_a_work_model(bench, native, mode, dtype, chunk):
         for with_dst in (False, True) if tag == "bwd" else (False,):
             for name in native.trace_stages(d, pass_, with_dst):
                 byt, fl = bench.stage_work(name, tag, mode, 4, 4, 2048, 256, 512, chunk, e)
+                if name == "seg_state" and dtype == "f32":
+                    assert (byt, fl) == (0, 0)   # no sequence split in fp32: nothing launched
+                    continue
                 assert byt > 0, (tag, name)
                 assert fl >= 0, (tag, name)
 

@@ -174,9 +174,18 @@ def test_long_sequence_chained(gla):
     from oracle.compare import normwise
     a, b = host(o1), host(o2)
     nw = normwise(b, a)
-    say(f"    chained vs single: normwise={nw:.3e} bitwise={np.array_equal(a, b)}")
-    assert nw <= 1e-6
-    assert normwise(host(S), host(S1)) <= 1e-6
+    nws = normwise(host(S), host(S1))
+    say(f"    chained vs single: o normwise={nw:.3e} bitwise={np.array_equal(a, b)}, "
+        f"S_T normwise={nws:.3e}")
+    # The one call splits its 320 chunks into 8 segments and the chained calls their 32
+    # into 8 each: the states at the segment starts are formed with a different fp32
+    # association (segment end states chained with products of chunk decays) than a
+    # sequential walk, so the two runs agree to fp32 rounding rather than bit for bit.
+    # Over a few hundred chunk steps that is well under 1e-5 on the fp32 state; o, rounded
+    # to bf16, then differs by one bf16 unit (2^-8 relative) only where its fp32 value lies
+    # within that rounding of a rounding boundary, a small fraction of elements.
+    assert nws <= 1e-5
+    assert nw <= 2e-4
     heads = _all_heads(cfg)
     say(f"    oracle on all {len(heads)} heads")
     ref = oracle_heads_pool(d, heads, bwd=False)
