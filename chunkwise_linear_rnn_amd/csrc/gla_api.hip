@@ -44,7 +44,8 @@ Dims dims_of(const gla_desc_t* d) {
 // Workspace carving.  Every region is 256-byte aligned.
 struct Plan {
   size_t g = 0, A = 0, Qh = 0, QhT = 0, Kh = 0, KhT = 0, eg = 0, st = 0, dst = 0, ST = 0,
-         cT = 0, Dloc = 0, crossF = 0, crossR = 0, carry = 0, smid = 0, dpart = 0, total = 0;
+         cT = 0, crossF = 0, crossR = 0, carry = 0, smid = 0, segdec = 0, dpart = 0,
+         total = 0;
 };
 
 Plan plan_of(const gla_desc_t* d, int pass) {
@@ -72,6 +73,7 @@ Plan plan_of(const gla_desc_t* d, int pass) {
     if (mat) p.st = take(stB);
     const int nseg = mat ? 1 : gla::fused_segments(x.dtype, (int)x.C, (int)x.N, (int)x.BH, (int)x.dv);
     if (nseg > 1) p.smid = take((size_t)(nseg - 1) * x.BH * x.dk * x.dv * 4);
+    if (nseg > 2) p.segdec = take((size_t)(nseg - 1) * x.BH * x.dk * 4);
   } else if (pass == GLA_PASS_BWD) {
     // the scans' transposed operands are kept in fp32 (split into two bf16 halves)
     const size_t op32 = rowsP * x.dk * 4;
@@ -336,14 +338,13 @@ gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void
     if (fa.nseg == 2) {
       sa.nsteps = (int)x.N / 2;
     } else {
-      sa.nseg = fa.nseg - 1; sa.seg_p = fa.nseg;
+      sa.nseg = fa.nseg - 1; sa.seg_p = fa.nseg; sa.seg_decay = (float*)(w + p.segdec);
     }
     sa.XT = w + p.KhT; sa.Y = v; sa.eg = (const float*)(w + p.eg); sa.S_in = S0;
     sa.S_out = (float*)(w + p.smid);
     if ((rs = dev(gla::launch_state_scan(sa, s))) != GLA_OK) return rs;
-    if ((rs = dev(gla::launch_seg_combine((float*)(w + p.smid), (const float*)(w + p.eg),
-                                          (int)x.BH, (int)x.dk, (int)x.dv, (int)x.N, fa.nseg,
-                                          s))) != GLA_OK)
+    if ((rs = dev(gla::launch_seg_combine((float*)(w + p.smid), (const float*)(w + p.segdec),
+                                          (int)x.BH, (int)x.dk, (int)x.dv, fa.nseg, s))) != GLA_OK)
       return rs;
     fa.S_mid = (const float*)(w + p.smid);
   }

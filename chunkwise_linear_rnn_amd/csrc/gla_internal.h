@@ -85,8 +85,10 @@ struct ScanArgs {
   // sequence segments (forward, store 0, no cross term): nseg > 1 walks segments
   // 0 .. nseg - 1 of the split into seg_p parts (chunks [s N / seg_p, (s + 1) N / seg_p))
   // in one launch, each from zero except the first (from S_in), each end state to
-  // S_out + s * BH * dk * dv
+  // S_out + s * BH * dk * dv, and each segment's total decay (product of its chunks'
+  // exp(gamma)) per row to seg_decay [nseg][BH][dk]
   int nseg, seg_p;
+  float* seg_decay;
 };
 hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s);
 // Two scans of the same shape and kind (the backward's forward and reverse scans) in one
@@ -95,9 +97,10 @@ hipError_t launch_state_scan2(const ScanArgs& a, const ScanArgs& b, hipStream_t 
 // Value columns per scan workgroup (the cross-term tiles come in dv / this many).
 int scan_tile_v(const ScanArgs& a);
 // Chains the segment end states of a segmented scan into the states at the segment
-// starts: S[s] <- diag(prod of exp(gamma) over segment s) S[s - 1] + S[s], s = 1 .. P - 2,
-// in place on S [P - 1][BH][dk][dv] (slot 0 already the state at the first boundary).
-hipError_t launch_seg_combine(float* S, const float* eg, int BH, int dk, int dv, int N, int P,
+// starts: S[s] <- diag(dec[s]) S[s - 1] + S[s], s = 1 .. P - 2, in place on
+// S [P - 1][BH][dk][dv] (slot 0 already the state at the first boundary), dec the
+// segments' decay products [P - 1][BH][dk] from the same scan.
+hipError_t launch_seg_combine(float* S, const float* dec, int BH, int dk, int dv, int P,
                               hipStream_t s);
 // Per-direction kernel arguments of the scan kernel.
 struct ScanDir {

@@ -67,7 +67,8 @@ template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS, 
 __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, ScanDir d1, int ndir,
                                                             const float* __restrict__ eg, int T,
                                                             int dk, int dv, int N, int nsteps,
-                                                            int nseg, int segp) {
+                                                            int nseg, int segp,
+                                                            float* __restrict__ segdec) {
   // TV value columns per workgroup: NJ accumulator tiles per wave, NY 64-column
   // value-side tiles per operand
   constexpr int NJ = TV / 16, NY = TV / 64;
@@ -210,9 +211,11 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // prefetch would make the next step wait for the write round trip.
   float part_prev = 0.f;   // cross term of the previous chunk for row krow
   int i_prev = -1;
+  float dprod = 1.f;   // product of the walked chunks' decays of row krow (segmented scan)
   auto body = [&](int step, Set& st) {
     const int i = chunk_of(step), ipre = chunk_of(step + DEPTH);
     const float egr = egs[(step % EB) * 64 + 16 * w + r];   // exp(gamma) of row krow
+    dprod *= egr;
     if constexpr (WT) {
       ywt.store((wsec ? y2s : ys) + 64 * wh * YLD);
     } else {
@@ -353,6 +356,9 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
     for (int j = 0; j < NJ; ++j)
       *reinterpret_cast<f32x4*>(S_out + ((long)bh * dk + krow) * dv + v0 + 16 * j + 4 * qd) = acc[j];
   }
+  // segmented scan: the segment's total decay per row, [nseg][BH][dk]
+  if (segdec && vt == 0 && qd == 0)
+    segdec[((long)sg * (base / (nvt * nkt)) + bh) * dk + krow] = dprod;
 }
 
 template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS, int TV>
@@ -368,7 +374,8 @@ static void launch_scan_k(const ScanArgs& a, const ScanArgs* b, hipStream_t s) {
   dim3 grid(ndir * nseg * (a.dv / TV) * (a.dk / 64) * a.BH);
   hipLaunchKernelGGL((k_state_scan<Tin, OpT, SPLIT, C, STORE, CROSS, TV>), grid, dim3(kThreads), 0,
                      s, dir(a), dir(b ? *b : a), ndir, a.eg, a.T, a.dk, a.dv, a.N,
-                     a.nsteps > 0 && a.nsteps < a.N ? a.nsteps : a.N, nseg, a.seg_p);
+                     a.nsteps > 0 && a.nsteps < a.N ? a.nsteps : a.N, nseg, a.seg_p,
+                     nseg > 1 ? a.seg_decay : nullptr);
 }
 
 int scan_tile_v(const ScanArgs& a) {
@@ -410,7 +417,7 @@ static hipError_t launch_scans(const ScanArgs& a, const ScanArgs* b, hipStream_t
   if (!frag_ok(a) || (b && !frag_ok(*b))) return hipErrorInvalidValue;
   // sequence segments: one forward scan without stores or cross terms, nseg < seg_p <= N
   if (a.nseg > 1 && (b || a.store != 0 || a.cross || a.reverse || a.seg_p <= a.nseg ||
-                     a.seg_p > a.N || !a.S_out))
+                     a.seg_p > a.N || !a.S_out || !a.seg_decay))
     return hipErrorInvalidValue;
   if (b && (b->dtype != a.dtype || b->C != a.C || b->BH != a.BH || b->T != a.T ||
             b->dk != a.dk || b->dv != a.dv || b->N != a.N || b->xt_f32 != a.xt_f32 ||
@@ -429,50 +436,43 @@ static hipError_t launch_scans(const ScanArgs& a, const ScanArgs* b, hipStream_t
 hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s) { return launch_scans(a, nullptr, s); }
 
 // Segment end states -> states at the segment starts (see launch_seg_combine): one
-// workgroup per (64 state rows, 64 columns, bh).  The decay product of each (segment, row)
-// is formed by four threads over every fourth chunk (independent loads), joined through
-// LDS; then each thread loads all segment slots of its 16 elements at once and chains them.
+// workgroup per (64 state rows, 64 columns, bh); each thread loads all segment slots of its
+// 16 elements at once and chains them with the segments' decay products.
 __global__ __launch_bounds__(kThreads) void k_seg_combine(float* __restrict__ S,
-                                                          const float* __restrict__ eg, int BH,
-                                                          int dk, int dv, int N, int P) {
-  __shared__ float Gp[4][8][64];
+                                                          const float* __restrict__ dec, int BH,
+                                                          int dk, int dv, int P) {
   const int c0 = 64 * blockIdx.x, k0 = 64 * blockIdx.y, bh = blockIdx.z;
-  const int row = threadIdx.x & 63, part = threadIdx.x >> 6;
-  for (int sg = 1; sg < P - 1; ++sg) {
-    const int ia = sg * N / P, ib = (sg + 1) * N / P;
-    float g = 1.f;
-#pragma unroll 4
-    for (int i = ia + part; i < ib; i += 4) g *= eg[((long)bh * N + i) * dk + k0 + row];
-    Gp[part][sg][row] = g;
-  }
-  __syncthreads();
   const long slot = (long)BH * dk * dv;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int idx = threadIdx.x + kThreads * u, kr = idx >> 4, c = (idx & 15) * 4;
     const long off = ((long)bh * dk + k0 + kr) * dv + c0 + c;
     f32x4 x[8];
+    float g[8];
 #pragma unroll
-    for (int sg = 0; sg < 8; ++sg)
-      if (sg < P - 1) x[sg] = *reinterpret_cast<const f32x4*>(S + sg * slot + off);
+    for (int sg = 0; sg < 8; ++sg) {
+      if (sg < P - 1) {
+        x[sg] = *reinterpret_cast<const f32x4*>(S + sg * slot + off);
+        g[sg] = dec[((long)sg * BH + bh) * dk + k0 + kr];
+      }
+    }
 #pragma unroll
     for (int sg = 1; sg < 8; ++sg) {
       if (sg < P - 1) {
-        const float gs = (Gp[0][sg][kr] * Gp[1][sg][kr]) * (Gp[2][sg][kr] * Gp[3][sg][kr]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[sg][e] = gs * x[sg - 1][e] + x[sg][e];
+        for (int e = 0; e < 4; ++e) x[sg][e] = g[sg] * x[sg - 1][e] + x[sg][e];
         *reinterpret_cast<f32x4*>(S + sg * slot + off) = x[sg];
       }
     }
   }
 }
 
-hipError_t launch_seg_combine(float* S, const float* eg, int BH, int dk, int dv, int N, int P,
+hipError_t launch_seg_combine(float* S, const float* dec, int BH, int dk, int dv, int P,
                               hipStream_t s) {
   if (P <= 2 || BH == 0) return hipSuccess;
   if (P > 9 || dk % 64 != 0 || dv % 64 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_seg_combine, dim3(dv / 64, dk / 64, BH), dim3(kThreads), 0, s, S, eg, BH,
-                     dk, dv, N, P);
+  hipLaunchKernelGGL(k_seg_combine, dim3(dv / 64, dk / 64, BH), dim3(kThreads), 0, s, S, dec, BH,
+                     dk, dv, P);
   return hipGetLastError();
 }
 hipError_t launch_state_scan2(const ScanArgs& a, const ScanArgs& b, hipStream_t s) {
