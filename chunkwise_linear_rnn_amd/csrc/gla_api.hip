@@ -45,8 +45,16 @@ Dims dims_of(const gla_desc_t* d) {
 struct Plan {
   size_t g = 0, A = 0, Qh = 0, QhT = 0, Kh = 0, KhT = 0, eg = 0, st = 0, dst = 0, ST = 0,
          cT = 0, crossF = 0, crossR = 0, carry = 0, smid = 0, segdec = 0, dpart = 0,
-         total = 0;
+         sslots = 0, sdec = 0, total = 0;
 };
+
+// The materialized forward's state scan (every chunk state written, [v][k]) for a shape.
+gla::ScanArgs mat_scan_shape(const Dims& x) {
+  gla::ScanArgs a{};
+  a.dtype = x.dtype; a.C = (int)x.C; a.BH = (int)x.BH; a.T = (int)x.T; a.dk = (int)x.dk;
+  a.dv = (int)x.dv; a.N = (int)x.N; a.reverse = false; a.store = 2;
+  return a;
+}
 
 Plan plan_of(const gla_desc_t* d, int pass) {
   const Dims x = dims_of(d);
@@ -66,6 +74,10 @@ Plan plan_of(const gla_desc_t* d, int pass) {
   const bool mat = d->state_mode == GLA_STATES_MATERIALIZED;
   if (pass == GLA_PASS_FWD) {
     if (mat) p.g = take(gB);
+    // a segmented materialized scan: the states at the segment starts and decay products
+    const int P = mat ? gla::scan_segments(mat_scan_shape(x)) : 1;
+    if (P > 1) p.sslots = take((size_t)(P - 1) * x.BH * x.dk * x.dv * 4);
+    if (P > 2) p.sdec = take((size_t)(P - 1) * x.BH * x.dk * 4);
     p.A = take(AB);
     p.Qh = take(opB);
     p.KhT = take(opB);
@@ -306,13 +318,14 @@ gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void
   rs = dev(gla::launch_intra(ia, s));
   if (rs != GLA_OK) return rs;
   if (mat) {
-    gla::ScanArgs sa{};
-    sa.dtype = x.dtype; sa.C = (int)x.C; sa.BH = (int)x.BH; sa.T = (int)x.T; sa.dk = (int)x.dk;
-    sa.dv = (int)x.dv; sa.N = (int)x.N; sa.reverse = false; sa.store = 2;
+    gla::ScanArgs sa = mat_scan_shape(x);
     sa.XT = w + p.KhT; sa.Y = v; sa.eg = (const float*)(w + p.eg); sa.S_in = S0;
     sa.states = w + p.st; sa.S_out = S_T;
     if ((rs = tr.mark()) != GLA_OK) return rs;
-    rs = dev(gla::launch_state_scan(sa, s));
+    // long sequences with few heads: the scan in parallel segments from their start states
+    const int P = gla::scan_segments(sa);
+    rs = dev(gla::launch_state_scan_seg(sa, P > 1 ? (float*)(w + p.sslots) : nullptr,
+                                        P > 2 ? (float*)(w + p.sdec) : nullptr, s));
     if (rs != GLA_OK) return rs;
     gla::OutArgs oa{};
     oa.dtype = x.dtype; oa.C = (int)x.C; oa.BH = (int)x.BH; oa.T = (int)x.T; oa.dk = (int)x.dk;
@@ -507,7 +520,8 @@ namespace {
 
 struct GsaPlan {
   size_t w = 0, g2 = 0, KhT = 0, eg = 0, S1 = 0, s = 0, p = 0, ws2 = 0, dp = 0, dw2 = 0,
-         dla2 = 0, ds = 0, QhT = 0, dS1 = 0, dw1 = 0, Dloc = 0, tot = 0, dla1 = 0, total = 0;
+         dla2 = 0, ds = 0, QhT = 0, dS1 = 0, dw1 = 0, Dloc = 0, tot = 0, dla1 = 0, sslots = 0,
+         sdec = 0, total = 0;
   size_t ws2_bytes = 0;
 };
 
@@ -517,6 +531,14 @@ gla_desc_t gsa_layer2(const gla_gsa_desc_t* d) {
   x.subchunk = 16; x.dtype = GLA_F32; x.state_mode = GLA_STATES_MATERIALIZED;
   x.gate = GLA_GATE_LOG_ALPHA; x.gate_tau = 1.f; x.gate_shape = GLA_GATE_PER_KEY;
   return x;
+}
+
+// The first pass's key-slot scan (state [slots][dk], every chunk state written, fp32).
+gla::ScanArgs gsa_slot_scan(const gla_gsa_desc_t* d) {
+  gla::ScanArgs sa{};
+  sa.dtype = 0; sa.C = 64; sa.BH = d->B * d->H; sa.T = d->T; sa.dk = d->slots; sa.dv = d->dk;
+  sa.N = (d->T + 63) / 64; sa.reverse = false; sa.store = 3;
+  return sa;
 }
 
 GsaPlan gsa_plan(const gla_gsa_desc_t* d, int pass) {
@@ -532,6 +554,10 @@ GsaPlan gsa_plan(const gla_gsa_desc_t* d, int pass) {
   const size_t TM = BH * T * m * 4;
   p.w = take(TM); p.g2 = take(TM); p.KhT = take(BH * N * m * 64 * 4); p.eg = take(BH * N * m * 4);
   p.S1 = take(BH * N * m * dk * 4); p.s = take(TM); p.p = take(TM);
+  // the key-slot scan in segments (few heads): states at the segment starts, decay products
+  const int P = gla::scan_segments(gsa_slot_scan(d));
+  if (P > 1) p.sslots = take((size_t)(P - 1) * BH * m * dk * 4);
+  if (P > 2) p.sdec = take((size_t)(P - 1) * BH * m * 4);
   const gla_desc_t l2 = gsa_layer2(d);
   const size_t b2 = plan_of(&l2, pass == GLA_PASS_BWD ? GLA_PASS_BWD : GLA_PASS_FWD).total;
   p.ws2 = take(b2); p.ws2_bytes = b2;
@@ -556,11 +582,13 @@ struct GsaFwd {   // the forward up to p (and o when asked)
     ia.KhT = w + p.KhT; ia.eg = (float*)(w + p.eg); ia.g2_out = (float*)(w + p.g2);
     ia.gate = gla::GateFn{0, 1.f};
     if ((rs = dev(gla::launch_intra(ia, s))) != GLA_OK) return rs;
-    gla::ScanArgs sa{};
-    sa.dtype = 0; sa.C = 64; sa.BH = BH; sa.T = T; sa.dk = m; sa.dv = DK; sa.N = N;
-    sa.reverse = false; sa.store = 3; sa.XT = w + p.KhT; sa.Y = k; sa.eg = (const float*)(w + p.eg);
-    sa.states = w + p.S1;
-    if ((rs = dev(gla::launch_state_scan(sa, s))) != GLA_OK) return rs;
+    gla::ScanArgs sa = gsa_slot_scan(d);
+    sa.XT = w + p.KhT; sa.Y = k; sa.eg = (const float*)(w + p.eg); sa.states = w + p.S1;
+    const int P = gla::scan_segments(sa);
+    if ((rs = dev(gla::launch_state_scan_seg(sa, P > 1 ? (float*)(w + p.sslots) : nullptr,
+                                             P > 2 ? (float*)(w + p.sdec) : nullptr, s))) !=
+        GLA_OK)
+      return rs;
     if ((rs = dev(gla::launch_vg_out(q, k, (const float*)(w + p.w), (const float*)(w + p.g2),
                                      (const float*)(w + p.S1), (float*)(w + p.s), BH, T, DK, m,
                                      s))) != GLA_OK)

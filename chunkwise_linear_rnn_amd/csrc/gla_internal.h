@@ -86,9 +86,11 @@ struct ScanArgs {
   // 0 .. nseg - 1 of the split into seg_p parts (chunks [s N / seg_p, (s + 1) N / seg_p))
   // in one launch, each from zero except the first (from S_in), each end state to
   // S_out + s * BH * dk * dv, and each segment's total decay (product of its chunks'
-  // exp(gamma)) per row to seg_decay [nseg][BH][dk]
+  // exp(gamma)) per row to seg_decay [nseg][BH][dk].  With stores (nseg == seg_p): every
+  // segment writes its chunks' states, segment s > 0 from seg_in + (s - 1) * BH * dk * dv.
   int nseg, seg_p;
   float* seg_decay;
+  const float* seg_in;
 };
 hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s);
 // Two scans of the same shape and kind (the backward's forward and reverse scans) in one
@@ -102,6 +104,15 @@ int scan_tile_v(const ScanArgs& a);
 // segments' decay products [P - 1][BH][dk] from the same scan.
 hipError_t launch_seg_combine(float* S, const float* dec, int BH, int dk, int dv, int P,
                               hipStream_t s);
+// Segments for a forward scan that writes every chunk's state (1: one walk): about 256
+// workgroups when B*H*(dk/64)*(dv/TV) is small, at most 8, at least two chunks each.
+int scan_segments(const ScanArgs& a);
+// A forward scan with stores run as scan_segments(a) segments in parallel: the segments'
+// end states from zero (one launch), chained into the states at the segment starts
+// (workspace slots: (P - 1) * BH * dk * dv floats at `slots`, (P - 1) * BH * dk at `dec`),
+// then every segment walked from its start state.  S_out (the final state) is formed by
+// the last segment.  One plain launch when scan_segments(a) == 1.
+hipError_t launch_state_scan_seg(const ScanArgs& a, float* slots, float* dec, hipStream_t s);
 // Per-direction kernel arguments of the scan kernel.
 struct ScanDir {
   const void *XT, *Y, *X2T, *Y2;

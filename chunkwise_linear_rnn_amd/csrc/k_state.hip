@@ -68,7 +68,8 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
                                                             const float* __restrict__ eg, int T,
                                                             int dk, int dv, int N, int nsteps,
                                                             int nseg, int segp,
-                                                            float* __restrict__ segdec) {
+                                                            float* __restrict__ segdec,
+                                                            const float* __restrict__ seg_in) {
   // TV value columns per workgroup: NJ accumulator tiles per wave, NY 64-column
   // value-side tiles per operand
   constexpr int NJ = TV / 16, NY = TV / 64;
@@ -99,9 +100,10 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   int lt = xcd_logical(blockIdx.x, gridDim.x);
   const bool second = lt >= tiles;
   if (second) lt -= tiles;
-  // nseg > 1 (forward, no stores): segment sg of the sequence split into segp parts,
-  // chunks [sg N / segp, (sg + 1) N / segp), from S_in for the first and from zero for the
-  // others; its end state goes to S_out + sg * BH * dk * dv
+  // nseg > 1 (forward): segment sg of the sequence split into segp parts, chunks
+  // [sg N / segp, (sg + 1) N / segp), from S_in for the first and, for the others, from
+  // slot sg - 1 of seg_in (the states at the segment starts) or from zero; its end state
+  // goes to S_out + sg * BH * dk * dv
   const int base = tiles / nseg, sg = lt / base;
   lt -= sg * base;
   const int i0 = nseg > 1 ? sg * N / segp : 0;
@@ -111,10 +113,17 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   const OpT* __restrict__ X2T = (const OpT*)(second ? d1.X2T : d0.X2T);
   const Tin* __restrict__ Y2 = (const Tin*)(second ? d1.Y2 : d0.Y2);
   float* __restrict__ cross = second ? d1.cross : d0.cross;
-  const float* __restrict__ S_in = sg > 0 ? nullptr : second ? d1.S_in : d0.S_in;
+  const float* __restrict__ S_in =
+      sg > 0 ? (seg_in ? seg_in + (long)(sg - 1) * (base / (nvt * nkt)) * dk * dv : nullptr)
+             : second ? d1.S_in : d0.S_in;
   void* __restrict__ states = second ? d1.states : d0.states;
   float* __restrict__ S_out = second ? d1.S_out : d0.S_out;
-  if (S_out) S_out += (long)sg * (base / (nvt * nkt)) * dk * dv;
+  // segment end states (no stores) go to slot sg; in the storing pass only the last segment
+  // forms the final state
+  if (S_out && nseg > 1) {
+    if (segp == nseg) S_out = sg == nseg - 1 ? S_out : nullptr;
+    else S_out += (long)sg * (base / (nvt * nkt)) * dk * dv;
+  }
   const int reverse = second ? d1.reverse : d0.reverse;
   const int frag_states = second ? d1.frag_states : d0.frag_states;
   const int vt = lt % nvt, kt = (lt / nvt) % nkt, bh = lt / (nvt * nkt);
@@ -375,7 +384,7 @@ static void launch_scan_k(const ScanArgs& a, const ScanArgs* b, hipStream_t s) {
   hipLaunchKernelGGL((k_state_scan<Tin, OpT, SPLIT, C, STORE, CROSS, TV>), grid, dim3(kThreads), 0,
                      s, dir(a), dir(b ? *b : a), ndir, a.eg, a.T, a.dk, a.dv, a.N,
                      a.nsteps > 0 && a.nsteps < a.N ? a.nsteps : a.N, nseg, a.seg_p,
-                     nseg > 1 ? a.seg_decay : nullptr);
+                     nseg > 1 ? a.seg_decay : nullptr, nseg > 1 ? a.seg_in : nullptr);
 }
 
 int scan_tile_v(const ScanArgs& a) {
@@ -415,9 +424,12 @@ static hipError_t launch_scans(const ScanArgs& a, const ScanArgs* b, hipStream_t
                               scan_tile_v(x) == 128);
   };
   if (!frag_ok(a) || (b && !frag_ok(*b))) return hipErrorInvalidValue;
-  // sequence segments: one forward scan without stores or cross terms, nseg < seg_p <= N
-  if (a.nseg > 1 && (b || a.store != 0 || a.cross || a.reverse || a.seg_p <= a.nseg ||
-                     a.seg_p > a.N || !a.S_out || !a.seg_decay))
+  // sequence segments: one forward scan without cross terms; without stores, the segments'
+  // end states (nseg < seg_p <= N); with stores, every segment from its start state
+  // (nseg == seg_p <= N)
+  if (a.nseg > 1 && (b || a.cross || a.reverse || a.seg_p > a.N ||
+                     (a.store == 0 && (a.seg_p <= a.nseg || !a.S_out || !a.seg_decay)) ||
+                     (a.store != 0 && (a.seg_p != a.nseg || !a.seg_in))))
     return hipErrorInvalidValue;
   if (b && (b->dtype != a.dtype || b->C != a.C || b->BH != a.BH || b->T != a.T ||
             b->dk != a.dk || b->dv != a.dv || b->N != a.N || b->xt_f32 != a.xt_f32 ||
@@ -434,6 +446,38 @@ static hipError_t launch_scans(const ScanArgs& a, const ScanArgs* b, hipStream_t
 }
 
 hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s) { return launch_scans(a, nullptr, s); }
+
+int scan_segments(const ScanArgs& a) {
+  if (a.reverse || a.cross || a.store == 0 || a.N < 4 || (a.nsteps > 0 && a.nsteps < a.N)) return 1;
+  const long tiles = (long)a.BH * (a.dk / 64) * (a.dv / scan_tile_v(a));
+  if (tiles >= 256) return 1;
+  int P = (int)(256 / tiles);
+  P = P > 8 ? 8 : P;
+  P = P > a.N / 2 ? a.N / 2 : P;
+  return P < 2 ? 2 : P;
+}
+
+hipError_t launch_state_scan_seg(const ScanArgs& a, float* slots, float* dec, hipStream_t s) {
+  const int P = scan_segments(a);
+  if (P <= 1) return launch_scans(a, nullptr, s);
+  if (!slots || (P > 2 && !dec)) return hipErrorInvalidValue;
+  // the states at the segment starts: segment end states from zero (the first from S_in),
+  // then chained
+  ScanArgs pre = a;
+  pre.store = 0; pre.states = nullptr; pre.S_out = slots; pre.seg_in = nullptr;
+  if (P == 2) {
+    pre.nseg = 0; pre.nsteps = a.N / 2; pre.seg_decay = nullptr;
+  } else {
+    pre.nseg = P - 1; pre.seg_p = P; pre.seg_decay = dec;
+  }
+  hipError_t e = launch_scans(pre, nullptr, s);
+  if (e != hipSuccess) return e;
+  if ((e = launch_seg_combine(slots, dec, a.BH, a.dk, a.dv, P, s)) != hipSuccess) return e;
+  // every segment from its start state, writing its chunks' states
+  ScanArgs run = a;
+  run.nseg = P; run.seg_p = P; run.seg_in = slots; run.seg_decay = nullptr;
+  return launch_scans(run, nullptr, s);
+}
 
 // Segment end states -> states at the segment starts (see launch_seg_combine): one
 // workgroup per (64 state rows, 64 columns, bh); each thread loads all segment slots of its
