@@ -451,7 +451,7 @@ int scan_segments(const ScanArgs& a) {
   if (a.reverse || a.cross || a.store == 0 || a.N < 4 || (a.nsteps > 0 && a.nsteps < a.N)) return 1;
   const long tiles = (long)a.BH * (a.dk / 64) * (a.dv / scan_tile_v(a));
   if (tiles >= 256) return 1;
-  int P = (int)(256 / tiles);
+  int P = (int)(512 / tiles);   // these scans hold two or more workgroups per CU
   P = P > 8 ? 8 : P;
   P = P > a.N / 2 ? a.N / 2 : P;
   return P < 2 ? 2 : P;
