@@ -689,11 +689,15 @@ gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* d, const void* q, const void* k, 
   ia.q = w + p.ds; ia.k = w + p.w; ia.la = la; ia.g = nullptr; ia.QhT = w + p.QhT;
   ia.eg = (float*)(w + p.eg); ia.gate = gla::GateFn{0, 1.f};
   if ((rs = dev(gla::launch_intra(ia, s))) != GLA_OK) return rs;
-  gla::ScanArgs ra{};
-  ra.dtype = 0; ra.C = 64; ra.BH = BH; ra.T = T; ra.dk = m; ra.dv = DK; ra.N = N;
-  ra.reverse = true; ra.store = 3; ra.XT = w + p.QhT; ra.Y = q; ra.eg = (const float*)(w + p.eg);
+  gla::ScanArgs ra = gsa_slot_scan(d);
+  ra.reverse = true; ra.XT = w + p.QhT; ra.Y = q; ra.eg = (const float*)(w + p.eg);
   ra.states = w + p.dS1;
-  if ((rs = dev(gla::launch_state_scan(ra, s))) != GLA_OK) return rs;
+  // in segments like the forward key-slot scan (same shape: the same workspace slots)
+  const int P = gla::scan_segments(ra);
+  if ((rs = dev(gla::launch_state_scan_seg(ra, P > 1 ? (float*)(w + p.sslots) : nullptr,
+                                           P > 2 ? (float*)(w + p.sdec) : nullptr, s))) !=
+      GLA_OK)
+    return rs;
   if ((rs = dev(gla::launch_vg_bwd((const float*)q, (const float*)k, (const float*)(w + p.w),
                                    (const float*)(w + p.g2), (const float*)(w + p.ds),
                                    (const float*)(w + p.s), (const float*)(w + p.S1),

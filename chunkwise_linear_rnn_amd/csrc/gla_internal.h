@@ -104,8 +104,8 @@ int scan_tile_v(const ScanArgs& a);
 // segments' decay products [P - 1][BH][dk] from the same scan.
 hipError_t launch_seg_combine(float* S, const float* dec, int BH, int dk, int dv, int P,
                               hipStream_t s);
-// Segments for a forward scan that writes every chunk's state (1: one walk): about 512
-// workgroups when B*H*(dk/64)*(dv/TV) is below 256, at most 8, at least two chunks each.
+// Segments for a scan that writes every chunk's state (1: one walk): about 512
+// workgroups when B*H*(dk/64)*(dv/TV) is below 256, at most 8, at least 8 chunks each.
 int scan_segments(const ScanArgs& a);
 // A forward scan with stores run as scan_segments(a) segments in parallel: the segments'
 // end states from zero (one launch), chained into the states at the segment starts

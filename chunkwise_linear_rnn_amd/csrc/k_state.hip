@@ -100,14 +100,17 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   int lt = xcd_logical(blockIdx.x, gridDim.x);
   const bool second = lt >= tiles;
   if (second) lt -= tiles;
-  // nseg > 1 (forward): segment sg of the sequence split into segp parts, chunks
-  // [sg N / segp, (sg + 1) N / segp), from S_in for the first and, for the others, from
-  // slot sg - 1 of seg_in (the states at the segment starts) or from zero; its end state
-  // goes to S_out + sg * BH * dk * dv
+  // nseg > 1: the sg-th segment in walk order of the sequence split into segp parts
+  // (forward: chunks [sg N / segp, (sg + 1) N / segp); reverse: the (segp - 1 - sg)-th
+  // part, walked downwards), from S_in for the first and, for the others, from slot sg - 1
+  // of seg_in (the states at the segment starts) or from zero; its end state goes to
+  // S_out + sg * BH * dk * dv
   const int base = tiles / nseg, sg = lt / base;
   lt -= sg * base;
-  const int i0 = nseg > 1 ? sg * N / segp : 0;
-  const int nst = nseg > 1 ? (sg + 1) * N / segp - i0 : nsteps;
+  const int rev0 = second ? d1.reverse : d0.reverse;
+  const int part = rev0 ? segp - 1 - sg : sg;
+  const int i0 = nseg > 1 ? part * N / segp : 0;
+  const int nst = nseg > 1 ? (part + 1) * N / segp - i0 : nsteps;
   const OpT* __restrict__ XT = (const OpT*)(second ? d1.XT : d0.XT);
   const Tin* __restrict__ Y = (const Tin*)(second ? d1.Y : d0.Y);
   const OpT* __restrict__ X2T = (const OpT*)(second ? d1.X2T : d0.X2T);
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // that every prefetch is unconditional and the compiler's wait counts stay exact
   auto chunk_of = [&](int step) {
     const int sc = min(step, nst - 1);
-    return reverse ? N - 1 - sc : i0 + sc;
+    return reverse ? (nseg > 1 ? i0 + nst - 1 - sc : N - 1 - sc) : i0 + sc;
   };
   // the decays of steps [sb, sb + EB) into LDS: read there at each step, they put no
   // global-memory round trip on the chain of dependent steps
@@ -424,10 +427,10 @@ static hipError_t launch_scans(const ScanArgs& a, const ScanArgs* b, hipStream_t
                               scan_tile_v(x) == 128);
   };
   if (!frag_ok(a) || (b && !frag_ok(*b))) return hipErrorInvalidValue;
-  // sequence segments: one forward scan without cross terms; without stores, the segments'
-  // end states (nseg < seg_p <= N); with stores, every segment from its start state
+  // sequence segments: one scan without cross terms; without stores, the segments' end
+  // states (nseg < seg_p <= N); with stores, every segment from its start state
   // (nseg == seg_p <= N)
-  if (a.nseg > 1 && (b || a.cross || a.reverse || a.seg_p > a.N ||
+  if (a.nseg > 1 && (b || a.cross || a.seg_p > a.N ||
                      (a.store == 0 && (a.seg_p <= a.nseg || !a.S_out || !a.seg_decay)) ||
                      (a.store != 0 && (a.seg_p != a.nseg || !a.seg_in))))
     return hipErrorInvalidValue;
@@ -448,12 +451,14 @@ static hipError_t launch_scans(const ScanArgs& a, const ScanArgs* b, hipStream_t
 hipError_t launch_state_scan(const ScanArgs& a, hipStream_t s) { return launch_scans(a, nullptr, s); }
 
 int scan_segments(const ScanArgs& a) {
-  if (a.reverse || a.cross || a.store == 0 || a.N < 4 || (a.nsteps > 0 && a.nsteps < a.N)) return 1;
+  // at least 8 chunks per segment: each pass has a fixed start-up cost (initial state,
+  // decay staging) that a shorter walk does not repay
+  if (a.cross || a.store == 0 || a.N < 16 || (a.nsteps > 0 && a.nsteps < a.N)) return 1;
   const long tiles = (long)a.BH * (a.dk / 64) * (a.dv / scan_tile_v(a));
   if (tiles >= 256) return 1;
   int P = (int)(512 / tiles);   // these scans hold two or more workgroups per CU
   P = P > 8 ? 8 : P;
-  P = P > a.N / 2 ? a.N / 2 : P;
+  P = P > a.N / 8 ? a.N / 8 : P;
   return P < 2 ? 2 : P;
 }
 
@@ -465,8 +470,8 @@ hipError_t launch_state_scan_seg(const ScanArgs& a, float* slots, float* dec, hi
   // then chained
   ScanArgs pre = a;
   pre.store = 0; pre.states = nullptr; pre.S_out = slots; pre.seg_in = nullptr;
-  if (P == 2) {
-    pre.nseg = 0; pre.nsteps = a.N / 2; pre.seg_decay = nullptr;
+  if (P == 2) {   // the first half in walk order (reverse: chunks [N / 2, N))
+    pre.nseg = 0; pre.nsteps = a.reverse ? a.N - a.N / 2 : a.N / 2; pre.seg_decay = nullptr;
   } else {
     pre.nseg = P - 1; pre.seg_p = P; pre.seg_decay = dec;
   }

@@ -35,6 +35,9 @@ CASES = [
     ("dk128_dv192", 2, 1, 200, 128, 192, 64, 2.0),
     ("slots128", 1, 1, 130, 64, 128, 128, -3.0),
     ("one_token", 1, 1, 1, 64, 64, 64, 0.0),
+    # 33 chunks of one head: the key-slot scans (forward and reverse) in 4 segments walked
+    # from their chained start states, ragged last chunk
+    ("thin_long", 1, 1, 2100, 64, 64, 64, -1.0),
 ]
 
 

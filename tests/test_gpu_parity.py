@@ -49,10 +49,17 @@ SMALL = [
     # a ragged last chunk, and a sequence shorter than one chunk
     ("bf16_c64_dv256", "bf16", 1, 2, 301, 128, 256, 64, 0.0),
     ("bf16_short_dv128", "bf16", 1, 1, 37, 64, 128, 64, 0.0),
-    # the recompute forward's sequence split at chunk N / 2: 9 chunks (halves of 4 and 5,
-    # ragged last chunk) and 7 chunks (halves of 3 and 4)
+    # the recompute forward's sequence segments (few workgroups per segment: up to N / 2
+    # segments): 9 chunks in 4 segments (ragged last chunk) and 7 chunks in 3
     ("bf16_c64_n9", "bf16", 1, 2, 520, 128, 128, 64, -1.0),
     ("bf16_c64_n7", "bf16", 2, 1, 400, 64, 128, 64, 0.5),
+    # long and thin: 32 chunks, recompute in 8 segments of 4, and the materialized scan in
+    # 4 segments walked from their chained start states (ragged last chunk); fp32 with 24
+    # chunks (materialized scan in 3 segments); chunk 128 with 17 chunks (recompute in 8
+    # segments, materialized in 2)
+    ("bf16_thin_n32", "bf16", 1, 1, 2000, 64, 128, 64, -1.0),
+    ("f32_thin_n24", "f32", 1, 1, 1500, 64, 64, 64, -0.5),
+    ("bf16_c128_thin_n17", "bf16", 1, 1, 2100, 64, 128, 128, 0.0),
     # chunk 128 walked in 64-row halves with the sequence split: 5 chunks (halves of 2 and
     # 3), the last one's second half partly (T = 600) or wholly (T = 540) past T
     ("bf16_c128_n5", "bf16", 1, 2, 600, 128, 128, 128, 0.5),
