@@ -87,3 +87,16 @@ def test_mfma_summary_is_well_formed(bench):
         pytest.skip("mfma_gla1p3b_t2k.json predates the current kernel sources")
     for st, v in got.items():
         assert st in stages and 0.0 <= v["mfma_busy_frac"] <= 1.0
+
+
+def test_metric_names_the_workload_it_ran(bench):
+    from gla_inputs import CONFIGS as WORKLOADS
+    head = WORKLOADS["gla1p3b_t2k"]
+    assert bench.metric_name(head, False) == bench.METRIC
+    for name in ("sweep_t8192_c64", "gla340m_t2k", "long_t20k"):
+        w = WORKLOADS[name]
+        m = bench.metric_name(w, name == "long_t20k")
+        assert name in m and f"T={w.T}" in m and "1.3B" not in m
+    assert bench.metric_name(WORKLOADS["long_t20k"], True).startswith("GLA fwd tokens/s")
+    # the headline shape run forward-only is not the headline metric either
+    assert bench.metric_name(head, True) != bench.METRIC
