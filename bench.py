@@ -28,10 +28,11 @@ summed over the key dimension).
 `gsa_step` times Gated Slot Attention (float32, fwd + bwd, --gsa-slots memory slots,
 default 64) at the workload's B, H, T, dk, dv.
 
-Every timed step runs after a 512 MiB device write that evicts the 256 MiB Infinity
-Cache, with HIP events around the step only (the write is not timed): the headline
-`value` is the cache-flushed rate, the inputs resident in HBM but not in any cache.
-`warm_cache` repeats the steps back to back without the write (inputs and workspaces
+Every timed step runs after an untimed cache flush (a 512 MiB device write, then a
+512 MiB read that evicts the write's own dirty lines), with HIP events around the step
+only: the headline `value` is the cache-flushed rate, the inputs resident in HBM but not
+in L2 or the 256 MiB Infinity Cache, and no write-backs of foreign data pending.
+`warm_cache` repeats the steps back to back without the flush (inputs and workspaces
 partly served from the Infinity Cache), for context.
 
 The CPU baseline times the fp64 oracle (step recurrence, then direct backward, each
@@ -518,10 +519,16 @@ def main():
         arr[dom_i], arr[dom_i + 1] = ev_dom[j][0], ev_dom[j][1]
         sparse.append(arr)
 
-    # The timed steps: each after a 512 MiB write that evicts the Infinity Cache (untimed),
-    # HIP events around the step itself, and the two events around the longest stage.
+    # The timed steps: each after an untimed flush, HIP events around the step itself, and
+    # the two events around the longest stage.  The flush writes 512 MiB and then reads
+    # another 512 MiB: the write evicts the previous step's data from L2 and the 256 MiB
+    # Infinity Cache, and the read evicts the write's own dirty lines, so that the timed
+    # step starts with none of its data cached and no foreign write-backs pending (a
+    # write alone left ~256 MiB of dirty lines that the timed step then paid to write back).
     flush = not args.no_flush
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if flush else None
+    scratch_rd = (torch.empty(128 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+                  if flush else None)
     ev_step = [hip.create(2) for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps{' (cache flushed before each)' if flush else ''}",
           file=sys.stderr, flush=True)
@@ -530,6 +537,7 @@ def main():
     for j in range(args.steps):
         if flush:
             scratch.fill_(j & 0xFF)
+            scratch_rd.sum()
         hip.record(ev_step[j][0], sp)
         if dom_pass == "fwd":
             step(sparse[j], None)
@@ -540,9 +548,9 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = sum(hip.elapsed_ms(e0, e1) for e0, e1 in ev_step) / args.steps
     dom_ms = sum(hip.elapsed_ms(ev_dom[j][0], ev_dom[j][1]) for j in range(args.steps)) / args.steps
-    del scratch
+    del scratch, scratch_rd
 
-    # The same steps back to back without the write (warm Infinity Cache), for context.
+    # The same steps back to back without the flush (warm Infinity Cache), for context.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for j in range(args.steps):
@@ -689,6 +697,7 @@ def main():
         "roofline": roof,
         "intra_mfma": intra_mfma or None,
         "cache_flushed": flush,
+        "cache_flush": "512 MiB write then 512 MiB read before each timed step, untimed" if flush else None,
         "warm_cache": warm_rec,
         "gate_logits_step": gate_fe,
         "scalar_gate_step": scalar_fe,
