@@ -105,6 +105,12 @@ Plan plan_of(const gla_desc_t* d, int pass) {
     p.carry = take(egB);
     if (d->gate_shape == GLA_GATE_SCALAR)
       p.dpart = take((size_t)x.BH * x.T * (x.dk / 64) * 4);
+    // the two scans in segments (few workgroups): both scans' segment start states and
+    // decay products
+    const int P = gla::scan2_segments(x.dtype, (int)x.C, (int)x.BH, (int)x.dk, (int)x.dv,
+                                      (int)x.N);
+    if (P > 1) p.sslots = take((size_t)2 * (P - 1) * x.BH * x.dk * x.dv * 4);
+    if (P > 2) p.sdec = take((size_t)2 * (P - 1) * x.BH * x.dk * 4);
   } else {
     p.KhT = take(opB);
     p.eg = take(egB);
@@ -424,9 +430,12 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   // workgroups stage dS transposed from them
   sa.frag_states = gla::scan_tile_v(sa) == 128;
   ra.frag_states = sa.frag_states;
-  // both scans in one launch
+  // both scans in one launch (in sequence segments when few workgroups would walk the
+  // whole sequence)
   if ((rs = tr.mark()) != GLA_OK) return rs;
-  rs = dev(gla::launch_state_scan2(sa, ra, s));
+  const int P2 = gla::scan2_segments(x.dtype, C, BH, DK, DV, N);
+  rs = dev(gla::launch_state_scan2_seg(sa, ra, P2 > 1 ? (float*)(w + p.sslots) : nullptr,
+                                       P2 > 2 ? (float*)(w + p.sdec) : nullptr, s));
   if (rs != GLA_OK) return rs;
   if (dS_T) {
     if ((rs = tr.mark()) != GLA_OK) return rs;

@@ -82,12 +82,15 @@ struct ScanArgs {
                          // order (see the scan kernel), for the backward chunk kernel
   float* S_out;          // [BH][dk][dv] or NULL
   int nsteps;            // chunks to walk (0: all N); the layout strides still use N
-  // sequence segments (forward, store 0, no cross term): nseg > 1 walks segments
-  // 0 .. nseg - 1 of the split into seg_p parts (chunks [s N / seg_p, (s + 1) N / seg_p))
-  // in one launch, each from zero except the first (from S_in), each end state to
+  // sequence segments (seg_p > 1): the sequence split into seg_p parts (chunks
+  // [s N / seg_p, (s + 1) N / seg_p)), indexed in walk order (a reverse scan's segment 0
+  // is the last part).  Without stores (0 < nseg < seg_p): segments 0 .. nseg - 1 in one
+  // launch, each from zero except the first (from S_in), each end state to
   // S_out + s * BH * dk * dv, and each segment's total decay (product of its chunks'
-  // exp(gamma)) per row to seg_decay [nseg][BH][dk].  With stores (nseg == seg_p): every
-  // segment writes its chunks' states, segment s > 0 from seg_in + (s - 1) * BH * dk * dv.
+  // exp(gamma)) per row to seg_decay [nseg][BH][dk] (may be NULL).  With stores
+  // (nseg == seg_p, cross terms allowed): every segment writes its chunks' states (and
+  // cross terms), segment s > 0 from seg_in + (s - 1) * BH * dk * dv; the last one forms
+  // S_out.
   int nseg, seg_p;
   float* seg_decay;
   const float* seg_in;
@@ -113,6 +116,16 @@ int scan_segments(const ScanArgs& a);
 // then every segment walked from its start state.  S_out (the final state) is formed by
 // the last segment.  One plain launch when scan_segments(a) == 1.
 hipError_t launch_state_scan_seg(const ScanArgs& a, float* slots, float* dec, hipStream_t s);
+// Segments for the backward's two scans with cross terms (1: one walk each): only where
+// the walk bounds them, below 256 workgroups for both scans; then about 512 workgroups,
+// at most 8 segments, at least 8 chunks per segment.
+int scan2_segments(int dtype, int C, int BH, int dk, int dv, int N);
+// launch_state_scan2 in scan2_segments segments: both scans' segment end states (one
+// launch, no stores), chained, then every segment of both scans walked from its start
+// state with stores and cross terms.  slots: 2 (P - 1) BH dk dv floats (a's slots, then
+// b's); dec: 2 (P - 1) BH dk floats (P > 2 only).
+hipError_t launch_state_scan2_seg(const ScanArgs& a, const ScanArgs& b, float* slots, float* dec,
+                                  hipStream_t s);
 // Per-direction kernel arguments of the scan kernel.
 struct ScanDir {
   const void *XT, *Y, *X2T, *Y2;
@@ -120,6 +133,8 @@ struct ScanDir {
   const float* S_in;
   void* states;
   float* S_out;
+  const float* seg_in;   // segment start states (see ScanArgs)
+  float* seg_dec;        // segment decay products (see ScanArgs)
   int reverse;
   int frag_states;
 };

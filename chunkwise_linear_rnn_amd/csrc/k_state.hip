@@ -67,9 +67,7 @@ template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS, 
 __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, ScanDir d1, int ndir,
                                                             const float* __restrict__ eg, int T,
                                                             int dk, int dv, int N, int nsteps,
-                                                            int nseg, int segp,
-                                                            float* __restrict__ segdec,
-                                                            const float* __restrict__ seg_in) {
+                                                            int nseg, int segp) {
   // TV value columns per workgroup: NJ accumulator tiles per wave, NY 64-column
   // value-side tiles per operand
   constexpr int NJ = TV / 16, NY = TV / 64;
@@ -100,17 +98,20 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   int lt = xcd_logical(blockIdx.x, gridDim.x);
   const bool second = lt >= tiles;
   if (second) lt -= tiles;
-  // nseg > 1: the sg-th segment in walk order of the sequence split into segp parts
-  // (forward: chunks [sg N / segp, (sg + 1) N / segp); reverse: the (segp - 1 - sg)-th
-  // part, walked downwards), from S_in for the first and, for the others, from slot sg - 1
-  // of seg_in (the states at the segment starts) or from zero; its end state goes to
-  // S_out + sg * BH * dk * dv
+  // segp > 1: the sg-th of nseg segments in walk order of the sequence split into segp
+  // parts (forward: chunks [sg N / segp, (sg + 1) N / segp); reverse: the
+  // (segp - 1 - sg)-th part, walked downwards), from S_in for the first and, for the
+  // others, from slot sg - 1 of seg_in (the states at the segment starts) or from zero;
+  // without stores its end state goes to S_out + sg * BH * dk * dv
   const int base = tiles / nseg, sg = lt / base;
   lt -= sg * base;
+  const bool segm = segp > 1;
   const int rev0 = second ? d1.reverse : d0.reverse;
   const int part = rev0 ? segp - 1 - sg : sg;
-  const int i0 = nseg > 1 ? part * N / segp : 0;
-  const int nst = nseg > 1 ? (part + 1) * N / segp - i0 : nsteps;
+  const int i0 = segm ? part * N / segp : 0;
+  const int nst = segm ? (part + 1) * N / segp - i0 : nsteps;
+  const float* __restrict__ seg_in = second ? d1.seg_in : d0.seg_in;
+  float* __restrict__ segdec = second ? d1.seg_dec : d0.seg_dec;
   const OpT* __restrict__ XT = (const OpT*)(second ? d1.XT : d0.XT);
   const Tin* __restrict__ Y = (const Tin*)(second ? d1.Y : d0.Y);
   const OpT* __restrict__ X2T = (const OpT*)(second ? d1.X2T : d0.X2T);
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   float* __restrict__ S_out = second ? d1.S_out : d0.S_out;
   // segment end states (no stores) go to slot sg; in the storing pass only the last segment
   // forms the final state
-  if (S_out && nseg > 1) {
+  if (S_out && segm) {
     if (segp == nseg) S_out = sg == nseg - 1 ? S_out : nullptr;
     else S_out += (long)sg * (base / (nvt * nkt)) * dk * dv;
   }
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // that every prefetch is unconditional and the compiler's wait counts stay exact
   auto chunk_of = [&](int step) {
     const int sc = min(step, nst - 1);
-    return reverse ? (nseg > 1 ? i0 + nst - 1 - sc : N - 1 - sc) : i0 + sc;
+    return reverse ? (segm ? i0 + nst - 1 - sc : N - 1 - sc) : i0 + sc;
   };
   // the decays of steps [sb, sb + EB) into LDS: read there at each step, they put no
   // global-memory round trip on the chain of dependent steps
@@ -380,14 +381,17 @@ static void launch_scan_k(const ScanArgs& a, const ScanArgs* b, hipStream_t s) {
     d.XT = x.XT; d.Y = x.Y; d.X2T = x.X2T; d.Y2 = x.Y2; d.cross = x.cross; d.S_in = x.S_in;
     d.states = x.states; d.S_out = x.S_out; d.reverse = x.reverse ? 1 : 0;
     d.frag_states = x.frag_states ? 1 : 0;
+    const bool segm = x.seg_p > 1;
+    d.seg_in = segm ? x.seg_in : nullptr;
+    d.seg_dec = segm ? x.seg_decay : nullptr;
     return d;
   };
-  const int ndir = b ? 2 : 1, nseg = a.nseg > 1 ? a.nseg : 1;
+  const bool segm = a.seg_p > 1;
+  const int ndir = b ? 2 : 1, nseg = segm ? a.nseg : 1;
   dim3 grid(ndir * nseg * (a.dv / TV) * (a.dk / 64) * a.BH);
   hipLaunchKernelGGL((k_state_scan<Tin, OpT, SPLIT, C, STORE, CROSS, TV>), grid, dim3(kThreads), 0,
                      s, dir(a), dir(b ? *b : a), ndir, a.eg, a.T, a.dk, a.dv, a.N,
-                     a.nsteps > 0 && a.nsteps < a.N ? a.nsteps : a.N, nseg, a.seg_p,
-                     nseg > 1 ? a.seg_decay : nullptr, nseg > 1 ? a.seg_in : nullptr);
+                     a.nsteps > 0 && a.nsteps < a.N ? a.nsteps : a.N, nseg, segm ? a.seg_p : 1);
 }
 
 int scan_tile_v(const ScanArgs& a) {
@@ -406,7 +410,10 @@ static hipError_t launch_scan_t(const ScanArgs& a, const ScanArgs* b, hipStream_
     }
     launch_scan_k<Tin, OpT, SPLIT, C, 1, true, 64>(a, b, s);
   } else if constexpr (SPLIT) {
-    return hipErrorInvalidValue;   // split operands come with the backward's cross term only
+    // split operands come with the backward's scans: the cross-term scans above, and the
+    // segment end states before them (no stores)
+    if (a.store != 0) return hipErrorInvalidValue;
+    launch_scan_k<Tin, OpT, SPLIT, C, 0, false, 64>(a, b, s);
   } else {
     switch (a.store) {
       case 0: launch_scan_k<Tin, OpT, SPLIT, C, 0, false, 64>(a, b, s); break;
@@ -427,12 +434,17 @@ static hipError_t launch_scans(const ScanArgs& a, const ScanArgs* b, hipStream_t
                               scan_tile_v(x) == 128);
   };
   if (!frag_ok(a) || (b && !frag_ok(*b))) return hipErrorInvalidValue;
-  // sequence segments: one scan without cross terms; without stores, the segments' end
-  // states (nseg < seg_p <= N); with stores, every segment from its start state
-  // (nseg == seg_p <= N)
-  if (a.nseg > 1 && (b || a.cross || a.seg_p > a.N ||
-                     (a.store == 0 && (a.seg_p <= a.nseg || !a.S_out || !a.seg_decay)) ||
-                     (a.store != 0 && (a.seg_p != a.nseg || !a.seg_in))))
+  // sequence segments (seg_p > 1): without stores, the end states of segments
+  // 0 .. nseg - 1 (0 < nseg < seg_p <= N; decay products wherever the segments are
+  // chained, nseg > 1); with stores, every segment from its start state
+  // (nseg == seg_p <= N); the same segments in both scans of a launch
+  auto seg_ok = [](const ScanArgs& x) {
+    if (x.seg_p <= 1) return x.nseg <= 1;
+    if (x.seg_p > x.N || x.nseg < 1) return false;
+    if (x.store == 0) return x.nseg < x.seg_p && x.S_out && (x.nseg == 1 || x.seg_decay);
+    return x.nseg == x.seg_p && x.seg_in != nullptr;
+  };
+  if (!seg_ok(a) || (b && (!seg_ok(*b) || b->seg_p != a.seg_p || b->nseg != a.nseg)))
     return hipErrorInvalidValue;
   if (b && (b->dtype != a.dtype || b->C != a.C || b->BH != a.BH || b->T != a.T ||
             b->dk != a.dk || b->dv != a.dv || b->N != a.N || b->xt_f32 != a.xt_f32 ||
@@ -482,6 +494,52 @@ hipError_t launch_state_scan_seg(const ScanArgs& a, float* slots, float* dec, hi
   ScanArgs run = a;
   run.nseg = P; run.seg_p = P; run.seg_in = slots; run.seg_decay = nullptr;
   return launch_scans(run, nullptr, s);
+}
+
+int scan2_segments(int dtype, int C, int BH, int dk, int dv, int N) {
+  // the value columns of a cross-term scan workgroup (as scan_tile_v)
+  const int TV = (dtype != 0 && C == 64 && dv % 128 == 0) ? 128 : 64;
+  const long wgs = 2L * BH * (dk / 64) * (dv / TV);   // both scans
+  // at one workgroup per CU and more the scans stream near the copy rate (bf16) or near
+  // the fp32 matrix-unit rate (fp32), and a pass for the segment end states costs more
+  // than the parallelism gains
+  if (N < 16 || wgs >= 256) return 1;
+  int P = (int)(512 / wgs);   // these scans hold two workgroups per CU
+  P = P > 8 ? 8 : P;
+  P = P > N / 8 ? N / 8 : P;
+  return P < 2 ? 2 : P;
+}
+
+hipError_t launch_state_scan2_seg(const ScanArgs& a, const ScanArgs& b, float* slots, float* dec,
+                                  hipStream_t s) {
+  const int P = scan2_segments(a.dtype, a.C, a.BH, a.dk, a.dv, a.N);
+  if (P <= 1 || (a.nsteps > 0 && a.nsteps < a.N)) return launch_scans(a, &b, s);
+  if (!slots || (P > 2 && !dec)) return hipErrorInvalidValue;
+  const long slot = (long)(P - 1) * a.BH * a.dk * a.dv, dslot = (long)(P - 1) * a.BH * a.dk;
+  // segment end states of both scans, from zero (each first segment from its S_in), no
+  // stores and no cross terms
+  auto pre = [&](const ScanArgs& x, int k) {
+    ScanArgs y = x;
+    y.store = 0; y.states = nullptr; y.frag_states = false; y.cross = nullptr;
+    y.X2T = nullptr; y.Y2 = nullptr; y.S_out = slots + k * slot; y.seg_in = nullptr;
+    y.nseg = P - 1; y.seg_p = P; y.seg_decay = P > 2 ? dec + k * dslot : nullptr;
+    return y;
+  };
+  const ScanArgs pa = pre(a, 0), pb = pre(b, 1);
+  hipError_t e = launch_scans(pa, &pb, s);
+  if (e != hipSuccess) return e;
+  if ((e = launch_seg_combine(slots, dec, a.BH, a.dk, a.dv, P, s)) != hipSuccess) return e;
+  if ((e = launch_seg_combine(slots + slot, P > 2 ? dec + dslot : nullptr, a.BH, a.dk, a.dv, P,
+                              s)) != hipSuccess)
+    return e;
+  // every segment of both scans from its start state, with stores and cross terms
+  auto run = [&](const ScanArgs& x, int k) {
+    ScanArgs y = x;
+    y.nseg = P; y.seg_p = P; y.seg_in = slots + k * slot; y.seg_decay = nullptr;
+    return y;
+  };
+  const ScanArgs ra = run(a, 0), rb = run(b, 1);
+  return launch_scans(ra, &rb, s);
 }
 
 // Segment end states -> states at the segment starts (see launch_seg_combine): one
