@@ -623,13 +623,19 @@ def main():
         gsa_step = gsa_measure(L, nat, hip, dev, sp, cfg, args.gsa_slots, max(5, args.steps // 5))
 
     if args.copy_calibration:
+        # 1 GiB each: a bf16 fill (writes only), three copies (the scale points) and three
+        # max-reductions (reads only) of the same buffer, the latter two as checks of the
+        # copy's scale factors
         nbytes = 1 << 30
         a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1)
         b = torch.empty_like(a)
         for _ in range(3):
             b.copy_(a)
+        for _ in range(3):
+            a.amax()
         torch.cuda.synchronize()
-        print(f"[bench] copy calibration: 3 x {nbytes} B copies", file=sys.stderr, flush=True)
+        print(f"[bench] copy calibration: 3 x {nbytes} B copies, 3 x {nbytes} B reductions",
+              file=sys.stderr, flush=True)
 
     e = 2 if cfg.dtype == "bf16" else 4
     mode_s = args.state_mode

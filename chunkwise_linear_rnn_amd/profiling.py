@@ -8,7 +8,9 @@
 `counters` turns two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of
 `bench.py --copy-calibration` into HBM bytes per launch of one stage: the counters are
 scaled so that the plain 1 GiB device copy in the same run reads and writes exactly its
-size; the result is written as JSON (matched by bench.py against the kernel source hash).
+size, and the factors that a read-only and a write-only kernel of the same size would
+give are reported beside them as checks; the result is written as JSON (matched by
+bench.py against the kernel source hash).
 
     python -m chunkwise_linear_rnn_amd.profiling mfma <counter csv> <workload> "<command>"
 
@@ -120,10 +122,19 @@ def counters(fetch_csv, write_csv, copy_bytes, stage, workload, command, root):
     sw = copy_bytes / (1024.0 * (sum(copy_w) / len(copy_w)))
     fetch = sum(kf) / len(kf) * 1024.0 * sf
     write = sum(kw) / len(kw) * 1024.0 * sw
+    # checks of the two factors on kernels of the same size that only read (the bf16
+    # max-reductions) or only write (the bf16 fill of the copy's source); the cache flush
+    # of the timed steps fills uint8 and sums float32, so it matches neither
+    red_f = [v for n, v in f if "reduce" in n.lower() and "maxops" in n.lower()
+             and "bfloat16" in n.lower()]
+    fill_w = [v for n, v in w if "fill" in n.lower() and "bfloat16" in n.lower()]
+    check_f = copy_bytes / (1024.0 * (sum(red_f) / len(red_f))) if red_f else None
+    check_w = copy_bytes / (1024.0 * max(fill_w)) if fill_w else None
     return {"stage": stage, "workload": workload,
             "source_sha256": source_digest(stage, root),
             "fetch_kib_raw": sum(kf) / len(kf), "write_kib_raw": sum(kw) / len(kw),
             "copy_scale_fetch": sf, "copy_scale_write": sw,
+            "read_only_scale_fetch": check_f, "write_only_scale_write": check_w,
             "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
             "traffic_bytes_per_launch": fetch + write, "launches": len(kf), "command": command}
 

@@ -13,3 +13,40 @@ def test_stage_maps_cover_each_other():
     assert set(profiling.STAGE_KERNEL) == set(profiling.STAGE_SOURCE)
     for stage in profiling.STAGE_SYMBOL:
         assert stage in profiling.STAGE_KERNEL
+
+
+def _csv(path, counter, rows):
+    with open(path, "w") as f:
+        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+        for name, v in rows:
+            f.write(f'"{name}",{counter},{v}\n')
+
+
+def test_counter_scaling_and_its_checks(tmp_path):
+    """The copy sets the scale; a read-only reduction and a write-only fill of the same
+    size are reported as checks; the timed steps' cache flush (uint8 fill, float sum) and
+    the stage's own kernels do not count as calibration points."""
+    gib = 1 << 30
+    kib = gib / 1024.0
+    fetch = [("__amd_rocclr_copyBuffer", kib / 2), ("__amd_rocclr_copyBuffer", kib / 2),
+             ("void at::native::reduce_kernel<512, 1, at::native::ReduceOp<c10::BFloat16, "
+              "at::native::MaxOps<float>, unsigned int, c10::BFloat16, 4, 4> >", kib / 2.5),
+             ("void at::native::reduce_kernel<512, 1, at::native::ReduceOp<float, "
+              "at::native::func_wrapper_t<float, at::native::sum_functor<float> > > >", 7.0),
+             ("k_bwd_dqk_dv<__hip_bfloat16>", 1000.0), ("k_bwd_dqk_dv<__hip_bfloat16>", 3000.0)]
+    write = [("__amd_rocclr_copyBuffer", kib), ("__amd_rocclr_copyBuffer", kib),
+             ("void at::native::vectorized_elementwise_kernel<16, at::native::FillFunctor<"
+              "c10::BFloat16>, std::array<char*, 1ul> >", kib / 1.25),
+             ("void at::native::vectorized_elementwise_kernel<16, at::native::FillFunctor<"
+              "unsigned char>, std::array<char*, 1ul> >", kib * 9),
+             ("k_bwd_dqk_dv<__hip_bfloat16>", 500.0), ("k_bwd_dqk_dv<__hip_bfloat16>", 500.0)]
+    fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
+    _csv(fp, "FETCH_SIZE", fetch)
+    _csv(wp, "WRITE_SIZE", write)
+    r = profiling.counters(str(fp), str(wp), gib, "bwd_dqk_dv", "w", "cmd", ".")
+    assert abs(r["copy_scale_fetch"] - 2.0) < 1e-12 and abs(r["copy_scale_write"] - 1.0) < 1e-12
+    assert abs(r["read_only_scale_fetch"] - 2.5) < 1e-12
+    assert abs(r["write_only_scale_write"] - 1.25) < 1e-12
+    assert r["launches"] == 2
+    assert abs(r["fetch_bytes_per_launch"] - 2000.0 * 1024 * 2.0) < 1e-6
+    assert abs(r["write_bytes_per_launch"] - 500.0 * 1024) < 1e-6
