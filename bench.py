@@ -25,8 +25,8 @@ logsigmoid(x)/16 formed inside the kernels, the gradient returned for x), and
 `scalar_gate_step` fed scalar gates (one per token and head, [B, H, T]; the gradient is
 summed over the key dimension).
 
-`gsa_step` times Gated Slot Attention (float32, fwd + bwd, --gsa-slots memory slots,
-default 64) at the workload's B, H, T, dk, dv.
+`gsa_step` and `gsa_step_bf16` time Gated Slot Attention (fwd + bwd, float32 and bf16,
+--gsa-slots memory slots, default 64) at the workload's B, H, T, dk, dv.
 
 Every timed step runs after an untimed cache flush (a 512 MiB device write, then a
 512 MiB read that evicts the write's own dirty lines), with HIP events around the step
@@ -306,16 +306,25 @@ def counter_mfma(workload, state_mode):
     return out
 
 
-def gsa_measure(L, nat, hip, dev, sp, cfg, slots, steps):
-    """Gated Slot Attention fwd + bwd (gla_gsa_fwd, gla_gsa_bwd; float32) on the workload's
-    B, H, T, dk, dv with `slots` memory slots: ms per step from HIP events around `steps`
-    back-to-back steps after 2 warm-up steps.  Inputs: gla_inputs.generate_gsa."""
+def gsa_measure(L, nat, hip, dev, sp, cfg, slots, steps, dtype="f32"):
+    """Gated Slot Attention fwd + bwd (gla_gsa_fwd, gla_gsa_bwd; float32 or bf16) on the
+    workload's B, H, T, dk, dv with `slots` memory slots: ms per step from HIP events
+    around `steps` back-to-back steps after 2 warm-up steps.  Inputs:
+    gla_inputs.generate_gsa."""
+    import numpy as np
     import torch
     from gla_inputs import generate_gsa
-    c32 = cfg.replace(dtype="f32")
-    d = generate_gsa(c32, slots)
-    t = {n: torch.from_numpy(d[n + "_store"]).to(dev) for n in ("q", "k", "v", "dO", "log_alpha_slot")}
-    desc = nat.make_gsa_desc(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, slots, nat.F32)
+    cd = cfg.replace(dtype=dtype)
+    d = generate_gsa(cd, slots)
+
+    def up(n):
+        a = np.ascontiguousarray(d[n + "_store"])
+        if dtype == "f32":
+            return torch.from_numpy(a).to(dev)
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    t = {n: up(n) for n in ("q", "k", "v", "dO", "log_alpha_slot")}
+    desc = nat.make_gsa_desc(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, slots,
+                             nat.F32 if dtype == "f32" else nat.BF16)
     o = torch.empty_like(t["v"])
     grads = [torch.empty_like(t[n]) for n in ("q", "k", "v", "log_alpha_slot")]
     need_f = nat.gsa_workspace_bytes(desc, nat.PASS_FWD)
@@ -342,7 +351,7 @@ def gsa_measure(L, nat, hip, dev, sp, cfg, slots, steps):
     ms = hip.elapsed_ms(evs[0], evs[1]) / steps
     hip.destroy(evs)
     return {"ms_per_step": ms, "value": cfg.B * cfg.T / (ms * 1e-3), "unit": "tokens/s",
-            "slots": slots, "dtype": "f32", "steps": steps}
+            "slots": slots, "dtype": dtype, "steps": steps}
 
 
 def decode_measure(L, nat, hip, dev, sp, H, dk, dv, batches=(4, 64), calls=200):
@@ -433,10 +442,12 @@ def main():
     if args.gsa_only:
         L = nat.lib()
         sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-        rec = gsa_measure(L, nat, HipEvents(), dev, sp, cfg, args.gsa_slots, args.steps)
+        hip_ = HipEvents()
+        rec = gsa_measure(L, nat, hip_, dev, sp, cfg, args.gsa_slots, args.steps)
         rec.update({"metric": "Gated Slot Attention fwd+bwd tokens/s", "n_gpus": 1,
                     "config": {"workload": cfg.name + f"_gsa{args.gsa_slots}", "B": cfg.B,
                                "H": cfg.H, "T": cfg.T, "dk": cfg.dk, "dv": cfg.dv}})
+        rec["bf16"] = gsa_measure(L, nat, hip_, dev, sp, cfg, args.gsa_slots, args.steps, "bf16")
         print(json.dumps(rec), flush=True)
         return
     print(f"[bench] generating {cfg}", file=sys.stderr, flush=True)
@@ -617,10 +628,12 @@ def main():
         dla_s = torch.empty_like(la_s)
         scalar_fe = time_variant(desc_s, la_s, dla_s, "scalar gates")
 
-    # Gated Slot Attention (float32) at the workload's head shape: one fwd + bwd step
-    gsa_step = None
+    # Gated Slot Attention (float32 and bf16) at the workload's head shape: fwd + bwd steps
+    gsa_step = gsa_step_h = None
     if not args.no_decode and not fwd_only:
         gsa_step = gsa_measure(L, nat, hip, dev, sp, cfg, args.gsa_slots, max(5, args.steps // 5))
+        gsa_step_h = gsa_measure(L, nat, hip, dev, sp, cfg, args.gsa_slots,
+                                 max(5, args.steps // 5), "bf16")
 
     if args.copy_calibration:
         # 1 GiB each: a bf16 fill (writes only), three copies (the scale points) and three
@@ -708,6 +721,7 @@ def main():
         "gate_logits_step": gate_fe,
         "scalar_gate_step": scalar_fe,
         "gsa_step": gsa_step,
+        "gsa_step_bf16": gsa_step_h,
     }
     for arr in evf + evb + ev_dom + ev_step:
         hip.destroy(arr)

@@ -524,6 +524,10 @@ gla_status_t gla_decode(const gla_desc_t* d, const void* q, const void* k, const
 // dlog_alpha2), ds = softmax backward, the intra-chunk kernel on (ds, log_alpha) ->
 // (ds * e^g)^T, the reverse scan with values q -> dS1, k_vg_bwd -> dq, dk, dw1 and the
 // gate terms, the closed-form gate scan, and dlog_alpha = dla1 + dla2 - (dw1 + dw2) e^la.
+// bf16: the first pass runs on fp32 copies of q, k and log_alpha; p and w go to the
+// second pass (the layer's bf16 path, recompute forward) rounded to bf16, its gradients
+// come back in bf16; the softmax backward, the first pass's backward and the gate
+// combination stay fp32; dq, dk, dlog_alpha are rounded to bf16 at the end.
 // =====================================================================================
 namespace {
 
@@ -531,13 +535,20 @@ struct GsaPlan {
   size_t w = 0, g2 = 0, KhT = 0, eg = 0, S1 = 0, s = 0, p = 0, ws2 = 0, dp = 0, dw2 = 0,
          dla2 = 0, ds = 0, QhT = 0, dS1 = 0, dw1 = 0, Dloc = 0, tot = 0, dla1 = 0, sslots = 0,
          sdec = 0, total = 0;
+  // bf16 only: fp32 copies of q, k, log_alpha; bf16 copies of p and w; the second pass's
+  // bf16 gradients for p, w and log_alpha; dq and dk in fp32 before the final rounding
+  size_t q32 = 0, k32 = 0, la32 = 0, p16 = 0, w16 = 0, dp16 = 0, dw2h = 0, dla2h = 0,
+         dq32 = 0, dk32 = 0;
   size_t ws2_bytes = 0;
 };
 
 gla_desc_t gsa_layer2(const gla_gsa_desc_t* d) {
   gla_desc_t x{};
   x.B = d->B; x.H = d->H; x.T = d->T; x.dk = d->slots; x.dv = d->dv; x.chunk = 64;
-  x.subchunk = 16; x.dtype = GLA_F32; x.state_mode = GLA_STATES_MATERIALIZED;
+  x.subchunk = 16; x.dtype = d->dtype;
+  // fp32: the materialized forward (the fused kernel reads fp32 operands from memory);
+  // bf16: the layer's fused recompute forward
+  x.state_mode = d->dtype == GLA_BF16 ? GLA_STATES_RECOMPUTE : GLA_STATES_MATERIALIZED;
   x.gate = GLA_GATE_LOG_ALPHA; x.gate_tau = 1.f; x.gate_shape = GLA_GATE_PER_KEY;
   return x;
 }
@@ -560,9 +571,14 @@ GsaPlan gsa_plan(const gla_gsa_desc_t* d, int pass) {
     off += align_up(bytes);
     return at;
   };
-  const size_t TM = BH * T * m * 4;
+  const size_t TM = BH * T * m * 4, TK = BH * T * dk * 4;
+  const bool h = d->dtype == GLA_BF16;
   p.w = take(TM); p.g2 = take(TM); p.KhT = take(BH * N * m * 64 * 4); p.eg = take(BH * N * m * 4);
   p.S1 = take(BH * N * m * dk * 4); p.s = take(TM); p.p = take(TM);
+  if (h) {
+    p.q32 = take(TK); p.k32 = take(TK); p.la32 = take(TM); p.p16 = take(TM / 2);
+    p.w16 = take(TM / 2);
+  }
   // the key-slot scan in segments (few heads): states at the segment starts, decay products
   const int P = gla::scan_segments(gsa_slot_scan(d));
   if (P > 1) p.sslots = take((size_t)(P - 1) * BH * m * dk * 4);
@@ -571,7 +587,13 @@ GsaPlan gsa_plan(const gla_gsa_desc_t* d, int pass) {
   const size_t b2 = plan_of(&l2, pass == GLA_PASS_BWD ? GLA_PASS_BWD : GLA_PASS_FWD).total;
   p.ws2 = take(b2); p.ws2_bytes = b2;
   if (pass == GLA_PASS_BWD) {
-    p.dp = take(TM); p.dw2 = take(TM); p.dla2 = take(TM); p.ds = take(TM);
+    p.dp = take(TM); p.ds = take(TM);
+    if (h) {
+      p.dp16 = take(TM / 2); p.dw2h = take(TM / 2); p.dla2h = take(TM / 2);
+      p.dq32 = take(TK); p.dk32 = take(TK);
+    } else {
+      p.dw2 = take(TM); p.dla2 = take(TM);
+    }
     p.QhT = take(BH * N * m * 64 * 4); p.dS1 = take(BH * N * m * dk * 4); p.dw1 = take(TM);
     p.Dloc = take(TM); p.tot = take(BH * N * m * 4); p.dla1 = take(TM);
   }
@@ -579,12 +601,22 @@ GsaPlan gsa_plan(const gla_gsa_desc_t* d, int pass) {
   return p;
 }
 
-struct GsaFwd {   // the forward up to p (and o when asked)
-  gla_status_t run(const gla_gsa_desc_t* d, const float* q, const float* k, const float* v,
-                   const float* la, float* o, char* w, const GsaPlan& p, hipStream_t s) {
+struct GsaFwd {   // the forward up to p (bf16: and its bf16 copies), and o when asked
+  gla_status_t run(const gla_gsa_desc_t* d, const void* q_in, const void* k_in, const void* v,
+                   const void* la_in, void* o, char* w, const GsaPlan& p, hipStream_t s) {
     const int BH = d->B * d->H, T = d->T, m = d->slots, DK = d->dk, N = (T + 63) / 64;
+    const bool h = d->dtype == GLA_BF16;
+    const long TK = (long)BH * T * DK, TM = (long)BH * T * m;
     gla_status_t rs;
-    if ((rs = dev(gla::launch_gsa_w(la, (float*)(w + p.w), (long)BH * T * m, s))) != GLA_OK) return rs;
+    const float *q = (const float*)q_in, *k = (const float*)k_in, *la = (const float*)la_in;
+    if (h) {   // the first pass in fp32
+      if ((rs = dev(gla::launch_cast_bf16_f32(q_in, (float*)(w + p.q32), TK, s))) != GLA_OK) return rs;
+      if ((rs = dev(gla::launch_cast_bf16_f32(k_in, (float*)(w + p.k32), TK, s))) != GLA_OK) return rs;
+      if ((rs = dev(gla::launch_cast_bf16_f32(la_in, (float*)(w + p.la32), TM, s))) != GLA_OK)
+        return rs;
+      q = (const float*)(w + p.q32); k = (const float*)(w + p.k32); la = (const float*)(w + p.la32);
+    }
+    if ((rs = dev(gla::launch_gsa_w(la, (float*)(w + p.w), TM, s))) != GLA_OK) return rs;
     gla::IntraArgs ia{};
     ia.dtype = 0; ia.C = 64; ia.BH = BH; ia.T = T; ia.dk = m; ia.N = N; ia.want_A = false;
     ia.q = w + p.w; ia.k = w + p.w; ia.la = la; ia.g = nullptr;
@@ -605,10 +637,16 @@ struct GsaFwd {   // the forward up to p (and o when asked)
     if ((rs = dev(gla::launch_softmax_rows((const float*)(w + p.s), (float*)(w + p.p),
                                            (long)BH * T, m, s))) != GLA_OK)
       return rs;
+    if (h) {   // the second pass's queries and keys in bf16
+      if ((rs = dev(gla::launch_cast_f32_bf16((const float*)(w + p.p), w + p.p16, TM, s))) != GLA_OK)
+        return rs;
+      if ((rs = dev(gla::launch_cast_f32_bf16((const float*)(w + p.w), w + p.w16, TM, s))) != GLA_OK)
+        return rs;
+    }
     if (!o) return GLA_OK;
     const gla_desc_t l2 = gsa_layer2(d);
-    return gla_chunk_fwd(&l2, w + p.p, w + p.w, v, la, nullptr, o, nullptr, w + p.ws2, p.ws2_bytes,
-                         s);
+    return gla_chunk_fwd(&l2, w + (h ? p.p16 : p.p), w + (h ? p.w16 : p.w), v, la_in, nullptr, o,
+                         nullptr, w + p.ws2, p.ws2_bytes, s);
   }
 };
 
@@ -628,7 +666,6 @@ gla_status_t gla_gsa_validate(const gla_gsa_desc_t* d) {
   if (d->B < 0 || d->H < 0 || d->T < 0 || d->dk < 0 || d->dv < 0 || d->slots < 0)
     return GLA_ERR_INVALID_ARG;
   if (d->dtype != GLA_F32 && d->dtype != GLA_BF16) return GLA_ERR_INVALID_ARG;
-  if (d->dtype != GLA_F32) return GLA_ERR_UNSUPPORTED;
   if (d->dk < 64 || d->dk > 256 || d->dk % 64 != 0) return GLA_ERR_UNSUPPORTED;
   if (d->slots < 64 || d->slots > 256 || d->slots % 64 != 0) return GLA_ERR_UNSUPPORTED;
   if (d->dv < 64 || d->dv > 1024 || d->dv % 64 != 0) return GLA_ERR_UNSUPPORTED;
@@ -659,8 +696,7 @@ gla_status_t gla_gsa_fwd(const gla_gsa_desc_t* d, const void* q, const void* k, 
   const GsaPlan p = gsa_plan(d, GLA_PASS_FWD);
   if (!ws || ws_bytes < p.total) return GLA_ERR_WORKSPACE;
   GsaFwd f;
-  return f.run(d, (const float*)q, (const float*)k, (const float*)v, (const float*)log_alpha,
-               (float*)o, (char*)ws, p, (hipStream_t)stream);
+  return f.run(d, q, k, v, log_alpha, o, (char*)ws, p, (hipStream_t)stream);
 }
 
 gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* d, const void* q, const void* k, const void* v,
@@ -678,17 +714,24 @@ gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* d, const void* q, const void* k, 
   if (!ws || ws_bytes < p.total) return GLA_ERR_WORKSPACE;
   char* w = (char*)ws;
   hipStream_t s = (hipStream_t)stream;
-  const float* la = (const float*)log_alpha;
+  const bool h = d->dtype == GLA_BF16;
   const int BH = d->B * d->H, T = d->T, m = d->slots, DK = d->dk, N = (T + 63) / 64;
-  const long TM = (long)BH * T * m;
+  const long TM = (long)BH * T * m, TK = (long)BH * T * DK;
   GsaFwd f;
-  gla_status_t rs = f.run(d, (const float*)q, (const float*)k, (const float*)v, la, nullptr, w, p, s);
+  gla_status_t rs = f.run(d, q, k, v, log_alpha, nullptr, w, p, s);
   if (rs != GLA_OK) return rs;
+  // the first pass's operands in fp32 (bf16: the copies the forward made)
+  const float* la = h ? (const float*)(w + p.la32) : (const float*)log_alpha;
+  const float* q32 = h ? (const float*)(w + p.q32) : (const float*)q;
+  const float* k32 = h ? (const float*)(w + p.k32) : (const float*)k;
   // second pass backward: gradients for p, w (as keys), v and log_alpha
   const gla_desc_t l2 = gsa_layer2(d);
-  rs = gla_chunk_bwd(&l2, w + p.p, w + p.w, v, la, nullptr, dO, nullptr, w + p.dp, w + p.dw2, dv,
-                     w + p.dla2, nullptr, w + p.ws2, p.ws2_bytes, s);
+  rs = gla_chunk_bwd(&l2, w + (h ? p.p16 : p.p), w + (h ? p.w16 : p.w), v, log_alpha, nullptr, dO,
+                     nullptr, w + (h ? p.dp16 : p.dp), w + (h ? p.dw2h : p.dw2), dv,
+                     w + (h ? p.dla2h : p.dla2), nullptr, w + p.ws2, p.ws2_bytes, s);
   if (rs != GLA_OK) return rs;
+  if (h && (rs = dev(gla::launch_cast_bf16_f32(w + p.dp16, (float*)(w + p.dp), TM, s))) != GLA_OK)
+    return rs;
   if ((rs = dev(gla::launch_softmax_bwd((const float*)(w + p.p), (const float*)(w + p.dp),
                                         (float*)(w + p.ds), (long)BH * T, m, s))) != GLA_OK)
     return rs;
@@ -699,7 +742,7 @@ gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* d, const void* q, const void* k, 
   ia.eg = (float*)(w + p.eg); ia.gate = gla::GateFn{0, 1.f};
   if ((rs = dev(gla::launch_intra(ia, s))) != GLA_OK) return rs;
   gla::ScanArgs ra = gsa_slot_scan(d);
-  ra.reverse = true; ra.XT = w + p.QhT; ra.Y = q; ra.eg = (const float*)(w + p.eg);
+  ra.reverse = true; ra.XT = w + p.QhT; ra.Y = q32; ra.eg = (const float*)(w + p.eg);
   ra.states = w + p.dS1;
   // in segments like the forward key-slot scan (same shape: the same workspace slots)
   const int P = gla::scan_segments(ra);
@@ -707,10 +750,12 @@ gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* d, const void* q, const void* k, 
                                            P > 2 ? (float*)(w + p.sdec) : nullptr, s))) !=
       GLA_OK)
     return rs;
-  if ((rs = dev(gla::launch_vg_bwd((const float*)q, (const float*)k, (const float*)(w + p.w),
+  float* dq32 = h ? (float*)(w + p.dq32) : (float*)dq;
+  float* dk32 = h ? (float*)(w + p.dk32) : (float*)dk;
+  if ((rs = dev(gla::launch_vg_bwd(q32, k32, (const float*)(w + p.w),
                                    (const float*)(w + p.g2), (const float*)(w + p.ds),
                                    (const float*)(w + p.s), (const float*)(w + p.S1),
-                                   (const float*)(w + p.dS1), (float*)dq, (float*)dk,
+                                   (const float*)(w + p.dS1), dq32, dk32,
                                    (float*)(w + p.dw1), (float*)(w + p.Dloc), (float*)(w + p.tot),
                                    BH, T, DK, m, s))) != GLA_OK)
     return rs;
@@ -718,9 +763,16 @@ gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* d, const void* q, const void* k, 
                                       nullptr, la, gla::GateFn{0, 1.f}, w + p.dla1, nullptr, BH, T,
                                       m, 64, s))) != GLA_OK)
     return rs;
-  return dev(gla::launch_gsa_combine(la, (const float*)(w + p.dla1), (const float*)(w + p.dla2),
-                                     (const float*)(w + p.dw1), (const float*)(w + p.dw2),
-                                     (float*)dlog_alpha, TM, s));
+  if (!h)
+    return dev(gla::launch_gsa_combine(la, (const float*)(w + p.dla1), (const float*)(w + p.dla2),
+                                       (const float*)(w + p.dw1), (const float*)(w + p.dw2),
+                                       (float*)dlog_alpha, TM, s));
+  if ((rs = dev(gla::launch_gsa_combine_bf16(la, (const float*)(w + p.dla1), w + p.dla2h,
+                                             (const float*)(w + p.dw1), w + p.dw2h, dlog_alpha,
+                                             TM, s))) != GLA_OK)
+    return rs;
+  if ((rs = dev(gla::launch_cast_f32_bf16(dq32, dq, TK, s))) != GLA_OK) return rs;
+  return dev(gla::launch_cast_f32_bf16(dk32, dk, TK, s));
 }
 
 }  // extern "C"

@@ -216,5 +216,12 @@ hipError_t launch_softmax_bwd(const float* p, const float* dp, float* ds, long n
 hipError_t launch_gsa_combine(const float* la, const float* dla1, const float* dla2,
                               const float* dw1, const float* dw2, float* dla, long n,
                               hipStream_t s);
+// bf16 Gated Slot Attention (bf16 pointers as void*): the combination with the second
+// pass's bf16 gradients dla2, dw2 and a bf16 dla; element conversions bf16 <-> fp32.
+hipError_t launch_gsa_combine_bf16(const float* la, const float* dla1, const void* dla2,
+                                   const float* dw1, const void* dw2, void* dla, long n,
+                                   hipStream_t s);
+hipError_t launch_cast_bf16_f32(const void* x, float* y, long n, hipStream_t s);
+hipError_t launch_cast_f32_bf16(const float* x, void* y, long n, hipStream_t s);
 
 }  // namespace gla

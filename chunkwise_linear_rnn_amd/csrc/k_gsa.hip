@@ -563,6 +563,26 @@ __global__ __launch_bounds__(kThreads) void k_gsa_combine(const float* __restric
     dla[i] = dla1[i] + dla2[i] - (dw1[i] + dw2[i]) * __expf(la[i]);
 }
 
+// bf16 Gated Slot Attention: the combination above with the second pass's gradients for
+// w and log_alpha in bf16 (the layer's bf16 outputs) and dlog_alpha written in bf16.
+__global__ __launch_bounds__(kThreads) void k_gsa_combine_bf16(const float* __restrict__ la,
+                                                               const float* __restrict__ dla1,
+                                                               const bf16* __restrict__ dla2,
+                                                               const float* __restrict__ dw1,
+                                                               const bf16* __restrict__ dw2,
+                                                               bf16* __restrict__ dla, long n) {
+  for (long i = blockIdx.x * (long)kThreads + threadIdx.x; i < n; i += (long)gridDim.x * kThreads)
+    dla[i] = (bf16)(dla1[i] + (float)dla2[i] - (dw1[i] + (float)dw2[i]) * __expf(la[i]));
+}
+
+// Element conversions between bf16 and fp32 (round to nearest even towards bf16).
+template <typename S, typename D>
+__global__ __launch_bounds__(kThreads) void k_cast(const S* __restrict__ x, D* __restrict__ y,
+                                                   long n) {
+  for (long i = blockIdx.x * (long)kThreads + threadIdx.x; i < n; i += (long)gridDim.x * kThreads)
+    y[i] = (D)x[i];
+}
+
 // ---------------------------------------------------------------------------------
 static unsigned grid1d(long n) {
   const long b = (n + kThreads - 1) / kThreads;
@@ -619,6 +639,29 @@ hipError_t launch_gsa_combine(const float* la, const float* dla1, const float* d
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(k_gsa_combine, dim3(grid1d(n)), dim3(kThreads), 0, s, la, dla1, dla2, dw1,
                      dw2, dla, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_gsa_combine_bf16(const float* la, const float* dla1, const void* dla2,
+                                   const float* dw1, const void* dw2, void* dla, long n,
+                                   hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gsa_combine_bf16, dim3(grid1d(n)), dim3(kThreads), 0, s, la, dla1,
+                     (const bf16*)dla2, dw1, (const bf16*)dw2, (bf16*)dla, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16_f32(const void* x, float* y, long n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_cast<bf16, float>), dim3(grid1d(n)), dim3(kThreads), 0, s,
+                     (const bf16*)x, y, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_f32_bf16(const float* x, void* y, long n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_cast<float, bf16>), dim3(grid1d(n)), dim3(kThreads), 0, s, x,
+                     (bf16*)y, n);
   return hipGetLastError();
 }
 

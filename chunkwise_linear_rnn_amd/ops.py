@@ -253,23 +253,24 @@ def gla(q, k, v, log_alpha, S0=None, chunk=64, subchunk=16, state_mode="recomput
 def _gsa_desc(q, v, log_alpha):
     if q.dim() != 4 or v.dim() != 4 or log_alpha.dim() != 4:
         raise ValueError("q, v and log_alpha must be [B, H, T, d]")
-    if q.dtype != torch.float32:
-        raise ValueError("Gated Slot Attention is float32 in this build")
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("Gated Slot Attention takes float32 or bfloat16 tensors")
     B, H, T, dk = q.shape
-    return make_gsa_desc(B, H, T, dk, v.shape[-1], log_alpha.shape[-1], F32)
+    return make_gsa_desc(B, H, T, dk, v.shape[-1], log_alpha.shape[-1],
+                         F32 if q.dtype == torch.float32 else BF16)
 
 
 def gsa_fwd(q, k, v, log_alpha, *, workspace=None):
     """o of Gated Slot Attention: key/value slots [slots, d] forgotten by the per-slot
     gates exp(log_alpha) [B, H, T, slots], written with weight 1 - alpha, read by
-    softmax(slots_k q) (float32)."""
+    softmax(slots_k q) (float32, or bfloat16 with the first pass in fp32)."""
     desc = _gsa_desc(q, v, log_alpha)
     dev = q.device
     B, H, T, dk, dv, m = desc.B, desc.H, desc.T, desc.dk, desc.dv, desc.slots
     for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)), (v, "v", (B, H, T, dv)),
                       (log_alpha, "log_alpha", (B, H, T, m))):
-        _check(t, n, shp, torch.float32, dev)
-    o = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+        _check(t, n, shp, q.dtype, dev)
+    o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
     ws, need = _ws_buffer(gsa_workspace_bytes(desc, PASS_FWD), dev, workspace)
     _call("gla_gsa_fwd", lib().gla_gsa_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                            _ptr(log_alpha), _ptr(o), _ptr(ws), need, _stream(dev)))
@@ -283,7 +284,7 @@ def gsa_bwd(q, k, v, log_alpha, dO, *, workspace=None):
     B, H, T, dk, dv, m = desc.B, desc.H, desc.T, desc.dk, desc.dv, desc.slots
     for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)), (v, "v", (B, H, T, dv)),
                       (log_alpha, "log_alpha", (B, H, T, m)), (dO, "dO", (B, H, T, dv))):
-        _check(t, n, shp, torch.float32, dev)
+        _check(t, n, shp, q.dtype, dev)
     dq, dk_, dv_, dla = (torch.empty_like(x) for x in (q, k, v, log_alpha))
     ws, need = _ws_buffer(gsa_workspace_bytes(desc, PASS_BWD), dev, workspace)
     _call("gla_gsa_bwd", lib().gla_gsa_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),

@@ -220,8 +220,12 @@ gla_status_t gla_decode(const gla_desc_t* desc, const void* q, const void* k, co
  *     Kt_t = diag(alpha_t) Kt_{t-1} + w_t^T k_t,   Vt_t = diag(alpha_t) Vt_{t-1} + w_t^T v_t,
  *     o_t  = softmax(Kt_t q_t)^T Vt_t     (softmax over the m slots; Kt, Vt start at zero)
  *
- * q, k [B,H,T,dk], v, o, dO, dv [B,H,T,dv], log_alpha, dlog_alpha [B,H,T,slots], all float32
- * (bf16 is GLA_ERR_UNSUPPORTED in this build), contiguous, 16-byte aligned, caller-owned.
+ * q, k [B,H,T,dk], v, o, dO, dv [B,H,T,dv], log_alpha, dlog_alpha [B,H,T,slots], all of
+ * element type desc->dtype, contiguous, 16-byte aligned, caller-owned.  GLA_F32: fp32
+ * throughout.  GLA_BF16: the first pass (slot scores) in fp32 on fp32 copies of q, k and
+ * log_alpha; softmax(scores) and 1 - alpha enter the second pass (the layer's bf16 path)
+ * rounded to bf16, whose gradients return in bf16; the softmax backward, the first pass's
+ * backward and the gate-gradient sum in fp32; outputs rounded to nearest even.
  * Scratch comes from `ws` (gla_gsa_workspace_bytes); no state is carried in or out.
  * Supported: dk and slots in {64, 128, 192, 256}, dv a multiple of 64 up to 1024,
  * B*H <= 65535, B*H*T < 2^31; B*H*T == 0 is a no-op.  Errors as for the layer's entry
@@ -230,7 +234,7 @@ typedef struct {
   int32_t B, H, T;
   int32_t dk, dv;
   int32_t slots;   /* m, the number of memory slots */
-  int32_t dtype;   /* gla_dtype_t; GLA_F32 */
+  int32_t dtype;   /* gla_dtype_t: GLA_F32 or GLA_BF16 */
 } gla_gsa_desc_t;
 
 gla_status_t gla_gsa_validate(const gla_gsa_desc_t* desc);

@@ -175,7 +175,7 @@ def test_gsa_descriptor_validation(native):
     G = native.make_gsa_desc
     L = native.lib()
     assert L.gla_gsa_validate(ctypes.byref(G(2, 2, 300, 128, 192, 64))) == 0
-    assert L.gla_gsa_validate(ctypes.byref(G(2, 2, 300, 128, 192, 64, native.BF16))) == 2
+    assert L.gla_gsa_validate(ctypes.byref(G(2, 2, 300, 128, 192, 64, native.BF16))) == 0
     assert L.gla_gsa_validate(ctypes.byref(G(2, 2, 300, 128, 192, 64, 7))) == 1
     for bad in ((1, 1, 64, 96, 64, 64), (1, 1, 64, 64, 64, 32), (1, 1, 64, 64, 96, 64),
                 (1, 1, 64, 64, 64, 320)):
@@ -185,6 +185,10 @@ def test_gsa_descriptor_validation(native):
     assert native.gsa_workspace_bytes(G(0, 2, 64, 64, 64, 64)) == 0
     assert native.gsa_workspace_bytes(G(1, 2, 64, 64, 64, 64), native.PASS_BWD) > \
         native.gsa_workspace_bytes(G(1, 2, 64, 64, 64, 64), native.PASS_FWD) > 0
+    # bf16: fp32 copies for the first pass, bf16 copies and gradients for the second
+    hb = G(1, 2, 64, 64, 64, 64, native.BF16)
+    assert native.gsa_workspace_bytes(hb, native.PASS_BWD) > \
+        native.gsa_workspace_bytes(hb, native.PASS_FWD) > 0
     p = ctypes.c_void_p(16)
     # a missing workspace is reported before any launch
     assert L.gla_gsa_fwd(ctypes.byref(G(1, 1, 64, 64, 64, 64)), p, p, p, p, p, None, 0, None) == 3

@@ -1,7 +1,7 @@
-"""GPU parity of Gated Slot Attention (gla_gsa_fwd / gla_gsa_bwd, float32) against the
-oracle's slot recurrence and its fp64 autograd gradient (oracle/gsa.py): ragged chunks,
-128 slots, a single token, the empty problem, and the 1.3B head shape with 64 slots
-(forward on a sampled head at full length, backward on a sampled head of a shorter run)."""
+"""GPU parity of Gated Slot Attention (gla_gsa_fwd / gla_gsa_bwd, float32 and bfloat16)
+against the oracle's slot recurrence and its fp64 autograd gradient (oracle/gsa.py) on the
+same (rounded) inputs: ragged chunks, 128 slots, a single token, a long thin head, the
+empty problem, and the 1.3B head shape with 64 slots (sampled heads)."""
 import numpy as np
 import pytest
 
@@ -25,8 +25,8 @@ def gla():
     return m
 
 
-def _dev(d):
-    return {n: to_dev(d[n + "_store"], "f32", DEV) for n in ("q", "k", "v", "dO", "log_alpha_slot")}
+def _dev(d, dt="f32"):
+    return {n: to_dev(d[n + "_store"], dt, DEV) for n in ("q", "k", "v", "dO", "log_alpha_slot")}
 
 
 CASES = [
@@ -58,6 +58,47 @@ def test_gsa_fwd_bwd_small(gla, case):
             ref = gsa.gsa_bwd(*a, d["dO"][b, h])
             for kname, t, r in zip(("dq", "dk", "dv", "dla"), g, ref):
                 check(f"{kname}[{b},{h}]", host(t)[b, h], r, "f32")
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_gsa_bf16_small(gla, case):
+    """bf16 inputs and outputs (first pass in fp32, second pass on the layer's bf16 path),
+    against the oracle on the same bf16-rounded inputs, at the bf16 tolerances."""
+    name, B, H, T, dk, dv, m, gm = case
+    cfg = GlaConfig(name=name, dtype="bf16", B=B, H=H, T=T, dk=dk, dv=dv, chunk=64,
+                    gate_mean=gm)
+    say(f"[gsa bf16] {cfg} slots={m}")
+    d = generate_gsa(cfg, m)
+    x = _dev(d, "bf16")
+    o = gla.gsa_fwd(x["q"], x["k"], x["v"], x["log_alpha_slot"])
+    g = gla.gsa_bwd(x["q"], x["k"], x["v"], x["log_alpha_slot"], x["dO"])
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16 and all(t.dtype == torch.bfloat16 for t in g)
+    for b in range(B):
+        for h in range(H):
+            a = (d["q"][b, h], d["k"][b, h], d["v"][b, h], d["log_alpha_slot"][b, h])
+            check(f"o[{b},{h}]", host(o)[b, h], gsa.gsa_fwd(*a), "bf16")
+            ref = gsa.gsa_bwd(*a, d["dO"][b, h])
+            for kname, t, r in zip(("dq", "dk", "dv", "dla"), g, ref):
+                check(f"{kname}[{b},{h}]", host(t)[b, h], r, "bf16")
+
+
+def test_gsa_bf16_full_size_sampled(gla):
+    """bf16 at B=4, H=4, dk=256, dv=512, 64 slots: forward and backward of two sampled heads
+    of a T=512 run."""
+    cfg = GlaConfig(name="gsa1p3b_bf16_t512", dtype="bf16", B=4, H=4, T=512, dk=256, dv=512,
+                    chunk=64)
+    say(f"[gsa bf16] {cfg}")
+    d = generate_gsa(cfg, 64)
+    x = _dev(d, "bf16")
+    o = gla.gsa_fwd(x["q"], x["k"], x["v"], x["log_alpha_slot"])
+    g = gla.gsa_bwd(x["q"], x["k"], x["v"], x["log_alpha_slot"], x["dO"])
+    torch.cuda.synchronize()
+    for b, h in ((0, 1), (3, 2)):
+        a = (d["q"][b, h], d["k"][b, h], d["v"][b, h], d["log_alpha_slot"][b, h])
+        check(f"o[{b},{h}]", host(o)[b, h], gsa.gsa_fwd(*a), "bf16")
+        for kname, t, r in zip(("dq", "dk", "dv", "dla"), g, gsa.gsa_bwd(*a, d["dO"][b, h])):
+            check(f"{kname}[{b},{h}]", host(t)[b, h], r, "bf16")
 
 
 def test_gsa_empty_is_noop(gla):
