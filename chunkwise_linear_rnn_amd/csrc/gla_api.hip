@@ -536,9 +536,8 @@ struct GsaPlan {
          dla2 = 0, ds = 0, QhT = 0, dS1 = 0, dw1 = 0, Dloc = 0, tot = 0, dla1 = 0, sslots = 0,
          sdec = 0, total = 0;
   // bf16 only: fp32 copies of q, k, log_alpha; bf16 copies of p and w; the second pass's
-  // bf16 gradients for p, w and log_alpha; dq and dk in fp32 before the final rounding
-  size_t q32 = 0, k32 = 0, la32 = 0, p16 = 0, w16 = 0, dp16 = 0, dw2h = 0, dla2h = 0,
-         dq32 = 0, dk32 = 0;
+  // bf16 gradients for p, w and log_alpha
+  size_t q32 = 0, k32 = 0, la32 = 0, p16 = 0, w16 = 0, dp16 = 0, dw2h = 0, dla2h = 0;
   size_t ws2_bytes = 0;
 };
 
@@ -590,7 +589,6 @@ GsaPlan gsa_plan(const gla_gsa_desc_t* d, int pass) {
     p.dp = take(TM); p.ds = take(TM);
     if (h) {
       p.dp16 = take(TM / 2); p.dw2h = take(TM / 2); p.dla2h = take(TM / 2);
-      p.dq32 = take(TK); p.dk32 = take(TK);
     } else {
       p.dw2 = take(TM); p.dla2 = take(TM);
     }
@@ -716,7 +714,7 @@ gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* d, const void* q, const void* k, 
   hipStream_t s = (hipStream_t)stream;
   const bool h = d->dtype == GLA_BF16;
   const int BH = d->B * d->H, T = d->T, m = d->slots, DK = d->dk, N = (T + 63) / 64;
-  const long TM = (long)BH * T * m, TK = (long)BH * T * DK;
+  const long TM = (long)BH * T * m;
   GsaFwd f;
   gla_status_t rs = f.run(d, q, k, v, log_alpha, nullptr, w, p, s);
   if (rs != GLA_OK) return rs;
@@ -750,12 +748,10 @@ gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* d, const void* q, const void* k, 
                                            P > 2 ? (float*)(w + p.sdec) : nullptr, s))) !=
       GLA_OK)
     return rs;
-  float* dq32 = h ? (float*)(w + p.dq32) : (float*)dq;
-  float* dk32 = h ? (float*)(w + p.dk32) : (float*)dk;
   if ((rs = dev(gla::launch_vg_bwd(q32, k32, (const float*)(w + p.w),
                                    (const float*)(w + p.g2), (const float*)(w + p.ds),
                                    (const float*)(w + p.s), (const float*)(w + p.S1),
-                                   (const float*)(w + p.dS1), dq32, dk32,
+                                   (const float*)(w + p.dS1), dq, dk, h ? 1 : 0,
                                    (float*)(w + p.dw1), (float*)(w + p.Dloc), (float*)(w + p.tot),
                                    BH, T, DK, m, s))) != GLA_OK)
     return rs;
@@ -767,12 +763,9 @@ gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* d, const void* q, const void* k, 
     return dev(gla::launch_gsa_combine(la, (const float*)(w + p.dla1), (const float*)(w + p.dla2),
                                        (const float*)(w + p.dw1), (const float*)(w + p.dw2),
                                        (float*)dlog_alpha, TM, s));
-  if ((rs = dev(gla::launch_gsa_combine_bf16(la, (const float*)(w + p.dla1), w + p.dla2h,
-                                             (const float*)(w + p.dw1), w + p.dw2h, dlog_alpha,
-                                             TM, s))) != GLA_OK)
-    return rs;
-  if ((rs = dev(gla::launch_cast_f32_bf16(dq32, dq, TK, s))) != GLA_OK) return rs;
-  return dev(gla::launch_cast_f32_bf16(dk32, dk, TK, s));
+  return dev(gla::launch_gsa_combine_bf16(la, (const float*)(w + p.dla1), w + p.dla2h,
+                                          (const float*)(w + p.dw1), w + p.dw2h, dlog_alpha, TM,
+                                          s));
 }
 
 }  // extern "C"

@@ -118,7 +118,7 @@ int scan_segments(const ScanArgs& a);
 hipError_t launch_state_scan_seg(const ScanArgs& a, float* slots, float* dec, hipStream_t s);
 // Segments for the backward's two scans with cross terms (1: one walk each): only where
 // the walk bounds them, below 256 workgroups for both scans; then about 512 workgroups,
-// at most 8 segments, at least 8 chunks per segment.
+// at most 8 segments, at least 32 chunks per segment.
 int scan2_segments(int dtype, int C, int BH, int dk, int dv, int N);
 // launch_state_scan2 in scan2_segments segments: both scans' segment end states (one
 // launch, no stores), chained, then every segment of both scans walked from its start
@@ -206,10 +206,11 @@ hipError_t launch_gsa_w(const float* la, float* w, long n, hipStream_t s);
 hipError_t launch_vg_out(const float* q, const float* k, const float* w, const float* g2,
                          const float* S1, float* s_out, int BH, int T, int dk, int m,
                          hipStream_t s);
+// (dq, dk: fp32, or bf16 with out_bf16)
 hipError_t launch_vg_bwd(const float* q, const float* k, const float* w, const float* g2,
                          const float* ds, const float* s_in, const float* S1, const float* dS1,
-                         float* dq, float* dk, float* dw, float* Dloc, float* tot, int BH, int T,
-                         int dkh, int m, hipStream_t s);
+                         void* dq, void* dk, int out_bf16, float* dw, float* Dloc, float* tot,
+                         int BH, int T, int dkh, int m, hipStream_t s);
 hipError_t launch_softmax_rows(const float* x, float* p, long nrows, int m, hipStream_t s);
 hipError_t launch_softmax_bwd(const float* p, const float* dp, float* ds, long nrows, int m,
                               hipStream_t s);

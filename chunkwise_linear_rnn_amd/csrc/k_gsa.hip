@@ -262,11 +262,13 @@ __global__ __launch_bounds__(kThreads, 3) void k_vg_out(const float* __restrict_
 // sub-chunk (dA on rho = 16 I for earlier sources, dw on rho' = 16 I + 15 for later
 // targets; every factor at most 1) with their diagonal sub-blocks summed directly.  Four
 // 64 x 64 fp32 tiles of LDS, reused phase by phase, keep two workgroups per CU.
+// dq, dk are written as OutT (fp32, or bf16 rounded to nearest even).
+template <typename OutT>
 __global__ __launch_bounds__(kThreads, 2) void k_vg_bwd(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ g2, const float* __restrict__ ds, const float* __restrict__ s,
-    const float* __restrict__ S1, const float* __restrict__ dS1, float* __restrict__ dq,
-    float* __restrict__ dk_out, float* __restrict__ dw, float* __restrict__ Dloc,
+    const float* __restrict__ S1, const float* __restrict__ dS1, OutT* __restrict__ dq,
+    OutT* __restrict__ dk_out, float* __restrict__ dw, float* __restrict__ Dloc,
     float* __restrict__ tot, int T, int dk, int m, int N) {
   __shared__ __attribute__((aligned(16))) float T0[kC * kFL], T1[kC * kFL], T2[kC * kFL],
       T3[kC * kFL];
@@ -511,8 +513,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_vg_bwd(
       if (t < rows) {
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-          dq[(rowbase + t) * dk + d0 + 16 * jt + r] = aq[jt][e];
-          dk_out[(rowbase + t) * dk + d0 + 16 * jt + r] = ak[jt][e];
+          dq[(rowbase + t) * dk + d0 + 16 * jt + r] = (OutT)aq[jt][e];
+          dk_out[(rowbase + t) * dk + d0 + 16 * jt + r] = (OutT)ak[jt][e];
         }
       }
     }
@@ -575,11 +577,36 @@ __global__ __launch_bounds__(kThreads) void k_gsa_combine_bf16(const float* __re
     dla[i] = (bf16)(dla1[i] + (float)dla2[i] - (dw1[i] + (float)dw2[i]) * __expf(la[i]));
 }
 
-// Element conversions between bf16 and fp32 (round to nearest even towards bf16).
+// Element conversions between bf16 and fp32 (round to nearest even towards bf16): eight
+// elements per thread step (one 16-byte bf16 vector, two 16-byte fp32 vectors; both
+// buffers 16-byte aligned), then the tail one by one.
 template <typename S, typename D>
 __global__ __launch_bounds__(kThreads) void k_cast(const S* __restrict__ x, D* __restrict__ y,
                                                    long n) {
-  for (long i = blockIdx.x * (long)kThreads + threadIdx.x; i < n; i += (long)gridDim.x * kThreads)
+  const long stride = (long)gridDim.x * kThreads, n8 = n / 8;
+  for (long i = blockIdx.x * (long)kThreads + threadIdx.x; i < n8; i += stride) {
+    float f[8];
+    if constexpr (sizeof(S) == 2) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(x + 8 * i);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = (float)b[e];
+    } else {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(x + 8 * i);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(x + 8 * i + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { f[e] = a[e]; f[4 + e] = b[e]; }
+    }
+    if constexpr (sizeof(D) == 2) {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (bf16)f[e];
+      *reinterpret_cast<bf16x8*>(y + 8 * i) = o;
+    } else {
+      *reinterpret_cast<f32x4*>(y + 8 * i) = f32x4{f[0], f[1], f[2], f[3]};
+      *reinterpret_cast<f32x4*>(y + 8 * i + 4) = f32x4{f[4], f[5], f[6], f[7]};
+    }
+  }
+  for (long i = 8 * n8 + blockIdx.x * (long)kThreads + threadIdx.x; i < n; i += stride)
     y[i] = (D)x[i];
 }
 
@@ -607,12 +634,16 @@ hipError_t launch_vg_out(const float* q, const float* k, const float* w, const f
 
 hipError_t launch_vg_bwd(const float* q, const float* k, const float* w, const float* g2,
                          const float* ds, const float* s_in, const float* S1, const float* dS1,
-                         float* dq, float* dk, float* dw, float* Dloc, float* tot, int BH, int T,
-                         int dkh, int m, hipStream_t s) {
+                         void* dq, void* dk, int out_bf16, float* dw, float* Dloc, float* tot,
+                         int BH, int T, int dkh, int m, hipStream_t s) {
   const int N = (T + kC - 1) / kC;
   if (BH == 0 || N == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_vg_bwd, dim3(N, BH), dim3(kThreads), 0, s, q, k, w, g2, ds, s_in, S1, dS1,
-                     dq, dk, dw, Dloc, tot, T, dkh, m, N);
+  if (out_bf16)
+    hipLaunchKernelGGL(k_vg_bwd<bf16>, dim3(N, BH), dim3(kThreads), 0, s, q, k, w, g2, ds, s_in,
+                       S1, dS1, (bf16*)dq, (bf16*)dk, dw, Dloc, tot, T, dkh, m, N);
+  else
+    hipLaunchKernelGGL(k_vg_bwd<float>, dim3(N, BH), dim3(kThreads), 0, s, q, k, w, g2, ds, s_in,
+                       S1, dS1, (float*)dq, (float*)dk, dw, Dloc, tot, T, dkh, m, N);
   return hipGetLastError();
 }
 
@@ -653,14 +684,14 @@ hipError_t launch_gsa_combine_bf16(const float* la, const float* dla1, const voi
 
 hipError_t launch_cast_bf16_f32(const void* x, float* y, long n, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_cast<bf16, float>), dim3(grid1d(n)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((k_cast<bf16, float>), dim3(grid1d((n + 7) / 8)), dim3(kThreads), 0, s,
                      (const bf16*)x, y, n);
   return hipGetLastError();
 }
 
 hipError_t launch_cast_f32_bf16(const float* x, void* y, long n, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_cast<float, bf16>), dim3(grid1d(n)), dim3(kThreads), 0, s, x,
+  hipLaunchKernelGGL((k_cast<float, bf16>), dim3(grid1d((n + 7) / 8)), dim3(kThreads), 0, s, x,
                      (bf16*)y, n);
   return hipGetLastError();
 }

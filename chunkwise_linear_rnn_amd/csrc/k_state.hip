@@ -502,11 +502,12 @@ int scan2_segments(int dtype, int C, int BH, int dk, int dv, int N) {
   const long wgs = 2L * BH * (dk / 64) * (dv / TV);   // both scans
   // at one workgroup per CU and more the scans stream near the copy rate (bf16) or near
   // the fp32 matrix-unit rate (fp32), and a pass for the segment end states costs more
-  // than the parallelism gains
-  if (N < 16 || wgs >= 256) return 1;
+  // than the parallelism gains; so does it for walks shorter than 32 chunks per segment
+  // (measured: 32 chunks of 128 workgroups ran fastest as one walk)
+  if (N < 64 || wgs >= 256) return 1;
   int P = (int)(512 / wgs);   // these scans hold two workgroups per CU
   P = P > 8 ? 8 : P;
-  P = P > N / 8 ? N / 8 : P;
+  P = P > N / 32 ? N / 32 : P;
   return P < 2 ? 2 : P;
 }
 

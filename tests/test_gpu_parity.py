@@ -60,10 +60,11 @@ SMALL = [
     ("bf16_thin_n32", "bf16", 1, 1, 2000, 64, 128, 64, -1.0),
     ("f32_thin_n24", "f32", 1, 1, 1500, 64, 64, 64, -0.5),
     ("bf16_c128_thin_n17", "bf16", 1, 1, 2100, 64, 128, 128, 0.0),
-    # the backward's two scans in sequence segments: the thin cases above take 4 (bf16,
-    # 128-column tiles), 3 (fp32) and 2 (chunk 128); here 41 chunks of dk 256 in 5 uneven
-    # segments (ragged last chunk)
-    ("bf16_thin_dk256_n41", "bf16", 1, 1, 2600, 256, 256, 64, -0.5),
+    # the backward's two scans in sequence segments (at least 32 chunks each): 100 chunks
+    # of dk 256 in 3 uneven segments (ragged last chunk; the forward in 8, the
+    # materialized scan in 8), and fp32 with 66 chunks in 2
+    ("bf16_thin_dk256_n100", "bf16", 1, 1, 6380, 256, 256, 64, -0.5),
+    ("f32_thin_n66", "f32", 1, 1, 4200, 64, 64, 64, -0.5),
     # chunk 128 walked in 64-row halves with the sequence split: 5 chunks (halves of 2 and
     # 3), the last one's second half partly (T = 600) or wholly (T = 540) past T
     ("bf16_c128_n5", "bf16", 1, 2, 600, 128, 128, 128, 0.5),
