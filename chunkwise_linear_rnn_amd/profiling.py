@@ -125,8 +125,8 @@ def counters(fetch_csv, write_csv, copy_bytes, stage, workload, command, root):
     # checks of the two factors on kernels of the same size that only read (the bf16
     # max-reductions) or only write (the bf16 fill of the copy's source); the cache flush
     # of the timed steps fills uint8 and sums float32, so it matches neither
-    red_f = [v for n, v in f if "reduce" in n.lower() and "maxops" in n.lower()
-             and "bfloat16" in n.lower()]
+    red_f = [v for n, v in f if "reduce" in n.lower() and "bfloat16" in n.lower()
+             and ("maxnan" in n.lower() or "maxops" in n.lower())]
     fill_w = [v for n, v in w if "fill" in n.lower() and "bfloat16" in n.lower()]
     check_f = copy_bytes / (1024.0 * (sum(red_f) / len(red_f))) if red_f else None
     check_w = copy_bytes / (1024.0 * max(fill_w)) if fill_w else None

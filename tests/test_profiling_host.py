@@ -30,7 +30,8 @@ def test_counter_scaling_and_its_checks(tmp_path):
     kib = gib / 1024.0
     fetch = [("__amd_rocclr_copyBuffer", kib / 2), ("__amd_rocclr_copyBuffer", kib / 2),
              ("void at::native::reduce_kernel<512, 1, at::native::ReduceOp<c10::BFloat16, "
-              "at::native::MaxOps<float>, unsigned int, c10::BFloat16, 4, 4> >", kib / 2.5),
+              "at::native::func_wrapper_t<c10::BFloat16, at::native::MaxNanFunctor<"
+              "c10::BFloat16> >, unsigned int, c10::BFloat16, 4, 4> >", kib / 2.5),
              ("void at::native::reduce_kernel<512, 1, at::native::ReduceOp<float, "
               "at::native::func_wrapper_t<float, at::native::sum_functor<float> > > >", 7.0),
              ("k_bwd_dqk_dv<__hip_bfloat16>", 1000.0), ("k_bwd_dqk_dv<__hip_bfloat16>", 3000.0)]
