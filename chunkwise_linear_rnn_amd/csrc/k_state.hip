@@ -544,33 +544,31 @@ hipError_t launch_state_scan2_seg(const ScanArgs& a, const ScanArgs& b, float* s
 }
 
 // Segment end states -> states at the segment starts (see launch_seg_combine): one
-// workgroup per (64 state rows, 64 columns, bh); each thread loads all segment slots of its
-// 16 elements at once and chains them with the segments' decay products.
+// workgroup per (16 state rows, 64 columns, bh), 512 and more for the shapes that take
+// segments; each thread loads all segment slots of its four elements at once and chains
+// them with the segments' decay products.
 __global__ __launch_bounds__(kThreads) void k_seg_combine(float* __restrict__ S,
                                                           const float* __restrict__ dec, int BH,
                                                           int dk, int dv, int P) {
-  const int c0 = 64 * blockIdx.x, k0 = 64 * blockIdx.y, bh = blockIdx.z;
+  const int c0 = 64 * blockIdx.x, k0 = 16 * blockIdx.y, bh = blockIdx.z;
   const long slot = (long)BH * dk * dv;
+  const int kr = threadIdx.x >> 4, c = (threadIdx.x & 15) * 4;
+  const long off = ((long)bh * dk + k0 + kr) * dv + c0 + c;
+  f32x4 x[8];
+  float g[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int idx = threadIdx.x + kThreads * u, kr = idx >> 4, c = (idx & 15) * 4;
-    const long off = ((long)bh * dk + k0 + kr) * dv + c0 + c;
-    f32x4 x[8];
-    float g[8];
-#pragma unroll
-    for (int sg = 0; sg < 8; ++sg) {
-      if (sg < P - 1) {
-        x[sg] = *reinterpret_cast<const f32x4*>(S + sg * slot + off);
-        g[sg] = dec[((long)sg * BH + bh) * dk + k0 + kr];
-      }
+  for (int sg = 0; sg < 8; ++sg) {
+    if (sg < P - 1) {
+      x[sg] = *reinterpret_cast<const f32x4*>(S + sg * slot + off);
+      g[sg] = dec[((long)sg * BH + bh) * dk + k0 + kr];
     }
+  }
 #pragma unroll
-    for (int sg = 1; sg < 8; ++sg) {
-      if (sg < P - 1) {
+  for (int sg = 1; sg < 8; ++sg) {
+    if (sg < P - 1) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[sg][e] = g[sg] * x[sg - 1][e] + x[sg][e];
-        *reinterpret_cast<f32x4*>(S + sg * slot + off) = x[sg];
-      }
+      for (int e = 0; e < 4; ++e) x[sg][e] = g[sg] * x[sg - 1][e] + x[sg][e];
+      *reinterpret_cast<f32x4*>(S + sg * slot + off) = x[sg];
     }
   }
 }
@@ -579,7 +577,8 @@ hipError_t launch_seg_combine(float* S, const float* dec, int BH, int dk, int dv
                               hipStream_t s) {
   if (P <= 2 || BH == 0) return hipSuccess;
   if (P > 9 || dk % 64 != 0 || dv % 64 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_seg_combine, dim3(dv / 64, dk / 64, BH), dim3(kThreads), 0, s, S, dec, BH,
+  static_assert(kThreads == 256, "16 rows of 16 four-column units per workgroup");
+  hipLaunchKernelGGL(k_seg_combine, dim3(dv / 64, dk / 16, BH), dim3(kThreads), 0, s, S, dec, BH,
                      dk, dv, P);
   return hipGetLastError();
 }
