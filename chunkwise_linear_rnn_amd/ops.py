@@ -200,26 +200,44 @@ def chunk_states(k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, workspace=N
 
 class GLAFunction(torch.autograd.Function):
     """Autograd wrapper: forward runs gla_chunk_fwd, backward gla_chunk_bwd (which
-    recomputes the chunk states from the saved inputs)."""
+    recomputes the chunk states from the saved inputs).  The gate options of fwd / bwd
+    (gate logits with gate_tau, a scalar gate per token, the diagonal precision) pass
+    through; the gradient for log_alpha is then the one for what log_alpha holds."""
 
     @staticmethod
-    def forward(ctx, q, k, v, log_alpha, S0, chunk, subchunk, state_mode):
+    def forward(ctx, q, k, v, log_alpha, S0, chunk, subchunk, state_mode, gate_tau, diag):
         o, S_T = fwd(q, k, v, log_alpha, S0, chunk=chunk, subchunk=subchunk,
-                     state_mode=state_mode)
+                     state_mode=state_mode, gate_tau=gate_tau, diag=diag)
         ctx.save_for_backward(q, k, v, log_alpha, S0)
-        ctx.cfg = (chunk, subchunk)
+        ctx.cfg = (chunk, subchunk, gate_tau, diag)
         return o, S_T
 
     @staticmethod
     def backward(ctx, dO, dS_T):
         q, k, v, log_alpha, S0 = ctx.saved_tensors
-        chunk, subchunk = ctx.cfg
-        dO = dO.contiguous() if dO is not None else torch.zeros_like(
-            q.new_empty(q.shape[:-1] + (v.shape[-1],)))
+        chunk, subchunk, gate_tau, diag = ctx.cfg
+        dO = dO.contiguous() if dO is not None else q.new_zeros(q.shape[:-1] + (v.shape[-1],))
         dS_T = dS_T.contiguous() if dS_T is not None else None
         dq, dk, dv, dla, dS0 = bwd(q, k, v, log_alpha, dO, S0, dS_T, chunk=chunk,
-                                   subchunk=subchunk, want_dS0=S0 is not None)
-        return dq, dk, dv, dla, dS0, None, None, None
+                                   subchunk=subchunk, want_dS0=S0 is not None,
+                                   gate_tau=gate_tau, diag=diag)
+        return dq, dk, dv, dla, dS0, None, None, None, None, None
+
+
+class GSAFunction(torch.autograd.Function):
+    """Autograd wrapper of Gated Slot Attention: forward gla_gsa_fwd, backward gla_gsa_bwd
+    (which recomputes the forward from the saved inputs)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, log_alpha):
+        o = gsa_fwd(q, k, v, log_alpha)
+        ctx.save_for_backward(q, k, v, log_alpha)
+        return o
+
+    @staticmethod
+    def backward(ctx, dO):
+        q, k, v, log_alpha = ctx.saved_tensors
+        return gsa_bwd(q, k, v, log_alpha, dO.contiguous())
 
 
 def decode(q, k, v, log_alpha, S, *, gate_tau=None):
@@ -245,9 +263,10 @@ def decode(q, k, v, log_alpha, S, *, gate_tau=None):
     return o
 
 
-def gla(q, k, v, log_alpha, S0=None, chunk=64, subchunk=16, state_mode="recompute"):
-    """Differentiable GLA layer: returns (o, S_T)."""
-    return GLAFunction.apply(q, k, v, log_alpha, S0, chunk, subchunk, state_mode)
+def gla(q, k, v, log_alpha, S0=None, chunk=64, subchunk=16, state_mode="recompute",
+        gate_tau=None, diag="f32"):
+    """Differentiable GLA layer: returns (o, S_T); options as for fwd."""
+    return GLAFunction.apply(q, k, v, log_alpha, S0, chunk, subchunk, state_mode, gate_tau, diag)
 
 
 def _gsa_desc(q, v, log_alpha):
@@ -291,3 +310,8 @@ def gsa_bwd(q, k, v, log_alpha, dO, *, workspace=None):
                                            _ptr(log_alpha), _ptr(dO), _ptr(dq), _ptr(dk_),
                                            _ptr(dv_), _ptr(dla), _ptr(ws), need, _stream(dev)))
     return dq, dk_, dv_, dla
+
+
+def gsa(q, k, v, log_alpha):
+    """Differentiable Gated Slot Attention: returns o (see gsa_fwd)."""
+    return GSAFunction.apply(q, k, v, log_alpha)
