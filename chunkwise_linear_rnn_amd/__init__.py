@@ -22,10 +22,10 @@ from ._native import (GlaDesc, GlaError, F32, BF16, MATERIALIZED, RECOMPUTE, PAS
                       lib, lib_path, make_desc, make_gsa_desc, gsa_workspace_bytes, status_string,
                       trace_stages,
                       validate, version, workspace_bytes)
-from .ops import (fwd, bwd, gate_cumsum, chunk_states, decode, GLAFunction, gla,  # noqa: F401
+from .ops import (fwd, bwd, check_gates, gate_cumsum, chunk_states, decode, GLAFunction, gla,  # noqa: F401
                   GSAFunction, gsa, gsa_fwd, gsa_bwd)
 
-__all__ = ["fwd", "bwd", "gate_cumsum", "chunk_states", "decode", "GLAFunction", "gla", "GlaDesc",
+__all__ = ["fwd", "bwd", "check_gates", "gate_cumsum", "chunk_states", "decode", "GLAFunction", "gla", "GlaDesc",
            "GSAFunction", "gsa", "gsa_fwd", "gsa_bwd", "make_gsa_desc", "gsa_workspace_bytes",
            "GlaError", "make_desc", "workspace_bytes", "validate", "status_string", "version",
            "lib", "lib_path"]

@@ -48,6 +48,7 @@ SIGNATURES = {
     "gla_version": (_i32, []),
     "gla_validate": (_i32, [_PDESC, _i32]),
     "gla_workspace_bytes": (_i32, [_PDESC, _i32, ctypes.POINTER(_sz)]),
+    "gla_check_gates": (_i32, [_PDESC, _vp, _vp, _sz, ctypes.POINTER(ctypes.c_int64), _vp]),
     "gla_gate_cumsum": (_i32, [_PDESC, _vp, _vp, _vp, _vp]),
     "gla_chunk_states": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "gla_chunk_fwd": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),

@@ -11,6 +11,7 @@
 //                                  form the chunk totals of q*dq - k*dk from their fp32
 //                                  states -> chunk backward (dq, dk, dv, chunk-local D
 //                                  suffix sums) -> closed-form gate gradient scan
+#include <cstdlib>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -45,7 +46,7 @@ Dims dims_of(const gla_desc_t* d) {
 struct Plan {
   size_t g = 0, A = 0, Qh = 0, QhT = 0, Kh = 0, KhT = 0, eg = 0, st = 0, dst = 0, ST = 0,
          cT = 0, crossF = 0, crossR = 0, carry = 0, smid = 0, segdec = 0, dpart = 0,
-         sslots = 0, sdec = 0, total = 0;
+         sslots = 0, sdec = 0, dbg = 0, total = 0;
 };
 
 // The materialized forward's state scan (every chunk state written, [v][k]) for a shape.
@@ -115,6 +116,8 @@ Plan plan_of(const gla_desc_t* d, int pass) {
     p.KhT = take(opB);
     p.eg = take(egB);
   }
+  // the gate check's counter (GLA_DEBUG_CHECKS)
+  if ((pass == GLA_PASS_FWD || pass == GLA_PASS_BWD) && x.BH * x.T > 0) p.dbg = take(256);
   p.total = off;
   return p;
 }
@@ -122,6 +125,32 @@ Plan plan_of(const gla_desc_t* d, int pass) {
 bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 
 gla_status_t dev(hipError_t e) { return e == hipSuccess ? GLA_OK : GLA_ERR_DEVICE; }
+
+// GLA_DEBUG_CHECKS=1 in the environment (read once, at the first call): the layer's
+// forward and backward first count the gate elements that break its precondition and
+// refuse the call (GLA_ERR_INVALID_ARG) if there are any, before touching an output.
+bool debug_checks() {
+  static const bool on = [] {
+    const char* e = std::getenv("GLA_DEBUG_CHECKS");
+    return e != nullptr && e[0] == '1' && e[1] == 0;
+  }();
+  return on;
+}
+
+// Elements of the gate operand of `d` that break the precondition (synchronizes `s`).
+gla_status_t count_bad_gates(const gla_desc_t* d, const void* la, void* counter, hipStream_t s,
+                             long long* n_bad) {
+  const long n = (long)d->B * d->H * d->T * (d->gate_shape == GLA_GATE_SCALAR ? 1 : d->dk);
+  unsigned long long* cnt = (unsigned long long*)counter;
+  gla_status_t rs = dev(gla::launch_count_bad_gates(d->dtype, la, n, d->gate == GLA_GATE_LOGITS,
+                                                     cnt, s));
+  if (rs != GLA_OK) return rs;
+  unsigned long long h = 0;
+  if ((rs = dev(hipMemcpyAsync(&h, cnt, sizeof(h), hipMemcpyDeviceToHost, s))) != GLA_OK) return rs;
+  if ((rs = dev(hipStreamSynchronize(s))) != GLA_OK) return rs;
+  *n_bad = (long long)h;
+  return GLA_OK;
+}
 
 bool gate_ok(const gla_desc_t* d) {
   if (d->gate_shape != GLA_GATE_PER_KEY && d->gate_shape != GLA_GATE_SCALAR) return false;
@@ -243,6 +272,21 @@ gla_status_t gla_workspace_bytes(const gla_desc_t* d, int32_t pass, size_t* byte
   return GLA_OK;
 }
 
+gla_status_t gla_check_gates(const gla_desc_t* d, const void* log_alpha, void* ws,
+                             size_t ws_bytes, int64_t* n_bad, void* stream) {
+  const gla_status_t st = gla_validate(d, GLA_PASS_FWD);
+  if (st != GLA_OK) return st;
+  if (!n_bad) return GLA_ERR_INVALID_ARG;
+  *n_bad = 0;
+  if ((long long)d->B * d->H * d->T == 0) return GLA_OK;
+  if (!log_alpha || !aligned16(log_alpha) || !aligned16(ws)) return GLA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < 8) return GLA_ERR_WORKSPACE;
+  long long bad = 0;
+  const gla_status_t rs = count_bad_gates(d, log_alpha, ws, (hipStream_t)stream, &bad);
+  if (rs == GLA_OK) *n_bad = bad;
+  return rs;
+}
+
 gla_status_t gla_gate_cumsum(const gla_desc_t* d, const void* log_alpha, float* g, float* gamma,
                              void* stream) {
   const gla_status_t st = gla_validate(d, GLA_PASS_FWD);
@@ -307,6 +351,11 @@ gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void
   char* w = (char*)ws;
   const bool mat = d->state_mode == GLA_STATES_MATERIALIZED;
   gla_status_t rs = GLA_OK;
+  if (debug_checks()) {
+    long long bad = 0;
+    if ((rs = count_bad_gates(d, log_alpha, w + p.dbg, s, &bad)) != GLA_OK) return rs;
+    if (bad) return GLA_ERR_INVALID_ARG;
+  }
   if (mat) {
     if ((rs = tr.mark()) != GLA_OK) return rs;
     rs = dev(gla::launch_gate_cumsum(x.dtype, log_alpha, gate_of(d), scalar_gate(d),
@@ -403,6 +452,11 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   const int C = (int)x.C, BH = (int)x.BH, T = (int)x.T, DK = (int)x.dk, DV = (int)x.dv,
             N = (int)x.N;
   gla_status_t rs = GLA_OK;
+  if (debug_checks()) {
+    long long bad = 0;
+    if ((rs = count_bad_gates(d, log_alpha, w + p.dbg, s, &bad)) != GLA_OK) return rs;
+    if (bad) return GLA_ERR_INVALID_ARG;
+  }
   gla::IntraArgs ia{};
   ia.dtype = x.dtype; ia.C = C; ia.BH = BH; ia.T = T; ia.dk = DK; ia.N = N; ia.want_A = true;
   ia.xt_f32 = x.dtype == GLA_BF16;

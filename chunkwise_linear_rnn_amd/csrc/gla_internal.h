@@ -197,6 +197,11 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
+// The number of gate elements (n of them, fp32 or bf16) that break the layer's
+// precondition (log_alpha finite and <= 0; with `logits`, finite) into *cnt (device).
+hipError_t launch_count_bad_gates(int dtype, const void* x, long n, int logits,
+                                  unsigned long long* cnt, hipStream_t s);
+
 // Gated Slot Attention (fp32): w = 1 - exp(log_alpha); the first (slot-gated) pass's chunk
 // output and chunk backward; row softmax and its backward; the gate-gradient combination.
 // Layouts: q, k [BH][T][dk]; w, g2 (chunk-local cumsum * log2 e), s, ds, dw, Dloc [BH][T][m];

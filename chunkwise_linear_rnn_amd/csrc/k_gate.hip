@@ -197,4 +197,39 @@ hipError_t launch_gate_grad(int dtype, const float* Dloc, const float* tot, cons
   return hipGetLastError();
 }
 
+// Precondition check of the gate operand (the layer reads log_alpha as finite and <= 0, and
+// gate logits as finite): the number of elements that break it, as an exact integer count
+// (per-thread counts, summed over the wave, one integer atomic per wave).
+__global__ __launch_bounds__(kThreads) void k_zero_count(unsigned long long* cnt) { *cnt = 0ull; }
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_count_bad_gates(const T* __restrict__ x, long n,
+                                                              int logits,
+                                                              unsigned long long* cnt) {
+  unsigned long long c = 0;
+  for (long i = blockIdx.x * (long)kThreads + threadIdx.x; i < n; i += (long)gridDim.x * kThreads) {
+    const float v = (float)x[i];
+    c += (!__builtin_isfinite(v) || (!logits && v > 0.f)) ? 1ull : 0ull;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  if (lane_id() == 0 && c) atomicAdd(cnt, c);
+}
+
+hipError_t launch_count_bad_gates(int dtype, const void* x, long n, int logits,
+                                  unsigned long long* cnt, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_count, dim3(1), dim3(1), 0, s, cnt);
+  if (n > 0) {
+    const long b = (n + kThreads - 1) / kThreads;
+    const dim3 grid((unsigned)(b < 4096 ? b : 4096));
+    if (dtype == 0)
+      hipLaunchKernelGGL(k_count_bad_gates<float>, grid, dim3(kThreads), 0, s, (const float*)x, n,
+                         logits, cnt);
+    else
+      hipLaunchKernelGGL(k_count_bad_gates<bf16>, grid, dim3(kThreads), 0, s, (const bf16*)x, n,
+                         logits, cnt);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace gla

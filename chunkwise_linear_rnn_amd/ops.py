@@ -120,6 +120,21 @@ def fwd(q, k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, state_mode="recom
     return o, S_T
 
 
+def check_gates(q, v, log_alpha, *, gate_tau=None):
+    """The number of elements of log_alpha that break the layer's precondition (finite and
+    <= 0; gate logits with gate_tau: finite), counted on the device (gla_check_gates;
+    synchronizes the stream).  Shapes and options as for fwd."""
+    desc = _desc_from(q, v, 64, 16, RECOMPUTE, gate_tau, _is_scalar(log_alpha))
+    dev = q.device
+    B, H, T, dk = desc.B, desc.H, desc.T, desc.dk
+    _check(log_alpha, "log_alpha", _gate_shape(log_alpha, B, H, T, dk), q.dtype, dev)
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    n = ctypes.c_int64(0)
+    _call("gla_check_gates", lib().gla_check_gates(ctypes.byref(desc), _ptr(log_alpha), _ptr(ws),
+                                                   256, ctypes.byref(n), _stream(dev)))
+    return int(n.value)
+
+
 def bwd(q, k, v, log_alpha, dO, S0=None, dS_T=None, *, chunk=64, subchunk=16,
         want_dS0=True, workspace=None, gate_tau=None, diag="f32"):
     """dq, dk, dv, dlog_alpha, dS0 for the loss gradient (dO, dS_T).  With gate_tau set

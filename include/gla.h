@@ -37,8 +37,13 @@
  *  - Errors are reported by status code; no C++ exception crosses this boundary.  All
  *    argument checks run on the host before any launch, and on an error no output is
  *    touched.  Kernel-launch failures surface as GLA_ERR_DEVICE.
- *  - Preconditions that are not checked: log_alpha finite and <= 0 (a value > 0 or a
- *    non-finite value gives unspecified output), inputs finite.
+ *  - Preconditions that are not checked by default: log_alpha finite and <= 0 (gate
+ *    logits: finite; a value breaking it gives unspecified output), inputs finite.  With
+ *    GLA_DEBUG_CHECKS=1 in the environment (read once, at the first call),
+ *    gla_chunk_fwd / gla_chunk_bwd (and their _traced and _noalloc forms) first count the
+ *    gate elements that break it on the device (gla_check_gates, in a 256-byte region
+ *    that the workspace always reserves), synchronize the stream, and return
+ *    GLA_ERR_INVALID_ARG before any launch that touches an output if there are any.
  */
 #ifndef GLA_MI355X_H
 #define GLA_MI355X_H
@@ -144,6 +149,16 @@ gla_status_t gla_validate(const gla_desc_t* desc, int32_t pass);
  * (GLA_PASS_BWD) or gla_chunk_states (pass = 2) for `desc`; writes them to *bytes.
  * Host-only; same errors as gla_validate, plus GLA_ERR_INVALID_ARG for bytes == NULL. */
 gla_status_t gla_workspace_bytes(const gla_desc_t* desc, int32_t pass, size_t* bytes);
+
+/* Gate precondition check (the layer reads log_alpha as finite and <= 0, gate logits as
+ * finite; see the gate fields of gla_desc_t): *n_bad (host) = the number of elements of
+ * log_alpha ([B,H,T,dk], or [B,H,T] with scalar gates; element type desc->dtype) that
+ * break it.  ws: device scratch of at least 8 bytes (its first 8 bytes are overwritten).
+ * Synchronous: the stream is synchronized before return.  Errors: as gla_validate;
+ * GLA_ERR_INVALID_ARG for n_bad == NULL or a NULL or misaligned log_alpha (B*H*T > 0);
+ * GLA_ERR_WORKSPACE for ws == NULL or ws_bytes < 8. */
+gla_status_t gla_check_gates(const gla_desc_t* desc, const void* log_alpha, void* ws,
+                             size_t ws_bytes, int64_t* n_bad, void* stream);
 
 /* Gate log-cumsum (the first step of the chunkwise form, Approach section):
  *   g[b,h,t,:] = sum of log_alpha[b,h,u,:] over u from the start of t's chunk to t,

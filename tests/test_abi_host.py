@@ -104,6 +104,26 @@ def test_errors_before_any_launch(native):
     assert L.gla_gate_cumsum(ctypes.byref(good), None, p, p, None) == 1
 
 
+def test_check_gates_errors_before_any_launch(native):
+    """gla_check_gates refuses bad arguments on the host (its count itself needs a GPU)."""
+    L = native.lib()
+    good = native.make_desc(1, 1, 64, 64, 64)
+    p = ctypes.c_void_p(16)
+    n = ctypes.c_int64(-1)
+    assert L.gla_check_gates(ctypes.byref(good), p, p, 256, None, None) == 1        # no n_bad
+    assert L.gla_check_gates(ctypes.byref(good), None, p, 256, ctypes.byref(n), None) == 1
+    assert L.gla_check_gates(ctypes.byref(good), ctypes.c_void_p(18), p, 256,
+                             ctypes.byref(n), None) == 1                             # misaligned
+    assert L.gla_check_gates(ctypes.byref(good), p, None, 0, ctypes.byref(n), None) == 3
+    assert L.gla_check_gates(ctypes.byref(good), p, p, 4, ctypes.byref(n), None) == 3
+    assert L.gla_check_gates(ctypes.byref(native.make_desc(1, 1, 8, 64, 96)), p, p, 256,
+                             ctypes.byref(n), None) == 2                             # unsupported
+    empty = native.make_desc(1, 1, 0, 64, 64)
+    n.value = -1
+    assert L.gla_check_gates(ctypes.byref(empty), None, None, 0, ctypes.byref(n), None) == 0
+    assert n.value == 0
+
+
 def test_decode_validation_before_any_launch(native):
     """gla_decode checks its own shape rules on the host (chunk fields are not used)."""
     L = native.lib()
