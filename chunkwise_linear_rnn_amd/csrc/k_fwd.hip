@@ -5,8 +5,10 @@
 //                computes O_i = Qh_i S_[i] + A_i V_i from the chunk-start state written by
 //                the state scan ([dv][dk] layout, so both MFMA operands are
 //                dk-contiguous) and the intra-chunk matrix A.
-//   k_fwd_fused  non-materialized states: one workgroup per (batch*head, 64 values) keeps
-//                its dk x 64 slice of the state in fp32 accumulators and walks the chunks:
+//   k_fwd_fused  non-materialized states: one workgroup per (batch*head, 64 values,
+//                sequence segment) keeps its dk x 64 slice of the state in fp32
+//                accumulators and walks the segment's chunks from the state at its start
+//                (S0, or one formed beforehand by a state scan without stores):
 //                O_i = Qh_i S + A_i V_i, then S <- diag(exp(gamma_i)) S + Kh_i^T V_i.  No
 //                per-chunk state ever reaches memory.  The state accumulators feed the
 //                Qh S product directly as the MFMA B operand (acc-order fragments).

@@ -49,7 +49,7 @@ STAGE_SOURCE = {"bwd_dqk_dv": "k_bwd.hip",
 # Stages whose kernel name is shared by several launches of a step: the template
 # arguments that pick the stage's instance (mangled, or demangled, symbol text).
 STAGE_SYMBOL = {"state_scans": ("ELi1ELb1E", ", 1, true"),     # stores states, cross terms
-                "seg_state": ("ELi0ELb0E", ", 0, false"),      # midpoint state only
+                "seg_state": ("ELi0ELb0E", ", 0, false"),      # segment end states only
                 "state_scan": ("ELi2ELb0E", ", 2, false"),     # materialized forward states
                 # the forward's intra-chunk kernel writes Kh^T in bf16, the backward's in fp32
                 "intra_fwd": ("DF16bDF16bDF16bLi", "bf16, bf16, bf16,"),
