@@ -100,3 +100,13 @@ def test_metric_names_the_workload_it_ran(bench):
     assert bench.metric_name(WORKLOADS["long_t20k"], True).startswith("GLA fwd tokens/s")
     # the headline shape run forward-only is not the headline metric either
     assert bench.metric_name(head, True) != bench.METRIC
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py --gpus N with N > 1 exits with a message (one GPU only), before any GPU use."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr and r.stdout.strip() == ""
