@@ -33,8 +33,15 @@ __global__ __launch_bounds__(kThreads) void k_output(const OpT* __restrict__ Qh,
                                                      const Tin* __restrict__ V,
                                                      Tin* __restrict__ O, int T, int dk, int dv,
                                                      int N) {
-  constexpr int TV = 64, VLD = C + 8, NM = C / 16;
+  constexpr int TV = 64, VLD = C + 8, NM = C / 16, DB = 64;
+  // Qh and the state tile move through LDS in 64-column blocks of the key dimension, as
+  // 16-byte row pieces (the state tile of a workgroup is one contiguous block of memory,
+  // streamed in order; Qh is read once per workgroup instead of once per wave); rows
+  // padded so that the fragment reads of 16 consecutive rows fall on distinct banks
+  constexpr int LD = sizeof(OpT) == 2 ? DB + 16 : DB + 4;
   __shared__ __attribute__((aligned(16))) OpT vs[TV * VLD];
+  __shared__ __attribute__((aligned(16))) OpT qs[C * LD];
+  __shared__ __attribute__((aligned(16))) OpT ss[TV * LD];
   // 1-D grid, XCD-aware: the dv tiles of one chunk share Qh and A
   const int nvt = dv / TV;
   const int lt = xcd_logical(blockIdx.x, gridDim.x);
@@ -42,25 +49,39 @@ __global__ __launch_bounds__(kThreads) void k_output(const OpT* __restrict__ Qh,
   const int w = wave_id(), l = lane_id(), r = l & 15, qd = l >> 4;
   const int t0 = i * C, rows = min(C, T - t0);
 
+  const OpT* qp = Qh + ((long)bh * N * C + t0) * dk;
+  const OpT* sp = STt + (((long)bh * N + i) * dv + v0) * dk;
+  RowTile<OpT, C, DB, LD> tq;
+  RowTile<OpT, TV, DB, LD> ts;
+  tq.load(qp, dk, C);
+  ts.load(sp, dk, TV);
   stage_cols<OpT, Tin, C, TV>(vs, VLD, V + ((long)bh * T + t0) * dv + v0, dv, rows);
 
   f32x4 acc[NM];   // acc[m][e] = O[16m + 4qd + e][v0 + 16w + r]
 #pragma unroll
   for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const OpT* sp = STt + (((long)bh * N + i) * dv + v0 + 16 * w + r) * dk;
-  const OpT* qp = Qh + ((long)bh * N * C + t0) * dk;
-  for (int kb = 0; kb < dk / 32; ++kb) {
-    Frag<OpT> fb;
-    load_frag_c(fb, sp + kb * 32);
+  for (int d0 = 0; d0 < dk; d0 += DB) {
+    __syncthreads();   // the previous block's fragment reads are done
+    tq.store(qs);
+    ts.store(ss);
+    __syncthreads();
+    // the next block (the last one refetches itself: no branch around a load)
+    const int dn = min(d0 + DB, dk - DB);
+    tq.load(qp + dn, dk, C);
+    ts.load(sp + dn, dk, TV);
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      Frag<OpT> fa;
-      load_frag_c(fa, qp + (long)(16 * m + r) * dk + kb * 32);
-      mma(acc[m], fa, fb);
+    for (int kb = 0; kb < DB / 32; ++kb) {
+      Frag<OpT> fb;
+      load_frag_c(fb, ss + (16 * w + r) * LD + kb * 32);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        Frag<OpT> fa;
+        load_frag_c(fa, qs + (16 * m + r) * LD + kb * 32);
+        mma(acc[m], fa, fb);
+      }
     }
   }
-  __syncthreads();
   const OpT* ap = A + ((long)bh * N + i) * C * C;
 #pragma unroll
   for (int kb = 0; kb < C / 32; ++kb) {
