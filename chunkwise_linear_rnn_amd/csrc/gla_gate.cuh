@@ -49,8 +49,10 @@ struct GBlock {
   }
   // The loaded units are unpacked first, in straight-line code, and rows are zeroed with
   // selects: a branch around the first use of a load makes the compiler wait for every
-  // memory operation in flight (the previous block's output stores included).
-  __device__ __forceinline__ void store(float* gs, int gld, GateFn gf) const {
+  // memory operation in flight (the previous block's output stores included).  `scale`:
+  // log2 e (the chunk kernels' base-2 exponentials), or 1 for natural-log units.
+  __device__ __forceinline__ void store(float* gs, int gld, GateFn gf,
+                                        float scale = kLog2e) const {
     constexpr int kF = sizeof(SrcT) == 2 ? 8 : 4;   // floats per unit
     float x[kPerThread][kF];
 #pragma unroll
@@ -68,7 +70,7 @@ struct GBlock {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j)
 #pragma unroll
-      for (int e = 0; e < kF; ++e) x[j][e] = gf(x[j][e]) * kLog2e;
+      for (int e = 0; e < kF; ++e) x[j][e] = gf(x[j][e]) * scale;
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       const int idx = threadIdx.x + j * kThreads, rr = idx / kUnitsRow, c = (idx % kUnitsRow) * kPer;

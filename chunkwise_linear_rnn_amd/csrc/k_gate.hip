@@ -11,36 +11,44 @@
 // All three are HBM-bound: coalesced along the contiguous d dimension, no MFMA.
 #include "gla_common.cuh"
 #include "gla_internal.h"
+#include "gla_gate.cuh"
 
 namespace gla {
 
-template <typename Tin>
+// One workgroup per (chunk, 64 key columns): the block of gates staged into LDS as fp32
+// (16-byte loads; rows past T zero, so the sum continues flat), the chunk-local inclusive
+// cumsum down each column in four row quarters (chunk_cumsum_cols, the same sums the
+// intra-chunk kernels form), then written out as 16-byte rows; gamma is the last row.
+template <typename Tin, int C>
 __global__ __launch_bounds__(kThreads) void k_gate_cumsum(const Tin* __restrict__ la,
                                                           GateFn gf, int gscalar,
                                                           float* __restrict__ g,
                                                           float* __restrict__ gamma, int T,
-                                                          int dk, int C, int N) {
-  constexpr int U = 16;   // rows loaded per batch, so the loads are in flight together
-  const int i = blockIdx.x, bh = blockIdx.y;
-  const int t0 = i * C, t1 = min(T, t0 + C);
-  const long base = (long)bh * T * dk;
-  // element (t, d) of the gate: [T][dk], or [T] shared by every d (scalar gates)
-  const long ls_t = gscalar ? 1 : dk, ls_d = gscalar ? 0 : 1, lbase = gscalar ? (long)bh * T : base;
-  for (int d = threadIdx.x; d < dk; d += kThreads) {
-    float acc = 0.f;
-    for (int tb = t0; tb < t1; tb += U) {
-      float x[U];
+                                                          int dk, int N) {
+  constexpr int DB = 64, GLD = DB + 4;
+  __shared__ __attribute__((aligned(16))) float gs[C * GLD];
+  __shared__ float segtot[4 * DB];
+  const int d0 = DB * blockIdx.x, i = blockIdx.y, bh = blockIdx.z;
+  const int t0 = i * C, rows = min(C, T - t0);
+  GBlock<Tin, C, DB> pg;
+  if (gscalar) pg.load_scalar(la + (long)bh * T + t0, rows);
+  else pg.load(la + ((long)bh * T + t0) * dk + d0, dk, rows, false);
+  pg.store(gs, GLD, gf, 1.f);
+  __syncthreads();
+  chunk_cumsum_cols<C, DB>(gs, GLD, segtot);
+  __syncthreads();
+  if (g) {
+    constexpr int kUnits = C * DB / 4;
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        x[u] = tb + u < t1 ? gf(to_f32(la[lbase + (long)(tb + u) * ls_t + d * ls_d])) : 0.f;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        acc += x[u];
-        if (g && tb + u < t1) g[base + (long)(tb + u) * dk + d] = acc;
-      }
+    for (int u_ = 0; u_ < kUnits / kThreads; ++u_) {   // fixed trip count
+      const int idx = threadIdx.x + u_ * kThreads, r = idx / (DB / 4), c = (idx % (DB / 4)) * 4;
+      if (r < rows)
+        *reinterpret_cast<f32x4*>(g + ((long)bh * T + t0 + r) * dk + d0 + c) =
+            *reinterpret_cast<const f32x4*>(gs + r * GLD + c);
     }
-    if (gamma) gamma[((long)bh * N + i) * dk + d] = acc;
   }
+  if (gamma && threadIdx.x < DB)
+    gamma[((long)bh * N + i) * dk + d0 + threadIdx.x] = gs[(C - 1) * GLD + threadIdx.x];
 }
 
 // One wave per state row d; lanes stride over v.
@@ -142,13 +150,18 @@ hipError_t launch_gate_cumsum(int dtype, const void* la, GateFn gate, int gscala
                               float* gamma, int BH, int T, int dk, int C, hipStream_t s) {
   const int N = (T + C - 1) / C;
   if (BH == 0 || N == 0) return hipSuccess;
-  dim3 grid(N, BH);
-  if (dtype == 0)
-    hipLaunchKernelGGL(k_gate_cumsum<float>, grid, dim3(kThreads), 0, s, (const float*)la, gate,
-                       gscalar, g, gamma, T, dk, C, N);
-  else
-    hipLaunchKernelGGL(k_gate_cumsum<bf16>, grid, dim3(kThreads), 0, s, (const bf16*)la, gate,
-                       gscalar, g, gamma, T, dk, C, N);
+  if (dk % 64 != 0 || (C != 64 && C != 128)) return hipErrorInvalidValue;
+  const dim3 grid(dk / 64, N, BH);
+  auto go = [&](auto kern, const auto* x) {
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, x, gate, gscalar, g, gamma, T, dk, N);
+  };
+  if (dtype == 0) {
+    if (C == 64) go(k_gate_cumsum<float, 64>, (const float*)la);
+    else go(k_gate_cumsum<float, 128>, (const float*)la);
+  } else {
+    if (C == 64) go(k_gate_cumsum<bf16, 64>, (const bf16*)la);
+    else go(k_gate_cumsum<bf16, 128>, (const bf16*)la);
+  }
   return hipGetLastError();
 }
 
