@@ -81,18 +81,13 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
     tok = BH * T
     tokp = BH * N * C                      # padded rows of per-chunk operands
     st = BH * N * dk * dv * e              # one materialized state tensor
-    if stage == "gate_cumsum":
-        return tok * dk * (e + 4), tok * dk
     if stage == "intra":
         if pass_ == "fwd":
             byt = 3 * tok * dk * e + 2 * tokp * dk * e + BH * N * C * C * e + BH * N * dk * 4
-            if mode == "materialized":
-                byt += tok * dk * (4 - e)  # reads fp32 g instead of log_alpha
-        else:   # reads log_alpha, q, k; writes A, Qh^T, Kh^T (fp32), Kh, e^gamma, and g (fp32)
-            # for the single-kernel chunk backward (bf16 at chunk 64 rebuilds g itself)
-            split = e == 2 and C == 64
-            byt = (3 * tok * dk * e + (0 if split else tok * dk * 4) + BH * N * C * C * e
-                   + 2 * tokp * dk * 4 + tokp * dk * e + BH * N * dk * 4)
+        else:   # reads log_alpha, q, k; writes A, Qh^T, Kh^T (fp32), Kh, e^gamma (the
+            # chunk kernel rebuilds g itself)
+            byt = (3 * tok * dk * e + BH * N * C * C * e + 2 * tokp * dk * 4 + tokp * dk * e
+                   + BH * N * dk * 4)
         return byt, tok * C * dk
     if stage in ("state_scan_fwd", "state_scan_rev", "state_scans"):
         # one scan: reads Kh^T and Qh^T (fp32 as bf16 pairs), v and dO; writes the states

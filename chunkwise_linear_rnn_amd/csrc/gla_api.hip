@@ -44,7 +44,7 @@ Dims dims_of(const gla_desc_t* d) {
 
 // Workspace carving.  Every region is 256-byte aligned.
 struct Plan {
-  size_t g = 0, A = 0, Qh = 0, QhT = 0, Kh = 0, KhT = 0, eg = 0, st = 0, dst = 0, ST = 0,
+  size_t A = 0, Qh = 0, QhT = 0, Kh = 0, KhT = 0, eg = 0, st = 0, dst = 0, ST = 0,
          cT = 0, crossF = 0, crossR = 0, carry = 0, smid = 0, segdec = 0, dpart = 0,
          sslots = 0, sdec = 0, dbg = 0, total = 0;
 };
@@ -67,14 +67,12 @@ Plan plan_of(const gla_desc_t* d, int pass) {
     return at;
   };
   const size_t rowsP = (size_t)x.BH * x.N * x.C;          // padded token rows
-  const size_t gB = (size_t)x.BH * x.T * x.dk * 4;
   const size_t AB = (size_t)x.BH * x.N * x.C * x.C * x.esz;
   const size_t opB = rowsP * x.dk * x.esz;
   const size_t egB = (size_t)x.BH * x.N * x.dk * 4;
   const size_t stB = (size_t)x.BH * x.N * x.dk * x.dv * x.esz;
   const bool mat = d->state_mode == GLA_STATES_MATERIALIZED;
   if (pass == GLA_PASS_FWD) {
-    if (mat) p.g = take(gB);
     // a segmented materialized scan: the states at the segment starts and decay products
     const int P = mat ? gla::scan_segments(mat_scan_shape(x)) : 1;
     if (P > 1) p.sslots = take((size_t)(P - 1) * x.BH * x.dk * x.dv * 4);
@@ -193,7 +191,7 @@ struct Tracer {
 };
 
 // Stage names of each pipeline, in launch order.
-const char* const kFwdMat[] = {"gate_cumsum", "intra", "state_scan", "output"};
+const char* const kFwdMat[] = {"intra", "state_scan", "output"};
 const char* const kFwdRec[] = {"intra", "seg_state", "fwd_fused"};
 const char* const kBwd[] = {"intra", "state_scans", "state_dot", "gate_tot", "bwd_dqk_dv"};
 
@@ -201,7 +199,7 @@ int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, in
   const char* const* src;
   int n;
   if (pass == GLA_PASS_FWD) {
-    if (d->state_mode == GLA_STATES_MATERIALIZED) { src = kFwdMat; n = 4; }
+    if (d->state_mode == GLA_STATES_MATERIALIZED) { src = kFwdMat; n = 3; }
     else { src = kFwdRec; n = 3; }
   } else {
     src = kBwd; n = 5;
@@ -317,7 +315,7 @@ gla_status_t gla_chunk_states(const gla_desc_t* d, const void* k, const void* v,
   char* w = (char*)ws;
   gla::IntraArgs ia{};
   ia.dtype = x.dtype; ia.C = (int)x.C; ia.BH = (int)x.BH; ia.T = (int)x.T; ia.dk = (int)x.dk;
-  ia.N = (int)x.N; ia.want_A = false; ia.q = k; ia.k = k; ia.la = log_alpha; ia.g = nullptr; ia.gate = gate_of(d);
+  ia.N = (int)x.N; ia.want_A = false; ia.q = k; ia.k = k; ia.la = log_alpha; ia.gate = gate_of(d);
   ia.gscalar = scalar_gate(d);
   ia.KhT = w + p.KhT; ia.eg = (float*)(w + p.eg);
   gla_status_t rs = dev(gla::launch_intra(ia, s));
@@ -356,18 +354,10 @@ gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void
     if ((rs = count_bad_gates(d, log_alpha, w + p.dbg, s, &bad)) != GLA_OK) return rs;
     if (bad) return GLA_ERR_INVALID_ARG;
   }
-  if (mat) {
-    if ((rs = tr.mark()) != GLA_OK) return rs;
-    rs = dev(gla::launch_gate_cumsum(x.dtype, log_alpha, gate_of(d), scalar_gate(d),
-                                     (float*)(w + p.g), nullptr, (int)x.BH, (int)x.T, (int)x.dk,
-                                     (int)x.C, s));
-    if (rs != GLA_OK) return rs;
-  }
   gla::IntraArgs ia{};
   ia.dtype = x.dtype; ia.C = (int)x.C; ia.BH = (int)x.BH; ia.T = (int)x.T; ia.dk = (int)x.dk;
   ia.N = (int)x.N; ia.want_A = true; ia.q = q; ia.k = k; ia.la = log_alpha; ia.gate = gate_of(d);
   ia.gscalar = scalar_gate(d); ia.diag_bf16 = d->diag == GLA_DIAG_BF16;
-  ia.g = mat ? (const float*)(w + p.g) : nullptr;
   ia.A = w + p.A; ia.Qh = w + p.Qh; ia.KhT = w + p.KhT; ia.eg = (float*)(w + p.eg);
   if ((rs = tr.mark()) != GLA_OK) return rs;
   rs = dev(gla::launch_intra(ia, s));
@@ -460,7 +450,7 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   gla::IntraArgs ia{};
   ia.dtype = x.dtype; ia.C = C; ia.BH = BH; ia.T = T; ia.dk = DK; ia.N = N; ia.want_A = true;
   ia.xt_f32 = x.dtype == GLA_BF16;
-  ia.q = q; ia.k = k; ia.la = log_alpha; ia.g = nullptr;
+  ia.q = q; ia.k = k; ia.la = log_alpha;
   ia.g2_out = nullptr;
   ia.gate = gate_of(d); ia.gscalar = scalar_gate(d); ia.diag_bf16 = d->diag == GLA_DIAG_BF16;
   ia.A = w + p.A; ia.QhT = w + p.QhT; ia.Kh = w + p.Kh; ia.KhT = w + p.KhT;
@@ -671,7 +661,7 @@ struct GsaFwd {   // the forward up to p (bf16: and its bf16 copies), and o when
     if ((rs = dev(gla::launch_gsa_w(la, (float*)(w + p.w), TM, s))) != GLA_OK) return rs;
     gla::IntraArgs ia{};
     ia.dtype = 0; ia.C = 64; ia.BH = BH; ia.T = T; ia.dk = m; ia.N = N; ia.want_A = false;
-    ia.q = w + p.w; ia.k = w + p.w; ia.la = la; ia.g = nullptr;
+    ia.q = w + p.w; ia.k = w + p.w; ia.la = la;
     ia.KhT = w + p.KhT; ia.eg = (float*)(w + p.eg); ia.g2_out = (float*)(w + p.g2);
     ia.gate = gla::GateFn{0, 1.f};
     if ((rs = dev(gla::launch_intra(ia, s))) != GLA_OK) return rs;
@@ -790,7 +780,7 @@ gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* d, const void* q, const void* k, 
   // first pass backward: (ds * e^g)^T per chunk, the reverse scan of the key slots
   gla::IntraArgs ia{};
   ia.dtype = 0; ia.C = 64; ia.BH = BH; ia.T = T; ia.dk = m; ia.N = N; ia.want_A = false;
-  ia.q = w + p.ds; ia.k = w + p.w; ia.la = la; ia.g = nullptr; ia.QhT = w + p.QhT;
+  ia.q = w + p.ds; ia.k = w + p.w; ia.la = la; ia.QhT = w + p.QhT;
   ia.eg = (float*)(w + p.eg); ia.gate = gla::GateFn{0, 1.f};
   if ((rs = dev(gla::launch_intra(ia, s))) != GLA_OK) return rs;
   gla::ScanArgs ra = gsa_slot_scan(d);

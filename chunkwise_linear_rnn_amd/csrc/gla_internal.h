@@ -33,12 +33,11 @@ struct IntraArgs {
   bool want_A;
   bool xt_f32;           // write QhT / KhT as bf16 high part + remainder (bf16 inputs only)
   const void *q, *k, *la;
-  const float* g;        // chunk-local cumsum from the gate kernel, or NULL (computed)
   void* A;               // [BH][N][C][C]       operand type
   void *Qh, *QhT, *Kh, *KhT;
   float* eg;             // [BH][N][dk]
   float* g2_out;         // [BH][T][dk] g * log2(e), or NULL
-  GateFn gate;           // applied to la (not to g, which is already a cumsum)
+  GateFn gate;           // applied to la
   bool gscalar;          // la holds one gate per token: [BH][T], broadcast over dk
   bool diag_bf16;        // rebased diagonal sub-blocks with bf16 operands (else fp32)
 };

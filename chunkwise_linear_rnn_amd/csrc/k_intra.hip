@@ -25,9 +25,10 @@
 // (XT = float with bf16 operands) as a bf16 high part plus bf16 remainder per row, which
 // the backward's scans feed to two MFMAs so the states carry no operand rounding.
 //
-// g either comes from the gate-cumsum kernel (G_WS) or is computed here from log_alpha
-// by a segmented column scan.  Internally g is held multiplied by log2(e) so every decay
-// is one v_exp_f32; g2_out (nullable) receives it for the backward chunk kernel.
+// g is computed here from log_alpha (through the gate front-end) by a segmented column
+// scan, the same one the gate-cumsum kernel runs.  Internally g is held multiplied by
+// log2(e) so every decay is one v_exp_f32; g2_out (nullable) receives it for the
+// backward chunk kernel.
 #include <type_traits>
 
 #include "gla_common.cuh"
@@ -87,11 +88,10 @@ __device__ __forceinline__ void store_xt(XT* __restrict__ dst, long bhi, int dk,
   }
 }
 
-template <typename Tin, typename OpT, typename XT, int C, bool G_WS, bool WANT_A, bool SG,
-          bool DIAG_BF16>
+template <typename Tin, typename OpT, typename XT, int C, bool WANT_A, bool DIAG_BF16>
 __global__ __launch_bounds__(kThreads) void k_intra(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ la,
-    const float* __restrict__ gws, OpT* __restrict__ A_out, OpT* __restrict__ Qh_out,
+    OpT* __restrict__ A_out, OpT* __restrict__ Qh_out,
     XT* __restrict__ QhT_out, OpT* __restrict__ Kh_out, XT* __restrict__ KhT_out,
     float* __restrict__ eg_out, float* __restrict__ g2_out, GateFn gf, int T, int dk, int N) {
   constexpr int DB = 64;                    // dk columns per pass
@@ -130,16 +130,13 @@ __global__ __launch_bounds__(kThreads) void k_intra(
   if constexpr (WANT_A)
     for (int item = threadIdx.x; item < NITEM; item += kThreads) dacc[item] = 0.f;
 
-  // The next dk block's g (or log_alpha), q and k are loaded into registers while the
-  // current block computes.
-  using GSrc = typename std::conditional<G_WS, float, Tin>::type;
-  GBlock<GSrc, C, DB> pg;
+  // The next dk block's log_alpha (or gate logits), q and k are loaded into registers
+  // while the current block computes.
+  GBlock<Tin, C, DB> pg;
   RowTile<Tin, C, DB, XLD> tq, tk;
   auto fetch = [&](int d0) {
-    // g from the gate kernel: rows past T continue the last valid row; log_alpha: zero
-    if constexpr (G_WS) pg.load(gws + in_base + d0, dk, rows, true);
-    else if constexpr (SG) pg.load_scalar(la + (long)bh * T + t0, rows);   // one gate per token
-    else pg.load(la + in_base + d0, dk, rows, false);
+    // rows past T zero (after the gate front-end too): they never decay the chunk
+    pg.load(la + in_base + d0, dk, rows, false);
     tq.load(q + in_base + d0, dk, rows);
     tk.load(k + in_base + d0, dk, rows);
   };
@@ -147,20 +144,16 @@ __global__ __launch_bounds__(kThreads) void k_intra(
 
   for (int d0 = 0; d0 < dk; d0 += DB) {
     // ---- g block (times log2 e), q, k -------------------------------------------------
-    // g from the gate kernel is already transformed; log_alpha (or logits) goes through gf
-    pg.store(gs, GLD, G_WS ? GateFn{0, 1.f} : gf);
+    // log_alpha (or logits, through the gate front-end gf)
+    pg.store(gs, GLD, gf);
     tq.store(qs);
     tk.store(ks);
     fetch(min(d0 + DB, dk - DB));   // unconditional (exact wait counts); the last refetches
     // wide: some 16-row sub-block of this block has a spread of g beyond kDiagRange
-    bool wide = false;
-    if constexpr (!G_WS) {
-      // chunk-local cumsum down each column; its spread decides at the barrier after it
-      __syncthreads();
-      wide = __syncthreads_or(!(chunk_cumsum_cols<C, DB>(gs, GLD, segtot) <= kDiagRange));
-    } else {
-      __syncthreads();
-    }
+    // chunk-local cumsum down each column; its spread decides at the barrier after it
+    __syncthreads();
+    const bool wide =
+        __syncthreads_or(!(chunk_cumsum_cols<C, DB>(gs, GLD, segtot) <= kDiagRange));
     if (g2_out) {   // g * log2 e for the backward chunk kernel
 #pragma unroll
       for (int u_ = 0; u_ < (C * (DB / 8) + kThreads - 1) / kThreads; ++u_) {   // fixed trip count
@@ -265,17 +258,6 @@ __global__ __launch_bounds__(kThreads) void k_intra(
       // case), an MFMA on operands rebased at the sub-block's first row, fp32 unless
       // opted into bf16 (entries above the diagonal are dropped when the block is
       // written); otherwise the exact fp32 log-space sum per (t, s, column).
-      if constexpr (G_WS) {   // g from the gate kernel: measure the spread here
-        for (int idx = threadIdx.x; idx < NS * DB; idx += kThreads) {
-          const int I = idx / DB, col = idx % DB;
-          const float g0 = gs[16 * I * GLD + col];
-          float mx = 0.f;
-#pragma unroll
-          for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, fabsf(gs[(16 * I + rr) * GLD + col] - g0));
-          wide = wide || !(mx <= kDiagRange);
-        }
-        wide = __syncthreads_or(wide);
-      }
       if (!wide) {
 #pragma unroll
         for (int dI = 0; dI < NDW; ++dI) {
@@ -577,13 +559,11 @@ __global__ __launch_bounds__(kThreads) void k_intra_scalar(
 }
 
 // ---------------------------------------------------------------------------------
-template <typename Tin, typename OpT, typename XT, int C, bool GW, bool WA, bool SG = false,
-          bool DB16 = false>
+template <typename Tin, typename OpT, typename XT, int C, bool WA, bool DB16 = false>
 static void launch_intra_k(const IntraArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_intra<Tin, OpT, XT, C, GW, WA, SG, DB16>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
-                     (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.la, a.g, (OpT*)a.A,
-                     (OpT*)a.Qh, (XT*)a.QhT, (OpT*)a.Kh, (XT*)a.KhT, a.eg, a.g2_out, a.gate, a.T,
-                     a.dk, a.N);
+  hipLaunchKernelGGL((k_intra<Tin, OpT, XT, C, WA, DB16>), dim3(a.N, a.BH), dim3(kThreads), 0, s,
+                     (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.la, (OpT*)a.A, (OpT*)a.Qh,
+                     (XT*)a.QhT, (OpT*)a.Kh, (XT*)a.KhT, a.eg, a.g2_out, a.gate, a.T, a.dk, a.N);
 }
 template <typename Tin, typename OpT, typename XT, int C>
 static hipError_t launch_intra_t(const IntraArgs& a, hipStream_t s) {
@@ -596,21 +576,10 @@ static hipError_t launch_intra_t(const IntraArgs& a, hipStream_t s) {
   }
   if (a.want_A) {
     // the bf16 diagonal is an option of bf16 operands only
-    const bool db16 = a.diag_bf16 && sizeof(OpT) == 2;
-    if (a.g) {
-      if (db16) launch_intra_k<Tin, OpT, XT, C, true, true, false, true>(a, s);
-      else launch_intra_k<Tin, OpT, XT, C, true, true>(a, s);
-    } else if (a.gscalar) {
-      if (db16) launch_intra_k<Tin, OpT, XT, C, false, true, true, true>(a, s);
-      else launch_intra_k<Tin, OpT, XT, C, false, true, true>(a, s);
-    } else {
-      if (db16) launch_intra_k<Tin, OpT, XT, C, false, true, false, true>(a, s);
-      else launch_intra_k<Tin, OpT, XT, C, false, true>(a, s);
-    }
+    if (a.diag_bf16 && sizeof(OpT) == 2) launch_intra_k<Tin, OpT, XT, C, true, true>(a, s);
+    else launch_intra_k<Tin, OpT, XT, C, true>(a, s);
   } else {
-    if (a.g) launch_intra_k<Tin, OpT, XT, C, true, false>(a, s);
-    else if (a.gscalar) launch_intra_k<Tin, OpT, XT, C, false, false, true>(a, s);
-    else launch_intra_k<Tin, OpT, XT, C, false, false>(a, s);
+    launch_intra_k<Tin, OpT, XT, C, false>(a, s);
   }
   return hipGetLastError();
 }

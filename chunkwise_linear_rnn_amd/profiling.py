@@ -34,14 +34,14 @@ STAGE_KERNEL = {"bwd_dqk_dv": "k_bwd_dqk_dv",
                 "fwd_fused": "k_fwd_fused", "intra": "k_intra",
                 "state_scan_fwd": "k_state_scan", "state_scan_rev": "k_state_scan",
                 "state_scans": "k_state_scan", "seg_state": "k_state_scan",
-                "output": "k_output", "gate_cumsum": "k_gate_cumsum", "gate_grad": "k_gate_grad",
+                "output": "k_output",
                 "gate_tot": "k_gate_tot", "gate_reduce": "k_gate_reduce", "state_dot": "k_state_dot",
                 "state_scan": "k_state_scan", "intra_fwd": "k_intra", "intra_bwd": "k_intra"}
 STAGE_SOURCE = {"bwd_dqk_dv": "k_bwd.hip",
                 "fwd_fused": "k_fwd.hip", "intra": "k_intra.hip",
                 "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip",
                 "state_scans": "k_state.hip", "seg_state": "k_state.hip",
-                "output": "k_fwd.hip", "gate_cumsum": "k_gate.hip", "gate_grad": "k_gate.hip",
+                "output": "k_fwd.hip",
                 "gate_tot": "k_gate.hip", "gate_reduce": "k_gate.hip", "state_dot": "k_gate.hip",
                 "state_scan": "k_state.hip", "intra_fwd": "k_intra.hip", "intra_bwd": "k_intra.hip"}
 
