@@ -45,7 +45,6 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // e^x with the hardware base-2 exponential.  Arguments here are differences of
 // cumulative log-gates (<= 0 in every use), so no overflow handling is needed.
-__device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
@@ -469,83 +468,6 @@ struct WaveColTile {
       const int c = 8 * cb + e;
       *reinterpret_cast<u32x4*>(lds + c * 64 + 8 * swz64(c, rb)) = o;
     }
-  }
-};
-
-// ---------------------------------------------------------------------------------
-// Transposing fragment reads (CDNA4 ds_read_b64_tr_b16).  Within each group of 16
-// lanes, lane i receives element i % 4 of the four 16-bit words addressed by lanes
-// i / 4 + 4e, e = 0..3 (checked on the device).  A tile kept in LDS in its global
-// orientation can so feed MFMA fragments whose k-index runs down its rows.
-// ---------------------------------------------------------------------------------
-// A ROWS x 64 bf16 tile of a row-major [*, gld] matrix (rows beyond `rows` zero) kept in
-// LDS in its own orientation: 128-byte rows, the eight 16-byte chunks of row t permuted
-// by chunk ^ 2 * ((t / 8) % 4).  With that permutation the row stores and the transposing
-// reads of load_frag_tr each touch every LDS bank the minimum number of times.
-template <int ROWS>
-struct SwzTile {
-  static constexpr int kUnits = ROWS * 8;
-  static constexpr int kPerThread = (kUnits + kThreads - 1) / kThreads;
-  u32x4 u[kPerThread];
-  __device__ __forceinline__ void load(const bf16* __restrict__ g, long gld, int rows) {
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int idx = threadIdx.x + j * kThreads, t = idx >> 3, h = idx & 7;
-      if (kUnits % kThreads == 0 || idx < kUnits)
-        u[j] = t < rows ? *reinterpret_cast<const u32x4*>(g + t * gld + 8 * h) : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(bf16* lds) const {
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int idx = threadIdx.x + j * kThreads, t = idx >> 3, h = idx & 7;
-      if (kUnits % kThreads == 0 || idx < kUnits)
-        *reinterpret_cast<u32x4*>(lds + t * 64 + 8 * (h ^ (2 * ((t >> 3) & 3)))) = u[j];
-    }
-  }
-};
-// Fragment (contiguous k order) whose k-index is the tile row: lane (r, q) receives
-// tile[k0 + 8q + e][c0 + r], e = 0..7; k0 a multiple of 32, c0 of 16.  It is the B operand
-// of a product over the tile's rows, or the A operand when the tile holds A transposed.
-__device__ __forceinline__ void load_frag_tr(Frag<bf16>& f, const bf16* tile, int k0, int c0) {
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  const int l = lane_id(), s = l & 15, q = l >> 4;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int t = k0 + 8 * q + 4 * h + (s >> 2);
-    const int pg = ((c0 >> 2) + (s & 3)) ^ (4 * ((t >> 3) & 3));   // 8-byte group, permuted
-    const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4s*)(tile + t * 64 + 4 * pg));
-    const bf16x4 b = __builtin_bit_cast(bf16x4, x);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f.v[4 * h + e] = b[e];
-  }
-}
-
-// The token-indexed operand of a k32 product over a chunk's tokens: a ROWS (tokens) x 64
-// (columns) slice of a row-major [*, gld] matrix, read as fragments for 16-column groups.
-// bf16: kept in its own orientation, read with transposing loads; fp32: staged
-// transposed (ColTile), read with plain fragment loads.
-template <typename OpT, int ROWS> struct KTile;
-template <int ROWS>
-struct KTile<bf16, ROWS> {
-  static constexpr int kLdsElems = ROWS * 64;
-  SwzTile<ROWS> t;
-  __device__ __forceinline__ void load(const bf16* __restrict__ g, long gld, int rows) { t.load(g, gld, rows); }
-  __device__ __forceinline__ void store(bf16* lds) const { t.store(lds); }
-  static __device__ __forceinline__ void frag(Frag<bf16>& f, const bf16* lds, int kb, int j) {
-    load_frag_tr(f, lds, 32 * kb, 16 * j);
-  }
-};
-template <int ROWS>
-struct KTile<float, ROWS> {
-  static constexpr int LD = ROWS + 8;
-  static constexpr int kLdsElems = 64 * LD;
-  ColTile<float, float, ROWS, LD> t;
-  __device__ __forceinline__ void load(const float* __restrict__ g, long gld, int rows) { t.load(g, gld, rows); }
-  __device__ __forceinline__ void store(float* lds) const { t.store(lds); }
-  static __device__ __forceinline__ void frag(Frag<float>& f, const float* lds, int kb, int j) {
-    load_frag_c(f, lds + (16 * j + (lane_id() & 15)) * LD + kb * 32);
   }
 };
 

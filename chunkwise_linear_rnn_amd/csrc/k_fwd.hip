@@ -580,10 +580,8 @@ static hipError_t launch_output_t(const OutArgs& a, hipStream_t s) {
 
 hipError_t launch_output(const OutArgs& a, hipStream_t s) {
   if (a.BH == 0 || a.N == 0) return hipSuccess;
-  if (a.dtype == 0) {
-    if (a.C == 64) return launch_output_t<float, float, 64>(a, s);
-    return launch_output_t<float, float, 128>(a, s);
-  }
+  if (a.dtype == 0)   // fp32 operands come with chunk 64 only
+    return a.C == 64 ? launch_output_t<float, float, 64>(a, s) : hipErrorInvalidValue;
   if (a.C == 64) return launch_output_t<bf16, bf16, 64>(a, s);
   return launch_output_t<bf16, bf16, 128>(a, s);
 }
@@ -605,20 +603,19 @@ static hipError_t launch_fused_t2(const FusedArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((k_fwd_fused_c128<Tin, DK>), grid, dim3(kFusedThreads), 0, s,
                        (const bf16*)a.Qh, (const bf16*)a.KhT, (const bf16*)a.A, a.eg,
                        (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N, nseg, a.S_mid);
-    return hipGetLastError();
-  }
-  if constexpr (C == 64 && sizeof(OpT) == 2) {
+  } else if constexpr (C == 64 && sizeof(OpT) == 2) {
     const int nseg = a.S_mid && a.nseg > 1 ? a.nseg : 1;
     dim3 grid((a.dv / 64) * a.BH * nseg);
     hipLaunchKernelGGL((k_fwd_fused_staged<Tin, OpT, C, DK>), grid, dim3(kFusedThreads), 0, s,
                        (const OpT*)a.Qh, (const OpT*)a.KhT, (const OpT*)a.A, a.eg,
                        (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N, nseg, a.S_mid);
-    return hipGetLastError();
+  } else {   // fp32, chunk 64: operand fragments read straight from memory
+    static_assert(C == 64, "fp32 operands come with chunk 64 only");
+    dim3 grid((a.dv / 64) * a.BH);
+    hipLaunchKernelGGL((k_fwd_fused<Tin, OpT, C, DK>), grid, dim3(kThreads), 0, s,
+                       (const OpT*)a.Qh, (const OpT*)a.KhT, (const OpT*)a.A, a.eg,
+                       (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N);
   }
-  dim3 grid((a.dv / 64) * a.BH);
-  hipLaunchKernelGGL((k_fwd_fused<Tin, OpT, C, DK>), grid, dim3(kThreads), 0, s,
-                     (const OpT*)a.Qh, (const OpT*)a.KhT, (const OpT*)a.A, a.eg,
-                     (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N);
   return hipGetLastError();
 }
 template <typename Tin, typename OpT, int C>
@@ -633,10 +630,8 @@ static hipError_t launch_fused_t(const FusedArgs& a, hipStream_t s) {
 
 hipError_t launch_fwd_fused(const FusedArgs& a, hipStream_t s) {
   if (a.BH == 0 || a.N == 0) return hipSuccess;
-  if (a.dtype == 0) {
-    if (a.C == 64) return launch_fused_t<float, float, 64>(a, s);
-    return launch_fused_t<float, float, 128>(a, s);
-  }
+  if (a.dtype == 0)
+    return a.C == 64 ? launch_fused_t<float, float, 64>(a, s) : hipErrorInvalidValue;
   if (a.C == 64) return launch_fused_t<bf16, bf16, 64>(a, s);
   return launch_fused_t<bf16, bf16, 128>(a, s);
 }
