@@ -82,6 +82,12 @@ constexpr int dqk_lds_bytes(int C, int ES = 2) {
   return C * (C + 4) * 4 + (C * 68 > 64 * (C + 4) ? C * 68 : 64 * (C + 4)) * 4 + 2 * C * 72 * ES;
 }
 constexpr int kDqkLds = dqk_lds_bytes(64);
+// LDS of a dv workgroup: the Kh block [C][row pad], the dS^T tile [64][64 + pad], A^T and
+// dO^T [C + 64][C + pad] (see bwd_dv_body)
+constexpr int dv_lds_bytes(int C, int ES = 2) {
+  return C * (ES == 2 ? 80 : 68) * ES + 64 * (ES == 2 ? 72 : 68) * ES +
+         (C + 64) * (ES == 2 ? C + 8 : C + 4) * ES;
+}
 // Row pad of a row-major 64-wide fragment-source tile in LDS: bf16 rows of 80 elements,
 // fp32 rows of 68 (16-byte fragment reads of 16 consecutive rows on distinct banks)
 template <typename T> constexpr int frag_row_ld() { return sizeof(T) == 2 ? 64 + 16 : 64 + 4; }
@@ -634,11 +640,12 @@ __device__ __forceinline__ void bwd_dv_body(char* __restrict__ arena, int lt,
   }
 }
 
-// The two backward chunk kernels as one launch: dq / dk / dlog_alpha workgroups and dv
-// workgroups interleaved in proportion (a dv workgroup needs neither the chunk totals nor
-// anything the dq / dk workgroups write), so that their memory phases overlap on each CU.
-template <typename Tin, typename OpT, bool SFRAG, bool SG, int C>
-__global__ __launch_bounds__(kThreads, C == 128 ? 1 : sizeof(OpT) == 2 ? 3 : 2) void k_bwd_dqk_dv(
+// The two backward chunk kernels as one launch (MODE 0): dq / dk / dlog_alpha workgroups
+// and dv workgroups interleaved in proportion (a dv workgroup needs neither the chunk
+// totals nor anything the dq / dk workgroups write), so that their memory phases overlap
+// on each CU.  MODE 1 / 2: one kind only, in a launch of its own, with its own LDS size.
+template <typename Tin, typename OpT, bool SFRAG, bool SG, int C, int MODE = 0>
+__global__ __launch_bounds__(kThreads, MODE == 2 ? 2 : C == 128 ? 1 : sizeof(OpT) == 2 ? 3 : 2) void k_bwd_dqk_dv(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dO, int gscalar, const OpT* __restrict__ S,
     const OpT* __restrict__ dS, Tin* __restrict__ dq, Tin* __restrict__ dk_out,
@@ -646,16 +653,24 @@ __global__ __launch_bounds__(kThreads, C == 128 ? 1 : sizeof(OpT) == 2 ? 3 : 2) 
     GateFn gf, Tin* __restrict__ dla, float* __restrict__ dla_part, const OpT* __restrict__ Kh,
     const OpT* __restrict__ A, Tin* __restrict__ dv_out, int T, int dk, int dv, int N,
     int n_dqk) {
-  __shared__ __attribute__((aligned(16))) char arena[dqk_lds_bytes(C, sizeof(OpT))];
+  __shared__ __attribute__((aligned(16)))
+  char arena[MODE == 2 ? dv_lds_bytes(C, sizeof(OpT)) : dqk_lds_bytes(C, sizeof(OpT))];
   const int L = xcd_logical(blockIdx.x, gridDim.x);
-  const long total = gridDim.x;
-  // Bresenham split: logical id L is a dq/dk workgroup when the count of them up to L grows
-  const int before = (int)(((long)L * n_dqk) / total), upto = (int)(((long)(L + 1) * n_dqk) / total);
-  if (upto > before)
-    bwd_dqk_body<Tin, OpT, SFRAG, SG, C>(arena, before, q, k, v, dO, gscalar, S, dS, dq, dk_out, tot, cT, la, gf,
-                           dla, dla_part, T, dk, dv, N);
-  else
-    bwd_dv_body<Tin, OpT, SFRAG, C>(arena, L - before, Kh, A, dS, dO, dv_out, T, dk, dv, N);
+  if constexpr (MODE == 1) {
+    bwd_dqk_body<Tin, OpT, SFRAG, SG, C>(arena, L, q, k, v, dO, gscalar, S, dS, dq, dk_out, tot,
+                                         cT, la, gf, dla, dla_part, T, dk, dv, N);
+  } else if constexpr (MODE == 2) {
+    bwd_dv_body<Tin, OpT, SFRAG, C>(arena, L, Kh, A, dS, dO, dv_out, T, dk, dv, N);
+  } else {
+    const long total = gridDim.x;
+    // Bresenham split: logical id L is a dq/dk workgroup when the count of them up to L grows
+    const int before = (int)(((long)L * n_dqk) / total), upto = (int)(((long)(L + 1) * n_dqk) / total);
+    if (upto > before)
+      bwd_dqk_body<Tin, OpT, SFRAG, SG, C>(arena, before, q, k, v, dO, gscalar, S, dS, dq, dk_out, tot, cT, la, gf,
+                             dla, dla_part, T, dk, dv, N);
+    else
+      bwd_dv_body<Tin, OpT, SFRAG, C>(arena, L - before, Kh, A, dS, dO, dv_out, T, dk, dv, N);
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -666,14 +681,25 @@ static hipError_t launch_bwd_t2(const BwdArgs& a, hipStream_t s) {
     // scalar gates: the C x C decay-matrix form of the intra-chunk terms; fragment-order
     // states come with bf16 and chunk 64 only (the scans' 128-column tiles)
     constexpr bool kSF = sizeof(OpT) == 2 && C == 64;
-    auto kern = a.gscalar ? (a.s_frag ? k_bwd_dqk_dv<Tin, OpT, kSF, true, C> : k_bwd_dqk_dv<Tin, OpT, false, true, C>)
-                          : (a.s_frag ? k_bwd_dqk_dv<Tin, OpT, kSF, false, C> : k_bwd_dqk_dv<Tin, OpT, false, false, C>);
-    hipLaunchKernelGGL(kern, dim3(n_dqk + n_dv), dim3(kThreads), 0, s,
-                       (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO,
-                       a.gscalar ? 1 : 0, (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq,
-                       (Tin*)a.dk_out, a.tot, a.cT,
-                       (const Tin*)a.la, a.gate, (Tin*)a.dla, a.dla_part, (const OpT*)a.Kh,
-                       (const OpT*)a.A, (Tin*)a.dv_out, a.T, a.dk, a.dv, a.N, n_dqk);
+    auto go = [&](auto kern, int nwg) {
+      hipLaunchKernelGGL(kern, dim3(nwg), dim3(kThreads), 0, s,
+                         (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, (const Tin*)a.dO,
+                         a.gscalar ? 1 : 0, (const OpT*)a.S, (const OpT*)a.dS, (Tin*)a.dq,
+                         (Tin*)a.dk_out, a.tot, a.cT,
+                         (const Tin*)a.la, a.gate, (Tin*)a.dla, a.dla_part, (const OpT*)a.Kh,
+                         (const OpT*)a.A, (Tin*)a.dv_out, a.T, a.dk, a.dv, a.N, n_dqk);
+    };
+    if constexpr (C == 128) {
+      // one dq/dk workgroup per CU (139 KB of LDS): the dv workgroups run in a launch of
+      // their own at two per CU
+      if (a.gscalar) go(k_bwd_dqk_dv<Tin, OpT, false, true, C, 1>, n_dqk);
+      else go(k_bwd_dqk_dv<Tin, OpT, false, false, C, 1>, n_dqk);
+      go(k_bwd_dqk_dv<Tin, OpT, false, false, C, 2>, n_dv);
+    } else {
+      auto kern = a.gscalar ? (a.s_frag ? k_bwd_dqk_dv<Tin, OpT, kSF, true, C> : k_bwd_dqk_dv<Tin, OpT, false, true, C>)
+                            : (a.s_frag ? k_bwd_dqk_dv<Tin, OpT, kSF, false, C> : k_bwd_dqk_dv<Tin, OpT, false, false, C>);
+      go(kern, n_dqk + n_dv);
+    }
   }
   return hipGetLastError();
 }
