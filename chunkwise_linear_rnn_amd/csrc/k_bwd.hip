@@ -24,8 +24,9 @@
 // their fp32 states (summed by the gate-total kernel before this launch).
 //
 // Kernel
-//   k_bwd_dqk_dv (bf16 with chunk 64 or 128, fp32 with chunk 64) one launch holding two
-//   kinds of workgroup, interleaved:
+//   k_bwd_dqk_dv (bf16 with chunk 64 or 128, fp32 with chunk 64) two kinds of workgroup,
+//   interleaved in one launch (chunk 64), or in a launch each (chunk 128, where the dq/dk
+//   workgroups' LDS would otherwise hold the dv workgroups to one per CU as well):
 //   dq/dk part  dq, dk and dlog_alpha per (chunk, 64-wide dk block): D as
 //              chunk-local suffix sums plus the carry from the later chunks' totals
 //              (formed by the gate-total kernel from the scans).  One pass over
@@ -37,7 +38,8 @@
 //              blocks.
 //   fp32 operands take tiles with rows padded for 4-byte elements, unswizzled
 //   transposed staging and the off-diagonal products as plain fp32 MFMAs (two
-//   workgroups per CU); chunk 128 keeps two dA row tiles per wave (one per CU).
+//   workgroups per CU); chunk 128 keeps two dA row tiles per wave (dq/dk workgroups one
+//   per CU, dv workgroups two).
 #include "gla_common.cuh"
 #include "gla_gate.cuh"
 #include "gla_internal.h"
