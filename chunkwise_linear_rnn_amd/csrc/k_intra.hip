@@ -127,8 +127,9 @@ __global__ __launch_bounds__(kThreads) void k_intra(
   for (int p = 0; p < (PPW > 0 ? PPW : 1); ++p) accp[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < NDW; ++p) accd[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (WANT_A)
-    for (int item = threadIdx.x; item < NITEM; item += kThreads) dacc[item] = 0.f;
+  // some pass took the log-space diagonal sums (their partials are in dacc, which the
+  // first such pass initializes: each item is only ever touched by its own thread there)
+  bool anywide = false;
 
   // The next dk block's log_alpha (or gate logits), q and k are loaded into registers
   // while the current block computes.
@@ -302,38 +303,57 @@ __global__ __launch_bounds__(kThreads) void k_intra(
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc += xq[e] * xk[e] * __builtin_amdgcn_exp2f(gt[e] - gsr[e]);
           }
-          dacc[item] += acc;
+          dacc[item] = (anywide ? dacc[item] : 0.f) + acc;
         }
       }
+      anywide = true;
       }
     }
     __syncthreads();
   }
 
   if constexpr (WANT_A) {
-    // the MFMA part of the diagonal entries (t = 4 qd + e, s = r in sub-block I) joins
-    // the fp32 part on the first column-quarter item of the entry
-#pragma unroll
-    for (int dI = 0; dI < NDW; ++dI) {
-      const int I = w + 4 * dI;
-      if (I < NS) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tt = 4 * qd + e;
-          if (r <= tt) dacc[(I * 136 + tt * (tt + 1) / 2 + r) << 2] += accd[dI][e];
-        }
-      }
-    }
     // The block is assembled in LDS (in the g tile, dead after the last pass) when it fits
-    // there, and leaves as 16-byte rows; otherwise it is written entry by entry.
+    // there, and leaves as 16-byte rows with the entries above the diagonal zeroed on the
+    // way; otherwise it is written entry by entry, zeros included.
     OpT* Ab = A_out + ((long)bh * N + i) * C * C;
     constexpr int ALD = C + 8;
     constexpr bool kStageA = C * ALD * (int)sizeof(OpT) <= C * GLD * 4;
     OpT* At = kStageA ? reinterpret_cast<OpT*>(gs) : Ab;
     const int ald = kStageA ? ALD : C;
-    for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {   // zero above the diagonal
-      const int t = idx / C, s = idx % C;
-      if (s > t) At[t * ald + s] = from_f32<OpT>(0.f);
+    if (anywide) {
+      // the MFMA part of the diagonal entries (t = 4 qd + e, s = r in sub-block I) joins
+      // the log-space part on the first column-quarter item of the entry
+#pragma unroll
+      for (int dI = 0; dI < NDW; ++dI) {
+        const int I = w + 4 * dI;
+        if (I < NS) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int tt = 4 * qd + e;
+            if (r <= tt) dacc[(I * 136 + tt * (tt + 1) / 2 + r) << 2] += accd[dI][e];
+          }
+        }
+      }
+    } else {
+      // every pass summed the diagonal sub-blocks on the matrix units: they are complete
+#pragma unroll
+      for (int dI = 0; dI < NDW; ++dI) {
+        const int I = w + 4 * dI;
+        if (I < NS) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int tt = 4 * qd + e;
+            At[(16 * I + tt) * ald + 16 * I + r] = from_f32<OpT>(r <= tt ? accd[dI][e] : 0.f);
+          }
+        }
+      }
+    }
+    if constexpr (!kStageA) {
+      for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {   // zero above the diagonal
+        const int t = idx / C, s = idx % C;
+        if (s / 16 > t / 16) At[t * ald + s] = from_f32<OpT>(0.f);
+      }
     }
 #pragma unroll
     for (int pi = 0; pi < PPW; ++pi) {
@@ -346,19 +366,22 @@ __global__ __launch_bounds__(kThreads) void k_intra(
           At[(16 * I + 4 * qd + e) * ald + 16 * J + r] = from_f32<OpT>(accp[pi][e]);
       }
     }
-    __syncthreads();
-    // four column-quarter partials of each diagonal entry sit in adjacent lanes
+    if (anywide) {
+      __syncthreads();
+      // four column-quarter partials of each diagonal entry sit in adjacent lanes
 #pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-      const int item = threadIdx.x + kThreads * j;
-      float v = item < NITEM ? dacc[item] : 0.f;
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      if (item < NITEM && (item & 3) == 0) {
-        const int pr = item >> 2, I = pr / 136;
-        int tt, ss;
-        tri_decode(pr % 136, tt, ss);
-        At[(16 * I + tt) * ald + 16 * I + ss] = from_f32<OpT>(v);
+      for (int j = 0; j < IPT; ++j) {
+        const int item = threadIdx.x + kThreads * j;
+        float v = item < NITEM ? dacc[item] : 0.f;
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        if (item < NITEM && (item & 3) == 0) {
+          const int pr = item >> 2, I = pr / 136;
+          int tt, ss;
+          tri_decode(pr % 136, tt, ss);
+          At[(16 * I + tt) * ald + 16 * I + ss] = from_f32<OpT>(v);
+          if (ss < tt) At[(16 * I + ss) * ald + 16 * I + tt] = from_f32<OpT>(0.f);
+        }
       }
     }
     if constexpr (kStageA) {
@@ -368,7 +391,12 @@ __global__ __launch_bounds__(kThreads) void k_intra(
 #pragma unroll
       for (int u_ = 0; u_ < C * kRowUnits / kThreads; ++u_) {
         const int idx = threadIdx.x + u_ * kThreads, rr = idx / kRowUnits, cc = (idx % kRowUnits) * kPer;
-        *reinterpret_cast<u32x4*>(Ab + rr * C + cc) = *reinterpret_cast<const u32x4*>(At + rr * ALD + cc);
+        union { u32x4 u; OpT x[kPer]; } row;
+        row.u = *reinterpret_cast<const u32x4*>(At + rr * ALD + cc);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+          if (cc + j > rr) row.x[j] = from_f32<OpT>(0.f);
+        *reinterpret_cast<u32x4*>(Ab + rr * C + cc) = row.u;
       }
     }
   }
