@@ -367,6 +367,40 @@ def test_diagonal_paths_bf16(gla):
         check(k, pick(host(t), heads), ref[k], "bf16")
 
 
+@pytest.mark.parametrize("dt,C", [("bf16", 128), ("f32", 64)])
+def test_diagonal_paths_mixed(gla, dt, C):
+    """As above for chunk 128 (bf16) and for fp32 inputs (whose A block is written entry by
+    entry): in each chunk one 64-column pass takes the log-space diagonal sums (a column at
+    log_alpha = -12) and the others the matrix-unit path, so the diagonal entries add both
+    kinds of partial sums, and the entries above the diagonal must come out zero."""
+    cfg = GlaConfig("diagmix", dt, 1, 2, 2 * C + 37, 128, 64, C, seed=13)
+    say(f"[edge] diagonal paths mixed {cfg}")
+    d = generate(cfg)
+    la = d["log_alpha"].copy()
+    la[:, :, 0:64, 5] = -12.0
+    la[:, :, C:C + 64, 70] = -12.0
+    la[:, :, 2 * C:, 100] = -12.0
+    d2 = dict(d)
+    if dt == "bf16":
+        from gla_inputs import round_to_bf16_bits, bf16_bits_to_f64
+        bits = round_to_bf16_bits(la)
+        d2["log_alpha"], d2["log_alpha_store"] = bf16_bits_to_f64(bits), bits
+    else:
+        d2["log_alpha"], d2["log_alpha_store"] = la, la.astype(np.float32)
+    x = dev_inputs(d2, dt, DEV)
+    o, ST = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], chunk=C)
+    om, _ = gla.fwd(x["q"], x["k"], x["v"], x["log_alpha"], chunk=C, state_mode="materialized")
+    g = gla.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["dO"], chunk=C)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (0, 1)]
+    ref = oracle_heads(d2, heads)
+    check_heads("o", host(o), ref["o"], heads, dt)
+    check_heads("o mat", host(om), ref["o"], heads, dt)
+    check_heads("S_T", host(ST), ref["S_T"], heads, dt)
+    for kname, t in zip(("dq", "dk", "dv", "dla", "dS0"), g):
+        check_heads(kname, host(t), ref[kname], heads, dt)
+
+
 @pytest.mark.parametrize("diag", ["f32", "bf16"])
 def test_diagonal_rebased_band(gla, diag):
     """The rebased diagonal sub-block product where its factors are largest: a few key
