@@ -277,15 +277,17 @@ gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* desc, const void* q, const void* 
  * gla_trace_stages returns n for a pass (with_dS_T: whether the backward gets a dS_T) and
  * writes up to max_names static stage names to `names` (nullable); -1 on a NULL desc or a
  * bad pass.  The stages are
- *   forward, materialized: gate_cumsum, intra, state_scan (in sequence segments when few
- *                          workgroups would walk the whole sequence), output
+ *   forward, materialized: intra (it forms the gate cumsum itself), state_scan (in
+ *                          sequence segments when few workgroups would walk the whole
+ *                          sequence), output
  *   forward, recompute:    intra, seg_state (bf16, at least 4 chunks: the states at the
  *                          starts of the sequence segments that the fused kernel walks in
  *                          parallel, and their chaining; no launch otherwise), fwd_fused
  *   backward:              intra, state_scans (the forward and the reverse scan, in one
  *                          launch, or in sequence segments when few workgroups would walk
  *                          them), [state_dot when dS_T is given], gate_tot, bwd_dqk_dv
- *                          (dq/dk/dlog_alpha and dv workgroups in one launch), and with
+ *                          (dq/dk/dlog_alpha and dv workgroups: one launch at chunk 64,
+ *                          two at chunk 128), and with
  *                          scalar gates gate_reduce (the gradient summed over dk) */
 int32_t gla_trace_stages(const gla_desc_t* desc, int32_t pass, int32_t with_dS_T,
                          const char** names, int32_t max_names);
