@@ -180,9 +180,9 @@ struct BwdArgs {
   bool gscalar;            // la holds one gate per token: [BH][T]
   bool s_frag;             // S and dS in MFMA fragment order, as the scans wrote them
 };
-// The backward chunk work (launch_bwd_chunk, after the chunk totals are formed): one
-// launch of dq / dk / dlog_alpha workgroups interleaved with dv workgroups (bf16 with
-// chunk 64 or 128, fp32 with chunk 64).
+// The backward chunk work (launch_bwd_chunk, after the chunk totals are formed): dq / dk /
+// dlog_alpha workgroups and dv workgroups (bf16 with chunk 64 or 128, fp32 with chunk 64),
+// interleaved in one launch at chunk 64, a launch each at chunk 128.
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s);
 
 // Recurrent evaluation (decoding): T tokens in order, state updated in place.
