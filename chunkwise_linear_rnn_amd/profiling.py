@@ -20,6 +20,12 @@ kernel belongs to one, with the kernel source hash): bf16 MFMA work per launch
 (MOPS x 512 flop), the busy fraction of the 1024 SIMDs' matrix units over the launch
 (busy cycles / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs)) and the achieved fraction of the
 2.5 PFLOP/s bf16 peak at 2.4 GHz.
+
+    python -m chunkwise_linear_rnn_amd.profiling valu <counter csv> <workload> "<command>"
+
+`valu` turns one `rocprofv3 --pmc` run of the counters in VALU_COUNTERS into per-kernel
+instruction mixes (JSON, like `mfma`): vector-ALU, transcendental, matrix, LDS and scalar
+instructions per wave, and the share of the SIMDs' cycles that the vector-ALU issue takes.
 """
 from __future__ import annotations
 
@@ -174,6 +180,46 @@ def mfma(path, workload, command, root):
             "kernels": kernels}
 
 
+VALU_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+                 "SQ_INSTS_SALU", "SQ_WAVES", "GRBM_GUI_ACTIVE")
+
+
+def valu(path, workload, command, root):
+    """Per-kernel instruction mix (averages per launch) from one counter run of
+    VALU_COUNTERS: instructions per wave, and the share of the 1024 SIMDs' cycles over the
+    launch that issuing the vector-ALU instructions takes, counting 4 cycles per wave64
+    instruction and 16 per transcendental (matrix instructions are not vector-ALU issue
+    here and are left out)."""
+    rows = list(csv.DictReader(open(path)))
+    agg = {}
+    for r in rows:
+        d = agg.setdefault(r["Kernel_Name"], {})
+        d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    kernels = []
+    for name, d in agg.items():
+        if any(c not in d for c in VALU_COUNTERS):
+            continue
+        mean = {c: sum(v) / len(v) for c, v in d.items()}
+        cycles = mean["GRBM_GUI_ACTIVE"] / XCDS
+        waves = max(mean["SQ_WAVES"], 1.0)
+        vec = mean["SQ_INSTS_VALU"] - mean["SQ_INSTS_MFMA"]
+        trans = mean["SQ_INSTS_VALU_TRANS_F32"]
+        issue = 4.0 * (vec - trans) + 16.0 * trans
+        kernels.append({"kernel": short(name), "symbol": name[:120],
+                        "launches": len(d["GRBM_GUI_ACTIVE"]),
+                        "gpu_cycles_per_launch": cycles, "waves": mean["SQ_WAVES"],
+                        "valu_per_wave": vec / waves, "trans_per_wave": trans / waves,
+                        "mfma_per_wave": mean["SQ_INSTS_MFMA"] / waves,
+                        "lds_per_wave": mean["SQ_INSTS_LDS"] / waves,
+                        "salu_per_wave": mean["SQ_INSTS_SALU"] / waves,
+                        "valu_issue_frac": issue / (cycles * SIMDS) if cycles else 0.0,
+                        "stages": [st for st in MFMA_STAGES if matches(st, name)]})
+    kernels.sort(key=lambda k: -k["gpu_cycles_per_launch"] * k["launches"])
+    digests = {st: source_digest(st, root) for st in MFMA_STAGES}
+    return {"workload": workload, "command": command, "source_sha256": digests,
+            "kernels": kernels}
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         sys.stdout.write(stats_table(sys.argv[2], sys.argv[3]))
@@ -185,3 +231,6 @@ if __name__ == "__main__":
     elif sys.argv[1] == "mfma":
         root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
         print(json.dumps(mfma(sys.argv[2], sys.argv[3], sys.argv[4], root), indent=1))
+    elif sys.argv[1] == "valu":
+        root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+        print(json.dumps(valu(sys.argv[2], sys.argv[3], sys.argv[4], root), indent=1))

@@ -51,3 +51,30 @@ def test_counter_scaling_and_its_checks(tmp_path):
     assert r["launches"] == 2
     assert abs(r["fetch_bytes_per_launch"] - 2000.0 * 1024 * 2.0) < 1e-6
     assert abs(r["write_bytes_per_launch"] - 500.0 * 1024) < 1e-6
+
+
+def test_valu_instruction_mix(tmp_path):
+    """Instructions per wave and the vector-ALU issue share: matrix instructions are taken
+    out of the vector-ALU count, transcendentals take 16 cycles, the others 4, over the
+    launch's cycles on 1024 SIMDs (GRBM_GUI_ACTIVE summed over 8 XCDs)."""
+    name = "_ZN3gla7k_intraIDF16bDF16bDF16bLi64ELb1ELb0EEEv"
+    vals = {"SQ_INSTS_VALU": [1100.0, 1300.0], "SQ_INSTS_VALU_TRANS_F32": [100.0, 100.0],
+            "SQ_INSTS_MFMA": [200.0, 200.0], "SQ_INSTS_LDS": [50.0, 70.0],
+            "SQ_INSTS_SALU": [10.0, 10.0], "SQ_WAVES": [4.0, 4.0],
+            "GRBM_GUI_ACTIVE": [8.0 * 100.0, 8.0 * 100.0]}
+    p = tmp_path / "v.csv"
+    with open(p, "w") as f:
+        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+        for c, vs in vals.items():
+            for v in vs:
+                f.write(f'"{name}",{c},{v}\n')
+        f.write('"other_kernel",SQ_INSTS_VALU,5\n')   # a kernel without the full set: skipped
+    r = profiling.valu(str(p), "w", "cmd", ".")
+    assert len(r["kernels"]) == 1
+    k = r["kernels"][0]
+    assert k["launches"] == 2 and k["gpu_cycles_per_launch"] == 100.0
+    assert k["valu_per_wave"] == (1200.0 - 200.0) / 4 and k["trans_per_wave"] == 25.0
+    assert k["mfma_per_wave"] == 50.0 and k["lds_per_wave"] == 15.0
+    issue = 4.0 * (1000.0 - 100.0) + 16.0 * 100.0
+    assert abs(k["valu_issue_frac"] - issue / (100.0 * 1024)) < 1e-15
+    assert k["stages"] == ["intra_fwd"]   # the forward variant (bf16 transposed operands)
