@@ -17,15 +17,15 @@ and GLAFunction, a torch.autograd.Function over fwd/bwd.
 from __future__ import annotations
 
 from ._native import (GlaDesc, GlaError, F32, BF16, MATERIALIZED, RECOMPUTE, PASS_FWD,  # noqa: F401
-                      PASS_BWD, PASS_STATES, GATE_LOG_ALPHA, GATE_LOGITS, GATE_PER_KEY, GATE_SCALAR,
+                      PASS_BWD, PASS_STATES, PASS_FWD_SAVE, PASS_BWD_SAVED, GATE_LOG_ALPHA, GATE_LOGITS, GATE_PER_KEY, GATE_SCALAR,
                       DIAG_F32, DIAG_BF16,
                       lib, lib_path, make_desc, make_gsa_desc, gsa_workspace_bytes, status_string,
-                      trace_stages,
+                      trace_stages, saved_bytes,
                       validate, version, workspace_bytes)
-from .ops import (fwd, bwd, check_gates, gate_cumsum, chunk_states, decode, GLAFunction, gla,  # noqa: F401
+from .ops import (fwd, bwd, fwd_save, bwd_saved, check_gates, gate_cumsum, chunk_states, decode, GLAFunction, gla,  # noqa: F401
                   GSAFunction, gsa, gsa_fwd, gsa_bwd)
 
-__all__ = ["fwd", "bwd", "check_gates", "gate_cumsum", "chunk_states", "decode", "GLAFunction", "gla", "GlaDesc",
+__all__ = ["fwd", "bwd", "fwd_save", "bwd_saved", "saved_bytes", "check_gates", "gate_cumsum", "chunk_states", "decode", "GLAFunction", "gla", "GlaDesc",
            "GSAFunction", "gsa", "gsa_fwd", "gsa_bwd", "make_gsa_desc", "gsa_workspace_bytes",
            "GlaError", "make_desc", "workspace_bytes", "validate", "status_string", "version",
            "lib", "lib_path"]

@@ -17,7 +17,7 @@ GATE_LOG_ALPHA, GATE_LOGITS = 0, 1
 GATE_PER_KEY, GATE_SCALAR = 0, 1
 MATERIALIZED, RECOMPUTE = 0, 1
 DIAG_F32, DIAG_BF16 = 0, 1
-PASS_FWD, PASS_BWD, PASS_STATES = 0, 1, 2
+PASS_FWD, PASS_BWD, PASS_STATES, PASS_FWD_SAVE, PASS_BWD_SAVED = 0, 1, 2, 3, 4
 
 # Every function include/gla.h declares, with its ctypes signature.
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
@@ -55,6 +55,11 @@ SIGNATURES = {
     "gla_chunk_bwd": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp, _sz, _vp]),
     "gla_chunk_fwd_noalloc": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "gla_saved_bytes": (_i32, [_PDESC, ctypes.POINTER(_sz)]),
+    "gla_chunk_fwd_save": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _sz,
+                                  _vp]),
+    "gla_chunk_bwd_saved": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _vp, _vp, _sz, _vp, _sz, _vp]),
     "gla_decode": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "gla_gsa_validate": (_i32, [_PGSA]),
     "gla_gsa_workspace_bytes": (_i32, [_PGSA, _i32, ctypes.POINTER(_sz)]),
@@ -65,6 +70,11 @@ SIGNATURES = {
                                     ctypes.POINTER(_vp), _i32]),
     "gla_chunk_bwd_traced": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _sz, _vp, ctypes.POINTER(_vp), _i32]),
+    "gla_chunk_fwd_save_traced": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                         _vp, _sz, _vp, ctypes.POINTER(_vp), _i32]),
+    "gla_chunk_bwd_saved_traced": (_i32, [_PDESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp,
+                                          ctypes.POINTER(_vp), _i32]),
 }
 
 _lib = None
@@ -123,6 +133,15 @@ def trace_stages(desc: GlaDesc, pass_: int, with_dS_T: bool = False) -> list:
     names = (ctypes.c_char_p * n)()
     lib().gla_trace_stages(ctypes.byref(desc), int(pass_), int(bool(with_dS_T)), names, n)
     return [x.decode() for x in names]
+
+
+def saved_bytes(desc: GlaDesc) -> int:
+    """Bytes of the buffer gla_chunk_fwd_save fills for gla_chunk_bwd_saved."""
+    out = _sz(0)
+    st = lib().gla_saved_bytes(ctypes.byref(desc), ctypes.byref(out))
+    if st != 0:
+        raise GlaError(st, "gla_saved_bytes")
+    return out.value
 
 
 def workspace_bytes(desc: GlaDesc, pass_: int = PASS_FWD) -> int:

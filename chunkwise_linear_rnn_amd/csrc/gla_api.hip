@@ -57,9 +57,15 @@ gla::ScanArgs mat_scan_shape(const Dims& x) {
   return a;
 }
 
+// Passes 3 (forward that saves the intra-chunk operands for the backward) and 4 (backward
+// that reads them): the forward / backward plan without those regions, which live in the
+// caller's saved buffer (saved_plan).
 Plan plan_of(const gla_desc_t* d, int pass) {
   const Dims x = dims_of(d);
   Plan p;
+  const bool saved = pass == GLA_PASS_FWD_SAVE || pass == GLA_PASS_BWD_SAVED;
+  if (pass == GLA_PASS_FWD_SAVE) pass = GLA_PASS_FWD;
+  if (pass == GLA_PASS_BWD_SAVED) pass = GLA_PASS_BWD;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -77,10 +83,12 @@ Plan plan_of(const gla_desc_t* d, int pass) {
     const int P = mat ? gla::scan_segments(mat_scan_shape(x)) : 1;
     if (P > 1) p.sslots = take((size_t)(P - 1) * x.BH * x.dk * x.dv * 4);
     if (P > 2) p.sdec = take((size_t)(P - 1) * x.BH * x.dk * 4);
-    p.A = take(AB);
-    p.Qh = take(opB);
-    p.KhT = take(opB);
-    p.eg = take(egB);
+    if (!saved) {
+      p.A = take(AB);
+      p.Qh = take(opB);
+      p.KhT = take(opB);
+      p.eg = take(egB);
+    }
     if (mat) p.st = take(stB);
     const int nseg = mat ? 1 : gla::fused_segments(x.dtype, (int)x.C, (int)x.N, (int)x.BH, (int)x.dv);
     if (nseg > 1) p.smid = take((size_t)(nseg - 1) * x.BH * x.dk * x.dv * 4);
@@ -90,11 +98,13 @@ Plan plan_of(const gla_desc_t* d, int pass) {
     const size_t op32 = rowsP * x.dk * 4;
     const size_t crossB = (size_t)x.BH * x.N * (x.dv / 64) * x.dk * 4;
     // (the chunk kernel rebuilds g from the gates: no g in the workspace)
-    p.A = take(AB);
-    p.QhT = take(op32);
-    p.Kh = take(opB);
-    p.KhT = take(op32);
-    p.eg = take(egB);
+    if (!saved) {
+      p.A = take(AB);
+      p.QhT = take(op32);
+      p.Kh = take(opB);
+      p.KhT = take(op32);
+      p.eg = take(egB);
+    }
     p.st = take(stB);
     p.dst = take(stB);
     p.ST = take((size_t)x.BH * x.dk * x.dv * 4);
@@ -116,6 +126,31 @@ Plan plan_of(const gla_desc_t* d, int pass) {
   }
   // the gate check's counter (GLA_DEBUG_CHECKS)
   if ((pass == GLA_PASS_FWD || pass == GLA_PASS_BWD) && x.BH * x.T > 0) p.dbg = take(256);
+  p.total = off;
+  return p;
+}
+
+// The saved buffer of a forward that keeps its intra-chunk operands for the backward: the
+// outputs of the backward's intra-chunk kernel (A, Qh^T and Kh^T as the scans read them,
+// Kh, e^gamma) plus the token-major Qh the fused forward reads.  Every region 256-byte
+// aligned.
+Plan saved_plan(const gla_desc_t* d) {
+  const Dims x = dims_of(d);
+  Plan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  const size_t rowsP = (size_t)x.BH * x.N * x.C;
+  const size_t opB = rowsP * x.dk * x.esz, op32 = rowsP * x.dk * 4;
+  p.A = take((size_t)x.BH * x.N * x.C * x.C * x.esz);
+  p.Qh = take(opB);
+  p.QhT = take(op32);
+  p.Kh = take(opB);
+  p.KhT = take(op32);
+  p.eg = take((size_t)x.BH * x.N * x.dk * 4);
   p.total = off;
   return p;
 }
@@ -194,23 +229,28 @@ struct Tracer {
 const char* const kFwdMat[] = {"intra", "state_scan", "output"};
 const char* const kFwdRec[] = {"intra", "seg_state", "fwd_fused"};
 const char* const kBwd[] = {"intra", "state_scans", "state_dot", "gate_tot", "bwd_dqk_dv"};
+const char* const kBwdSaved[] = {"state_scans", "state_dot", "gate_tot", "bwd_dqk_dv"};
 
 int stage_list(const gla_desc_t* d, int pass, int with_dST, const char** out, int max) {
   const char* const* src;
   int n;
-  if (pass == GLA_PASS_FWD) {
+  const bool bwd = pass == GLA_PASS_BWD || pass == GLA_PASS_BWD_SAVED;
+  int dot = 2;   // position of state_dot
+  if (pass == GLA_PASS_FWD || pass == GLA_PASS_FWD_SAVE) {
     if (d->state_mode == GLA_STATES_MATERIALIZED) { src = kFwdMat; n = 3; }
     else { src = kFwdRec; n = 3; }
+  } else if (pass == GLA_PASS_BWD_SAVED) {
+    src = kBwdSaved; n = 4; dot = 1;
   } else {
     src = kBwd; n = 5;
   }
   int m = 0;
   for (int j = 0; j < n; ++j) {
-    if (pass == GLA_PASS_BWD && j == 2 && !with_dST) continue;
+    if (bwd && j == dot && !with_dST) continue;
     if (out && m < max) out[m] = src[j];
     ++m;
   }
-  if (pass == GLA_PASS_BWD && d->gate_shape == GLA_GATE_SCALAR) {   // the sum over d
+  if (bwd && d->gate_shape == GLA_GATE_SCALAR) {   // the sum over d
     if (out && m < max) out[m] = "gate_reduce";
     ++m;
   }
@@ -223,7 +263,9 @@ extern "C" {
 
 int32_t gla_trace_stages(const gla_desc_t* d, int32_t pass, int32_t with_dS_T, const char** names,
                          int32_t max_names) {
-  if (!d || (pass != GLA_PASS_FWD && pass != GLA_PASS_BWD)) return -1;
+  if (!d || (pass != GLA_PASS_FWD && pass != GLA_PASS_BWD && pass != GLA_PASS_FWD_SAVE &&
+             pass != GLA_PASS_BWD_SAVED))
+    return -1;
   return stage_list(d, pass, with_dS_T, names, max_names);
 }
 
@@ -242,7 +284,7 @@ int32_t gla_version(void) { return 10000 * 0 + 100 * 2 + 0; }
 
 gla_status_t gla_validate(const gla_desc_t* d, int32_t pass) {
   if (!d) return GLA_ERR_INVALID_ARG;
-  if (pass < 0 || pass > 2) return GLA_ERR_INVALID_ARG;
+  if (pass < 0 || pass > GLA_PASS_BWD_SAVED) return GLA_ERR_INVALID_ARG;
   if (d->B < 0 || d->H < 0 || d->T < 0 || d->dk < 0 || d->dv < 0) return GLA_ERR_INVALID_ARG;
   if (d->chunk < 1 || d->subchunk < 1 || d->chunk % d->subchunk != 0) return GLA_ERR_INVALID_ARG;
   if (d->dtype != GLA_F32 && d->dtype != GLA_BF16) return GLA_ERR_INVALID_ARG;
@@ -259,6 +301,16 @@ gla_status_t gla_validate(const gla_desc_t* d, int32_t pass) {
   if (bh > 65535) return GLA_ERR_UNSUPPORTED;
   if (bh * (long long)d->T > (1LL << 31) - 1) return GLA_ERR_UNSUPPORTED;
   if (((long long)d->T + d->chunk - 1) / d->chunk > 65535) return GLA_ERR_UNSUPPORTED;
+  // the forward that saves for the backward walks the recomputed states
+  if (pass == GLA_PASS_FWD_SAVE && d->state_mode != GLA_STATES_RECOMPUTE) return GLA_ERR_UNSUPPORTED;
+  return GLA_OK;
+}
+
+gla_status_t gla_saved_bytes(const gla_desc_t* d, size_t* bytes) {
+  if (!bytes) return GLA_ERR_INVALID_ARG;
+  const gla_status_t st = gla_validate(d, GLA_PASS_FWD_SAVE);
+  if (st != GLA_OK) return st;
+  *bytes = saved_plan(d).total;
   return GLA_OK;
 }
 
@@ -328,13 +380,16 @@ gla_status_t gla_chunk_states(const gla_desc_t* d, const void* k, const void* v,
   return dev(gla::launch_state_scan(sa, s));
 }
 
-gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void* k,
-                                  const void* v, const void* log_alpha, const float* S0, void* o,
-                                  float* S_T, void* ws, size_t ws_bytes, void* stream,
-                                  void** events, int32_t n_events) {
-  const gla_status_t st = gla_validate(d, GLA_PASS_FWD);
+// The layer forward; save: the intra-chunk operands go to `saved` in the backward's layout
+// (saved_plan) for a later backward from them, and the rest of the forward reads them there.
+static gla_status_t fwd_run(const gla_desc_t* d, const void* q, const void* k, const void* v,
+                            const void* log_alpha, const float* S0, void* o, float* S_T,
+                            bool save, void* saved, size_t saved_bytes, void* ws,
+                            size_t ws_bytes, void* stream, void** events, int32_t n_events) {
+  const int pass = save ? GLA_PASS_FWD_SAVE : GLA_PASS_FWD;
+  const gla_status_t st = gla_validate(d, pass);
   if (st != GLA_OK) return st;
-  if (events && n_events < stage_list(d, GLA_PASS_FWD, 0, nullptr, 0) + 1)
+  if (events && n_events < stage_list(d, pass, 0, nullptr, 0) + 1)
     return GLA_ERR_INVALID_ARG;
   Tracer tr{events, n_events, (hipStream_t)stream};
   const Dims x = dims_of(d);
@@ -342,11 +397,18 @@ gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void
   if (x.BH == 0) return GLA_OK;
   if (x.T == 0) return state_copy(S0, S_T, x.BH * x.dk * x.dv, s);
   if (!q || !k || !v || !log_alpha || !o) return GLA_ERR_INVALID_ARG;
-  for (const void* p : std::initializer_list<const void*>{q, k, v, log_alpha, S0, o, S_T, ws})
+  for (const void* p : std::initializer_list<const void*>{q, k, v, log_alpha, S0, o, S_T, ws,
+                                                          saved})
     if (!aligned16(p)) return GLA_ERR_INVALID_ARG;
-  const Plan p = plan_of(d, GLA_PASS_FWD);
+  const Plan p = plan_of(d, pass);
   if (!ws || ws_bytes < p.total) return GLA_ERR_WORKSPACE;
+  const Plan sp = save ? saved_plan(d) : Plan{};
+  if (save && (!saved || saved_bytes < sp.total)) return GLA_ERR_WORKSPACE;
   char* w = (char*)ws;
+  // where the intra-chunk operands live: the workspace, or the saved buffer
+  char* ob = save ? (char*)saved : w;
+  const Plan& op = save ? sp : p;
+  const bool split = save && x.dtype == GLA_BF16;   // bf16 Kh^T with its remainder
   const bool mat = d->state_mode == GLA_STATES_MATERIALIZED;
   gla_status_t rs = GLA_OK;
   if (debug_checks()) {
@@ -358,7 +420,11 @@ gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void
   ia.dtype = x.dtype; ia.C = (int)x.C; ia.BH = (int)x.BH; ia.T = (int)x.T; ia.dk = (int)x.dk;
   ia.N = (int)x.N; ia.want_A = true; ia.q = q; ia.k = k; ia.la = log_alpha; ia.gate = gate_of(d);
   ia.gscalar = scalar_gate(d); ia.diag_bf16 = d->diag == GLA_DIAG_BF16;
-  ia.A = w + p.A; ia.Qh = w + p.Qh; ia.KhT = w + p.KhT; ia.eg = (float*)(w + p.eg);
+  ia.A = ob + op.A; ia.Qh = ob + op.Qh; ia.KhT = ob + op.KhT; ia.eg = (float*)(ob + op.eg);
+  if (save) {   // also the backward's operands, the transposed ones as its scans read them
+    ia.xt_f32 = x.dtype == GLA_BF16;
+    ia.QhT = ob + op.QhT; ia.Kh = ob + op.Kh;
+  }
   if ((rs = tr.mark()) != GLA_OK) return rs;
   rs = dev(gla::launch_intra(ia, s));
   if (rs != GLA_OK) return rs;
@@ -382,8 +448,9 @@ gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void
   }
   gla::FusedArgs fa{};
   fa.dtype = x.dtype; fa.C = (int)x.C; fa.BH = (int)x.BH; fa.T = (int)x.T; fa.dk = (int)x.dk;
-  fa.dv = (int)x.dv; fa.N = (int)x.N; fa.Qh = w + p.Qh; fa.KhT = w + p.KhT; fa.A = w + p.A;
-  fa.v = v; fa.eg = (const float*)(w + p.eg); fa.S0 = S0; fa.o = o; fa.S_T = S_T;
+  fa.dv = (int)x.dv; fa.N = (int)x.N; fa.Qh = ob + op.Qh; fa.KhT = ob + op.KhT;
+  fa.A = ob + op.A; fa.kht_split = split;
+  fa.v = v; fa.eg = (const float*)(ob + op.eg); fa.S0 = S0; fa.o = o; fa.S_T = S_T;
   fa.nseg = gla::fused_segments(x.dtype, (int)x.C, (int)x.N, (int)x.BH, (int)x.dv);
   // with a split, the states at the segment starts come first (no per-chunk states
   // written): two segments, a state scan over the first half; more, every segment but the
@@ -398,7 +465,8 @@ gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void
     } else {
       sa.nseg = fa.nseg - 1; sa.seg_p = fa.nseg; sa.seg_decay = (float*)(w + p.segdec);
     }
-    sa.XT = w + p.KhT; sa.Y = v; sa.eg = (const float*)(w + p.eg); sa.S_in = S0;
+    sa.XT = ob + op.KhT; sa.Y = v; sa.eg = (const float*)(ob + op.eg); sa.S_in = S0;
+    sa.xt_f32 = split;   // (then the split operand: high part and remainder)
     sa.S_out = (float*)(w + p.smid);
     if ((rs = dev(gla::launch_state_scan(sa, s))) != GLA_OK) return rs;
     if ((rs = dev(gla::launch_seg_combine((float*)(w + p.smid), (const float*)(w + p.segdec),
@@ -411,20 +479,50 @@ gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void
   return tr.mark();
 }
 
+gla_status_t gla_chunk_fwd_traced(const gla_desc_t* d, const void* q, const void* k,
+                                  const void* v, const void* log_alpha, const float* S0, void* o,
+                                  float* S_T, void* ws, size_t ws_bytes, void* stream,
+                                  void** events, int32_t n_events) {
+  return fwd_run(d, q, k, v, log_alpha, S0, o, S_T, false, nullptr, 0, ws, ws_bytes, stream,
+                 events, n_events);
+}
+
 gla_status_t gla_chunk_fwd(const gla_desc_t* d, const void* q, const void* k, const void* v,
                            const void* log_alpha, const float* S0, void* o, float* S_T, void* ws,
                            size_t ws_bytes, void* stream) {
-  return gla_chunk_fwd_traced(d, q, k, v, log_alpha, S0, o, S_T, ws, ws_bytes, stream, nullptr, 0);
+  return fwd_run(d, q, k, v, log_alpha, S0, o, S_T, false, nullptr, 0, ws, ws_bytes, stream,
+                 nullptr, 0);
 }
 
-gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void* k,
-                                  const void* v, const void* log_alpha, const float* S0,
-                                  const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
-                                  void* dlog_alpha, float* dS0, void* ws, size_t ws_bytes,
-                                  void* stream, void** events, int32_t n_events) {
-  const gla_status_t st = gla_validate(d, GLA_PASS_BWD);
+gla_status_t gla_chunk_fwd_save_traced(const gla_desc_t* d, const void* q, const void* k,
+                                       const void* v, const void* log_alpha, const float* S0,
+                                       void* o, float* S_T, void* saved, size_t saved_bytes,
+                                       void* ws, size_t ws_bytes, void* stream, void** events,
+                                       int32_t n_events) {
+  return fwd_run(d, q, k, v, log_alpha, S0, o, S_T, true, saved, saved_bytes, ws, ws_bytes,
+                 stream, events, n_events);
+}
+
+gla_status_t gla_chunk_fwd_save(const gla_desc_t* d, const void* q, const void* k, const void* v,
+                                const void* log_alpha, const float* S0, void* o, float* S_T,
+                                void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return fwd_run(d, q, k, v, log_alpha, S0, o, S_T, true, saved, saved_bytes, ws, ws_bytes,
+                 stream, nullptr, 0);
+}
+
+// The layer backward; from_saved: the intra-chunk operands come from `saved` (written by a
+// forward that saved them for the same inputs) and the intra-chunk kernel does not run.
+static gla_status_t bwd_run(const gla_desc_t* d, const void* q, const void* k, const void* v,
+                            const void* log_alpha, const float* S0, const void* dO,
+                            const float* dS_T, void* dq, void* dk, void* dv, void* dlog_alpha,
+                            float* dS0, bool from_saved, const void* saved, size_t saved_bytes,
+                            void* ws, size_t ws_bytes, void* stream, void** events,
+                            int32_t n_events) {
+  const int pass = from_saved ? GLA_PASS_BWD_SAVED : GLA_PASS_BWD;
+  const gla_status_t st = gla_validate(d, pass);
   if (st != GLA_OK) return st;
-  if (events && n_events < stage_list(d, GLA_PASS_BWD, dS_T != nullptr, nullptr, 0) + 1)
+  if (events && n_events < stage_list(d, pass, dS_T != nullptr, nullptr, 0) + 1)
     return GLA_ERR_INVALID_ARG;
   Tracer tr{events, n_events, (hipStream_t)stream};
   const Dims x = dims_of(d);
@@ -434,11 +532,16 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   if (!q || !k || !v || !log_alpha || !dO || !dq || !dk || !dv || !dlog_alpha)
     return GLA_ERR_INVALID_ARG;
   for (const void* p : std::initializer_list<const void*>{q, k, v, log_alpha, S0, dO, dS_T, dq,
-                                                          dk, dv, dlog_alpha, dS0, ws})
+                                                          dk, dv, dlog_alpha, dS0, ws, saved})
     if (!aligned16(p)) return GLA_ERR_INVALID_ARG;
-  const Plan p = plan_of(d, GLA_PASS_BWD);
+  const Plan p = plan_of(d, pass);
   if (!ws || ws_bytes < p.total) return GLA_ERR_WORKSPACE;
+  const Plan sp = from_saved ? saved_plan(d) : Plan{};
+  if (from_saved && (!saved || saved_bytes < sp.total)) return GLA_ERR_WORKSPACE;
   char* w = (char*)ws;
+  // where the intra-chunk operands live: the workspace, or the saved buffer
+  char* ob = from_saved ? (char*)saved : w;
+  const Plan& op = from_saved ? sp : p;
   const int C = (int)x.C, BH = (int)x.BH, T = (int)x.T, DK = (int)x.dk, DV = (int)x.dv,
             N = (int)x.N;
   gla_status_t rs = GLA_OK;
@@ -453,21 +556,23 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   ia.q = q; ia.k = k; ia.la = log_alpha;
   ia.g2_out = nullptr;
   ia.gate = gate_of(d); ia.gscalar = scalar_gate(d); ia.diag_bf16 = d->diag == GLA_DIAG_BF16;
-  ia.A = w + p.A; ia.QhT = w + p.QhT; ia.Kh = w + p.Kh; ia.KhT = w + p.KhT;
-  ia.eg = (float*)(w + p.eg);
-  if ((rs = tr.mark()) != GLA_OK) return rs;
-  rs = dev(gla::launch_intra(ia, s));
-  if (rs != GLA_OK) return rs;
+  ia.A = ob + op.A; ia.QhT = ob + op.QhT; ia.Kh = ob + op.Kh; ia.KhT = ob + op.KhT;
+  ia.eg = (float*)(ob + op.eg);
+  if (!from_saved) {
+    if ((rs = tr.mark()) != GLA_OK) return rs;
+    rs = dev(gla::launch_intra(ia, s));
+    if (rs != GLA_OK) return rs;
+  }
   // forward scan: chunk-start states S_[i]; cross term rowsum(S_[i] * Qh_i^T dO_i)
   gla::ScanArgs sa{};
   sa.dtype = x.dtype; sa.C = C; sa.BH = BH; sa.T = T; sa.dk = DK; sa.dv = DV; sa.N = N;
   sa.reverse = false; sa.xt_f32 = ia.xt_f32; sa.store = 1;
-  sa.XT = w + p.KhT; sa.Y = v; sa.X2T = w + p.QhT; sa.Y2 = dO; sa.cross = (float*)(w + p.crossF);
-  sa.eg = (const float*)(w + p.eg); sa.S_in = S0; sa.states = w + p.st;
+  sa.XT = ob + op.KhT; sa.Y = v; sa.X2T = ob + op.QhT; sa.Y2 = dO; sa.cross = (float*)(w + p.crossF);
+  sa.eg = (const float*)(ob + op.eg); sa.S_in = S0; sa.states = w + p.st;
   sa.S_out = dS_T ? (float*)(w + p.ST) : nullptr;
   // reverse scan: dS_[i+1]; cross term rowsum(dS_[i+1] * Kh_i^T V_i)
   gla::ScanArgs ra = sa;
-  ra.reverse = true; ra.XT = w + p.QhT; ra.Y = dO; ra.X2T = w + p.KhT; ra.Y2 = v;
+  ra.reverse = true; ra.XT = ob + op.QhT; ra.Y = dO; ra.X2T = ob + op.KhT; ra.Y2 = v;
   ra.cross = (float*)(w + p.crossR); ra.S_in = dS_T; ra.states = w + p.dst; ra.S_out = dS0;
   // S and dS go to the backward chunk kernel in MFMA fragment order when the scans run
   // 128-column tiles (bf16, chunk 64): its dq / dk workgroups load whole fragments, its dv
@@ -492,7 +597,7 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   ba.q = q; ba.k = k; ba.v = v; ba.dO = dO;
   ba.gscalar = scalar_gate(d);
   ba.s_frag = sa.frag_states;
-  ba.A = w + p.A; ba.Kh = w + p.Kh; ba.S = w + p.st; ba.dS = w + p.dst;
+  ba.A = ob + op.A; ba.Kh = ob + op.Kh; ba.S = w + p.st; ba.dS = w + p.dst;
   ba.dq = dq; ba.dk_out = dk; ba.dv_out = dv;
   ba.tot = (const float*)(w + p.carry); ba.cT = dS_T ? (const float*)(w + p.cT) : nullptr;
   ba.dla = dlog_alpha; ba.la = log_alpha; ba.gate = gate_of(d);
@@ -524,12 +629,41 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void
   return tr.mark();
 }
 
+gla_status_t gla_chunk_bwd_traced(const gla_desc_t* d, const void* q, const void* k,
+                                  const void* v, const void* log_alpha, const float* S0,
+                                  const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
+                                  void* dlog_alpha, float* dS0, void* ws, size_t ws_bytes,
+                                  void* stream, void** events, int32_t n_events) {
+  return bwd_run(d, q, k, v, log_alpha, S0, dO, dS_T, dq, dk, dv, dlog_alpha, dS0, false,
+                 nullptr, 0, ws, ws_bytes, stream, events, n_events);
+}
+
 gla_status_t gla_chunk_bwd(const gla_desc_t* d, const void* q, const void* k, const void* v,
                            const void* log_alpha, const float* S0, const void* dO,
                            const float* dS_T, void* dq, void* dk, void* dv, void* dlog_alpha,
                            float* dS0, void* ws, size_t ws_bytes, void* stream) {
-  return gla_chunk_bwd_traced(d, q, k, v, log_alpha, S0, dO, dS_T, dq, dk, dv, dlog_alpha, dS0, ws,
-                              ws_bytes, stream, nullptr, 0);
+  return bwd_run(d, q, k, v, log_alpha, S0, dO, dS_T, dq, dk, dv, dlog_alpha, dS0, false,
+                 nullptr, 0, ws, ws_bytes, stream, nullptr, 0);
+}
+
+gla_status_t gla_chunk_bwd_saved_traced(const gla_desc_t* d, const void* q, const void* k,
+                                        const void* v, const void* log_alpha, const float* S0,
+                                        const void* dO, const float* dS_T, void* dq, void* dk,
+                                        void* dv, void* dlog_alpha, float* dS0,
+                                        const void* saved, size_t saved_bytes, void* ws,
+                                        size_t ws_bytes, void* stream, void** events,
+                                        int32_t n_events) {
+  return bwd_run(d, q, k, v, log_alpha, S0, dO, dS_T, dq, dk, dv, dlog_alpha, dS0, true, saved,
+                 saved_bytes, ws, ws_bytes, stream, events, n_events);
+}
+
+gla_status_t gla_chunk_bwd_saved(const gla_desc_t* d, const void* q, const void* k,
+                                 const void* v, const void* log_alpha, const float* S0,
+                                 const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
+                                 void* dlog_alpha, float* dS0, const void* saved,
+                                 size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
+  return bwd_run(d, q, k, v, log_alpha, S0, dO, dS_T, dq, dk, dv, dlog_alpha, dS0, true, saved,
+                 saved_bytes, ws, ws_bytes, stream, nullptr, 0);
 }
 
 gla_status_t gla_decode(const gla_desc_t* d, const void* q, const void* k, const void* v,

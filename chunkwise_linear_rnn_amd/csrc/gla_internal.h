@@ -157,6 +157,10 @@ struct FusedArgs {
   // chunk); nseg = 1: one walk over all chunks
   int nseg;
   const float* S_mid;
+  // bf16: Kh^T in the backward's layout (each fragment followed by its bf16 remainder,
+  // as the backward's intra-chunk kernel writes it for the scans); only the fragments are
+  // read
+  bool kht_split;
 };
 // The number of sequence segments of the fused forward for a shape (1: no split): enough
 // for about 256 workgroups (one per CU) when B*H*dv/64 is small, at most 8, and at least

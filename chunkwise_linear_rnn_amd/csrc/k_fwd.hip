@@ -105,12 +105,38 @@ __global__ __launch_bounds__(kThreads) void k_output(const OpT* __restrict__ Qh,
     }
 }
 
+// A chunk's Kh^T as bf16 MFMA fragments (1 KB each), copied to LDS as they are.  kst = 1:
+// the forward's layout, fragments back to back; kst = 2: the backward's, each fragment
+// followed by its bf16 remainder, which is skipped (the forward's operand is the rounded
+// value, the fragment itself).
+template <int UNITS, int NT>
+struct KhtTile {
+  static constexpr int kPerThread = (UNITS + NT - 1) / NT;
+  u32x4 u[kPerThread];
+  __device__ __forceinline__ void load(const bf16* __restrict__ g, int kst) {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int idx = threadIdx.x + j * NT;
+      if (UNITS % NT == 0 || idx < UNITS)
+        u[j] = *reinterpret_cast<const u32x4*>(g + ((long)idx + (long)(kst - 1) * (idx & ~63)) * 8);
+    }
+  }
+  __device__ __forceinline__ void store(bf16* lds) const {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int idx = threadIdx.x + j * NT;
+      if (UNITS % NT == 0 || idx < UNITS) *reinterpret_cast<u32x4*>(lds + idx * 8) = u[j];
+    }
+  }
+};
+
 template <typename Tin, typename OpT, int C, int DK>
 __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
     const OpT* __restrict__ Qh, const OpT* __restrict__ KhT, const OpT* __restrict__ A,
     const float* __restrict__ eg, const Tin* __restrict__ V, const float* __restrict__ S0,
     Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N, int nseg,
-    const float* __restrict__ S_mid) {
+    const float* __restrict__ S_mid, int kst) {
+  static_assert(sizeof(OpT) == 2, "bf16 operands");
   constexpr int NT = kFusedThreads, TV = 64, NM = C / 16, KH = DK / 2, NP = KH / 16;
   // Kh^T arrives in MFMA fragment order (lane 16 q + r of fragment (16-row block, 32-token
   // block) holds row r, tokens 8 q ..) and is copied to LDS as is: each fragment read is 1 KB
@@ -149,14 +175,15 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_staged(
       S[p][e] = Sinit ? Sinit[((long)bh * DK + k0 + 16 * p + 4 * qd + e) * dv + col] : 0.f;
 
   FlatTile<OpT, C, DK, QLD, NT> tq;
-  FlatTile<OpT, DK, C, KLD, NT> tk;
+  static_assert(KLD == C, "the Kh^T tile is copied as is");
+  KhtTile<DK * C / 8, NT> tk;
   FlatTile<OpT, C, C, ALD, NT> ta;
   ColTile<OpT, Tin, C, VLD, NT, true> tv;   // chunk-swizzled (conflict-free stores)
   float egr = 0.f;
   auto fetch = [&](int i) {
     const int t0 = i * C;
     tq.load(Qh + ((long)bh * N * C + t0) * DK);
-    tk.load(KhT + ((long)bh * N + i) * DK * C);
+    tk.load(KhT + ((long)bh * N + i) * DK * C * kst, kst);
     ta.load(A + ((long)bh * N + i) * C * C);
     tv.load(V + ((long)bh * T + t0) * dv + v0, dv, min(C, T - t0));
     if (threadIdx.x < DK) egr = eg[((long)bh * N + i) * DK + threadIdx.x];
@@ -280,7 +307,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_c128(
     const bf16* __restrict__ Qh, const bf16* __restrict__ KhT, const bf16* __restrict__ A,
     const float* __restrict__ eg, const Tin* __restrict__ V, const float* __restrict__ S0,
     Tin* __restrict__ O, float* __restrict__ S_T, int T, int dv, int N, int nseg,
-    const float* __restrict__ S_mid) {
+    const float* __restrict__ S_mid, int kst) {
   using OpT = bf16;
   constexpr int C = 128, H = 64;   // chunk, half-step rows
   constexpr int NT = kFusedThreads, TV = 64, NM = H / 16, KH = DK / 2, NP = KH / 16;
@@ -325,13 +352,14 @@ __global__ __launch_bounds__(kFusedThreads) void k_fwd_fused_c128(
     ta.load(A + (((long)bh * N + i) * C + h * H) * C);
     tv.load(V + ((long)bh * T + min(t0, T - 1)) * dv + v0, dv, max(rows, 1));
     tv.nrows = max(rows, 0);
-    const bf16* kb0 = KhT + ((long)bh * N + i) * DK * C;
+    // (kst = 2: the backward's layout, each fragment followed by its remainder, skipped)
+    const bf16* kb0 = KhT + ((long)bh * N + i) * DK * C * kst;
 #pragma unroll
     for (int j = 0; j < kKPer; ++j) {
       const int u = threadIdx.x + j * NT;   // unit: (row block p, local fragment f, lane piece)
       const int pb = u / 128, f = (u / 64) % 2, pc = u % 64;
       if (kKUnits % NT == 0 || u < kKUnits)
-        ku[j] = *reinterpret_cast<const u32x4*>(kb0 + ((pb * 4 + 2 * h + f) * 64 + pc) * 8);
+        ku[j] = *reinterpret_cast<const u32x4*>(kb0 + ((pb * 4 + 2 * h + f) * kst * 64 + pc) * 8);
     }
     egr = eg[((long)bh * N + i) * DK + min((int)threadIdx.x, DK - 1)];
   };
@@ -602,14 +630,17 @@ static hipError_t launch_fused_t2(const FusedArgs& a, hipStream_t s) {
     dim3 grid((a.dv / 64) * a.BH * nseg);
     hipLaunchKernelGGL((k_fwd_fused_c128<Tin, DK>), grid, dim3(kFusedThreads), 0, s,
                        (const bf16*)a.Qh, (const bf16*)a.KhT, (const bf16*)a.A, a.eg,
-                       (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N, nseg, a.S_mid);
+                       (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N, nseg, a.S_mid,
+                       a.kht_split ? 2 : 1);
   } else if constexpr (C == 64 && sizeof(OpT) == 2) {
     const int nseg = a.S_mid && a.nseg > 1 ? a.nseg : 1;
     dim3 grid((a.dv / 64) * a.BH * nseg);
     hipLaunchKernelGGL((k_fwd_fused_staged<Tin, OpT, C, DK>), grid, dim3(kFusedThreads), 0, s,
                        (const OpT*)a.Qh, (const OpT*)a.KhT, (const OpT*)a.A, a.eg,
-                       (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N, nseg, a.S_mid);
+                       (const Tin*)a.v, a.S0, (Tin*)a.o, a.S_T, a.T, a.dv, a.N, nseg, a.S_mid,
+                       a.kht_split ? 2 : 1);
   } else {   // fp32, chunk 64: operand fragments read straight from memory
+    // (fp32 Kh^T has the same [dk][C] rows in the forward and the backward: no split)
     static_assert(C == 64, "fp32 operands come with chunk 64 only");
     dim3 grid((a.dv / 64) * a.BH);
     hipLaunchKernelGGL((k_fwd_fused<Tin, OpT, C, DK>), grid, dim3(kThreads), 0, s,

@@ -9,7 +9,8 @@ import torch
 
 from ._native import (BF16, DIAG_BF16, DIAG_F32, F32, GATE_LOG_ALPHA, GATE_LOGITS,
                       GATE_PER_KEY, GATE_SCALAR,
-                      MATERIALIZED, RECOMPUTE, PASS_BWD, PASS_FWD, PASS_STATES, GlaError, lib,
+                      MATERIALIZED, RECOMPUTE, PASS_BWD, PASS_FWD, PASS_STATES, PASS_FWD_SAVE,
+                      PASS_BWD_SAVED, saved_bytes, GlaError, lib,
                       make_desc, make_gsa_desc, gsa_workspace_bytes, workspace_bytes)
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
@@ -102,6 +103,18 @@ def fwd(q, k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, state_mode="recom
     logsigmoid(x) / gate_tau.  log_alpha [B, H, T] (instead of [B, H, T, dk]) is a scalar
     gate per token, shared by every key dimension.  diag: "f32" or "bf16" diagonal
     intra-chunk sub-blocks."""
+    desc, o, S_T = _fwd_args(q, k, v, log_alpha, S0, chunk, subchunk, state_mode, gate_tau,
+                             diag, final_state)
+    dev = q.device
+    ws, need = _workspace(desc, PASS_FWD, dev, workspace)
+    _call("gla_chunk_fwd", lib().gla_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(log_alpha), _ptr(S0), _ptr(o), _ptr(S_T),
+                                               _ptr(ws), need, _stream(dev)))
+    return o, S_T
+
+
+def _fwd_args(q, k, v, log_alpha, S0, chunk, subchunk, state_mode, gate_tau, diag,
+              final_state):
     desc = _desc_from(q, v, chunk, subchunk, state_mode, gate_tau, _is_scalar(log_alpha), diag)
     dev, dt = q.device, q.dtype
     B, H, T, dk, dv = desc.B, desc.H, desc.T, desc.dk, desc.dv
@@ -113,11 +126,23 @@ def fwd(q, k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, state_mode="recom
         _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
     o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
     S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if final_state else None
-    ws, need = _workspace(desc, PASS_FWD, dev, workspace)
-    _call("gla_chunk_fwd", lib().gla_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
-                                               _ptr(log_alpha), _ptr(S0), _ptr(o), _ptr(S_T),
-                                               _ptr(ws), need, _stream(dev)))
-    return o, S_T
+    return desc, o, S_T
+
+
+def fwd_save(q, k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, final_state=True,
+             workspace=None, saved=None, gate_tau=None, diag="f32"):
+    """o, S_T, saved: the recomputed-states forward of fwd (gla_chunk_fwd_save) that also
+    keeps the backward's intra-chunk operands in `saved` (a uint8 device tensor of at least
+    saved_bytes(desc) bytes, allocated when None) for bwd_saved with the same inputs."""
+    desc, o, S_T = _fwd_args(q, k, v, log_alpha, S0, chunk, subchunk, RECOMPUTE, gate_tau,
+                             diag, final_state)
+    dev = q.device
+    ws, need = _workspace(desc, PASS_FWD_SAVE, dev, workspace)
+    sv, sneed = _ws_buffer(saved_bytes(desc), dev, saved)
+    _call("gla_chunk_fwd_save", lib().gla_chunk_fwd_save(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(S0), _ptr(o),
+        _ptr(S_T), _ptr(sv), sneed, _ptr(ws), need, _stream(dev)))
+    return o, S_T, sv
 
 
 def check_gates(q, v, log_alpha, *, gate_tau=None):
@@ -140,6 +165,19 @@ def bwd(q, k, v, log_alpha, dO, S0=None, dS_T=None, *, chunk=64, subchunk=16,
     """dq, dk, dv, dlog_alpha, dS0 for the loss gradient (dO, dS_T).  With gate_tau set
     (gate logits in log_alpha) the fourth output is the gradient with respect to them.
     A scalar gate (log_alpha [B, H, T]) gets its gradient summed over the key dimension."""
+    desc, outs = _bwd_args(q, k, v, log_alpha, dO, S0, dS_T, chunk, subchunk, gate_tau, diag,
+                           want_dS0)
+    dq, dk_, dv_, dla, dS0 = outs
+    dev = q.device
+    ws, need = _workspace(desc, PASS_BWD, dev, workspace)
+    _call("gla_chunk_bwd", lib().gla_chunk_bwd(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(S0), _ptr(dO),
+        _ptr(dS_T), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(dS0), _ptr(ws), need,
+        _stream(dev)))
+    return dq, dk_, dv_, dla, dS0
+
+
+def _bwd_args(q, k, v, log_alpha, dO, S0, dS_T, chunk, subchunk, gate_tau, diag, want_dS0):
     desc = _desc_from(q, v, chunk, subchunk, RECOMPUTE, gate_tau, _is_scalar(log_alpha), diag)
     dev, dt = q.device, q.dtype
     B, H, T, dk, dv = desc.B, desc.H, desc.T, desc.dk, desc.dv
@@ -156,11 +194,28 @@ def bwd(q, k, v, log_alpha, dO, S0=None, dS_T=None, *, chunk=64, subchunk=16,
     dv_ = torch.empty_like(v)
     dla = torch.empty_like(log_alpha)
     dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None
-    ws, need = _workspace(desc, PASS_BWD, dev, workspace)
-    _call("gla_chunk_bwd", lib().gla_chunk_bwd(
+    return desc, (dq, dk_, dv_, dla, dS0)
+
+
+def bwd_saved(q, k, v, log_alpha, dO, saved, S0=None, dS_T=None, *, chunk=64, subchunk=16,
+              want_dS0=True, workspace=None, gate_tau=None, diag="f32"):
+    """bwd from the intra-chunk operands that fwd_save kept in `saved` for the same q, k,
+    log_alpha and options (gla_chunk_bwd_saved): the same results, without the backward's
+    intra-chunk kernel."""
+    desc, outs = _bwd_args(q, k, v, log_alpha, dO, S0, dS_T, chunk, subchunk, gate_tau, diag,
+                           want_dS0)
+    dq, dk_, dv_, dla, dS0 = outs
+    dev = q.device
+    need_s = saved_bytes(desc)
+    if (not isinstance(saved, torch.Tensor) or saved.device != dev or not saved.is_contiguous()
+            or saved.numel() * saved.element_size() < need_s):
+        raise ValueError(f"saved must be the contiguous buffer of fwd_save on {dev} "
+                         f"(at least {need_s} bytes)")
+    ws, need = _workspace(desc, PASS_BWD_SAVED, dev, workspace)
+    _call("gla_chunk_bwd_saved", lib().gla_chunk_bwd_saved(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(S0), _ptr(dO),
-        _ptr(dS_T), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(dS0), _ptr(ws), need,
-        _stream(dev)))
+        _ptr(dS_T), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(dS0), _ptr(saved),
+        saved.numel() * saved.element_size(), _ptr(ws), need, _stream(dev)))
     return dq, dk_, dv_, dla, dS0
 
 
@@ -214,28 +269,39 @@ def chunk_states(k, v, log_alpha, S0=None, *, chunk=64, subchunk=16, workspace=N
 
 
 class GLAFunction(torch.autograd.Function):
-    """Autograd wrapper: forward runs gla_chunk_fwd, backward gla_chunk_bwd (which
-    recomputes the chunk states from the saved inputs).  The gate options of fwd / bwd
-    (gate logits with gate_tau, a scalar gate per token, the diagonal precision) pass
-    through; the gradient for log_alpha is then the one for what log_alpha holds."""
+    """Autograd wrapper.  Recomputed states (the default): forward gla_chunk_fwd_save,
+    which keeps the backward's intra-chunk operands, and backward gla_chunk_bwd_saved from
+    them (the chunk states are recomputed by the backward's scans).  Materialized states:
+    forward gla_chunk_fwd, backward gla_chunk_bwd from the saved inputs.  The gate options
+    of fwd / bwd (gate logits with gate_tau, a scalar gate per token, the diagonal
+    precision) pass through; the gradient for log_alpha is then the one for what
+    log_alpha holds."""
 
     @staticmethod
     def forward(ctx, q, k, v, log_alpha, S0, chunk, subchunk, state_mode, gate_tau, diag):
-        o, S_T = fwd(q, k, v, log_alpha, S0, chunk=chunk, subchunk=subchunk,
-                     state_mode=state_mode, gate_tau=gate_tau, diag=diag)
-        ctx.save_for_backward(q, k, v, log_alpha, S0)
+        if state_mode == "recompute":
+            o, S_T, sv = fwd_save(q, k, v, log_alpha, S0, chunk=chunk, subchunk=subchunk,
+                                  gate_tau=gate_tau, diag=diag)
+        else:
+            o, S_T = fwd(q, k, v, log_alpha, S0, chunk=chunk, subchunk=subchunk,
+                         state_mode=state_mode, gate_tau=gate_tau, diag=diag)
+            sv = None
+        ctx.save_for_backward(q, k, v, log_alpha, S0, sv)
         ctx.cfg = (chunk, subchunk, gate_tau, diag)
         return o, S_T
 
     @staticmethod
     def backward(ctx, dO, dS_T):
-        q, k, v, log_alpha, S0 = ctx.saved_tensors
+        q, k, v, log_alpha, S0, sv = ctx.saved_tensors
         chunk, subchunk, gate_tau, diag = ctx.cfg
         dO = dO.contiguous() if dO is not None else q.new_zeros(q.shape[:-1] + (v.shape[-1],))
         dS_T = dS_T.contiguous() if dS_T is not None else None
-        dq, dk, dv, dla, dS0 = bwd(q, k, v, log_alpha, dO, S0, dS_T, chunk=chunk,
-                                   subchunk=subchunk, want_dS0=S0 is not None,
-                                   gate_tau=gate_tau, diag=diag)
+        opts = dict(chunk=chunk, subchunk=subchunk, want_dS0=S0 is not None, gate_tau=gate_tau,
+                    diag=diag)
+        if sv is not None:
+            dq, dk, dv, dla, dS0 = bwd_saved(q, k, v, log_alpha, dO, sv, S0, dS_T, **opts)
+        else:
+            dq, dk, dv, dla, dS0 = bwd(q, k, v, log_alpha, dO, S0, dS_T, **opts)
         return dq, dk, dv, dla, dS0, None, None, None, None, None
 
 

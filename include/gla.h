@@ -76,7 +76,14 @@ typedef enum { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype_t;
  * stateless); the mode only changes the forward. */
 typedef enum { GLA_STATES_MATERIALIZED = 0, GLA_STATES_RECOMPUTE = 1 } gla_state_mode_t;
 
-typedef enum { GLA_PASS_FWD = 0, GLA_PASS_BWD = 1 } gla_pass_t;
+/* Passes of gla_validate / gla_workspace_bytes.  2 is gla_chunk_states; FWD_SAVE and
+ * BWD_SAVED are the training pair gla_chunk_fwd_save / gla_chunk_bwd_saved. */
+typedef enum {
+  GLA_PASS_FWD = 0,
+  GLA_PASS_BWD = 1,
+  GLA_PASS_FWD_SAVE = 3,
+  GLA_PASS_BWD_SAVED = 4
+} gla_pass_t;
 
 /* What the log_alpha argument of every entry point holds (Approach section: the gate is
  * data-dependent).
@@ -146,8 +153,9 @@ int32_t gla_version(void);
 gla_status_t gla_validate(const gla_desc_t* desc, int32_t pass);
 
 /* Workspace bytes needed by gla_chunk_fwd (pass = GLA_PASS_FWD), gla_chunk_bwd
- * (GLA_PASS_BWD) or gla_chunk_states (pass = 2) for `desc`; writes them to *bytes.
- * Host-only; same errors as gla_validate, plus GLA_ERR_INVALID_ARG for bytes == NULL. */
+ * (GLA_PASS_BWD), gla_chunk_states (pass = 2), gla_chunk_fwd_save (GLA_PASS_FWD_SAVE) or
+ * gla_chunk_bwd_saved (GLA_PASS_BWD_SAVED) for `desc`; writes them to *bytes.  Host-only;
+ * same errors as gla_validate, plus GLA_ERR_INVALID_ARG for bytes == NULL. */
 gla_status_t gla_workspace_bytes(const gla_desc_t* desc, int32_t pass, size_t* bytes);
 
 /* Gate precondition check (the layer reads log_alpha as finite and <= 0, gate logits as
@@ -208,6 +216,46 @@ gla_status_t gla_chunk_bwd(const gla_desc_t* desc, const void* q, const void* k,
                            void* dv, void* dlog_alpha, float* dS0, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* Training pair: a forward that keeps what the backward would otherwise recompute, and a
+ * backward that starts from it (page "Gated Linear Attention Transformers with
+ * Hardware-Efficient Training", atlas.scime.ai summary, Approach: what to keep from the
+ * forward pass and what to recompute in the backward is a trade of memory against work;
+ * the chunk states themselves are still recomputed by the backward's scans).
+ *
+ * gla_chunk_fwd_save: gla_chunk_fwd with the recomputed-states forward only
+ * (state_mode GLA_STATES_RECOMPUTE, else GLA_ERR_UNSUPPORTED), whose intra-chunk kernel also
+ * writes the backward's intra-chunk operands into `saved` (device, 16-byte aligned, at least
+ * gla_saved_bytes(desc) bytes, caller-owned; contents opaque): the decayed causal matrix A,
+ * Q*e^g token-major and transposed, K*e^(gamma-g) token-major and transposed (the
+ * transposed ones as the backward's scans read them: bf16 inputs as a bf16 high part and
+ * bf16 remainder) and e^gamma.  o and S_T are those of gla_chunk_fwd; with bf16 inputs the
+ * second and later sequence segments start from states formed from the unrounded decayed
+ * keys (high part and remainder), so o may differ from gla_chunk_fwd's in the last bits.
+ * ws: at least gla_workspace_bytes(desc, GLA_PASS_FWD_SAVE) bytes.
+ *
+ * gla_chunk_bwd_saved: gla_chunk_bwd without its intra-chunk kernel, reading those operands
+ * from `saved` as written by gla_chunk_fwd_save for the same desc and the same q, k,
+ * log_alpha (not checked; anything else gives wrong gradients).  The results are the bits
+ * gla_chunk_bwd returns for the same inputs.  ws: at least
+ * gla_workspace_bytes(desc, GLA_PASS_BWD_SAVED) bytes.
+ *
+ * Errors: as gla_chunk_fwd / gla_chunk_bwd; GLA_ERR_WORKSPACE also for a NULL or short
+ * `saved` (B*H*T > 0).  The stream orders the pair: saved is written by the forward's
+ * first kernel and read by the backward's kernels. */
+gla_status_t gla_saved_bytes(const gla_desc_t* desc, size_t* bytes);
+
+gla_status_t gla_chunk_fwd_save(const gla_desc_t* desc, const void* q, const void* k,
+                                const void* v, const void* log_alpha, const float* S0,
+                                void* o, float* S_T, void* saved, size_t saved_bytes,
+                                void* ws, size_t ws_bytes, void* stream);
+
+gla_status_t gla_chunk_bwd_saved(const gla_desc_t* desc, const void* q, const void* k,
+                                 const void* v, const void* log_alpha, const float* S0,
+                                 const void* dO, const float* dS_T, void* dq, void* dk,
+                                 void* dv, void* dlog_alpha, float* dS0, const void* saved,
+                                 size_t saved_bytes, void* ws, size_t ws_bytes,
+                                 void* stream);
+
 /* Recurrent evaluation, for decoding (page "Gated Slot Attention for Efficient
  * Linear-Time Sequence Modeling", mlsanity.com summary, Abstract: linear attention and its
  * gated variants infer recurrently; here the layer's own recurrence, one state per
@@ -266,7 +314,8 @@ gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* desc, const void* q, const void* 
                          void* stream);
 
 /* Stage tracing, for profiling.  The *_traced variants behave exactly like
- * gla_chunk_fwd / gla_chunk_bwd and additionally record caller-created hipEvent_t
+ * gla_chunk_fwd / gla_chunk_bwd / gla_chunk_fwd_save / gla_chunk_bwd_saved and
+ * additionally record caller-created hipEvent_t
  * handles on `stream`: events[j] right before the j-th kernel launch and events[n] after
  * the last, where n is the stage count from gla_trace_stages (events == NULL records
  * nothing; a NULL entry records nothing at its boundary, so two events time one stage
@@ -274,9 +323,12 @@ gla_status_t gla_gsa_bwd(const gla_gsa_desc_t* desc, const void* q, const void* 
  * duration of stage j.  n_events smaller than n + 1 is GLA_ERR_INVALID_ARG (checked
  * before any launch).
  *
- * gla_trace_stages returns n for a pass (with_dS_T: whether the backward gets a dS_T) and
- * writes up to max_names static stage names to `names` (nullable); -1 on a NULL desc or a
- * bad pass.  The stages are
+ * gla_trace_stages returns n for a pass (GLA_PASS_FWD, GLA_PASS_BWD, GLA_PASS_FWD_SAVE,
+ * GLA_PASS_BWD_SAVED; with_dS_T: whether the backward gets a dS_T) and writes up to
+ * max_names static stage names to `names` (nullable); -1 on a NULL desc or a bad pass.
+ * The forward that saves has the recompute forward's stages (its intra-chunk kernel
+ * writes more), the backward from saved operands the backward's without intra.  The
+ * stages are
  *   forward, materialized: intra (it forms the gate cumsum itself), state_scan (in
  *                          sequence segments when few workgroups would walk the whole
  *                          sequence), output
@@ -303,6 +355,20 @@ gla_status_t gla_chunk_bwd_traced(const gla_desc_t* desc, const void* q, const v
                                   void* dv, void* dlog_alpha, float* dS0, void* ws,
                                   size_t ws_bytes, void* stream, void** events,
                                   int32_t n_events);
+
+gla_status_t gla_chunk_fwd_save_traced(const gla_desc_t* desc, const void* q, const void* k,
+                                       const void* v, const void* log_alpha, const float* S0,
+                                       void* o, float* S_T, void* saved, size_t saved_bytes,
+                                       void* ws, size_t ws_bytes, void* stream, void** events,
+                                       int32_t n_events);
+
+gla_status_t gla_chunk_bwd_saved_traced(const gla_desc_t* desc, const void* q, const void* k,
+                                        const void* v, const void* log_alpha, const float* S0,
+                                        const void* dO, const float* dS_T, void* dq, void* dk,
+                                        void* dv, void* dlog_alpha, float* dS0,
+                                        const void* saved, size_t saved_bytes, void* ws,
+                                        size_t ws_bytes, void* stream, void** events,
+                                        int32_t n_events);
 
 #ifdef __cplusplus
 }

@@ -256,3 +256,61 @@ def test_noalloc_refuses_oversized_problem_on_host(native):
     bad = D(1, 1, 64, 96, 64)
     assert L.gla_chunk_fwd_noalloc(ctypes.byref(bad), p, p, p, p, None, p, None, None) == 2
     assert L.gla_chunk_fwd_noalloc(None, p, p, p, p, None, p, None, None) == 1
+
+
+def test_training_pair_planning_and_errors(native):
+    """The saving forward and the backward from saved operands: the intra-chunk operands
+    move from the workspaces to the saved buffer (sizes as laid out: A, Qh, Qh^T and Kh^T as
+    fp32 words, Kh, e^gamma, each region 256-byte aligned); materialized states have no
+    saving forward; a missing or short saved buffer is refused before any launch."""
+    L = native.lib()
+    D = native.make_desc
+    al = lambda n: (n + 255) // 256 * 256
+    B, H, T, dk, dv, C = 4, 4, 2048, 256, 512, 64
+    d = D(B, H, T, dk, dv, C, 16, native.BF16, native.RECOMPUTE)
+    rows = B * H * (T // C) * C
+    A, op, op32, eg = (al(B * H * (T // C) * C * C * 2), al(rows * dk * 2), al(rows * dk * 4),
+                       al(B * H * (T // C) * dk * 4))
+    assert native.saved_bytes(d) == A + op + op32 + op + op32 + eg
+    fwd, fwd_s = (native.workspace_bytes(d, native.PASS_FWD),
+                  native.workspace_bytes(d, native.PASS_FWD_SAVE))
+    bwd, bwd_s = (native.workspace_bytes(d, native.PASS_BWD),
+                  native.workspace_bytes(d, native.PASS_BWD_SAVED))
+    assert fwd - fwd_s == A + op + op + eg
+    assert bwd - bwd_s == A + op32 + op + op32 + eg
+    out = ctypes.c_size_t(0)
+    assert L.gla_saved_bytes(ctypes.byref(d), None) == 1
+    m = D(B, H, T, dk, dv, C, 16, native.BF16, native.MATERIALIZED)
+    assert L.gla_saved_bytes(ctypes.byref(m), ctypes.byref(out)) == 2
+    assert native.validate(m, native.PASS_FWD_SAVE) == 2
+    assert native.validate(m, native.PASS_BWD_SAVED) == 0
+    # stage lists: the saving forward has the recompute forward's, the backward from saved
+    # operands the backward's without the intra-chunk kernel
+    def names(pass_, dst):
+        n = L.gla_trace_stages(ctypes.byref(d), pass_, dst, None, 0)
+        arr = (ctypes.c_char_p * n)()
+        L.gla_trace_stages(ctypes.byref(d), pass_, dst, arr, n)
+        return [s.decode() for s in arr]
+    assert names(native.PASS_FWD_SAVE, 0) == names(native.PASS_FWD, 0)
+    assert names(native.PASS_BWD_SAVED, 0) == names(native.PASS_BWD, 0)[1:]
+    assert names(native.PASS_BWD_SAVED, 1) == names(native.PASS_BWD, 1)[1:]
+    assert L.gla_trace_stages(ctypes.byref(d), 5, 0, None, 0) == -1
+    # refusals on the host: no saved buffer, a short one, a materialized descriptor
+    small = D(1, 1, 64, 64, 64)
+    p = ctypes.c_void_p(16)
+    need = native.saved_bytes(small)
+    ws = 1 << 30
+    assert L.gla_chunk_fwd_save(ctypes.byref(small), p, p, p, p, None, p, None, None, 0, p, ws,
+                                None) == 3
+    assert L.gla_chunk_fwd_save(ctypes.byref(small), p, p, p, p, None, p, None, p, need - 1, p,
+                                ws, None) == 3
+    ms = D(1, 1, 64, 64, 64, 64, 16, native.BF16, native.MATERIALIZED)
+    assert L.gla_chunk_fwd_save(ctypes.byref(ms), p, p, p, p, None, p, None, p, need, p, ws,
+                                None) == 2
+    assert L.gla_chunk_bwd_saved(ctypes.byref(small), p, p, p, p, None, p, None, p, p, p, p, None,
+                                 None, 0, p, ws, None) == 3
+    assert L.gla_chunk_bwd_saved(ctypes.byref(small), p, p, p, p, None, p, None, p, p, p, p, None,
+                                 p, need - 1, p, ws, None) == 3
+    q = ctypes.c_void_p(18)   # a misaligned saved buffer
+    assert L.gla_chunk_bwd_saved(ctypes.byref(small), p, p, p, p, None, p, None, p, p, p, p, None,
+                                 q, need, p, ws, None) == 1
