@@ -3,8 +3,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gla1p3b_t2k]
 
-A step is one gla_chunk_fwd plus one gla_chunk_bwd over the whole batch of seeded
-synthetic inputs (already resident in device memory), with every output and workspace
+A step is one training pair, gla_chunk_fwd_save plus gla_chunk_bwd_saved (the forward
+keeps the intra-chunk operands for the backward, which then skips its intra-chunk kernel),
+over the whole batch of seeded synthetic inputs (already resident in device memory), with every output and workspace
 preallocated.  K steps are timed between two device synchronisations; every kernel
 launch is also bracketed by HIP events (the traced entry points of the C ABI, recorded
 on the stream the kernels run on) to get each stage's average duration.  One JSON line
@@ -15,6 +16,10 @@ MI355X peak for its bound (HBM 8 TB/s, or dense bf16 MFMA 2.5 PFLOP/s); its `ach
 uses the algorithmic bytes or flops per launch from stage_work() below.  `traffic`
 is the measured HBM bytes per launch of that stage from the committed rocprofv3 counter
 summary, or null when no summary matches the current kernel source.
+
+`recompute_pair_step` times the other pair, gla_chunk_fwd plus gla_chunk_bwd (the backward
+rebuilds the intra-chunk operands; nothing is kept between the passes), back to back like
+`warm_cache`; `--pair recompute` makes it the timed step instead.
 
 `decode_step` times the recurrent entry point (one token per sequence, float32 state
 read and written in place) at the workload's head shape for a small and a serving-size
@@ -71,18 +76,26 @@ def metric_name(cfg, fwd_only):
 
 
 
-def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
+def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e, save=False):
     """(algorithmic HBM bytes, algorithmic flops) of one launch of `stage`.
 
     Per token and head: each tensor the stage must read or write once, in its storage
     type; flops count a multiply-add as 2 and the causal intra-chunk products at half
-    the chunk (C/2 average partners)."""
+    the chunk (C/2 average partners).  `save`: the forward of the training pair, whose
+    intra-chunk kernel also writes the backward's operands and whose Kh^T is stored as
+    fp32 (with bf16 inputs: a bf16 high part and remainder, 4 bytes an element)."""
     BH, N = B * H, (T + C - 1) // C
     tok = BH * T
     tokp = BH * N * C                      # padded rows of per-chunk operands
     st = BH * N * dk * dv * e              # one materialized state tensor
+    kt = 4 if save else e                  # bytes of one stored Kh^T element
     if stage == "intra":
-        if pass_ == "fwd":
+        if pass_ == "fwd" and save:
+            # reads log_alpha, q, k; writes A, Qh and Kh (storage type), Qh^T and Kh^T
+            # (fp32), e^gamma
+            byt = (3 * tok * dk * e + 2 * tokp * dk * e + 2 * tokp * dk * 4
+                   + BH * N * C * C * e + BH * N * dk * 4)
+        elif pass_ == "fwd":
             byt = 3 * tok * dk * e + 2 * tokp * dk * e + BH * N * C * C * e + BH * N * dk * 4
         else:   # reads log_alpha, q, k; writes A, Qh^T, Kh^T (fp32), Kh, e^gamma (the
             # chunk kernel rebuilds g itself)
@@ -106,12 +119,12 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e):
         ns = (P - 1) * N // P
         h = BH * ns * C
         st4 = BH * dk * dv * 4
-        byt = h * dk * e + h * dv * e + BH * ns * dk * 4 + (P - 1) * st4
+        byt = h * dk * kt + h * dv * e + BH * ns * dk * 4 + (P - 1) * st4
         if P > 2:
             byt += 2 * (P - 2) * st4
         return byt, h * 2 * dk * dv
     if stage == "fwd_fused":
-        byt = 2 * tokp * dk * e + BH * N * C * C * e + 2 * tok * dv * e + BH * dk * dv * 4
+        byt = tokp * dk * (e + kt) + BH * N * C * C * e + 2 * tok * dv * e + BH * dk * dv * 4
         return byt, tok * (4 * dk * dv + C * dv)
     if stage == "bwd_dqk_dv":
         # dq/dk part: reads q, k, v, dO, log_alpha, S, dS, chunk totals; writes dq, dk, dla
@@ -258,15 +271,23 @@ def cpu_baseline(d, cfg, T_sample):
             "fwd_s": wall_f, "bwd_s": wall_b, "cpu_model": _cpu_model()}
 
 
-def counter_traffic(stage, workload, state_mode="recompute"):
+BWD_SHARED = ("bwd_dqk_dv", "state_scans", "state_dot", "gate_tot")
+
+
+def counter_traffic(stage, workload, kind="recompute"):
     """HBM bytes per launch from a committed counter summary that matches the current
-    kernel source, else None.  A summary taken in materialized state mode carries that
-    suffix; the backward's kernels are the same in both modes."""
+    kernel source, else None.  `kind`: "recompute" (the training pair in recompute state
+    mode, the summaries without suffix), "materialized" or "recompute_pair", whose
+    summaries carry that suffix; the backward's scans and its dq/dk/dv and gate kernels
+    are the same launches in all three, so those fall back to the summary without
+    suffix."""
     path = os.path.join(ROOT, "profiles", f"counters_{stage}_{workload}.json")
-    if state_mode == "materialized":
-        mpath = os.path.join(ROOT, "profiles", f"counters_{stage}_{workload}_materialized.json")
+    if kind != "recompute":
+        mpath = os.path.join(ROOT, "profiles", f"counters_{stage}_{workload}_{kind}.json")
         if os.path.exists(mpath):
             path = mpath
+        elif stage not in BWD_SHARED:
+            return None
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -277,12 +298,13 @@ def counter_traffic(stage, workload, state_mode="recompute"):
     return rec.get("traffic_bytes_per_launch")
 
 
-def counter_mfma(workload, state_mode):
+def counter_mfma(workload, kind):
     """Matrix-unit figures per stage from the committed `rocprofv3 --pmc
     SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE` summary of this
-    workload and state mode: {stage: {mfma_busy_frac, bf16_peak_frac, ...}} for the stages
-    whose kernel source still matches the summary's hash; {} when there is none."""
-    suffix = "_materialized" if state_mode == "materialized" else ""
+    workload and kind (as counter_traffic): {stage: {mfma_busy_frac, bf16_peak_frac, ...}}
+    for the stages whose kernel source still matches the summary's hash; {} when there is
+    none."""
+    suffix = "" if kind == "recompute" else "_" + kind
     path = os.path.join(ROOT, "profiles", f"mfma_{workload}{suffix}.json")
     if not os.path.exists(path):
         return {}
@@ -392,6 +414,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE_WORKLOAD)
     ap.add_argument("--state-mode", default="recompute", choices=["recompute", "materialized"])
+    ap.add_argument("--pair", default="train", choices=["train", "recompute"],
+                    help="the timed step: the training pair (the forward keeps the "
+                         "intra-chunk operands for the backward) or the recompute pair; the "
+                         "materialized state mode and forward-only workloads time the latter")
     ap.add_argument("--scalar-gates", action="store_true",
                     help="time the step with scalar gates (one per token and head, [B, H, T]) "
                          "as the main measurement, with its per-stage table")
@@ -466,14 +492,18 @@ def main():
     o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
     S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     dq, dk_, dv_, dla = (torch.empty_like(x) for x in (q, k, v, la))
-    wsf_n = nat.workspace_bytes(desc, nat.PASS_FWD)
-    wsb_n = nat.workspace_bytes(desc, nat.PASS_BWD)
-    wsf = torch.empty(wsf_n, dtype=torch.uint8, device=dev)
-    wsb = torch.empty(wsb_n, dtype=torch.uint8, device=dev)
     # a forward-only workload (the long sequence with state carry) times gla_chunk_fwd alone
     fwd_only = not cfg.bwd
-    fwd_stages = nat.trace_stages(desc, nat.PASS_FWD)
-    bwd_stages = [] if fwd_only else nat.trace_stages(desc, nat.PASS_BWD, False)
+    train = args.pair == "train" and mode == nat.RECOMPUTE and not fwd_only
+    pass_f, pass_b = (nat.PASS_FWD_SAVE, nat.PASS_BWD_SAVED) if train else (nat.PASS_FWD, nat.PASS_BWD)
+    wsf_n = nat.workspace_bytes(desc, pass_f)
+    wsb_n = nat.workspace_bytes(desc, pass_b)
+    wsf = torch.empty(max(1, wsf_n), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(max(1, wsb_n), dtype=torch.uint8, device=dev)
+    sv_n = nat.saved_bytes(desc) if train else 0
+    saved = torch.empty(max(1, sv_n), dtype=torch.uint8, device=dev)
+    fwd_stages = nat.trace_stages(desc, pass_f)
+    bwd_stages = [] if fwd_only else nat.trace_stages(desc, pass_b, False)
     nf, nb = len(fwd_stages) + 1, len(bwd_stages) + 1
     L = nat.lib()
     stream = torch.cuda.current_stream(dev)
@@ -488,17 +518,28 @@ def main():
     evb = [hip.create(nb) for _ in range(args.warmup)]
 
     def step(ef, eb):
-        st = L.gla_chunk_fwd_traced(ctypes.byref(desc), P(q), P(k), P(v), P(la), None, P(o), P(S_T),
-                                    P(wsf), wsf_n, sp, ef, nf if ef is not None else 0)
+        n_ef, n_eb = (nf if ef is not None else 0), (nb if eb is not None else 0)
+        if train:
+            st = L.gla_chunk_fwd_save_traced(ctypes.byref(desc), P(q), P(k), P(v), P(la), None,
+                                             P(o), P(S_T), P(saved), sv_n, P(wsf), wsf_n, sp,
+                                             ef, n_ef)
+        else:
+            st = L.gla_chunk_fwd_traced(ctypes.byref(desc), P(q), P(k), P(v), P(la), None, P(o),
+                                        P(S_T), P(wsf), wsf_n, sp, ef, n_ef)
         if st:
-            raise nat.GlaError(st, "gla_chunk_fwd_traced")
+            raise nat.GlaError(st, "forward (traced)")
         if fwd_only:
             return
-        st = L.gla_chunk_bwd_traced(ctypes.byref(desc), P(q), P(k), P(v), P(la), None, P(dO), None,
-                                    P(dq), P(dk_), P(dv_), P(dla), None, P(wsb), wsb_n, sp, eb,
-                                    nb if eb is not None else 0)
+        if train:
+            st = L.gla_chunk_bwd_saved_traced(ctypes.byref(desc), P(q), P(k), P(v), P(la), None,
+                                              P(dO), None, P(dq), P(dk_), P(dv_), P(dla), None,
+                                              P(saved), sv_n, P(wsb), wsb_n, sp, eb, n_eb)
+        else:
+            st = L.gla_chunk_bwd_traced(ctypes.byref(desc), P(q), P(k), P(v), P(la), None, P(dO),
+                                        None, P(dq), P(dk_), P(dv_), P(dla), None, P(wsb), wsb_n,
+                                        sp, eb, n_eb)
         if st:
-            raise nat.GlaError(st, "gla_chunk_bwd_traced")
+            raise nat.GlaError(st, "backward (traced)")
 
     def stage_means(evs_f, evs_b, n_steps, agg=statistics.fmean):
         acc = {}
@@ -582,21 +623,35 @@ def main():
     # The same steps with other gate inputs: gate logits (log_alpha = logsigmoid(x)/16
     # formed in the kernels, the gradient returned for x), and scalar gates (one per token,
     # [B, H, T], gradient summed over the key dimension).
-    def time_variant(desc_v, gate_t, dla_t, what):
-        ws_f = torch.empty(max(1, nat.workspace_bytes(desc_v, nat.PASS_FWD)), dtype=torch.uint8,
-                           device=dev)
-        ws_b = torch.empty(max(1, nat.workspace_bytes(desc_v, nat.PASS_BWD)), dtype=torch.uint8,
-                           device=dev)
+    def time_variant(desc_v, gate_t, dla_t, what, train_v=train):
+        pf_, pb_ = (nat.PASS_FWD_SAVE, nat.PASS_BWD_SAVED) if train_v else (nat.PASS_FWD, nat.PASS_BWD)
+        ws_f = torch.empty(max(1, nat.workspace_bytes(desc_v, pf_)), dtype=torch.uint8, device=dev)
+        ws_b = torch.empty(max(1, nat.workspace_bytes(desc_v, pb_)), dtype=torch.uint8, device=dev)
+        sv = torch.empty(max(1, nat.saved_bytes(desc_v) if train_v else 1), dtype=torch.uint8,
+                         device=dev)
         evs = hip.create(2)
 
         def step_v():
-            for st in (L.gla_chunk_fwd(ctypes.byref(desc_v), P(q), P(k), P(v), P(gate_t), None,
-                                       P(o), P(S_T), P(ws_f), ws_f.numel(), sp),
-                       L.gla_chunk_bwd(ctypes.byref(desc_v), P(q), P(k), P(v), P(gate_t), None,
-                                       P(dO), None, P(dq), P(dk_), P(dv_), P(dla_t), None,
-                                       P(ws_b), ws_b.numel(), sp)):
-                if st:
-                    raise nat.GlaError(st, f"gla_chunk_fwd/bwd with {what}")
+            if train_v:
+                calls = (L.gla_chunk_fwd_save(ctypes.byref(desc_v), P(q), P(k), P(v), P(gate_t),
+                                              None, P(o), P(S_T), P(sv), sv.numel(), P(ws_f),
+                                              ws_f.numel(), sp),
+                         lambda: L.gla_chunk_bwd_saved(ctypes.byref(desc_v), P(q), P(k), P(v),
+                                                       P(gate_t), None, P(dO), None, P(dq),
+                                                       P(dk_), P(dv_), P(dla_t), None, P(sv),
+                                                       sv.numel(), P(ws_b), ws_b.numel(), sp))
+            else:
+                calls = (L.gla_chunk_fwd(ctypes.byref(desc_v), P(q), P(k), P(v), P(gate_t), None,
+                                         P(o), P(S_T), P(ws_f), ws_f.numel(), sp),
+                         lambda: L.gla_chunk_bwd(ctypes.byref(desc_v), P(q), P(k), P(v),
+                                                 P(gate_t), None, P(dO), None, P(dq), P(dk_),
+                                                 P(dv_), P(dla_t), None, P(ws_b), ws_b.numel(),
+                                                 sp))
+            if calls[0]:
+                raise nat.GlaError(calls[0], f"forward with {what}")
+            st = calls[1]()
+            if st:
+                raise nat.GlaError(st, f"backward with {what}")
         for _ in range(3):
             step_v()
         n_v = max(5, args.steps // 2)
@@ -607,11 +662,14 @@ def main():
         torch.cuda.synchronize()
         vms = hip.elapsed_ms(evs[0], evs[1]) / n_v
         hip.destroy(evs)
-        del ws_f, ws_b
+        del ws_f, ws_b, sv
         return {"ms_per_step": vms, "value": B * T / (vms * 1e-3), "steps": n_v}
 
-    gate_fe = scalar_fe = None
+    gate_fe = scalar_fe = other_pair = None
     if not args.no_decode and not fwd_only:
+        if mode == nat.RECOMPUTE:
+            other_pair = time_variant(desc, la, dla, "the other pair", not train)
+            other_pair["pair"] = "recompute" if train else "train"
         dt_code = nat.BF16 if cfg.dtype == "bf16" else nat.F32
         desc_g = nat.make_desc(B, H, T, dk, dv, C, cfg.subchunk, dt_code, mode, nat.GATE_LOGITS,
                                16.0)
@@ -656,12 +714,13 @@ def main():
     for (tag, name), ms in stages.items():
         if ms <= 0.0:   # a stage with no launch for this shape
             continue
-        byt, fl = stage_work(name, tag, mode_s, B, H, T, dk, dv, C, e)
+        byt, fl = stage_work(name, tag, mode_s, B, H, T, dk, dv, C, e, train and tag == "fwd")
         print(f"{tag:4s} {name:16s} {ms * 1e3:9.2f} {byt / ms / 1e6:8.0f} {fl / ms / 1e9:8.1f}",
               file=sys.stderr)
     print(f"[bench] {dom_key[0]}:{dom_key[1]} in the timed steps: {dom_ms * 1e3:.2f} us",
           file=sys.stderr)
-    byt, fl = stage_work(dom_key[1], dom_key[0], mode_s, B, H, T, dk, dv, C, e)
+    byt, fl = stage_work(dom_key[1], dom_key[0], mode_s, B, H, T, dk, dv, C, e,
+                         train and dom_key[0] == "fwd")
     ai = fl / byt if byt else float("inf")
     ridge = PEAK_BF16 / PEAK_HBM
     if ai < ridge:
@@ -671,8 +730,11 @@ def main():
         roof = {"bound": "mfma", "achieved": fl / (dom_ms * 1e-3) / 1e12, "peak": PEAK_BF16 / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    stage_key = {"intra": f"intra_{dom_key[0]}"}.get(dom_key[1], dom_key[1])
-    roof["traffic"] = counter_traffic(stage_key, cfg.name, mode_s)
+    # the training pair's forward runs the intra-chunk kernel's fp32-operand instance
+    ikey = lambda tag: "intra_save" if train and tag == "fwd" else f"intra_{tag}"  # noqa: E731
+    kind = mode_s if (train or mode_s == "materialized" or fwd_only) else "recompute_pair"
+    stage_key = ikey(dom_key[0]) if dom_key[1] == "intra" else dom_key[1]
+    roof["traffic"] = counter_traffic(stage_key, cfg.name, kind)
     roof["kernel"] = f"{dom_key[0]}:{dom_key[1]}"
     roof["avg_launch_us"] = dom_ms * 1e3
     roof["algorithmic_bytes_per_launch"] = byt
@@ -680,7 +742,7 @@ def main():
     roof["ai_flop_per_byte"] = ai
     # measured matrix-unit use (committed counter summary of the default gate options):
     # the dominant stage's busy fraction, and every MFMA stage's alongside
-    mf = counter_mfma(cfg.name, mode_s) if not (args.scalar_gates or args.diag == "bf16") else {}
+    mf = counter_mfma(cfg.name, kind) if not (args.scalar_gates or args.diag == "bf16") else {}
     roof["mfma_busy_frac"] = mf.get(stage_key, {}).get("mfma_busy_frac")
     roof["mfma_counters"] = mf or None
     # the intra-chunk kernel against the bf16 MFMA peak: its algorithmic flops over its live
@@ -689,10 +751,10 @@ def main():
     for tag in ("fwd", "bwd"):
         ms_i = stages.get((tag, "intra"), 0.0)
         if ms_i > 0.0:
-            _, fl_i = stage_work("intra", tag, mode_s, B, H, T, dk, dv, C, e)
+            _, fl_i = stage_work("intra", tag, mode_s, B, H, T, dk, dv, C, e, train and tag == "fwd")
             intra_mfma[tag] = {"us": ms_i * 1e3, "tflops": fl_i / ms_i / 1e9,
                                "bf16_peak_frac": fl_i / (ms_i * 1e-3) / PEAK_BF16,
-                               "mfma_busy_frac": mf.get(f"intra_{tag}", {}).get("mfma_busy_frac")}
+                               "mfma_busy_frac": mf.get(ikey(tag), {}).get("mfma_busy_frac")}
 
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)
@@ -705,7 +767,8 @@ def main():
         "config": {"workload": cfg.name + ("_scalar_gates" if args.scalar_gates else "")
                    + ("_diag_bf16" if args.diag == "bf16" else ""),
                    "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": C,
-                   "subchunk": cfg.subchunk, "state_mode": mode_s, "global_batch": B,
+                   "subchunk": cfg.subchunk, "state_mode": mode_s,
+                   "pair": "train" if train else "recompute", "global_batch": B,
                    "seq_len": T, "parallelism": "none (1 GPU)"},
         "tflops": tflops, "mfma_peak_frac": flops / (ms_per_step * 1e-3) / PEAK_BF16,
         "roofline": roof,
@@ -713,6 +776,7 @@ def main():
         "cache_flushed": flush,
         "cache_flush": "512 MiB write then 512 MiB read before each timed step, untimed" if flush else None,
         "warm_cache": warm_rec,
+        "recompute_pair_step" if train else "train_pair_step": other_pair,
         "gate_logits_step": gate_fe,
         "scalar_gate_step": scalar_fe,
         "gsa_step": gsa_step,

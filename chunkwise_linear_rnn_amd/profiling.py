@@ -42,14 +42,16 @@ STAGE_KERNEL = {"bwd_dqk_dv": "k_bwd_dqk_dv",
                 "state_scans": "k_state_scan", "seg_state": "k_state_scan",
                 "output": "k_output",
                 "gate_tot": "k_gate_tot", "gate_reduce": "k_gate_reduce", "state_dot": "k_state_dot",
-                "state_scan": "k_state_scan", "intra_fwd": "k_intra", "intra_bwd": "k_intra"}
+                "state_scan": "k_state_scan", "intra_fwd": "k_intra", "intra_bwd": "k_intra",
+                "intra_save": "k_intra"}
 STAGE_SOURCE = {"bwd_dqk_dv": "k_bwd.hip",
                 "fwd_fused": "k_fwd.hip", "intra": "k_intra.hip",
                 "state_scan_fwd": "k_state.hip", "state_scan_rev": "k_state.hip",
                 "state_scans": "k_state.hip", "seg_state": "k_state.hip",
                 "output": "k_fwd.hip",
                 "gate_tot": "k_gate.hip", "gate_reduce": "k_gate.hip", "state_dot": "k_gate.hip",
-                "state_scan": "k_state.hip", "intra_fwd": "k_intra.hip", "intra_bwd": "k_intra.hip"}
+                "state_scan": "k_state.hip", "intra_fwd": "k_intra.hip", "intra_bwd": "k_intra.hip",
+                "intra_save": "k_intra.hip"}
 
 
 # Stages whose kernel name is shared by several launches of a step: the template
@@ -57,9 +59,12 @@ STAGE_SOURCE = {"bwd_dqk_dv": "k_bwd.hip",
 STAGE_SYMBOL = {"state_scans": ("ELi1ELb1E", ", 1, true"),     # stores states, cross terms
                 "seg_state": ("ELi0ELb0E", ", 0, false"),      # segment end states only
                 "state_scan": ("ELi2ELb0E", ", 2, false"),     # materialized forward states
-                # the forward's intra-chunk kernel writes Kh^T in bf16, the backward's in fp32
+                # the forward's intra-chunk kernel writes Kh^T in bf16, the backward's in fp32;
+                # the training pair's forward (which keeps the backward's operands) runs the
+                # backward's instance
                 "intra_fwd": ("DF16bDF16bDF16bLi", "bf16, bf16, bf16,"),
-                "intra_bwd": ("DF16bDF16bfLi", "bf16, bf16, float,")}
+                "intra_bwd": ("DF16bDF16bfLi", "bf16, bf16, float,"),
+                "intra_save": ("DF16bDF16bfLi", "bf16, bf16, float,")}
 
 
 def matches(stage: str, name: str) -> bool:
@@ -146,7 +151,7 @@ def counters(fetch_csv, write_csv, copy_bytes, stage, workload, command, root):
 
 
 MFMA_STAGES = ("fwd_fused", "bwd_dqk_dv", "state_scans", "seg_state", "output",
-               "state_scan", "intra_fwd", "intra_bwd")
+               "state_scan", "intra_fwd", "intra_bwd", "intra_save")
 SIMDS, XCDS, CLOCK_HZ, PEAK_BF16 = 1024, 8, 2.4e9, 2.5e15
 
 

@@ -45,6 +45,31 @@ def test_every_traced_stage_has_a_work_model(bench, native, mode, dtype, chunk):
                     continue
                 assert byt > 0, (tag, name)
                 assert fl >= 0, (tag, name)
+    if mode != "recompute":
+        return
+    # the training pair (recompute state mode only): its forward keeps the backward's
+    # operands, whose backward has no intra-chunk stage
+    for pass_, tag in ((native.PASS_FWD_SAVE, "fwd"), (native.PASS_BWD_SAVED, "bwd")):
+        names = native.trace_stages(d, pass_)
+        if tag == "bwd":
+            assert "intra" not in names
+        for name in names:
+            byt, fl = bench.stage_work(name, tag, mode, 4, 4, 2048, 256, 512, chunk, e,
+                                       tag == "fwd")
+            if name == "seg_state" and dtype == "f32":
+                continue
+            assert byt > 0, (tag, name)
+            if tag == "fwd" and dtype == "bf16":
+                # the kept operands: Qh^T and Kh^T in fp32 (4 bytes a key element) on top
+                # of what the plain forward writes; Kh^T read at 4 bytes by the fused and
+                # segment-state kernels
+                plain, _ = bench.stage_work(name, tag, mode, 4, 4, 2048, 256, 512, chunk, e)
+                tokp = 16 * ((2048 + chunk - 1) // chunk) * chunk
+                extra = {"intra": 2 * tokp * 256 * 4, "fwd_fused": tokp * 256 * 2}
+                if name in extra:
+                    assert byt - plain == extra[name], name
+                elif name == "seg_state":
+                    assert byt > plain
 
 
 def test_dominant_kernel_figures_at_1p3b(bench):
@@ -81,7 +106,8 @@ def test_mfma_summary_is_well_formed(bench):
         assert 0.0 <= k["bf16_peak_frac"] <= 1.0, k["kernel"]
         assert k["gpu_cycles_per_launch"] > 0, k["kernel"]
         stages.update(k["stages"])
-    assert {"bwd_dqk_dv", "fwd_fused", "state_scans", "intra_fwd", "intra_bwd"} <= stages
+    # the training pair's kernels (the forward runs the fp32-operand intra-chunk instance)
+    assert {"bwd_dqk_dv", "fwd_fused", "state_scans", "seg_state", "intra_save"} <= stages
     got = bench.counter_mfma("gla1p3b_t2k", "recompute")
     if not got:
         pytest.skip("mfma_gla1p3b_t2k.json predates the current kernel sources")
