@@ -83,7 +83,8 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e, save=False):
     type; flops count a multiply-add as 2 and the causal intra-chunk products at half
     the chunk (C/2 average partners).  `save`: the forward of the training pair, whose
     intra-chunk kernel also writes the backward's operands and whose Kh^T is stored as
-    fp32 (with bf16 inputs: a bf16 high part and remainder, 4 bytes an element)."""
+    fp32 (with bf16 inputs: a bf16 high part and remainder, 4 bytes an element; the
+    segment-state prepass reads both parts)."""
     BH, N = B * H, (T + C - 1) // C
     tok = BH * T
     tokp = BH * N * C                      # padded rows of per-chunk operands
@@ -124,7 +125,8 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e, save=False):
             byt += 2 * (P - 2) * st4
         return byt, h * 2 * dk * dv
     if stage == "fwd_fused":
-        byt = tokp * dk * (e + kt) + BH * N * C * C * e + 2 * tok * dv * e + BH * dk * dv * 4
+        # (the training pair's split Kh^T is read by its high part only: e bytes an element)
+        byt = 2 * tokp * dk * e + BH * N * C * C * e + 2 * tok * dv * e + BH * dk * dv * 4
         return byt, tok * (4 * dk * dv + C * dv)
     if stage == "bwd_dqk_dv":
         # dq/dk part: reads q, k, v, dO, log_alpha, S, dS, chunk totals; writes dq, dk, dla
