@@ -83,13 +83,12 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e, save=False):
     type; flops count a multiply-add as 2 and the causal intra-chunk products at half
     the chunk (C/2 average partners).  `save`: the forward of the training pair, whose
     intra-chunk kernel also writes the backward's operands and whose Kh^T is stored as
-    fp32 (with bf16 inputs: a bf16 high part and remainder, 4 bytes an element; the
-    segment-state prepass reads both parts)."""
+    fp32 (with bf16 inputs: a bf16 high part and remainder, 4 bytes an element, of which
+    the forward's later kernels read the high part alone)."""
     BH, N = B * H, (T + C - 1) // C
     tok = BH * T
     tokp = BH * N * C                      # padded rows of per-chunk operands
     st = BH * N * dk * dv * e              # one materialized state tensor
-    kt = 4 if save else e                  # bytes of one stored Kh^T element
     if stage == "intra":
         if pass_ == "fwd" and save:
             # reads log_alpha, q, k; writes A, Qh and Kh (storage type), Qh^T and Kh^T
@@ -120,12 +119,11 @@ def stage_work(stage, pass_, mode, B, H, T, dk, dv, C, e, save=False):
         ns = (P - 1) * N // P
         h = BH * ns * C
         st4 = BH * dk * dv * 4
-        byt = h * dk * kt + h * dv * e + BH * ns * dk * 4 + (P - 1) * st4
+        byt = h * dk * e + h * dv * e + BH * ns * dk * 4 + (P - 1) * st4
         if P > 2:
             byt += 2 * (P - 2) * st4
         return byt, h * 2 * dk * dv
     if stage == "fwd_fused":
-        # (the training pair's split Kh^T is read by its high part only: e bytes an element)
         byt = 2 * tokp * dk * e + BH * N * C * C * e + 2 * tok * dv * e + BH * dk * dv * 4
         return byt, tok * (4 * dk * dv + C * dv)
     if stage == "bwd_dqk_dv":

@@ -466,7 +466,9 @@ static gla_status_t fwd_run(const gla_desc_t* d, const void* q, const void* k, c
       sa.nseg = fa.nseg - 1; sa.seg_p = fa.nseg; sa.seg_decay = (float*)(w + p.segdec);
     }
     sa.XT = ob + op.KhT; sa.Y = v; sa.eg = (const float*)(ob + op.eg); sa.S_in = S0;
-    sa.xt_f32 = split;   // (then the split operand: high part and remainder)
+    // the split operand's high part alone: the bf16 rounding the plain forward stores, so
+    // that the segment start states, and o, are those of gla_chunk_fwd
+    sa.xt_hi = split;
     sa.S_out = (float*)(w + p.smid);
     if ((rs = dev(gla::launch_state_scan(sa, s))) != GLA_OK) return rs;
     if ((rs = dev(gla::launch_seg_combine((float*)(w + p.smid), (const float*)(w + p.segdec),

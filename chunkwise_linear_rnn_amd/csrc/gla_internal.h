@@ -68,6 +68,7 @@ struct ScanArgs {
   int dtype, C, BH, T, dk, dv, N;
   bool reverse;
   bool xt_f32;           // XT / X2T rows hold a bf16 high part then its remainder
+  bool xt_hi;            // bf16 XT / X2T in that split layout, read by the high part alone
   int store;
   const void* XT;        // [BH][N][dk][C] (Kh^T forward, Qh^T reverse)
   const void* Y;         // [BH][T][dv]    input type (v forward, dO reverse)

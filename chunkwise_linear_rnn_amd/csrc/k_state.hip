@@ -36,19 +36,20 @@ namespace gla {
 // order, as the intra-chunk kernel writes it: for each 16-row block and 32-token block kb,
 // the 64 lanes' 16-byte pieces (lane 16 q + r: row r, tokens 32 kb + 8 q ..), and with
 // SPLIT the high-part fragment followed by the remainder's; `at` = the row block's first
-// piece plus the lane's, so that every load reads 1 KB of whole cache lines.
+// piece plus the lane's, so that every load reads 1 KB of whole cache lines.  Without
+// SPLIT, `kst` = 2 reads the high parts of a split operand alone (every other fragment).
 template <typename OpT, bool SPLIT, int C>
 struct XRegs {
   static constexpr int KB = C / 32;
   Frag<OpT> hi[KB], lo[SPLIT ? KB : 1];
-  __device__ __forceinline__ void load(const OpT* __restrict__ at) {
+  __device__ __forceinline__ void load(const OpT* __restrict__ at, int kst) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       if constexpr (SPLIT) {
         hi[kb].v = *reinterpret_cast<const bf16x8*>(at + (2 * kb) * 64 * 8);
         lo[kb].v = *reinterpret_cast<const bf16x8*>(at + (2 * kb + 1) * 64 * 8);
       } else if constexpr (sizeof(OpT) == 2) {
-        hi[kb].v = *reinterpret_cast<const bf16x8*>(at + kb * 64 * 8);
+        hi[kb].v = *reinterpret_cast<const bf16x8*>(at + kb * kst * 64 * 8);
       } else {
         load_frag_c(hi[kb], at + kb * 32);
       }
@@ -67,7 +68,7 @@ template <typename Tin, typename OpT, bool SPLIT, int C, int STORE, bool CROSS, 
 __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, ScanDir d1, int ndir,
                                                             const float* __restrict__ eg, int T,
                                                             int dk, int dv, int N, int nsteps,
-                                                            int nseg, int segp) {
+                                                            int nseg, int segp, int kst) {
   // TV value columns per workgroup: NJ accumulator tiles per wave, NY 64-column
   // value-side tiles per operand
   constexpr int NJ = TV / 16, NY = TV / 64;
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
   // where this lane's rows of a chunk's transposed operand start (see XRegs)
   auto xrow = [&](int i) {
     if constexpr (sizeof(OpT) == 2)
-      return ((((long)bh * N + i) * (dk / 16) + (k0 / 16 + w)) * ((SPLIT ? 2 : 1) * (C / 32)) * 64 + l) * 8;
+      return ((((long)bh * N + i) * (dk / 16) + (k0 / 16 + w)) * ((SPLIT ? 2 : kst) * (C / 32)) * 64 + l) * 8;
     else
       return (((long)bh * N + i) * dk + k0 + 16 * w + r) * (long)C;
   };
@@ -214,8 +215,8 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
     for (int d = 0; d < DEPTH; ++d) {
       const int i0 = chunk_of(d);
       if (!WT || d == 0) fetch_y(sets[d], i0);
-      sets[d].cx.load(XT + xrow(i0));
-      if constexpr (CROSS) sets[d].cx2.load(X2T + xrow(i0));
+      sets[d].cx.load(XT + xrow(i0), kst);
+      if constexpr (CROSS) sets[d].cx2.load(X2T + xrow(i0), kst);
     }
   }
 
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
 #pragma unroll
         for (int e = 0; e < 4; ++e) sum += acc[j][e] * P[e];
       }
-      st.cx2.load(X2T + xrow(ipre));
+      st.cx2.load(X2T + xrow(ipre), kst);
       sum += __shfl_xor(sum, 16);
       sum += __shfl_xor(sum, 32);
       part_prev = sum;
@@ -340,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 256 / TV) void k_state_scan(ScanDir d0, S
         yfrag(fb, ys, 16 * j + r, kb);
         st.cx.apply_t(acc[j], kb, fb);
       }
-    st.cx.load(XT + xrow(ipre));
+    st.cx.load(XT + xrow(ipre), kst);
     __syncthreads();
   };
   // blocks of EB steps (EB even: step s runs on set s % DEPTH throughout); each step ends
@@ -391,7 +392,8 @@ static void launch_scan_k(const ScanArgs& a, const ScanArgs* b, hipStream_t s) {
   dim3 grid(ndir * nseg * (a.dv / TV) * (a.dk / 64) * a.BH);
   hipLaunchKernelGGL((k_state_scan<Tin, OpT, SPLIT, C, STORE, CROSS, TV>), grid, dim3(kThreads), 0,
                      s, dir(a), dir(b ? *b : a), ndir, a.eg, a.T, a.dk, a.dv, a.N,
-                     a.nsteps > 0 && a.nsteps < a.N ? a.nsteps : a.N, nseg, segm ? a.seg_p : 1);
+                     a.nsteps > 0 && a.nsteps < a.N ? a.nsteps : a.N, nseg, segm ? a.seg_p : 1,
+                     a.xt_hi ? 2 : 1);
 }
 
 int scan_tile_v(const ScanArgs& a) {
@@ -448,9 +450,12 @@ static hipError_t launch_scans(const ScanArgs& a, const ScanArgs* b, hipStream_t
     return hipErrorInvalidValue;
   if (b && (b->dtype != a.dtype || b->C != a.C || b->BH != a.BH || b->T != a.T ||
             b->dk != a.dk || b->dv != a.dv || b->N != a.N || b->xt_f32 != a.xt_f32 ||
+            b->xt_hi != a.xt_hi ||
             b->store != a.store || (b->cross != nullptr) != (a.cross != nullptr) || b->eg != a.eg ||
             b->nsteps != a.nsteps))
     return hipErrorInvalidValue;
+  // the high parts alone: bf16 operands in the split layout, read as unsplit ones
+  if (a.xt_hi && (a.dtype == 0 || a.xt_f32)) return hipErrorInvalidValue;
   if (a.dtype == 0) return launch_scan_t<float, float, false, 64>(a, b, s);
   if (a.xt_f32) {
     if (a.C == 64) return launch_scan_t<bf16, bf16, true, 64>(a, b, s);

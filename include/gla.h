@@ -228,9 +228,9 @@ gla_status_t gla_chunk_bwd(const gla_desc_t* desc, const void* q, const void* k,
  * gla_saved_bytes(desc) bytes, caller-owned; contents opaque): the decayed causal matrix A,
  * Q*e^g token-major and transposed, K*e^(gamma-g) token-major and transposed (the
  * transposed ones as the backward's scans read them: bf16 inputs as a bf16 high part and
- * bf16 remainder) and e^gamma.  o and S_T are those of gla_chunk_fwd; with bf16 inputs the
- * second and later sequence segments start from states formed from the unrounded decayed
- * keys (high part and remainder), so o may differ from gla_chunk_fwd's in the last bits.
+ * bf16 remainder) and e^gamma.  o and S_T are bit for bit those of gla_chunk_fwd (with bf16
+ * inputs the forward's later kernels read the high parts of the transposed keys alone,
+ * the bf16 rounding gla_chunk_fwd stores).
  * ws: at least gla_workspace_bytes(desc, GLA_PASS_FWD_SAVE) bytes.
  *
  * gla_chunk_bwd_saved: gla_chunk_bwd without its intra-chunk kernel, reading those operands

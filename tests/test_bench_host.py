@@ -61,15 +61,12 @@ def test_every_traced_stage_has_a_work_model(bench, native, mode, dtype, chunk):
             assert byt > 0, (tag, name)
             if tag == "fwd" and dtype == "bf16":
                 # the kept operands: Qh^T and Kh^T in fp32 (4 bytes a key element) on top
-                # of what the plain forward writes; the segment-state prepass reads both
-                # parts of the split Kh^T, the fused kernel its high part only
+                # of what the plain forward writes; the later kernels read the split
+                # Kh^T's high part alone
                 plain, _ = bench.stage_work(name, tag, mode, 4, 4, 2048, 256, 512, chunk, e)
                 tokp = 16 * ((2048 + chunk - 1) // chunk) * chunk
-                extra = {"intra": 2 * tokp * 256 * 4, "fwd_fused": 0}
-                if name in extra:
-                    assert byt - plain == extra[name], name
-                elif name == "seg_state":
-                    assert byt > plain
+                extra = {"intra": 2 * tokp * 256 * 4}
+                assert byt - plain == extra.get(name, 0), name
 
 
 def test_dominant_kernel_figures_at_1p3b(bench):
