@@ -82,10 +82,12 @@ def test_train_pair_small(gla, case):
             check(k, pick(host(got[k]), heads), ref[k], dt)
 
 
-def test_train_pair_full_shape(gla):
-    """The 1.3B head shape: every head's output and gradients bit for bit those of
-    gla_chunk_fwd and gla_chunk_bwd, one head against the oracle."""
-    cfg = CONFIGS["gla1p3b_t2k"]
+@pytest.mark.parametrize("name", ["gla1p3b_t2k", "gla340m_t2k", "sweep_t4096_c128"])
+def test_train_pair_full_shape(gla, name):
+    """The full workloads (the 1.3B and 340M head shapes at chunk 64, a chunk-128 sweep
+    point): every head's output and gradients bit for bit those of gla_chunk_fwd and
+    gla_chunk_bwd, one head against the oracle."""
+    cfg = CONFIGS[name]
     say(f"[train pair] full shape {cfg}")
     d = generate(cfg)
     x = dev_inputs(d, cfg.dtype, DEV)
@@ -93,7 +95,7 @@ def test_train_pair_full_shape(gla):
     for nm, a, b in zip(("dq", "dk", "dv", "dla", "dS0"), gs, g):
         assert torch.equal(a, b), f"{nm} differs from gla_chunk_bwd"
     assert torch.equal(o, o2) and torch.equal(ST, ST2), "forward differs from gla_chunk_fwd"
-    heads = [(1, 2)]
+    heads = [(cfg.B - 1, cfg.H - 2)]
     ref = oracle_heads(d, heads)
     got = {"o": o, "dq": gs[0], "dk": gs[1], "dv": gs[2], "dla": gs[3]}
     for k in ("o", "dq", "dk", "dv", "dla"):
